@@ -1,0 +1,425 @@
+"""Pins for the CPU oracle: each test checks it against something other than
+itself -- values the page prints, closed forms, invariants the method implies,
+special cases that reduce to textbook routines, and brute force on tiny inputs.
+
+Page: "ShadowKV: KV Cache in Shadows for High-Throughput Long-Context LLM
+Inference" (xllm-io paper-review blog), section 三 (Algorithms 1 and 2, the
+equivalent-bandwidth formula, the key-parameter table); the Telegram write-up
+"Ускорение E2E-инференса ... Часть II" for the set-difference cache.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import Shape
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# Independent formulations used by the pins (not the oracle's code paths)
+# ---------------------------------------------------------------------------
+def rope_complex(x, pos, base=10000.0):
+    """Rotate-half RoPE written as complex multiplication: the pair
+    (x_i, x_{i+d/2}) is the complex number x_i + i x_{i+d/2}, turned by the
+    angle pos * base^(-2i/d)."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    h = d // 2
+    theta = base ** (-2.0 * np.arange(h) / d)
+    z = x[..., :h] + 1j * x[..., h:]
+    z = z * np.exp(1j * np.multiply.outer(np.asarray(pos, dtype=np.float64), theta))
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+def dense_attention(q, K, V):
+    """softmax(q K^T / sqrt(d)) V for one head (SnapKV review page's attention
+    definition), computed with a max-shifted softmax."""
+    logits = K @ q / math.sqrt(q.shape[-1])
+    p = np.exp(logits - logits.max())
+    return (p / p.sum()) @ V
+
+
+def tiny_shape(**kw):
+    base = dict(b=1, h_q=4, h_kv=2, d=8, s=64, c=4, r=16, o=2, k=3, w=8, bf16=False)
+    base.update(kw)
+    return Shape(**base)
+
+
+# ---------------------------------------------------------------------------
+# Printed values
+# ---------------------------------------------------------------------------
+def test_equiv_bandwidth_matches_printed_example():
+    g = json.load(open(os.path.join(GOLDEN, "equiv_bandwidth.json")))
+    i = g["inputs"]
+    bw = oracle.equiv_bandwidth(i["S"], i["C"], i["K"], i["O"], i["alpha"], i["B_gpu"], i["B_pcie"])
+    assert round(bw / 1e12, g["printed_digits"]) == g["printed_TBps"]
+    assert round(bw / i["B_gpu"], 1) == g["printed_ratio_to_B_gpu"]
+    # "128K" read as 128000 would print 7.0, not 7.2.
+    assert round(oracle.equiv_bandwidth(128000, 8, 256, 48, 0.6, 2e12, 31.5e9) / 1e12, 1) == 7.0
+    # Closed-form limits of the formula: with no PCIe term and only the
+    # landmark read, B~ = 2 C B_GPU.
+    assert oracle.equiv_bandwidth(1 << 20, 8, 0, 0, 1.0, 1.0, 1.0) == pytest.approx(16.0)
+    # A perfect cache removes the PCIe term entirely.
+    assert oracle.equiv_bandwidth(131072, 8, 256, 48, 1.0, 2e12, 31.5e9) == pytest.approx(
+        2 * 131072 * 2e12 / (131072 / 8 + 2 * 304 * 8))
+
+
+def test_key_parameters_and_budget():
+    g = json.load(open(os.path.join(GOLDEN, "key_parameters.json")))
+    from sparse_kv_cache_step_amd import synth
+    for wl in synth.WORKLOADS.values():
+        if wl.name == "tiny-fp32":
+            continue
+        assert wl.c == g["chunk"] and wl.r == g["rank"] and wl.o == g["outlier_chunks"]
+        # 1.56 % budget: k chunks of n (k = n/64 = 1.5625 %).
+        assert round(100.0 * wl.k / wl.n, 2) == g["budget_percent"]
+
+
+# ---------------------------------------------------------------------------
+# bfloat16 rounding (storage points)
+# ---------------------------------------------------------------------------
+def test_round_bf16_against_torch_conversion():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-39).astype(np.float32),     # subnormal range
+        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 3.0e38, -3.4e38, 0.0], np.float32),
+    ])
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.round_bf16(x.astype(np.float64))
+    np.testing.assert_array_equal(got, ref)
+    # ties to even, by hand
+    assert oracle.round_bf16([1 + 2 ** -8])[0] == 1.0
+    assert oracle.round_bf16([1 + 3 * 2 ** -8])[0] == 1 + 2 ** -6
+
+
+# ---------------------------------------------------------------------------
+# RoPE
+# ---------------------------------------------------------------------------
+def test_rope_matches_complex_rotation_and_invariants():
+    rng = np.random.default_rng(1)
+    for d in (2, 4, 64, 128):
+        x = rng.standard_normal(d)
+        for pos in (0, 1, 7, 1000, 249855):
+            y = oracle.rope(x, pos)
+            # the angle pos*theta carries ~pos * 2^-52 of rounding on either side
+            np.testing.assert_allclose(y, rope_complex(x, pos), rtol=0, atol=1e-12 + pos * 1e-15)
+            assert np.linalg.norm(y) == pytest.approx(np.linalg.norm(x), rel=1e-13)
+        np.testing.assert_array_equal(oracle.rope(x, 0), x)
+    # relative-position property: <R(m) q, R(n) k> depends on m - n only
+    q, k = rng.standard_normal(128), rng.standard_normal(128)
+    a = oracle.rope(q, 100) @ oracle.rope(k, 37)
+    b = oracle.rope(q, 163) @ oracle.rope(k, 100)
+    assert a == pytest.approx(b, rel=1e-11)
+    # d = 4 written out: pairs (0, 2) and (1, 3), frequencies 1 and base^-1/2
+    x = np.array([1.0, 2.0, 3.0, 4.0])
+    p = 5.0
+    t1 = 10000.0 ** -0.5
+    expect = [1 * math.cos(p) - 3 * math.sin(p), 2 * math.cos(p * t1) - 4 * math.sin(p * t1),
+              3 * math.cos(p) + 1 * math.sin(p), 4 * math.cos(p * t1) + 2 * math.sin(p * t1)]
+    np.testing.assert_allclose(oracle.rope(x, p), expect, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# ArgTopK
+# ---------------------------------------------------------------------------
+def test_topk_brute_force_with_ties():
+    rng = np.random.default_rng(2)
+    for trial in range(200):
+        n = int(rng.integers(1, 60))
+        k = int(rng.integers(0, n + 1))
+        key = rng.integers(0, 6, n).astype(np.float64)  # many exact ties
+        valid = rng.random(n) < 0.8
+        if valid.sum() < k:
+            continue
+        got = oracle.topk(key, k, valid)
+        # brute force: sort candidates by (-key, index)
+        cands = sorted((-key[j], j) for j in range(n) if valid[j])
+        expect = sorted(j for _, j in cands[:k])
+        assert list(got) == expect
+
+
+# ---------------------------------------------------------------------------
+# Algorithm 1 step 1: SVD factors
+# ---------------------------------------------------------------------------
+def test_svd_exact_when_true_rank_at_most_r():
+    rng = np.random.default_rng(3)
+    b, hkv, s, d, R = 2, 2, 96, 16, 6
+    shape = tiny_shape(b=b, h_kv=hkv, h_q=4, d=d, s=s, r=8, o=1, k=2, w=8)
+    K = np.einsum("bsr,brk->bsk", rng.standard_normal((b, s, R)), rng.standard_normal((b, R, hkv * d)))
+    K = K.reshape(b, s, hkv, d).transpose(0, 2, 1, 3)
+    K = K.astype(np.float32).astype(np.float64)
+    A, B = oracle.svd_factors(shape, K)
+    assert A.shape == (b, s, 8) and B.shape == (b, hkv, 8, d)
+    for bi in range(b):
+        for h in range(hkv):
+            np.testing.assert_allclose(A[bi] @ B[bi, h], K[bi, h], rtol=0, atol=1e-5)  # fp32-stored factors
+    # full rank r = h_kv * d reproduces any K
+    full = tiny_shape(b=1, h_kv=2, d=8, s=64, r=16)
+    K2 = rng.standard_normal((1, 2, 64, 8)).astype(np.float32).astype(np.float64)
+    A2, B2 = oracle.svd_factors(full, K2)
+    for h in range(2):
+        np.testing.assert_allclose(A2[0] @ B2[0, h], K2[0, h], atol=1e-5)
+    # the rank-r product is the best rank-r approximation (Eckart-Young):
+    # its error equals the tail of the singular values
+    K3 = rng.standard_normal((1, 2, 64, 8))
+    sh = tiny_shape(b=1, h_kv=2, d=8, s=64, r=5)
+    A3, B3 = oracle.svd_factors(sh, K3)
+    M = K3[0].transpose(1, 0, 2).reshape(64, 16)
+    approx = np.concatenate([A3[0] @ B3[0, h] for h in range(2)], axis=1)
+    sv = np.linalg.svd(M, compute_uv=False)
+    assert np.linalg.norm(M - approx) == pytest.approx(np.sqrt((sv[5:] ** 2).sum()), rel=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# Algorithm 1 steps 2-5: landmarks, cosine-min, outliers, static buffers
+# ---------------------------------------------------------------------------
+def _unrotated_chunks(rng, shape, base=10000.0):
+    """K_pre whose post-RoPE keys are constant within each chunk: token t of
+    chunk j holds R(-t) x_j, so R(t) K_pre[t] = x_j."""
+    b, h, s, d, c = shape.b, shape.h_kv, shape.s, shape.d, shape.c
+    x = rng.standard_normal((b, h, s // c, d))
+    xt = np.repeat(x, c, axis=2)
+    pos = np.arange(s)
+    return rope_complex(xt, -pos[None, None, :], base), x
+
+
+def test_prefill_constant_chunks_give_unit_cosine_and_exact_landmarks():
+    rng = np.random.default_rng(4)
+    shape = tiny_shape(b=2, h_kv=2, d=16, s=128, c=8, o=3, k=4, w=16)
+    K, x = _unrotated_chunks(rng, shape)
+    V = rng.standard_normal(K.shape)
+    m = oracle.prefill(shape, K, V)
+    # landmark = the chunk's common post-RoPE key (stored in fp32)
+    np.testing.assert_allclose(m["landmarks"], x, rtol=0, atol=1e-6)
+    np.testing.assert_allclose(m["min_cos"], 1.0, atol=1e-6)
+
+
+def test_prefill_landmarks_are_chunk_means_of_rotated_keys():
+    rng = np.random.default_rng(5)
+    shape = tiny_shape(b=1, h_kv=2, d=8, s=64, c=4, o=2, k=3, w=8)
+    K = rng.standard_normal((1, 2, 64, 8))
+    V = rng.standard_normal(K.shape)
+    m = oracle.prefill(shape, K, V)
+    Kr = rope_complex(K, np.arange(64)[None, None, :]).astype(np.float32).astype(np.float64)
+    L = Kr.reshape(1, 2, 16, 4, 8).mean(axis=3)
+    np.testing.assert_allclose(m["landmarks"], L, rtol=1e-6, atol=1e-6)
+    # min cosine by brute force over the c tokens of every chunk
+    for h in range(2):
+        for j in range(16):
+            cs = [Kr[0, h, j * 4 + t] @ L[0, h, j] / np.linalg.norm(Kr[0, h, j * 4 + t]) / np.linalg.norm(L[0, h, j])
+                  for t in range(4)]
+            assert m["min_cos"][0, h, j] == pytest.approx(min(cs), abs=1e-6)
+
+
+def test_prefill_outliers_static_buffers_and_candidates():
+    rng = np.random.default_rng(6)
+    shape = tiny_shape(b=2, h_kv=2, d=8, s=96, c=4, o=3, k=4, w=12)
+    n, n_loc = 24, 3
+    K, _ = _unrotated_chunks(rng, shape)
+    # make chunk 5 of (0, 0) and chunk 9 of (1, 1) very non-uniform, and the
+    # local window's last chunk too (it must not be chosen)
+    for (bi, h, j) in [(0, 0, 5), (1, 1, 9), (0, 0, n - 1), (1, 1, n - 2)]:
+        K[bi, h, j * 4:(j + 1) * 4] = rng.standard_normal((4, 8))
+    V = rng.standard_normal(K.shape)
+    m = oracle.prefill(shape, K, V)
+    assert 5 in m["outliers"][0, 0] and 9 in m["outliers"][1, 1]
+    for bi in range(2):
+        for h in range(2):
+            outl = m["outliers"][bi, h]
+            assert list(outl) == sorted(outl) and len(set(outl)) == 3
+            assert all(j < n - n_loc for j in outl)
+            # the o lowest binary32 min-cosines (ties: lower index) -- brute force
+            mc = m["min_cos"][bi, h, : n - n_loc].astype(np.float32)
+            expect = sorted(sorted(range(n - n_loc), key=lambda j: (mc[j], j))[:3])
+            assert list(outl) == expect
+            for a, j in enumerate(outl):
+                np.testing.assert_array_equal(m["v_out"][bi, h, a * 4:(a + 1) * 4], V[bi, h, j * 4:(j + 1) * 4])
+                Kr = rope_complex(K[bi, h, j * 4:(j + 1) * 4], np.arange(j * 4, j * 4 + 4))
+                np.testing.assert_allclose(m["k_out"][bi, h, a * 4:(a + 1) * 4], Kr, atol=1e-6)
+            np.testing.assert_array_equal(m["v_loc"][bi, h], V[bi, h, -12:])
+            np.testing.assert_allclose(m["k_loc"][bi, h], rope_complex(K[bi, h, -12:], np.arange(84, 96)), atol=1e-6)
+            cand = m["cand"][bi, h]
+            assert cand.sum() == n - n_loc - 3
+            assert not cand[outl].any() and not cand[n - n_loc:].any()
+
+
+def test_cosine_min_is_scale_invariant():
+    rng = np.random.default_rng(7)
+    shape = tiny_shape(b=1, h_kv=1, h_q=2, d=8, s=64, c=8, o=1, k=2, w=8)
+    K = rng.standard_normal((1, 1, 64, 8))
+    V = rng.standard_normal(K.shape)
+    a = oracle.prefill(shape, K, V)
+    K2 = K.copy()
+    K2[0, 0, 16:24] *= 5.0
+    b = oracle.prefill(shape, K2, V)
+    np.testing.assert_allclose(a["min_cos"], b["min_cos"], atol=1e-6)
+    np.testing.assert_allclose(b["landmarks"][0, 0, 2], 5.0 * a["landmarks"][0, 0, 2], rtol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# Algorithm 2
+# ---------------------------------------------------------------------------
+def _meta_and_factors(shape, K, V):
+    meta = oracle.prefill(shape, K, V)
+    A, B = oracle.svd_factors(shape, K)
+    return meta, A, B
+
+
+def test_scores_are_the_textbook_gemv_and_s2_is_a_distribution():
+    rng = np.random.default_rng(8)
+    shape = tiny_shape(b=2, h_q=6, h_kv=2, d=8, s=96, c=4, r=16, o=2, k=5, w=8)
+    K = rng.standard_normal((2, 2, 96, 8))
+    V = rng.standard_normal(K.shape)
+    q = rng.standard_normal((2, 6, 8))
+    meta, A, B = _meta_and_factors(shape, K, V)
+    res = oracle.decode(shape, q, meta, A, B, V)
+    G = 3
+    for bi in range(2):
+        for g in range(6):
+            h = g // G
+            ref = meta["landmarks"][bi, h] @ q[bi, g] / math.sqrt(8)
+            cand = meta["cand"][bi, h].astype(bool)
+            np.testing.assert_allclose(res["P"][bi, g][cand], ref[cand], rtol=1e-12)
+            assert np.all(np.isneginf(res["P"][bi, g][~cand]))
+        for h in range(2):
+            cand = meta["cand"][bi, h].astype(bool)
+            assert res["S2"][bi, h][cand].sum() == pytest.approx(1.0, rel=1e-12)
+            assert np.all(res["S2"][bi, h][~cand] == 0)
+
+
+def test_selection_brute_force_and_group_one_reduces_to_score_topk():
+    rng = np.random.default_rng(9)
+    for G in (1, 4):
+        shape = tiny_shape(b=1, h_q=2 * G, h_kv=2, d=8, s=128, c=4, r=16, o=2, k=6, w=8)
+        K = rng.standard_normal((1, 2, 128, 8))
+        V = rng.standard_normal(K.shape)
+        q = rng.standard_normal((1, 2 * G, 8)) * 3
+        meta, A, B = _meta_and_factors(shape, K, V)
+        res = oracle.decode(shape, q, meta, A, B, V)
+        for h in range(2):
+            cand = np.flatnonzero(meta["cand"][0, h])
+            # brute force: per-head softmax over the candidates, mean over the group
+            Lc = meta["landmarks"][0, h, cand]
+            s2 = np.zeros(len(cand))
+            for gi in range(G):
+                p = Lc @ q[0, h * G + gi] / math.sqrt(8)
+                e = np.exp(p - p.max())
+                s2 += e / e.sum() / G
+            order = sorted(range(len(cand)), key=lambda i: (-np.float32(s2[i]), cand[i]))
+            assert list(res["sel"][0, h]) == sorted(cand[order[:6]])
+            if G == 1:
+                p = Lc @ q[0, h] / math.sqrt(8)
+                assert list(res["sel"][0, h]) == sorted(cand[np.argsort(-p, kind="stable")[:6]])
+
+
+def test_full_budget_full_rank_is_dense_attention():
+    """With every selectable chunk chosen and rank h_kv*d, the concatenation
+    [K_outlier; RoPE(K_sparse); K_local] covers every token once and the rank-r
+    keys are exact, so the step must equal dense softmax(qK^T/sqrt d)V over the
+    whole context with keys rotated at their own positions."""
+    rng = np.random.default_rng(10)
+    b, hq, hkv, d, s, c, o, w = 2, 4, 2, 8, 64, 4, 2, 8
+    n = s // c
+    shape = Shape(b=b, h_q=hq, h_kv=hkv, d=d, s=s, c=c, r=hkv * d, o=o, k=n - o - w // c, w=w, bf16=False)
+    K = rng.standard_normal((b, hkv, s, d)).astype(np.float32).astype(np.float64)
+    V = rng.standard_normal((b, hkv, s, d)).astype(np.float32).astype(np.float64)
+    q = rng.standard_normal((b, hq, d))
+    meta, A, B = _meta_and_factors(shape, K, V)
+    res = oracle.decode(shape, q, meta, A, B, V)
+    Kr = rope_complex(K, np.arange(s)[None, None, :])
+    for bi in range(b):
+        for g in range(hq):
+            h = g // (hq // hkv)
+            ref = dense_attention(q[bi, g], Kr[bi, h], V[bi, h])
+            np.testing.assert_allclose(res["out"][bi, g], ref, rtol=0, atol=2e-6)
+
+
+def test_partial_budget_is_attention_over_the_partition():
+    """At a partial budget and full rank the output is dense attention over
+    exactly the tokens of the outlier, selected and local chunks."""
+    rng = np.random.default_rng(11)
+    b, hq, hkv, d, s, c, o, w, k = 1, 4, 2, 8, 128, 4, 3, 8, 5
+    shape = Shape(b=b, h_q=hq, h_kv=hkv, d=d, s=s, c=c, r=hkv * d, o=o, k=k, w=w, bf16=False)
+    K = rng.standard_normal((b, hkv, s, d)).astype(np.float32).astype(np.float64)
+    V = rng.standard_normal((b, hkv, s, d))
+    q = rng.standard_normal((b, hq, d)) * 2
+    meta, A, B = _meta_and_factors(shape, K, V)
+    res = oracle.decode(shape, q, meta, A, B, V)
+    Kr = rope_complex(K, np.arange(s)[None, None, :])
+    for g in range(hq):
+        h = g // 2
+        chunks = sorted(set(meta["outliers"][0, h]) | set(res["sel"][0, h]) | set(range(s // c - w // c, s // c)))
+        toks = np.concatenate([np.arange(j * c, (j + 1) * c) for j in chunks])
+        ref = dense_attention(q[0, g], Kr[0, h, toks], V[0, h, toks])
+        np.testing.assert_allclose(res["out"][0, g], ref, atol=2e-6)
+
+
+def test_gqa_head_mapping_and_convexity():
+    rng = np.random.default_rng(12)
+    b, hq, hkv, d, s, c = 1, 8, 2, 8, 64, 4
+    shape = Shape(b=b, h_q=hq, h_kv=hkv, d=d, s=s, c=c, r=16, o=2, k=4, w=8, bf16=False)
+    K = rng.standard_normal((b, hkv, s, d))
+    V = np.empty((b, hkv, s, d))
+    V[:, 0] = -1.0
+    V[:, 1] = 1.0
+    q = rng.standard_normal((b, hq, d))
+    meta, A, B = _meta_and_factors(shape, K, V)
+    res = oracle.decode(shape, q, meta, A, B, V)
+    # q heads 0..3 read KV head 0, heads 4..7 read KV head 1
+    np.testing.assert_allclose(res["out"][0, :4], -1.0, atol=1e-12)
+    np.testing.assert_allclose(res["out"][0, 4:], 1.0, atol=1e-12)
+    V2 = rng.standard_normal((b, hkv, s, d))
+    meta2, _, _ = _meta_and_factors(shape, K, V2)
+    out = oracle.decode(shape, q, meta2, A, B, V2)["out"]
+    for g in range(hq):
+        h = g // 4
+        assert np.all(out[0, g] <= V2[0, h].max(axis=0) + 1e-12)
+        assert np.all(out[0, g] >= V2[0, h].min(axis=0) - 1e-12)
+
+
+def test_keys_rebuilt_from_low_rank_factors_at_original_positions():
+    """With true rank <= r the rebuilt keys are exact, so a budget equal to all
+    selectable chunks reproduces dense attention even at r < h_kv*d; moving a
+    key to a wrong position would break it."""
+    rng = np.random.default_rng(13)
+    b, hq, hkv, d, s, c, o, w = 1, 4, 2, 16, 96, 8, 1, 16
+    n = s // c
+    R = 5
+    M = rng.standard_normal((s, R)) @ rng.standard_normal((R, hkv * d))
+    K = M.reshape(s, hkv, d).transpose(1, 0, 2)[None].astype(np.float32).astype(np.float64)
+    V = rng.standard_normal((b, hkv, s, d))
+    shape = Shape(b=b, h_q=hq, h_kv=hkv, d=d, s=s, c=c, r=8, o=o, k=n - o - w // c, w=w, bf16=False)
+    q = rng.standard_normal((b, hq, d)) * 0.3
+    meta, A, B = _meta_and_factors(shape, K, V)
+    res = oracle.decode(shape, q, meta, A, B, V)
+    Kr = rope_complex(K, np.arange(s)[None, None, :])
+    for g in range(hq):
+        ref = dense_attention(q[0, g], Kr[0, g // 2], V[0, g // 2])
+        np.testing.assert_allclose(res["out"][0, g], ref, atol=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# The set-difference cache
+# ---------------------------------------------------------------------------
+def test_cache_simulation_counts_set_intersections():
+    rng = np.random.default_rng(14)
+    sim = oracle.CacheSim(2, 3)
+    prev = None
+    for t in range(6):
+        sel = np.stack([np.stack([np.sort(rng.choice(40, 7, replace=False)) for _ in range(3)]) for _ in range(2)])
+        hits, misses = sim.step(sel)
+        if prev is None:
+            assert hits == 0 and misses == 2 * 3 * 7
+        else:
+            brute = sum(len(np.intersect1d(sel[bi, h], prev[bi, h])) for bi in range(2) for h in range(3))
+            assert hits == brute and misses == 2 * 3 * 7 - brute
+        prev = sel
+    sim.reset()
+    assert sim.step(prev) == (0, 2 * 3 * 7)
