@@ -1,0 +1,229 @@
+/*
+ * shadowkv.h -- C ABI of the MI355X (gfx950) ShadowKV sparse decode step.
+ *
+ * The method is the one described on the review page "ShadowKV: KV Cache in
+ * Shadows for High-Throughput Long-Context LLM Inference" (xllm-io
+ * paper-review blog), section 三 技术架构: Algorithm 1 (Pre-filling) builds
+ * per-layer metadata once; Algorithm 2 (Decoding) runs per layer and per
+ * generated token.  The per-layer cache that loads only the set difference
+ * between consecutive steps follows the Telegram write-up "Ускорение
+ * E2E-инференса через оптимизацию KV-кэша. Часть II".
+ *
+ * Conventions for every entry point
+ *   - Tensors are dense and row-major with the shapes given below; their
+ *     element type is the layer's `dtype` (binary32 or bfloat16) unless an
+ *     integer type is named.  "device" pointers are HIP device memory of the
+ *     GPU that was current when the layer was created; "pinned host" pointers
+ *     come from shadowkv_host_alloc (or hipHostMalloc).
+ *   - `stream` is a hipStream_t passed as void* (NULL: the null stream).
+ *     Calls enqueue work on it and return without waiting unless noted.
+ *   - Return value: SKV_OK (0) or a negative SKV_E_* code; the message is in
+ *     shadowkv_last_error() (per calling thread).  On a shape/argument error
+ *     nothing is enqueued and the layer is unchanged.
+ *   - A layer handle is not thread-safe; different layers may be used from
+ *     different threads and streams.
+ *
+ * Ownership: the caller owns every pointer it passes.  Device inputs are
+ * read only by the work enqueued by the call (keep them alive until that
+ * work has run).  The pinned host V buffer is borrowed for the layer's
+ * lifetime.  The library owns its copies of A and B, the landmarks, the
+ * outlier and local buffers, the resident V cache with its slot map, all
+ * scratch, and one extra HIP stream plus events per layer.
+ */
+#ifndef SHADOWKV_H
+#define SHADOWKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+enum { SKV_F32 = 0, SKV_BF16 = 1 };
+
+/* Status codes. */
+enum {
+    SKV_OK = 0,
+    SKV_E_INVAL = -1,  /* null pointer, bad dtype, host buffer not pinned   */
+    SKV_E_SHAPE = -2,  /* sizes violate the constraints listed below        */
+    SKV_E_STATE = -3,  /* decode before prefill/load                        */
+    SKV_E_NOMEM = -4,  /* device or pinned-host allocation failed           */
+    SKV_E_HIP = -5     /* a HIP runtime call failed (text in last_error)    */
+};
+
+/*
+ * Layer sizes (Algorithm 1's input list plus the key-parameter table of
+ * section 三: chunk 8, rank 160, 48 outlier chunks, budget 1.56 %).
+ * Constraints (SKV_E_SHAPE otherwise):
+ *   batch >= 1; heads_kv >= 1; heads_q a multiple of heads_kv with
+ *   group = heads_q / heads_kv <= 16; head_dim in {64, 128};
+ *   1 <= chunk <= 64 and seq_len a positive multiple of chunk;
+ *   local_window a multiple of chunk, 0 <= local_window <= seq_len;
+ *   n = seq_len / chunk, n_loc = local_window / chunk;
+ *   0 <= n_outlier <= n - n_loc; 0 <= top_k <= n - n_loc - n_outlier and
+ *   top_k <= 4096; at least one attended key; 1 <= rank <= 256;
+ *   rope_base > 0.
+ */
+typedef struct {
+    int32_t batch;         /* b: sequences decoded together                  */
+    int32_t heads_q;       /* h_q: query heads                               */
+    int32_t heads_kv;      /* h_kv: key/value heads (GQA: q head g -> g/group)*/
+    int32_t head_dim;      /* d                                              */
+    int32_t seq_len;       /* s: context tokens held by the layer            */
+    int32_t chunk;         /* c: tokens per chunk (landmark granularity)     */
+    int32_t rank;          /* r: rank of the pre-RoPE key factors            */
+    int32_t n_outlier;     /* o: outlier chunks kept at full rank on the GPU */
+    int32_t top_k;         /* k: chunks selected per (sequence, KV head)     */
+    int32_t local_window;  /* w: last tokens always attended (dense)         */
+    float rope_base;       /* RoPE base (theta_i = base^(-2i/d))             */
+    int32_t dtype;         /* SKV_F32 or SKV_BF16                            */
+} skv_config;
+
+typedef struct skv_layer skv_layer;
+
+/* Counters accumulated by the decode steps since creation or the last
+ * shadowkv_reset_stats.  hits/misses count chunks per (sequence, KV head);
+ * bytes_h2d is the V payload read from pinned host memory. */
+typedef struct {
+    int64_t steps;
+    int64_t hits;
+    int64_t misses;
+    int64_t bytes_h2d;
+} skv_stats;
+
+/* Create a layer: validates `cfg` and allocates every device buffer the
+ * layer will use (nothing is allocated later).  *out receives the handle. */
+int shadowkv_layer_create(const skv_config *cfg, skv_layer **out);
+
+/* Release the layer's memory, stream and events (synchronizes its streams). */
+void shadowkv_layer_destroy(skv_layer *layer);
+
+/*
+ * Algorithm 1 (Pre-filling), steps 2-5, on the device.  Step 1's factors are
+ * inputs: the review page places the SVD of the pre-RoPE keys in prefill and
+ * the build computes it once on the host side, outside this library.
+ *   k_pre       device (b, h_kv, s, d)  pre-RoPE keys.
+ *   k_rope      device (b, h_kv, s, d)  post-RoPE keys, or NULL: then they
+ *               are computed here from k_pre (rotate-half RoPE, 0-based
+ *               positions, angle reduced in double precision) and rounded
+ *               to dtype.
+ *   v           device (b, h_kv, s, d)  values.
+ *   A           device (b, s, r)        left factor, shared by the KV heads.
+ *   B           device (b, h_kv, r, d)  right factor per KV head;
+ *               A[b] . B[b,h] approximates head h's pre-RoPE keys.
+ *   v_host      pinned host (b, h_kv, s, d): receives V (the offload of
+ *               step 5); must stay allocated while the layer is used.
+ * Computes the chunk means of the post-RoPE keys (landmarks), each chunk's
+ * minimum cosine to its landmark, the n_outlier chunks with the lowest
+ * minimum (ties: lower index; chunks of the local window excluded), gathers
+ * the full-rank post-RoPE K and V of outlier chunks and of the last
+ * local_window tokens, marks the remaining chunks selectable, copies V to
+ * v_host and empties the resident V cache.
+ */
+int shadowkv_prefill_meta(skv_layer *layer, const void *k_pre, const void *k_rope,
+                          const void *v, const void *A, const void *B,
+                          void *v_host, void *stream);
+
+/*
+ * Install precomputed prefill metadata instead of computing it (resume from
+ * saved metadata).  All device pointers except v_host (pinned host, already
+ * holding V of shape (b, h_kv, s, d)):
+ *   landmarks (b, h_kv, n, d); outliers int32 (b, h_kv, o), each row
+ *   strictly ascending, values in [0, n - n_loc); k_out, v_out
+ *   (b, h_kv, o*c, d) post-RoPE; k_loc, v_loc (b, h_kv, w, d) post-RoPE;
+ *   A (b, s, r); B (b, h_kv, r, d).
+ * Also empties the resident V cache.
+ */
+int shadowkv_load_meta(skv_layer *layer, const void *landmarks, const int32_t *outliers,
+                       const void *k_out, const void *v_out, const void *k_loc,
+                       const void *v_loc, const void *A, const void *B,
+                       void *v_host, void *stream);
+
+/*
+ * Algorithm 2 (Decoding): one step of one layer for all b sequences.
+ *   q    device (b, h_q, d)  post-RoPE queries.
+ *   out  device (b, h_q, d)  attention output.
+ * Steps: P = q . L^T / sqrt(d) over selectable chunks; the group score S2
+ * (each head's softmax over selectable chunks, averaged over the heads of a
+ * KV group -- the page leaves S2 undefined, this is the reading taken);
+ * I = ArgTopK(S2, k) per (sequence, KV head) with ties to the lower index;
+ * the set difference against the previous step's resident chunks; V of the
+ * missing chunks read from v_host on the layer's second stream while the
+ * selected keys are rebuilt as Gather(A, I) . B and rotated at their
+ * original positions; softmax attention over
+ * [outlier keys; rebuilt keys; local-window keys] with the matching values.
+ * Enqueued on `stream`; `out` is valid once `stream` has reached this point.
+ * SKV_E_STATE before prefill_meta / load_meta.
+ */
+int shadowkv_decode_step(skv_layer *layer, const void *q, void *out, void *stream);
+
+/* Empty the resident V cache (all later chunks load again).  The cache is
+ * lossless, so outputs do not change; only the hit counts do. */
+int shadowkv_reset_cache(skv_layer *layer, void *stream);
+
+/* Read the counters (synchronizes the layer's streams). */
+int shadowkv_get_stats(skv_layer *layer, skv_stats *out);
+int shadowkv_reset_stats(skv_layer *layer);
+
+/* Debug / test access to the layer's device state.  shadowkv_read copies
+ * tensor `which` into dst (device or host memory, `bytes` must equal
+ * shadowkv_tensor_bytes) ordered on `stream`. */
+enum {
+    SKV_T_LANDMARKS = 0,    /* dtype (b, h_kv, n, d)                          */
+    SKV_T_MIN_COS = 1,      /* f32 (b, h_kv, n): prefill cosine minimum       */
+    SKV_T_OUTLIERS = 2,     /* int32 (b, h_kv, o), ascending                  */
+    SKV_T_CAND_MASK = 3,    /* uint32 (b, h_kv, ceil(n/32)): selectable bits  */
+    SKV_T_SCORES = 4,       /* f32 (b, h_q, n): last step's P, -inf masked    */
+    SKV_T_GROUP_SCORES = 5, /* f32 (b, h_kv, n): last step's S2, 0 masked     */
+    SKV_T_SELECTION = 6,    /* int32 (b, h_kv, k): last step's I, ascending   */
+    SKV_T_SLOT_CHUNKS = 7,  /* int32 (b, h_kv, k): chunk held by each slot    */
+    SKV_T_CACHE_V = 8,      /* dtype (b, h_kv, k*c, d): resident V by slot    */
+    SKV_T_K_OUT = 9,        /* dtype (b, h_kv, o*c, d)                        */
+    SKV_T_V_OUT = 10,
+    SKV_T_K_LOC = 11,       /* dtype (b, h_kv, w, d)                          */
+    SKV_T_V_LOC = 12,
+    SKV_T_COUNT = 13
+};
+size_t shadowkv_tensor_bytes(const skv_layer *layer, int which);
+int shadowkv_read(skv_layer *layer, int which, void *dst, size_t bytes, void *stream);
+
+/* Per-kernel timing with HIP events recorded on the stream each kernel runs
+ * on.  While enabled, every decode step records a start/stop pair around
+ * each kernel.  shadowkv_get_timing synchronizes, writes the summed
+ * milliseconds of each kernel (SKV_K_COUNT entries) and the number of steps
+ * they cover, and clears the record. */
+enum {
+    SKV_K_SCORE = 0,    /* landmark scores + per-tile softmax partials      */
+    SKV_K_GROUP = 1,    /* group score S2                                   */
+    SKV_K_TOPK = 2,     /* ArgTopK                                          */
+    SKV_K_SETDIFF = 3,  /* set difference, slot assignment                  */
+    SKV_K_FETCH = 4,    /* V of missing chunks from pinned host (2nd stream)*/
+    SKV_K_QK = 5,       /* key rebuild + RoPE + logits (all key blocks)     */
+    SKV_K_PV = 6,       /* probabilities times values, split partials       */
+    SKV_K_COMBINE = 7,  /* merge of split partials into out                 */
+    SKV_K_COUNT = 8
+};
+int shadowkv_set_timing(skv_layer *layer, int enable);
+int shadowkv_get_timing(skv_layer *layer, double *ms_out, int64_t *steps_out);
+
+/* Pinned host memory that the device can read directly. */
+int shadowkv_host_alloc(size_t bytes, void **out);
+int shadowkv_host_free(void *ptr);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char *shadowkv_last_error(void);
+
+/* Equivalent bandwidth of section 三's 核心公式:
+ *   B~ = 2 S B_gpu / (S/C + 2 (K + O) C + (1 - alpha) K C B_gpu / B_pcie)
+ * S tokens, C chunk size, K selected and O outlier chunks, alpha the cache
+ * hit rate; the result has the unit of b_gpu. */
+double shadowkv_equiv_bandwidth(double S, double C, double K, double O, double alpha,
+                                double b_gpu, double b_pcie);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SHADOWKV_H */

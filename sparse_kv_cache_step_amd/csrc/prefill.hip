@@ -1,0 +1,359 @@
+// Prefill-side kernels of the ShadowKV step (review page, section 三,
+// Algorithm 1 steps 2-5): RoPE of the pre-RoPE keys, chunk means
+// (landmarks), each chunk's minimum token-to-landmark cosine, the static
+// outlier / local-window buffers and the selectable-chunk bitmask.
+#include "skv_device.h"
+
+namespace skv {
+
+// Post-RoPE key pair (i, i + d/2) of one token, computed in double precision
+// (angle, sin/cos, rotation) and rounded once to the storage type.  Prefill is
+// off the decode path, so it affords the exact arithmetic: the stored keys and
+// landmarks equal the correctly rounded values.
+template <typename T>
+__device__ __forceinline__ void rope_store_pair(const T *k_pre, const T *k_rope, size_t off, int i, int half,
+                                                int pos, double theta, float &y1, float &y2) {
+    if (k_rope) {
+        y1 = Elem<T>::ld(k_rope, off + i);
+        y2 = Elem<T>::ld(k_rope, off + i + half);
+        return;
+    }
+    double sn, cs;
+    sincos(static_cast<double>(pos) * theta, &sn, &cs);
+    const double x1 = Elem<T>::ld(k_pre, off + i), x2 = Elem<T>::ld(k_pre, off + i + half);
+    y1 = Elem<T>::rnd_d(x1 * cs - x2 * sn);
+    y2 = Elem<T>::rnd_d(x2 * cs + x1 * sn);
+}
+
+// One wave per chunk.  Lane i < d/2 owns the RoPE pair (i, i + d/2).  The
+// chunk mean is accumulated in double and rounded once; the cosines use the
+// stored (rounded) keys and landmark and are accumulated in double.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void landmarks_kernel(const T *__restrict__ k_pre,
+                                                        const T *__restrict__ k_rope,
+                                                        const double *__restrict__ theta,
+                                                        T *__restrict__ landmarks,
+                                                        float *__restrict__ min_cos, int n, int c, int s) {
+    extern __shared__ float ys[];  // [4 waves][c][D] stored post-RoPE keys
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int bh = blockIdx.y;
+    const int j = blockIdx.x * 4 + wave;
+    if (j >= n) return;  // whole wave leaves together; no block barrier below
+    constexpr int H = D / 2;
+    const bool act = lane < H;
+    float *y = ys + static_cast<size_t>(wave) * c * D;
+    const size_t base = (static_cast<size_t>(bh) * s + static_cast<size_t>(j) * c) * D;
+    double sum1 = 0.0, sum2 = 0.0;
+    for (int t = 0; t < c; ++t) {
+        float y1 = 0.f, y2 = 0.f;
+        if (act) {
+            rope_store_pair<T>(k_pre, k_rope, base + static_cast<size_t>(t) * D, lane, H, j * c + t, theta[lane], y1, y2);
+            y[t * D + lane] = y1;
+            y[t * D + lane + H] = y2;
+        }
+        sum1 += y1;
+        sum2 += y2;
+    }
+    double l1 = act ? Elem<T>::rnd_d(sum1 / c) : 0.0;
+    double l2 = act ? Elem<T>::rnd_d(sum2 / c) : 0.0;
+    if (act) {
+        const size_t lo = (static_cast<size_t>(bh) * n + j) * D;
+        Elem<T>::st(landmarks, lo + lane, static_cast<float>(l1));
+        Elem<T>::st(landmarks, lo + lane + H, static_cast<float>(l2));
+    }
+    const double lnorm = sqrt(wave_sum_d(l1 * l1 + l2 * l2));
+    double mn = INFINITY;
+    for (int t = 0; t < c; ++t) {
+        const double y1 = act ? y[t * D + lane] : 0.0;
+        const double y2 = act ? y[t * D + lane + H] : 0.0;
+        const double dot = wave_sum_d(y1 * l1 + y2 * l2);
+        const double den = sqrt(wave_sum_d(y1 * y1 + y2 * y2)) * lnorm;
+        mn = fmin(mn, dot / (den > 1e-12 ? den : 1e-12));
+    }
+    if (lane == 0) min_cos[static_cast<size_t>(bh) * n + j] = static_cast<float>(mn);
+}
+
+// Radix select of the k largest keys per row, exact ties to the lower index,
+// written in ascending index order.  key(j) = float_key(sign * vals[j]) for
+// valid entries (j < n_valid_prefix and, if a mask is given, its bit set),
+// 0 otherwise.  Four 8-bit passes over keys held in LDS (or in global scratch
+// when a row does not fit), then an ordered compaction.
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restrict__ vals, int n,
+                                                            int n_valid_prefix,
+                                                            const uint32_t *__restrict__ mask,
+                                                            int mask_words, float sign, int k,
+                                                            int32_t *__restrict__ out,
+                                                            uint32_t *__restrict__ gscratch, int use_lds) {
+    extern __shared__ uint32_t lds_keys[];
+    __shared__ uint32_t hist[256];
+    __shared__ int wcnt[kTopkThreads / 64];
+    __shared__ uint32_t s_digit;
+    __shared__ int s_above;
+    const int row = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (k <= 0) return;
+    uint32_t *keys = use_lds ? lds_keys : gscratch + static_cast<size_t>(row) * n;
+    const float *rv = vals + static_cast<size_t>(row) * n;
+    const uint32_t *rm = mask ? mask + static_cast<size_t>(row) * mask_words : nullptr;
+    for (int j = tid; j < n; j += kTopkThreads) {
+        bool valid = j < n_valid_prefix && (!rm || mask_bit(rm, j));
+        keys[j] = valid ? float_key(sign * rv[j]) : 0u;
+    }
+    __syncthreads();
+
+    uint32_t prefix = 0, pmask = 0;
+    int krem = k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0;
+        __syncthreads();
+        for (int j = tid; j < n; j += kTopkThreads) {
+            uint32_t key = keys[j];
+            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // lane covers bins 255-4*lane .. 252-4*lane, scanned from the top
+            int cnt[4], local = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { cnt[i] = static_cast<int>(hist[255 - (lane * 4 + i)]); local += cnt[i]; }
+            int incl = local;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                int t = __shfl_up(incl, off, 64);
+                if (lane >= off) incl += t;
+            }
+            int excl = incl - local;
+            if (excl < krem && krem <= incl) {
+                int acc = excl;
+                for (int i = 0; i < 4; ++i) {
+                    if (acc + cnt[i] >= krem) { s_digit = 255u - (lane * 4 + i); s_above = acc; break; }
+                    acc += cnt[i];
+                }
+            }
+        }
+        __syncthreads();
+        prefix |= s_digit << shift;
+        pmask |= 255u << shift;
+        krem -= s_above;
+        __syncthreads();
+    }
+    const uint32_t thr = prefix;
+    const int need_eq = krem;  // keys equal to thr to take, lowest index first
+
+    int written = 0, eq_seen = 0;
+    int32_t *ro = out + static_cast<size_t>(row) * k;
+    for (int j0 = 0; j0 < n && written < k; j0 += kTopkThreads) {
+        const int j = j0 + tid;
+        const uint32_t key = j < n ? keys[j] : 0u;
+        const bool gt = j < n && key > thr;
+        const bool eq = j < n && key == thr;
+        int eq_tot, take_tot;
+        const int eq_pre = block_excl_count(eq, wcnt, &eq_tot);
+        const bool take = gt || (eq && eq_seen + eq_pre < need_eq);
+        const int pos = block_excl_count(take, wcnt, &take_tot);
+        if (take && written + pos < k) ro[written + pos] = j;
+        written += take_tot;
+        eq_seen += eq_tot;
+    }
+}
+
+// Gather the full-rank post-RoPE K and the V of every outlier chunk and of
+// the last w tokens.  One wave per token row; RoPE is recomputed with the
+// same arithmetic as landmarks_kernel, so the stored keys are identical to
+// the ones the landmarks were built from.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void gather_static_kernel(const T *__restrict__ k_pre,
+                                                            const T *__restrict__ k_rope,
+                                                            const T *__restrict__ v,
+                                                            const int32_t *__restrict__ outliers,
+                                                            const double *__restrict__ theta,
+                                                            T *__restrict__ k_out, T *__restrict__ v_out,
+                                                            T *__restrict__ k_loc, T *__restrict__ v_loc,
+                                                            int s, int c, int o, int w) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int bh = blockIdx.y;
+    const int rr = blockIdx.x * 4 + wave;
+    const int OC = o * c;
+    if (rr >= OC + w) return;
+    int pos;
+    T *kd, *vd;
+    size_t drow;
+    if (rr < OC) {
+        pos = outliers[static_cast<size_t>(bh) * o + rr / c] * c + rr % c;
+        kd = k_out; vd = v_out; drow = static_cast<size_t>(bh) * OC + rr;
+    } else {
+        pos = s - w + (rr - OC);
+        kd = k_loc; vd = v_loc; drow = static_cast<size_t>(bh) * w + (rr - OC);
+    }
+    constexpr int H = D / 2;
+    const size_t src = (static_cast<size_t>(bh) * s + pos) * D;
+    const size_t dst = drow * D;
+    if (lane < H) {
+        float y1, y2;
+        rope_store_pair<T>(k_pre, k_rope, src, lane, H, pos, theta[lane], y1, y2);
+        Elem<T>::st(kd, dst + lane, y1);
+        Elem<T>::st(kd, dst + lane + H, y2);
+        vd[dst + lane] = v[src + lane];
+        vd[dst + lane + H] = v[src + lane + H];
+    }
+}
+
+// Selectable chunks: outside the local window and not outliers.
+__global__ void cand_mask_kernel(const int32_t *__restrict__ outliers, uint32_t *__restrict__ cand, int n,
+                                 int n_loc, int o, int mask_words) {
+    const int bh = blockIdx.y;
+    const int wi = blockIdx.x * blockDim.x + threadIdx.x;
+    if (wi >= mask_words) return;
+    const int32_t *ol = outliers + static_cast<size_t>(bh) * o;
+    uint32_t bits = 0;
+    for (int bit = 0; bit < 32; ++bit) {
+        const int j = wi * 32 + bit;
+        if (j >= n - n_loc) break;
+        int lo = 0, hi = o;  // binary search in the ascending outlier list
+        while (lo < hi) {
+            int mid = (lo + hi) >> 1;
+            if (ol[mid] < j) lo = mid + 1; else hi = mid;
+        }
+        if (!(lo < o && ol[lo] == j)) bits |= 1u << bit;
+    }
+    cand[static_cast<size_t>(bh) * mask_words + wi] = bits;
+}
+
+// Outlier rows supplied by a caller must be strictly ascending and lie in
+// [0, n - n_loc); counts offending rows.
+__global__ void validate_outliers_kernel(const int32_t *__restrict__ outliers, int rows, int o, int limit,
+                                         int32_t *__restrict__ bad) {
+    const int row = blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= rows) return;
+    const int32_t *ol = outliers + static_cast<size_t>(row) * o;
+    bool ok = true;
+    for (int a = 0; a < o; ++a) {
+        ok = ok && ol[a] >= 0 && ol[a] < limit && (a == 0 || ol[a] > ol[a - 1]);
+    }
+    if (!ok) atomicAdd(bad, 1);
+}
+
+// Bt[b,h][i][e] = B[b,h][e][i]: the right factor stored column-major per head
+// so a rank slice of one output column is contiguous.
+template <typename T>
+__global__ void transpose_b_kernel(const T *__restrict__ B, T *__restrict__ Bt, int r, int d) {
+    const int bh = blockIdx.y;
+    const size_t off = static_cast<size_t>(bh) * r * d;
+    for (int idx = blockIdx.x * blockDim.x + threadIdx.x; idx < r * d; idx += gridDim.x * blockDim.x) {
+        const int e = idx / d, i = idx % d;
+        Bt[off + static_cast<size_t>(i) * r + e] = B[off + idx];
+    }
+}
+
+__global__ void fill_i32_kernel(int32_t *p, int32_t value, size_t count) {
+    for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < count;
+         i += static_cast<size_t>(gridDim.x) * blockDim.x)
+        p[i] = value;
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+static hipError_t allow_lds(const void *fn, size_t bytes) {
+    if (bytes <= 64 * 1024) return hipSuccess;
+    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
+}
+
+template <typename T, int D>
+static hipError_t landmarks_t(const Dims &dm, const void *k_pre, const void *k_rope, const double *theta,
+                              void *landmarks, float *min_cos, hipStream_t st) {
+    dim3 grid((dm.n + 3) / 4, dm.b * dm.hkv);
+    size_t lds = 4ull * dm.c * D * sizeof(float);
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(landmarks_kernel<T, D>), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((landmarks_kernel<T, D>), grid, dim3(256), lds, st, static_cast<const T *>(k_pre),
+                       static_cast<const T *>(k_rope), theta, static_cast<T *>(landmarks), min_cos, dm.n, dm.c,
+                       dm.s);
+    return hipGetLastError();
+}
+
+hipError_t launch_landmarks(const Dims &dm, const void *k_pre, const void *k_rope, const double *theta,
+                            void *landmarks, float *min_cos, hipStream_t st) {
+    if (dm.bf16) {
+        return dm.d == 128 ? landmarks_t<uint16_t, 128>(dm, k_pre, k_rope, theta, landmarks, min_cos, st)
+                           : landmarks_t<uint16_t, 64>(dm, k_pre, k_rope, theta, landmarks, min_cos, st);
+    }
+    return dm.d == 128 ? landmarks_t<float, 128>(dm, k_pre, k_rope, theta, landmarks, min_cos, st)
+                       : landmarks_t<float, 64>(dm, k_pre, k_rope, theta, landmarks, min_cos, st);
+}
+
+hipError_t launch_topk(const Dims &dm, const float *vals, int rows, int n, int n_valid_prefix,
+                       const uint32_t *mask, float sign, int k, int32_t *out, uint32_t *gscratch,
+                       int lds_limit, hipStream_t st) {
+    (void)dm;
+    if (k <= 0 || rows <= 0) return hipSuccess;
+    const size_t need = static_cast<size_t>(n) * sizeof(uint32_t);
+    const int use_lds = need <= static_cast<size_t>(lds_limit) ? 1 : 0;
+    const size_t lds = use_lds ? need : 0;
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(topk_kernel), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kTopkThreads), lds, st, vals, n, n_valid_prefix, mask,
+                       (n + 31) / 32, sign, k, out, gscratch, use_lds);
+    return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t gather_t(const Dims &dm, const void *k_pre, const void *k_rope, const void *v,
+                           const int32_t *outliers, const double *theta, void *k_out, void *v_out, void *k_loc,
+                           void *v_loc, hipStream_t st) {
+    const int rows = dm.OC + dm.w;
+    if (rows == 0) return hipSuccess;
+    dim3 grid((rows + 3) / 4, dm.b * dm.hkv);
+    hipLaunchKernelGGL((gather_static_kernel<T, D>), grid, dim3(256), 0, st, static_cast<const T *>(k_pre),
+                       static_cast<const T *>(k_rope), static_cast<const T *>(v), outliers, theta,
+                       static_cast<T *>(k_out), static_cast<T *>(v_out), static_cast<T *>(k_loc),
+                       static_cast<T *>(v_loc), dm.s, dm.c, dm.o, dm.w);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_static(const Dims &dm, const void *k_pre, const void *k_rope, const void *v,
+                                const int32_t *outliers, const double *theta, void *k_out, void *v_out,
+                                void *k_loc, void *v_loc, hipStream_t st) {
+    if (dm.bf16) {
+        return dm.d == 128
+                   ? gather_t<uint16_t, 128>(dm, k_pre, k_rope, v, outliers, theta, k_out, v_out, k_loc, v_loc, st)
+                   : gather_t<uint16_t, 64>(dm, k_pre, k_rope, v, outliers, theta, k_out, v_out, k_loc, v_loc, st);
+    }
+    return dm.d == 128 ? gather_t<float, 128>(dm, k_pre, k_rope, v, outliers, theta, k_out, v_out, k_loc, v_loc, st)
+                       : gather_t<float, 64>(dm, k_pre, k_rope, v, outliers, theta, k_out, v_out, k_loc, v_loc, st);
+}
+
+hipError_t launch_cand_mask(const Dims &dm, const int32_t *outliers, uint32_t *cand, hipStream_t st) {
+    dim3 grid((dm.mask_words + 255) / 256, dm.b * dm.hkv);
+    hipLaunchKernelGGL(cand_mask_kernel, grid, dim3(256), 0, st, outliers, cand, dm.n, dm.n_loc, dm.o,
+                       dm.mask_words);
+    return hipGetLastError();
+}
+
+hipError_t launch_validate_outliers(const Dims &dm, const int32_t *outliers, int32_t *bad, hipStream_t st) {
+    const int rows = dm.b * dm.hkv;
+    hipLaunchKernelGGL(validate_outliers_kernel, dim3((rows + 255) / 256), dim3(256), 0, st, outliers, rows,
+                       dm.o, dm.n - dm.n_loc, bad);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_b(const Dims &dm, const void *B, void *Bt, hipStream_t st) {
+    dim3 grid((dm.r * dm.d + 255) / 256, dm.b * dm.hkv);
+    if (dm.bf16)
+        hipLaunchKernelGGL(transpose_b_kernel<uint16_t>, grid, dim3(256), 0, st,
+                           static_cast<const uint16_t *>(B), static_cast<uint16_t *>(Bt), dm.r, dm.d);
+    else
+        hipLaunchKernelGGL(transpose_b_kernel<float>, grid, dim3(256), 0, st, static_cast<const float *>(B),
+                           static_cast<float *>(Bt), dm.r, dm.d);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t *p, int32_t value, size_t count, hipStream_t st) {
+    if (count == 0) return hipSuccess;
+    size_t blocks = (count + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, p, value, count);
+    return hipGetLastError();
+}
+
+}  // namespace skv

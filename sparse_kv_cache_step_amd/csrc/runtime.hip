@@ -1,0 +1,515 @@
+// Host runtime and C ABI of the ShadowKV decode step (declared in
+// include/shadowkv.h): per-layer device state, argument validation, the
+// two-stream schedule of one decode step, counters and per-kernel timing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "shadowkv.h"
+#include "skv_dims.h"
+
+using skv::Dims;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string &msg) {
+    g_last_error = msg;
+    return code;
+}
+
+#define SKV_HIP(expr)                                                                          \
+    do {                                                                                       \
+        hipError_t e_ = (expr);                                                                \
+        if (e_ != hipSuccess) return fail(SKV_E_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+    } while (0)
+
+int round_up(int x, int m) { return (x + m - 1) / m * m; }
+
+// Validates a configuration and derives the sizes the kernels use.
+int make_dims(const skv_config &c, Dims *dm, std::string *why) {
+    auto bad = [&](const char *m) { *why = m; return SKV_E_SHAPE; };
+    if (c.dtype != SKV_F32 && c.dtype != SKV_BF16) { *why = "dtype must be SKV_F32 or SKV_BF16"; return SKV_E_INVAL; }
+    if (c.batch < 1 || c.heads_kv < 1) return bad("batch and heads_kv must be >= 1");
+    if (c.heads_q < c.heads_kv || c.heads_q % c.heads_kv) return bad("heads_q must be a multiple of heads_kv");
+    if (c.heads_q / c.heads_kv > skv::kMaxGroup) return bad("heads_q / heads_kv must be <= 16");
+    if (c.head_dim != 64 && c.head_dim != 128) return bad("head_dim must be 64 or 128");
+    if (c.chunk < 1 || c.chunk > 64) return bad("chunk must be in [1, 64]");
+    if (c.seq_len < c.chunk || c.seq_len % c.chunk) return bad("seq_len must be a positive multiple of chunk");
+    if (c.local_window < 0 || c.local_window % c.chunk || c.local_window > c.seq_len)
+        return bad("local_window must be a multiple of chunk in [0, seq_len]");
+    const int n = c.seq_len / c.chunk, n_loc = c.local_window / c.chunk;
+    if (c.n_outlier < 0 || c.n_outlier > n - n_loc) return bad("n_outlier must be in [0, n - n_loc]");
+    if (c.top_k < 0 || c.top_k > n - n_loc - c.n_outlier) return bad("top_k must be in [0, n - n_loc - n_outlier]");
+    if (c.top_k > 4096) return bad("top_k must be <= 4096");
+    if (c.rank < 1 || c.rank > 256) return bad("rank must be in [1, 256]");
+    if (!(c.rope_base > 0.f)) return bad("rope_base must be > 0");
+    const long long nk = 1LL * c.n_outlier * c.chunk + 1LL * c.top_k * c.chunk + c.local_window;
+    if (nk < 1) return bad("at least one key must be attended");
+    const long long seq_elems = 1LL * c.batch * c.heads_kv * c.seq_len * c.head_dim;
+    if (seq_elems >= (1LL << 40)) return bad("tensor too large");
+    Dims &d = *dm;
+    d.b = c.batch; d.hq = c.heads_q; d.hkv = c.heads_kv; d.d = c.head_dim; d.s = c.seq_len; d.c = c.chunk;
+    d.r = c.rank; d.o = c.n_outlier; d.k = c.top_k; d.w = c.local_window;
+    d.n = n; d.n_loc = n_loc; d.G = c.heads_q / c.heads_kv;
+    d.GP = d.G <= 4 ? 4 : (d.G <= 8 ? 8 : 16);
+    d.mask_words = (n + 31) / 32;
+    d.score_tiles = (n + skv::kScoreTile - 1) / skv::kScoreTile;
+    d.OC = c.n_outlier * c.chunk; d.KC = c.top_k * c.chunk; d.NK = static_cast<int>(nk);
+    d.pv_tiles = (d.NK + skv::kPvTile - 1) / skv::kPvTile;
+    d.esize = c.dtype == SKV_BF16 ? 2 : 4;
+    d.bf16 = c.dtype == SKV_BF16;
+    d.r_pad = round_up(c.rank, 32);
+    d.scale = 1.0f / std::sqrt(static_cast<float>(c.head_dim));
+    return SKV_OK;
+}
+
+struct Mark {
+    int kernel;
+    hipEvent_t start, stop;
+};
+
+}  // namespace
+
+struct skv_layer {
+    skv_config cfg{};
+    Dims dm{};
+    int device = 0;
+    int lds_limit = 0;
+    std::vector<void *> allocs;
+    // parameters and metadata
+    void *A = nullptr, *Bt = nullptr, *L = nullptr;
+    void *k_out = nullptr, *v_out = nullptr, *k_loc = nullptr, *v_loc = nullptr;
+    uint32_t *cand = nullptr;
+    int32_t *outliers = nullptr;
+    float *min_cos = nullptr;
+    double *theta = nullptr;
+    float2 *rope_off = nullptr;
+    // resident V cache
+    void *vc = nullptr;
+    int32_t *slot_chunk = nullptr;
+    // per-step scratch
+    int32_t *sel = nullptr;
+    float *P = nullptr, *S2 = nullptr, *logits = nullptr, *part_acc = nullptr;
+    float2 *stats = nullptr, *part_ml = nullptr;
+    int2 *misses = nullptr;
+    int32_t *miss_count = nullptr;
+    unsigned long long *counters = nullptr;  // hits, misses, steps
+    uint32_t *topk_scratch = nullptr;
+    int32_t *bad = nullptr;
+    // host V
+    void *v_host_dev = nullptr;
+    bool ready = false;
+    // second stream for the host-V fetch
+    hipStream_t copy = nullptr;
+    hipEvent_t ev_sel = nullptr, ev_fetch = nullptr;
+    int fetch_blocks = 1;
+    // timing
+    bool timing = false;
+    std::vector<hipEvent_t> ev_pool;
+    size_t ev_used = 0;
+    std::vector<Mark> marks;
+    int64_t timed_steps = 0;
+};
+
+namespace {
+
+int dalloc(skv_layer *ly, size_t bytes, void **p) {
+    if (bytes == 0) bytes = 256;
+    hipError_t e = hipMalloc(p, bytes);
+    if (e != hipSuccess) {
+        *p = nullptr;
+        return fail(SKV_E_NOMEM, std::string("hipMalloc(") + std::to_string(bytes) + "): " + hipGetErrorString(e));
+    }
+    ly->allocs.push_back(*p);
+    return SKV_OK;
+}
+
+template <typename P>
+int dalloc_t(skv_layer *ly, size_t bytes, P **p) {
+    void *v = nullptr;
+    int rc = dalloc(ly, bytes, &v);
+    *p = static_cast<P *>(v);
+    return rc;
+}
+
+void release(skv_layer *ly) {
+    if (ly->copy) (void)hipStreamSynchronize(ly->copy);
+    (void)hipDeviceSynchronize();
+    for (void *p : ly->allocs) (void)hipFree(p);
+    ly->allocs.clear();
+    for (hipEvent_t e : ly->ev_pool) (void)hipEventDestroy(e);
+    ly->ev_pool.clear();
+    if (ly->ev_sel) (void)hipEventDestroy(ly->ev_sel);
+    if (ly->ev_fetch) (void)hipEventDestroy(ly->ev_fetch);
+    if (ly->copy) (void)hipStreamDestroy(ly->copy);
+}
+
+hipEvent_t pool_event(skv_layer *ly) {
+    if (ly->ev_used == ly->ev_pool.size()) {
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        ly->ev_pool.push_back(e);
+    }
+    return ly->ev_pool[ly->ev_used++];
+}
+
+// Brackets one kernel launch with timing events when timing is enabled.
+struct Timed {
+    skv_layer *ly;
+    int kernel;
+    hipStream_t st;
+    hipEvent_t stop = nullptr;
+    Timed(skv_layer *l, int k, hipStream_t s) : ly(l), kernel(k), st(s) {
+        if (!ly->timing) return;
+        hipEvent_t start = pool_event(ly);
+        stop = pool_event(ly);
+        if (!start || !stop) { stop = nullptr; return; }
+        (void)hipEventRecord(start, st);
+        ly->marks.push_back({kernel, start, stop});
+    }
+    ~Timed() {
+        if (stop) (void)hipEventRecord(stop, st);
+    }
+};
+
+int check_pinned(const void *host, void **dev) {
+    if (!host) return fail(SKV_E_INVAL, "v_host is null");
+    hipError_t e = hipHostGetDevicePointer(dev, const_cast<void *>(host), 0);
+    if (e != hipSuccess || !*dev) {
+        (void)hipGetLastError();
+        return fail(SKV_E_INVAL, "v_host is not pinned, device-mapped host memory (use shadowkv_host_alloc)");
+    }
+    return SKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *shadowkv_last_error(void) { return g_last_error.c_str(); }
+
+double shadowkv_equiv_bandwidth(double S, double C, double K, double O, double alpha, double b_gpu, double b_pcie) {
+    return 2.0 * S * b_gpu / (S / C + 2.0 * (K + O) * C + (1.0 - alpha) * K * C * b_gpu / b_pcie);
+}
+
+int shadowkv_host_alloc(size_t bytes, void **out) {
+    if (!out) return fail(SKV_E_INVAL, "out is null");
+    *out = nullptr;
+    hipError_t e = hipHostMalloc(out, bytes ? bytes : 1, hipHostMallocMapped);
+    if (e != hipSuccess) return fail(SKV_E_NOMEM, std::string("hipHostMalloc: ") + hipGetErrorString(e));
+    return SKV_OK;
+}
+
+int shadowkv_host_free(void *ptr) {
+    if (!ptr) return SKV_OK;
+    SKV_HIP(hipHostFree(ptr));
+    return SKV_OK;
+}
+
+int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
+    if (!cfg || !out) return fail(SKV_E_INVAL, "null argument");
+    *out = nullptr;
+    Dims dm{};
+    std::string why;
+    int rc = make_dims(*cfg, &dm, &why);
+    if (rc) return fail(rc, why);
+
+    skv_layer *ly = new skv_layer();
+    ly->cfg = *cfg;
+    ly->dm = dm;
+    auto bail = [&](int code) {
+        std::string msg = g_last_error;
+        release(ly);
+        delete ly;
+        g_last_error = msg;
+        return code;
+    };
+    if (hipGetDevice(&ly->device) != hipSuccess) return bail(fail(SKV_E_HIP, "hipGetDevice failed"));
+    int lds = 0;
+    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, ly->device) != hipSuccess)
+        return bail(fail(SKV_E_HIP, "hipDeviceGetAttribute(MaxSharedMemoryPerBlock) failed"));
+    ly->lds_limit = lds - 8 * 1024;  // room for the select kernel's static LDS
+
+    const size_t B = dm.b, HKV = dm.hkv, HQ = dm.hq, D = dm.d, S = dm.s, E = dm.esize;
+    const size_t bh = B * HKV;
+#define ALLOC(ptr, bytes) \
+    if ((rc = dalloc_t(ly, (bytes), &ly->ptr))) return bail(rc)
+    ALLOC(A, B * S * dm.r * E);
+    ALLOC(Bt, bh * D * dm.r * E);
+    ALLOC(L, bh * dm.n * D * E);
+    ALLOC(cand, bh * dm.mask_words * 4);
+    ALLOC(outliers, bh * dm.o * 4);
+    ALLOC(min_cos, bh * dm.n * 4);
+    ALLOC(k_out, bh * dm.OC * D * E);
+    ALLOC(v_out, bh * dm.OC * D * E);
+    ALLOC(k_loc, bh * dm.w * D * E);
+    ALLOC(v_loc, bh * dm.w * D * E);
+    ALLOC(vc, bh * dm.KC * D * E);
+    ALLOC(slot_chunk, bh * dm.k * 4);
+    ALLOC(sel, bh * dm.k * 4);
+    ALLOC(P, B * HQ * dm.n * 4);
+    ALLOC(stats, B * HQ * dm.score_tiles * sizeof(float2));
+    ALLOC(S2, bh * dm.n * 4);
+    ALLOC(misses, bh * dm.k * sizeof(int2));
+    ALLOC(miss_count, bh * 4);
+    ALLOC(logits, B * HQ * dm.NK * 4);
+    ALLOC(part_ml, B * HQ * dm.pv_tiles * sizeof(float2));
+    ALLOC(part_acc, B * HQ * dm.pv_tiles * D * 4);
+    ALLOC(counters, 4 * sizeof(unsigned long long));
+    ALLOC(bad, 4);
+    ALLOC(theta, D / 2 * sizeof(double));
+    ALLOC(rope_off, static_cast<size_t>(dm.c) * D / 2 * sizeof(float2));
+    if (static_cast<size_t>(dm.n) * 4 > static_cast<size_t>(ly->lds_limit)) ALLOC(topk_scratch, bh * dm.n * 4);
+#undef ALLOC
+
+    // RoPE tables: theta_i = base^(-2i/d) in double, and the in-chunk offsets
+    // (cos t*theta_i, sin t*theta_i) for t < chunk.
+    std::vector<double> th(D / 2);
+    std::vector<float2> off(static_cast<size_t>(dm.c) * D / 2);
+    for (size_t i = 0; i < D / 2; ++i) th[i] = std::pow(static_cast<double>(cfg->rope_base), -2.0 * i / D);
+    for (int t = 0; t < dm.c; ++t)
+        for (size_t i = 0; i < D / 2; ++i)
+            off[t * D / 2 + i] = make_float2(static_cast<float>(std::cos(t * th[i])), static_cast<float>(std::sin(t * th[i])));
+    if (hipMemcpy(ly->theta, th.data(), th.size() * sizeof(double), hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(ly->rope_off, off.data(), off.size() * sizeof(float2), hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemset(ly->counters, 0, 4 * sizeof(unsigned long long)) != hipSuccess)
+        return bail(fail(SKV_E_HIP, "initialising layer tables failed"));
+    if (hipStreamCreateWithFlags(&ly->copy, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ly->ev_sel, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ly->ev_fetch, hipEventDisableTiming) != hipSuccess)
+        return bail(fail(SKV_E_HIP, "creating the fetch stream or events failed"));
+
+    // Fetch grid: about 4096 waves across all (sequence, KV head) rows.
+    const int rows = static_cast<int>(bh);
+    int per_row = 1024 / rows;
+    if (per_row < 1) per_row = 1;
+    const int need = (dm.k + 3) / 4;
+    if (per_row > need) per_row = need > 0 ? need : 1;
+    ly->fetch_blocks = per_row;
+
+    *out = ly;
+    return SKV_OK;
+}
+
+void shadowkv_layer_destroy(skv_layer *layer) {
+    if (!layer) return;
+    release(layer);
+    delete layer;
+}
+
+static int install_common(skv_layer *ly, const void *A, const void *B, void *v_host, hipStream_t st) {
+    const Dims &dm = ly->dm;
+    SKV_HIP(hipMemcpyAsync(ly->A, A, static_cast<size_t>(dm.b) * dm.s * dm.r * dm.esize, hipMemcpyDefault, st));
+    SKV_HIP(skv::launch_transpose_b(dm, B, ly->Bt, st));
+    SKV_HIP(skv::launch_cand_mask(dm, ly->outliers, ly->cand, st));
+    SKV_HIP(skv::launch_fill_i32(ly->slot_chunk, -1, static_cast<size_t>(dm.b) * dm.hkv * dm.k, st));
+    (void)v_host;
+    return SKV_OK;
+}
+
+int shadowkv_prefill_meta(skv_layer *ly, const void *k_pre, const void *k_rope, const void *v, const void *A,
+                          const void *B, void *v_host, void *stream) {
+    if (!ly) return fail(SKV_E_INVAL, "layer is null");
+    if ((!k_pre && !k_rope) || !v || !A || !B) return fail(SKV_E_INVAL, "null input pointer");
+    void *vdev = nullptr;
+    int rc = check_pinned(v_host, &vdev);
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Dims &dm = ly->dm;
+    ly->ready = false;
+    SKV_HIP(skv::launch_landmarks(dm, k_pre, k_rope, ly->theta, ly->L, ly->min_cos, st));
+    SKV_HIP(skv::launch_topk(dm, ly->min_cos, dm.b * dm.hkv, dm.n, dm.n - dm.n_loc, nullptr, -1.0f, dm.o,
+                             ly->outliers, ly->topk_scratch, ly->lds_limit, st));
+    SKV_HIP(skv::launch_gather_static(dm, k_pre, k_rope, v, ly->outliers, ly->theta, ly->k_out, ly->v_out,
+                                      ly->k_loc, ly->v_loc, st));
+    if ((rc = install_common(ly, A, B, v_host, st))) return rc;
+    SKV_HIP(hipMemcpyAsync(v_host, v, static_cast<size_t>(dm.b) * dm.hkv * dm.s * dm.d * dm.esize,
+                           hipMemcpyDeviceToHost, st));
+    ly->v_host_dev = vdev;
+    ly->ready = true;
+    return SKV_OK;
+}
+
+int shadowkv_load_meta(skv_layer *ly, const void *landmarks, const int32_t *outliers, const void *k_out,
+                       const void *v_out, const void *k_loc, const void *v_loc, const void *A, const void *B,
+                       void *v_host, void *stream) {
+    if (!ly) return fail(SKV_E_INVAL, "layer is null");
+    const Dims &dm = ly->dm;
+    if (!landmarks || !A || !B || (dm.o > 0 && (!outliers || !k_out || !v_out)) || (dm.w > 0 && (!k_loc || !v_loc)))
+        return fail(SKV_E_INVAL, "null input pointer");
+    void *vdev = nullptr;
+    int rc = check_pinned(v_host, &vdev);
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const size_t bh = static_cast<size_t>(dm.b) * dm.hkv, E = dm.esize, D = dm.d;
+    ly->ready = false;
+    if (dm.o > 0) {
+        SKV_HIP(hipMemcpyAsync(ly->outliers, outliers, bh * dm.o * 4, hipMemcpyDefault, st));
+        SKV_HIP(skv::launch_fill_i32(ly->bad, 0, 1, st));
+        SKV_HIP(skv::launch_validate_outliers(dm, ly->outliers, ly->bad, st));
+        int32_t nbad = 0;
+        SKV_HIP(hipMemcpyAsync(&nbad, ly->bad, 4, hipMemcpyDeviceToHost, st));
+        SKV_HIP(hipStreamSynchronize(st));
+        if (nbad) return fail(SKV_E_SHAPE, "outlier rows must be strictly ascending and lie in [0, n - n_loc)");
+        SKV_HIP(hipMemcpyAsync(ly->k_out, k_out, bh * dm.OC * D * E, hipMemcpyDefault, st));
+        SKV_HIP(hipMemcpyAsync(ly->v_out, v_out, bh * dm.OC * D * E, hipMemcpyDefault, st));
+    }
+    SKV_HIP(hipMemcpyAsync(ly->L, landmarks, bh * dm.n * D * E, hipMemcpyDefault, st));
+    if (dm.w > 0) {
+        SKV_HIP(hipMemcpyAsync(ly->k_loc, k_loc, bh * dm.w * D * E, hipMemcpyDefault, st));
+        SKV_HIP(hipMemcpyAsync(ly->v_loc, v_loc, bh * dm.w * D * E, hipMemcpyDefault, st));
+    }
+    if ((rc = install_common(ly, A, B, v_host, st))) return rc;
+    ly->v_host_dev = vdev;
+    ly->ready = true;
+    return SKV_OK;
+}
+
+int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) {
+    if (!ly) return fail(SKV_E_INVAL, "layer is null");
+    if (!q || !out) return fail(SKV_E_INVAL, "null q or out");
+    if (!ly->ready) return fail(SKV_E_STATE, "decode_step before prefill_meta / load_meta");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const Dims &dm = ly->dm;
+    {
+        Timed t(ly, SKV_K_SCORE, st);
+        SKV_HIP(skv::launch_score(dm, q, ly->L, ly->cand, ly->P, ly->stats, st));
+    }
+    {
+        Timed t(ly, SKV_K_GROUP, st);
+        SKV_HIP(skv::launch_group(dm, ly->P, ly->stats, ly->cand, ly->S2, st));
+    }
+    {
+        Timed t(ly, SKV_K_TOPK, st);
+        SKV_HIP(skv::launch_topk(dm, ly->S2, dm.b * dm.hkv, dm.n, dm.n, ly->cand, 1.0f, dm.k, ly->sel,
+                                 ly->topk_scratch, ly->lds_limit, st));
+    }
+    {
+        Timed t(ly, SKV_K_SETDIFF, st);
+        SKV_HIP(skv::launch_setdiff(dm, ly->sel, ly->slot_chunk, ly->misses, ly->miss_count, ly->counters, st));
+    }
+    // fork: the fetch of missing V runs on the layer's second stream while
+    // the keys are rebuilt and scored on the caller's stream
+    SKV_HIP(hipEventRecord(ly->ev_sel, st));
+    SKV_HIP(hipStreamWaitEvent(ly->copy, ly->ev_sel, 0));
+    {
+        Timed t(ly, SKV_K_FETCH, ly->copy);
+        SKV_HIP(skv::launch_fetch(dm, ly->v_host_dev, ly->vc, ly->misses, ly->miss_count, ly->fetch_blocks, ly->copy));
+    }
+    SKV_HIP(hipEventRecord(ly->ev_fetch, ly->copy));
+    {
+        Timed t(ly, SKV_K_QK, st);
+        SKV_HIP(skv::launch_qk(dm, q, ly->k_out, ly->k_loc, ly->A, ly->Bt, ly->slot_chunk, ly->theta, ly->rope_off,
+                               ly->logits, st));
+    }
+    // join
+    SKV_HIP(hipStreamWaitEvent(st, ly->ev_fetch, 0));
+    {
+        Timed t(ly, SKV_K_PV, st);
+        SKV_HIP(skv::launch_pv(dm, ly->logits, ly->v_out, ly->vc, ly->v_loc, ly->part_ml, ly->part_acc, st));
+    }
+    {
+        Timed t(ly, SKV_K_COMBINE, st);
+        SKV_HIP(skv::launch_combine(dm, ly->part_ml, ly->part_acc, out, st));
+    }
+    if (ly->timing) ++ly->timed_steps;
+    return SKV_OK;
+}
+
+int shadowkv_reset_cache(skv_layer *ly, void *stream) {
+    if (!ly) return fail(SKV_E_INVAL, "layer is null");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    SKV_HIP(hipStreamWaitEvent(st, ly->ev_fetch, 0));
+    SKV_HIP(skv::launch_fill_i32(ly->slot_chunk, -1, static_cast<size_t>(ly->dm.b) * ly->dm.hkv * ly->dm.k, st));
+    return SKV_OK;
+}
+
+int shadowkv_get_stats(skv_layer *ly, skv_stats *out) {
+    if (!ly || !out) return fail(SKV_E_INVAL, "null argument");
+    SKV_HIP(hipDeviceSynchronize());
+    unsigned long long c[4] = {0, 0, 0, 0};
+    SKV_HIP(hipMemcpy(c, ly->counters, sizeof(c), hipMemcpyDeviceToHost));
+    out->hits = static_cast<int64_t>(c[0]);
+    out->misses = static_cast<int64_t>(c[1]);
+    out->steps = static_cast<int64_t>(c[2]);
+    out->bytes_h2d = out->misses * ly->dm.c * ly->dm.d * ly->dm.esize;
+    return SKV_OK;
+}
+
+int shadowkv_reset_stats(skv_layer *ly) {
+    if (!ly) return fail(SKV_E_INVAL, "layer is null");
+    SKV_HIP(hipDeviceSynchronize());
+    SKV_HIP(hipMemset(ly->counters, 0, 4 * sizeof(unsigned long long)));
+    return SKV_OK;
+}
+
+static const void *tensor_ptr(const skv_layer *ly, int which, size_t *bytes) {
+    const Dims &dm = ly->dm;
+    const size_t bh = static_cast<size_t>(dm.b) * dm.hkv, E = dm.esize, D = dm.d;
+    switch (which) {
+        case SKV_T_LANDMARKS: *bytes = bh * dm.n * D * E; return ly->L;
+        case SKV_T_MIN_COS: *bytes = bh * dm.n * 4; return ly->min_cos;
+        case SKV_T_OUTLIERS: *bytes = bh * dm.o * 4; return ly->outliers;
+        case SKV_T_CAND_MASK: *bytes = bh * dm.mask_words * 4; return ly->cand;
+        case SKV_T_SCORES: *bytes = static_cast<size_t>(dm.b) * dm.hq * dm.n * 4; return ly->P;
+        case SKV_T_GROUP_SCORES: *bytes = bh * dm.n * 4; return ly->S2;
+        case SKV_T_SELECTION: *bytes = bh * dm.k * 4; return ly->sel;
+        case SKV_T_SLOT_CHUNKS: *bytes = bh * dm.k * 4; return ly->slot_chunk;
+        case SKV_T_CACHE_V: *bytes = bh * dm.KC * D * E; return ly->vc;
+        case SKV_T_K_OUT: *bytes = bh * dm.OC * D * E; return ly->k_out;
+        case SKV_T_V_OUT: *bytes = bh * dm.OC * D * E; return ly->v_out;
+        case SKV_T_K_LOC: *bytes = bh * dm.w * D * E; return ly->k_loc;
+        case SKV_T_V_LOC: *bytes = bh * dm.w * D * E; return ly->v_loc;
+        default: *bytes = 0; return nullptr;
+    }
+}
+
+size_t shadowkv_tensor_bytes(const skv_layer *ly, int which) {
+    if (!ly) return 0;
+    size_t bytes = 0;
+    tensor_ptr(ly, which, &bytes);
+    return bytes;
+}
+
+int shadowkv_read(skv_layer *ly, int which, void *dst, size_t bytes, void *stream) {
+    if (!ly || !dst) return fail(SKV_E_INVAL, "null argument");
+    size_t need = 0;
+    const void *src = tensor_ptr(ly, which, &need);
+    if (!src) return fail(SKV_E_INVAL, "unknown tensor id");
+    if (bytes != need) return fail(SKV_E_SHAPE, "byte count does not match the tensor size");
+    if (need == 0) return SKV_OK;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    SKV_HIP(hipStreamWaitEvent(st, ly->ev_fetch, 0));
+    SKV_HIP(hipMemcpyAsync(dst, src, need, hipMemcpyDefault, st));
+    return SKV_OK;
+}
+
+int shadowkv_set_timing(skv_layer *ly, int enable) {
+    if (!ly) return fail(SKV_E_INVAL, "layer is null");
+    ly->timing = enable != 0;
+    return SKV_OK;
+}
+
+int shadowkv_get_timing(skv_layer *ly, double *ms_out, int64_t *steps_out) {
+    if (!ly || !ms_out) return fail(SKV_E_INVAL, "null argument");
+    SKV_HIP(hipDeviceSynchronize());
+    for (int i = 0; i < SKV_K_COUNT; ++i) ms_out[i] = 0.0;
+    for (const Mark &m : ly->marks) {
+        float ms = 0.f;
+        SKV_HIP(hipEventElapsedTime(&ms, m.start, m.stop));
+        ms_out[m.kernel] += ms;
+    }
+    if (steps_out) *steps_out = ly->timed_steps;
+    ly->marks.clear();
+    ly->ev_used = 0;
+    ly->timed_steps = 0;
+    return SKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,156 @@
+// Device-side helpers shared by the gfx950 kernels of the ShadowKV decode
+// step: storage conversions, wave64 reductions and scans, order-preserving
+// float keys for radix selection, and RoPE with a double-precision angle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "skv_dims.h"
+
+namespace skv {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Storage types: binary32 (float) or bfloat16 carried as its 16 raw bits.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+    return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest, ties to even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+// Nearest bfloat16 of a double, rounded once (ties to even): 8 significant
+// bits, binary32's exponent range (subnormal spacing 2^-133).
+__device__ __forceinline__ uint16_t f64_to_bf16_bits(double x) {
+    if (x == 0.0 || !isfinite(x)) return f32_to_bf16_bits(static_cast<float>(x));
+    int e;
+    frexp(x, &e);
+    int q = e - 8;
+    if (q < -133) q = -133;
+    const double y = ldexp(rint(ldexp(x, -q)), q);  // a bfloat16 value (or 2^128)
+    return static_cast<uint16_t>(__float_as_uint(static_cast<float>(y)) >> 16);
+}
+
+template <typename T> struct Elem;
+
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float ld(const float *p, size_t i) { return p[i]; }
+    static __device__ __forceinline__ void st(float *p, size_t i, float v) { p[i] = v; }
+    // storage value of a double (one rounding)
+    static __device__ __forceinline__ float rnd_d(double v) { return static_cast<float>(v); }
+};
+
+template <> struct Elem<uint16_t> {
+    static __device__ __forceinline__ float ld(const uint16_t *p, size_t i) { return bf16_bits_to_f32(p[i]); }
+    static __device__ __forceinline__ void st(uint16_t *p, size_t i, float v) { p[i] = f32_to_bf16_bits(v); }
+    static __device__ __forceinline__ float rnd_d(double v) { return bf16_bits_to_f32(f64_to_bf16_bits(v)); }
+};
+
+// ---------------------------------------------------------------------------
+// Wave64 reductions.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+// Merge two (running max, sum of exp(x - max)) pairs.
+__device__ __forceinline__ void ms_merge(float &m, float &s, float m2, float s2) {
+    float mn = fmaxf(m, m2);
+    if (mn == -INFINITY) { m = mn; s = 0.f; return; }
+    s = s * expf(m - mn) + s2 * expf(m2 - mn);
+    m = mn;
+}
+
+// (max, sum) merge across lanes whose index differs in the bits of `mask_bits`
+// (xor distances 1, 2, 4, ... up to the highest bit set).
+__device__ __forceinline__ void ms_reduce_lanes(float &m, float &s, int width) {
+    for (int off = 1; off < width; off <<= 1) {
+        float m2 = __shfl_xor(m, off, kWave);
+        float s2 = __shfl_xor(s, off, kWave);
+        ms_merge(m, s, m2, s2);
+    }
+}
+
+// Exclusive count of `flag` over the threads of the block (thread order) and
+// the block total.  Every thread of the block must call it.  `wcnt` holds at
+// least blockDim.x / 64 ints of shared memory.
+__device__ __forceinline__ int block_excl_count(bool flag, int *wcnt, int *total) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int nwaves = blockDim.x / kWave;
+    const uint64_t m = __ballot(flag);
+    const uint64_t lt = lane ? (~0ull >> (kWave - lane)) : 0ull;
+    const int pre = __popcll(m & lt);
+    if (lane == 0) wcnt[wave] = __popcll(m);
+    __syncthreads();
+    int before = 0, tot = 0;
+    for (int w = 0; w < nwaves; ++w) {
+        int c = wcnt[w];
+        before += (w < wave) ? c : 0;
+        tot += c;
+    }
+    __syncthreads();
+    *total = tot;
+    return before + pre;
+}
+
+// ---------------------------------------------------------------------------
+// Order-preserving 32-bit key of a float (larger float -> larger key, -0 and
+// +0 equal); 0 is below every finite or infinite value's key.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t float_key(float x) {
+    x = x + 0.0f;  // -0 -> +0
+    uint32_t u = __float_as_uint(x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------------------
+// RoPE.  The angle pos * theta is formed in double precision and reduced to
+// [-pi, pi] with a two-part 2*pi before single-precision sin/cos, so large
+// positions (2.5e5) keep ~1e-7 accuracy.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void angle_sincos(double a, float *sn, float *cs) {
+    const double kInv2Pi = 0.15915494309189535;
+    const double k2PiHi = 6.283185307179586;
+    const double k2PiLo = 2.4492935982947064e-16;
+    double turns = rint(a * kInv2Pi);
+    double red = fma(-turns, k2PiHi, a);
+    red = fma(-turns, k2PiLo, red);
+    sincosf(static_cast<float>(red), sn, cs);
+}
+
+__device__ __forceinline__ void rope_rotate(float x1, float x2, float sn, float cs, float &y1, float &y2) {
+    y1 = x1 * cs - x2 * sn;
+    y2 = x2 * cs + x1 * sn;
+}
+
+__device__ __forceinline__ bool mask_bit(const uint32_t *words, int j) {
+    return (words[j >> 5] >> (j & 31)) & 1u;
+}
+
+}  // namespace skv

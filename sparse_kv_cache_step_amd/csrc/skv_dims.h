@@ -1,0 +1,66 @@
+// Derived sizes of one layer and the kernel launchers of the ShadowKV step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace skv {
+
+// Tile sizes.
+constexpr int kScoreTile = 256;   // chunks per scoring workgroup (4 waves x 64)
+constexpr int kGroupTile = 256;   // chunks per group-score workgroup
+constexpr int kTopkThreads = 1024;
+constexpr int kQkTile = 64;       // keys per generic QK workgroup
+constexpr int kQkMfmaTile = 256;  // keys per MFMA QK workgroup (4 waves x 64)
+constexpr int kPvTile = 256;      // keys per PV workgroup
+constexpr int kMaxGroup = 16;     // query heads per KV head
+
+struct Dims {
+    int b, hq, hkv, d, s, c, r, o, k, w;
+    int n;           // chunks per sequence
+    int n_loc;       // chunks of the local window
+    int G;           // query heads per KV head
+    int GP;          // G rounded up to 4, 8 or 16 (MFMA QK variant)
+    int mask_words;  // ceil(n / 32)
+    int score_tiles; // ceil(n / kScoreTile)
+    int OC, KC, NK;  // outlier keys, rebuilt keys, all keys per (b, h_kv)
+    int pv_tiles;    // ceil(NK / kPvTile)
+    int esize;       // bytes per stored element
+    int bf16;        // storage type
+    int r_pad;       // rank rounded up to 32
+    float scale;     // 1 / sqrt(d)
+};
+
+// ---- launchers (return the launch status) ----------------------------------
+// Prefill.
+hipError_t launch_landmarks(const Dims &dm, const void *k_pre, const void *k_rope, const double *theta,
+                            void *landmarks, float *min_cos, hipStream_t st);
+hipError_t launch_topk(const Dims &dm, const float *vals, int rows, int n, int n_valid_prefix,
+                       const uint32_t *mask, float sign, int k, int32_t *out, uint32_t *gscratch,
+                       int lds_limit, hipStream_t st);
+hipError_t launch_gather_static(const Dims &dm, const void *k_pre, const void *k_rope, const void *v,
+                                const int32_t *outliers, const double *theta, void *k_out, void *v_out,
+                                void *k_loc, void *v_loc, hipStream_t st);
+hipError_t launch_cand_mask(const Dims &dm, const int32_t *outliers, uint32_t *cand, hipStream_t st);
+hipError_t launch_transpose_b(const Dims &dm, const void *B, void *Bt, hipStream_t st);
+hipError_t launch_fill_i32(int32_t *p, int32_t value, size_t count, hipStream_t st);
+hipError_t launch_validate_outliers(const Dims &dm, const int32_t *outliers, int32_t *bad, hipStream_t st);
+
+// Decode.
+hipError_t launch_score(const Dims &dm, const void *q, const void *landmarks, const uint32_t *cand,
+                        float *P, float2 *stats, hipStream_t st);
+hipError_t launch_group(const Dims &dm, const float *P, const float2 *stats, const uint32_t *cand,
+                        float *S2, hipStream_t st);
+hipError_t launch_setdiff(const Dims &dm, const int32_t *sel, int32_t *slot_chunk, int2 *misses,
+                          int32_t *miss_count, unsigned long long *counters, hipStream_t st);
+hipError_t launch_fetch(const Dims &dm, const void *v_host, void *vc, const int2 *misses,
+                        const int32_t *miss_count, int blocks_per_bh, hipStream_t st);
+hipError_t launch_qk(const Dims &dm, const void *q, const void *k_out, const void *k_loc, const void *A,
+                     const void *Bt, const int32_t *slot_chunk, const double *theta,
+                     const float2 *rope_off, float *logits, hipStream_t st);
+hipError_t launch_pv(const Dims &dm, const float *logits, const void *v_out, const void *vc,
+                     const void *v_loc, float2 *part_ml, float *part_acc, hipStream_t st);
+hipError_t launch_combine(const Dims &dm, const float2 *part_ml, const float *part_acc, void *out,
+                          hipStream_t st);
+
+}  // namespace skv

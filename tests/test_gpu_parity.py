@@ -1,0 +1,220 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle
+on the same seeded inputs.
+
+Each case runs both sides end to end from the raw synthetic inputs (K_pre,
+V, the queries): the GPU through shadowkv_prefill_meta / decode_step with the
+factors from sparse_kv_cache_step_amd.setup, the oracle through its own
+prefill, SVD and decode.  Prefill state is compared first (landmarks and
+stored keys to one unit in the last place of the storage type, cosine minima
+to 1e-6, outlier sets exactly or at near-ties), then every decode step:
+scores, group scores, the selection (exact or near-tie swaps), the output to
+1e-4 (binary32) / 2e-2 (bfloat16) max-abs, the cache hit counts, and the
+lossless-cache invariant (resident V rows equal the host V rows of I_t).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from parity_helpers import (OUT_TOL, bf16_ulp, check_outliers, check_selection, layer_kwargs, log, oracle_shape,
+                            tdtype, to_dev, to_np)
+from sparse_kv_cache_step_amd import binding as skv
+from sparse_kv_cache_step_amd import synth
+from sparse_kv_cache_step_amd.setup import svd_factors
+
+pytestmark = pytest.mark.gpu
+
+T = synth.TINY_FP32
+CASES = {
+    # the tiny binary32 workload as specified
+    "tiny-fp32": T,
+    # several scoring tiles with a ragged tail (n = 1000), b = 2, drifting q
+    "fp32-ragged-b2": T.with_(b=2, s=8000, d=128, r=48, o=5, k=37, w=24, steps=3, rho=0.9, n_scaled_chunks=6),
+    # chunk size 4
+    "fp32-chunk4": T.with_(s=512, c=4, o=3, k=9, w=12, steps=2, rho=0.9),
+    # the Llama-3-8B-shaped 32K single layer, 16 steps
+    "bf16-llama-32k": synth.LLAMA_32K,
+    # GLM-shaped GQA 16, ragged n = 1500, rank 160
+    "bf16-g16-ragged": synth.GLM_244K.with_(b=2, s=12000, o=10, k=23, steps=4),
+    # one query head per KV head, d = 64, rank padded (40 -> 64)
+    "bf16-d64-g1": synth.LLAMA_32K.with_(b=1, h_q=4, h_kv=4, d=64, s=4096, r=40, o=3, k=17, w=16, steps=3,
+                                         true_rank=20, rho=0.9),
+    # no outliers and no local window
+    "bf16-no-static": synth.LLAMA_32K.with_(h_q=8, h_kv=2, s=2048, r=96, o=0, k=12, w=0, steps=3, rho=0.9),
+    # full budget: every selectable chunk is attended
+    "bf16-full-budget": synth.LLAMA_32K.with_(h_q=8, h_kv=2, s=1024, o=4, k=120, w=32, steps=2, rho=0.9),
+}
+
+
+def _gpu_state(wl, k_pre, v):
+    dt = tdtype(wl)
+    k_pre_d, v_d = to_dev(k_pre, dt), to_dev(v, dt)
+    A_d, B_d = svd_factors(k_pre_d, wl.r)
+    layer = skv.Layer(**layer_kwargs(wl))
+    hb = layer.host_buffer()
+    layer.prefill_meta(k_pre_d, v_d, A_d, B_d, hb)
+    torch.cuda.synchronize()
+    return layer, hb
+
+
+def _compare_prefill(wl, layer, hb, meta, v):
+    L_g = to_np(layer.read(skv.SKV_T_LANDMARKS))
+    ulp = bf16_ulp(meta["landmarks"]) if wl.bf16 else np.abs(np.spacing(meta["landmarks"].astype(np.float32)))
+    assert np.all(np.abs(L_g - meta["landmarks"]) <= ulp), "landmarks differ by more than one unit in the last place"
+    mc_g = to_np(layer.read(skv.SKV_T_MIN_COS))
+    assert np.max(np.abs(mc_g - meta["min_cos"])) <= 1e-6
+    if wl.o:
+        out_g = to_np(layer.read(skv.SKV_T_OUTLIERS))
+        exact = check_outliers(out_g, meta["outliers"], meta["min_cos"], wl.n - wl.n_loc)
+        assert exact, "outlier sets differ (near-tie); this seed should not have any"
+        ko = to_np(layer.read(skv.SKV_T_K_OUT))
+        ulp_k = bf16_ulp(meta["k_out"]) if wl.bf16 else np.abs(np.spacing(meta["k_out"].astype(np.float32)))
+        assert np.all(np.abs(ko - meta["k_out"]) <= ulp_k)
+        np.testing.assert_array_equal(to_np(layer.read(skv.SKV_T_V_OUT)), meta["v_out"])
+    if wl.w:
+        kl = to_np(layer.read(skv.SKV_T_K_LOC))
+        ulp_k = bf16_ulp(meta["k_loc"]) if wl.bf16 else np.abs(np.spacing(meta["k_loc"].astype(np.float32)))
+        assert np.all(np.abs(kl - meta["k_loc"]) <= ulp_k)
+        np.testing.assert_array_equal(to_np(layer.read(skv.SKV_T_V_LOC)), meta["v_loc"])
+    words = layer.read(skv.SKV_T_CAND_MASK).cpu().numpy().view(np.uint32)
+    bits = ((words[..., :, None] >> np.arange(32, dtype=np.uint32)) & 1).reshape(wl.b, wl.h_kv, -1)[..., :wl.n]
+    np.testing.assert_array_equal(bits, meta["cand"])
+    hv = hb.tensor(tdtype(wl), (wl.b, wl.h_kv, wl.s, wl.d)).float().numpy()
+    np.testing.assert_array_equal(hv, v)
+
+
+def _check_cache_lossless(wl, layer, v, sel):
+    slots = to_np(layer.read(skv.SKV_T_SLOT_CHUNKS))
+    vc = to_np(layer.read(skv.SKV_T_CACHE_V)).reshape(wl.b, wl.h_kv, wl.k, wl.c, wl.d)
+    for b in range(wl.b):
+        for h in range(wl.h_kv):
+            assert sorted(slots[b, h]) == sorted(sel[b, h])
+            rows = v[b, h].reshape(wl.n, wl.c, wl.d)[slots[b, h]]
+            np.testing.assert_array_equal(vc[b, h], rows)
+
+
+@pytest.mark.parametrize("case", list(CASES))
+def test_end_to_end_matches_oracle(case):
+    wl = CASES[case]
+    log(f"[{case}] b={wl.b} h_q={wl.h_q} h_kv={wl.h_kv} d={wl.d} s={wl.s} c={wl.c} r={wl.r} o={wl.o} "
+        f"k={wl.k} w={wl.w} bf16={wl.bf16} steps={wl.steps}")
+    shape = oracle_shape(wl)
+    k_pre, v, qs = synth.k_pre_numpy(wl), synth.v_numpy(wl), synth.queries_numpy(wl)
+    meta = oracle.prefill(shape, k_pre, v)
+    A_o, B_o = oracle.svd_factors(shape, k_pre)
+    layer, hb = _gpu_state(wl, k_pre, v)
+    _compare_prefill(wl, layer, hb, meta, v)
+    sim = oracle.CacheSim(wl.b, wl.h_kv)
+    prev_hits = 0
+    for t in range(qs.shape[0]):
+        q_d = to_dev(qs[t], tdtype(wl))
+        out_d = torch.empty_like(q_d)
+        layer.decode_step(q_d, out_d)
+        torch.cuda.synchronize()
+        res = oracle.decode(shape, qs[t], meta, A_o, B_o, v)
+        cand = meta["cand"].astype(bool)
+        P_g = to_np(layer.read(skv.SKV_T_SCORES))
+        candq = np.repeat(cand, wl.group, axis=1)
+        assert np.all(np.isneginf(P_g[~candq]))
+        p_tol = 1e-4 if wl.bf16 else 1e-5
+        assert np.max(np.abs(P_g[candq] - res["P"][candq])) <= p_tol
+        S2_g = to_np(layer.read(skv.SKV_T_GROUP_SCORES))
+        assert np.all(np.abs(S2_g[cand] - res["S2"][cand]) <= 1e-4 * res["S2"][cand] + 1e-12)
+        sel_g = to_np(layer.read(skv.SKV_T_SELECTION))
+        exact = check_selection(sel_g, res["sel"], res["S2"], meta["cand"])
+        ref = res["out"] if exact else oracle.attend(shape, qs[t], sel_g, A_o, B_o, v, meta)
+        err = float(np.max(np.abs(to_np(out_d) - ref)))
+        log(f"[{case}] step {t}: selection {'exact' if exact else 'near-tie'}, max|out - oracle| = {err:.3g}")
+        assert err <= OUT_TOL[wl.bf16], f"step {t}: max abs error {err}"
+        # cache: hits follow the set intersections of consecutive selections
+        hits, _ = sim.step(sel_g)
+        st = layer.stats()
+        assert st["steps"] == t + 1
+        assert st["hits"] - prev_hits == hits
+        assert st["hits"] + st["misses"] == (t + 1) * wl.b * wl.h_kv * wl.k
+        prev_hits = st["hits"]
+        _check_cache_lossless(wl, layer, v, sel_g)
+    layer.close()
+    hb.free()
+
+
+def test_load_meta_decode_and_reset_cache():
+    """Metadata installed with shadowkv_load_meta (the oracle's prefill and
+    factors) decodes like the oracle; emptying the cache changes no output
+    beyond summation order, only the hit count."""
+    wl = synth.LLAMA_32K.with_(s=8192, steps=4, rho=0.9)
+    shape = oracle_shape(wl)
+    k_pre, v, qs = synth.k_pre_numpy(wl), synth.v_numpy(wl), synth.queries_numpy(wl)
+    meta = oracle.prefill(shape, k_pre, v)
+    A_o, B_o = oracle.svd_factors(shape, k_pre)
+    dt = tdtype(wl)
+    layer = skv.Layer(**layer_kwargs(wl))
+    hb = layer.host_buffer()
+    hb.tensor(dt, (wl.b, wl.h_kv, wl.s, wl.d)).copy_(torch.from_numpy(v).to(dt))
+    layer.load_meta(to_dev(meta["landmarks"], dt), torch.from_numpy(meta["outliers"]).cuda(),
+                    to_dev(meta["k_out"], dt), to_dev(meta["v_out"], dt), to_dev(meta["k_loc"], dt),
+                    to_dev(meta["v_loc"], dt), to_dev(A_o, dt), to_dev(B_o, dt), hb)
+    outs = []
+    for t in range(wl.steps):
+        q_d = to_dev(qs[t], dt)
+        out_d = torch.empty_like(q_d)
+        layer.decode_step(q_d, out_d)
+        torch.cuda.synchronize()
+        res = oracle.decode(shape, qs[t], meta, A_o, B_o, v)
+        sel_g = to_np(layer.read(skv.SKV_T_SELECTION))
+        exact = check_selection(sel_g, res["sel"], res["S2"], meta["cand"])
+        ref = res["out"] if exact else oracle.attend(shape, qs[t], sel_g, A_o, B_o, v, meta)
+        err = float(np.max(np.abs(to_np(out_d) - ref)))
+        log(f"[load_meta] step {t}: max|out - oracle| = {err:.3g}")
+        assert err <= OUT_TOL[True]
+        outs.append(to_np(out_d))
+    hits_warm = layer.stats()["hits"]
+    # repeat the last step warm (all hits) and after a reset (all misses)
+    q_d = to_dev(qs[-1], dt)
+    warm = torch.empty_like(q_d)
+    layer.decode_step(q_d, warm)
+    torch.cuda.synchronize()
+    assert layer.stats()["hits"] - hits_warm == wl.b * wl.h_kv * wl.k
+    layer.reset_cache()
+    cold = torch.empty_like(q_d)
+    layer.decode_step(q_d, cold)
+    torch.cuda.synchronize()
+    st = layer.stats()
+    assert st["hits"] - hits_warm == wl.b * wl.h_kv * wl.k  # no hits after the reset
+    w_np, c_np = to_np(warm), to_np(cold)
+    np.testing.assert_array_equal(w_np, outs[-1])  # same resident layout -> bitwise equal
+    assert np.all(np.abs(w_np - c_np) <= 2 * bf16_ulp(w_np))
+    layer.close()
+    hb.free()
+
+
+def test_error_paths_on_device():
+    wl = synth.TINY_FP32
+    layer = skv.Layer(**layer_kwargs(wl))
+    q = torch.zeros((wl.b, wl.h_q, wl.d), device="cuda")
+    with pytest.raises(skv.ShadowKVError) as e:
+        layer.decode_step(q, torch.empty_like(q))
+    assert e.value.code == skv.SKV_E_STATE
+    # a pageable host buffer is refused for V
+    pageable = np.zeros(wl.b * wl.h_kv * wl.s * wl.d, dtype=np.float32)
+    k = torch.zeros((wl.b, wl.h_kv, wl.s, wl.d), device="cuda")
+    A = torch.zeros((wl.b, wl.s, wl.r), device="cuda")
+    B = torch.zeros((wl.b, wl.h_kv, wl.r, wl.d), device="cuda")
+    with pytest.raises(skv.ShadowKVError) as e:
+        skv.shadowkv_prefill_meta(layer.h, k.data_ptr(), None, k.data_ptr(), A.data_ptr(), B.data_ptr(),
+                                  pageable.ctypes.data, torch.cuda.current_stream().cuda_stream)
+    assert e.value.code == skv.SKV_E_INVAL
+    # unsorted outlier rows are refused by load_meta
+    hb = layer.host_buffer()
+    bad = torch.tensor([[[3, 1, 2, 9], [0, 1, 2, 3]]], dtype=torch.int32, device="cuda")
+    zk = lambda *s: torch.zeros(s, device="cuda")
+    with pytest.raises(skv.ShadowKVError) as e:
+        layer.load_meta(zk(wl.b, wl.h_kv, wl.n, wl.d), bad, zk(wl.b, wl.h_kv, wl.o * wl.c, wl.d),
+                        zk(wl.b, wl.h_kv, wl.o * wl.c, wl.d), zk(wl.b, wl.h_kv, wl.w, wl.d),
+                        zk(wl.b, wl.h_kv, wl.w, wl.d), A, B, hb)
+    assert e.value.code == skv.SKV_E_SHAPE
+    # shape mismatch is caught by the binding before any launch
+    with pytest.raises(ValueError):
+        layer.decode_step(torch.zeros((1, 2, 3), device="cuda"), torch.empty_like(q))
+    layer.close()
+    hb.free()
