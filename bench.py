@@ -1,0 +1,296 @@
+"""Throughput of the ShadowKV sparse decode step on one MI355X.
+
+A step is one decode step of the model: every layer's shadowkv_decode_step
+(score landmarks, select top-k chunks, set-difference cache update, host-V
+fetch of the misses on a second stream, MFMA key rebuild + RoPE + logits,
+PV and combine) for all b sequences, one token each.  The metric is
+layer-steps/s (one layer-step = one shadowkv_decode_step call) with the
+effective HBM bandwidth (algorithmic bytes / time) and the equivalent
+bandwidth (dense K+V bytes / time, the review page's B~ measured).
+
+Inputs are seeded synthetic arrays with the workload's shapes, generated on
+the device; the low-rank factors, prefill metadata and the pinned host V are
+built before the timed region (prefill is not part of the metric).  Queries
+for every timed step are resident in HBM before timing starts.  The host-V
+fetch over PCIe is a step of the method itself (Algorithm 2 step 3), so it is
+inside the timed region.
+
+Output: one JSON line on stdout (progress goes to stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM = 8.0e12       # bytes/s, MI355X HBM3E
+PEAK_PCIE = 64.0e9      # bytes/s per direction, PCIe Gen5 x16
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(wl) -> dict:
+    """Bytes one layer-step must move at minimum, by kernel (bf16: 2 B)."""
+    E = 2 if wl.bf16 else 4
+    bh = wl.b * wl.h_kv
+    return {
+        "landmarks": bh * wl.n * wl.d * E,                    # score: all of L
+        "q": wl.b * wl.h_q * wl.d * E,
+        "a_rows": bh * wl.k * wl.c * wl.r * E,                # rebuild: gathered A rows
+        "b_factor": bh * wl.r * wl.d * E,
+        "outlier_kv": 2 * bh * wl.o * wl.c * wl.d * E,
+        "local_kv": 2 * bh * wl.w * wl.d * E,
+        "selected_v": bh * wl.k * wl.c * wl.d * E,
+        "out": wl.b * wl.h_q * wl.d * E,
+    }
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_kv_cache_step_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the score kernel from committed rocprofv3
+    counter runs, if they were taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_score_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--workload", default="llama3-8b-128k-b8")
+    ap.add_argument("--layers", type=int, default=None, help="default: the workload's layer count")
+    ap.add_argument("--host-v-share", type=int, default=0,
+                    help="layers share this many pinned host-V buffers (0: one per layer)")
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-events", choices=["on", "off"], default="on")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from sparse_kv_cache_step_amd import binding as skv
+    from sparse_kv_cache_step_amd import synth
+    from sparse_kv_cache_step_amd.setup import svd_factors
+
+    if not os.path.exists(skv.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+
+    wl = synth.WORKLOADS[args.workload]
+    layers = args.layers or wl.layers
+    wl = wl.with_(layers=layers)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    dt = torch.bfloat16 if wl.bf16 else torch.float32
+    nq = args.warmup + args.steps
+    log(f"bench: {wl.name} b={wl.b} s={wl.s} h_q={wl.h_q} h_kv={wl.h_kv} d={wl.d} r={wl.r} o={wl.o} k={wl.k} "
+        f"w={wl.w} layers={layers} steps={args.steps} warmup={args.warmup}")
+
+    # ---- setup (untimed): data, factors, prefill, pinned host V ----------------
+    t0 = time.time()
+    n_host = layers if args.host_v_share <= 0 else min(layers, args.host_v_share)
+    host_bufs = []
+    Ls, qs = [], []
+    keep = {}  # inputs of the spot-checked layer, for the oracle
+    spot_layer = layers - 1
+    for l in range(layers):
+        k_pre = synth.k_pre_torch(wl, l, dev)
+        v = synth.v_torch(wl, l, dev)
+        A, B = svd_factors(k_pre, wl.r)
+        lay = skv.Layer(batch=wl.b, heads_q=wl.h_q, heads_kv=wl.h_kv, head_dim=wl.d, seq_len=wl.s, chunk=wl.c,
+                        rank=wl.r, n_outlier=wl.o, top_k=wl.k, local_window=wl.w, rope_base=wl.rope_base,
+                        bf16=wl.bf16)
+        if l < n_host:
+            host_bufs.append(lay.host_buffer())
+        lay.prefill_meta(k_pre, v, A, B, host_bufs[l % n_host])
+        qs.append(synth.queries_torch(wl, l, dev, steps=nq))
+        torch.cuda.synchronize()
+        if l == spot_layer and not args.no_cpu_baseline:
+            sample = [0, wl.b // 2] if wl.b > 1 else [0]
+            keep = {"seqs": sample, "k_pre": k_pre[sample].float().cpu(), "v": v[sample].float().cpu()}
+        del k_pre, v, A, B
+        Ls.append(lay)
+        if l % 4 == 3 or l == layers - 1:
+            log(f"  setup: {l + 1}/{layers} layers ready ({time.time() - t0:.0f}s)")
+    torch.cuda.empty_cache()
+    outs = [torch.empty((wl.b, wl.h_q, wl.d), dtype=dt, device=dev) for _ in range(layers)]
+    stream = torch.cuda.current_stream()
+
+    def run_steps(t_begin, t_count):
+        for t in range(t_begin, t_begin + t_count):
+            for l in range(layers):
+                Ls[l].decode_step(qs[l][t], outs[l], stream)
+
+    # ---- warmup ---------------------------------------------------------------
+    run_steps(0, args.warmup)
+    torch.cuda.synchronize()
+    for lay in Ls:
+        lay.reset_stats()
+
+    # ---- timed region ---------------------------------------------------------
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    e0.record(stream)
+    run_steps(args.warmup, args.steps)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    last_out = outs[spot_layer].clone()  # output of the last timed step
+    wall = time.perf_counter() - wall0
+    elapsed = e0.elapsed_time(e1) / 1e3
+    log(f"timed: {args.steps} steps x {layers} layers in {elapsed * 1e3:.2f} ms (host wall {wall * 1e3:.2f} ms)")
+    stats = [lay.stats() for lay in Ls]
+    hits = sum(s["hits"] for s in stats)
+    misses = sum(s["misses"] for s in stats)
+    alpha = hits / max(1, hits + misses)
+    h2d_bytes = sum(s["bytes_h2d"] for s in stats)
+
+    # ---- per-kernel durations: the same steps again with HIP events ----------
+    kern_ms = {name: 0.0 for name in skv.KERNELS}
+    kern_steps = 0
+    if args.kernel_events == "on":
+        for lay in Ls:
+            lay.set_timing(True)
+        run_steps(args.warmup, args.steps)
+        torch.cuda.synchronize()
+        for lay in Ls:
+            ms, st = lay.get_timing()
+            lay.set_timing(False)
+            kern_steps += st
+            for kname, v_ms in ms.items():
+                kern_ms[kname] += v_ms
+    per_launch_us = {k: (v * 1e3 / kern_steps if kern_steps else None) for k, v in kern_ms.items()}
+
+    layer_steps = args.steps * layers
+    ab = algorithmic_bytes(wl)
+    alg_total = sum(ab.values())
+    t_ls = elapsed / layer_steps
+    dense_kv = 2 * wl.b * wl.h_kv * wl.s * wl.d * (2 if wl.bf16 else 4)
+
+    roofline = None
+    kernels = {}
+    if kern_steps:
+        score_bytes = ab["landmarks"] + ab["q"]
+        qk_bytes = ab["a_rows"] + ab["b_factor"] + ab["outlier_kv"] // 2 + ab["local_kv"] // 2 + ab["q"]
+        pv_bytes = ab["selected_v"] + ab["outlier_kv"] // 2 + ab["local_kv"] // 2 + ab["out"]
+        fetch_bytes = h2d_bytes / max(1, layer_steps)
+        for name, nbytes, peak in (("score", score_bytes, PEAK_HBM), ("qk", qk_bytes, PEAK_HBM),
+                                   ("pv", pv_bytes, PEAK_HBM), ("fetch", fetch_bytes, PEAK_PCIE)):
+            us = per_launch_us[name]
+            gbs = nbytes / (us * 1e-6) / 1e9 if us else None
+            kernels[name] = {"us_per_launch": round(us, 3), "bytes_per_launch": int(nbytes),
+                             "GBps": round(gbs, 1) if gbs else None, "peak_GBps": peak / 1e9,
+                             "frac": round(gbs * 1e9 / peak, 4) if gbs else None}
+        for name in ("group", "topk", "setdiff", "combine"):
+            kernels[name] = {"us_per_launch": round(per_launch_us[name], 3)}
+        sc = kernels["score"]
+        traffic = measured_traffic(wl.name)
+        roofline = {"kernel": "score_mfma_kernel (landmark scoring)", "bound": "hbm",
+                    "achieved": sc["GBps"], "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": sc["frac"],
+                    "traffic": traffic, "bytes_per_launch": sc["bytes_per_launch"],
+                    "us_per_launch": sc["us_per_launch"]}
+
+    fetch_gbs = kernels.get("fetch", {}).get("GBps") if kernels else None
+    closed_form = None
+    if fetch_gbs:
+        closed_form = skv.shadowkv_equiv_bandwidth(wl.s, wl.c, wl.k, wl.o, alpha, PEAK_HBM, fetch_gbs * 1e9) / 1e12
+
+    # ---- oracle on the host, bounded sample of the same workload --------------
+    cpu_baseline = None
+    parity = None
+    if not args.no_cpu_baseline and keep:
+        import oracle
+        from oracle import Shape
+        seqs = keep["seqs"]
+        shape = Shape(b=len(seqs), h_q=wl.h_q, h_kv=wl.h_kv, d=wl.d, s=wl.s, c=wl.c, r=wl.r, o=wl.o, k=wl.k,
+                      w=wl.w, rope_base=wl.rope_base, bf16=wl.bf16)
+        kp = keep["k_pre"].double().numpy()
+        vv = keep["v"].double().numpy()
+        log(f"cpu baseline: oracle prefill + SVD for sequences {seqs} of layer {spot_layer} (untimed)")
+        meta = oracle.prefill(shape, kp, vv)
+        A_o, B_o = oracle.svd_factors(shape, kp)
+        q_all = qs[spot_layer][:, seqs].float().cpu().double().numpy()
+        # decode steps 0, 1, ... until the time budget is spent or the last
+        # timed step is reached (then the GPU's output there is spot-checked)
+        t_last = args.warmup + args.steps - 1
+        t_start = time.perf_counter()
+        n_done, res = 0, None
+        for t in range(nq):
+            res = oracle.decode(shape, q_all[t], meta, A_o, B_o, vv)
+            n_done += 1
+            if time.perf_counter() - t_start > args.cpu_baseline_seconds:
+                break
+        cpu_s = time.perf_counter() - t_start
+        per_seq_step = cpu_s / (n_done * len(seqs))
+        cores = min(os.cpu_count() or 1, len(seqs) * wl.h_kv)
+        cpu_baseline = {"value": round(1.0 / (per_seq_step * wl.b), 4), "unit": "layer-steps/s", "cores": cores,
+                        "kind": "oracle",
+                        "sample": f"{n_done} decode steps of sequences {seqs} (of {wl.b}) of one layer; "
+                                  f"{cpu_s:.1f} s of CPU time; scaled to all {wl.b} sequences"}
+        if n_done - 1 == t_last:
+            gpu_out = last_out[seqs].float().cpu().double().numpy()
+            gpu_sel = Ls[spot_layer].read(skv.SKV_T_SELECTION)[seqs].cpu().numpy()
+            parity = {"layer": spot_layer, "step": t_last, "sequences": seqs,
+                      "selection_equal": bool(np.array_equal(gpu_sel, res["sel"])),
+                      "max_abs_err_vs_oracle": float(np.max(np.abs(gpu_out - res["out"]))),
+                      "tolerance": 2e-2 if wl.bf16 else 1e-4}
+        log(f"cpu baseline: {cpu_baseline['value']} layer-steps/s on {cores} threads")
+
+    value = layer_steps / elapsed
+    line = {
+        "metric": "sparse decode layer-steps/sec + effective & equivalent HBM TB/s at 128K, 1 GPU",
+        "value": round(value, 2), "unit": "layer-steps/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.bf16 else "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.b, "seq_len": wl.s, "heads_q": wl.h_q, "heads_kv": wl.h_kv,
+                   "head_dim": wl.d, "chunk": wl.c, "rank": wl.r, "outlier_chunks": wl.o, "top_k": wl.k,
+                   "local_window": wl.w, "layers": layers, "host_v_buffers": n_host},
+        "us_per_layer_step": round(t_ls * 1e6, 3),
+        "effective_TBps": round(alg_total / t_ls / 1e12, 4),
+        "equivalent_TBps": round(dense_kv / t_ls / 1e12, 4),
+        "alpha": round(alpha, 4),
+        "h2d_GB": round(h2d_bytes / 1e9, 4),
+        "closed_form_equiv_TBps": round(closed_form, 3) if closed_form else None,
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu_baseline,
+        "parity_spot_check": parity,
+        "setup_s": round(time.time() - t0, 1),
+    }
+    print(json.dumps(line), flush=True)
+    for lay in Ls:
+        lay.close()
+    for hb in host_bufs:
+        hb.free()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
