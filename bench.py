@@ -86,6 +86,8 @@ def main() -> int:
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-events", choices=["on", "off"], default="on")
+    ap.add_argument("--overlap", choices=["on", "off"], default="off",
+                    help="fetch beside the key rebuild (on) or before it (off)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -136,6 +138,7 @@ def main() -> int:
             sample = [0, wl.b // 2] if wl.b > 1 else [0]
             keep = {"seqs": sample, "k_pre": k_pre[sample].float().cpu(), "v": v[sample].float().cpu()}
         del k_pre, v, A, B
+        lay.set_overlap(args.overlap == "on")
         Ls.append(lay)
         if l % 4 == 3 or l == layers - 1:
             log(f"  setup: {l + 1}/{layers} layers ready ({time.time() - t0:.0f}s)")
@@ -208,8 +211,7 @@ def main() -> int:
             kernels[name] = {"us_per_launch": round(us, 3), "bytes_per_launch": int(nbytes),
                              "GBps": round(gbs, 1) if gbs else None, "peak_GBps": peak / 1e9,
                              "frac": round(gbs * 1e9 / peak, 4) if gbs else None}
-        for name in ("group", "topk", "setdiff", "combine"):
-            kernels[name] = {"us_per_launch": round(per_launch_us[name], 3)}
+        kernels["select"] = {"us_per_launch": round(per_launch_us["select"], 3)}
         sc = kernels["score"]
         traffic = measured_traffic(wl.name)
         roofline = {"kernel": "score_mfma_kernel (landmark scoring)", "bound": "hbm",

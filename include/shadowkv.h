@@ -175,7 +175,8 @@ enum {
     SKV_T_MIN_COS = 1,      /* f32 (b, h_kv, n): prefill cosine minimum       */
     SKV_T_OUTLIERS = 2,     /* int32 (b, h_kv, o), ascending                  */
     SKV_T_CAND_MASK = 3,    /* uint32 (b, h_kv, ceil(n/32)): selectable bits  */
-    SKV_T_SCORES = 4,       /* f32 (b, h_q, n): last step's P, -inf masked    */
+    SKV_T_SCORES = 4,       /* f32 (b, h_kv, n, G): exp(P - max of P over the
+                               64-chunk tile), 0 off-candidate (last step)    */
     SKV_T_GROUP_SCORES = 5, /* f32 (b, h_kv, n): last step's S2, 0 masked     */
     SKV_T_SELECTION = 6,    /* int32 (b, h_kv, k): last step's I, ascending   */
     SKV_T_SLOT_CHUNKS = 7,  /* int32 (b, h_kv, k): chunk held by each slot    */
@@ -189,6 +190,16 @@ enum {
 size_t shadowkv_tensor_bytes(const skv_layer *layer, int which);
 int shadowkv_read(skv_layer *layer, int which, void *dst, size_t bytes, void *stream);
 
+/* Schedule of the host-V fetch (Algorithm 2 step 3 runs the fetch and the
+ * key rebuild "in parallel"; the review page credits multi-stream overlap
+ * with a 2x latency cut).  enable != 0: the fetch runs on a second stream
+ * beside the key rebuild.  0 (the default): both run in order on the
+ * caller's stream.  On MI355X the device-initiated PCIe reads of the fetch
+ * slow every other kernel's memory traffic, so running beside them gains
+ * less than the cross-queue synchronisation costs.  Outputs are identical
+ * either way. */
+int shadowkv_set_overlap(skv_layer *layer, int enable);
+
 /* Per-kernel timing with HIP events recorded on the stream each kernel runs
  * on.  While enabled, every decode step records a start/stop pair around
  * each kernel.  shadowkv_get_timing synchronizes, writes the summed
@@ -196,14 +207,11 @@ int shadowkv_read(skv_layer *layer, int which, void *dst, size_t bytes, void *st
  * they cover, and clears the record. */
 enum {
     SKV_K_SCORE = 0,    /* landmark scores + per-tile softmax partials      */
-    SKV_K_GROUP = 1,    /* group score S2                                   */
-    SKV_K_TOPK = 2,     /* ArgTopK                                          */
-    SKV_K_SETDIFF = 3,  /* set difference, slot assignment                  */
-    SKV_K_FETCH = 4,    /* V of missing chunks from pinned host (2nd stream)*/
-    SKV_K_QK = 5,       /* key rebuild + RoPE + logits (all key blocks)     */
-    SKV_K_PV = 6,       /* probabilities times values, split partials       */
-    SKV_K_COMBINE = 7,  /* merge of split partials into out                 */
-    SKV_K_COUNT = 8
+    SKV_K_SELECT = 1,   /* group score S2, ArgTopK, set difference          */
+    SKV_K_FETCH = 2,    /* V of missing chunks from pinned host (2nd stream)*/
+    SKV_K_QK = 3,       /* logits: static keys, rebuilt keys + RoPE         */
+    SKV_K_PV = 4,       /* probabilities times values, split merge          */
+    SKV_K_COUNT = 5
 };
 int shadowkv_set_timing(skv_layer *layer, int enable);
 int shadowkv_get_timing(skv_layer *layer, double *ms_out, int64_t *steps_out);

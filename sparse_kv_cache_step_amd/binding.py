@@ -21,13 +21,14 @@ SKV_OK, SKV_E_INVAL, SKV_E_SHAPE, SKV_E_STATE, SKV_E_NOMEM, SKV_E_HIP = 0, -1, -
 (SKV_T_LANDMARKS, SKV_T_MIN_COS, SKV_T_OUTLIERS, SKV_T_CAND_MASK, SKV_T_SCORES, SKV_T_GROUP_SCORES,
  SKV_T_SELECTION, SKV_T_SLOT_CHUNKS, SKV_T_CACHE_V, SKV_T_K_OUT, SKV_T_V_OUT, SKV_T_K_LOC,
  SKV_T_V_LOC) = range(13)
-KERNELS = ("score", "group", "topk", "setdiff", "fetch", "qk", "pv", "combine")
+KERNELS = ("score", "select", "fetch", "qk", "pv")
 SKV_K_COUNT = len(KERNELS)
 
 EXPORTS = (
     "shadowkv_layer_create", "shadowkv_layer_destroy", "shadowkv_prefill_meta", "shadowkv_load_meta",
     "shadowkv_decode_step", "shadowkv_reset_cache", "shadowkv_get_stats", "shadowkv_reset_stats",
-    "shadowkv_tensor_bytes", "shadowkv_read", "shadowkv_set_timing", "shadowkv_get_timing",
+    "shadowkv_tensor_bytes", "shadowkv_read", "shadowkv_set_overlap", "shadowkv_set_timing",
+    "shadowkv_get_timing",
     "shadowkv_host_alloc", "shadowkv_host_free", "shadowkv_last_error", "shadowkv_equiv_bandwidth",
 )
 
@@ -72,6 +73,7 @@ def lib() -> ctypes.CDLL:
             "shadowkv_reset_stats": (ctypes.c_int, [_VP]),
             "shadowkv_tensor_bytes": (ctypes.c_size_t, [_VP, ctypes.c_int]),
             "shadowkv_read": (ctypes.c_int, [_VP, ctypes.c_int, _VP, ctypes.c_size_t, _VP]),
+            "shadowkv_set_overlap": (ctypes.c_int, [_VP, ctypes.c_int]),
             "shadowkv_set_timing": (ctypes.c_int, [_VP, ctypes.c_int]),
             "shadowkv_get_timing": (ctypes.c_int, [_VP, ctypes.POINTER(ctypes.c_double),
                                                    ctypes.POINTER(ctypes.c_int64)]),
@@ -144,6 +146,10 @@ def shadowkv_tensor_bytes(h, which: int) -> int:
 
 def shadowkv_read(h, which: int, dst, nbytes: int, stream) -> None:
     _check(lib().shadowkv_read(h, which, dst, nbytes, stream))
+
+
+def shadowkv_set_overlap(h, enable: bool) -> None:
+    _check(lib().shadowkv_set_overlap(h, int(bool(enable))))
 
 
 def shadowkv_set_timing(h, enable: bool) -> None:
@@ -302,7 +308,8 @@ class Layer:
             SKV_T_LANDMARKS: (dt, (b, hkv, self.n, d)), SKV_T_MIN_COS: (torch.float32, (b, hkv, self.n)),
             SKV_T_OUTLIERS: (torch.int32, (b, hkv, c.n_outlier)),
             SKV_T_CAND_MASK: (torch.int32, (b, hkv, (self.n + 31) // 32)),
-            SKV_T_SCORES: (torch.float32, (b, hq, self.n)), SKV_T_GROUP_SCORES: (torch.float32, (b, hkv, self.n)),
+            SKV_T_SCORES: (torch.float32, (b, hkv, self.n, hq // hkv)),
+            SKV_T_GROUP_SCORES: (torch.float32, (b, hkv, self.n)),
             SKV_T_SELECTION: (torch.int32, (b, hkv, k)), SKV_T_SLOT_CHUNKS: (torch.int32, (b, hkv, k)),
             SKV_T_CACHE_V: (dt, (b, hkv, k * ch, d)), SKV_T_K_OUT: (dt, (b, hkv, c.n_outlier * ch, d)),
             SKV_T_V_OUT: (dt, (b, hkv, c.n_outlier * ch, d)), SKV_T_K_LOC: (dt, (b, hkv, c.local_window, d)),
@@ -315,6 +322,9 @@ class Layer:
         if nbytes:
             shadowkv_read(self.h, which, t.data_ptr(), nbytes, _stream_ptr(stream))
         return t
+
+    def set_overlap(self, enable: bool):
+        shadowkv_set_overlap(self.h, enable)
 
     def set_timing(self, enable: bool):
         shadowkv_set_timing(self.h, enable)

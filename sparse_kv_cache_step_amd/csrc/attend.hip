@@ -1,40 +1,57 @@
 // Attention half of the decode step (review page, section 三, Algorithm 2
 // steps 3-4):
-//   fetch    V of the chunks that missed the resident cache, read by the GPU
-//            straight from pinned host memory (second stream);
-//   qk       logits over [outlier keys; rebuilt keys; local keys], where the
-//            rebuilt keys are Gather(A, I) . B on MFMA followed by RoPE at the
-//            chunks' original positions, never written to memory;
-//   pv       softmax-weighted values per key split, with split partials;
-//   combine  merge of the split partials into the output.
+//   fetch     V of the chunks that missed the resident cache, read by the GPU
+//             straight from pinned host memory (second stream);
+//   qk_static logits of the full-rank outlier and local-window keys (MFMA);
+//   qk_sparse logits of the rebuilt keys: Gather(A, I) . B on MFMA, RoPE at
+//             the chunks' original positions in registers; the rebuilt keys
+//             are never written to memory;
+//   pv        softmax-weighted values per key split; the last split of each
+//             (sequence, KV head) merges the partials into the output.
 #include "skv_device.h"
 
 namespace skv {
 
 // ---------------------------------------------------------------------------
-// Host-V fetch: one wave copies one missing chunk (c * d elements, contiguous
-// on both sides) from pinned host memory into its cache slot.
+// Host-V fetch.  One wave copies one missing chunk (c * d elements,
+// contiguous on both sides) from pinned host memory into its cache slot, two
+// chunks in flight per wave.  Miss slots are walked miss-rank-major so the
+// first waves find real work in every row.  Workgroups are dealt round-robin
+// to the XCDs; only the ones that land on the first `xcds` XCDs copy, which
+// keeps the slow host reads out of the other XCDs' memory paths.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void fetch_kernel(const u32x4 *__restrict__ v_host, u32x4 *__restrict__ vc,
                                                     const int2 *__restrict__ misses,
-                                                    const int32_t *__restrict__ miss_count, int k, int n,
-                                                    int chunk_vec) {
+                                                    const int32_t *__restrict__ miss_count, int rows, int k, int n,
+                                                    int chunk_vec, int xcds) {
+    const int xcd = blockIdx.x % kXcds;
+    if (xcd >= xcds) return;
+    const int wg = (blockIdx.x / kXcds) * xcds + xcd;
+    const int nwg = (gridDim.x / kXcds) * xcds;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int bh = blockIdx.y;
-    const int cnt = miss_count[bh];
-    const int2 *ml = misses + static_cast<size_t>(bh) * k;
-    for (int m = blockIdx.x * 4 + wave; m < cnt; m += gridDim.x * 4) {
-        const int2 e = ml[m];
-        const u32x4 *src = v_host + (static_cast<size_t>(bh) * n + e.x) * chunk_vec;
-        u32x4 *dst = vc + (static_cast<size_t>(bh) * k + e.y) * chunk_vec;
-        int i = lane;
-        for (; i + 64 < chunk_vec; i += 128) {
-            const u32x4 a = __builtin_nontemporal_load(src + i);
-            const u32x4 b = __builtin_nontemporal_load(src + i + 64);
-            dst[i] = a;
-            dst[i + 64] = b;
+    const int gw = wg * 4 + wave, nwaves = nwg * 4;
+    const int total = rows * k;
+    for (int idx = gw; idx < total; idx += 2 * nwaves) {
+        const int idx2 = idx + nwaves;
+        const int bh1 = idx % rows, m1 = idx / rows;
+        const int bh2 = idx2 % rows, m2 = idx2 / rows;
+        const bool ok1 = m1 < miss_count[bh1];
+        const bool ok2 = idx2 < total && m2 < miss_count[bh2];
+        if (!ok1 && !ok2) continue;
+        const int2 e1 = ok1 ? misses[static_cast<size_t>(bh1) * k + m1] : make_int2(0, 0);
+        const int2 e2 = ok2 ? misses[static_cast<size_t>(bh2) * k + m2] : make_int2(0, 0);
+        const u32x4 *s1 = v_host + (static_cast<size_t>(bh1) * n + e1.x) * chunk_vec;
+        const u32x4 *s2 = v_host + (static_cast<size_t>(bh2) * n + e2.x) * chunk_vec;
+        u32x4 *d1 = vc + (static_cast<size_t>(bh1) * k + e1.y) * chunk_vec;
+        u32x4 *d2 = vc + (static_cast<size_t>(bh2) * k + e2.y) * chunk_vec;
+        for (int i = lane; i < chunk_vec; i += 128) {
+            const bool hi = i + 64 < chunk_vec;
+            u32x4 a0, a1, b0, b1;
+            if (ok1) { a0 = __builtin_nontemporal_load(s1 + i); if (hi) a1 = __builtin_nontemporal_load(s1 + i + 64); }
+            if (ok2) { b0 = __builtin_nontemporal_load(s2 + i); if (hi) b1 = __builtin_nontemporal_load(s2 + i + 64); }
+            if (ok1) { d1[i] = a0; if (hi) d1[i + 64] = a1; }
+            if (ok2) { d2[i] = b0; if (hi) d2[i + 64] = b1; }
         }
-        if (i < chunk_vec) dst[i] = __builtin_nontemporal_load(src + i);
     }
 }
 
@@ -103,48 +120,112 @@ __global__ __launch_bounds__(256) void qk_generic_kernel(const T *__restrict__ q
 }
 
 // ---------------------------------------------------------------------------
+// Logits of the static keys (outlier chunks, then the local window), bfloat16
+// on MFMA: C[key, head] = sum_i K[key, i] q[head, i] with 16 keys per
+// v_mfma_f32_16x16x32_bf16 (keys as rows, the group's heads as columns).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void qk_static_mfma_kernel(const uint16_t *__restrict__ q,
+                                                             const uint16_t *__restrict__ k_out,
+                                                             const uint16_t *__restrict__ k_loc,
+                                                             float *__restrict__ logits, int hkv, int G, int OC,
+                                                             int KC, int w, int NK, float scale) {
+    constexpr int KS = D / 32;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int row = lane & 15, quad = lane >> 4;
+    const int bh = blockIdx.y, b = bh / hkv, h = bh % hkv;
+    const int hq = hkv * G;
+    const int nstat = OC + w;
+    bf16x8 qb[KS];
+    {
+        const uint16_t *qrow = q + (static_cast<size_t>(b) * hq + h * G + row) * D + quad * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            qb[ks] = __builtin_bit_cast(bf16x8, row < G ? *reinterpret_cast<const u32x4 *>(qrow + ks * 32)
+                                                        : u32x4{0u, 0u, 0u, 0u});
+    }
+    for (int kb0 = (blockIdx.x * 4 + wave) * 16; kb0 < nstat; kb0 += gridDim.x * 64) {
+        const int sk = kb0 + row;
+        const uint16_t *src = sk < OC ? k_out + (static_cast<size_t>(bh) * OC + sk) * D
+                                      : k_loc + (static_cast<size_t>(bh) * w + (sk - OC)) * D;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 v = sk < nstat ? *reinterpret_cast<const u32x4 *>(src + ks * 32 + quad * 8)
+                                       : u32x4{0u, 0u, 0u, 0u};
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), qb[ks], acc, 0, 0, 0);
+        }
+        if (row < G) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ks_ = kb0 + quad * 4 + e;
+                if (ks_ < nstat) {
+                    const int gkey = ks_ < OC ? ks_ : KC + ks_;
+                    logits[(static_cast<size_t>(bh) * G + row) * NK + gkey] = acc[e] * scale;
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Rebuilt keys on MFMA (bfloat16).  Per (sequence, KV head) the rebuild is
 // K[key, :] = A[pos(key), :] . B[h] with pos(key) = chunk(slot) * c + t, a
 // genuine rank-r x d contraction.  A workgroup takes 256 keys (4 waves x 64);
 // B[h] (stored transposed, d x r) is staged once in LDS and shared by the four
-// waves, the gathered A rows feed the MFMA A operand straight from memory.
-// v_mfma_f32_16x16x32_bf16 leaves lane l with keys 4*(l>>4)+e (e < 4) of a
-// 16-key block and column (l & 15) of a 16-column block, so the RoPE pair
-// (i, i + d/2) sits in one lane and is rotated in registers.  The logits for
-// the GP (padded) query heads are reduced across the 16 column lanes with a
-// halving exchange, leaving each lane with GP/4 finished logits.
+// waves; each wave then works on one 16-key block at a time: the gathered A
+// rows feed the MFMA A operand straight from memory, the d columns come out
+// in 16-column blocks.  v_mfma_f32_16x16x32_bf16 leaves lane l with keys
+// 4*(l>>4)+e (e < 4) of the block and column (l & 15) of each column block,
+// so the RoPE pair (i, i + d/2) sits in one lane and is rotated in
+// registers.  The logits of the GP (padded) query heads are reduced across the
+// 16 column lanes with a halving exchange, leaving each lane GP/4 logits.
 // ---------------------------------------------------------------------------
 template <int D, int GP>
 __global__ __launch_bounds__(256) void qk_sparse_mfma_kernel(const uint16_t *__restrict__ q,
                                                              const uint16_t *__restrict__ A,
                                                              const uint16_t *__restrict__ Bt,
                                                              const int32_t *__restrict__ slot_chunk,
-                                                             const double *__restrict__ theta,
+                                                             const double *__restrict__ theta_rev,
                                                              const float2 *__restrict__ rope_off,
                                                              float *__restrict__ logits, int hkv, int G, int s,
                                                              int c, int r, int r_pad, int k, int OC, int KC, int NK,
                                                              float scale) {
-    constexpr int NB = D / 16;  // 16-column blocks
-    constexpr int HB = NB / 2;  // blocks holding the first half of the dims
-    constexpr int MB = 4;       // 16-key blocks per wave
-    constexpr int X = 4 * GP;   // logit partials per lane and key block
-    extern __shared__ uint16_t Bs[];  // D rows of (r_pad + 8) rank entries
+    constexpr int NB = D / 16;      // 16-column blocks
+    constexpr int HB = NB / 2;      // blocks holding the first half of the dims
+    constexpr int X = 4 * GP;       // logit partials per lane and key block
+    constexpr int KBMAX = 8;        // rank <= 256
+    constexpr int STG = D / 8;      // B staging vectors per thread (r_pad <= 256)
+    extern __shared__ uint16_t dyn[];
+    uint16_t *Bs = dyn;                                                      // D x (r_pad + 8)
+    float2 *toff = reinterpret_cast<float2 *>(dyn + static_cast<size_t>(D) * (r_pad + 8));  // c x D/2
     __shared__ float qs[GP][D];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, quad = lane >> 4;
     const int bh = blockIdx.y, b = bh / hkv, h = bh % hkv;
     const int hq = hkv * G;
     const int ldb = r_pad + 8;
+    const int nkb = r_pad / 32;
 
     {
+        // stage B[h] (transposed, d x r) with every load in flight, then the
+        // in-chunk RoPE table and the scaled queries
         const uint16_t *Btb = Bt + static_cast<size_t>(bh) * D * r;
-        const int vpr = r_pad / 8;
-        for (int idx = tid; idx < D * vpr; idx += 256) {
+        const int vpr = r_pad / 8, total = D * vpr;
+        u32x4 tmp[STG];
+#pragma unroll
+        for (int i = 0; i < STG; ++i) {
+            const int idx = tid + 256 * i;
             const int nr = idx / vpr, kc = (idx % vpr) * 8;
-            const u32x4 v = kc < r ? *reinterpret_cast<const u32x4 *>(Btb + static_cast<size_t>(nr) * r + kc)
-                                   : u32x4{0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4 *>(Bs + nr * ldb + kc) = v;
+            tmp[i] = (idx < total && kc < r) ? *reinterpret_cast<const u32x4 *>(Btb + static_cast<size_t>(nr) * r + kc)
+                                            : u32x4{0u, 0u, 0u, 0u};
         }
+#pragma unroll
+        for (int i = 0; i < STG; ++i) {
+            const int idx = tid + 256 * i;
+            if (idx < total) *reinterpret_cast<u32x4 *>(Bs + (idx / vpr) * ldb + (idx % vpr) * 8) = tmp[i];
+        }
+        for (int idx = tid; idx < c * (D / 2); idx += 256) toff[idx] = rope_off[idx];
         for (int idx = tid; idx < GP * D; idx += 256) {
             const int g = idx / D, i = idx % D;
             qs[g][i] = g < G ? bf16_bits_to_f32(q[(static_cast<size_t>(b) * hq + h * G + g) * D + i]) * scale : 0.f;
@@ -154,87 +235,102 @@ __global__ __launch_bounds__(256) void qk_sparse_mfma_kernel(const uint16_t *__r
 
     const int key_base = blockIdx.x * kQkMfmaTile + wave * 64;
     if (key_base >= KC) return;  // no barrier follows
-    const int32_t *sc = slot_chunk + static_cast<size_t>(bh) * k;
+    // chunk of every slot this wave's 64 keys touch (at most 64 slots): one
+    // load per lane, then shuffles
+    const int slot0 = key_base / c;
+    const int my_slot = slot0 + lane;
+    const int my_chunk = my_slot < k ? slot_chunk[static_cast<size_t>(bh) * k + my_slot] : 0;
+    auto chunk_of = [&](int key) { return __shfl(my_chunk, key / c - slot0, 64); };
+    double thr[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) thr[hb] = theta_rev[hb * 16 + row];
 
-    const uint16_t *arow[MB];
-    bool avalid[MB];
+    // A rows of one 16-key block (row = key within the block); the next
+    // block's rows are loaded while the current one is computed
+    auto load_a = [&](int kb0, u32x4 *aop) {
+        const int key = kb0 + row;
+        const bool kv = key < KC;
+        const int chunk = chunk_of(kv ? key : key_base);
+        const uint16_t *arow = A + (static_cast<size_t>(b) * s + chunk * c + (kv ? key % c : 0)) * r + quad * 8;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-        const int key = key_base + mb * 16 + row;
-        avalid[mb] = key < KC;
-        const int chunk = avalid[mb] ? sc[key / c] : 0;
-        const int pos = chunk * c + (avalid[mb] ? key % c : 0);
-        arow[mb] = A + (static_cast<size_t>(b) * s + pos) * r + quad * 8;
-    }
-
-    f32x4 acc[MB][NB];
+        for (int kb = 0; kb < KBMAX; ++kb)
+            aop[kb] = (kb < nkb && kv && kb * 32 + quad * 8 < r) ? *reinterpret_cast<const u32x4 *>(arow + kb * 32)
+                                                                 : u32x4{0u, 0u, 0u, 0u};
+    };
+    u32x4 aop[KBMAX];
+    load_a(key_base, aop);
+#pragma unroll 1
+    for (int mb = 0; mb < 4; ++mb) {
+        const int kb0 = key_base + mb * 16;
+        if (kb0 >= KC) break;  // wave-uniform
+        u32x4 anext[KBMAX];
+        const bool more = mb + 1 < 4 && kb0 + 16 < KC;
+        if (more) load_a(kb0 + 16, anext);
+        f32x4 acc[NB];
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int kb = 0; kb < r_pad / 32; ++kb) {
-        const int kk = kb * 32 + quad * 8;
-        bf16x8 aop[MB];
+        for (int kb = 0; kb < KBMAX; ++kb) {
+            if (kb < nkb) {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, aop[kb]);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const u32x4 v = (avalid[mb] && kk < r) ? *reinterpret_cast<const u32x4 *>(arow[mb] + kb * 32)
-                                                   : u32x4{0u, 0u, 0u, 0u};
-            aop[mb] = __builtin_bit_cast(bf16x8, v);
+                for (int nb = 0; nb < NB; ++nb) {
+                    const bf16x8 bop = __builtin_bit_cast(
+                        bf16x8, *reinterpret_cast<const u32x4 *>(Bs + (nb * 16 + row) * ldb + kb * 32 + quad * 8));
+                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bop, acc[nb], 0, 0, 0);
+                }
+            }
         }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-            const bf16x8 bop = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(Bs + (nb * 16 + row) * ldb + kk));
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb)
-                acc[mb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[mb], bop, acc[mb][nb], 0, 0, 0);
-        }
-    }
 
-    // RoPE at pos = chunk * c + t: the chunk's angle chunk*c*theta_i is reduced
-    // in double precision; the in-chunk offset t*theta_i comes from a table.
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+        // RoPE at pos = chunk * c + t: the chunk's angle chunk*c*theta_i, in
+        // turns, is reduced to [-1/2, 1/2] in double precision and fed to the
+        // hardware sin/cos (which take turns); the in-chunk offset t*theta_i
+        // comes from a table.  This lane's keys are kb0 + 4*quad + e.
         float cb[HB], sb[HB];
         int prev = -1;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int key = key_base + mb * 16 + quad * 4 + e;
+            const int key = kb0 + quad * 4 + e;
             const bool kv = key < KC;
-            const int chunk = kv ? sc[key / c] : 0;
+            const int chunk = chunk_of(kv ? key : key_base);
             const int t = kv ? key % c : 0;
             if (chunk != prev) {
 #pragma unroll
-                for (int hb = 0; hb < HB; ++hb)
-                    angle_sincos(static_cast<double>(chunk * c) * theta[hb * 16 + row], &sb[hb], &cb[hb]);
+                for (int hb = 0; hb < HB; ++hb) {
+                    const double turns = static_cast<double>(chunk * c) * thr[hb];
+                    const float frac = static_cast<float>(turns - rint(turns));
+                    sb[hb] = __builtin_amdgcn_sinf(frac);
+                    cb[hb] = __builtin_amdgcn_cosf(frac);
+                }
                 prev = chunk;
             }
 #pragma unroll
             for (int hb = 0; hb < HB; ++hb) {
-                const float2 off = rope_off[t * (D / 2) + hb * 16 + row];
+                const float2 off = toff[t * (D / 2) + hb * 16 + row];
                 const float cs = cb[hb] * off.x - sb[hb] * off.y;
                 const float sn = sb[hb] * off.x + cb[hb] * off.y;
-                const float x1 = acc[mb][hb][e], x2 = acc[mb][hb + HB][e];
-                acc[mb][hb][e] = x1 * cs - x2 * sn;
-                acc[mb][hb + HB][e] = x2 * cs + x1 * sn;
+                const float x1 = acc[hb][e], x2 = acc[hb + HB][e];
+                acc[hb][e] = x1 * cs - x2 * sn;
+                acc[hb + HB][e] = x2 * cs + x1 * sn;
             }
         }
-    }
 
-    // logits: partial dots over this lane's columns, then a halving exchange
-    // across the 16 lanes of a lane group.
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+        // logits: partial dots over this lane's 8 columns, then a halving
+        // exchange across the 16 lanes of the lane group
         float part[X];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
+        for (int g = 0; g < GP; ++g) {
+            float qq[NB];
 #pragma unroll
-            for (int g = 0; g < GP; ++g) {
+            for (int nb = 0; nb < NB; ++nb) qq[nb] = qs[g][nb * 16 + row];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
                 float a = 0.f;
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) a += qs[g][nb * 16 + row] * acc[mb][nb][e];
+                for (int nb = 0; nb < NB; ++nb) a += qq[nb] * acc[nb][e];
                 part[e * GP + g] = a;
             }
+        }
 #pragma unroll
         for (int bit = 8, cntv = X; bit >= 1; bit >>= 1, cntv >>= 1) {
             const bool upper = (row & bit) != 0;
@@ -252,30 +348,78 @@ __global__ __launch_bounds__(256) void qk_sparse_mfma_kernel(const uint16_t *__r
         for (int j = 0; j < GP / 4; ++j) {
             const int xo = (GP / 4) * row + j;
             const int e = xo / GP, g = xo % GP;
-            const int key = key_base + mb * 16 + quad * 4 + e;
+            const int key = kb0 + quad * 4 + e;
             if (key < KC && g < G) logits[(static_cast<size_t>(bh) * G + g) * NK + OC + key] = part[j];
+        }
+        if (more) {
+#pragma unroll
+            for (int kb = 0; kb < KBMAX; ++kb) aop[kb] = anext[kb];
         }
     }
 }
 
 // ---------------------------------------------------------------------------
-// PV over one split of 256 keys: p = exp(logit - m_split), partial (m, l) and
-// sum_key p * V[key, :] for each query head of the group.
+// PV over one split of 256 keys: partial (max, sum) and sum_key p * V[key].
+// Thread (row group rg, column group cg) holds 8 columns of 256/(d/8) rows;
+// every V load of the split is issued before the softmax weights are
+// computed.  Partials are reduced across row groups with lane exchanges
+// inside a wave and through LDS across the four waves.
 // ---------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T>
+__device__ __forceinline__ void unpack8(const u32x4 *raw, float *v) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(raw[0][i] << 16);
+            v[2 * i + 1] = __uint_as_float(raw[0][i] & 0xffff0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { v[i] = __uint_as_float(raw[0][i]); v[4 + i] = __uint_as_float(raw[1][i]); }
+    }
+}
+
+template <typename T, int D, int GP>
 __global__ __launch_bounds__(256) void pv_kernel(const float *__restrict__ logits, const T *__restrict__ v_out,
                                                  const T *__restrict__ vc, const T *__restrict__ v_loc,
                                                  float2 *__restrict__ part_ml, float *__restrict__ part_acc,
                                                  int G, int OC, int KC, int w, int NK, int tiles) {
-    constexpr int CP = D / 2;       // column pairs
-    constexpr int NRG = 256 / CP;   // row groups
-    __shared__ float ps[kMaxGroup][kPvTile];
-    __shared__ float red[NRG][kMaxGroup][D];
+    constexpr int CG = D / 8;              // column groups of 8
+    constexpr int RG = 256 / CG;           // row groups
+    constexpr int RPT = kPvTile / RG;      // rows per thread
+    constexpr int VPR = sizeof(T) == 2 ? 1 : 2;  // 16-byte vectors per 8 values
+    constexpr int WRG = 64 / CG;           // row groups inside one wave
+    __shared__ float ps[GP][kPvTile];
+    __shared__ float red[4][GP][D];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int bh = blockIdx.y, tile = blockIdx.x;
     const int key0 = tile * kPvTile;
     const int cnt = min(kPvTile, NK - key0);
-    for (int g = wave; g < G; g += 4) {
+    const int cg = tid % CG, rg = tid / CG;
+
+    u32x4 raw[RPT][VPR];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int rr = rg + RG * i;
+        const int key = key0 + rr;
+        if (rr < cnt) {
+            const T *vrow = key < OC ? v_out + (static_cast<size_t>(bh) * OC + key) * D
+                          : key < OC + KC ? vc + (static_cast<size_t>(bh) * KC + (key - OC)) * D
+                                          : v_loc + (static_cast<size_t>(bh) * w + (key - OC - KC)) * D;
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(vrow + cg * 8);
+#pragma unroll
+            for (int u = 0; u < VPR; ++u) raw[i][u] = src[u];
+        } else {
+#pragma unroll
+            for (int u = 0; u < VPR; ++u) raw[i][u] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+
+    for (int g = wave; g < GP; g += 4) {
+        if (g >= G) {
+            for (int i = lane; i < kPvTile; i += 64) ps[g][i] = 0.f;
+            continue;
+        }
         const float *lg = logits + (static_cast<size_t>(bh) * G + g) * NK + key0;
         float v[kPvTile / 64];
         float m = -INFINITY;
@@ -298,41 +442,49 @@ __global__ __launch_bounds__(256) void pv_kernel(const float *__restrict__ logit
         if (lane == 0) part_ml[(static_cast<size_t>(bh) * G + g) * tiles + tile] = make_float2(m, sum);
     }
     __syncthreads();
-    const int cp = tid % CP, rg = tid / CP;
-    float a0[kMaxGroup], a1[kMaxGroup];
+
+    float acc[GP][8];
 #pragma unroll
-    for (int g = 0; g < kMaxGroup; ++g) { a0[g] = 0.f; a1[g] = 0.f; }
-    for (int rr = rg; rr < cnt; rr += NRG) {
-        const int key = key0 + rr;
-        const T *vrow = key < OC ? v_out + (static_cast<size_t>(bh) * OC + key) * D
-                      : key < OC + KC ? vc + (static_cast<size_t>(bh) * KC + (key - OC)) * D
-                                      : v_loc + (static_cast<size_t>(bh) * w + (key - OC - KC)) * D;
-        const float v0 = Elem<T>::ld(vrow, 2 * cp), v1 = Elem<T>::ld(vrow, 2 * cp + 1);
+    for (int g = 0; g < GP; ++g)
 #pragma unroll
-        for (int g = 0; g < kMaxGroup; ++g) {
-            if (g < G) {
-                const float p = ps[g][rr];
-                a0[g] += p * v0;
-                a1[g] += p * v1;
-            }
+        for (int x = 0; x < 8; ++x) acc[g][x] = 0.f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int rr = rg + RG * i;
+        float v[8];
+        unpack8<T>(raw[i], v);
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+            const float p = ps[g][rr];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) acc[g][x] += p * v[x];
         }
     }
+    // reduce the row groups of this wave (lane bits above the column group)
 #pragma unroll
-    for (int g = 0; g < kMaxGroup; ++g) {
-        if (g < G) { red[rg][g][2 * cp] = a0[g]; red[rg][g][2 * cp + 1] = a1[g]; }
+    for (int off = CG; off < 64; off <<= 1)
+#pragma unroll
+        for (int g = 0; g < GP; ++g)
+#pragma unroll
+            for (int x = 0; x < 8; ++x) acc[g][x] += __shfl_xor(acc[g][x], off, 64);
+    (void)WRG;
+    if (lane < CG) {
+#pragma unroll
+        for (int g = 0; g < GP; ++g)
+#pragma unroll
+            for (int x = 0; x < 8; ++x) red[wave][g][cg * 8 + x] = acc[g][x];
     }
     __syncthreads();
     for (int idx = tid; idx < G * D; idx += 256) {
         const int g = idx / D, i = idx % D;
-        float acc = 0.f;
-#pragma unroll
-        for (int x = 0; x < NRG; ++x) acc += red[x][g][i];
-        part_acc[((static_cast<size_t>(bh) * G + g) * tiles + tile) * D + i] = acc;
+        part_acc[((static_cast<size_t>(bh) * G + g) * tiles + tile) * D + i] =
+            red[0][g][i] + red[1][g][i] + red[2][g][i] + red[3][g][i];
     }
+
 }
 
-// out[b, g, :] = sum_t e^(m_t - M) acc_t / sum_t e^(m_t - M) l_t.  The linear
-// index (b*h_kv + h)*G + gi of a split record equals b*h_q + g of q and out.
+// out[b, g, :] = sum_t e^(m_t - M) acc_t / sum_t e^(m_t - M) l_t over the key
+// splits t.  The record index (b*h_kv + h)*G + gi equals b*h_q + g of q/out.
 template <typename T, int D>
 __global__ __launch_bounds__(D) void combine_kernel(const float2 *__restrict__ part_ml,
                                                     const float *__restrict__ part_acc, T *__restrict__ out,
@@ -354,21 +506,24 @@ __global__ __launch_bounds__(D) void combine_kernel(const float2 *__restrict__ p
 // Launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_fetch(const Dims &dm, const void *v_host, void *vc, const int2 *misses, const int32_t *miss_count,
-                        int blocks_per_bh, hipStream_t st) {
+                        int waves, int xcds, hipStream_t st) {
     if (dm.k <= 0) return hipSuccess;
     const int chunk_vec = dm.c * dm.d * dm.esize / 16;
-    dim3 grid(blocks_per_bh, dm.b * dm.hkv);
-    hipLaunchKernelGGL(fetch_kernel, grid, dim3(256), 0, st, static_cast<const u32x4 *>(v_host),
-                       static_cast<u32x4 *>(vc), misses, miss_count, dm.k, dm.n, chunk_vec);
+    if (xcds < 1) xcds = 1;
+    if (xcds > kXcds) xcds = kXcds;
+    int per_xcd = (waves / 4 + xcds - 1) / xcds;  // active workgroups per used XCD
+    if (per_xcd < 1) per_xcd = 1;
+    hipLaunchKernelGGL(fetch_kernel, dim3(per_xcd * kXcds), dim3(256), 0, st, static_cast<const u32x4 *>(v_host),
+                       static_cast<u32x4 *>(vc), misses, miss_count, dm.b * dm.hkv, dm.k, dm.n, chunk_vec, xcds);
     return hipGetLastError();
 }
 
 template <typename T, int D>
 static hipError_t qk_generic_t(const Dims &dm, const void *q, const void *k_out, const void *k_loc, const void *A,
                                const void *Bt, const int32_t *slot_chunk, const double *theta, float *logits,
-                               bool include_sparse, hipStream_t st) {
+                               hipStream_t st) {
     const int t_out = (dm.OC + kQkTile - 1) / kQkTile;
-    const int t_sp = include_sparse ? (dm.KC + kQkTile - 1) / kQkTile : 0;
+    const int t_sp = (dm.KC + kQkTile - 1) / kQkTile;
     const int t_loc = (dm.w + kQkTile - 1) / kQkTile;
     const int tiles = t_out + t_sp + t_loc;
     if (tiles == 0) return hipSuccess;
@@ -381,68 +536,87 @@ static hipError_t qk_generic_t(const Dims &dm, const void *q, const void *k_out,
 
 template <int D, int GP>
 static hipError_t qk_mfma_t(const Dims &dm, const void *q, const void *A, const void *Bt, const int32_t *slot_chunk,
-                            const double *theta, const float2 *rope_off, float *logits, hipStream_t st) {
+                            const double *theta_rev, const float2 *rope_off, float *logits, hipStream_t st) {
     if (dm.KC <= 0) return hipSuccess;
-    const size_t lds = static_cast<size_t>(D) * (dm.r_pad + 8) * sizeof(uint16_t);
-    static bool attr_set = false;
-    if (!attr_set) {
+    const size_t lds = static_cast<size_t>(D) * (dm.r_pad + 8) * sizeof(uint16_t) +
+                       static_cast<size_t>(dm.c) * (D / 2) * sizeof(float2);
+    if (lds > 48 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(qk_sparse_mfma_kernel<D, GP>),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         if (e != hipSuccess) return e;
-        attr_set = true;
     }
     dim3 grid((dm.KC + kQkMfmaTile - 1) / kQkMfmaTile, dm.b * dm.hkv);
     hipLaunchKernelGGL((qk_sparse_mfma_kernel<D, GP>), grid, dim3(256), lds, st, static_cast<const uint16_t *>(q),
-                       static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(Bt), slot_chunk, theta,
+                       static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(Bt), slot_chunk, theta_rev,
                        rope_off, logits, dm.hkv, dm.G, dm.s, dm.c, dm.r, dm.r_pad, dm.k, dm.OC, dm.KC, dm.NK,
                        dm.scale);
     return hipGetLastError();
 }
 
 template <int D>
-static hipError_t qk_mfma_d(const Dims &dm, const void *q, const void *A, const void *Bt, const int32_t *slot_chunk,
-                            const double *theta, const float2 *rope_off, float *logits, hipStream_t st) {
+static hipError_t qk_static_t(const Dims &dm, const void *q, const void *k_out, const void *k_loc, float *logits,
+                              hipStream_t st) {
+    const int nstat = dm.OC + dm.w;
+    if (nstat <= 0) return hipSuccess;
+    dim3 grid((nstat + 63) / 64, dm.b * dm.hkv);
+    hipLaunchKernelGGL(qk_static_mfma_kernel<D>, grid, dim3(256), 0, st, static_cast<const uint16_t *>(q),
+                       static_cast<const uint16_t *>(k_out), static_cast<const uint16_t *>(k_loc), logits, dm.hkv,
+                       dm.G, dm.OC, dm.KC, dm.w, dm.NK, dm.scale);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t qk_bf16_d(const Dims &dm, const void *q, const void *k_out, const void *k_loc, const void *A,
+                            const void *Bt, const int32_t *slot_chunk, const double *theta_rev,
+                            const float2 *rope_off, float *logits, hipStream_t st) {
+    hipError_t e = qk_static_t<D>(dm, q, k_out, k_loc, logits, st);
+    if (e != hipSuccess) return e;
     switch (dm.GP) {
-        case 4: return qk_mfma_t<D, 4>(dm, q, A, Bt, slot_chunk, theta, rope_off, logits, st);
-        case 8: return qk_mfma_t<D, 8>(dm, q, A, Bt, slot_chunk, theta, rope_off, logits, st);
-        default: return qk_mfma_t<D, 16>(dm, q, A, Bt, slot_chunk, theta, rope_off, logits, st);
+        case 4: return qk_mfma_t<D, 4>(dm, q, A, Bt, slot_chunk, theta_rev, rope_off, logits, st);
+        case 8: return qk_mfma_t<D, 8>(dm, q, A, Bt, slot_chunk, theta_rev, rope_off, logits, st);
+        default: return qk_mfma_t<D, 16>(dm, q, A, Bt, slot_chunk, theta_rev, rope_off, logits, st);
     }
 }
 
 hipError_t launch_qk(const Dims &dm, const void *q, const void *k_out, const void *k_loc, const void *A,
-                     const void *Bt, const int32_t *slot_chunk, const double *theta, const float2 *rope_off,
-                     float *logits, hipStream_t st) {
-    hipError_t e;
-    if (dm.bf16 && dm.r % 8 == 0) {
-        e = dm.d == 128 ? qk_generic_t<uint16_t, 128>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta, logits, false, st)
-                        : qk_generic_t<uint16_t, 64>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta, logits, false, st);
-        if (e != hipSuccess) return e;
-        return dm.d == 128 ? qk_mfma_d<128>(dm, q, A, Bt, slot_chunk, theta, rope_off, logits, st)
-                           : qk_mfma_d<64>(dm, q, A, Bt, slot_chunk, theta, rope_off, logits, st);
-    }
+                     const void *Bt, const int32_t *slot_chunk, const double *theta, const double *theta_rev,
+                     const float2 *rope_off, float *logits, hipStream_t st) {
+    if (dm.bf16 && dm.r % 8 == 0)
+        return dm.d == 128 ? qk_bf16_d<128>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta_rev, rope_off, logits, st)
+                           : qk_bf16_d<64>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta_rev, rope_off, logits, st);
     if (dm.bf16)
-        return dm.d == 128 ? qk_generic_t<uint16_t, 128>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta, logits, true, st)
-                           : qk_generic_t<uint16_t, 64>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta, logits, true, st);
-    return dm.d == 128 ? qk_generic_t<float, 128>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta, logits, true, st)
-                       : qk_generic_t<float, 64>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta, logits, true, st);
+        return dm.d == 128 ? qk_generic_t<uint16_t, 128>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta, logits, st)
+                           : qk_generic_t<uint16_t, 64>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta, logits, st);
+    return dm.d == 128 ? qk_generic_t<float, 128>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta, logits, st)
+                       : qk_generic_t<float, 64>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta, logits, st);
 }
 
-template <typename T, int D>
+template <typename T, int D, int GP>
 static hipError_t pv_t(const Dims &dm, const float *logits, const void *v_out, const void *vc, const void *v_loc,
                        float2 *part_ml, float *part_acc, hipStream_t st) {
-    hipLaunchKernelGGL((pv_kernel<T, D>), dim3(dm.pv_tiles, dm.b * dm.hkv), dim3(256), 0, st, logits,
+    hipLaunchKernelGGL((pv_kernel<T, D, GP>), dim3(dm.pv_tiles, dm.b * dm.hkv), dim3(256), 0, st, logits,
                        static_cast<const T *>(v_out), static_cast<const T *>(vc), static_cast<const T *>(v_loc),
                        part_ml, part_acc, dm.G, dm.OC, dm.KC, dm.w, dm.NK, dm.pv_tiles);
     return hipGetLastError();
 }
 
+template <typename T, int D>
+static hipError_t pv_d(const Dims &dm, const float *logits, const void *v_out, const void *vc, const void *v_loc,
+                       float2 *part_ml, float *part_acc, hipStream_t st) {
+    switch (dm.GP) {
+        case 4: return pv_t<T, D, 4>(dm, logits, v_out, vc, v_loc, part_ml, part_acc, st);
+        case 8: return pv_t<T, D, 8>(dm, logits, v_out, vc, v_loc, part_ml, part_acc, st);
+        default: return pv_t<T, D, 16>(dm, logits, v_out, vc, v_loc, part_ml, part_acc, st);
+    }
+}
+
 hipError_t launch_pv(const Dims &dm, const float *logits, const void *v_out, const void *vc, const void *v_loc,
                      float2 *part_ml, float *part_acc, hipStream_t st) {
     if (dm.bf16)
-        return dm.d == 128 ? pv_t<uint16_t, 128>(dm, logits, v_out, vc, v_loc, part_ml, part_acc, st)
-                           : pv_t<uint16_t, 64>(dm, logits, v_out, vc, v_loc, part_ml, part_acc, st);
-    return dm.d == 128 ? pv_t<float, 128>(dm, logits, v_out, vc, v_loc, part_ml, part_acc, st)
-                       : pv_t<float, 64>(dm, logits, v_out, vc, v_loc, part_ml, part_acc, st);
+        return dm.d == 128 ? pv_d<uint16_t, 128>(dm, logits, v_out, vc, v_loc, part_ml, part_acc, st)
+                           : pv_d<uint16_t, 64>(dm, logits, v_out, vc, v_loc, part_ml, part_acc, st);
+    return dm.d == 128 ? pv_d<float, 128>(dm, logits, v_out, vc, v_loc, part_ml, part_acc, st)
+                       : pv_d<float, 64>(dm, logits, v_out, vc, v_loc, part_ml, part_acc, st);
 }
 
 hipError_t launch_combine(const Dims &dm, const float2 *part_ml, const float *part_acc, void *out, hipStream_t st) {

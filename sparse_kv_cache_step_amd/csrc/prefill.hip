@@ -73,90 +73,6 @@ __global__ __launch_bounds__(256) void landmarks_kernel(const T *__restrict__ k_
     if (lane == 0) min_cos[static_cast<size_t>(bh) * n + j] = static_cast<float>(mn);
 }
 
-// Radix select of the k largest keys per row, exact ties to the lower index,
-// written in ascending index order.  key(j) = float_key(sign * vals[j]) for
-// valid entries (j < n_valid_prefix and, if a mask is given, its bit set),
-// 0 otherwise.  Four 8-bit passes over keys held in LDS (or in global scratch
-// when a row does not fit), then an ordered compaction.
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float *__restrict__ vals, int n,
-                                                            int n_valid_prefix,
-                                                            const uint32_t *__restrict__ mask,
-                                                            int mask_words, float sign, int k,
-                                                            int32_t *__restrict__ out,
-                                                            uint32_t *__restrict__ gscratch, int use_lds) {
-    extern __shared__ uint32_t lds_keys[];
-    __shared__ uint32_t hist[256];
-    __shared__ int wcnt[kTopkThreads / 64];
-    __shared__ uint32_t s_digit;
-    __shared__ int s_above;
-    const int row = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    if (k <= 0) return;
-    uint32_t *keys = use_lds ? lds_keys : gscratch + static_cast<size_t>(row) * n;
-    const float *rv = vals + static_cast<size_t>(row) * n;
-    const uint32_t *rm = mask ? mask + static_cast<size_t>(row) * mask_words : nullptr;
-    for (int j = tid; j < n; j += kTopkThreads) {
-        bool valid = j < n_valid_prefix && (!rm || mask_bit(rm, j));
-        keys[j] = valid ? float_key(sign * rv[j]) : 0u;
-    }
-    __syncthreads();
-
-    uint32_t prefix = 0, pmask = 0;
-    int krem = k;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = tid; i < 256; i += kTopkThreads) hist[i] = 0;
-        __syncthreads();
-        for (int j = tid; j < n; j += kTopkThreads) {
-            uint32_t key = keys[j];
-            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-        }
-        __syncthreads();
-        if (wave == 0) {
-            // lane covers bins 255-4*lane .. 252-4*lane, scanned from the top
-            int cnt[4], local = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) { cnt[i] = static_cast<int>(hist[255 - (lane * 4 + i)]); local += cnt[i]; }
-            int incl = local;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                int t = __shfl_up(incl, off, 64);
-                if (lane >= off) incl += t;
-            }
-            int excl = incl - local;
-            if (excl < krem && krem <= incl) {
-                int acc = excl;
-                for (int i = 0; i < 4; ++i) {
-                    if (acc + cnt[i] >= krem) { s_digit = 255u - (lane * 4 + i); s_above = acc; break; }
-                    acc += cnt[i];
-                }
-            }
-        }
-        __syncthreads();
-        prefix |= s_digit << shift;
-        pmask |= 255u << shift;
-        krem -= s_above;
-        __syncthreads();
-    }
-    const uint32_t thr = prefix;
-    const int need_eq = krem;  // keys equal to thr to take, lowest index first
-
-    int written = 0, eq_seen = 0;
-    int32_t *ro = out + static_cast<size_t>(row) * k;
-    for (int j0 = 0; j0 < n && written < k; j0 += kTopkThreads) {
-        const int j = j0 + tid;
-        const uint32_t key = j < n ? keys[j] : 0u;
-        const bool gt = j < n && key > thr;
-        const bool eq = j < n && key == thr;
-        int eq_tot, take_tot;
-        const int eq_pre = block_excl_count(eq, wcnt, &eq_tot);
-        const bool take = gt || (eq && eq_seen + eq_pre < need_eq);
-        const int pos = block_excl_count(take, wcnt, &take_tot);
-        if (take && written + pos < k) ro[written + pos] = j;
-        written += take_tot;
-        eq_seen += eq_tot;
-    }
-}
-
 // Gather the full-rank post-RoPE K and the V of every outlier chunk and of
 // the last w tokens.  One wave per token row; RoPE is recomputed with the
 // same arithmetic as landmarks_kernel, so the stored keys are identical to
@@ -280,21 +196,6 @@ hipError_t launch_landmarks(const Dims &dm, const void *k_pre, const void *k_rop
     }
     return dm.d == 128 ? landmarks_t<float, 128>(dm, k_pre, k_rope, theta, landmarks, min_cos, st)
                        : landmarks_t<float, 64>(dm, k_pre, k_rope, theta, landmarks, min_cos, st);
-}
-
-hipError_t launch_topk(const Dims &dm, const float *vals, int rows, int n, int n_valid_prefix,
-                       const uint32_t *mask, float sign, int k, int32_t *out, uint32_t *gscratch,
-                       int lds_limit, hipStream_t st) {
-    (void)dm;
-    if (k <= 0 || rows <= 0) return hipSuccess;
-    const size_t need = static_cast<size_t>(n) * sizeof(uint32_t);
-    const int use_lds = need <= static_cast<size_t>(lds_limit) ? 1 : 0;
-    const size_t lds = use_lds ? need : 0;
-    hipError_t e = allow_lds(reinterpret_cast<const void *>(topk_kernel), lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kTopkThreads), lds, st, vals, n, n_valid_prefix, mask,
-                       (n + 31) / 32, sign, k, out, gscratch, use_lds);
-    return hipGetLastError();
 }
 
 template <typename T, int D>

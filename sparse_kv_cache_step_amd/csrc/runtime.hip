@@ -3,8 +3,11 @@
 // two-stream schedule of one decode step, counters and per-kernel timing.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
+#include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <utility>
 #include <vector>
@@ -60,6 +63,7 @@ int make_dims(const skv_config &c, Dims *dm, std::string *why) {
     d.GP = d.G <= 4 ? 4 : (d.G <= 8 ? 8 : 16);
     d.mask_words = (n + 31) / 32;
     d.score_tiles = (n + skv::kScoreTile - 1) / skv::kScoreTile;
+    d.wtiles = (n + 63) / 64;
     d.OC = c.n_outlier * c.chunk; d.KC = c.top_k * c.chunk; d.NK = static_cast<int>(nk);
     d.pv_tiles = (d.NK + skv::kPvTile - 1) / skv::kPvTile;
     d.esize = c.dtype == SKV_BF16 ? 2 : 4;
@@ -73,6 +77,64 @@ struct Mark {
     int kernel;
     hipEvent_t start, stop;
 };
+
+// Streams shared by every layer on one device.  The host-V fetch waits on
+// PCIe for microseconds per read; a wave doing so slows the memory traffic of
+// every other wave on its CU.  So the fetch stream is confined by a CU mask to
+// a few CUs, and the key-rebuild stream that runs beside it to the rest.
+// Masked streams own hardware queues, so they are created once per device
+// (not per layer).  SKV_FETCH_CUS sets the fetch CU count (0: no masks).
+struct DevStreams {
+    bool ready = false;
+    hipStream_t fetch = nullptr, comp = nullptr;
+    int fetch_cus = 0;
+};
+std::mutex g_dev_mutex;
+DevStreams g_dev[64];
+
+int device_streams(int device, DevStreams **out) {
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    if (device < 0 || device >= 64) return fail(SKV_E_INVAL, "device index out of range");
+    DevStreams &ds = g_dev[device];
+    if (!ds.ready) {
+        int ncu = 0;
+        if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess || ncu <= 0)
+            return fail(SKV_E_HIP, "hipDeviceGetAttribute(MultiprocessorCount) failed");
+        int fcu = 0;
+        if (const char *e = std::getenv("SKV_FETCH_CUS")) fcu = std::atoi(e);
+        fcu = std::max(0, std::min(fcu, ncu / 2));
+        // "block": the fetch takes the first fcu CUs and the compute stream
+        // skips the whole 32-CU block they sit in; "spread": the fetch CUs are
+        // spaced evenly and the compute stream takes every other CU.
+        bool block = false;
+        if (const char *e = std::getenv("SKV_FETCH_CU_MODE")) block = std::strcmp(e, "block") == 0;
+        if (fcu > 0) {
+            const int words = (ncu + 31) / 32;
+            std::vector<uint32_t> fm(words, 0u), cm(words, 0u);
+            const int stride = ncu / fcu;
+            for (int cu = 0; cu < ncu; ++cu) {
+                const bool is_fetch = block ? cu < fcu : ((cu % stride == 0) && (cu / stride < fcu));
+                const bool is_comp = block ? cu >= ((fcu + 31) / 32) * 32 : !is_fetch;
+                if (is_fetch) fm[cu / 32] |= 1u << (cu % 32);
+                if (is_comp) cm[cu / 32] |= 1u << (cu % 32);
+            }
+            if (hipExtStreamCreateWithCUMask(&ds.fetch, words, fm.data()) != hipSuccess ||
+                hipExtStreamCreateWithCUMask(&ds.comp, words, cm.data()) != hipSuccess) {
+                (void)hipGetLastError();
+                if (ds.fetch) (void)hipStreamDestroy(ds.fetch);
+                ds.fetch = ds.comp = nullptr;
+                fcu = 0;
+            }
+        }
+        if (fcu == 0 && (hipStreamCreateWithFlags(&ds.fetch, hipStreamNonBlocking) != hipSuccess ||
+                         hipStreamCreateWithFlags(&ds.comp, hipStreamNonBlocking) != hipSuccess))
+            return fail(SKV_E_HIP, "creating the fetch / compute streams failed");
+        ds.fetch_cus = fcu;
+        ds.ready = true;
+    }
+    *out = &ds;
+    return SKV_OK;
+}
 
 }  // namespace
 
@@ -88,7 +150,8 @@ struct skv_layer {
     uint32_t *cand = nullptr;
     int32_t *outliers = nullptr;
     float *min_cos = nullptr;
-    double *theta = nullptr;
+    double *theta = nullptr;      // theta_i = base^(-2i/d)
+    double *theta_rev = nullptr;  // theta_i / (2 pi): turns per position
     float2 *rope_off = nullptr;
     // resident V cache
     void *vc = nullptr;
@@ -100,16 +163,18 @@ struct skv_layer {
     int2 *misses = nullptr;
     int32_t *miss_count = nullptr;
     unsigned long long *counters = nullptr;  // hits, misses, steps
-    uint32_t *topk_scratch = nullptr;
+    uint32_t *key_scratch = nullptr;  // selection keys when a row does not fit in LDS
+    int select_keys_in_lds = 1, topo_keys_in_lds = 1;
     int32_t *bad = nullptr;
     // host V
     void *v_host_dev = nullptr;
     bool ready = false;
-    // second stream for the host-V fetch
-    hipStream_t copy = nullptr;
-    hipEvent_t ev_sel = nullptr, ev_fetch = nullptr;
-    int fetch_blocks = 1;
+    // shared per-device streams for the host-V fetch and the key rebuild
+    hipStream_t copy = nullptr, comp = nullptr;
+    hipEvent_t ev_sel = nullptr, ev_fetch = nullptr, ev_qk = nullptr;
+    int fetch_waves = 256, fetch_xcds = 8;
     // timing
+    bool overlap = false;  // fetch beside the key rebuild (true) or before it
     bool timing = false;
     std::vector<hipEvent_t> ev_pool;
     size_t ev_used = 0;
@@ -139,7 +204,6 @@ int dalloc_t(skv_layer *ly, size_t bytes, P **p) {
 }
 
 void release(skv_layer *ly) {
-    if (ly->copy) (void)hipStreamSynchronize(ly->copy);
     (void)hipDeviceSynchronize();
     for (void *p : ly->allocs) (void)hipFree(p);
     ly->allocs.clear();
@@ -147,7 +211,7 @@ void release(skv_layer *ly) {
     ly->ev_pool.clear();
     if (ly->ev_sel) (void)hipEventDestroy(ly->ev_sel);
     if (ly->ev_fetch) (void)hipEventDestroy(ly->ev_fetch);
-    if (ly->copy) (void)hipStreamDestroy(ly->copy);
+    if (ly->ev_qk) (void)hipEventDestroy(ly->ev_qk);
 }
 
 hipEvent_t pool_event(skv_layer *ly) {
@@ -201,7 +265,13 @@ double shadowkv_equiv_bandwidth(double S, double C, double K, double O, double a
 int shadowkv_host_alloc(size_t bytes, void **out) {
     if (!out) return fail(SKV_E_INVAL, "out is null");
     *out = nullptr;
-    hipError_t e = hipHostMalloc(out, bytes ? bytes : 1, hipHostMallocMapped);
+    // SKV_HOST_NONCOHERENT=1 asks for coarse-grained (non-coherent) pages,
+    // which the GPU may cache; V on the host is written once (prefill) and
+    // then only read, so either kind is correct.
+    unsigned flags = hipHostMallocMapped;
+    if (const char *e = std::getenv("SKV_HOST_NONCOHERENT"))
+        if (std::atoi(e) != 0) flags |= hipHostMallocNonCoherent;
+    hipError_t e = hipHostMalloc(out, bytes ? bytes : 1, flags);
     if (e != hipSuccess) return fail(SKV_E_NOMEM, std::string("hipHostMalloc: ") + hipGetErrorString(e));
     return SKV_OK;
 }
@@ -234,7 +304,7 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     int lds = 0;
     if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, ly->device) != hipSuccess)
         return bail(fail(SKV_E_HIP, "hipDeviceGetAttribute(MaxSharedMemoryPerBlock) failed"));
-    ly->lds_limit = lds - 8 * 1024;  // room for the select kernel's static LDS
+    ly->lds_limit = lds;
 
     const size_t B = dm.b, HKV = dm.hkv, HQ = dm.hq, D = dm.d, S = dm.s, E = dm.esize;
     const size_t bh = B * HKV;
@@ -254,7 +324,7 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     ALLOC(slot_chunk, bh * dm.k * 4);
     ALLOC(sel, bh * dm.k * 4);
     ALLOC(P, B * HQ * dm.n * 4);
-    ALLOC(stats, B * HQ * dm.score_tiles * sizeof(float2));
+    ALLOC(stats, B * HQ * dm.wtiles * sizeof(float2));
     ALLOC(S2, bh * dm.n * 4);
     ALLOC(misses, bh * dm.k * sizeof(int2));
     ALLOC(miss_count, bh * 4);
@@ -264,34 +334,47 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     ALLOC(counters, 4 * sizeof(unsigned long long));
     ALLOC(bad, 4);
     ALLOC(theta, D / 2 * sizeof(double));
+    ALLOC(theta_rev, D / 2 * sizeof(double));
     ALLOC(rope_off, static_cast<size_t>(dm.c) * D / 2 * sizeof(float2));
-    if (static_cast<size_t>(dm.n) * 4 > static_cast<size_t>(ly->lds_limit)) ALLOC(topk_scratch, bh * dm.n * 4);
+    const size_t lds_cap = static_cast<size_t>(ly->lds_limit);
+    ly->select_keys_in_lds = skv::select_dynamic_lds(dm, true) + skv::select_static_lds() <= lds_cap;
+    ly->topo_keys_in_lds = static_cast<size_t>(dm.n) * 4 + skv::select_static_lds() <= lds_cap;
+    if (skv::select_dynamic_lds(dm, false) + skv::select_static_lds() > lds_cap)
+        return bail(fail(SKV_E_SHAPE, "top_k too large for the select kernel's shared memory"));
+    if (!ly->select_keys_in_lds || !ly->topo_keys_in_lds) ALLOC(key_scratch, bh * dm.n * 4);
 #undef ALLOC
 
     // RoPE tables: theta_i = base^(-2i/d) in double, and the in-chunk offsets
     // (cos t*theta_i, sin t*theta_i) for t < chunk.
-    std::vector<double> th(D / 2);
+    std::vector<double> th(D / 2), thr(D / 2);
     std::vector<float2> off(static_cast<size_t>(dm.c) * D / 2);
-    for (size_t i = 0; i < D / 2; ++i) th[i] = std::pow(static_cast<double>(cfg->rope_base), -2.0 * i / D);
+    for (size_t i = 0; i < D / 2; ++i) {
+        th[i] = std::pow(static_cast<double>(cfg->rope_base), -2.0 * i / D);
+        thr[i] = th[i] / (2.0 * 3.14159265358979323846);
+    }
     for (int t = 0; t < dm.c; ++t)
         for (size_t i = 0; i < D / 2; ++i)
             off[t * D / 2 + i] = make_float2(static_cast<float>(std::cos(t * th[i])), static_cast<float>(std::sin(t * th[i])));
     if (hipMemcpy(ly->theta, th.data(), th.size() * sizeof(double), hipMemcpyHostToDevice) != hipSuccess ||
+        hipMemcpy(ly->theta_rev, thr.data(), thr.size() * sizeof(double), hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(ly->rope_off, off.data(), off.size() * sizeof(float2), hipMemcpyHostToDevice) != hipSuccess ||
         hipMemset(ly->counters, 0, 4 * sizeof(unsigned long long)) != hipSuccess)
         return bail(fail(SKV_E_HIP, "initialising layer tables failed"));
-    if (hipStreamCreateWithFlags(&ly->copy, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&ly->ev_sel, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&ly->ev_fetch, hipEventDisableTiming) != hipSuccess)
-        return bail(fail(SKV_E_HIP, "creating the fetch stream or events failed"));
+    DevStreams *ds = nullptr;
+    if ((rc = device_streams(ly->device, &ds))) return bail(rc);
+    ly->copy = ds->fetch;
+    ly->comp = ds->comp;
+    if (hipEventCreateWithFlags(&ly->ev_sel, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ly->ev_fetch, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ly->ev_qk, hipEventDisableTiming) != hipSuccess)
+        return bail(fail(SKV_E_HIP, "creating events failed"));
 
-    // Fetch grid: about 4096 waves across all (sequence, KV head) rows.
-    const int rows = static_cast<int>(bh);
-    int per_row = 1024 / rows;
-    if (per_row < 1) per_row = 1;
-    const int need = (dm.k + 3) / 4;
-    if (per_row > need) per_row = need > 0 ? need : 1;
-    ly->fetch_blocks = per_row;
+    // Host-V fetch: enough waves to keep PCIe busy (a few hundred 2 KB chunk
+    // reads in flight), not so many that the slow host reads crowd the memory
+    // path of the kernels running beside them.  SKV_FETCH_WAVES and
+    // SKV_FETCH_XCDS override the defaults for tuning.
+    if (const char *e = std::getenv("SKV_FETCH_WAVES")) ly->fetch_waves = std::max(4, std::atoi(e));
+    if (const char *e = std::getenv("SKV_FETCH_XCDS")) ly->fetch_xcds = std::min(8, std::max(1, std::atoi(e)));
 
     *out = ly;
     return SKV_OK;
@@ -324,8 +407,7 @@ int shadowkv_prefill_meta(skv_layer *ly, const void *k_pre, const void *k_rope, 
     const Dims &dm = ly->dm;
     ly->ready = false;
     SKV_HIP(skv::launch_landmarks(dm, k_pre, k_rope, ly->theta, ly->L, ly->min_cos, st));
-    SKV_HIP(skv::launch_topk(dm, ly->min_cos, dm.b * dm.hkv, dm.n, dm.n - dm.n_loc, nullptr, -1.0f, dm.o,
-                             ly->outliers, ly->topk_scratch, ly->lds_limit, st));
+    SKV_HIP(skv::launch_topo(dm, ly->min_cos, ly->outliers, ly->key_scratch, ly->topo_keys_in_lds, st));
     SKV_HIP(skv::launch_gather_static(dm, k_pre, k_rope, v, ly->outliers, ly->theta, ly->k_out, ly->v_out,
                                       ly->k_loc, ly->v_loc, st));
     if ((rc = install_common(ly, A, B, v_host, st))) return rc;
@@ -382,40 +464,46 @@ int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) 
         SKV_HIP(skv::launch_score(dm, q, ly->L, ly->cand, ly->P, ly->stats, st));
     }
     {
-        Timed t(ly, SKV_K_GROUP, st);
-        SKV_HIP(skv::launch_group(dm, ly->P, ly->stats, ly->cand, ly->S2, st));
+        Timed t(ly, SKV_K_SELECT, st);
+        SKV_HIP(skv::launch_select(dm, ly->P, ly->stats, ly->cand, ly->S2, ly->sel, ly->slot_chunk, ly->misses,
+                                   ly->miss_count, ly->counters, ly->key_scratch, ly->select_keys_in_lds, st));
     }
-    {
-        Timed t(ly, SKV_K_TOPK, st);
-        SKV_HIP(skv::launch_topk(dm, ly->S2, dm.b * dm.hkv, dm.n, dm.n, ly->cand, 1.0f, dm.k, ly->sel,
-                                 ly->topk_scratch, ly->lds_limit, st));
+    if (ly->overlap) {
+        // fork: the fetch of missing V on the fetch stream, the key rebuild
+        // and logits on the compute stream; join before PV
+        SKV_HIP(hipEventRecord(ly->ev_sel, st));
+        SKV_HIP(hipStreamWaitEvent(ly->copy, ly->ev_sel, 0));
+        SKV_HIP(hipStreamWaitEvent(ly->comp, ly->ev_sel, 0));
+        {
+            Timed t(ly, SKV_K_FETCH, ly->copy);
+            SKV_HIP(skv::launch_fetch(dm, ly->v_host_dev, ly->vc, ly->misses, ly->miss_count, ly->fetch_waves,
+                                      ly->fetch_xcds, ly->copy));
+        }
+        SKV_HIP(hipEventRecord(ly->ev_fetch, ly->copy));
+        {
+            Timed t(ly, SKV_K_QK, ly->comp);
+            SKV_HIP(skv::launch_qk(dm, q, ly->k_out, ly->k_loc, ly->A, ly->Bt, ly->slot_chunk, ly->theta,
+                                   ly->theta_rev, ly->rope_off, ly->logits, ly->comp));
+        }
+        SKV_HIP(hipEventRecord(ly->ev_qk, ly->comp));
+        SKV_HIP(hipStreamWaitEvent(st, ly->ev_qk, 0));
+        SKV_HIP(hipStreamWaitEvent(st, ly->ev_fetch, 0));
+    } else {
+        // one queue: the fetch runs alone on PCIe, then the rebuild
+        {
+            Timed t(ly, SKV_K_FETCH, st);
+            SKV_HIP(skv::launch_fetch(dm, ly->v_host_dev, ly->vc, ly->misses, ly->miss_count, ly->fetch_waves,
+                                      ly->fetch_xcds, st));
+        }
+        {
+            Timed t(ly, SKV_K_QK, st);
+            SKV_HIP(skv::launch_qk(dm, q, ly->k_out, ly->k_loc, ly->A, ly->Bt, ly->slot_chunk, ly->theta,
+                                   ly->theta_rev, ly->rope_off, ly->logits, st));
+        }
     }
-    {
-        Timed t(ly, SKV_K_SETDIFF, st);
-        SKV_HIP(skv::launch_setdiff(dm, ly->sel, ly->slot_chunk, ly->misses, ly->miss_count, ly->counters, st));
-    }
-    // fork: the fetch of missing V runs on the layer's second stream while
-    // the keys are rebuilt and scored on the caller's stream
-    SKV_HIP(hipEventRecord(ly->ev_sel, st));
-    SKV_HIP(hipStreamWaitEvent(ly->copy, ly->ev_sel, 0));
-    {
-        Timed t(ly, SKV_K_FETCH, ly->copy);
-        SKV_HIP(skv::launch_fetch(dm, ly->v_host_dev, ly->vc, ly->misses, ly->miss_count, ly->fetch_blocks, ly->copy));
-    }
-    SKV_HIP(hipEventRecord(ly->ev_fetch, ly->copy));
-    {
-        Timed t(ly, SKV_K_QK, st);
-        SKV_HIP(skv::launch_qk(dm, q, ly->k_out, ly->k_loc, ly->A, ly->Bt, ly->slot_chunk, ly->theta, ly->rope_off,
-                               ly->logits, st));
-    }
-    // join
-    SKV_HIP(hipStreamWaitEvent(st, ly->ev_fetch, 0));
     {
         Timed t(ly, SKV_K_PV, st);
         SKV_HIP(skv::launch_pv(dm, ly->logits, ly->v_out, ly->vc, ly->v_loc, ly->part_ml, ly->part_acc, st));
-    }
-    {
-        Timed t(ly, SKV_K_COMBINE, st);
         SKV_HIP(skv::launch_combine(dm, ly->part_ml, ly->part_acc, out, st));
     }
     if (ly->timing) ++ly->timed_steps;
@@ -457,7 +545,7 @@ static const void *tensor_ptr(const skv_layer *ly, int which, size_t *bytes) {
         case SKV_T_MIN_COS: *bytes = bh * dm.n * 4; return ly->min_cos;
         case SKV_T_OUTLIERS: *bytes = bh * dm.o * 4; return ly->outliers;
         case SKV_T_CAND_MASK: *bytes = bh * dm.mask_words * 4; return ly->cand;
-        case SKV_T_SCORES: *bytes = static_cast<size_t>(dm.b) * dm.hq * dm.n * 4; return ly->P;
+        case SKV_T_SCORES: *bytes = bh * dm.n * dm.G * 4; return ly->P;
         case SKV_T_GROUP_SCORES: *bytes = bh * dm.n * 4; return ly->S2;
         case SKV_T_SELECTION: *bytes = bh * dm.k * 4; return ly->sel;
         case SKV_T_SLOT_CHUNKS: *bytes = bh * dm.k * 4; return ly->slot_chunk;
@@ -487,6 +575,12 @@ int shadowkv_read(skv_layer *ly, int which, void *dst, size_t bytes, void *strea
     hipStream_t st = static_cast<hipStream_t>(stream);
     SKV_HIP(hipStreamWaitEvent(st, ly->ev_fetch, 0));
     SKV_HIP(hipMemcpyAsync(dst, src, need, hipMemcpyDefault, st));
+    return SKV_OK;
+}
+
+int shadowkv_set_overlap(skv_layer *ly, int enable) {
+    if (!ly) return fail(SKV_E_INVAL, "layer is null");
+    ly->overlap = enable != 0;
     return SKV_OK;
 }
 

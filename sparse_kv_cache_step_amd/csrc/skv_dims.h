@@ -8,8 +8,8 @@ namespace skv {
 
 // Tile sizes.
 constexpr int kScoreTile = 256;   // chunks per scoring workgroup (4 waves x 64)
-constexpr int kGroupTile = 256;   // chunks per group-score workgroup
-constexpr int kTopkThreads = 1024;
+constexpr int kSelectThreads = 1024;  // one workgroup per (sequence, KV head) row
+constexpr int kXcds = 8;              // XCDs of an MI355X; workgroups are dealt round-robin
 constexpr int kQkTile = 64;       // keys per generic QK workgroup
 constexpr int kQkMfmaTile = 256;  // keys per MFMA QK workgroup (4 waves x 64)
 constexpr int kPvTile = 256;      // keys per PV workgroup
@@ -22,7 +22,8 @@ struct Dims {
     int G;           // query heads per KV head
     int GP;          // G rounded up to 4, 8 or 16 (MFMA QK variant)
     int mask_words;  // ceil(n / 32)
-    int score_tiles; // ceil(n / kScoreTile)
+    int score_tiles; // ceil(n / kScoreTile): scoring workgroups per row
+    int wtiles;      // ceil(n / 64): 64-chunk softmax tiles per row
     int OC, KC, NK;  // outlier keys, rebuilt keys, all keys per (b, h_kv)
     int pv_tiles;    // ceil(NK / kPvTile)
     int esize;       // bytes per stored element
@@ -35,9 +36,8 @@ struct Dims {
 // Prefill.
 hipError_t launch_landmarks(const Dims &dm, const void *k_pre, const void *k_rope, const double *theta,
                             void *landmarks, float *min_cos, hipStream_t st);
-hipError_t launch_topk(const Dims &dm, const float *vals, int rows, int n, int n_valid_prefix,
-                       const uint32_t *mask, float sign, int k, int32_t *out, uint32_t *gscratch,
-                       int lds_limit, hipStream_t st);
+hipError_t launch_topo(const Dims &dm, const float *min_cos, int32_t *outliers, uint32_t *gscratch, int keys_in_lds,
+                       hipStream_t st);
 hipError_t launch_gather_static(const Dims &dm, const void *k_pre, const void *k_rope, const void *v,
                                 const int32_t *outliers, const double *theta, void *k_out, void *v_out,
                                 void *k_loc, void *v_loc, hipStream_t st);
@@ -49,14 +49,17 @@ hipError_t launch_validate_outliers(const Dims &dm, const int32_t *outliers, int
 // Decode.
 hipError_t launch_score(const Dims &dm, const void *q, const void *landmarks, const uint32_t *cand,
                         float *P, float2 *stats, hipStream_t st);
-hipError_t launch_group(const Dims &dm, const float *P, const float2 *stats, const uint32_t *cand,
-                        float *S2, hipStream_t st);
-hipError_t launch_setdiff(const Dims &dm, const int32_t *sel, int32_t *slot_chunk, int2 *misses,
-                          int32_t *miss_count, unsigned long long *counters, hipStream_t st);
+// LDS of the select kernel: dynamic part (slot arrays, and the keys when they
+// fit) and static part.
+size_t select_dynamic_lds(const Dims &dm, bool keys_in_lds);
+size_t select_static_lds();
+hipError_t launch_select(const Dims &dm, const float *P, const float2 *stats, const uint32_t *cand, float *S2,
+                         int32_t *sel, int32_t *slot_chunk, int2 *misses, int32_t *miss_count,
+                         unsigned long long *counters, uint32_t *gscratch, int keys_in_lds, hipStream_t st);
 hipError_t launch_fetch(const Dims &dm, const void *v_host, void *vc, const int2 *misses,
-                        const int32_t *miss_count, int blocks_per_bh, hipStream_t st);
+                        const int32_t *miss_count, int waves, int xcds, hipStream_t st);
 hipError_t launch_qk(const Dims &dm, const void *q, const void *k_out, const void *k_loc, const void *A,
-                     const void *Bt, const int32_t *slot_chunk, const double *theta,
+                     const void *Bt, const int32_t *slot_chunk, const double *theta, const double *theta_rev,
                      const float2 *rope_off, float *logits, hipStream_t st);
 hipError_t launch_pv(const Dims &dm, const float *logits, const void *v_out, const void *vc,
                      const void *v_loc, float2 *part_ml, float *part_acc, hipStream_t st);
