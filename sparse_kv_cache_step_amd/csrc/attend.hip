@@ -1,56 +1,78 @@
 // Attention half of the decode step (review page, section 三, Algorithm 2
 // steps 3-4):
 //   fetch     V of the chunks that missed the resident cache, read by the GPU
-//             straight from pinned host memory (second stream);
+//             straight from pinned host memory;
 //   qk_static logits of the full-rank outlier and local-window keys (MFMA);
 //   qk_sparse logits of the rebuilt keys: Gather(A, I) . B on MFMA, RoPE at
 //             the chunks' original positions in registers; the rebuilt keys
 //             are never written to memory;
 //   pv        softmax-weighted values per key split; the last split of each
 //             (sequence, KV head) merges the partials into the output.
+#include <algorithm>
+
 #include "skv_device.h"
 
 namespace skv {
 
 // ---------------------------------------------------------------------------
-// Host-V fetch.  One wave copies one missing chunk (c * d elements,
-// contiguous on both sides) from pinned host memory into its cache slot, two
-// chunks in flight per wave.  Miss slots are walked miss-rank-major so the
-// first waves find real work in every row.  Workgroups are dealt round-robin
-// to the XCDs; only the ones that land on the first `xcds` XCDs copy, which
-// keeps the slow host reads out of the other XCDs' memory paths.
+// Host-V fetch.  The select kernel leaves, per (sequence, KV head) row, a
+// compacted list of the chunks that missed the resident cache and the slots
+// freed for them.  Each workgroup first forms the prefix sums of the per-row
+// miss counts in LDS; its waves then walk the global miss index (rows one
+// after another), find each miss's row by binary search, and copy the missing
+// chunk (c * d elements, contiguous on both sides) from pinned host memory
+// into its cache slot, every load of the chunk in flight before the stores.
+// Only real misses are visited, so the PCIe reads are issued back to back.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void fetch_kernel(const u32x4 *__restrict__ v_host, u32x4 *__restrict__ vc,
                                                     const int2 *__restrict__ misses,
                                                     const int32_t *__restrict__ miss_count, int rows, int k, int n,
-                                                    int chunk_vec, int xcds) {
-    const int xcd = blockIdx.x % kXcds;
-    if (xcd >= xcds) return;
-    const int wg = (blockIdx.x / kXcds) * xcds + xcd;
-    const int nwg = (gridDim.x / kXcds) * xcds;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int gw = wg * 4 + wave, nwaves = nwg * 4;
-    const int total = rows * k;
-    for (int idx = gw; idx < total; idx += 2 * nwaves) {
-        const int idx2 = idx + nwaves;
-        const int bh1 = idx % rows, m1 = idx / rows;
-        const int bh2 = idx2 % rows, m2 = idx2 / rows;
-        const bool ok1 = m1 < miss_count[bh1];
-        const bool ok2 = idx2 < total && m2 < miss_count[bh2];
-        if (!ok1 && !ok2) continue;
-        const int2 e1 = ok1 ? misses[static_cast<size_t>(bh1) * k + m1] : make_int2(0, 0);
-        const int2 e2 = ok2 ? misses[static_cast<size_t>(bh2) * k + m2] : make_int2(0, 0);
-        const u32x4 *s1 = v_host + (static_cast<size_t>(bh1) * n + e1.x) * chunk_vec;
-        const u32x4 *s2 = v_host + (static_cast<size_t>(bh2) * n + e2.x) * chunk_vec;
-        u32x4 *d1 = vc + (static_cast<size_t>(bh1) * k + e1.y) * chunk_vec;
-        u32x4 *d2 = vc + (static_cast<size_t>(bh2) * k + e2.y) * chunk_vec;
-        for (int i = lane; i < chunk_vec; i += 128) {
-            const bool hi = i + 64 < chunk_vec;
-            u32x4 a0, a1, b0, b1;
-            if (ok1) { a0 = __builtin_nontemporal_load(s1 + i); if (hi) a1 = __builtin_nontemporal_load(s1 + i + 64); }
-            if (ok2) { b0 = __builtin_nontemporal_load(s2 + i); if (hi) b1 = __builtin_nontemporal_load(s2 + i + 64); }
-            if (ok1) { d1[i] = a0; if (hi) d1[i + 64] = a1; }
-            if (ok2) { d2[i] = b0; if (hi) d2[i + 64] = b1; }
+                                                    int chunk_vec) {
+    extern __shared__ int pre[];  // rows + 1 prefix sums
+    __shared__ int wsum[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int carry = 0;
+    for (int base = 0; base < rows; base += 256) {
+        const int r = base + tid;
+        int v = r < rows ? miss_count[r] : 0;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int t = __shfl_up(v, off, 64);
+            if (lane >= off) v += t;
+        }
+        if (lane == 63) wsum[wave] = v;
+        __syncthreads();
+        int before = carry;
+        for (int w = 0; w < wave; ++w) before += wsum[w];
+        if (r < rows) pre[r + 1] = before + v;
+        carry += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        __syncthreads();
+    }
+    if (tid == 0) pre[0] = 0;
+    __syncthreads();
+    const int total = pre[rows];
+    const int gw = blockIdx.x * 4 + wave, nw = gridDim.x * 4;
+    for (int g = gw; g < total; g += nw) {
+        int lo = 0, hi = rows - 1;  // the row r with pre[r] <= g < pre[r + 1]
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pre[mid] <= g) lo = mid; else hi = mid - 1;
+        }
+        const int2 e = misses[static_cast<size_t>(lo) * k + (g - pre[lo])];
+        const u32x4 *src = v_host + (static_cast<size_t>(lo) * n + e.x) * chunk_vec;
+        u32x4 *dst = vc + (static_cast<size_t>(lo) * k + e.y) * chunk_vec;
+        for (int i0 = 0; i0 < chunk_vec; i0 += 256) {
+            u32x4 t[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + u * 64 + lane;
+                if (i < chunk_vec) t[u] = __builtin_nontemporal_load(src + i);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int i = i0 + u * 64 + lane;
+                if (i < chunk_vec) dst[i] = t[u];
+            }
         }
     }
 }
@@ -173,43 +195,56 @@ __global__ __launch_bounds__(256) void qk_static_mfma_kernel(const uint16_t *__r
 // K[key, :] = A[pos(key), :] . B[h] with pos(key) = chunk(slot) * c + t, a
 // genuine rank-r x d contraction.  A workgroup takes 256 keys (4 waves x 64);
 // B[h] (stored transposed, d x r) is staged once in LDS and shared by the four
-// waves; each wave then works on one 16-key block at a time: the gathered A
-// rows feed the MFMA A operand straight from memory, the d columns come out
-// in 16-column blocks.  v_mfma_f32_16x16x32_bf16 leaves lane l with keys
-// 4*(l>>4)+e (e < 4) of the block and column (l & 15) of each column block,
-// so the RoPE pair (i, i + d/2) sits in one lane and is rotated in
-// registers.  The logits of the GP (padded) query heads are reduced across the
-// 16 column lanes with a halving exchange, leaving each lane GP/4 logits.
+// waves; each wave then works on one 16-key block at a time and computes the
+// block transposed, K^T[dim, key] = sum_r Bt[dim, r] A[key, r]: the staged
+// Bt rows are the MFMA A operand and the gathered A rows, read straight from
+// memory, the B operand.  v_mfma_f32_16x16x32_bf16 then leaves lane l with
+// key (l & 15) of the block and dims 16*nb + 4*(l >> 4) + e (e < 4) of every
+// 16-dim block nb, so the RoPE pair (i, i + d/2) sits in one lane and each
+// lane rotates its own key at its own position.  A lane's partial logits over
+// its 32 (or 16) dims are summed over the four lane groups by two permlane
+// swaps, which leave lane l with the logits of heads (GP/4)*(l >> 4) + x.
 // ---------------------------------------------------------------------------
-template <int D, int GP>
+// v_permlane32_swap exchanges the upper 32 lanes of its first operand with the
+// lower 32 lanes of its second, so the sum of the two results holds, in lanes
+// 0-31, lo(l) + lo(l + 32) and, in lanes 32-63, hi(l - 32) + hi(l).
+__device__ __forceinline__ float swap_sum32(float lo, float hi) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// v_permlane16_swap exchanges the odd 16-lane rows of its first operand with
+// the even rows of its second: rows 0 and 2 end with lo summed over the row
+// pair, rows 1 and 3 with hi summed over it.
+__device__ __forceinline__ float swap_sum16(float lo, float hi) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int D, int GP, int NKB>
 __global__ __launch_bounds__(256) void qk_sparse_mfma_kernel(const uint16_t *__restrict__ q,
                                                              const uint16_t *__restrict__ A,
                                                              const uint16_t *__restrict__ Bt,
                                                              const int32_t *__restrict__ slot_chunk,
                                                              const double *__restrict__ theta_rev,
-                                                             const float2 *__restrict__ rope_off,
                                                              float *__restrict__ logits, int hkv, int G, int s,
                                                              int c, int r, int r_pad, int k, int OC, int KC, int NK,
                                                              float scale) {
-    constexpr int NB = D / 16;      // 16-column blocks
+    constexpr int NB = D / 16;      // 16-dim blocks
     constexpr int HB = NB / 2;      // blocks holding the first half of the dims
-    constexpr int X = 4 * GP;       // logit partials per lane and key block
-    constexpr int KBMAX = 8;        // rank <= 256
+    constexpr int HPL = GP / 4;     // heads per lane after the reduction
     constexpr int STG = D / 8;      // B staging vectors per thread (r_pad <= 256)
     extern __shared__ uint16_t dyn[];
-    uint16_t *Bs = dyn;                                                      // D x (r_pad + 8)
-    float2 *toff = reinterpret_cast<float2 *>(dyn + static_cast<size_t>(D) * (r_pad + 8));  // c x D/2
+    uint16_t *Bs = dyn;             // D x (r_pad + 8)
     __shared__ float qs[GP][D];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, quad = lane >> 4;
     const int bh = blockIdx.y, b = bh / hkv, h = bh % hkv;
     const int hq = hkv * G;
     const int ldb = r_pad + 8;
-    const int nkb = r_pad / 32;
 
     {
         // stage B[h] (transposed, d x r) with every load in flight, then the
-        // in-chunk RoPE table and the scaled queries
+        // scaled queries
         const uint16_t *Btb = Bt + static_cast<size_t>(bh) * D * r;
         const int vpr = r_pad / 8, total = D * vpr;
         u32x4 tmp[STG];
@@ -225,7 +260,6 @@ __global__ __launch_bounds__(256) void qk_sparse_mfma_kernel(const uint16_t *__r
             const int idx = tid + 256 * i;
             if (idx < total) *reinterpret_cast<u32x4 *>(Bs + (idx / vpr) * ldb + (idx % vpr) * 8) = tmp[i];
         }
-        for (int idx = tid; idx < c * (D / 2); idx += 256) toff[idx] = rope_off[idx];
         for (int idx = tid; idx < GP * D; idx += 256) {
             const int g = idx / D, i = idx % D;
             qs[g][i] = g < G ? bf16_bits_to_f32(q[(static_cast<size_t>(b) * hq + h * G + g) * D + i]) * scale : 0.f;
@@ -240,121 +274,98 @@ __global__ __launch_bounds__(256) void qk_sparse_mfma_kernel(const uint16_t *__r
     const int slot0 = key_base / c;
     const int my_slot = slot0 + lane;
     const int my_chunk = my_slot < k ? slot_chunk[static_cast<size_t>(bh) * k + my_slot] : 0;
-    auto chunk_of = [&](int key) { return __shfl(my_chunk, key / c - slot0, 64); };
-    double thr[HB];
+    // rotation rates (turns per position) of this lane's dims 16*hb + 4*quad + e
+    double thr[HB][4];
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb) thr[hb] = theta_rev[hb * 16 + row];
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) thr[hb][e] = theta_rev[hb * 16 + quad * 4 + e];
 
-    // A rows of one 16-key block (row = key within the block); the next
-    // block's rows are loaded while the current one is computed
-    auto load_a = [&](int kb0, u32x4 *aop) {
+    // Gathered A row of this lane's key in a 16-key block, 8 rank values per
+    // 32-wide rank block, through a buffer resource over this sequence's A:
+    // keys past KC, rank columns past r and the prefetch after the last block
+    // read zeros without a memory access, so no branch surrounds a load and
+    // the next block's rows stay in flight while one block is computed.
+    const Rsrc ar = make_rsrc(A + static_cast<size_t>(b) * s * r, static_cast<uint32_t>(s) * r * 2);
+    const Rsrc lr = make_rsrc(logits + static_cast<size_t>(bh) * G * NK, static_cast<uint32_t>(G) * NK * 4);
+    auto load_a = [&](int kb0, bool on, u32x4 *aop, int &pos) {
         const int key = kb0 + row;
-        const bool kv = key < KC;
-        const int chunk = chunk_of(kv ? key : key_base);
-        const uint16_t *arow = A + (static_cast<size_t>(b) * s + chunk * c + (kv ? key % c : 0)) * r + quad * 8;
+        const bool kv = on && key < KC;
+        const int kk = key < KC ? key : key_base;
+        const int chunk = __shfl(my_chunk, kk / c - slot0, 64);
+        pos = chunk * c + kk % c;
+        const int base = (pos * r + quad * 8) * 2;
 #pragma unroll
-        for (int kb = 0; kb < KBMAX; ++kb)
-            aop[kb] = (kb < nkb && kv && kb * 32 + quad * 8 < r) ? *reinterpret_cast<const u32x4 *>(arow + kb * 32)
-                                                                 : u32x4{0u, 0u, 0u, 0u};
+        for (int kb = 0; kb < NKB; ++kb)
+            aop[kb] = buf_ld128(ar, kv && kb * 32 + quad * 8 < r ? base + kb * 64 : kOob);
     };
-    u32x4 aop[KBMAX];
-    load_a(key_base, aop);
+    u32x4 aop[NKB];
+    int pos;
+    load_a(key_base, true, aop, pos);
 #pragma unroll 1
     for (int mb = 0; mb < 4; ++mb) {
         const int kb0 = key_base + mb * 16;
         if (kb0 >= KC) break;  // wave-uniform
-        u32x4 anext[KBMAX];
+        u32x4 anext[NKB];
+        int pos_next = 0;
         const bool more = mb + 1 < 4 && kb0 + 16 < KC;
-        if (more) load_a(kb0 + 16, anext);
+        load_a(kb0 + 16, more, anext, pos_next);
         f32x4 acc[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < KBMAX; ++kb) {
-            if (kb < nkb) {
-                const bf16x8 a = __builtin_bit_cast(bf16x8, aop[kb]);
+        for (int kb = 0; kb < NKB; ++kb) {
+            const bf16x8 bop = __builtin_bit_cast(bf16x8, aop[kb]);
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const bf16x8 bop = __builtin_bit_cast(
-                        bf16x8, *reinterpret_cast<const u32x4 *>(Bs + (nb * 16 + row) * ldb + kb * 32 + quad * 8));
-                    acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bop, acc[nb], 0, 0, 0);
-                }
+            for (int nb = 0; nb < NB; ++nb) {
+                const bf16x8 aw = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4 *>(Bs + (nb * 16 + row) * ldb + kb * 32 + quad * 8));
+                acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bop, acc[nb], 0, 0, 0);
             }
         }
 
-        // RoPE at pos = chunk * c + t: the chunk's angle chunk*c*theta_i, in
-        // turns, is reduced to [-1/2, 1/2] in double precision and fed to the
-        // hardware sin/cos (which take turns); the in-chunk offset t*theta_i
-        // comes from a table.  This lane's keys are kb0 + 4*quad + e.
-        float cb[HB], sb[HB];
-        int prev = -1;
+        // RoPE of this lane's key at its original position: the angle in
+        // turns, pos * theta_i / (2 pi), is reduced to [-1/2, 1/2] in double
+        // precision and fed to the hardware sin/cos (which take turns)
+        const double posd = static_cast<double>(pos);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int key = kb0 + quad * 4 + e;
-            const bool kv = key < KC;
-            const int chunk = chunk_of(kv ? key : key_base);
-            const int t = kv ? key % c : 0;
-            if (chunk != prev) {
+        for (int hb = 0; hb < HB; ++hb) {
 #pragma unroll
-                for (int hb = 0; hb < HB; ++hb) {
-                    const double turns = static_cast<double>(chunk * c) * thr[hb];
-                    const float frac = static_cast<float>(turns - rint(turns));
-                    sb[hb] = __builtin_amdgcn_sinf(frac);
-                    cb[hb] = __builtin_amdgcn_cosf(frac);
-                }
-                prev = chunk;
-            }
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb) {
-                const float2 off = toff[t * (D / 2) + hb * 16 + row];
-                const float cs = cb[hb] * off.x - sb[hb] * off.y;
-                const float sn = sb[hb] * off.x + cb[hb] * off.y;
+            for (int e = 0; e < 4; ++e) {
+                const double turns = posd * thr[hb][e];
+                const float frac = static_cast<float>(turns - rint(turns));
+                const float sn = __builtin_amdgcn_sinf(frac), cs = __builtin_amdgcn_cosf(frac);
                 const float x1 = acc[hb][e], x2 = acc[hb + HB][e];
                 acc[hb][e] = x1 * cs - x2 * sn;
                 acc[hb + HB][e] = x2 * cs + x1 * sn;
             }
         }
 
-        // logits: partial dots over this lane's 8 columns, then a halving
-        // exchange across the 16 lanes of the lane group
-        float part[X];
+        // partial logits over this lane's dims, then the lane-group sum
+        float part[GP];
 #pragma unroll
         for (int g = 0; g < GP; ++g) {
-            float qq[NB];
+            float a = 0.f;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) qq[nb] = qs[g][nb * 16 + row];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float a = 0.f;
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) a += qq[nb] * acc[nb][e];
-                part[e * GP + g] = a;
+            for (int nb = 0; nb < NB; ++nb) {
+                const float4 qv = *reinterpret_cast<const float4 *>(&qs[g][nb * 16 + quad * 4]);
+                a += qv.x * acc[nb][0] + qv.y * acc[nb][1] + qv.z * acc[nb][2] + qv.w * acc[nb][3];
             }
+            part[g] = a;
         }
 #pragma unroll
-        for (int bit = 8, cntv = X; bit >= 1; bit >>= 1, cntv >>= 1) {
-            const bool upper = (row & bit) != 0;
-            const int half = cntv / 2;
+        for (int x = 0; x < GP / 2; ++x) part[x] = swap_sum32(part[x], part[x + GP / 2]);
 #pragma unroll
-            for (int x = 0; x < X / 2; ++x) {
-                if (x < half) {
-                    const float send = upper ? part[x] : part[x + half];
-                    const float keep = upper ? part[x + half] : part[x];
-                    part[x] = keep + __shfl_xor(send, bit, 64);
-                }
-            }
+        for (int x = 0; x < HPL; ++x) part[x] = swap_sum16(part[x], part[x + HPL]);
+        const int key = kb0 + row;
+#pragma unroll
+        for (int x = 0; x < HPL; ++x) {
+            const int g = quad * HPL + x;
+            buf_st32(part[x], lr, key < KC && g < G ? (g * NK + OC + key) * 4 : kOob);
         }
 #pragma unroll
-        for (int j = 0; j < GP / 4; ++j) {
-            const int xo = (GP / 4) * row + j;
-            const int e = xo / GP, g = xo % GP;
-            const int key = kb0 + quad * 4 + e;
-            if (key < KC && g < G) logits[(static_cast<size_t>(bh) * G + g) * NK + OC + key] = part[j];
-        }
-        if (more) {
-#pragma unroll
-            for (int kb = 0; kb < KBMAX; ++kb) aop[kb] = anext[kb];
-        }
+        for (int kb = 0; kb < NKB; ++kb) aop[kb] = anext[kb];
+        pos = pos_next;
     }
 }
 
@@ -506,18 +517,21 @@ __global__ __launch_bounds__(D) void combine_kernel(const float2 *__restrict__ p
 // Launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_fetch(const Dims &dm, const void *v_host, void *vc, const int2 *misses, const int32_t *miss_count,
-                        int waves, int xcds, hipStream_t st) {
+                        int waves, hipStream_t st) {
     if (dm.k <= 0) return hipSuccess;
+    const int rows = dm.b * dm.hkv;
     const int chunk_vec = dm.c * dm.d * dm.esize / 16;
-    if (xcds < 1) xcds = 1;
-    if (xcds > kXcds) xcds = kXcds;
-    int per_xcd = (waves / 4 + xcds - 1) / xcds;  // active workgroups per used XCD
-    if (per_xcd < 1) per_xcd = 1;
-    hipLaunchKernelGGL(fetch_kernel, dim3(per_xcd * kXcds), dim3(256), 0, st, static_cast<const u32x4 *>(v_host),
-                       static_cast<u32x4 *>(vc), misses, miss_count, dm.b * dm.hkv, dm.k, dm.n, chunk_vec, xcds);
+    const size_t lds = static_cast<size_t>(rows + 1) * sizeof(int);
+    if (lds > 48 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fetch_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(fetch_kernel, dim3(std::max(1, (waves + 3) / 4)), dim3(256), lds, st,
+                       static_cast<const u32x4 *>(v_host), static_cast<u32x4 *>(vc), misses, miss_count, rows, dm.k,
+                       dm.n, chunk_vec);
     return hipGetLastError();
 }
-
 template <typename T, int D>
 static hipError_t qk_generic_t(const Dims &dm, const void *q, const void *k_out, const void *k_loc, const void *A,
                                const void *Bt, const int32_t *slot_chunk, const double *theta, float *logits,
@@ -534,23 +548,35 @@ static hipError_t qk_generic_t(const Dims &dm, const void *q, const void *k_out,
     return hipGetLastError();
 }
 
-template <int D, int GP>
+template <int D, int GP, int NKB>
 static hipError_t qk_mfma_t(const Dims &dm, const void *q, const void *A, const void *Bt, const int32_t *slot_chunk,
-                            const double *theta_rev, const float2 *rope_off, float *logits, hipStream_t st) {
+                            const double *theta_rev, float *logits, hipStream_t st) {
     if (dm.KC <= 0) return hipSuccess;
-    const size_t lds = static_cast<size_t>(D) * (dm.r_pad + 8) * sizeof(uint16_t) +
-                       static_cast<size_t>(dm.c) * (D / 2) * sizeof(float2);
+    const int r_pad = NKB * 32;
+    const size_t lds = static_cast<size_t>(D) * (r_pad + 8) * sizeof(uint16_t);
     if (lds > 48 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(qk_sparse_mfma_kernel<D, GP>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(qk_sparse_mfma_kernel<D, GP, NKB>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         if (e != hipSuccess) return e;
     }
     dim3 grid((dm.KC + kQkMfmaTile - 1) / kQkMfmaTile, dm.b * dm.hkv);
-    hipLaunchKernelGGL((qk_sparse_mfma_kernel<D, GP>), grid, dim3(256), lds, st, static_cast<const uint16_t *>(q),
-                       static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(Bt), slot_chunk, theta_rev,
-                       rope_off, logits, dm.hkv, dm.G, dm.s, dm.c, dm.r, dm.r_pad, dm.k, dm.OC, dm.KC, dm.NK,
-                       dm.scale);
+    hipLaunchKernelGGL((qk_sparse_mfma_kernel<D, GP, NKB>), grid, dim3(256), lds, st,
+                       static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(A),
+                       static_cast<const uint16_t *>(Bt), slot_chunk, theta_rev, logits, dm.hkv, dm.G, dm.s, dm.c,
+                       dm.r, r_pad, dm.k, dm.OC, dm.KC, dm.NK, dm.scale);
     return hipGetLastError();
+}
+
+// rank blocks of 32: the smallest supported count that covers the rank
+template <int D, int GP>
+static hipError_t qk_mfma_r(const Dims &dm, const void *q, const void *A, const void *Bt, const int32_t *slot_chunk,
+                            const double *theta_rev, float *logits, hipStream_t st) {
+    const int need = (dm.r + 31) / 32;
+    if (need <= 2) return qk_mfma_t<D, GP, 2>(dm, q, A, Bt, slot_chunk, theta_rev, logits, st);
+    if (need <= 4) return qk_mfma_t<D, GP, 4>(dm, q, A, Bt, slot_chunk, theta_rev, logits, st);
+    if (need <= 5) return qk_mfma_t<D, GP, 5>(dm, q, A, Bt, slot_chunk, theta_rev, logits, st);
+    if (need <= 6) return qk_mfma_t<D, GP, 6>(dm, q, A, Bt, slot_chunk, theta_rev, logits, st);
+    return qk_mfma_t<D, GP, 8>(dm, q, A, Bt, slot_chunk, theta_rev, logits, st);
 }
 
 template <int D>
@@ -568,22 +594,22 @@ static hipError_t qk_static_t(const Dims &dm, const void *q, const void *k_out, 
 template <int D>
 static hipError_t qk_bf16_d(const Dims &dm, const void *q, const void *k_out, const void *k_loc, const void *A,
                             const void *Bt, const int32_t *slot_chunk, const double *theta_rev,
-                            const float2 *rope_off, float *logits, hipStream_t st) {
+                            float *logits, hipStream_t st) {
     hipError_t e = qk_static_t<D>(dm, q, k_out, k_loc, logits, st);
     if (e != hipSuccess) return e;
     switch (dm.GP) {
-        case 4: return qk_mfma_t<D, 4>(dm, q, A, Bt, slot_chunk, theta_rev, rope_off, logits, st);
-        case 8: return qk_mfma_t<D, 8>(dm, q, A, Bt, slot_chunk, theta_rev, rope_off, logits, st);
-        default: return qk_mfma_t<D, 16>(dm, q, A, Bt, slot_chunk, theta_rev, rope_off, logits, st);
+        case 4: return qk_mfma_r<D, 4>(dm, q, A, Bt, slot_chunk, theta_rev, logits, st);
+        case 8: return qk_mfma_r<D, 8>(dm, q, A, Bt, slot_chunk, theta_rev, logits, st);
+        default: return qk_mfma_r<D, 16>(dm, q, A, Bt, slot_chunk, theta_rev, logits, st);
     }
 }
 
 hipError_t launch_qk(const Dims &dm, const void *q, const void *k_out, const void *k_loc, const void *A,
                      const void *Bt, const int32_t *slot_chunk, const double *theta, const double *theta_rev,
-                     const float2 *rope_off, float *logits, hipStream_t st) {
+                     float *logits, hipStream_t st) {
     if (dm.bf16 && dm.r % 8 == 0)
-        return dm.d == 128 ? qk_bf16_d<128>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta_rev, rope_off, logits, st)
-                           : qk_bf16_d<64>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta_rev, rope_off, logits, st);
+        return dm.d == 128 ? qk_bf16_d<128>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta_rev, logits, st)
+                           : qk_bf16_d<64>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta_rev, logits, st);
     if (dm.bf16)
         return dm.d == 128 ? qk_generic_t<uint16_t, 128>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta, logits, st)
                            : qk_generic_t<uint16_t, 64>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta, logits, st);

@@ -56,6 +56,12 @@ int make_dims(const skv_config &c, Dims *dm, std::string *why) {
     if (nk < 1) return bad("at least one key must be attended");
     const long long seq_elems = 1LL * c.batch * c.heads_kv * c.seq_len * c.head_dim;
     if (seq_elems >= (1LL << 40)) return bad("tensor too large");
+    // kernels address each (sequence, KV head) row of a tensor, and each
+    // sequence of A, through buffer resources of less than 1 GiB
+    const long long es = c.dtype == SKV_BF16 ? 2 : 4;
+    if (1LL * n * c.head_dim * es >= (1LL << 30) || 1LL * n * (c.heads_q / c.heads_kv) * 4 >= (1LL << 30) ||
+        1LL * c.seq_len * c.rank * es >= (1LL << 30))
+        return bad("a per-row tensor would reach 1 GiB (sequence too long)");
     Dims &d = *dm;
     d.b = c.batch; d.hq = c.heads_q; d.hkv = c.heads_kv; d.d = c.head_dim; d.s = c.seq_len; d.c = c.chunk;
     d.r = c.rank; d.o = c.n_outlier; d.k = c.top_k; d.w = c.local_window;
@@ -152,7 +158,6 @@ struct skv_layer {
     float *min_cos = nullptr;
     double *theta = nullptr;      // theta_i = base^(-2i/d)
     double *theta_rev = nullptr;  // theta_i / (2 pi): turns per position
-    float2 *rope_off = nullptr;
     // resident V cache
     void *vc = nullptr;
     int32_t *slot_chunk = nullptr;
@@ -163,7 +168,8 @@ struct skv_layer {
     int2 *misses = nullptr;
     int32_t *miss_count = nullptr;
     unsigned long long *counters = nullptr;  // hits, misses, steps
-    uint32_t *key_scratch = nullptr;  // selection keys when a row does not fit in LDS
+    uint32_t *keys = nullptr;    // selection keys (b, h_kv, n)
+    uint2 *kbounds = nullptr;    // (min, max) selectable key per row and group slice
     int select_keys_in_lds = 1, topo_keys_in_lds = 1;
     int32_t *bad = nullptr;
     // host V
@@ -172,7 +178,8 @@ struct skv_layer {
     // shared per-device streams for the host-V fetch and the key rebuild
     hipStream_t copy = nullptr, comp = nullptr;
     hipEvent_t ev_sel = nullptr, ev_fetch = nullptr, ev_qk = nullptr;
-    int fetch_waves = 256, fetch_xcds = 8;
+    int fetch_waves = 256;
+    int score_wgs = 0;  // workgroups of the scoring kernel (0: two tiles per wave)
     // timing
     bool overlap = false;  // fetch beside the key rebuild (true) or before it
     bool timing = false;
@@ -305,6 +312,10 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, ly->device) != hipSuccess)
         return bail(fail(SKV_E_HIP, "hipDeviceGetAttribute(MaxSharedMemoryPerBlock) failed"));
     ly->lds_limit = lds;
+    // Scoring grid: 0 picks two 64-chunk tiles per wave; SKV_SCORE_WGS
+    // overrides the workgroup count for tuning.
+    ly->score_wgs = 0;
+    if (const char *e = std::getenv("SKV_SCORE_WGS")) ly->score_wgs = std::max(1, std::atoi(e));
 
     const size_t B = dm.b, HKV = dm.hkv, HQ = dm.hq, D = dm.d, S = dm.s, E = dm.esize;
     const size_t bh = B * HKV;
@@ -335,29 +346,24 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     ALLOC(bad, 4);
     ALLOC(theta, D / 2 * sizeof(double));
     ALLOC(theta_rev, D / 2 * sizeof(double));
-    ALLOC(rope_off, static_cast<size_t>(dm.c) * D / 2 * sizeof(float2));
     const size_t lds_cap = static_cast<size_t>(ly->lds_limit);
     ly->select_keys_in_lds = skv::select_dynamic_lds(dm, true) + skv::select_static_lds() <= lds_cap;
     ly->topo_keys_in_lds = static_cast<size_t>(dm.n) * 4 + skv::select_static_lds() <= lds_cap;
     if (skv::select_dynamic_lds(dm, false) + skv::select_static_lds() > lds_cap)
         return bail(fail(SKV_E_SHAPE, "top_k too large for the select kernel's shared memory"));
-    if (!ly->select_keys_in_lds || !ly->topo_keys_in_lds) ALLOC(key_scratch, bh * dm.n * 4);
+    ALLOC(keys, bh * dm.n * 4);
+    ALLOC(kbounds, bh * skv::group_slices(dm) * sizeof(uint2));
 #undef ALLOC
 
-    // RoPE tables: theta_i = base^(-2i/d) in double, and the in-chunk offsets
-    // (cos t*theta_i, sin t*theta_i) for t < chunk.
+    // RoPE rates: theta_i = base^(-2i/d) in double, and the same in turns
+    // (theta_i / 2 pi) for the hardware sin/cos.
     std::vector<double> th(D / 2), thr(D / 2);
-    std::vector<float2> off(static_cast<size_t>(dm.c) * D / 2);
     for (size_t i = 0; i < D / 2; ++i) {
         th[i] = std::pow(static_cast<double>(cfg->rope_base), -2.0 * i / D);
         thr[i] = th[i] / (2.0 * 3.14159265358979323846);
     }
-    for (int t = 0; t < dm.c; ++t)
-        for (size_t i = 0; i < D / 2; ++i)
-            off[t * D / 2 + i] = make_float2(static_cast<float>(std::cos(t * th[i])), static_cast<float>(std::sin(t * th[i])));
     if (hipMemcpy(ly->theta, th.data(), th.size() * sizeof(double), hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(ly->theta_rev, thr.data(), thr.size() * sizeof(double), hipMemcpyHostToDevice) != hipSuccess ||
-        hipMemcpy(ly->rope_off, off.data(), off.size() * sizeof(float2), hipMemcpyHostToDevice) != hipSuccess ||
         hipMemset(ly->counters, 0, 4 * sizeof(unsigned long long)) != hipSuccess)
         return bail(fail(SKV_E_HIP, "initialising layer tables failed"));
     DevStreams *ds = nullptr;
@@ -371,10 +377,9 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
 
     // Host-V fetch: enough waves to keep PCIe busy (a few hundred 2 KB chunk
     // reads in flight), not so many that the slow host reads crowd the memory
-    // path of the kernels running beside them.  SKV_FETCH_WAVES and
-    // SKV_FETCH_XCDS override the defaults for tuning.
+    // path of the kernels running beside them.  SKV_FETCH_WAVES overrides the
+    // default for tuning.
     if (const char *e = std::getenv("SKV_FETCH_WAVES")) ly->fetch_waves = std::max(4, std::atoi(e));
-    if (const char *e = std::getenv("SKV_FETCH_XCDS")) ly->fetch_xcds = std::min(8, std::max(1, std::atoi(e)));
 
     *out = ly;
     return SKV_OK;
@@ -407,7 +412,7 @@ int shadowkv_prefill_meta(skv_layer *ly, const void *k_pre, const void *k_rope, 
     const Dims &dm = ly->dm;
     ly->ready = false;
     SKV_HIP(skv::launch_landmarks(dm, k_pre, k_rope, ly->theta, ly->L, ly->min_cos, st));
-    SKV_HIP(skv::launch_topo(dm, ly->min_cos, ly->outliers, ly->key_scratch, ly->topo_keys_in_lds, st));
+    SKV_HIP(skv::launch_topo(dm, ly->min_cos, ly->outliers, ly->keys, ly->topo_keys_in_lds, st));
     SKV_HIP(skv::launch_gather_static(dm, k_pre, k_rope, v, ly->outliers, ly->theta, ly->k_out, ly->v_out,
                                       ly->k_loc, ly->v_loc, st));
     if ((rc = install_common(ly, A, B, v_host, st))) return rc;
@@ -461,12 +466,13 @@ int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) 
     const Dims &dm = ly->dm;
     {
         Timed t(ly, SKV_K_SCORE, st);
-        SKV_HIP(skv::launch_score(dm, q, ly->L, ly->cand, ly->P, ly->stats, st));
+        SKV_HIP(skv::launch_score(dm, q, ly->L, ly->cand, ly->P, ly->stats, ly->score_wgs, st));
     }
     {
         Timed t(ly, SKV_K_SELECT, st);
-        SKV_HIP(skv::launch_select(dm, ly->P, ly->stats, ly->cand, ly->S2, ly->sel, ly->slot_chunk, ly->misses,
-                                   ly->miss_count, ly->counters, ly->key_scratch, ly->select_keys_in_lds, st));
+        SKV_HIP(skv::launch_group(dm, ly->P, ly->stats, ly->cand, ly->S2, ly->keys, ly->kbounds, st));
+        SKV_HIP(skv::launch_select(dm, ly->keys, ly->kbounds, ly->sel, ly->slot_chunk, ly->misses, ly->miss_count,
+                                   ly->counters, ly->select_keys_in_lds, st));
     }
     if (ly->overlap) {
         // fork: the fetch of missing V on the fetch stream, the key rebuild
@@ -477,13 +483,13 @@ int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) 
         {
             Timed t(ly, SKV_K_FETCH, ly->copy);
             SKV_HIP(skv::launch_fetch(dm, ly->v_host_dev, ly->vc, ly->misses, ly->miss_count, ly->fetch_waves,
-                                      ly->fetch_xcds, ly->copy));
+                                      ly->copy));
         }
         SKV_HIP(hipEventRecord(ly->ev_fetch, ly->copy));
         {
             Timed t(ly, SKV_K_QK, ly->comp);
             SKV_HIP(skv::launch_qk(dm, q, ly->k_out, ly->k_loc, ly->A, ly->Bt, ly->slot_chunk, ly->theta,
-                                   ly->theta_rev, ly->rope_off, ly->logits, ly->comp));
+                                   ly->theta_rev, ly->logits, ly->comp));
         }
         SKV_HIP(hipEventRecord(ly->ev_qk, ly->comp));
         SKV_HIP(hipStreamWaitEvent(st, ly->ev_qk, 0));
@@ -493,12 +499,12 @@ int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) 
         {
             Timed t(ly, SKV_K_FETCH, st);
             SKV_HIP(skv::launch_fetch(dm, ly->v_host_dev, ly->vc, ly->misses, ly->miss_count, ly->fetch_waves,
-                                      ly->fetch_xcds, st));
+                                      st));
         }
         {
             Timed t(ly, SKV_K_QK, st);
             SKV_HIP(skv::launch_qk(dm, q, ly->k_out, ly->k_loc, ly->A, ly->Bt, ly->slot_chunk, ly->theta,
-                                   ly->theta_rev, ly->rope_off, ly->logits, st));
+                                   ly->theta_rev, ly->logits, st));
         }
     }
     {

@@ -2,12 +2,14 @@
 // steps 1-2, and the Telegram write-up's set-difference cache):
 //   score   P = q . L^T / sqrt(d) for every chunk, with per-tile softmax
 //           partials over the selectable chunks;
-//   select  one workgroup per (sequence, KV head): the group score
-//           S2 = per-head softmax over selectable chunks averaged over the
-//           query heads of the KV group, ArgTopK(S2, k) by radix selection,
-//           and the set difference against the previous step's resident
-//           chunks (miss list, hit counts).
+//   group   the group score S2 = per-head softmax over selectable chunks
+//           averaged over the query heads of the KV group, as selection keys;
+//   select  one workgroup per (sequence, KV head): ArgTopK(S2, k) by radix
+//           selection, and the set difference against the previous step's
+//           resident chunks (miss list, hit counts).
 // The same radix selection picks the prefill's outlier chunks.
+#include <algorithm>
+
 #include "skv_device.h"
 
 namespace skv {
@@ -18,8 +20,11 @@ namespace skv {
 // group (padded to 16), N = chunks, K = d.  One v_mfma_f32_16x16x32_bf16 takes
 // 16 chunks x 32 dims: lane l feeds head (l & 15) of q and chunk (l & 15) of
 // L with dims 32*ks + 8*(l >> 4) .. +8, so the four lane groups of one load
-// instruction read 64 contiguous bytes of each landmark row.  Each wave
-// scores a tile of 64 chunks (4 rounds of 16, all loads issued up front).
+// instruction read 64 contiguous bytes of each landmark row.  The kernel is
+// persistent: each wave scores a contiguous run of 64-chunk tiles (4 rounds
+// of 16 chunks), and as soon as a round's MFMAs have consumed its registers
+// the same round of the next tile is loaded into them, so every wave keeps a
+// whole tile of landmark loads in flight while it finishes the current one.
 //
 // Softmax bookkeeping per tile and head: M = max of the tile's selectable
 // scores, u[j] = exp(P[j] - M) (0 for non-selectable chunks) written as
@@ -40,112 +45,163 @@ __device__ __forceinline__ float sel_sum16(float v) {
     return v;
 }
 
-template <int D, bool SMALLG>
+// MODE 0: G <= 4 (U stored one value per lane); 1: G > 4, G % 4 == 0 (four
+// heads per 16-byte store); 2: other G > 4 (four single stores).
+template <int D, int MODE>
 __global__ __launch_bounds__(256) void score_mfma_kernel(const uint16_t *__restrict__ q,
                                                          const uint16_t *__restrict__ L,
                                                          const uint32_t *__restrict__ cand, int mask_words,
                                                          float *__restrict__ U, float2 *__restrict__ stats,
-                                                         int hkv, int G, int n, int wtiles, float scale) {
+                                                         int hkv, int G, int n, int wtiles, int rows,
+                                                         int tiles_per_wave, float scale) {
     constexpr int KS = D / 32;
     constexpr int ROUNDS = 4;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row = lane & 15, quad = lane >> 4;
-    const int bh = blockIdx.y, b = bh / hkv, h = bh % hkv;
     const int hq = hkv * G;
-    const int wt = blockIdx.x * 4 + wave;  // 64-chunk tile of this wave
-    if (wt >= wtiles) return;              // no barrier in this kernel
+    const int total = rows * wtiles;
+    int T = (blockIdx.x * 4 + wave) * tiles_per_wave;  // this wave's run of tiles
+    const int t_end = min(total, T + tiles_per_wave);
+    if (T >= t_end) return;  // no barrier in this kernel
+
+    // Loads and stores go through buffer resources: the next tile's loads are
+    // switched off (not branched around) after the last tile, chunks past n
+    // read zeros and their stores are dropped.
+    const Rsrc qr = make_rsrc(q, static_cast<uint32_t>(rows) * G * D * 2);
+    const Rsrc cr = make_rsrc(cand, static_cast<uint32_t>(rows) * mask_words * 4);
+    const uint32_t lrow_bytes = static_cast<uint32_t>(n) * D * 2;
+    auto l_rsrc = [&](int bh) { return make_rsrc(L + static_cast<size_t>(bh) * n * D, lrow_bytes); };
+    // query rows of the group: lane row = head; rows past G repeat the last
+    // head and their MFMA outputs are ignored
+    auto q_off = [&](int bh) {
+        const int b = bh / hkv, h = bh % hkv;
+        return ((b * hq + h * G + min(row, G - 1)) * D + quad * 8) * 2;
+    };
+    auto load_q = [&](int off, bf16x8 *qa) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qa[ks] = __builtin_bit_cast(bf16x8, buf_ld128(qr, off + ks * 64));
+    };
+    // round rd (16 chunks) of a tile: lane row takes chunk 64*wt + 16*rd + row
+    auto load_round = [&](Rsrc lr, int off, u32x4 *dst) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) dst[ks] = buf_ld128(lr, off + ks * 64);
+    };
+    auto round_off = [&](int wt, int rd) { return ((wt * 64 + rd * 16 + row) * D + quad * 8) * 2; };
 
     bf16x8 qa[KS];
-    {
-        const uint16_t *qrow = q + (static_cast<size_t>(b) * hq + h * G + row) * D + quad * 8;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const u32x4 v = row < G ? *reinterpret_cast<const u32x4 *>(qrow + ks * 32) : u32x4{0u, 0u, 0u, 0u};
-            qa[ks] = __builtin_bit_cast(bf16x8, v);
-        }
-    }
-    const int wbase = wt * 64;
-    const uint16_t *Lbh = L + static_cast<size_t>(bh) * n * D;
     u32x4 lb[ROUNDS][KS];
+    uint32_t mw0, mw1;
+    {
+        // the prologue issues its loads in the loop body's order (query,
+        // mask, rounds 0-3), so the wait counts at the loop head hold on both
+        // paths into it
+        const int bh = T / wtiles, wt = T - bh * wtiles;
+        load_q(q_off(bh), qa);
+        __builtin_amdgcn_sched_barrier(0);
+        mw0 = buf_ld32(cr, (bh * mask_words + 2 * wt) * 4);
+        mw1 = buf_ld32(cr, 2 * wt + 1 < mask_words ? (bh * mask_words + 2 * wt + 1) * 4 : kOob);
+        __builtin_amdgcn_sched_barrier(0);
+        const Rsrc lr = l_rsrc(bh);
 #pragma unroll
-    for (int rd = 0; rd < ROUNDS; ++rd) {
-        const int j = wbase + rd * 16 + row;
-        const uint16_t *lrow = Lbh + static_cast<size_t>(j < n ? j : 0) * D + quad * 8;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            lb[rd][ks] = j < n ? *reinterpret_cast<const u32x4 *>(lrow + ks * 32) : u32x4{0u, 0u, 0u, 0u};
+        for (int rd = 0; rd < ROUNDS; ++rd) {
+            load_round(lr, round_off(wt, rd), lb[rd]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
-    const uint32_t *cm = cand + static_cast<size_t>(bh) * mask_words;
-    float *Ub = U + static_cast<size_t>(bh) * n * G;
-    float2 *st = stats + static_cast<size_t>(bh) * G * wtiles;
 
-    if constexpr (SMALLG) {
-        // lane (quad, row) <- head quad of chunk row of each round
-        float p[ROUNDS];
+    for (; T < t_end; ++T) {
+        const int bh = T / wtiles, wt = T - bh * wtiles;
+        const int wbase = wt * 64;
+        const bool more = T + 1 < t_end;
+        const int bhn = more ? (T + 1) / wtiles : bh, wtn = more ? T + 1 - bhn * wtiles : wt;
+        const bool new_row = bhn != bh;
+        bf16x8 qn[KS];
+        load_q(new_row ? q_off(bhn) : kOob, qn);
+        const uint32_t m0 = mw0, m1 = mw1;
+        mw0 = buf_ld32(cr, more ? (bhn * mask_words + 2 * wtn) * 4 : kOob);
+        mw1 = buf_ld32(cr, more && 2 * wtn + 1 < mask_words ? (bhn * mask_words + 2 * wtn + 1) * 4 : kOob);
+        const Rsrc lrn = l_rsrc(bhn);
+        const Rsrc ur = make_rsrc(U + static_cast<size_t>(bh) * n * G, static_cast<uint32_t>(n) * G * 4);
+        const Rsrc sr = make_rsrc(stats + static_cast<size_t>(bh) * G * wtiles, static_cast<uint32_t>(G) * wtiles * 8);
+        auto valid_chunk = [&](int rd) {
+            const int jl = rd * 16 + row;  // chunk within the tile
+            const uint32_t word = jl < 32 ? m0 : m1;
+            return wbase + jl < n && ((word >> (jl & 31)) & 1u);
+        };
+
+        if constexpr (MODE == 0) {
+            // lane (quad, row) <- head quad of chunk row of each round
+            float p[ROUNDS];
 #pragma unroll
-        for (int rd = 0; rd < ROUNDS; ++rd) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int rd = 0; rd < ROUNDS; ++rd) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], __builtin_bit_cast(bf16x8, lb[rd][ks]), acc, 0, 0, 0);
-            const float t0 = __shfl(acc[0], row, 64), t1 = __shfl(acc[1], row, 64);
-            const float t2 = __shfl(acc[2], row, 64), t3 = __shfl(acc[3], row, 64);
-            const float mine = quad == 0 ? t0 : (quad == 1 ? t1 : (quad == 2 ? t2 : t3));
-            const int j = wbase + rd * 16 + row;
-            const bool valid = quad < G && j < n && mask_bit(cm, j);
-            p[rd] = valid ? mine * scale : -INFINITY;
-        }
-        float M = fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3]));
-        M = sel_max16(M);
-        float S = 0.f;
-#pragma unroll
-        for (int rd = 0; rd < ROUNDS; ++rd) {
-            const float u = p[rd] == -INFINITY ? 0.f : expf(p[rd] - M);
-            S += u;
-            const int j = wbase + rd * 16 + row;
-            if (quad < G && j < n) Ub[static_cast<size_t>(j) * G + quad] = u;
-        }
-        S = sel_sum16(S);
-        if (row == 0 && quad < G) st[static_cast<size_t>(quad) * wtiles + wt] = make_float2(M, S);
-    } else {
-        // lane holds heads 4*quad + e of chunk row; G > 4 keeps that layout
-        float p[ROUNDS][4];
-#pragma unroll
-        for (int rd = 0; rd < ROUNDS; ++rd) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], __builtin_bit_cast(bf16x8, lb[rd][ks]), acc, 0, 0, 0);
-            const int j = wbase + rd * 16 + row;
-            const bool jv = j < n && mask_bit(cm, j);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) p[rd][e] = (jv && quad * 4 + e < G) ? acc[e] * scale : -INFINITY;
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            float M = fmaxf(fmaxf(p[0][e], p[1][e]), fmaxf(p[2][e], p[3][e]));
+                for (int ks = 0; ks < KS; ++ks)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], __builtin_bit_cast(bf16x8, lb[rd][ks]), acc,
+                                                                  0, 0, 0);
+                load_round(lrn, more ? round_off(wtn, rd) : kOob, lb[rd]);
+                const float t0 = __shfl(acc[0], row, 64), t1 = __shfl(acc[1], row, 64);
+                const float t2 = __shfl(acc[2], row, 64), t3 = __shfl(acc[3], row, 64);
+                const float mine = quad == 0 ? t0 : (quad == 1 ? t1 : (quad == 2 ? t2 : t3));
+                p[rd] = (quad < G && valid_chunk(rd)) ? mine * scale : -INFINITY;
+            }
+            float M = fmaxf(fmaxf(p[0], p[1]), fmaxf(p[2], p[3]));
             M = sel_max16(M);
             float S = 0.f;
 #pragma unroll
             for (int rd = 0; rd < ROUNDS; ++rd) {
-                const float u = p[rd][e] == -INFINITY ? 0.f : expf(p[rd][e] - M);
-                p[rd][e] = u;
+                const float u = p[rd] == -INFINITY ? 0.f : expf(p[rd] - M);
                 S += u;
+                const int j = wbase + rd * 16 + row;
+                buf_st32(u, ur, quad < G ? (j * G + quad) * 4 : kOob);
             }
             S = sel_sum16(S);
-            if (row == 0 && quad * 4 + e < G) st[static_cast<size_t>(quad * 4 + e) * wtiles + wt] = make_float2(M, S);
-        }
+            buf_st64(make_float2(M, S), sr, row == 0 && quad < G ? (quad * wtiles + wt) * 8 : kOob);
+        } else {
+            // lane holds heads 4*quad + e of chunk row
+            float p[ROUNDS][4];
 #pragma unroll
-        for (int rd = 0; rd < ROUNDS; ++rd) {
-            const int j = wbase + rd * 16 + row;
-            if (j < n && quad * 4 < G) {
-                float *dst = Ub + static_cast<size_t>(j) * G + quad * 4;
-                if (G % 4 == 0) {
-                    *reinterpret_cast<float4 *>(dst) = make_float4(p[rd][0], p[rd][1], p[rd][2], p[rd][3]);
+            for (int rd = 0; rd < ROUNDS; ++rd) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], __builtin_bit_cast(bf16x8, lb[rd][ks]), acc,
+                                                                  0, 0, 0);
+                load_round(lrn, more ? round_off(wtn, rd) : kOob, lb[rd]);
+                const bool jv = valid_chunk(rd);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) p[rd][e] = (jv && quad * 4 + e < G) ? acc[e] * scale : -INFINITY;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float M = fmaxf(fmaxf(p[0][e], p[1][e]), fmaxf(p[2][e], p[3][e]));
+                M = sel_max16(M);
+                float S = 0.f;
+#pragma unroll
+                for (int rd = 0; rd < ROUNDS; ++rd) {
+                    const float u = p[rd][e] == -INFINITY ? 0.f : expf(p[rd][e] - M);
+                    p[rd][e] = u;
+                    S += u;
+                }
+                S = sel_sum16(S);
+                buf_st64(make_float2(M, S), sr, row == 0 && quad * 4 + e < G ? ((quad * 4 + e) * wtiles + wt) * 8 : kOob);
+            }
+#pragma unroll
+            for (int rd = 0; rd < ROUNDS; ++rd) {
+                const int j = wbase + rd * 16 + row;
+                if constexpr (MODE == 1) {
+                    buf_st128(make_float4(p[rd][0], p[rd][1], p[rd][2], p[rd][3]), ur,
+                              quad * 4 < G ? (j * G + quad * 4) * 4 : kOob);
                 } else {
-                    for (int e = 0; e < 4 && quad * 4 + e < G; ++e) dst[e] = p[rd][e];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) buf_st32(p[rd][e], ur, quad * 4 + e < G ? (j * G + quad * 4 + e) * 4 : kOob);
                 }
             }
+        }
+        if (new_row) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) qa[ks] = qn[ks];
         }
     }
 }
@@ -188,7 +244,7 @@ __global__ __launch_bounds__(256) void score_generic_kernel(const T *__restrict_
 // Block-wide helpers (blockDim.x threads, a multiple of 64, at most 2048).
 // ---------------------------------------------------------------------------
 struct SelectScratch {
-    uint32_t hist[4096];
+    alignas(16) uint32_t hist[4096];
     int wtmp[2][32];
     uint32_t digit;
     int above;
@@ -219,80 +275,116 @@ __device__ __forceinline__ void block_scan2(int &a, int &b, SelectScratch &sc, i
     *tb = sb;
 }
 
+// Minimum and maximum of per-thread values over the block (one pair of
+// barriers); every thread gets both.
+__device__ __forceinline__ void block_minmax(uint32_t &mn, uint32_t &mx, SelectScratch &sc) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        mn = min(mn, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mn), off, 64)));
+        mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), off, 64)));
+    }
+    if (lane == 0) { sc.wtmp[0][wave] = static_cast<int>(mn); sc.wtmp[1][wave] = static_cast<int>(mx); }
+    __syncthreads();
+    for (int w = 0; w < nw; ++w) {
+        mn = min(mn, static_cast<uint32_t>(sc.wtmp[0][w]));
+        mx = max(mx, static_cast<uint32_t>(sc.wtmp[1][w]));
+    }
+    __syncthreads();
+}
+
 // The k largest of keys[0, n), exact ties to the lower index, written to
-// out[0, k) (and to lds_out if given) in ascending index order.  Radix
-// selection on 12 + 12 + 8 bits finds the k-th largest key T and how many
-// keys equal to T are taken: all threads build a histogram of the current
-// digit, one wave scans it from the top to find the digit holding the k-th
-// key (and clears it).  An ordered compaction over contiguous per-thread
-// segments then writes the indices.  Requires 1 <= k <= n.  Every thread of
-// the block must call it; sc.hist must be zero on entry.
-__device__ void radix_topk(const uint32_t *keys, int n, int k, int32_t *out, int32_t *lds_out, SelectScratch &sc) {
-    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6;
-    uint32_t prefix = 0, pmask = 0;
+// out[0, k) (and to lds_out if given) in ascending index order.  The caller
+// passes kmin <= kmax bounding the candidate keys: at least k keys lie in
+// [kmin, kmax], none above kmax, and keys below kmin are never taken.
+// Radix selection runs on the offsets key - kmin, 12 bits per pass from the
+// highest bit the range needs, so a tight range takes two passes and spreads
+// over many bins.  Each pass: all threads build the histogram of the current
+// digit among the keys that match the prefix found so far; every thread then
+// takes four bins (highest first), clears them, and a block scan finds the bin
+// holding the k-th largest key.  The threshold T and the number of keys equal
+// to T to take follow; an ordered compaction over wave-contiguous segments
+// (ballots and popcounts) writes the indices.  Requires blockDim.x == 1024
+// (four bins per thread) and 1 <= k; every thread of the block must call it;
+// sc.hist must be zero on entry and is zero again on return.
+__device__ void radix_topk(const uint32_t *keys, int n, int k, uint32_t kmin, uint32_t kmax, int32_t *out,
+                           int32_t *lds_out, SelectScratch &sc) {
+    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
+    const uint32_t range = kmax - kmin;
+    int hi = range == 0 ? 0 : 32 - __clz(static_cast<int>(range));  // bits of the offsets
+    uint64_t prefix = 0;  // offset bits fixed so far (above hi)
     int krem = k;
-    for (int pass = 0; pass < 3; ++pass) {
-        const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
-        const int nbins = pass == 2 ? 256 : 4096;
-        const uint32_t dmask = static_cast<uint32_t>(nbins - 1);
+    while (hi > 0) {
+        const int lo = hi > 12 ? hi - 12 : 0;
+        const uint32_t dmask = (1u << (hi - lo)) - 1u;
+        const uint64_t want = prefix >> hi;
         for (int j = tid; j < n; j += nt) {
             const uint32_t key = keys[j];
-            if ((key & pmask) == prefix) atomicAdd(&sc.hist[(key >> shift) & dmask], 1u);
+            const uint64_t rel = static_cast<uint64_t>(key - kmin);
+            if (key >= kmin && (rel >> hi) == want) atomicAdd(&sc.hist[(rel >> lo) & dmask], 1u);
         }
-        __syncthreads();
-        if (wave == 0) {
-            const int per = nbins / 64;  // lane l owns bins top-l*per .. downwards
-            const int top = nbins - 1 - lane * per;
-            int local = 0;
-            for (int i = 0; i < per; ++i) local += static_cast<int>(sc.hist[top - i]);
-            int incl = local;
+        __syncthreads();  // every thread has also read the previous pass's digit
+        if (tid == 0) { sc.digit = 0; sc.above = 0; }
+        // thread t takes bins nb4 - 4t - 4 .. nb4 - 4t - 1 (highest first)
+        const int nb4 = max(4, static_cast<int>(dmask) + 1);
+        const int base = nb4 - 4 * (tid + 1);
+        u32x4 cnt = {0u, 0u, 0u, 0u};
+        if (base >= 0) {
+            cnt = *reinterpret_cast<const u32x4 *>(&sc.hist[base]);
+            *reinterpret_cast<u32x4 *>(&sc.hist[base]) = u32x4{0u, 0u, 0u, 0u};
+        }
+        const int local = static_cast<int>(cnt[0] + cnt[1] + cnt[2] + cnt[3]);
+        int incl = local, dummy = 0, tot, tot2;
+        block_scan2(incl, dummy, sc, &tot, &tot2);
+        const int excl = incl - local;
+        if (base >= 0 && excl < krem && krem <= incl) {
+            int acc = excl;
 #pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int t = __shfl_up(incl, off, 64);
-                if (lane >= off) incl += t;
+            for (int i = 3; i >= 0; --i) {
+                const int c = static_cast<int>(cnt[i]);
+                if (acc + c >= krem) { sc.digit = static_cast<uint32_t>(base + i); sc.above = acc; break; }
+                acc += c;
             }
-            const int excl = incl - local;
-            if (excl < krem && krem <= incl) {
-                int acc = excl;
-                for (int i = 0; i < per; ++i) {
-                    const int cnt = static_cast<int>(sc.hist[top - i]);
-                    if (acc + cnt >= krem) { sc.digit = static_cast<uint32_t>(top - i); sc.above = acc; break; }
-                    acc += cnt;
-                }
-            }
-            for (int i = 0; i < per; ++i) sc.hist[top - i] = 0;  // ready for the next pass
         }
         __syncthreads();
-        prefix |= sc.digit << shift;
-        pmask |= dmask << shift;
+        prefix |= static_cast<uint64_t>(sc.digit) << lo;
         krem -= sc.above;
+        hi = lo;
     }
-    const uint32_t thr = prefix;
-    const int need_eq = krem;
-    const int seg = (n + nt - 1) / nt;
-    const int j0 = min(n, tid * seg), j1 = min(n, j0 + seg);
-    int gt = 0, eq = 0;
-    for (int j = j0; j < j1; ++j) {
-        const uint32_t key = keys[j];
-        gt += key > thr;
-        eq += key == thr;
+    const uint32_t thr = kmin + static_cast<uint32_t>(prefix);
+    const int need_eq = krem;  // keys equal to thr that are taken, lowest index first
+
+    // ordered compaction: wave w owns keys [w * seg, (w + 1) * seg)
+    const int seg = ((n + nw - 1) / nw + 63) & ~63;
+    const int j0 = min(n, wave * seg), j1 = min(n, j0 + seg);
+    int cg = 0, ce = 0;
+    for (int jb = j0; jb < j1; jb += 64) {
+        const int j = jb + lane;
+        const uint32_t key = j < j1 ? keys[j] : 0u;
+        cg += __popcll(__ballot(key > thr));
+        ce += __popcll(__ballot(key == thr && j < j1));
     }
-    int gt_incl = gt, eq_incl = eq, tg, te;
-    block_scan2(gt_incl, eq_incl, sc, &tg, &te);
-    const int gt_before = gt_incl - gt, eq_before = eq_incl - eq;
-    // equal keys are taken in index order until need_eq of them are taken
-    const int take_eq = min(max(need_eq - eq_before, 0), eq);
-    int pos = gt_before + min(eq_before, need_eq);
-    int eq_seen = 0;
-    for (int j = j0; j < j1 && pos < k; ++j) {
-        const uint32_t key = keys[j];
-        bool t = key > thr;
-        if (key == thr) t = eq_seen++ < take_eq;
-        if (t) {
-            out[pos] = j;
-            if (lds_out) lds_out[pos] = j;
-            ++pos;
+    if (lane == 0) { sc.wtmp[0][wave] = cg; sc.wtmp[1][wave] = ce; }
+    __syncthreads();
+    int gt_run = 0, eq_run = 0;
+    for (int w = 0; w < wave; ++w) { gt_run += sc.wtmp[0][w]; eq_run += sc.wtmp[1][w]; }
+    __syncthreads();
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int jb = j0; jb < j1 && gt_run + min(eq_run, need_eq) < k; jb += 64) {
+        const int j = jb + lane;
+        const uint32_t key = j < j1 ? keys[j] : 0u;
+        const bool g = key > thr, e = key == thr && j < j1;
+        const uint64_t bg = __ballot(g), be = __ballot(e);
+        const int gb = gt_run + __popcll(bg & below), eb = eq_run + __popcll(be & below);
+        if (g || (e && eb < need_eq)) {
+            const int pos = gb + min(eb, need_eq);
+            if (pos < k) {
+                out[pos] = j;
+                if (lds_out) lds_out[pos] = j;
+            }
         }
+        gt_run += __popcll(bg);
+        eq_run += __popcll(be);
     }
 }
 
@@ -305,124 +397,167 @@ __global__ __launch_bounds__(kSelectThreads) void topo_kernel(const float *__res
     __shared__ SelectScratch sc;
     const int row = blockIdx.x;
     uint32_t *keys = use_lds ? dyn : gscratch + static_cast<size_t>(row) * n;
-    for (int j = threadIdx.x; j < n; j += blockDim.x)
-        keys[j] = j < n_valid ? float_key(-min_cos[static_cast<size_t>(row) * n + j]) : 0u;
+    uint32_t kmn = 0xffffffffu, kmx = 0u;
+    for (int j = threadIdx.x; j < n; j += blockDim.x) {
+        const uint32_t key = j < n_valid ? float_key(-min_cos[static_cast<size_t>(row) * n + j]) : 0u;
+        keys[j] = key;
+        if (j < n_valid) { kmn = min(kmn, key); kmx = max(kmx, key); }
+    }
     for (int i = threadIdx.x; i < 4096; i += blockDim.x) sc.hist[i] = 0;
-    __syncthreads();
-    if (o > 0) radix_topk(keys, n, o, out + static_cast<size_t>(row) * o, nullptr, sc);
+    block_minmax(kmn, kmx, sc);  // its barriers also publish keys and hist
+    if (o > 0 && kmn <= kmx) radix_topk(keys, n, o, kmn, kmx, out + static_cast<size_t>(row) * o, nullptr, sc);
 }
 
 // ---------------------------------------------------------------------------
-// Group score of one (sequence, KV head) row: S2[j] = sum_g U[j, g] w[t, g]
-// with t the 64-chunk tile of j and w[t, g] = exp(M_t,g - m_g) / (Z_g G);
-// selectable chunks only (0 elsewhere).  Written to S2 and kept as
-// order-preserving keys (selectable keys > 0).  Each thread takes 64/GP
-// chunks per batch and issues all their loads before any arithmetic.
+// Group score, one workgroup per (slice of kGroupSlice chunks, row):
+//  1. per query head g of the group, m_g = max over tiles of M_t,g and
+//     Z_g = sum_t S_t,g exp(M_t,g - m_g) (every workgroup of a row repeats
+//     this small reduction over the tile statistics);
+//  2. tile weights w[t, g] = exp(M_t,g - m_g) / (Z_g G) of the slice's tiles;
+//  3. S2[j] = sum_g U[j, g] w[t(j), g] = (1/G) sum_g softmax_g(P)[j] over
+//     the selectable chunks j (0 elsewhere), written to S2 and as
+//     order-preserving keys (selectable keys > 0), with the slice's smallest
+//     and largest selectable key.
 // ---------------------------------------------------------------------------
 template <int GP>
-__device__ __forceinline__ void group_scores(const float *Ub, const uint32_t *cm, const float *w, int G, int n,
-                                             float *S2b, uint32_t *keys) {
-    constexpr int UNR = 64 / GP;
-    const int tid = threadIdx.x, nt = blockDim.x;
-    for (int j0 = 0; j0 < n; j0 += nt * UNR) {
-        float v[UNR][GP];
-        uint32_t word[UNR];
+__global__ __launch_bounds__(256) void group_kernel(const float *__restrict__ U, const float2 *__restrict__ stats,
+                                                    const uint32_t *__restrict__ cand, int mask_words,
+                                                    float *__restrict__ S2, uint32_t *__restrict__ keys,
+                                                    uint2 *__restrict__ kbounds, int G, int n, int tiles,
+                                                    int slices) {
+    constexpr int TPS = kGroupSlice / 64;  // tiles per slice
+    constexpr int UNR = kGroupSlice / 256;  // chunks per thread
+    __shared__ float s_w[TPS][GP];
+    __shared__ float s_m[GP], s_inv[GP];
+    __shared__ uint32_t s_red[2][4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int sl = blockIdx.x, bh = blockIdx.y;
+    const int j0 = sl * kGroupSlice;
+    const float *Ub = U + static_cast<size_t>(bh) * n * G;
+    const uint32_t *cm = cand + static_cast<size_t>(bh) * mask_words;
+
+    // the slice's U rows and mask words are loaded first, under the reduction
+    float v[UNR][GP];
+    uint32_t word[UNR];
 #pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            const int j = j0 + tid + nt * u;
-            const int jj = j < n ? j : 0;
-            word[u] = cm[jj >> 5];
-            if (G == GP) {
+    for (int u = 0; u < UNR; ++u) {
+        const int j = min(j0 + tid + 256 * u, n - 1);
+        word[u] = cm[j >> 5];
+        if (G == GP) {
 #pragma unroll
-                for (int q4 = 0; q4 < GP / 4; ++q4) {
-                    const float4 f = *reinterpret_cast<const float4 *>(Ub + static_cast<size_t>(jj) * GP + 4 * q4);
-                    v[u][4 * q4] = f.x; v[u][4 * q4 + 1] = f.y; v[u][4 * q4 + 2] = f.z; v[u][4 * q4 + 3] = f.w;
-                }
-            } else {
-#pragma unroll
-                for (int g = 0; g < GP; ++g) v[u][g] = g < G ? Ub[static_cast<size_t>(jj) * G + g] : 0.f;
+            for (int q4 = 0; q4 < GP / 4; ++q4) {
+                const float4 f = *reinterpret_cast<const float4 *>(Ub + static_cast<size_t>(j) * GP + 4 * q4);
+                v[u][4 * q4] = f.x; v[u][4 * q4 + 1] = f.y; v[u][4 * q4 + 2] = f.z; v[u][4 * q4 + 3] = f.w;
             }
-        }
+        } else {
 #pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            const int j = j0 + tid + nt * u;
-            if (j >= n) continue;
-            const bool valid = (word[u] >> (j & 31)) & 1u;
-            const float *wt = w + (j >> 6) * G;
-            float acc = 0.f;
-#pragma unroll
-            for (int g = 0; g < GP; ++g)
-                if (g < G) acc += v[u][g] * wt[g];
-            S2b[j] = valid ? acc : 0.f;
-            keys[j] = valid ? float_key(acc) : 0u;
+            for (int g = 0; g < GP; ++g) v[u][g] = g < G ? Ub[static_cast<size_t>(j) * G + g] : 0.f;
         }
+    }
+    for (int g = wave; g < G; g += 4) {
+        const float2 *st = stats + (static_cast<size_t>(bh) * G + g) * tiles;
+        float m = -INFINITY;
+        for (int t = lane; t < tiles; t += 64) m = fmaxf(m, st[t].x);
+        m = wave_max(m);
+        float z = 0.f;
+        for (int t = lane; t < tiles; t += 64) {
+            const float2 x = st[t];
+            z += x.x == -INFINITY ? 0.f : x.y * expf(x.x - m);
+        }
+        z = wave_sum(z);
+        if (lane == 0) {
+            s_m[g] = m;
+            s_inv[g] = z > 0.f ? 1.f / (z * static_cast<float>(G)) : 0.f;
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < TPS * G; i += 256) {
+        const int tl = i / G, g = i % G, t = j0 / 64 + tl;
+        const float2 x = t < tiles ? stats[(static_cast<size_t>(bh) * G + g) * tiles + t] : make_float2(-INFINITY, 0.f);
+        s_w[tl][g] = x.x == -INFINITY ? 0.f : expf(x.x - s_m[g]) * s_inv[g];
+    }
+    __syncthreads();
+    uint32_t kmn = 0xffffffffu, kmx = 0u;
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+        const int j = j0 + tid + 256 * u;
+        if (j >= n) continue;
+        const bool valid = (word[u] >> (j & 31)) & 1u;
+        const float *wt = s_w[(j - j0) >> 6];
+        float acc = 0.f;
+#pragma unroll
+        for (int g = 0; g < GP; ++g)
+            if (g < G) acc += v[u][g] * wt[g];
+        S2[static_cast<size_t>(bh) * n + j] = valid ? acc : 0.f;
+        const uint32_t key = float_key(acc);
+        keys[static_cast<size_t>(bh) * n + j] = valid ? key : 0u;
+        if (valid) { kmn = min(kmn, key); kmx = max(kmx, key); }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        kmn = min(kmn, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmn), off, 64)));
+        kmx = max(kmx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmx), off, 64)));
+    }
+    if (lane == 0) { s_red[0][wave] = kmn; s_red[1][wave] = kmx; }
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t a = s_red[0][0], c = s_red[1][0];
+        for (int w = 1; w < 4; ++w) { a = min(a, s_red[0][w]); c = max(c, s_red[1][w]); }
+        kbounds[static_cast<size_t>(bh) * slices + sl] = make_uint2(a, c);
     }
 }
 
 // ---------------------------------------------------------------------------
-// Decode selection, one workgroup per (sequence, KV head):
-//  1. (m_g, Z_g) of every query head of the group from the score tiles;
-//  2. S2[j] = (1/G) sum_g exp(P[j, g] - m_g) / Z_g over selectable j (0
-//     elsewhere), kept as order-preserving keys (selectable keys > 0);
-//  3. I = ArgTopK(S2, k), ascending;
-//  4. set difference against the resident chunks: a slot keeps its chunk when
+// Decode selection, one workgroup per (sequence, KV head) row:
+//  1. the row's keys (from the group kernel) into LDS when they fit, and
+//     their bounds from the per-slice minima and maxima;
+//  2. I = ArgTopK(S2, k) by radix selection, ascending;
+//  3. set difference against the resident chunks: a slot keeps its chunk when
 //     the chunk is selected again (hit); the m-th missing chunk (ascending)
 //     goes to the m-th freed slot (ascending); emit the miss list and count
 //     hits and misses.
 // ---------------------------------------------------------------------------
-template <int GP>
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(
-    const float *__restrict__ P, const float2 *__restrict__ stats, const uint32_t *__restrict__ cand, int mask_words,
-    float *__restrict__ S2, int32_t *__restrict__ sel, int32_t *__restrict__ slot_chunk, int2 *__restrict__ misses,
-    int32_t *__restrict__ miss_count, unsigned long long *__restrict__ counters, uint32_t *__restrict__ gscratch,
-    int use_lds, int G, int n, int k, int tiles) {
+    const uint32_t *__restrict__ keys_g, const uint2 *__restrict__ kbounds, int slices, int32_t *__restrict__ sel,
+    int32_t *__restrict__ slot_chunk, int2 *__restrict__ misses, int32_t *__restrict__ miss_count,
+    unsigned long long *__restrict__ counters, int use_lds, int n, int k) {
     extern __shared__ uint32_t dyn[];
     __shared__ SelectScratch sc;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nt = blockDim.x, nw = nt >> 6;
+    const int tid = threadIdx.x, nt = blockDim.x;
     const int bh = blockIdx.x;
     int32_t *s_sel = reinterpret_cast<int32_t *>(dyn);  // k selected chunks, ascending
     int32_t *s_keep = s_sel + k;                        // k: chunk kept by each slot, -1 if freed
     int32_t *s_hit = s_keep + k;                        // k: 1 if selected chunk i is resident
     int32_t *s_rank = s_hit + k;                        // k: index in s_sel of the m-th miss
-    float *s_w = reinterpret_cast<float *>(s_rank + k);  // tiles * G tile weights
-    uint32_t *keys = use_lds ? reinterpret_cast<uint32_t *>(s_w + tiles * G) : gscratch + static_cast<size_t>(bh) * n;
+    const uint32_t *krow = keys_g + static_cast<size_t>(bh) * n;
+    uint32_t *keys = use_lds ? reinterpret_cast<uint32_t *>(s_rank + k) : const_cast<uint32_t *>(krow);
 
-    // per head: m = max_t M_t, Z = sum_t S_t exp(M_t - m); w[t] = exp(M_t - m) / (Z G)
+    if (use_lds) {
+        for (int j0 = 0; j0 < n; j0 += 4 * nt) {
+            uint32_t t[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int j = j0 + tid + u * nt;
+                t[u] = j < n ? krow[j] : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int j = j0 + tid + u * nt;
+                if (j < n) keys[j] = t[u];
+            }
+        }
+    }
     for (int i = tid; i < 4096; i += nt) sc.hist[i] = 0;
     for (int i = tid; i < k; i += nt) s_hit[i] = 0;
-    for (int g = wave; g < G; g += nw) {
-        const float2 *st = stats + (static_cast<size_t>(bh) * G + g) * tiles;
-        constexpr int TPL = 8;  // tiles held per lane (more are streamed)
-        float2 v[TPL];
-#pragma unroll
-        for (int i = 0; i < TPL; ++i) {
-            const int t = lane + 64 * i;
-            v[i] = t < tiles ? st[t] : make_float2(-INFINITY, 0.f);
-        }
-        float m = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < TPL; ++i) m = fmaxf(m, v[i].x);
-        for (int t = lane + 64 * TPL; t < tiles; t += 64) m = fmaxf(m, st[t].x);
-        m = wave_max(m);
-        float z = 0.f;
-#pragma unroll
-        for (int i = 0; i < TPL; ++i) z += v[i].x == -INFINITY ? 0.f : v[i].y * expf(v[i].x - m);
-        for (int t = lane + 64 * TPL; t < tiles; t += 64) z += st[t].x == -INFINITY ? 0.f : st[t].y * expf(st[t].x - m);
-        z = wave_sum(z);
-        const float inv = z > 0.f ? 1.f / (z * static_cast<float>(G)) : 0.f;
-#pragma unroll
-        for (int i = 0; i < TPL; ++i) {
-            const int t = lane + 64 * i;
-            if (t < tiles) s_w[t * G + g] = v[i].x == -INFINITY ? 0.f : expf(v[i].x - m) * inv;
-        }
-        for (int t = lane + 64 * TPL; t < tiles; t += 64) s_w[t * G + g] = st[t].x == -INFINITY ? 0.f : expf(st[t].x - m) * inv;
+    uint32_t kmn = 0xffffffffu, kmx = 0u;
+    for (int i = tid; i < slices; i += nt) {
+        const uint2 b2 = kbounds[static_cast<size_t>(bh) * slices + i];
+        kmn = min(kmn, b2.x);
+        kmx = max(kmx, b2.y);
     }
-    __syncthreads();
-    group_scores<GP>(P + static_cast<size_t>(bh) * n * G, cand + static_cast<size_t>(bh) * mask_words, s_w, G, n,
-                     S2 + static_cast<size_t>(bh) * n, keys);
-    __syncthreads();
-    if (k <= 0) return;
-    radix_topk(keys, n, k, sel + static_cast<size_t>(bh) * k, s_sel, sc);
+    block_minmax(kmn, kmx, sc);  // its barriers also publish the keys
+    if (k <= 0 || kmn > kmx) return;
+    radix_topk(keys, n, k, kmn, kmx, sel + static_cast<size_t>(bh) * k, s_sel, sc);
     __syncthreads();
 
     // set difference: a slot keeps its chunk if the chunk is selected again
@@ -485,24 +620,33 @@ static hipError_t allow_lds(const void *fn, size_t bytes) {
     return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
 }
 
+static int score_mode(const Dims &dm) { return dm.G <= 4 ? 0 : (dm.G % 4 == 0 ? 1 : 2); }
+
 hipError_t launch_score(const Dims &dm, const void *q, const void *landmarks, const uint32_t *cand, float *P,
-                        float2 *stats, hipStream_t st) {
-    dim3 grid(dm.score_tiles, dm.b * dm.hkv);
+                        float2 *stats, int score_wgs, hipStream_t st) {
     if (dm.bf16) {
         const uint16_t *qq = static_cast<const uint16_t *>(q), *LL = static_cast<const uint16_t *>(landmarks);
-        if (dm.d == 128 && dm.G <= 4)
-            hipLaunchKernelGGL((score_mfma_kernel<128, true>), grid, dim3(256), 0, st, qq, LL, cand, dm.mask_words, P,
-                               stats, dm.hkv, dm.G, dm.n, dm.wtiles, dm.scale);
-        else if (dm.d == 128)
-            hipLaunchKernelGGL((score_mfma_kernel<128, false>), grid, dim3(256), 0, st, qq, LL, cand, dm.mask_words, P,
-                               stats, dm.hkv, dm.G, dm.n, dm.wtiles, dm.scale);
-        else if (dm.G <= 4)
-            hipLaunchKernelGGL((score_mfma_kernel<64, true>), grid, dim3(256), 0, st, qq, LL, cand, dm.mask_words, P,
-                               stats, dm.hkv, dm.G, dm.n, dm.wtiles, dm.scale);
-        else
-            hipLaunchKernelGGL((score_mfma_kernel<64, false>), grid, dim3(256), 0, st, qq, LL, cand, dm.mask_words, P,
-                               stats, dm.hkv, dm.G, dm.n, dm.wtiles, dm.scale);
+        const int rows = dm.b * dm.hkv, total = rows * dm.wtiles;
+        // default: two tiles per wave (measured best on MI355X at 128K)
+        const int want = score_wgs > 0 ? score_wgs : (total + 7) / 8;
+        const int wgs = std::max(1, std::min(want, (total + 3) / 4));
+        const int tpw = (total + 4 * wgs - 1) / (4 * wgs);
+        auto go = [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3(wgs), dim3(256), 0, st, qq, LL, cand, dm.mask_words, P, stats, dm.hkv,
+                               dm.G, dm.n, dm.wtiles, rows, tpw, dm.scale);
+        };
+        const int m = score_mode(dm);
+        if (dm.d == 128) {
+            if (m == 0) go(score_mfma_kernel<128, 0>);
+            else if (m == 1) go(score_mfma_kernel<128, 1>);
+            else go(score_mfma_kernel<128, 2>);
+        } else {
+            if (m == 0) go(score_mfma_kernel<64, 0>);
+            else if (m == 1) go(score_mfma_kernel<64, 1>);
+            else go(score_mfma_kernel<64, 2>);
+        }
     } else {
+        dim3 grid(dm.score_tiles, dm.b * dm.hkv);
         if (dm.d == 128)
             hipLaunchKernelGGL((score_generic_kernel<float, 128>), grid, dim3(256), 0, st,
                                static_cast<const float *>(q), static_cast<const float *>(landmarks), cand,
@@ -516,36 +660,38 @@ hipError_t launch_score(const Dims &dm, const void *q, const void *landmarks, co
 }
 
 size_t select_dynamic_lds(const Dims &dm, bool keys_in_lds) {
-    return 4ull * dm.k * sizeof(int32_t) + static_cast<size_t>(dm.wtiles) * dm.G * sizeof(float) +
-           (keys_in_lds ? static_cast<size_t>(dm.n) * sizeof(uint32_t) : 0);
+    return 4ull * dm.k * sizeof(int32_t) + (keys_in_lds ? static_cast<size_t>(dm.n) * sizeof(uint32_t) : 0);
 }
 
 size_t select_static_lds() { return sizeof(SelectScratch); }
 
-template <int GP>
-static hipError_t select_t(const Dims &dm, const float *P, const float2 *stats, const uint32_t *cand, float *S2,
-                           int32_t *sel, int32_t *slot_chunk, int2 *misses, int32_t *miss_count,
-                           unsigned long long *counters, uint32_t *gscratch, int keys_in_lds, hipStream_t st) {
-    const size_t lds = select_dynamic_lds(dm, keys_in_lds != 0);
-    hipError_t e = allow_lds(reinterpret_cast<const void *>(select_kernel<GP>), lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(select_kernel<GP>, dim3(dm.b * dm.hkv), dim3(kSelectThreads), lds, st, P, stats, cand,
-                       dm.mask_words, S2, sel, slot_chunk, misses, miss_count, counters, gscratch, keys_in_lds,
-                       dm.G, dm.n, dm.k, dm.wtiles);
+int group_slices(const Dims &dm) { return (dm.n + kGroupSlice - 1) / kGroupSlice; }
+
+hipError_t launch_group(const Dims &dm, const float *P, const float2 *stats, const uint32_t *cand, float *S2,
+                        uint32_t *keys, uint2 *kbounds, hipStream_t st) {
+    const int slices = group_slices(dm);
+    dim3 grid(slices, dm.b * dm.hkv);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, P, stats, cand, dm.mask_words, S2, keys, kbounds, dm.G, dm.n,
+                           dm.wtiles, slices);
+    };
+    switch (dm.GP) {
+        case 4: go(group_kernel<4>); break;
+        case 8: go(group_kernel<8>); break;
+        default: go(group_kernel<16>); break;
+    }
     return hipGetLastError();
 }
 
-hipError_t launch_select(const Dims &dm, const float *P, const float2 *stats, const uint32_t *cand, float *S2,
-                         int32_t *sel, int32_t *slot_chunk, int2 *misses, int32_t *miss_count,
-                         unsigned long long *counters, uint32_t *gscratch, int keys_in_lds, hipStream_t st) {
-    switch (dm.GP) {
-        case 4: return select_t<4>(dm, P, stats, cand, S2, sel, slot_chunk, misses, miss_count, counters, gscratch,
-                                   keys_in_lds, st);
-        case 8: return select_t<8>(dm, P, stats, cand, S2, sel, slot_chunk, misses, miss_count, counters, gscratch,
-                                   keys_in_lds, st);
-        default: return select_t<16>(dm, P, stats, cand, S2, sel, slot_chunk, misses, miss_count, counters,
-                                     gscratch, keys_in_lds, st);
-    }
+hipError_t launch_select(const Dims &dm, const uint32_t *keys, const uint2 *kbounds, int32_t *sel,
+                         int32_t *slot_chunk, int2 *misses, int32_t *miss_count, unsigned long long *counters,
+                         int keys_in_lds, hipStream_t st) {
+    const size_t lds = select_dynamic_lds(dm, keys_in_lds != 0);
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(select_kernel), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(select_kernel, dim3(dm.b * dm.hkv), dim3(kSelectThreads), lds, st, keys, kbounds,
+                       group_slices(dm), sel, slot_chunk, misses, miss_count, counters, keys_in_lds, dm.n, dm.k);
+    return hipGetLastError();
 }
 
 hipError_t launch_topo(const Dims &dm, const float *min_cos, int32_t *outliers, uint32_t *gscratch, int keys_in_lds,

@@ -17,6 +17,35 @@ typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 constexpr int kWave = 64;
 
 // ---------------------------------------------------------------------------
+// Raw buffer access.  A buffer resource covers `bytes` bytes from `base`
+// (bytes < kOob, checked on the host by the layer's shape validation); a load at an offset at or past the end returns zeros and a
+// store there is dropped, by the hardware and without a memory access.
+// Kernels use this for predicated loads and stores: every lane issues the
+// same instruction (kOob as the offset switches a lane off), so there are no
+// branches around memory operations and the compiler's wait counts stay
+// exact.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+constexpr int kOob = 0x7fff0000;  // an offset past every resource, far from 2^32
+
+__device__ __forceinline__ Rsrc make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_ld128(Rsrc r, int off) { return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0); }
+__device__ __forceinline__ uint32_t buf_ld32(Rsrc r, int off) { return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0); }
+__device__ __forceinline__ void buf_st32(float v, Rsrc r, int off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_st64(float2 v, Rsrc r, int off) {
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(v.x), __float_as_uint(v.y)}, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_st128(float4 v, Rsrc r, int off) {
+    __builtin_amdgcn_raw_buffer_store_b128(
+        u32x4{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)}, r, off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
 // Storage types: binary32 (float) or bfloat16 carried as its 16 raw bits.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {

@@ -9,7 +9,7 @@ namespace skv {
 // Tile sizes.
 constexpr int kScoreTile = 256;   // chunks per scoring workgroup (4 waves x 64)
 constexpr int kSelectThreads = 1024;  // one workgroup per (sequence, KV head) row
-constexpr int kXcds = 8;              // XCDs of an MI355X; workgroups are dealt round-robin
+constexpr int kGroupSlice = 1024;     // chunks per group-score workgroup
 constexpr int kQkTile = 64;       // keys per generic QK workgroup
 constexpr int kQkMfmaTile = 256;  // keys per MFMA QK workgroup (4 waves x 64)
 constexpr int kPvTile = 256;      // keys per PV workgroup
@@ -47,20 +47,27 @@ hipError_t launch_fill_i32(int32_t *p, int32_t value, size_t count, hipStream_t 
 hipError_t launch_validate_outliers(const Dims &dm, const int32_t *outliers, int32_t *bad, hipStream_t st);
 
 // Decode.
+// score_wgs: workgroups of the persistent bfloat16 scoring kernel (0: two
+// 64-chunk tiles per wave).
 hipError_t launch_score(const Dims &dm, const void *q, const void *landmarks, const uint32_t *cand,
-                        float *P, float2 *stats, hipStream_t st);
+                        float *P, float2 *stats, int score_wgs, hipStream_t st);
+// Group score: kbounds holds one (min, max) key pair per row and slice of
+// kGroupSlice chunks.
+int group_slices(const Dims &dm);
+hipError_t launch_group(const Dims &dm, const float *P, const float2 *stats, const uint32_t *cand, float *S2,
+                        uint32_t *keys, uint2 *kbounds, hipStream_t st);
 // LDS of the select kernel: dynamic part (slot arrays, and the keys when they
 // fit) and static part.
 size_t select_dynamic_lds(const Dims &dm, bool keys_in_lds);
 size_t select_static_lds();
-hipError_t launch_select(const Dims &dm, const float *P, const float2 *stats, const uint32_t *cand, float *S2,
-                         int32_t *sel, int32_t *slot_chunk, int2 *misses, int32_t *miss_count,
-                         unsigned long long *counters, uint32_t *gscratch, int keys_in_lds, hipStream_t st);
+hipError_t launch_select(const Dims &dm, const uint32_t *keys, const uint2 *kbounds, int32_t *sel,
+                         int32_t *slot_chunk, int2 *misses, int32_t *miss_count, unsigned long long *counters,
+                         int keys_in_lds, hipStream_t st);
 hipError_t launch_fetch(const Dims &dm, const void *v_host, void *vc, const int2 *misses,
-                        const int32_t *miss_count, int waves, int xcds, hipStream_t st);
+                        const int32_t *miss_count, int waves, hipStream_t st);
 hipError_t launch_qk(const Dims &dm, const void *q, const void *k_out, const void *k_loc, const void *A,
                      const void *Bt, const int32_t *slot_chunk, const double *theta, const double *theta_rev,
-                     const float2 *rope_off, float *logits, hipStream_t st);
+                     float *logits, hipStream_t st);
 hipError_t launch_pv(const Dims &dm, const float *logits, const void *v_out, const void *vc,
                      const void *v_loc, float2 *part_ml, float *part_acc, hipStream_t st);
 hipError_t launch_combine(const Dims &dm, const float2 *part_ml, const float *part_acc, void *out,
