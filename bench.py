@@ -1,9 +1,9 @@
 """Throughput of the ShadowKV sparse decode step on one MI355X.
 
 A step is one decode step of the model: every layer's shadowkv_decode_step
-(score landmarks, select top-k chunks, set-difference cache update, host-V
-fetch of the misses on a second stream, MFMA key rebuild + RoPE + logits,
-PV and combine) for all b sequences, one token each.  The metric is
+(score landmarks, group score, select top-k chunks, set-difference cache
+update, host-V fetch of the misses, MFMA key rebuild + RoPE + logits, PV and
+combine) for all b sequences, one token each.  The metric is
 layer-steps/s (one layer-step = one shadowkv_decode_step call) with the
 effective HBM bandwidth (algorithmic bytes / time) and the equivalent
 bandwidth (dense K+V bytes / time, the review page's B~ measured).
@@ -16,6 +16,14 @@ fetch over PCIe is a step of the method itself (Algorithm 2 step 3), so it is
 inside the timed region.
 
 Output: one JSON line on stdout (progress goes to stderr).
+
+Traffic counters: run the bench twice under `rocprofv3 --pmc FETCH_SIZE`
+and `--pmc WRITE_SIZE` (CSV output) with --copy-calibration, which adds a
+device copy of known size; `bench.py --ingest-counters FETCH.csv WRITE.csv`
+then writes profiles/traffic_score_<workload>.json (bytes per launch of the
+scoring kernel, each counter scaled by what it reads for the copy), which
+later bench lines report as roofline.traffic while the kernel sources are
+unchanged.
 """
 from __future__ import annotations
 
@@ -74,6 +82,49 @@ def measured_traffic(workload: str):
     return rec.get("bytes_per_launch")
 
 
+COPY_BYTES = 256 << 20  # the calibration copy
+
+
+def ingest_counters(fetch_csv: str, write_csv: str, workload: str, command: str) -> int:
+    """Scoring-kernel HBM bytes per launch from two rocprofv3 counter CSVs."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals, names = {}, {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            vals[d] = vals.get(d, 0.0) + float(r["Counter_Value"])
+            names[d] = r["Kernel_Name"]
+        score = sorted(d for d in vals if "score_mfma_kernel" in names[d])
+        # the calibration copy is the last copy dispatched before the first
+        # scoring launch (bench.py runs it right before the warmup)
+        copies = [d for d in vals if "copyBuffer" in names[d] and score and d < score[0]]
+        if not score or not copies:
+            raise SystemExit(f"{path}: no {counter} values for the scoring kernel or the calibration copy")
+        return sum(vals[d] for d in score) / len(score), vals[max(copies)], len(score)
+
+    f_kib, f_copy_kib, nf = per_kernel(fetch_csv, "FETCH_SIZE")
+    w_kib, w_copy_kib, nw = per_kernel(write_csv, "WRITE_SIZE")
+    f_scale = COPY_BYTES / (f_copy_kib * 1024.0)
+    w_scale = COPY_BYTES / (w_copy_kib * 1024.0)
+    fetch_b = f_kib * 1024.0 * f_scale
+    write_b = w_kib * 1024.0 * w_scale
+    rec = {"workload": workload, "kernel": "score_mfma_kernel", "source_hash": kernel_source_hash(),
+           "fetch_bytes_per_launch": int(fetch_b), "write_bytes_per_launch": int(write_b),
+           "bytes_per_launch": int(fetch_b + write_b),
+           "raw_KiB": {"FETCH_SIZE": f_kib, "WRITE_SIZE": w_kib, "copy_FETCH_SIZE": f_copy_kib,
+                       "copy_WRITE_SIZE": w_copy_kib},
+           "copy_scale": {"FETCH_SIZE": f_scale, "WRITE_SIZE": w_scale}, "dispatches": [nf, nw],
+           "command": command}
+    out = os.path.join(ROOT, "profiles", f"traffic_score_{workload}.json")
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -88,7 +139,16 @@ def main() -> int:
     ap.add_argument("--kernel-events", choices=["on", "off"], default="on")
     ap.add_argument("--overlap", choices=["on", "off"], default="off",
                     help="fetch beside the key rebuild (on) or before it (off)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a device copy of 256 MiB (traffic-counter calibration)")
+    ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_score_<workload>.json from rocprofv3 counter CSVs and exit")
+    ap.add_argument("--counter-command", default="",
+                    help="with --ingest-counters: the command that produced the CSVs (recorded)")
     args = ap.parse_args()
+    if args.ingest_counters:
+        return ingest_counters(args.ingest_counters[0], args.ingest_counters[1], args.workload,
+                               args.counter_command)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -150,6 +210,13 @@ def main() -> int:
         for t in range(t_begin, t_begin + t_count):
             for l in range(layers):
                 Ls[l].decode_step(qs[l][t], outs[l], stream)
+
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # ---- warmup ---------------------------------------------------------------
     run_steps(0, args.warmup)
@@ -239,29 +306,35 @@ def main() -> int:
         meta = oracle.prefill(shape, kp, vv)
         A_o, B_o = oracle.svd_factors(shape, kp)
         q_all = qs[spot_layer][:, seqs].float().cpu().double().numpy()
-        # decode steps 0, 1, ... until the time budget is spent or the last
-        # timed step is reached (then the GPU's output there is spot-checked)
+        # decode steps 0, 1, ..., nq - 1 (the GPU's output at the last timed
+        # step is spot-checked there), then again from step 0 until the time
+        # budget is spent; the oracle's decode does not depend on the cache
         t_last = args.warmup + args.steps - 1
         t_start = time.perf_counter()
-        n_done, res = 0, None
-        for t in range(nq):
+        n_done, res, res_last = 0, None, None
+        while True:
+            t = n_done % nq
             res = oracle.decode(shape, q_all[t], meta, A_o, B_o, vv)
+            if t == t_last:
+                res_last = res
             n_done += 1
-            if time.perf_counter() - t_start > args.cpu_baseline_seconds:
+            if n_done >= nq and time.perf_counter() - t_start > args.cpu_baseline_seconds:
                 break
         cpu_s = time.perf_counter() - t_start
         per_seq_step = cpu_s / (n_done * len(seqs))
-        cores = min(os.cpu_count() or 1, len(seqs) * wl.h_kv)
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+        cores = min(threads, os.cpu_count() or 1, len(seqs) * wl.h_kv)
         cpu_baseline = {"value": round(1.0 / (per_seq_step * wl.b), 4), "unit": "layer-steps/s", "cores": cores,
                         "kind": "oracle",
-                        "sample": f"{n_done} decode steps of sequences {seqs} (of {wl.b}) of one layer; "
-                                  f"{cpu_s:.1f} s of CPU time; scaled to all {wl.b} sequences"}
-        if n_done - 1 == t_last:
+                        "sample": f"{n_done} decode steps (steps 0..{nq - 1}, cycled) of sequences {seqs} "
+                                  f"(of {wl.b}) of layer {spot_layer}; {cpu_s:.1f} s of CPU time; "
+                                  f"scaled to all {wl.b} sequences"}
+        if res_last is not None:
             gpu_out = last_out[seqs].float().cpu().double().numpy()
             gpu_sel = Ls[spot_layer].read(skv.SKV_T_SELECTION)[seqs].cpu().numpy()
             parity = {"layer": spot_layer, "step": t_last, "sequences": seqs,
-                      "selection_equal": bool(np.array_equal(gpu_sel, res["sel"])),
-                      "max_abs_err_vs_oracle": float(np.max(np.abs(gpu_out - res["out"]))),
+                      "selection_equal": bool(np.array_equal(gpu_sel, res_last["sel"])),
+                      "max_abs_err_vs_oracle": float(np.max(np.abs(gpu_out - res_last["out"]))),
                       "tolerance": 2e-2 if wl.bf16 else 1e-4}
         log(f"cpu baseline: {cpu_baseline['value']} layer-steps/s on {cores} threads")
 

@@ -28,7 +28,8 @@
  * work has run).  The pinned host V buffer is borrowed for the layer's
  * lifetime.  The library owns its copies of A and B, the landmarks, the
  * outlier and local buffers, the resident V cache with its slot map, all
- * scratch, and one extra HIP stream plus events per layer.
+ * scratch, the layer's events, and two HIP streams per device (shared by the
+ * layers on it) for the optional fetch / rebuild overlap.
  */
 #ifndef SHADOWKV_H
 #define SHADOWKV_H
@@ -150,9 +151,10 @@ int shadowkv_load_meta(skv_layer *layer, const void *landmarks, const int32_t *o
  * KV group -- the page leaves S2 undefined, this is the reading taken);
  * I = ArgTopK(S2, k) per (sequence, KV head) with ties to the lower index;
  * the set difference against the previous step's resident chunks; V of the
- * missing chunks read from v_host on the layer's second stream while the
- * selected keys are rebuilt as Gather(A, I) . B and rotated at their
- * original positions; softmax attention over
+ * missing chunks read from v_host (after the selection; beside the key
+ * rebuild on a second stream if shadowkv_set_overlap enabled it); the
+ * selected keys rebuilt as Gather(A, I) . B and rotated at their original
+ * positions; softmax attention over
  * [outlier keys; rebuilt keys; local-window keys] with the matching values.
  * Enqueued on `stream`; `out` is valid once `stream` has reached this point.
  * SKV_E_STATE before prefill_meta / load_meta.
@@ -208,7 +210,7 @@ int shadowkv_set_overlap(skv_layer *layer, int enable);
 enum {
     SKV_K_SCORE = 0,    /* landmark scores + per-tile softmax partials      */
     SKV_K_SELECT = 1,   /* group score S2, ArgTopK, set difference          */
-    SKV_K_FETCH = 2,    /* V of missing chunks from pinned host (2nd stream)*/
+    SKV_K_FETCH = 2,    /* V of missing chunks from pinned host memory      */
     SKV_K_QK = 3,       /* logits: static keys, rebuilt keys + RoPE         */
     SKV_K_PV = 4,       /* probabilities times values, split merge          */
     SKV_K_COUNT = 5

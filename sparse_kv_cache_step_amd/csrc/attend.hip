@@ -24,6 +24,7 @@ namespace skv {
 // into its cache slot, every load of the chunk in flight before the stores.
 // Only real misses are visited, so the PCIe reads are issued back to back.
 // ---------------------------------------------------------------------------
+template <int VPL>  // 16-byte vectors per lane and chunk (0: any, looped)
 __global__ __launch_bounds__(256) void fetch_kernel(const u32x4 *__restrict__ v_host, u32x4 *__restrict__ vc,
                                                     const int2 *__restrict__ misses,
                                                     const int32_t *__restrict__ miss_count, int rows, int k, int n,
@@ -52,27 +53,48 @@ __global__ __launch_bounds__(256) void fetch_kernel(const u32x4 *__restrict__ v_
     __syncthreads();
     const int total = pre[rows];
     const int gw = blockIdx.x * 4 + wave, nw = gridDim.x * 4;
-    for (int g = gw; g < total; g += nw) {
-        int lo = 0, hi = rows - 1;  // the row r with pre[r] <= g < pre[r + 1]
+    // the miss with global index g: its row (pre[r] <= g < pre[r + 1]) and
+    // its (chunk, slot) entry
+    auto locate = [&](int g, int &row) {
+        int lo = 0, hi = rows - 1;
         while (lo < hi) {
             const int mid = (lo + hi + 1) >> 1;
             if (pre[mid] <= g) lo = mid; else hi = mid - 1;
         }
-        const int2 e = misses[static_cast<size_t>(lo) * k + (g - pre[lo])];
-        const u32x4 *src = v_host + (static_cast<size_t>(lo) * n + e.x) * chunk_vec;
-        u32x4 *dst = vc + (static_cast<size_t>(lo) * k + e.y) * chunk_vec;
-        for (int i0 = 0; i0 < chunk_vec; i0 += 256) {
-            u32x4 t[4];
+        row = lo;
+        return misses[static_cast<size_t>(lo) * k + (g - pre[lo])];
+    };
+    int g = gw, row = 0;
+    int2 e = g < total ? locate(g, row) : make_int2(0, 0);
+    for (; g < total; g += nw) {
+        const u32x4 *src = v_host + (static_cast<size_t>(row) * n + e.x) * chunk_vec;
+        u32x4 *dst = vc + (static_cast<size_t>(row) * k + e.y) * chunk_vec;
+        if constexpr (VPL > 0) {
+            u32x4 t[VPL];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i = i0 + u * 64 + lane;
-                if (i < chunk_vec) t[u] = __builtin_nontemporal_load(src + i);
-            }
+            for (int u = 0; u < VPL; ++u) t[u] = __builtin_nontemporal_load(src + u * 64 + lane);
+            // the next miss is located while this chunk's host reads are in flight
+            int row_n = row;
+            const int2 e_n = g + nw < total ? locate(g + nw, row_n) : e;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i = i0 + u * 64 + lane;
-                if (i < chunk_vec) dst[i] = t[u];
+            for (int u = 0; u < VPL; ++u) dst[u * 64 + lane] = t[u];
+            row = row_n;
+            e = e_n;
+        } else {
+            for (int i0 = 0; i0 < chunk_vec; i0 += 256) {
+                u32x4 t[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int i = i0 + u * 64 + lane;
+                    if (i < chunk_vec) t[u] = __builtin_nontemporal_load(src + i);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int i = i0 + u * 64 + lane;
+                    if (i < chunk_vec) dst[i] = t[u];
+                }
             }
+            if (g + nw < total) e = locate(g + nw, row);
         }
     }
 }
@@ -502,13 +524,41 @@ __global__ __launch_bounds__(D) void combine_kernel(const float2 *__restrict__ p
                                                     int tiles) {
     const int bg = blockIdx.x, i = threadIdx.x;
     const float2 *ml = part_ml + static_cast<size_t>(bg) * tiles;
+    const float *pa = part_acc + static_cast<size_t>(bg) * tiles * D + i;
+    constexpr int TMAX = 16;  // splits held in registers (all loads in flight); more are streamed
+    if (tiles <= TMAX) {
+        const Rsrc mr = make_rsrc(ml, static_cast<uint32_t>(tiles) * 8);
+        const Rsrc ar = make_rsrc(pa - i, static_cast<uint32_t>(tiles) * D * 4);
+        float m[TMAX], l[TMAX], a[TMAX];
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+            m[t] = __uint_as_float(buf_ld32(mr, t < tiles ? t * 8 : kOob));
+            l[t] = __uint_as_float(buf_ld32(mr, t < tiles ? t * 8 + 4 : kOob));
+            a[t] = __uint_as_float(buf_ld32(ar, t < tiles ? (t * D + i) * 4 : kOob));
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t)
+            if (t < tiles) M = fmaxf(M, m[t]);
+        float L = 0.f, acc = 0.f;
+#pragma unroll
+        for (int t = 0; t < TMAX; ++t) {
+            if (t < tiles) {
+                const float wgt = expf(m[t] - M);
+                L += wgt * l[t];
+                acc += wgt * a[t];
+            }
+        }
+        Elem<T>::st(out, static_cast<size_t>(bg) * D + i, acc / L);
+        return;
+    }
     float M = -INFINITY;
     for (int t = 0; t < tiles; ++t) M = fmaxf(M, ml[t].x);
     float L = 0.f, acc = 0.f;
     for (int t = 0; t < tiles; ++t) {
         const float wgt = expf(ml[t].x - M);
         L += wgt * ml[t].y;
-        acc += wgt * part_acc[(static_cast<size_t>(bg) * tiles + t) * D + i];
+        acc += wgt * pa[static_cast<size_t>(t) * D];
     }
     Elem<T>::st(out, static_cast<size_t>(bg) * D + i, acc / L);
 }
@@ -522,15 +572,23 @@ hipError_t launch_fetch(const Dims &dm, const void *v_host, void *vc, const int2
     const int rows = dm.b * dm.hkv;
     const int chunk_vec = dm.c * dm.d * dm.esize / 16;
     const size_t lds = static_cast<size_t>(rows + 1) * sizeof(int);
-    if (lds > 48 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fetch_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        if (e != hipSuccess) return e;
+    auto go = [&](auto kern) {
+        if (lds > 48 * 1024) {
+            hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(kern, dim3(std::max(1, (waves + 3) / 4)), dim3(256), lds, st,
+                           static_cast<const u32x4 *>(v_host), static_cast<u32x4 *>(vc), misses, miss_count, rows,
+                           dm.k, dm.n, chunk_vec);
+        return hipGetLastError();
+    };
+    switch (chunk_vec) {
+        case 64: return go(fetch_kernel<1>);
+        case 128: return go(fetch_kernel<2>);
+        case 256: return go(fetch_kernel<4>);
+        default: return go(fetch_kernel<0>);
     }
-    hipLaunchKernelGGL(fetch_kernel, dim3(std::max(1, (waves + 3) / 4)), dim3(256), lds, st,
-                       static_cast<const u32x4 *>(v_host), static_cast<u32x4 *>(vc), misses, miss_count, rows, dm.k,
-                       dm.n, chunk_vec);
-    return hipGetLastError();
 }
 template <typename T, int D>
 static hipError_t qk_generic_t(const Dims &dm, const void *q, const void *k_out, const void *k_loc, const void *A,

@@ -178,7 +178,7 @@ struct skv_layer {
     // shared per-device streams for the host-V fetch and the key rebuild
     hipStream_t copy = nullptr, comp = nullptr;
     hipEvent_t ev_sel = nullptr, ev_fetch = nullptr, ev_qk = nullptr;
-    int fetch_waves = 256;
+    int fetch_waves = 128;
     int score_wgs = 0;  // workgroups of the scoring kernel (0: two tiles per wave)
     // timing
     bool overlap = false;  // fetch beside the key rebuild (true) or before it

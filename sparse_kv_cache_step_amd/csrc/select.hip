@@ -318,10 +318,16 @@ __device__ void radix_topk(const uint32_t *keys, int n, int k, uint32_t kmin, ui
         const int lo = hi > 12 ? hi - 12 : 0;
         const uint32_t dmask = (1u << (hi - lo)) - 1u;
         const uint64_t want = prefix >> hi;
-        for (int j = tid; j < n; j += nt) {
-            const uint32_t key = keys[j];
-            const uint64_t rel = static_cast<uint64_t>(key - kmin);
-            if (key >= kmin && (rel >> hi) == want) atomicAdd(&sc.hist[(rel >> lo) & dmask], 1u);
+        for (int j0 = tid; j0 < n; j0 += 4 * nt) {
+            uint32_t kk[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) kk[u] = j0 + u * nt < n ? keys[j0 + u * nt] : 0u;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const uint64_t rel = static_cast<uint64_t>(kk[u] - kmin);
+                if (j0 + u * nt < n && kk[u] >= kmin && (rel >> hi) == want)
+                    atomicAdd(&sc.hist[(rel >> lo) & dmask], 1u);
+            }
         }
         __syncthreads();  // every thread has also read the previous pass's digit
         if (tid == 0) { sc.digit = 0; sc.above = 0; }
@@ -358,11 +364,16 @@ __device__ void radix_topk(const uint32_t *keys, int n, int k, uint32_t kmin, ui
     const int seg = ((n + nw - 1) / nw + 63) & ~63;
     const int j0 = min(n, wave * seg), j1 = min(n, j0 + seg);
     int cg = 0, ce = 0;
-    for (int jb = j0; jb < j1; jb += 64) {
-        const int j = jb + lane;
-        const uint32_t key = j < j1 ? keys[j] : 0u;
-        cg += __popcll(__ballot(key > thr));
-        ce += __popcll(__ballot(key == thr && j < j1));
+    for (int jb = j0; jb < j1; jb += 256) {
+        uint32_t kk[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) kk[u] = jb + u * 64 + lane < j1 ? keys[jb + u * 64 + lane] : 0u;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool in = jb + u * 64 + lane < j1;
+            cg += __popcll(__ballot(in && kk[u] > thr));
+            ce += __popcll(__ballot(in && kk[u] == thr));
+        }
     }
     if (lane == 0) { sc.wtmp[0][wave] = cg; sc.wtmp[1][wave] = ce; }
     __syncthreads();
@@ -370,21 +381,26 @@ __device__ void radix_topk(const uint32_t *keys, int n, int k, uint32_t kmin, ui
     for (int w = 0; w < wave; ++w) { gt_run += sc.wtmp[0][w]; eq_run += sc.wtmp[1][w]; }
     __syncthreads();
     const uint64_t below = (1ull << lane) - 1ull;
-    for (int jb = j0; jb < j1 && gt_run + min(eq_run, need_eq) < k; jb += 64) {
-        const int j = jb + lane;
-        const uint32_t key = j < j1 ? keys[j] : 0u;
-        const bool g = key > thr, e = key == thr && j < j1;
-        const uint64_t bg = __ballot(g), be = __ballot(e);
-        const int gb = gt_run + __popcll(bg & below), eb = eq_run + __popcll(be & below);
-        if (g || (e && eb < need_eq)) {
-            const int pos = gb + min(eb, need_eq);
-            if (pos < k) {
-                out[pos] = j;
-                if (lds_out) lds_out[pos] = j;
+    for (int jb = j0; jb < j1 && gt_run + min(eq_run, need_eq) < k; jb += 256) {
+        uint32_t kk[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) kk[u] = jb + u * 64 + lane < j1 ? keys[jb + u * 64 + lane] : 0u;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = jb + u * 64 + lane;
+            const bool g = j < j1 && kk[u] > thr, e = j < j1 && kk[u] == thr;
+            const uint64_t bg = __ballot(g), be = __ballot(e);
+            const int gb = gt_run + __popcll(bg & below), eb = eq_run + __popcll(be & below);
+            if (g || (e && eb < need_eq)) {
+                const int pos = gb + min(eb, need_eq);
+                if (pos < k) {
+                    out[pos] = j;
+                    if (lds_out) lds_out[pos] = j;
+                }
             }
+            gt_run += __popcll(bg);
+            eq_run += __popcll(be);
         }
-        gt_run += __popcll(bg);
-        eq_run += __popcll(be);
     }
 }
 
@@ -427,8 +443,8 @@ __global__ __launch_bounds__(256) void group_kernel(const float *__restrict__ U,
                                                     int slices) {
     constexpr int TPS = kGroupSlice / 64;  // tiles per slice
     constexpr int UNR = kGroupSlice / 256;  // chunks per thread
+    static_assert(TPS <= 64 && 64 % TPS == 0, "a slice's tiles sit in one 64-tile register block");
     __shared__ float s_w[TPS][GP];
-    __shared__ float s_m[GP], s_inv[GP];
     __shared__ uint32_t s_red[2][4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int sl = blockIdx.x, bh = blockIdx.y;
@@ -454,27 +470,46 @@ __global__ __launch_bounds__(256) void group_kernel(const float *__restrict__ U,
             for (int g = 0; g < GP; ++g) v[u][g] = g < G ? Ub[static_cast<size_t>(j) * G + g] : 0.f;
         }
     }
+    // per head (one wave per head): all of the row's tile statistics in
+    // flight at once (TPL per lane, more are streamed), the two wave
+    // reductions, then the slice's tile weights straight from registers
+    const int t0 = j0 / 64;  // first tile of the slice (a multiple of TPS)
     for (int g = wave; g < G; g += 4) {
         const float2 *st = stats + (static_cast<size_t>(bh) * G + g) * tiles;
+        constexpr int TPL = 8;
+        float2 sv[TPL];
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            const int t = lane + 64 * i;
+            sv[i] = t < tiles ? st[t] : make_float2(-INFINITY, 0.f);
+        }
         float m = -INFINITY;
-        for (int t = lane; t < tiles; t += 64) m = fmaxf(m, st[t].x);
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) m = fmaxf(m, sv[i].x);
+        for (int t = lane + 64 * TPL; t < tiles; t += 64) m = fmaxf(m, st[t].x);
         m = wave_max(m);
         float z = 0.f;
-        for (int t = lane; t < tiles; t += 64) {
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) z += sv[i].x == -INFINITY ? 0.f : sv[i].y * expf(sv[i].x - m);
+        for (int t = lane + 64 * TPL; t < tiles; t += 64) {
             const float2 x = st[t];
             z += x.x == -INFINITY ? 0.f : x.y * expf(x.x - m);
         }
         z = wave_sum(z);
-        if (lane == 0) {
-            s_m[g] = m;
-            s_inv[g] = z > 0.f ? 1.f / (z * static_cast<float>(G)) : 0.f;
+        const float inv = z > 0.f ? 1.f / (z * static_cast<float>(G)) : 0.f;
+        const int tl = lane - (t0 & 63);  // this lane's tile within the slice
+        if (tl >= 0 && tl < TPS) {
+            const int t = t0 + tl;
+            float2 x = make_float2(-INFINITY, 0.f);
+            if (t0 / 64 < TPL) {
+#pragma unroll
+                for (int i = 0; i < TPL; ++i)
+                    if (i == t0 / 64) x = sv[i];
+            } else if (t < tiles) {
+                x = st[t];
+            }
+            s_w[tl][g] = x.x == -INFINITY ? 0.f : expf(x.x - m) * inv;
         }
-    }
-    __syncthreads();
-    for (int i = tid; i < TPS * G; i += 256) {
-        const int tl = i / G, g = i % G, t = j0 / 64 + tl;
-        const float2 x = t < tiles ? stats[(static_cast<size_t>(bh) * G + g) * tiles + t] : make_float2(-INFINITY, 0.f);
-        s_w[tl][g] = x.x == -INFINITY ? 0.f : expf(x.x - s_m[g]) * s_inv[g];
     }
     __syncthreads();
     uint32_t kmn = 0xffffffffu, kmx = 0u;
@@ -533,19 +568,23 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
     uint32_t *keys = use_lds ? reinterpret_cast<uint32_t *>(s_rank + k) : const_cast<uint32_t *>(krow);
 
     if (use_lds) {
-        for (int j0 = 0; j0 < n; j0 += 4 * nt) {
-            uint32_t t[4];
+        // 16-byte loads, four per thread in flight (16384 keys per batch)
+        const int nv = (n & 3) == 0 && (reinterpret_cast<uintptr_t>(krow) & 15) == 0 ? n / 4 : 0;
+        const u32x4 *kv = reinterpret_cast<const u32x4 *>(krow);
+        for (int v0 = 0; v0 < nv; v0 += 4 * nt) {
+            u32x4 t[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int j = j0 + tid + u * nt;
-                t[u] = j < n ? krow[j] : 0u;
+                const int v = v0 + tid + u * nt;
+                if (v < nv) t[u] = kv[v];
             }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int j = j0 + tid + u * nt;
-                if (j < n) keys[j] = t[u];
+                const int v = v0 + tid + u * nt;
+                if (v < nv) reinterpret_cast<u32x4 *>(keys)[v] = t[u];
             }
         }
+        for (int j = 4 * nv + tid; j < n; j += nt) keys[j] = krow[j];
     }
     for (int i = tid; i < 4096; i += nt) sc.hist[i] = 0;
     for (int i = tid; i < k; i += nt) s_hit[i] = 0;
