@@ -430,44 +430,52 @@ __global__ __launch_bounds__(256) void pv_kernel(const float *__restrict__ logit
     const int cnt = min(kPvTile, NK - key0);
     const int cg = tid % CG, rg = tid / CG;
 
+    // 1. the logits of this wave's heads first: the softmax then waits only
+    //    for them, not for the V rows issued after them.  Every load below is
+    //    unconditional (past the tile, the last key's row is read and weighted
+    //    by zero), so the compiler's wait counts stay exact.
+    constexpr int HPW = (GP + 3) / 4;  // heads per wave
+    float lv[HPW][kPvTile / 64];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+        const int g = min(wave + 4 * hh, G - 1);
+        const float *lg = logits + (static_cast<size_t>(bh) * G + g) * NK + key0;
+#pragma unroll
+        for (int i = 0; i < kPvTile / 64; ++i) lv[hh][i] = lg[min(lane + 64 * i, cnt - 1)];
+    }
+    // 2. the V rows of this thread's 8 columns
     u32x4 raw[RPT][VPR];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-        const int rr = rg + RG * i;
-        const int key = key0 + rr;
-        if (rr < cnt) {
-            const T *vrow = key < OC ? v_out + (static_cast<size_t>(bh) * OC + key) * D
-                          : key < OC + KC ? vc + (static_cast<size_t>(bh) * KC + (key - OC)) * D
-                                          : v_loc + (static_cast<size_t>(bh) * w + (key - OC - KC)) * D;
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(vrow + cg * 8);
+        const int key = key0 + min(rg + RG * i, cnt - 1);
+        const T *vrow = key < OC ? v_out + (static_cast<size_t>(bh) * OC + key) * D
+                      : key < OC + KC ? vc + (static_cast<size_t>(bh) * KC + (key - OC)) * D
+                                      : v_loc + (static_cast<size_t>(bh) * w + (key - OC - KC)) * D;
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(vrow + cg * 8);
 #pragma unroll
-            for (int u = 0; u < VPR; ++u) raw[i][u] = src[u];
-        } else {
-#pragma unroll
-            for (int u = 0; u < VPR; ++u) raw[i][u] = u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int u = 0; u < VPR; ++u) raw[i][u] = src[u];
     }
 
-    for (int g = wave; g < GP; g += 4) {
+    // 3. each head's softmax partial over the tile: (max, sum) to part_ml,
+    //    the weights to LDS
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+        const int g = wave + 4 * hh;
+        if (g >= GP) break;
         if (g >= G) {
             for (int i = lane; i < kPvTile; i += 64) ps[g][i] = 0.f;
             continue;
         }
-        const float *lg = logits + (static_cast<size_t>(bh) * G + g) * NK + key0;
-        float v[kPvTile / 64];
         float m = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < kPvTile / 64; ++i) {
-            const int kk = lane + 64 * i;
-            v[i] = kk < cnt ? lg[kk] : -INFINITY;
-            m = fmaxf(m, v[i]);
-        }
+        for (int i = 0; i < kPvTile / 64; ++i)
+            if (lane + 64 * i < cnt) m = fmaxf(m, lv[hh][i]);
         m = wave_max(m);
         float sum = 0.f;
 #pragma unroll
         for (int i = 0; i < kPvTile / 64; ++i) {
             const int kk = lane + 64 * i;
-            const float p = kk < cnt ? expf(v[i] - m) : 0.f;
+            const float p = kk < cnt ? expf(lv[hh][i] - m) : 0.f;
             ps[g][kk] = p;
             sum += p;
         }
@@ -493,20 +501,42 @@ __global__ __launch_bounds__(256) void pv_kernel(const float *__restrict__ logit
             for (int x = 0; x < 8; ++x) acc[g][x] += p * v[x];
         }
     }
-    // reduce the row groups of this wave (lane bits above the column group)
-#pragma unroll
-    for (int off = CG; off < 64; off <<= 1)
-#pragma unroll
-        for (int g = 0; g < GP; ++g)
-#pragma unroll
-            for (int x = 0; x < 8; ++x) acc[g][x] += __shfl_xor(acc[g][x], off, 64);
-    (void)WRG;
-    if (lane < CG) {
+    if constexpr (CG == 16) {
+        // sum over the wave's four row groups (lanes l, l+16, l+32, l+48) with
+        // two halving permlane exchanges: lane group r ends with the values
+        // r*(2*GP) .. r*(2*GP) + 2*GP - 1 of the flattened (head, column) list
+        constexpr int NV = GP * 8;
+        float a[NV];
 #pragma unroll
         for (int g = 0; g < GP; ++g)
 #pragma unroll
-            for (int x = 0; x < 8; ++x) red[wave][g][cg * 8 + x] = acc[g][x];
+            for (int x = 0; x < 8; ++x) a[g * 8 + x] = acc[g][x];
+#pragma unroll
+        for (int v = 0; v < NV / 2; ++v) a[v] = swap_sum32(a[v], a[v + NV / 2]);
+#pragma unroll
+        for (int v = 0; v < NV / 4; ++v) a[v] = swap_sum16(a[v], a[v + NV / 4]);
+        const int r = lane >> 4;
+#pragma unroll
+        for (int v = 0; v < NV / 4; ++v) {
+            const int f = r * (NV / 4) + v;
+            red[wave][f >> 3][cg * 8 + (f & 7)] = a[v];
+        }
+    } else {
+        // reduce the row groups of this wave (lane bits above the column group)
+#pragma unroll
+        for (int off = CG; off < 64; off <<= 1)
+#pragma unroll
+            for (int g = 0; g < GP; ++g)
+#pragma unroll
+                for (int x = 0; x < 8; ++x) acc[g][x] += __shfl_xor(acc[g][x], off, 64);
+        if (lane < CG) {
+#pragma unroll
+            for (int g = 0; g < GP; ++g)
+#pragma unroll
+                for (int x = 0; x < 8; ++x) red[wave][g][cg * 8 + x] = acc[g][x];
+        }
     }
+    (void)WRG;
     __syncthreads();
     for (int idx = tid; idx < G * D; idx += 256) {
         const int g = idx / D, i = idx % D;

@@ -1,12 +1,17 @@
-"""Parity at the full 128K workload size (Llama-3-8B-shaped, b = 8,
-s = 131072, h_q = 32, h_kv = 8, d = 128, r = 160, o = 48, k = 256), in the
-configuration the benchmark times: one layer, device-generated inputs, GPU
-prefill and decode.  The oracle recomputes one sampled sequence (all its KV
-heads) from the same inputs with its own prefill and SVD, and the GPU's
-landmarks, outliers, selections and outputs for that sequence are compared
-to the acceptance bar.  Every sequence's selection is also checked for
-validity (ascending, selectable) and the cache for losslessness on a sampled
-head.
+"""Parity at the full workload sizes, in the configuration the benchmark
+times: one layer, device-generated inputs, GPU prefill and decode.
+
+  * Llama-3-8B-shaped 128K: b = 8, s = 131072, h_q = 32, h_kv = 8, k = 256;
+  * Llama-3-8B-shaped 60K batch scaling: b = 48, s = 61440, k = 120
+    (384 (sequence, KV head) rows, per-sequence true rank 80..150);
+  * GLM-4-9B-shaped 244K: b = 12, s = 249856, h_kv = 2 (GQA 16), k = 488
+    (31,232 chunks per row).
+
+The oracle recomputes one sampled sequence (all its KV heads) from the same
+inputs with its own prefill and SVD, and the GPU's landmarks, outliers,
+selections and outputs for that sequence are compared to the acceptance
+bar.  Every sequence's selection is also checked for validity (ascending,
+selectable) and the cache for losslessness on a sampled head.
 """
 import numpy as np
 import pytest
@@ -22,11 +27,19 @@ from sparse_kv_cache_step_amd.setup import svd_factors
 pytestmark = pytest.mark.gpu
 
 
-def test_full_size_128k_sampled_sequence():
-    wl = synth.LLAMA_128K
-    steps, layer_id, seq = 3, 0, 5
+FULL = {
+    "llama-128k-b8": (synth.LLAMA_128K, 0, 5),
+    "llama-60k-b48": (synth.LLAMA_60K_B48, 1, 33),
+    "glm-244k-b12": (synth.GLM_244K, 2, 7),
+}
+
+
+@pytest.mark.parametrize("case", list(FULL))
+def test_full_size_sampled_sequence(case):
+    wl, layer_id, seq = FULL[case]
+    steps = 3
     dev = torch.device("cuda")
-    log(f"[128k] generating b={wl.b} s={wl.s} on the device")
+    log(f"[{case}] generating b={wl.b} s={wl.s} layer={layer_id} on the device; oracle on sequence {seq}")
     k_pre = synth.k_pre_torch(wl, layer_id, dev)
     v = synth.v_torch(wl, layer_id, dev)
     qs = synth.queries_torch(wl, layer_id, dev, steps=steps)
@@ -43,7 +56,7 @@ def test_full_size_128k_sampled_sequence():
         sels.append(layer.read(skv.SKV_T_SELECTION))
         outs.append(out)
     torch.cuda.synchronize()
-    log("[128k] GPU done; oracle on sequence", seq)
+    log(f"[{case}] GPU done; oracle on sequence {seq}")
 
     shape = Shape(b=1, h_q=wl.h_q, h_kv=wl.h_kv, d=wl.d, s=wl.s, c=wl.c, r=wl.r, o=wl.o, k=wl.k, w=wl.w, bf16=True)
     kp = to_np(k_pre[seq:seq + 1])
@@ -54,7 +67,7 @@ def test_full_size_128k_sampled_sequence():
     assert check_outliers(to_np(layer.read(skv.SKV_T_OUTLIERS)[seq:seq + 1]), meta["outliers"],
                           meta["min_cos"], wl.n - wl.n_loc)
     A_o, B_o = oracle.svd_factors(shape, kp)
-    log("[128k] oracle prefill + SVD done")
+    log(f"[{case}] oracle prefill + SVD done")
     for t in range(steps):
         q = to_np(qs[t][seq:seq + 1])
         res = oracle.decode(shape, q, meta, A_o, B_o, vv)
@@ -62,19 +75,19 @@ def test_full_size_128k_sampled_sequence():
         exact = check_selection(sel_g, res["sel"], res["S2"], meta["cand"])
         ref = res["out"] if exact else oracle.attend(shape, q, sel_g, A_o, B_o, vv, meta)
         err = float(np.max(np.abs(to_np(outs[t][seq:seq + 1]) - ref)))
-        log(f"[128k] step {t}: selection {'exact' if exact else 'near-tie'}, max|out - oracle| = {err:.3g}")
+        log(f"[{case}] step {t}: selection {'exact' if exact else 'near-tie'}, max|out - oracle| = {err:.3g}")
         assert err <= OUT_TOL[True]
         all_sel = to_np(sels[t])
         assert np.all(np.diff(all_sel, axis=-1) > 0) and all_sel.min() >= 0 and all_sel.max() < wl.n - wl.n_loc
     # lossless cache on one sampled head of the sampled sequence
-    h = 3
+    h = min(3, wl.h_kv - 1)
     slots = to_np(layer.read(skv.SKV_T_SLOT_CHUNKS)[seq, h])
     vc = layer.read(skv.SKV_T_CACHE_V)[seq, h].view(wl.k, wl.c, wl.d)
     rows = v[seq, h].view(wl.n, wl.c, wl.d)[torch.from_numpy(slots).long().cuda()]
     assert torch.equal(vc, rows)
     assert sorted(slots) == sorted(to_np(sels[-1][seq, h]))
     st = layer.stats()
-    log(f"[128k] hits={st['hits']} misses={st['misses']} alpha(after step 0)="
+    log(f"[{case}] hits={st['hits']} misses={st['misses']} alpha(after step 0)="
         f"{st['hits'] / max(1, (steps - 1) * wl.b * wl.h_kv * wl.k):.3f}")
     layer.close()
     hb.free()

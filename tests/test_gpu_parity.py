@@ -228,3 +228,28 @@ def test_error_paths_on_device():
         layer.decode_step(torch.zeros((1, 2, 3), device="cuda"), torch.empty_like(q))
     layer.close()
     hb.free()
+
+
+def test_overlap_schedule_is_identical():
+    """The fetch beside the key rebuild (second stream) and the default
+    single-queue order run the same kernels: outputs, selections and hit
+    counts must agree bit for bit."""
+    wl = synth.LLAMA_32K.with_(b=2, s=16384, k=32, steps=4, rho=0.9)
+    log(f"[overlap] b={wl.b} s={wl.s} k={wl.k} steps={wl.steps}")
+    k_pre, v, qs = synth.k_pre_numpy(wl), synth.v_numpy(wl), synth.queries_numpy(wl)
+    serial, hb1 = _gpu_state(wl, k_pre, v)
+    overlap, hb2 = _gpu_state(wl, k_pre, v)
+    overlap.set_overlap(True)
+    for t in range(qs.shape[0]):
+        q_d = to_dev(qs[t], tdtype(wl))
+        o1, o2 = torch.empty_like(q_d), torch.empty_like(q_d)
+        serial.decode_step(q_d, o1)
+        overlap.decode_step(q_d, o2)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2), f"step {t}: outputs differ between the schedules"
+        assert torch.equal(serial.read(skv.SKV_T_SELECTION), overlap.read(skv.SKV_T_SELECTION))
+        assert torch.equal(serial.read(skv.SKV_T_CACHE_V), overlap.read(skv.SKV_T_CACHE_V))
+    assert serial.stats() == overlap.stats()
+    for lay, hb in ((serial, hb1), (overlap, hb2)):
+        lay.close()
+        hb.free()
