@@ -139,6 +139,13 @@ def main() -> int:
     ap.add_argument("--kernel-events", choices=["on", "off"], default="on")
     ap.add_argument("--overlap", choices=["on", "off"], default="off",
                     help="fetch beside the key rebuild (on) or before it (off)")
+    ap.add_argument("--chunk", type=int, default=None,
+                    help="chunk size override (top-k and outlier chunks scaled to keep their token budgets)")
+    ap.add_argument("--top-k", type=int, default=None, help="selected chunks per KV head (budget) override")
+    ap.add_argument("--rank", type=int, default=None, help="rank of the key factors override")
+    ap.add_argument("--outlier-chunks", type=int, default=None, help="outlier chunks override")
+    ap.add_argument("--sweep", action="store_true",
+                    help="run chunk-size / budget / rank variants of the workload, one JSON line each")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a device copy of 256 MiB (traffic-counter calibration)")
     ap.add_argument("--ingest-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -165,205 +172,240 @@ def main() -> int:
         import __graft_entry__
         __graft_entry__.build()
 
-    wl = synth.WORKLOADS[args.workload]
-    layers = args.layers or wl.layers
-    wl = wl.with_(layers=layers)
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    dt = torch.bfloat16 if wl.bf16 else torch.float32
-    nq = args.warmup + args.steps
-    log(f"bench: {wl.name} b={wl.b} s={wl.s} h_q={wl.h_q} h_kv={wl.h_kv} d={wl.d} r={wl.r} o={wl.o} k={wl.k} "
-        f"w={wl.w} layers={layers} steps={args.steps} warmup={args.warmup}")
+    base = synth.WORKLOADS[args.workload]
 
-    # ---- setup (untimed): data, factors, prefill, pinned host V ----------------
-    t0 = time.time()
-    n_host = layers if args.host_v_share <= 0 else min(layers, args.host_v_share)
-    host_bufs = []
-    Ls, qs = [], []
-    keep = {}  # inputs of the spot-checked layer, for the oracle
-    spot_layer = layers - 1
-    for l in range(layers):
-        k_pre = synth.k_pre_torch(wl, l, dev)
-        v = synth.v_torch(wl, l, dev)
-        A, B = svd_factors(k_pre, wl.r)
-        lay = skv.Layer(batch=wl.b, heads_q=wl.h_q, heads_kv=wl.h_kv, head_dim=wl.d, seq_len=wl.s, chunk=wl.c,
-                        rank=wl.r, n_outlier=wl.o, top_k=wl.k, local_window=wl.w, rope_base=wl.rope_base,
-                        bf16=wl.bf16)
-        if l < n_host:
-            host_bufs.append(lay.host_buffer())
-        lay.prefill_meta(k_pre, v, A, B, host_bufs[l % n_host])
-        qs.append(synth.queries_torch(wl, l, dev, steps=nq))
+    def variant(wl, chunk=None, top_k=None, rank=None, outliers=None):
+        """The workload with another chunk size (top-k and outlier chunks
+        scaled to keep their token budgets), budget or rank."""
+        kw, tags = {}, []
+        if chunk and chunk != wl.c:
+            kw.update(c=chunk, k=max(1, wl.k * wl.c // chunk), o=wl.o * wl.c // chunk)
+            tags.append(f"c={chunk}")
+        if top_k:
+            kw["k"] = top_k
+            tags.append(f"k={top_k}")
+        if rank:
+            kw["r"] = rank
+            tags.append(f"r={rank}")
+        if outliers is not None:
+            kw["o"] = outliers
+            tags.append(f"o={outliers}")
+        if not kw:
+            return wl
+        return wl.with_(name=f"{wl.name}[{','.join(tags)}]", **kw)
+
+    def run_one(wl) -> dict:
+        layers = args.layers or wl.layers
+        wl = wl.with_(layers=layers)
+        dev = torch.device("cuda", 0)
+        torch.cuda.set_device(dev)
+        dt = torch.bfloat16 if wl.bf16 else torch.float32
+        nq = args.warmup + args.steps
+        log(f"bench: {wl.name} b={wl.b} s={wl.s} h_q={wl.h_q} h_kv={wl.h_kv} d={wl.d} r={wl.r} o={wl.o} k={wl.k} "
+            f"w={wl.w} layers={layers} steps={args.steps} warmup={args.warmup}")
+
+        # ---- setup (untimed): data, factors, prefill, pinned host V ----------------
+        t0 = time.time()
+        n_host = layers if args.host_v_share <= 0 else min(layers, args.host_v_share)
+        host_bufs = []
+        Ls, qs = [], []
+        keep = {}  # inputs of the spot-checked layer, for the oracle
+        spot_layer = layers - 1
+        for l in range(layers):
+            k_pre = synth.k_pre_torch(wl, l, dev)
+            v = synth.v_torch(wl, l, dev)
+            A, B = svd_factors(k_pre, wl.r)
+            lay = skv.Layer(batch=wl.b, heads_q=wl.h_q, heads_kv=wl.h_kv, head_dim=wl.d, seq_len=wl.s, chunk=wl.c,
+                            rank=wl.r, n_outlier=wl.o, top_k=wl.k, local_window=wl.w, rope_base=wl.rope_base,
+                            bf16=wl.bf16)
+            if l < n_host:
+                host_bufs.append(lay.host_buffer())
+            lay.prefill_meta(k_pre, v, A, B, host_bufs[l % n_host])
+            qs.append(synth.queries_torch(wl, l, dev, steps=nq))
+            torch.cuda.synchronize()
+            if l == spot_layer and not args.no_cpu_baseline:
+                sample = [0, wl.b // 2] if wl.b > 1 else [0]
+                keep = {"seqs": sample, "k_pre": k_pre[sample].float().cpu(), "v": v[sample].float().cpu()}
+            del k_pre, v, A, B
+            lay.set_overlap(args.overlap == "on")
+            Ls.append(lay)
+            if l % 4 == 3 or l == layers - 1:
+                log(f"  setup: {l + 1}/{layers} layers ready ({time.time() - t0:.0f}s)")
+        torch.cuda.empty_cache()
+        outs = [torch.empty((wl.b, wl.h_q, wl.d), dtype=dt, device=dev) for _ in range(layers)]
+        stream = torch.cuda.current_stream()
+
+        def run_steps(t_begin, t_count):
+            for t in range(t_begin, t_begin + t_count):
+                for l in range(layers):
+                    Ls[l].decode_step(qs[l][t], outs[l], stream)
+
+        if args.copy_calibration:
+            src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
+
+        # ---- warmup ---------------------------------------------------------------
+        run_steps(0, args.warmup)
         torch.cuda.synchronize()
-        if l == spot_layer and not args.no_cpu_baseline:
-            sample = [0, wl.b // 2] if wl.b > 1 else [0]
-            keep = {"seqs": sample, "k_pre": k_pre[sample].float().cpu(), "v": v[sample].float().cpu()}
-        del k_pre, v, A, B
-        lay.set_overlap(args.overlap == "on")
-        Ls.append(lay)
-        if l % 4 == 3 or l == layers - 1:
-            log(f"  setup: {l + 1}/{layers} layers ready ({time.time() - t0:.0f}s)")
-    torch.cuda.empty_cache()
-    outs = [torch.empty((wl.b, wl.h_q, wl.d), dtype=dt, device=dev) for _ in range(layers)]
-    stream = torch.cuda.current_stream()
-
-    def run_steps(t_begin, t_count):
-        for t in range(t_begin, t_begin + t_count):
-            for l in range(layers):
-                Ls[l].decode_step(qs[l][t], outs[l], stream)
-
-    if args.copy_calibration:
-        src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-
-    # ---- warmup ---------------------------------------------------------------
-    run_steps(0, args.warmup)
-    torch.cuda.synchronize()
-    for lay in Ls:
-        lay.reset_stats()
-
-    # ---- timed region ---------------------------------------------------------
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    e0.record(stream)
-    run_steps(args.warmup, args.steps)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    last_out = outs[spot_layer].clone()  # output of the last timed step
-    wall = time.perf_counter() - wall0
-    elapsed = e0.elapsed_time(e1) / 1e3
-    log(f"timed: {args.steps} steps x {layers} layers in {elapsed * 1e3:.2f} ms (host wall {wall * 1e3:.2f} ms)")
-    stats = [lay.stats() for lay in Ls]
-    hits = sum(s["hits"] for s in stats)
-    misses = sum(s["misses"] for s in stats)
-    alpha = hits / max(1, hits + misses)
-    h2d_bytes = sum(s["bytes_h2d"] for s in stats)
-
-    # ---- per-kernel durations: the same steps again with HIP events ----------
-    kern_ms = {name: 0.0 for name in skv.KERNELS}
-    kern_steps = 0
-    if args.kernel_events == "on":
         for lay in Ls:
-            lay.set_timing(True)
+            lay.reset_stats()
+
+        # ---- timed region ---------------------------------------------------------
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        wall0 = time.perf_counter()
+        e0.record(stream)
         run_steps(args.warmup, args.steps)
+        e1.record(stream)
         torch.cuda.synchronize()
+        last_out = outs[spot_layer].clone()  # output of the last timed step
+        wall = time.perf_counter() - wall0
+        elapsed = e0.elapsed_time(e1) / 1e3
+        log(f"timed: {args.steps} steps x {layers} layers in {elapsed * 1e3:.2f} ms (host wall {wall * 1e3:.2f} ms)")
+        stats = [lay.stats() for lay in Ls]
+        hits = sum(s["hits"] for s in stats)
+        misses = sum(s["misses"] for s in stats)
+        alpha = hits / max(1, hits + misses)
+        h2d_bytes = sum(s["bytes_h2d"] for s in stats)
+
+        # ---- per-kernel durations: the same steps again with HIP events ----------
+        kern_ms = {name: 0.0 for name in skv.KERNELS}
+        kern_steps = 0
+        if args.kernel_events == "on":
+            for lay in Ls:
+                lay.set_timing(True)
+            run_steps(args.warmup, args.steps)
+            torch.cuda.synchronize()
+            for lay in Ls:
+                ms, st = lay.get_timing()
+                lay.set_timing(False)
+                kern_steps += st
+                for kname, v_ms in ms.items():
+                    kern_ms[kname] += v_ms
+        per_launch_us = {k: (v * 1e3 / kern_steps if kern_steps else None) for k, v in kern_ms.items()}
+
+        layer_steps = args.steps * layers
+        ab = algorithmic_bytes(wl)
+        alg_total = sum(ab.values())
+        t_ls = elapsed / layer_steps
+        dense_kv = 2 * wl.b * wl.h_kv * wl.s * wl.d * (2 if wl.bf16 else 4)
+
+        roofline = None
+        kernels = {}
+        if kern_steps:
+            score_bytes = ab["landmarks"] + ab["q"]
+            qk_bytes = ab["a_rows"] + ab["b_factor"] + ab["outlier_kv"] // 2 + ab["local_kv"] // 2 + ab["q"]
+            pv_bytes = ab["selected_v"] + ab["outlier_kv"] // 2 + ab["local_kv"] // 2 + ab["out"]
+            fetch_bytes = h2d_bytes / max(1, layer_steps)
+            for name, nbytes, peak in (("score", score_bytes, PEAK_HBM), ("qk", qk_bytes, PEAK_HBM),
+                                       ("pv", pv_bytes, PEAK_HBM), ("fetch", fetch_bytes, PEAK_PCIE)):
+                us = per_launch_us[name]
+                gbs = nbytes / (us * 1e-6) / 1e9 if us else None
+                kernels[name] = {"us_per_launch": round(us, 3), "bytes_per_launch": int(nbytes),
+                                 "GBps": round(gbs, 1) if gbs else None, "peak_GBps": peak / 1e9,
+                                 "frac": round(gbs * 1e9 / peak, 4) if gbs else None}
+            kernels["select"] = {"us_per_launch": round(per_launch_us["select"], 3)}
+            sc = kernels["score"]
+            traffic = measured_traffic(wl.name)
+            roofline = {"kernel": "score_mfma_kernel (landmark scoring)", "bound": "hbm",
+                        "achieved": sc["GBps"], "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": sc["frac"],
+                        "traffic": traffic, "bytes_per_launch": sc["bytes_per_launch"],
+                        "us_per_launch": sc["us_per_launch"]}
+
+        fetch_gbs = kernels.get("fetch", {}).get("GBps") if kernels else None
+        closed_form = None
+        if fetch_gbs:
+            closed_form = skv.shadowkv_equiv_bandwidth(wl.s, wl.c, wl.k, wl.o, alpha, PEAK_HBM, fetch_gbs * 1e9) / 1e12
+
+        # ---- oracle on the host, bounded sample of the same workload --------------
+        cpu_baseline = None
+        parity = None
+        if not args.no_cpu_baseline and keep:
+            import oracle
+            from oracle import Shape
+            seqs = keep["seqs"]
+            shape = Shape(b=len(seqs), h_q=wl.h_q, h_kv=wl.h_kv, d=wl.d, s=wl.s, c=wl.c, r=wl.r, o=wl.o, k=wl.k,
+                          w=wl.w, rope_base=wl.rope_base, bf16=wl.bf16)
+            kp = keep["k_pre"].double().numpy()
+            vv = keep["v"].double().numpy()
+            log(f"cpu baseline: oracle prefill + SVD for sequences {seqs} of layer {spot_layer} (untimed)")
+            meta = oracle.prefill(shape, kp, vv)
+            A_o, B_o = oracle.svd_factors(shape, kp)
+            q_all = qs[spot_layer][:, seqs].float().cpu().double().numpy()
+            # decode steps 0, 1, ..., nq - 1 (the GPU's output at the last timed
+            # step is spot-checked there), then again from step 0 until the time
+            # budget is spent; the oracle's decode does not depend on the cache
+            t_last = args.warmup + args.steps - 1
+            t_start = time.perf_counter()
+            n_done, res, res_last = 0, None, None
+            while True:
+                t = n_done % nq
+                res = oracle.decode(shape, q_all[t], meta, A_o, B_o, vv)
+                if t == t_last:
+                    res_last = res
+                n_done += 1
+                if n_done >= nq and time.perf_counter() - t_start > args.cpu_baseline_seconds:
+                    break
+            cpu_s = time.perf_counter() - t_start
+            per_seq_step = cpu_s / (n_done * len(seqs))
+            threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
+            cores = min(threads, os.cpu_count() or 1, len(seqs) * wl.h_kv)
+            cpu_baseline = {"value": round(1.0 / (per_seq_step * wl.b), 4), "unit": "layer-steps/s", "cores": cores,
+                            "kind": "oracle",
+                            "sample": f"{n_done} decode steps (steps 0..{nq - 1}, cycled) of sequences {seqs} "
+                                      f"(of {wl.b}) of layer {spot_layer}; {cpu_s:.1f} s of CPU time; "
+                                      f"scaled to all {wl.b} sequences"}
+            if res_last is not None:
+                gpu_out = last_out[seqs].float().cpu().double().numpy()
+                gpu_sel = Ls[spot_layer].read(skv.SKV_T_SELECTION)[seqs].cpu().numpy()
+                parity = {"layer": spot_layer, "step": t_last, "sequences": seqs,
+                          "selection_equal": bool(np.array_equal(gpu_sel, res_last["sel"])),
+                          "max_abs_err_vs_oracle": float(np.max(np.abs(gpu_out - res_last["out"]))),
+                          "tolerance": 2e-2 if wl.bf16 else 1e-4}
+            log(f"cpu baseline: {cpu_baseline['value']} layer-steps/s on {cores} threads")
+
+        value = layer_steps / elapsed
+        line = {
+            "metric": "sparse decode layer-steps/sec + effective & equivalent HBM TB/s at 128K, 1 GPU",
+            "value": round(value, 2), "unit": "layer-steps/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.bf16 else "f32", "data": "synthetic",
+            "config": {"workload": wl.name, "batch": wl.b, "seq_len": wl.s, "heads_q": wl.h_q, "heads_kv": wl.h_kv,
+                       "head_dim": wl.d, "chunk": wl.c, "rank": wl.r, "outlier_chunks": wl.o, "top_k": wl.k,
+                       "local_window": wl.w, "layers": layers, "host_v_buffers": n_host},
+            "us_per_layer_step": round(t_ls * 1e6, 3),
+            "effective_TBps": round(alg_total / t_ls / 1e12, 4),
+            "equivalent_TBps": round(dense_kv / t_ls / 1e12, 4),
+            "alpha": round(alpha, 4),
+            "h2d_GB": round(h2d_bytes / 1e9, 4),
+            "closed_form_equiv_TBps": round(closed_form, 3) if closed_form else None,
+            "roofline": roofline,
+            "kernels": kernels,
+            "cpu_baseline": cpu_baseline,
+            "parity_spot_check": parity,
+            "setup_s": round(time.time() - t0, 1),
+        }
         for lay in Ls:
-            ms, st = lay.get_timing()
-            lay.set_timing(False)
-            kern_steps += st
-            for kname, v_ms in ms.items():
-                kern_ms[kname] += v_ms
-    per_launch_us = {k: (v * 1e3 / kern_steps if kern_steps else None) for k, v in kern_ms.items()}
+            lay.close()
+        for hb in host_bufs:
+            hb.free()
+        torch.cuda.empty_cache()
+        return line
 
-    layer_steps = args.steps * layers
-    ab = algorithmic_bytes(wl)
-    alg_total = sum(ab.values())
-    t_ls = elapsed / layer_steps
-    dense_kv = 2 * wl.b * wl.h_kv * wl.s * wl.d * (2 if wl.bf16 else 4)
-
-    roofline = None
-    kernels = {}
-    if kern_steps:
-        score_bytes = ab["landmarks"] + ab["q"]
-        qk_bytes = ab["a_rows"] + ab["b_factor"] + ab["outlier_kv"] // 2 + ab["local_kv"] // 2 + ab["q"]
-        pv_bytes = ab["selected_v"] + ab["outlier_kv"] // 2 + ab["local_kv"] // 2 + ab["out"]
-        fetch_bytes = h2d_bytes / max(1, layer_steps)
-        for name, nbytes, peak in (("score", score_bytes, PEAK_HBM), ("qk", qk_bytes, PEAK_HBM),
-                                   ("pv", pv_bytes, PEAK_HBM), ("fetch", fetch_bytes, PEAK_PCIE)):
-            us = per_launch_us[name]
-            gbs = nbytes / (us * 1e-6) / 1e9 if us else None
-            kernels[name] = {"us_per_launch": round(us, 3), "bytes_per_launch": int(nbytes),
-                             "GBps": round(gbs, 1) if gbs else None, "peak_GBps": peak / 1e9,
-                             "frac": round(gbs * 1e9 / peak, 4) if gbs else None}
-        kernels["select"] = {"us_per_launch": round(per_launch_us["select"], 3)}
-        sc = kernels["score"]
-        traffic = measured_traffic(wl.name)
-        roofline = {"kernel": "score_mfma_kernel (landmark scoring)", "bound": "hbm",
-                    "achieved": sc["GBps"], "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": sc["frac"],
-                    "traffic": traffic, "bytes_per_launch": sc["bytes_per_launch"],
-                    "us_per_launch": sc["us_per_launch"]}
-
-    fetch_gbs = kernels.get("fetch", {}).get("GBps") if kernels else None
-    closed_form = None
-    if fetch_gbs:
-        closed_form = skv.shadowkv_equiv_bandwidth(wl.s, wl.c, wl.k, wl.o, alpha, PEAK_HBM, fetch_gbs * 1e9) / 1e12
-
-    # ---- oracle on the host, bounded sample of the same workload --------------
-    cpu_baseline = None
-    parity = None
-    if not args.no_cpu_baseline and keep:
-        import oracle
-        from oracle import Shape
-        seqs = keep["seqs"]
-        shape = Shape(b=len(seqs), h_q=wl.h_q, h_kv=wl.h_kv, d=wl.d, s=wl.s, c=wl.c, r=wl.r, o=wl.o, k=wl.k,
-                      w=wl.w, rope_base=wl.rope_base, bf16=wl.bf16)
-        kp = keep["k_pre"].double().numpy()
-        vv = keep["v"].double().numpy()
-        log(f"cpu baseline: oracle prefill + SVD for sequences {seqs} of layer {spot_layer} (untimed)")
-        meta = oracle.prefill(shape, kp, vv)
-        A_o, B_o = oracle.svd_factors(shape, kp)
-        q_all = qs[spot_layer][:, seqs].float().cpu().double().numpy()
-        # decode steps 0, 1, ..., nq - 1 (the GPU's output at the last timed
-        # step is spot-checked there), then again from step 0 until the time
-        # budget is spent; the oracle's decode does not depend on the cache
-        t_last = args.warmup + args.steps - 1
-        t_start = time.perf_counter()
-        n_done, res, res_last = 0, None, None
-        while True:
-            t = n_done % nq
-            res = oracle.decode(shape, q_all[t], meta, A_o, B_o, vv)
-            if t == t_last:
-                res_last = res
-            n_done += 1
-            if n_done >= nq and time.perf_counter() - t_start > args.cpu_baseline_seconds:
-                break
-        cpu_s = time.perf_counter() - t_start
-        per_seq_step = cpu_s / (n_done * len(seqs))
-        threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
-        cores = min(threads, os.cpu_count() or 1, len(seqs) * wl.h_kv)
-        cpu_baseline = {"value": round(1.0 / (per_seq_step * wl.b), 4), "unit": "layer-steps/s", "cores": cores,
-                        "kind": "oracle",
-                        "sample": f"{n_done} decode steps (steps 0..{nq - 1}, cycled) of sequences {seqs} "
-                                  f"(of {wl.b}) of layer {spot_layer}; {cpu_s:.1f} s of CPU time; "
-                                  f"scaled to all {wl.b} sequences"}
-        if res_last is not None:
-            gpu_out = last_out[seqs].float().cpu().double().numpy()
-            gpu_sel = Ls[spot_layer].read(skv.SKV_T_SELECTION)[seqs].cpu().numpy()
-            parity = {"layer": spot_layer, "step": t_last, "sequences": seqs,
-                      "selection_equal": bool(np.array_equal(gpu_sel, res_last["sel"])),
-                      "max_abs_err_vs_oracle": float(np.max(np.abs(gpu_out - res_last["out"]))),
-                      "tolerance": 2e-2 if wl.bf16 else 1e-4}
-        log(f"cpu baseline: {cpu_baseline['value']} layer-steps/s on {cores} threads")
-
-    value = layer_steps / elapsed
-    line = {
-        "metric": "sparse decode layer-steps/sec + effective & equivalent HBM TB/s at 128K, 1 GPU",
-        "value": round(value, 2), "unit": "layer-steps/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(elapsed / args.steps * 1e3, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.bf16 else "f32", "data": "synthetic",
-        "config": {"workload": wl.name, "batch": wl.b, "seq_len": wl.s, "heads_q": wl.h_q, "heads_kv": wl.h_kv,
-                   "head_dim": wl.d, "chunk": wl.c, "rank": wl.r, "outlier_chunks": wl.o, "top_k": wl.k,
-                   "local_window": wl.w, "layers": layers, "host_v_buffers": n_host},
-        "us_per_layer_step": round(t_ls * 1e6, 3),
-        "effective_TBps": round(alg_total / t_ls / 1e12, 4),
-        "equivalent_TBps": round(dense_kv / t_ls / 1e12, 4),
-        "alpha": round(alpha, 4),
-        "h2d_GB": round(h2d_bytes / 1e9, 4),
-        "closed_form_equiv_TBps": round(closed_form, 3) if closed_form else None,
-        "roofline": roofline,
-        "kernels": kernels,
-        "cpu_baseline": cpu_baseline,
-        "parity_spot_check": parity,
-        "setup_s": round(time.time() - t0, 1),
-    }
+    if args.sweep:
+        # chunk size, budget and rank around the workload, every kernel reused;
+        # one JSON line per configuration
+        n8 = base.s // 8
+        grid = [dict(), dict(chunk=4), dict(chunk=16), dict(top_k=n8 // 128), dict(top_k=n8 // 32),
+                dict(rank=96), dict(rank=128), dict(rank=192)]
+        for g in grid:
+            print(json.dumps(run_one(variant(base, **g))), flush=True)
+        return 0
+    line = run_one(variant(base, args.chunk, args.top_k, args.rank, args.outlier_chunks))
     print(json.dumps(line), flush=True)
-    for lay in Ls:
-        lay.close()
-    for hb in host_bufs:
-        hb.free()
     return 0
 
 

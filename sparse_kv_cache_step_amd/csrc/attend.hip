@@ -217,15 +217,18 @@ __global__ __launch_bounds__(256) void qk_static_mfma_kernel(const uint16_t *__r
 // K[key, :] = A[pos(key), :] . B[h] with pos(key) = chunk(slot) * c + t, a
 // genuine rank-r x d contraction.  A workgroup takes 256 keys (4 waves x 64);
 // B[h] (stored transposed, d x r) is staged once in LDS and shared by the four
-// waves; each wave then works on one 16-key block at a time and computes the
-// block transposed, K^T[dim, key] = sum_r Bt[dim, r] A[key, r]: the staged
-// Bt rows are the MFMA A operand and the gathered A rows, read straight from
-// memory, the B operand.  v_mfma_f32_16x16x32_bf16 then leaves lane l with
-// key (l & 15) of the block and dims 16*nb + 4*(l >> 4) + e (e < 4) of every
-// 16-dim block nb, so the RoPE pair (i, i + d/2) sits in one lane and each
-// lane rotates its own key at its own position.  A lane's partial logits over
-// its 32 (or 16) dims are summed over the four lane groups by two permlane
-// swaps, which leave lane l with the logits of heads (GP/4)*(l >> 4) + x.
+// waves; each wave requests the gathered A rows of all four of its 16-key
+// blocks at once and then computes the blocks in turn, transposed,
+// K^T[dim, key] = sum_r Bt[dim, r] A[key, r]: the staged Bt rows are the MFMA
+// A operand and the gathered A rows the B operand.  v_mfma_f32_16x16x32_bf16
+// then leaves lane l with key (l & 15) of the block and dims
+// 16*nb + 4*(l >> 4) + e (e < 4) of every 16-dim block nb, so the RoPE pair
+// (i, i + d/2) sits in one lane and each lane rotates its own key at its own
+// position.  The logits are a second contraction on MFMA: in a fixed
+// permutation of the head dimension (dims 32p + 4*(l >> 4) + e and
+// 32p + 16 + 4*(l >> 4) + e of dim pair p), the rotated keys, rounded to
+// bfloat16, already sit in the B-operand layout, and the group's queries,
+// permuted the same way, are the A operand (query heads as rows).
 // ---------------------------------------------------------------------------
 // v_permlane32_swap exchanges the upper 32 lanes of its first operand with the
 // lower 32 lanes of its second, so the sum of the two results holds, in lanes
@@ -242,6 +245,16 @@ __device__ __forceinline__ float swap_sum16(float lo, float hi) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+__device__ __forceinline__ bf16x8 pack_bf16x8(f32x4 a, f32x4 b) {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r[e] = static_cast<__bf16>(a[e]);
+        r[4 + e] = static_cast<__bf16>(b[e]);
+    }
+    return r;
+}
+
 template <int D, int GP, int NKB>
 __global__ __launch_bounds__(256) void qk_sparse_mfma_kernel(const uint16_t *__restrict__ q,
                                                              const uint16_t *__restrict__ A,
@@ -251,22 +264,38 @@ __global__ __launch_bounds__(256) void qk_sparse_mfma_kernel(const uint16_t *__r
                                                              float *__restrict__ logits, int hkv, int G, int s,
                                                              int c, int r, int r_pad, int k, int OC, int KC, int NK,
                                                              float scale) {
+    static_assert(GP <= 16, "query heads are the rows of one 16-row MFMA block");
     constexpr int NB = D / 16;      // 16-dim blocks
     constexpr int HB = NB / 2;      // blocks holding the first half of the dims
-    constexpr int HPL = GP / 4;     // heads per lane after the reduction
+    constexpr int NP = NB / 2;      // 32-dim pairs of blocks (logit MFMA steps)
+    constexpr int MB = 4;           // 16-key blocks per wave
     constexpr int STG = D / 8;      // B staging vectors per thread (r_pad <= 256)
     extern __shared__ uint16_t dyn[];
     uint16_t *Bs = dyn;             // D x (r_pad + 8)
-    __shared__ float qs[GP][D];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, quad = lane >> 4;
     const int bh = blockIdx.y, b = bh / hkv, h = bh % hkv;
     const int hq = hkv * G;
     const int ldb = r_pad + 8;
+    const int key_base = blockIdx.x * kQkMfmaTile + wave * 64;
+    const bool active = key_base < KC;  // wave-uniform
+
+    // The A side does not depend on the staged B: the chunk of every slot
+    // this wave's 64 keys touch (at most 64 slots, one load per lane, then
+    // shuffles) and the rotation rates are requested first, and the gathered
+    // A rows of all four key blocks and the queries right after B is written
+    // to LDS (the staging registers are free by then), before the barrier.
+    const int slot0 = key_base / c;
+    const int my_chunk = slot_chunk[static_cast<size_t>(bh) * k + min(slot0 + lane, k - 1)];
+    // rotation rates (turns per position) of this lane's dims 16*hb + 4*quad + e
+    double thr[HB][4];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) thr[hb][e] = theta_rev[hb * 16 + quad * 4 + e];
 
     {
-        // stage B[h] (transposed, d x r) with every load in flight, then the
-        // scaled queries
+        // stage B[h] (transposed, d x r) with every load in flight
         const uint16_t *Btb = Bt + static_cast<size_t>(bh) * D * r;
         const int vpr = r_pad / 8, total = D * vpr;
         u32x4 tmp[STG];
@@ -282,62 +311,54 @@ __global__ __launch_bounds__(256) void qk_sparse_mfma_kernel(const uint16_t *__r
             const int idx = tid + 256 * i;
             if (idx < total) *reinterpret_cast<u32x4 *>(Bs + (idx / vpr) * ldb + (idx % vpr) * 8) = tmp[i];
         }
-        for (int idx = tid; idx < GP * D; idx += 256) {
-            const int g = idx / D, i = idx % D;
-            qs[g][i] = g < G ? bf16_bits_to_f32(q[(static_cast<size_t>(b) * hq + h * G + g) * D + i]) * scale : 0.f;
-        }
     }
-    __syncthreads();
-
-    const int key_base = blockIdx.x * kQkMfmaTile + wave * 64;
-    if (key_base >= KC) return;  // no barrier follows
-    // chunk of every slot this wave's 64 keys touch (at most 64 slots): one
-    // load per lane, then shuffles
-    const int slot0 = key_base / c;
-    const int my_slot = slot0 + lane;
-    const int my_chunk = my_slot < k ? slot_chunk[static_cast<size_t>(bh) * k + my_slot] : 0;
-    // rotation rates (turns per position) of this lane's dims 16*hb + 4*quad + e
-    double thr[HB][4];
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) thr[hb][e] = theta_rev[hb * 16 + quad * 4 + e];
-
     // Gathered A row of this lane's key in a 16-key block, 8 rank values per
     // 32-wide rank block, through a buffer resource over this sequence's A:
-    // keys past KC, rank columns past r and the prefetch after the last block
-    // read zeros without a memory access, so no branch surrounds a load and
-    // the next block's rows stay in flight while one block is computed.
+    // keys past KC and rank columns past r read zeros without a memory
+    // access, so no branch surrounds a load.
     const Rsrc ar = make_rsrc(A + static_cast<size_t>(b) * s * r, static_cast<uint32_t>(s) * r * 2);
     const Rsrc lr = make_rsrc(logits + static_cast<size_t>(bh) * G * NK, static_cast<uint32_t>(G) * NK * 4);
-    auto load_a = [&](int kb0, bool on, u32x4 *aop, int &pos) {
-        const int key = kb0 + row;
-        const bool kv = on && key < KC;
+    u32x4 aop[MB][NKB];
+    int pos[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int key = key_base + mb * 16 + row;
+        const bool kv = active && key < KC;
         const int kk = key < KC ? key : key_base;
         const int chunk = __shfl(my_chunk, kk / c - slot0, 64);
-        pos = chunk * c + kk % c;
-        const int base = (pos * r + quad * 8) * 2;
+        pos[mb] = chunk * c + kk % c;
+        const int base = (pos[mb] * r + quad * 8) * 2;
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
-            aop[kb] = buf_ld128(ar, kv && kb * 32 + quad * 8 < r ? base + kb * 64 : kOob);
-    };
-    u32x4 aop[NKB];
-    int pos;
-    load_a(key_base, true, aop, pos);
-#pragma unroll 1
-    for (int mb = 0; mb < 4; ++mb) {
+            aop[mb][kb] = buf_ld128(ar, kv && kb * 32 + quad * 8 < r ? base + kb * 64 : kOob);
+    }
+    // the group's queries (raw bfloat16) as the logit MFMA's A operand: lane
+    // (quad, row) holds head `row` (rows past G repeat the last head; their
+    // outputs are dropped) in the permuted dim order
+    bf16x8 qa[NP];
+    {
+        const uint16_t *qrow = q + (static_cast<size_t>(b) * hq + h * G + min(row, G - 1)) * D + quad * 4;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const u32x2 lo = *reinterpret_cast<const u32x2 *>(qrow + 32 * p);
+            const u32x2 hi = *reinterpret_cast<const u32x2 *>(qrow + 32 * p + 16);
+            qa[p] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        }
+    }
+
+    __syncthreads();
+    if (!active) return;  // no barrier follows
+
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
         const int kb0 = key_base + mb * 16;
         if (kb0 >= KC) break;  // wave-uniform
-        u32x4 anext[NKB];
-        int pos_next = 0;
-        const bool more = mb + 1 < 4 && kb0 + 16 < KC;
-        load_a(kb0 + 16, more, anext, pos_next);
         f32x4 acc[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-            const bf16x8 bop = __builtin_bit_cast(bf16x8, aop[kb]);
+            const bf16x8 bop = __builtin_bit_cast(bf16x8, aop[mb][kb]);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 const bf16x8 aw = __builtin_bit_cast(
@@ -349,7 +370,7 @@ __global__ __launch_bounds__(256) void qk_sparse_mfma_kernel(const uint16_t *__r
         // RoPE of this lane's key at its original position: the angle in
         // turns, pos * theta_i / (2 pi), is reduced to [-1/2, 1/2] in double
         // precision and fed to the hardware sin/cos (which take turns)
-        const double posd = static_cast<double>(pos);
+        const double posd = static_cast<double>(pos[mb]);
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb) {
 #pragma unroll
@@ -363,31 +384,18 @@ __global__ __launch_bounds__(256) void qk_sparse_mfma_kernel(const uint16_t *__r
             }
         }
 
-        // partial logits over this lane's dims, then the lane-group sum
-        float part[GP];
+        // logits[head, key] = sum over dims of q . K_rot: lane (quad, row)
+        // ends with heads 4*quad + e of key kb0 + row
+        f32x4 lg = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int g = 0; g < GP; ++g) {
-            float a = 0.f;
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const float4 qv = *reinterpret_cast<const float4 *>(&qs[g][nb * 16 + quad * 4]);
-                a += qv.x * acc[nb][0] + qv.y * acc[nb][1] + qv.z * acc[nb][2] + qv.w * acc[nb][3];
-            }
-            part[g] = a;
-        }
-#pragma unroll
-        for (int x = 0; x < GP / 2; ++x) part[x] = swap_sum32(part[x], part[x + GP / 2]);
-#pragma unroll
-        for (int x = 0; x < HPL; ++x) part[x] = swap_sum16(part[x], part[x + HPL]);
+        for (int p = 0; p < NP; ++p)
+            lg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[p], pack_bf16x8(acc[2 * p], acc[2 * p + 1]), lg, 0, 0, 0);
         const int key = kb0 + row;
 #pragma unroll
-        for (int x = 0; x < HPL; ++x) {
-            const int g = quad * HPL + x;
-            buf_st32(part[x], lr, key < KC && g < G ? (g * NK + OC + key) * 4 : kOob);
+        for (int e = 0; e < 4; ++e) {
+            const int g = quad * 4 + e;
+            buf_st32(lg[e] * scale, lr, key < KC && g < G ? (g * NK + OC + key) * 4 : kOob);
         }
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) aop[kb] = anext[kb];
-        pos = pos_next;
     }
 }
 

@@ -43,6 +43,11 @@ CASES = {
     "bf16-no-static": synth.LLAMA_32K.with_(h_q=8, h_kv=2, s=2048, r=96, o=0, k=12, w=0, steps=3, rho=0.9),
     # full budget: every selectable chunk is attended
     "bf16-full-budget": synth.LLAMA_32K.with_(h_q=8, h_kv=2, s=1024, o=4, k=120, w=32, steps=2, rho=0.9),
+    # the sweep's other chunk sizes and ranks: chunk 16 (one chunk per 16-key
+    # block), rank 96 with chunk 4 (rank blocks padded 3 -> 4), rank 192 (6)
+    "bf16-chunk16": synth.LLAMA_32K.with_(s=8192, c=16, o=3, k=8, w=32, steps=3, rho=0.9),
+    "bf16-rank96-chunk4": synth.LLAMA_32K.with_(s=4096, c=4, r=96, o=6, k=16, w=32, steps=3, rho=0.9),
+    "bf16-rank192": synth.LLAMA_32K.with_(s=4096, r=192, o=4, k=8, w=32, steps=3, rho=0.9),
 }
 
 
