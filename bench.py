@@ -61,10 +61,13 @@ def algorithmic_bytes(wl) -> dict:
     }
 
 
+SCORE_SOURCES = ("select.hip", "skv_device.h", "skv_dims.h")  # the files the scoring kernel is built from
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_kv_cache_step_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in SCORE_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
