@@ -44,6 +44,7 @@ class _Cfg(ctypes.Structure):
         ("d", ctypes.c_int32), ("s", ctypes.c_int32), ("c", ctypes.c_int32),
         ("r", ctypes.c_int32), ("o", ctypes.c_int32), ("k", ctypes.c_int32),
         ("w", ctypes.c_int32), ("rope_base", ctypes.c_double), ("bf16", ctypes.c_int32),
+        ("n_app", ctypes.c_int32),
     ]
 
 
@@ -67,9 +68,9 @@ class Shape:
     def n(self) -> int:
         return self.s // self.c
 
-    def _c(self) -> _Cfg:
+    def _c(self, n_app: int = 0) -> _Cfg:
         return _Cfg(self.b, self.h_q, self.h_kv, self.d, self.s, self.c, self.r,
-                    self.o, self.k, self.w, float(self.rope_base), int(self.bf16))
+                    self.o, self.k, self.w, float(self.rope_base), int(self.bf16), int(n_app))
 
 
 def build(force: bool = False) -> str:
@@ -206,6 +207,35 @@ def prefill(shape: Shape, k_pre, v) -> dict:
 
 
 # --------------------------------------------------------------------------
+# Decode-token append: the token generated at position s + t joins the dense
+# local block (the third key block of Algorithm 2 step 4), its key rotated at
+# that position like every other stored key and rounded once to storage.
+# --------------------------------------------------------------------------
+def append(shape: Shape, meta: dict, k_new, v_new) -> dict:
+    """meta with the new token's key (pre-RoPE, (b, h_kv, d)) and value
+    appended to k_loc / v_loc; the token's position is s plus the number of
+    tokens appended before it."""
+    k_new, v_new = _f64(k_new), _f64(v_new)
+    b, hkv, d = shape.b, shape.h_kv, shape.d
+    assert k_new.shape == (b, hkv, d) and v_new.shape == (b, hkv, d)
+    pos = shape.s + _n_app(shape, meta)
+    k_rot = np.empty_like(k_new)
+    for bi in range(b):
+        for h in range(hkv):
+            k_rot[bi, h] = rope(k_new[bi, h], pos, shape.rope_base)
+    out = dict(meta)
+    out["k_loc"] = np.concatenate([_f64(meta["k_loc"]), round_store(k_rot, shape.bf16)[:, :, None, :]], axis=2)
+    out["v_loc"] = np.concatenate([_f64(meta["v_loc"]), v_new[:, :, None, :]], axis=2)
+    return out
+
+
+def _n_app(shape: Shape, meta: dict) -> int:
+    n = meta["k_loc"].shape[2] - shape.w
+    assert n >= 0 and meta["v_loc"].shape[2] == shape.w + n
+    return n
+
+
+# --------------------------------------------------------------------------
 # Algorithm 2
 # --------------------------------------------------------------------------
 def attend(shape: Shape, q, sel, A, B, v_host, meta: dict) -> np.ndarray:
@@ -214,7 +244,7 @@ def attend(shape: Shape, q, sel, A, B, v_host, meta: dict) -> np.ndarray:
     sel = np.ascontiguousarray(sel, dtype=np.int32)
     assert sel.shape == (shape.b, shape.h_kv, shape.k)
     out = np.empty((shape.b, shape.h_q, shape.d))
-    cfg = shape._c()
+    cfg = shape._c(_n_app(shape, meta))
     m = {key: _f64(meta[key]) for key in ("k_out", "v_out", "k_loc", "v_loc")}
     rc = _lib().orc_attend(ctypes.byref(cfg), _p(q, _D), _p(sel, _I32), _p(A, _D), _p(B, _D),
                            _p(v_host, _D), _p(m["k_out"], _D), _p(m["v_out"], _D),
@@ -232,7 +262,7 @@ def decode(shape: Shape, q, meta: dict, A, B, v_host) -> dict:
                sel=np.empty((b, hkv, k), dtype=np.int32), out=np.empty((b, hq, d)))
     m = {key: _f64(meta[key]) for key in ("landmarks", "k_out", "v_out", "k_loc", "v_loc")}
     cand = np.ascontiguousarray(meta["cand"], dtype=np.uint8)
-    cfg = shape._c()
+    cfg = shape._c(_n_app(shape, meta))
     rc = _lib().orc_decode(ctypes.byref(cfg), _p(q, _D), _p(m["landmarks"], _D), _p(cand, _U8),
                            _p(A, _D), _p(B, _D), _p(v_host, _D), _p(m["k_out"], _D),
                            _p(m["v_out"], _D), _p(m["k_loc"], _D), _p(m["v_loc"], _D),

@@ -59,6 +59,8 @@ typedef struct {
     int32_t w;       /* local window in tokens, a multiple of c*/
     double rope_base;
     int32_t bf16;    /* 1: stored tensors are bfloat16         */
+    int32_t n_app;   /* decode tokens appended after the window:
+                        the local block holds w + n_app tokens  */
 } orc_cfg;
 
 enum { ORC_OK = 0, ORC_E_SHAPE = -2, ORC_E_NOMEM = -4 };
@@ -155,6 +157,7 @@ static int check_cfg(const orc_cfg *g)
     if (g->k < 0 || g->k > n - n_loc - g->o) return ORC_E_SHAPE;
     if ((int64_t)g->o * g->c + (int64_t)g->k * g->c + g->w < 1) return ORC_E_SHAPE;
     if (g->r < 1) return ORC_E_SHAPE;
+    if (g->n_app < 0) return ORC_E_SHAPE;
     return ORC_OK;
 }
 
@@ -269,7 +272,8 @@ int orc_attend(const orc_cfg *cfg, const double *q, const int32_t *sel,
     int rc = check_cfg(cfg);
     if (rc) return rc;
     const int32_t Bn = cfg->b, H = cfg->h_kv, Hq = cfg->h_q, G = Hq / H, d = cfg->d;
-    const int32_t s = cfg->s, c = cfg->c, r = cfg->r, o = cfg->o, k = cfg->k, w = cfg->w;
+    const int32_t s = cfg->s, c = cfg->c, r = cfg->r, o = cfg->o, k = cfg->k;
+    const int32_t w = cfg->w + cfg->n_app;  /* local block: the window, then the appended tokens */
     const int32_t nk = o * c + k * c + w;
     const double scale = 1.0 / sqrt((double)d);
     int failed = 0;

@@ -361,6 +361,49 @@ def test_partial_budget_is_attention_over_the_partition():
         np.testing.assert_allclose(res["out"][0, g], ref, atol=2e-6)
 
 
+def test_appended_tokens_join_the_dense_context():
+    """Decode-token append: tokens generated at positions s, s+1, ... join the
+    dense local block.  With every selectable chunk chosen and full rank, the
+    step must equal dense attention over all s + t tokens, each key rotated
+    at its own position (the appended ones included); at a partial budget,
+    dense attention over the partition plus the appended tokens."""
+    rng = np.random.default_rng(21)
+    b, hq, hkv, d, s, c, o, w, t = 2, 4, 2, 8, 64, 4, 2, 8, 3
+    n = s // c
+    shape = Shape(b=b, h_q=hq, h_kv=hkv, d=d, s=s, c=c, r=hkv * d, o=o, k=n - o - w // c, w=w, bf16=False)
+    K = rng.standard_normal((b, hkv, s + t, d)).astype(np.float32).astype(np.float64)
+    V = rng.standard_normal((b, hkv, s + t, d)).astype(np.float32).astype(np.float64)
+    q = rng.standard_normal((b, hq, d))
+    meta, A, B = _meta_and_factors(shape, K[:, :, :s], V[:, :, :s])
+    # no append: unchanged
+    np.testing.assert_array_equal(oracle.decode(shape, q, meta, A, B, V[:, :, :s])["out"],
+                                  oracle.decode(shape, q, dict(meta), A, B, V[:, :, :s])["out"])
+    for j in range(t):
+        meta = oracle.append(shape, meta, K[:, :, s + j], V[:, :, s + j])
+    assert meta["k_loc"].shape == (b, hkv, w + t, d)
+    res = oracle.decode(shape, q, meta, A, B, V[:, :, :s])
+    Kr = rope_complex(K, np.arange(s + t)[None, None, :])
+    for bi in range(b):
+        for g in range(hq):
+            h = g // (hq // hkv)
+            ref = dense_attention(q[bi, g], Kr[bi, h], V[bi, h])
+            np.testing.assert_allclose(res["out"][bi, g], ref, rtol=0, atol=2e-6)
+    # partial budget: the partition of the context plus the appended tokens
+    shape_p = Shape(b=b, h_q=hq, h_kv=hkv, d=d, s=s, c=c, r=hkv * d, o=o, k=3, w=w, bf16=False)
+    meta_p, A_p, B_p = _meta_and_factors(shape_p, K[:, :, :s], V[:, :, :s])
+    for j in range(t):
+        meta_p = oracle.append(shape_p, meta_p, K[:, :, s + j], V[:, :, s + j])
+    res_p = oracle.decode(shape_p, q, meta_p, A_p, B_p, V[:, :, :s])
+    for bi in range(b):
+        for g in range(hq):
+            h = g // (hq // hkv)
+            chunks = sorted(set(meta_p["outliers"][bi, h]) | set(res_p["sel"][bi, h]) |
+                            set(range(n - w // c, n)))
+            toks = np.concatenate([np.arange(j * c, (j + 1) * c) for j in chunks] + [np.arange(s, s + t)])
+            ref = dense_attention(q[bi, g], Kr[bi, h, toks], V[bi, h, toks])
+            np.testing.assert_allclose(res_p["out"][bi, g], ref, rtol=0, atol=2e-6)
+
+
 def test_gqa_head_mapping_and_convexity():
     rng = np.random.default_rng(12)
     b, hq, hkv, d, s, c = 1, 8, 2, 8, 64, 4
