@@ -147,6 +147,9 @@ def main() -> int:
     ap.add_argument("--top-k", type=int, default=None, help="selected chunks per KV head (budget) override")
     ap.add_argument("--rank", type=int, default=None, help="rank of the key factors override")
     ap.add_argument("--outlier-chunks", type=int, default=None, help="outlier chunks override")
+    ap.add_argument("--append", action="store_true",
+                    help="generation loop: each layer-step also appends the generated token to the local block "
+                         "(no oracle baseline in this mode)")
     ap.add_argument("--sweep", action="store_true",
                     help="run chunk-size / budget / rank variants of the workload, one JSON line each")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -213,6 +216,7 @@ def main() -> int:
         host_bufs = []
         Ls, qs = [], []
         keep = {}  # inputs of the spot-checked layer, for the oracle
+        new_kv = []  # decode-token append: (keys, values) per layer
         spot_layer = layers - 1
         for l in range(layers):
             k_pre = synth.k_pre_torch(wl, l, dev)
@@ -220,13 +224,19 @@ def main() -> int:
             A, B = svd_factors(k_pre, wl.r)
             lay = skv.Layer(batch=wl.b, heads_q=wl.h_q, heads_kv=wl.h_kv, head_dim=wl.d, seq_len=wl.s, chunk=wl.c,
                             rank=wl.r, n_outlier=wl.o, top_k=wl.k, local_window=wl.w, rope_base=wl.rope_base,
-                            bf16=wl.bf16)
+                            bf16=wl.bf16, max_new=(nq + args.steps) if args.append else 0)
             if l < n_host:
                 host_bufs.append(lay.host_buffer())
             lay.prefill_meta(k_pre, v, A, B, host_bufs[l % n_host])
             qs.append(synth.queries_torch(wl, l, dev, steps=nq))
+            if args.append:
+                # the generated tokens' pre-RoPE keys and values, one per step
+                g = torch.Generator(device=dev)
+                g.manual_seed(1000003 * (l + 1) + wl.wid)
+                new_kv.append((torch.randn((nq, wl.b, wl.h_kv, wl.d), generator=g, device=dev).to(dt),
+                               torch.randn((nq, wl.b, wl.h_kv, wl.d), generator=g, device=dev).to(dt)))
             torch.cuda.synchronize()
-            if l == spot_layer and not args.no_cpu_baseline:
+            if l == spot_layer and not args.no_cpu_baseline and not args.append:
                 sample = [0, wl.b // 2] if wl.b > 1 else [0]
                 keep = {"seqs": sample, "k_pre": k_pre[sample].float().cpu(), "v": v[sample].float().cpu()}
             del k_pre, v, A, B
@@ -242,6 +252,8 @@ def main() -> int:
             for t in range(t_begin, t_begin + t_count):
                 for l in range(layers):
                     Ls[l].decode_step(qs[l][t], outs[l], stream)
+                    if args.append:  # the generated token joins the local block
+                        Ls[l].append(new_kv[l][0][t], new_kv[l][1][t], stream)
 
         if args.copy_calibration:
             src = torch.ones(COPY_BYTES, dtype=torch.uint8, device=dev)
@@ -378,7 +390,8 @@ def main() -> int:
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16" if wl.bf16 else "f32", "data": "synthetic",
             "config": {"workload": wl.name, "batch": wl.b, "seq_len": wl.s, "heads_q": wl.h_q, "heads_kv": wl.h_kv,
                        "head_dim": wl.d, "chunk": wl.c, "rank": wl.r, "outlier_chunks": wl.o, "top_k": wl.k,
-                       "local_window": wl.w, "layers": layers, "host_v_buffers": n_host},
+                       "local_window": wl.w, "layers": layers, "host_v_buffers": n_host,
+                       **({"append": True} if args.append else {})},
             "us_per_layer_step": round(t_ls * 1e6, 3),
             "effective_TBps": round(alg_total / t_ls / 1e12, 4),
             "equivalent_TBps": round(dense_kv / t_ls / 1e12, 4),

@@ -65,7 +65,7 @@ enum {
  *   n = seq_len / chunk, n_loc = local_window / chunk;
  *   0 <= n_outlier <= n - n_loc; 0 <= top_k <= n - n_loc - n_outlier and
  *   top_k <= 4096; at least one attended key; 1 <= rank <= 256;
- *   rope_base > 0.
+ *   rope_base > 0; 0 <= max_new <= 2^20.
  */
 typedef struct {
     int32_t batch;         /* b: sequences decoded together                  */
@@ -80,6 +80,8 @@ typedef struct {
     int32_t local_window;  /* w: last tokens always attended (dense)         */
     float rope_base;       /* RoPE base (theta_i = base^(-2i/d))             */
     int32_t dtype;         /* SKV_F32 or SKV_BF16                            */
+    int32_t max_new;       /* decode tokens shadowkv_append may add to the
+                              local block (0: none)                          */
 } skv_config;
 
 typedef struct skv_layer skv_layer;
@@ -143,6 +145,22 @@ int shadowkv_load_meta(skv_layer *layer, const void *landmarks, const int32_t *o
                        void *v_host, void *stream);
 
 /*
+ * Decode-token append: the token generated at position seq_len + t (t =
+ * tokens appended since the last prefill_meta / load_meta) joins the dense
+ * local block, the third key block of Algorithm 2 step 4, and every later
+ * decode step attends to it.  The pages do not describe generation beyond the
+ * decoding step; this reading keeps generated tokens dense and uncompressed.
+ *   k_new  device (b, h_kv, d)  the token's pre-RoPE key; rotated here at its
+ *          position exactly like the prefill keys and rounded to dtype.
+ *   v_new  device (b, h_kv, d)  its value.
+ * Enqueued on `stream` (later decode steps must be ordered after it).
+ * SKV_E_STATE before prefill_meta / load_meta; SKV_E_SHAPE once max_new
+ * tokens have been appended.  prefill_meta and load_meta empty the appended
+ * part of the block.
+ */
+int shadowkv_append(skv_layer *layer, const void *k_new, const void *v_new, void *stream);
+
+/*
  * Algorithm 2 (Decoding): one step of one layer for all b sequences.
  *   q    device (b, h_q, d)  post-RoPE queries.
  *   out  device (b, h_q, d)  attention output.
@@ -185,7 +203,8 @@ enum {
     SKV_T_CACHE_V = 8,      /* dtype (b, h_kv, k*c, d): resident V by slot    */
     SKV_T_K_OUT = 9,        /* dtype (b, h_kv, o*c, d)                        */
     SKV_T_V_OUT = 10,
-    SKV_T_K_LOC = 11,       /* dtype (b, h_kv, w, d)                          */
+    SKV_T_K_LOC = 11,       /* dtype (b, h_kv, w + max_new, d): the window's
+                               keys, then the appended ones                   */
     SKV_T_V_LOC = 12,
     SKV_T_COUNT = 13
 };

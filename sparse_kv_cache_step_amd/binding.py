@@ -26,7 +26,7 @@ SKV_K_COUNT = len(KERNELS)
 
 EXPORTS = (
     "shadowkv_layer_create", "shadowkv_layer_destroy", "shadowkv_prefill_meta", "shadowkv_load_meta",
-    "shadowkv_decode_step", "shadowkv_reset_cache", "shadowkv_get_stats", "shadowkv_reset_stats",
+    "shadowkv_append", "shadowkv_decode_step", "shadowkv_reset_cache", "shadowkv_get_stats", "shadowkv_reset_stats",
     "shadowkv_tensor_bytes", "shadowkv_read", "shadowkv_set_overlap", "shadowkv_set_timing",
     "shadowkv_get_timing",
     "shadowkv_host_alloc", "shadowkv_host_free", "shadowkv_last_error", "shadowkv_equiv_bandwidth",
@@ -37,7 +37,8 @@ class skv_config(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("rank", ctypes.c_int32), ("n_outlier", ctypes.c_int32), ("top_k", ctypes.c_int32),
-                ("local_window", ctypes.c_int32), ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("local_window", ctypes.c_int32), ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("max_new", ctypes.c_int32)]
 
 
 class skv_stats(ctypes.Structure):
@@ -67,6 +68,7 @@ def lib() -> ctypes.CDLL:
             "shadowkv_layer_destroy": (None, [_VP]),
             "shadowkv_prefill_meta": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
             "shadowkv_load_meta": (ctypes.c_int, [_VP] * 11),
+            "shadowkv_append": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
             "shadowkv_decode_step": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
             "shadowkv_reset_cache": (ctypes.c_int, [_VP, _VP]),
             "shadowkv_get_stats": (ctypes.c_int, [_VP, ctypes.POINTER(skv_stats)]),
@@ -120,6 +122,10 @@ def shadowkv_prefill_meta(h, k_pre, k_rope, v, A, B, v_host, stream) -> None:
 
 def shadowkv_load_meta(h, landmarks, outliers, k_out, v_out, k_loc, v_loc, A, B, v_host, stream) -> None:
     _check(lib().shadowkv_load_meta(h, landmarks, outliers, k_out, v_out, k_loc, v_loc, A, B, v_host, stream))
+
+
+def shadowkv_append(h, k_new, v_new, stream) -> None:
+    _check(lib().shadowkv_append(h, k_new, v_new, stream))
 
 
 def shadowkv_decode_step(h, q, out, stream) -> None:
@@ -219,10 +225,10 @@ class Layer:
     """One model layer's ShadowKV state on the current GPU."""
 
     def __init__(self, *, batch, heads_q, heads_kv, head_dim, seq_len, chunk, rank, n_outlier, top_k,
-                 local_window, rope_base=10000.0, bf16=True):
+                 local_window, rope_base=10000.0, bf16=True, max_new=0):
         torch = _torch()
         self.cfg = skv_config(batch, heads_q, heads_kv, head_dim, seq_len, chunk, rank, n_outlier, top_k,
-                              local_window, float(rope_base), SKV_BF16 if bf16 else SKV_F32)
+                              local_window, float(rope_base), SKV_BF16 if bf16 else SKV_F32, max_new)
         self.dtype = torch.bfloat16 if bf16 else torch.float32
         self.n = seq_len // chunk if chunk > 0 else 0
         self.device = torch.device("cuda", torch.cuda.current_device())
@@ -239,6 +245,7 @@ class Layer:
             "landmarks": (b, hkv, self.n, d), "outliers": (b, hkv, c.n_outlier),
             "k_out": (b, hkv, c.n_outlier * ch, d), "v_out": (b, hkv, c.n_outlier * ch, d),
             "k_loc": (b, hkv, c.local_window, d), "v_loc": (b, hkv, c.local_window, d),
+            "k_new": (b, hkv, d), "v_new": (b, hkv, d),
         }[name]
 
     def _dev(self, name, t, dtype=None, optional=False):
@@ -285,6 +292,9 @@ class Layer:
                            _stream_ptr(stream))
         self._v_host = v_host
 
+    def append(self, k_new, v_new, stream=None):
+        shadowkv_append(self.h, self._dev("k_new", k_new), self._dev("v_new", v_new), _stream_ptr(stream))
+
     def decode_step(self, q, out, stream=None):
         shadowkv_decode_step(self.h, self._dev("q", q), self._dev("out", out), _stream_ptr(stream))
 
@@ -312,8 +322,8 @@ class Layer:
             SKV_T_GROUP_SCORES: (torch.float32, (b, hkv, self.n)),
             SKV_T_SELECTION: (torch.int32, (b, hkv, k)), SKV_T_SLOT_CHUNKS: (torch.int32, (b, hkv, k)),
             SKV_T_CACHE_V: (dt, (b, hkv, k * ch, d)), SKV_T_K_OUT: (dt, (b, hkv, c.n_outlier * ch, d)),
-            SKV_T_V_OUT: (dt, (b, hkv, c.n_outlier * ch, d)), SKV_T_K_LOC: (dt, (b, hkv, c.local_window, d)),
-            SKV_T_V_LOC: (dt, (b, hkv, c.local_window, d)),
+            SKV_T_V_OUT: (dt, (b, hkv, c.n_outlier * ch, d)), SKV_T_K_LOC: (dt, (b, hkv, c.local_window + c.max_new, d)),
+            SKV_T_V_LOC: (dt, (b, hkv, c.local_window + c.max_new, d)),
         }[which]
         t = torch.empty(spec[1], dtype=spec[0], device=self.device)
         nbytes = t.numel() * t.element_size()

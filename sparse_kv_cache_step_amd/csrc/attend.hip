@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void qk_generic_kernel(const T *__restrict__ q
                                                          const int32_t *__restrict__ slot_chunk,
                                                          const double *__restrict__ theta,
                                                          float *__restrict__ logits, int hkv, int G, int s, int c,
-                                                         int r, int k, int OC, int KC, int w, int NK, int t_out,
+                                                         int r, int k, int OC, int KC, int w, int wcap, int NK, int t_out,
                                                          int t_sp, float scale) {
     __shared__ float Ks[kQkTile][D + 1];
     __shared__ float qs[kMaxGroup][D];
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void qk_generic_kernel(const T *__restrict__ q
         qs[i / D][i % D] = Elem<T>::ld(q, (static_cast<size_t>(b) * hq + h * G) * D + i) * scale;
     if (seg != 1) {
         const T *src = seg == 0 ? k_out + (static_cast<size_t>(bh) * OC + key0) * D
-                                : k_loc + (static_cast<size_t>(bh) * w + key0) * D;
+                                : k_loc + (static_cast<size_t>(bh) * wcap + key0) * D;
         for (int idx = threadIdx.x; idx < cnt * D; idx += 256) Ks[idx / D][idx % D] = Elem<T>::ld(src, idx);
     } else {
         const T *Bh = Bt + static_cast<size_t>(bh) * D * r;
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(256) void qk_static_mfma_kernel(const uint16_t *__r
                                                              const uint16_t *__restrict__ k_out,
                                                              const uint16_t *__restrict__ k_loc,
                                                              float *__restrict__ logits, int hkv, int G, int OC,
-                                                             int KC, int w, int NK, float scale) {
+                                                             int KC, int w, int wcap, int NK, float scale) {
     constexpr int KS = D / 32;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row = lane & 15, quad = lane >> 4;
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256) void qk_static_mfma_kernel(const uint16_t *__r
     for (int kb0 = (blockIdx.x * 4 + wave) * 16; kb0 < nstat; kb0 += gridDim.x * 64) {
         const int sk = kb0 + row;
         const uint16_t *src = sk < OC ? k_out + (static_cast<size_t>(bh) * OC + sk) * D
-                                      : k_loc + (static_cast<size_t>(bh) * w + (sk - OC)) * D;
+                                      : k_loc + (static_cast<size_t>(bh) * wcap + (sk - OC)) * D;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -424,7 +424,7 @@ template <typename T, int D, int GP>
 __global__ __launch_bounds__(256) void pv_kernel(const float *__restrict__ logits, const T *__restrict__ v_out,
                                                  const T *__restrict__ vc, const T *__restrict__ v_loc,
                                                  float2 *__restrict__ part_ml, float *__restrict__ part_acc,
-                                                 int G, int OC, int KC, int w, int NK, int tiles) {
+                                                 int G, int OC, int KC, int w, int wcap, int NK, int tiles) {
     constexpr int CG = D / 8;              // column groups of 8
     constexpr int RG = 256 / CG;           // row groups
     constexpr int RPT = kPvTile / RG;      // rows per thread
@@ -458,7 +458,7 @@ __global__ __launch_bounds__(256) void pv_kernel(const float *__restrict__ logit
         const int key = key0 + min(rg + RG * i, cnt - 1);
         const T *vrow = key < OC ? v_out + (static_cast<size_t>(bh) * OC + key) * D
                       : key < OC + KC ? vc + (static_cast<size_t>(bh) * KC + (key - OC)) * D
-                                      : v_loc + (static_cast<size_t>(bh) * w + (key - OC - KC)) * D;
+                                      : v_loc + (static_cast<size_t>(bh) * wcap + (key - OC - KC)) * D;
         const u32x4 *src = reinterpret_cast<const u32x4 *>(vrow + cg * 8);
 #pragma unroll
         for (int u = 0; u < VPR; ++u) raw[i][u] = src[u];
@@ -640,7 +640,7 @@ static hipError_t qk_generic_t(const Dims &dm, const void *q, const void *k_out,
     hipLaunchKernelGGL((qk_generic_kernel<T, D>), dim3(tiles, dm.b * dm.hkv), dim3(256), 0, st,
                        static_cast<const T *>(q), static_cast<const T *>(k_out), static_cast<const T *>(k_loc),
                        static_cast<const T *>(A), static_cast<const T *>(Bt), slot_chunk, theta, logits, dm.hkv,
-                       dm.G, dm.s, dm.c, dm.r, dm.k, dm.OC, dm.KC, dm.w, dm.NK, t_out, t_sp, dm.scale);
+                       dm.G, dm.s, dm.c, dm.r, dm.k, dm.OC, dm.KC, dm.w, dm.wcap, dm.NK, t_out, t_sp, dm.scale);
     return hipGetLastError();
 }
 
@@ -683,7 +683,7 @@ static hipError_t qk_static_t(const Dims &dm, const void *q, const void *k_out, 
     dim3 grid((nstat + 63) / 64, dm.b * dm.hkv);
     hipLaunchKernelGGL(qk_static_mfma_kernel<D>, grid, dim3(256), 0, st, static_cast<const uint16_t *>(q),
                        static_cast<const uint16_t *>(k_out), static_cast<const uint16_t *>(k_loc), logits, dm.hkv,
-                       dm.G, dm.OC, dm.KC, dm.w, dm.NK, dm.scale);
+                       dm.G, dm.OC, dm.KC, dm.w, dm.wcap, dm.NK, dm.scale);
     return hipGetLastError();
 }
 
@@ -718,7 +718,7 @@ static hipError_t pv_t(const Dims &dm, const float *logits, const void *v_out, c
                        float2 *part_ml, float *part_acc, hipStream_t st) {
     hipLaunchKernelGGL((pv_kernel<T, D, GP>), dim3(dm.pv_tiles, dm.b * dm.hkv), dim3(256), 0, st, logits,
                        static_cast<const T *>(v_out), static_cast<const T *>(vc), static_cast<const T *>(v_loc),
-                       part_ml, part_acc, dm.G, dm.OC, dm.KC, dm.w, dm.NK, dm.pv_tiles);
+                       part_ml, part_acc, dm.G, dm.OC, dm.KC, dm.w, dm.wcap, dm.NK, dm.pv_tiles);
     return hipGetLastError();
 }
 

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void gather_static_kernel(const T *__restrict_
                                                             const double *__restrict__ theta,
                                                             T *__restrict__ k_out, T *__restrict__ v_out,
                                                             T *__restrict__ k_loc, T *__restrict__ v_loc,
-                                                            int s, int c, int o, int w) {
+                                                            int s, int c, int o, int w, int wcap) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int bh = blockIdx.y;
     const int rr = blockIdx.x * 4 + wave;
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256) void gather_static_kernel(const T *__restrict_
         kd = k_out; vd = v_out; drow = static_cast<size_t>(bh) * OC + rr;
     } else {
         pos = s - w + (rr - OC);
-        kd = k_loc; vd = v_loc; drow = static_cast<size_t>(bh) * w + (rr - OC);
+        kd = k_loc; vd = v_loc; drow = static_cast<size_t>(bh) * wcap + (rr - OC);
     }
     constexpr int H = D / 2;
     const size_t src = (static_cast<size_t>(bh) * s + pos) * D;
@@ -208,7 +208,7 @@ static hipError_t gather_t(const Dims &dm, const void *k_pre, const void *k_rope
     hipLaunchKernelGGL((gather_static_kernel<T, D>), grid, dim3(256), 0, st, static_cast<const T *>(k_pre),
                        static_cast<const T *>(k_rope), static_cast<const T *>(v), outliers, theta,
                        static_cast<T *>(k_out), static_cast<T *>(v_out), static_cast<T *>(k_loc),
-                       static_cast<T *>(v_loc), dm.s, dm.c, dm.o, dm.w);
+                       static_cast<T *>(v_loc), dm.s, dm.c, dm.o, dm.w, dm.wcap);
     return hipGetLastError();
 }
 
@@ -255,6 +255,47 @@ hipError_t launch_fill_i32(int32_t *p, int32_t value, size_t count, hipStream_t 
     if (blocks > 4096) blocks = 4096;
     hipLaunchKernelGGL(fill_i32_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, st, p, value, count);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Decode-token append: the key of the token generated at position `pos` is
+// rotated exactly like the prefill keys (angle in double precision, result
+// rounded once to the storage type) and written, with its value, to row
+// `row` of its (sequence, KV head)'s local block.  Thread i owns the RoPE
+// pair (i, i + d/2).
+// ---------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(D / 2) void append_kernel(const T *__restrict__ k_new, const T *__restrict__ v_new,
+                                                       const double *__restrict__ theta, T *__restrict__ k_loc,
+                                                       T *__restrict__ v_loc, int wcap, int row, int pos) {
+    constexpr int H = D / 2;
+    const int bh = blockIdx.x, i = threadIdx.x;
+    const size_t src = static_cast<size_t>(bh) * D;
+    const size_t dst = (static_cast<size_t>(bh) * wcap + row) * D;
+    float y1, y2;
+    rope_store_pair<T>(k_new, nullptr, src, i, H, pos, theta[i], y1, y2);
+    Elem<T>::st(k_loc, dst + i, y1);
+    Elem<T>::st(k_loc, dst + i + H, y2);
+    v_loc[dst + i] = v_new[src + i];
+    v_loc[dst + i + H] = v_new[src + i + H];
+}
+
+template <typename T, int D>
+static hipError_t append_t(const Dims &dm, const void *k_new, const void *v_new, const double *theta, void *k_loc,
+                           void *v_loc, int row, int pos, hipStream_t st) {
+    hipLaunchKernelGGL((append_kernel<T, D>), dim3(dm.b * dm.hkv), dim3(D / 2), 0, st, static_cast<const T *>(k_new),
+                       static_cast<const T *>(v_new), theta, static_cast<T *>(k_loc), static_cast<T *>(v_loc), dm.wcap,
+                       row, pos);
+    return hipGetLastError();
+}
+
+hipError_t launch_append(const Dims &dm, const void *k_new, const void *v_new, const double *theta, void *k_loc,
+                         void *v_loc, int row, int pos, hipStream_t st) {
+    if (dm.bf16)
+        return dm.d == 128 ? append_t<uint16_t, 128>(dm, k_new, v_new, theta, k_loc, v_loc, row, pos, st)
+                           : append_t<uint16_t, 64>(dm, k_new, v_new, theta, k_loc, v_loc, row, pos, st);
+    return dm.d == 128 ? append_t<float, 128>(dm, k_new, v_new, theta, k_loc, v_loc, row, pos, st)
+                       : append_t<float, 64>(dm, k_new, v_new, theta, k_loc, v_loc, row, pos, st);
 }
 
 }  // namespace skv

@@ -52,6 +52,7 @@ int make_dims(const skv_config &c, Dims *dm, std::string *why) {
     if (c.top_k > 4096) return bad("top_k must be <= 4096");
     if (c.rank < 1 || c.rank > 256) return bad("rank must be in [1, 256]");
     if (!(c.rope_base > 0.f)) return bad("rope_base must be > 0");
+    if (c.max_new < 0 || c.max_new > (1 << 20)) return bad("max_new must be in [0, 2^20]");
     const long long nk = 1LL * c.n_outlier * c.chunk + 1LL * c.top_k * c.chunk + c.local_window;
     if (nk < 1) return bad("at least one key must be attended");
     const long long seq_elems = 1LL * c.batch * c.heads_kv * c.seq_len * c.head_dim;
@@ -62,9 +63,13 @@ int make_dims(const skv_config &c, Dims *dm, std::string *why) {
     if (1LL * n * c.head_dim * es >= (1LL << 30) || 1LL * n * (c.heads_q / c.heads_kv) * 4 >= (1LL << 30) ||
         1LL * c.seq_len * c.rank * es >= (1LL << 30))
         return bad("a per-row tensor would reach 1 GiB (sequence too long)");
+    if ((1LL * c.n_outlier * c.chunk + 1LL * c.top_k * c.chunk + c.local_window + c.max_new) * (c.heads_q / c.heads_kv) * 4 >=
+        (1LL << 30))
+        return bad("a per-row logit block would reach 1 GiB");
     Dims &d = *dm;
     d.b = c.batch; d.hq = c.heads_q; d.hkv = c.heads_kv; d.d = c.head_dim; d.s = c.seq_len; d.c = c.chunk;
     d.r = c.rank; d.o = c.n_outlier; d.k = c.top_k; d.w = c.local_window;
+    d.wcap = c.local_window + c.max_new;
     d.n = n; d.n_loc = n_loc; d.G = c.heads_q / c.heads_kv;
     d.GP = d.G <= 4 ? 4 : (d.G <= 8 ? 8 : 16);
     d.mask_words = (n + 31) / 32;
@@ -77,6 +82,15 @@ int make_dims(const skv_config &c, Dims *dm, std::string *why) {
     d.r_pad = round_up(c.rank, 32);
     d.scale = 1.0f / std::sqrt(static_cast<float>(c.head_dim));
     return SKV_OK;
+}
+
+// The sizes of a decode step whose local block holds `w_local` keys.
+Dims dims_with_local(const Dims &dm, int w_local) {
+    Dims d = dm;
+    d.w = w_local;
+    d.NK = d.OC + d.KC + w_local;
+    d.pv_tiles = (d.NK + skv::kPvTile - 1) / skv::kPvTile;
+    return d;
 }
 
 struct Mark {
@@ -180,6 +194,7 @@ struct skv_layer {
     hipEvent_t ev_sel = nullptr, ev_fetch = nullptr, ev_qk = nullptr;
     int fetch_waves = 128;
     int score_wgs = 0;  // workgroups of the scoring kernel (0: two tiles per wave)
+    int n_app = 0;      // decode tokens appended to the local block since the last prefill / load
     // timing
     bool overlap = false;  // fetch beside the key rebuild (true) or before it
     bool timing = false;
@@ -329,8 +344,8 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     ALLOC(min_cos, bh * dm.n * 4);
     ALLOC(k_out, bh * dm.OC * D * E);
     ALLOC(v_out, bh * dm.OC * D * E);
-    ALLOC(k_loc, bh * dm.w * D * E);
-    ALLOC(v_loc, bh * dm.w * D * E);
+    ALLOC(k_loc, bh * dm.wcap * D * E);
+    ALLOC(v_loc, bh * dm.wcap * D * E);
     ALLOC(vc, bh * dm.KC * D * E);
     ALLOC(slot_chunk, bh * dm.k * 4);
     ALLOC(sel, bh * dm.k * 4);
@@ -339,9 +354,12 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     ALLOC(S2, bh * dm.n * 4);
     ALLOC(misses, bh * dm.k * sizeof(int2));
     ALLOC(miss_count, bh * 4);
-    ALLOC(logits, B * HQ * dm.NK * 4);
-    ALLOC(part_ml, B * HQ * dm.pv_tiles * sizeof(float2));
-    ALLOC(part_acc, B * HQ * dm.pv_tiles * D * 4);
+    // logits and split partials sized for a full local block (window plus
+    // every appended token)
+    const Dims dfull = dims_with_local(dm, dm.wcap);
+    ALLOC(logits, B * HQ * dfull.NK * 4);
+    ALLOC(part_ml, B * HQ * dfull.pv_tiles * sizeof(float2));
+    ALLOC(part_acc, B * HQ * dfull.pv_tiles * D * 4);
     ALLOC(counters, 4 * sizeof(unsigned long long));
     ALLOC(bad, 4);
     ALLOC(theta, D / 2 * sizeof(double));
@@ -364,7 +382,9 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     }
     if (hipMemcpy(ly->theta, th.data(), th.size() * sizeof(double), hipMemcpyHostToDevice) != hipSuccess ||
         hipMemcpy(ly->theta_rev, thr.data(), thr.size() * sizeof(double), hipMemcpyHostToDevice) != hipSuccess ||
-        hipMemset(ly->counters, 0, 4 * sizeof(unsigned long long)) != hipSuccess)
+        hipMemset(ly->counters, 0, 4 * sizeof(unsigned long long)) != hipSuccess ||
+        (dm.wcap > 0 && (hipMemset(ly->k_loc, 0, bh * dm.wcap * D * E) != hipSuccess ||
+                         hipMemset(ly->v_loc, 0, bh * dm.wcap * D * E) != hipSuccess)))
         return bail(fail(SKV_E_HIP, "initialising layer tables failed"));
     DevStreams *ds = nullptr;
     if ((rc = device_streams(ly->device, &ds))) return bail(rc);
@@ -419,6 +439,7 @@ int shadowkv_prefill_meta(skv_layer *ly, const void *k_pre, const void *k_rope, 
     SKV_HIP(hipMemcpyAsync(v_host, v, static_cast<size_t>(dm.b) * dm.hkv * dm.s * dm.d * dm.esize,
                            hipMemcpyDeviceToHost, st));
     ly->v_host_dev = vdev;
+    ly->n_app = 0;
     ly->ready = true;
     return SKV_OK;
 }
@@ -449,12 +470,28 @@ int shadowkv_load_meta(skv_layer *ly, const void *landmarks, const int32_t *outl
     }
     SKV_HIP(hipMemcpyAsync(ly->L, landmarks, bh * dm.n * D * E, hipMemcpyDefault, st));
     if (dm.w > 0) {
-        SKV_HIP(hipMemcpyAsync(ly->k_loc, k_loc, bh * dm.w * D * E, hipMemcpyDefault, st));
-        SKV_HIP(hipMemcpyAsync(ly->v_loc, v_loc, bh * dm.w * D * E, hipMemcpyDefault, st));
+        // (b, h_kv, w, d) into the local buffers' rows of w + max_new
+        const size_t row = static_cast<size_t>(dm.w) * D * E, pitch = static_cast<size_t>(dm.wcap) * D * E;
+        SKV_HIP(hipMemcpy2DAsync(ly->k_loc, pitch, k_loc, row, row, bh, hipMemcpyDefault, st));
+        SKV_HIP(hipMemcpy2DAsync(ly->v_loc, pitch, v_loc, row, row, bh, hipMemcpyDefault, st));
     }
     if ((rc = install_common(ly, A, B, v_host, st))) return rc;
     ly->v_host_dev = vdev;
+    ly->n_app = 0;
     ly->ready = true;
+    return SKV_OK;
+}
+
+int shadowkv_append(skv_layer *ly, const void *k_new, const void *v_new, void *stream) {
+    if (!ly) return fail(SKV_E_INVAL, "layer is null");
+    if (!k_new || !v_new) return fail(SKV_E_INVAL, "null k_new or v_new");
+    if (!ly->ready) return fail(SKV_E_STATE, "append before prefill_meta / load_meta");
+    const Dims &dm = ly->dm;
+    if (ly->n_app >= dm.wcap - dm.w) return fail(SKV_E_SHAPE, "the local block is full (max_new tokens appended)");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    SKV_HIP(skv::launch_append(dm, k_new, v_new, ly->theta, ly->k_loc, ly->v_loc, dm.w + ly->n_app,
+                               dm.s + ly->n_app, st));
+    ++ly->n_app;
     return SKV_OK;
 }
 
@@ -463,7 +500,7 @@ int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) 
     if (!q || !out) return fail(SKV_E_INVAL, "null q or out");
     if (!ly->ready) return fail(SKV_E_STATE, "decode_step before prefill_meta / load_meta");
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const Dims &dm = ly->dm;
+    const Dims dm = dims_with_local(ly->dm, ly->dm.w + ly->n_app);
     {
         Timed t(ly, SKV_K_SCORE, st);
         SKV_HIP(skv::launch_score(dm, q, ly->L, ly->cand, ly->P, ly->stats, ly->score_wgs, st));
@@ -558,8 +595,8 @@ static const void *tensor_ptr(const skv_layer *ly, int which, size_t *bytes) {
         case SKV_T_CACHE_V: *bytes = bh * dm.KC * D * E; return ly->vc;
         case SKV_T_K_OUT: *bytes = bh * dm.OC * D * E; return ly->k_out;
         case SKV_T_V_OUT: *bytes = bh * dm.OC * D * E; return ly->v_out;
-        case SKV_T_K_LOC: *bytes = bh * dm.w * D * E; return ly->k_loc;
-        case SKV_T_V_LOC: *bytes = bh * dm.w * D * E; return ly->v_loc;
+        case SKV_T_K_LOC: *bytes = bh * dm.wcap * D * E; return ly->k_loc;
+        case SKV_T_V_LOC: *bytes = bh * dm.wcap * D * E; return ly->v_loc;
         default: *bytes = 0; return nullptr;
     }
 }

@@ -16,7 +16,9 @@ constexpr int kPvTile = 256;      // keys per PV workgroup
 constexpr int kMaxGroup = 16;     // query heads per KV head
 
 struct Dims {
-    int b, hq, hkv, d, s, c, r, o, k, w;
+    int b, hq, hkv, d, s, c, r, o, k;
+    int w;           // local keys attended: the window, plus the tokens appended so far
+    int wcap;        // rows of the local K/V buffers: window + append capacity
     int n;           // chunks per sequence
     int n_loc;       // chunks of the local window
     int G;           // query heads per KV head
@@ -24,7 +26,7 @@ struct Dims {
     int mask_words;  // ceil(n / 32)
     int score_tiles; // ceil(n / kScoreTile): scoring workgroups per row
     int wtiles;      // ceil(n / 64): 64-chunk softmax tiles per row
-    int OC, KC, NK;  // outlier keys, rebuilt keys, all keys per (b, h_kv)
+    int OC, KC, NK;  // outlier keys, rebuilt keys, all keys per (b, h_kv) (NK with w)
     int pv_tiles;    // ceil(NK / kPvTile)
     int esize;       // bytes per stored element
     int bf16;        // storage type
@@ -45,6 +47,10 @@ hipError_t launch_cand_mask(const Dims &dm, const int32_t *outliers, uint32_t *c
 hipError_t launch_transpose_b(const Dims &dm, const void *B, void *Bt, hipStream_t st);
 hipError_t launch_fill_i32(int32_t *p, int32_t value, size_t count, hipStream_t st);
 hipError_t launch_validate_outliers(const Dims &dm, const int32_t *outliers, int32_t *bad, hipStream_t st);
+// Decode-token append: rotate the new key (pre-RoPE, (b, h_kv, d)) at `pos`
+// and write it and its value to row `row` of the local buffers.
+hipError_t launch_append(const Dims &dm, const void *k_new, const void *v_new, const double *theta, void *k_loc,
+                         void *v_loc, int row, int pos, hipStream_t st);
 
 // Decode.
 // score_wgs: workgroups of the persistent bfloat16 scoring kernel (0: two

@@ -258,3 +258,57 @@ def test_overlap_schedule_is_identical():
     for lay, hb in ((serial, hb1), (overlap, hb2)):
         lay.close()
         hb.free()
+
+
+@pytest.mark.parametrize("case", ["fp32", "bf16"])
+def test_append_decode_tokens_matches_oracle(case):
+    """Decode-token append: after the prefill, every step decodes and then
+    appends the token it generated (pre-RoPE key at position s + t, value).
+    The appended keys must equal the oracle's (rotated at s + t, rounded once)
+    to one unit in the last place, every later step's output must match the
+    oracle's attention over the grown local block, and an append past
+    max_new must be refused."""
+    if case == "fp32":
+        wl = T.with_(b=2, s=2048, d=128, r=48, o=4, k=9, w=32, steps=5, rho=0.9)
+    else:
+        wl = synth.LLAMA_32K.with_(b=2, s=8192, k=16, steps=5, rho=0.9)
+    max_new = wl.steps - 1
+    log(f"[append-{case}] b={wl.b} s={wl.s} w={wl.w} max_new={max_new} steps={wl.steps}")
+    shape = oracle_shape(wl)
+    k_pre, v, qs = synth.k_pre_numpy(wl), synth.v_numpy(wl), synth.queries_numpy(wl)
+    rng = np.random.default_rng([wl.wid, 77])
+    new_k = oracle.round_store(rng.standard_normal((max_new, wl.b, wl.h_kv, wl.d)), wl.bf16)
+    new_v = oracle.round_store(rng.standard_normal((max_new, wl.b, wl.h_kv, wl.d)), wl.bf16)
+    meta = oracle.prefill(shape, k_pre, v)
+    A_o, B_o = oracle.svd_factors(shape, k_pre)
+    dt = tdtype(wl)
+    k_pre_d, v_d = to_dev(k_pre, dt), to_dev(v, dt)
+    A_d, B_d = svd_factors(k_pre_d, wl.r)
+    layer = skv.Layer(**layer_kwargs(wl), max_new=max_new)
+    hb = layer.host_buffer()
+    layer.prefill_meta(k_pre_d, v_d, A_d, B_d, hb)
+    for t in range(wl.steps):
+        q_d = to_dev(qs[t], dt)
+        out_d = torch.empty_like(q_d)
+        layer.decode_step(q_d, out_d)
+        torch.cuda.synchronize()
+        res = oracle.decode(shape, qs[t], meta, A_o, B_o, v)
+        sel_g = to_np(layer.read(skv.SKV_T_SELECTION))
+        exact = check_selection(sel_g, res["sel"], res["S2"], meta["cand"])
+        ref = res["out"] if exact else oracle.attend(shape, qs[t], sel_g, A_o, B_o, v, meta)
+        err = float(np.max(np.abs(to_np(out_d) - ref)))
+        log(f"[append-{case}] step {t} ({t} appended): max|out - oracle| = {err:.3g}")
+        assert err <= OUT_TOL[wl.bf16], f"step {t}: max abs error {err}"
+        if t < max_new:
+            layer.append(to_dev(new_k[t], dt), to_dev(new_v[t], dt))
+            meta = oracle.append(shape, meta, new_k[t], new_v[t])
+            torch.cuda.synchronize()
+            kl = to_np(layer.read(skv.SKV_T_K_LOC))[:, :, :wl.w + t + 1]
+            ulp = bf16_ulp(meta["k_loc"]) if wl.bf16 else np.abs(np.spacing(meta["k_loc"].astype(np.float32)))
+            assert np.all(np.abs(kl - meta["k_loc"]) <= ulp), "appended keys differ by more than one ulp"
+            np.testing.assert_array_equal(to_np(layer.read(skv.SKV_T_V_LOC))[:, :, :wl.w + t + 1], meta["v_loc"])
+    with pytest.raises(skv.ShadowKVError) as e:
+        layer.append(to_dev(new_k[0], dt), to_dev(new_v[0], dt))
+    assert e.value.code == skv.SKV_E_SHAPE
+    layer.close()
+    hb.free()
