@@ -150,6 +150,8 @@ def main() -> int:
     ap.add_argument("--append", action="store_true",
                     help="generation loop: each layer-step also appends the generated token to the local block "
                          "(no oracle baseline in this mode)")
+    ap.add_argument("--host-eigh", action="store_true",
+                    help="setup: solve the factors' eigenproblems on the host instead of the device")
     ap.add_argument("--sweep", action="store_true",
                     help="run chunk-size / budget / rank variants of the workload, one JSON line each")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -218,16 +220,25 @@ def main() -> int:
         keep = {}  # inputs of the spot-checked layer, for the oracle
         new_kv = []  # decode-token append: (keys, values) per layer
         spot_layer = layers - 1
+        prefill_ms = {"svd_factors": 0.0, "prefill_meta": 0.0}
         for l in range(layers):
             k_pre = synth.k_pre_torch(wl, l, dev)
             v = synth.v_torch(wl, l, dev)
-            A, B = svd_factors(k_pre, wl.r)
+            torch.cuda.synchronize()
+            ts = time.perf_counter()
+            A, B = svd_factors(k_pre, wl.r, host_eigh=args.host_eigh)
+            torch.cuda.synchronize()
+            prefill_ms["svd_factors"] += (time.perf_counter() - ts) * 1e3
             lay = skv.Layer(batch=wl.b, heads_q=wl.h_q, heads_kv=wl.h_kv, head_dim=wl.d, seq_len=wl.s, chunk=wl.c,
                             rank=wl.r, n_outlier=wl.o, top_k=wl.k, local_window=wl.w, rope_base=wl.rope_base,
                             bf16=wl.bf16, max_new=(nq + args.steps) if args.append else 0)
             if l < n_host:
                 host_bufs.append(lay.host_buffer())
+            torch.cuda.synchronize()
+            ts = time.perf_counter()
             lay.prefill_meta(k_pre, v, A, B, host_bufs[l % n_host])
+            torch.cuda.synchronize()
+            prefill_ms["prefill_meta"] += (time.perf_counter() - ts) * 1e3
             qs.append(synth.queries_torch(wl, l, dev, steps=nq))
             if args.append:
                 # the generated tokens' pre-RoPE keys and values, one per step
@@ -403,6 +414,7 @@ def main() -> int:
             "cpu_baseline": cpu_baseline,
             "parity_spot_check": parity,
             "setup_s": round(time.time() - t0, 1),
+            "prefill_ms_per_layer": {k: round(v / layers, 2) for k, v in prefill_ms.items()},
         }
         for lay in Ls:
             lay.close()

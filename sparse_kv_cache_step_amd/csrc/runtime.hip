@@ -431,13 +431,20 @@ int shadowkv_prefill_meta(skv_layer *ly, const void *k_pre, const void *k_rope, 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const Dims &dm = ly->dm;
     ly->ready = false;
+    // Step 5's V offload (a DMA copy over PCIe, tens of milliseconds at long
+    // context) runs on the layer's copy stream beside steps 2-4's kernels,
+    // which need only HBM; the caller's stream waits for it at the end.
+    SKV_HIP(hipEventRecord(ly->ev_sel, st));
+    SKV_HIP(hipStreamWaitEvent(ly->copy, ly->ev_sel, 0));
+    SKV_HIP(hipMemcpyAsync(v_host, v, static_cast<size_t>(dm.b) * dm.hkv * dm.s * dm.d * dm.esize,
+                           hipMemcpyDeviceToHost, ly->copy));
+    SKV_HIP(hipEventRecord(ly->ev_fetch, ly->copy));
     SKV_HIP(skv::launch_landmarks(dm, k_pre, k_rope, ly->theta, ly->L, ly->min_cos, st));
     SKV_HIP(skv::launch_topo(dm, ly->min_cos, ly->outliers, ly->keys, ly->topo_keys_in_lds, st));
     SKV_HIP(skv::launch_gather_static(dm, k_pre, k_rope, v, ly->outliers, ly->theta, ly->k_out, ly->v_out,
                                       ly->k_loc, ly->v_loc, st));
     if ((rc = install_common(ly, A, B, v_host, st))) return rc;
-    SKV_HIP(hipMemcpyAsync(v_host, v, static_cast<size_t>(dm.b) * dm.hkv * dm.s * dm.d * dm.esize,
-                           hipMemcpyDeviceToHost, st));
+    SKV_HIP(hipStreamWaitEvent(st, ly->ev_fetch, 0));
     ly->v_host_dev = vdev;
     ly->n_app = 0;
     ly->ready = true;

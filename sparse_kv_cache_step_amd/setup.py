@@ -7,14 +7,15 @@ Per sequence the keys form the s x (h_kv*d) matrix M whose column h*d+i is
 head h's dimension i.  Its rank-r truncated SVD M ~ U_r S_r V_r^T gives
 A = U_r S_r = M V_r and B = V_r^T split by head.  V_r is taken from the
 eigenvectors of the Gram matrix M^T M (double precision; the Gram product
-runs on M's device, the (h_kv*d)^2 eigenproblem on the host), which gives
-the same subspace as the SVD.  This is setup, not part of the decode step:
-its results are inputs of shadowkv_prefill_meta.
+and the (h_kv*d)^2 eigenproblems run on M's device, or the eigenproblems on
+the host with host_eigh=True), which gives the same subspace as the SVD.
+This is setup, not part of the decode step: its results are inputs of
+shadowkv_prefill_meta.
 """
 from __future__ import annotations
 
 
-def svd_factors(k_pre, rank: int, dtype=None, batch_eigh: int = 8):
+def svd_factors(k_pre, rank: int, dtype=None, batch_eigh: int = 8, host_eigh: bool = False):
     """k_pre: (b, h_kv, s, d) tensor (any float dtype, any device).
     Returns (A (b, s, r), B (b, h_kv, r, d)) on k_pre's device in `dtype`
     (default: k_pre's dtype)."""
@@ -32,7 +33,8 @@ def svd_factors(k_pre, rank: int, dtype=None, batch_eigh: int = 8):
         grams = []
         for bi in seqs:
             M = k_pre[bi].transpose(0, 1).reshape(s, hd).to(torch.float64)
-            grams.append(torch.mm(M.t().contiguous(), M).cpu())
+            gram = torch.mm(M.t().contiguous(), M)
+            grams.append(gram.cpu() if host_eigh else gram)
             del M
         _, vecs = torch.linalg.eigh(torch.stack(grams))  # ascending eigenvalues
         for i, bi in enumerate(seqs):
