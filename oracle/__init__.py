@@ -272,6 +272,60 @@ def decode(shape: Shape, q, meta: dict, A, B, v_host) -> dict:
     return res
 
 
+# --------------------------------------------------------------------------
+# SnapKV-style selection (the SnapKV review page, 核心公式: importance =
+# attention summed over the heads and the observation window's queries, then
+# average pooling, then Top-K), at chunk level against the landmarks: the
+# selection is made once from a window of queries and then kept.
+# --------------------------------------------------------------------------
+def snapkv_scores(shape: Shape, q_obs, meta: dict) -> np.ndarray:
+    """(b, h_kv, n): for each KV head, the softmax over selectable chunks of
+    q . L^T / sqrt(d), summed over the group's query heads and the window's
+    queries (0 elsewhere).  q_obs: (b, h_q, w_obs, d) post-RoPE."""
+    q_obs = _f64(q_obs)
+    b, hq, w_obs, d = q_obs.shape
+    assert (b, hq, d) == (shape.b, shape.h_q, shape.d)
+    # each (query head, window position) pair as a query head of its group:
+    # the decode step's group score of these heads is their mean softmax
+    virt = Shape(b=shape.b, h_q=hq * w_obs, h_kv=shape.h_kv, d=d, s=shape.s, c=shape.c, r=shape.r, o=shape.o,
+                 k=shape.k, w=shape.w, rope_base=shape.rope_base, bf16=shape.bf16)
+    q = q_obs.reshape(b, hq * w_obs, d)
+    res = dict(P=np.empty((b, hq * w_obs, shape.n)), S2=np.empty((b, shape.h_kv, shape.n)),
+               sel=np.empty((b, shape.h_kv, shape.k), dtype=np.int32), out=np.empty((b, hq * w_obs, d)))
+    m = {key: _f64(meta[key]) for key in ("landmarks", "k_out", "v_out", "k_loc", "v_loc")}
+    cand = np.ascontiguousarray(meta["cand"], dtype=np.uint8)
+    zero_a = np.zeros((b, shape.s, shape.r))
+    zero_b = np.zeros((b, shape.h_kv, shape.r, d))
+    zero_v = np.zeros((b, shape.h_kv, shape.s, d))
+    cfg = virt._c(_n_app(shape, meta))
+    rc = _lib().orc_decode(ctypes.byref(cfg), _p(q, _D), _p(m["landmarks"], _D), _p(cand, _U8),
+                           _p(zero_a, _D), _p(zero_b, _D), _p(zero_v, _D), _p(m["k_out"], _D),
+                           _p(m["v_out"], _D), _p(m["k_loc"], _D), _p(m["v_loc"], _D),
+                           _p(res["P"], _D), _p(res["S2"], _D), _p(res["sel"], _I32), _p(res["out"], _D))
+    _check(rc, "snapkv scores")
+    return res["S2"] * (hq // shape.h_kv) * w_obs
+
+
+def snapkv_select(shape: Shape, q_obs, meta: dict, pool: int) -> dict:
+    """The importance of snapkv_scores, average-pooled over `pool` (odd)
+    neighbouring chunks (zero padding, divided by `pool`), then the k
+    selectable chunks of largest pooled importance (ties to the lower index,
+    decided on binary32 values like the decode step), ascending."""
+    assert pool >= 1 and pool % 2 == 1
+    S = snapkv_scores(shape, q_obs, meta)
+    half = pool // 2
+    pad = np.pad(S, ((0, 0), (0, 0), (half, half)))
+    pooled = sum(pad[:, :, i:i + shape.n] for i in range(pool)) / pool
+    cand = meta["cand"].astype(bool)
+    pooled = np.where(cand, pooled, 0.0)
+    sel = np.empty((shape.b, shape.h_kv, shape.k), dtype=np.int32)
+    for bi in range(shape.b):
+        for h in range(shape.h_kv):
+            key = pooled[bi, h].astype(np.float32).astype(np.float64)
+            sel[bi, h] = topk(key, shape.k, cand[bi, h])
+    return dict(S=S, pooled=pooled, sel=sel)
+
+
 class CacheSim:
     """Per-layer resident set of the set-difference cache: R_t = I_t, and
     step t loads only I_t \\ R_{t-1}."""

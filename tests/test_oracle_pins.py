@@ -466,3 +466,63 @@ def test_cache_simulation_counts_set_intersections():
         prev = sel
     sim.reset()
     assert sim.step(prev) == (0, 2 * 3 * 7)
+
+
+# ---------------------------------------------------------------------------
+# SnapKV-style selection (SnapKV review page, 核心公式 and 池化策略)
+# ---------------------------------------------------------------------------
+def test_snapkv_one_query_without_pooling_is_the_decode_selection():
+    """A window of one query and pooling 1: the summed importance is G times
+    the decode step's group score (G a power of two, so exactly), and the
+    selection must be the decode step's."""
+    rng = np.random.default_rng(31)
+    shape = tiny_shape(b=2, s=128, k=5)
+    K = rng.standard_normal((2, 2, 128, 8))
+    V = rng.standard_normal((2, 2, 128, 8))
+    meta = oracle.prefill(shape, K, V)
+    A, B = oracle.svd_factors(shape, K)
+    q = rng.standard_normal((2, 4, 8))
+    dec = oracle.decode(shape, q, meta, A, B, V)
+    snap = oracle.snapkv_select(shape, q[:, :, None, :], meta, pool=1)
+    np.testing.assert_array_equal(snap["sel"], dec["sel"])
+    np.testing.assert_allclose(snap["S"], dec["S2"] * 2, rtol=1e-15, atol=0)
+
+
+def test_snapkv_importance_is_summed_attention_and_pooling_spreads_it():
+    """The importance is attention summed over the group's heads and the
+    window's queries: each (head, query) softmax sums to one over the
+    selectable chunks, so a KV head's importance sums to G * w_obs, and a
+    window repeated twice doubles it without changing the selection.  With
+    one landmark aligned with every query, the pooled importance of that
+    chunk's neighbours rises to a third of its peak (pool 3), so the top-3 is
+    the chunk and its two neighbours; at the first chunk the zero padding
+    leaves its only neighbour and the next-largest chunk."""
+    rng = np.random.default_rng(32)
+    shape = tiny_shape(b=1, s=128, k=3, o=0)
+    K = rng.standard_normal((1, 2, 128, 8)) * 0.05
+    V = rng.standard_normal((1, 2, 128, 8))
+    meta = oracle.prefill(shape, K, V)
+    q = rng.standard_normal((1, 4, 3, 8))
+    S = oracle.snapkv_scores(shape, q, meta)
+    np.testing.assert_allclose(S.sum(axis=-1), 2 * 3, rtol=1e-12)
+    r1 = oracle.snapkv_select(shape, q, meta, pool=3)
+    r2 = oracle.snapkv_select(shape, np.concatenate([q, q], axis=2), meta, pool=3)
+    np.testing.assert_allclose(r2["S"], 2 * r1["S"], rtol=1e-12)
+    np.testing.assert_array_equal(r1["sel"], r2["sel"])
+    # plant: chunk j's landmark points along every query of the group
+    for j in (9, 0):
+        m = dict(meta)
+        L = m["landmarks"].copy()
+        qdir = rng.standard_normal(8)
+        L[0, :, j] = qdir * 40.0
+        m["landmarks"] = L
+        qq = np.broadcast_to(qdir, (1, 4, 2, 8)).copy()
+        r = oracle.snapkv_select(shape, qq, m, pool=3)
+        for h in range(2):
+            assert r["S"][0, h, j] > 2 * 2 * 0.999  # nearly all of G * w_obs = 4
+            if j > 0:
+                assert list(r["sel"][0, h]) == [j - 1, j, j + 1]
+            else:
+                assert {0, 1} <= set(r["sel"][0, h])
+        r_nopool = oracle.snapkv_select(shape, qq, m, pool=1)
+        assert all(j in r_nopool["sel"][0, h] for h in range(2))
