@@ -150,6 +150,10 @@ def main() -> int:
     ap.add_argument("--append", action="store_true",
                     help="generation loop: each layer-step also appends the generated token to the local block "
                          "(no oracle baseline in this mode)")
+    ap.add_argument("--snapkv", default=None, metavar="W,POOL",
+                    help="SnapKV-style fixed selection: after the prefill each layer selects once from a window "
+                         "of W queries with average pooling over POOL chunks; the timed steps keep that "
+                         "selection (no oracle baseline in this mode)")
     ap.add_argument("--host-eigh", action="store_true",
                     help="setup: solve the factors' eigenproblems on the host instead of the device")
     ap.add_argument("--sweep", action="store_true",
@@ -181,6 +185,10 @@ def main() -> int:
         __graft_entry__.build()
 
     base = synth.WORKLOADS[args.workload]
+    snap = None
+    if args.snapkv:
+        w_obs, pool = (int(x) for x in args.snapkv.split(","))
+        snap = (w_obs, pool)
 
     def variant(wl, chunk=None, top_k=None, rank=None, outliers=None):
         """The workload with another chunk size (top-k and outlier chunks
@@ -219,6 +227,7 @@ def main() -> int:
         Ls, qs = [], []
         keep = {}  # inputs of the spot-checked layer, for the oracle
         new_kv = []  # decode-token append: (keys, values) per layer
+        q_obs = []  # SnapKV-style selection: each layer's window queries
         spot_layer = layers - 1
         prefill_ms = {"svd_factors": 0.0, "prefill_meta": 0.0}
         for l in range(layers):
@@ -239,7 +248,14 @@ def main() -> int:
             lay.prefill_meta(k_pre, v, A, B, host_bufs[l % n_host])
             torch.cuda.synchronize()
             prefill_ms["prefill_meta"] += (time.perf_counter() - ts) * 1e3
-            qs.append(synth.queries_torch(wl, l, dev, steps=nq))
+            if snap:
+                # the observation window's queries come before the decoded ones
+                q_all = synth.queries_torch(wl, l, dev, steps=snap[0] + nq)
+                q_obs.append(q_all[:snap[0]].permute(1, 2, 0, 3).contiguous())
+                qs.append(q_all[snap[0]:].contiguous())
+                del q_all
+            else:
+                qs.append(synth.queries_torch(wl, l, dev, steps=nq))
             if args.append:
                 # the generated tokens' pre-RoPE keys and values, one per step
                 g = torch.Generator(device=dev)
@@ -247,7 +263,7 @@ def main() -> int:
                 new_kv.append((torch.randn((nq, wl.b, wl.h_kv, wl.d), generator=g, device=dev).to(dt),
                                torch.randn((nq, wl.b, wl.h_kv, wl.d), generator=g, device=dev).to(dt)))
             torch.cuda.synchronize()
-            if l == spot_layer and not args.no_cpu_baseline and not args.append:
+            if l == spot_layer and not args.no_cpu_baseline and not args.append and not snap:
                 sample = [0, wl.b // 2] if wl.b > 1 else [0]
                 keep = {"seqs": sample, "k_pre": k_pre[sample].float().cpu(), "v": v[sample].float().cpu()}
             del k_pre, v, A, B
@@ -272,6 +288,20 @@ def main() -> int:
             dst.copy_(src)
             torch.cuda.synchronize()
             del src, dst
+
+        snap_us = None
+        if snap:
+            # one selection per layer (timed on its own), then decode with it
+            torch.cuda.synchronize()
+            s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s0.record(stream)
+            for l in range(layers):
+                Ls[l].snapkv_select(q_obs[l], snap[1], stream)
+            s1.record(stream)
+            torch.cuda.synchronize()
+            snap_us = s0.elapsed_time(s1) * 1e3 / layers
+            log(f"snapkv selection: {snap_us:.1f} us per layer (w_obs={snap[0]}, pool={snap[1]})")
+            del q_obs[:]
 
         # ---- warmup ---------------------------------------------------------------
         run_steps(0, args.warmup)
@@ -315,6 +345,8 @@ def main() -> int:
 
         layer_steps = args.steps * layers
         ab = algorithmic_bytes(wl)
+        if snap:
+            del ab["landmarks"]  # a fixed selection reads no landmarks
         alg_total = sum(ab.values())
         t_ls = elapsed / layer_steps
         dense_kv = 2 * wl.b * wl.h_kv * wl.s * wl.d * (2 if wl.bf16 else 4)
@@ -322,24 +354,35 @@ def main() -> int:
         roofline = None
         kernels = {}
         if kern_steps:
-            score_bytes = ab["landmarks"] + ab["q"]
+            score_bytes = ab.get("landmarks", 0) + ab["q"]
             qk_bytes = ab["a_rows"] + ab["b_factor"] + ab["outlier_kv"] // 2 + ab["local_kv"] // 2 + ab["q"]
             pv_bytes = ab["selected_v"] + ab["outlier_kv"] // 2 + ab["local_kv"] // 2 + ab["out"]
             fetch_bytes = h2d_bytes / max(1, layer_steps)
             for name, nbytes, peak in (("score", score_bytes, PEAK_HBM), ("qk", qk_bytes, PEAK_HBM),
                                        ("pv", pv_bytes, PEAK_HBM), ("fetch", fetch_bytes, PEAK_PCIE)):
                 us = per_launch_us[name]
+                if not us:
+                    continue  # not run in this mode (a fixed selection scores and fetches nothing)
                 gbs = nbytes / (us * 1e-6) / 1e9 if us else None
                 kernels[name] = {"us_per_launch": round(us, 3), "bytes_per_launch": int(nbytes),
                                  "GBps": round(gbs, 1) if gbs else None, "peak_GBps": peak / 1e9,
                                  "frac": round(gbs * 1e9 / peak, 4) if gbs else None}
-            kernels["select"] = {"us_per_launch": round(per_launch_us["select"], 3)}
-            sc = kernels["score"]
-            traffic = measured_traffic(wl.name)
-            roofline = {"kernel": "score_mfma_kernel (landmark scoring)", "bound": "hbm",
-                        "achieved": sc["GBps"], "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": sc["frac"],
-                        "traffic": traffic, "bytes_per_launch": sc["bytes_per_launch"],
-                        "us_per_launch": sc["us_per_launch"]}
+            if per_launch_us["select"]:
+                kernels["select"] = {"us_per_launch": round(per_launch_us["select"], 3)}
+            if snap:
+                # a fixed selection runs no scoring: the key rebuild dominates
+                sc = kernels["qk"]
+                roofline = {"kernel": "qk_sparse_mfma_kernel + qk_static_kernel (key rebuild, logits)",
+                            "bound": "hbm", "achieved": sc["GBps"], "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                            "frac": sc["frac"], "traffic": None, "bytes_per_launch": sc["bytes_per_launch"],
+                            "us_per_launch": sc["us_per_launch"]}
+            else:
+                sc = kernels["score"]
+                traffic = measured_traffic(wl.name)
+                roofline = {"kernel": "score_mfma_kernel (landmark scoring)", "bound": "hbm",
+                            "achieved": sc["GBps"], "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": sc["frac"],
+                            "traffic": traffic, "bytes_per_launch": sc["bytes_per_launch"],
+                            "us_per_launch": sc["us_per_launch"]}
 
         fetch_gbs = kernels.get("fetch", {}).get("GBps") if kernels else None
         closed_form = None
@@ -402,11 +445,12 @@ def main() -> int:
             "config": {"workload": wl.name, "batch": wl.b, "seq_len": wl.s, "heads_q": wl.h_q, "heads_kv": wl.h_kv,
                        "head_dim": wl.d, "chunk": wl.c, "rank": wl.r, "outlier_chunks": wl.o, "top_k": wl.k,
                        "local_window": wl.w, "layers": layers, "host_v_buffers": n_host,
-                       **({"append": True} if args.append else {})},
+                       **({"append": True} if args.append else {}),
+                       **({"snapkv": {"w_obs": snap[0], "pool": snap[1]}} if snap else {})},
             "us_per_layer_step": round(t_ls * 1e6, 3),
             "effective_TBps": round(alg_total / t_ls / 1e12, 4),
             "equivalent_TBps": round(dense_kv / t_ls / 1e12, 4),
-            "alpha": round(alpha, 4),
+            "alpha": None if snap else round(alpha, 4),
             "h2d_GB": round(h2d_bytes / 1e9, 4),
             "closed_form_equiv_TBps": round(closed_form, 3) if closed_form else None,
             "roofline": roofline,
@@ -416,6 +460,8 @@ def main() -> int:
             "setup_s": round(time.time() - t0, 1),
             "prefill_ms_per_layer": {k: round(v / layers, 2) for k, v in prefill_ms.items()},
         }
+        if snap:
+            line["snapkv_select_us_per_layer"] = round(snap_us, 2)
         for lay in Ls:
             lay.close()
         for hb in host_bufs:

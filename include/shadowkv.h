@@ -161,6 +161,27 @@ int shadowkv_load_meta(skv_layer *layer, const void *landmarks, const int32_t *o
 int shadowkv_append(skv_layer *layer, const void *k_new, const void *v_new, void *stream);
 
 /*
+ * SnapKV-style fixed selection (the SnapKV review page, section on the core
+ * formulas: importance S_i as attention summed over heads and queries, then
+ * TopK, the compressed cache, and average pooling of the scores).  Taken at
+ * the chunk granularity of this layer: each query of an observation window
+ * scores the selectable chunks by softmax(q . L^T / sqrt(d)); S sums those
+ * probabilities over the KV group's query heads and the window's queries; S
+ * is average-pooled over `pool` neighbouring chunks (zero padding, divided
+ * by `pool`); the k selectable chunks of largest pooled S (ties to the lower
+ * index) become the layer's selection and stay fixed: later decode steps
+ * skip scoring and selection, the first of them fetches the V of the chunks
+ * not yet resident, and the rest fetch nothing.  prefill_meta, load_meta and
+ * reset_cache return the layer to per-step selection.
+ *   q_obs  device (b, h_q, w_obs, d)  post-RoPE queries of the window.
+ *   w_obs  1 ..= 4096 window queries; pool odd, 1 ..= 63.
+ * Enqueued on `stream`.  SKV_E_STATE before prefill_meta / load_meta;
+ * SKV_E_SHAPE for top_k = 0, a bad w_obs or pool, or q_obs of 1 GiB or more.
+ * The hit / miss counters count the selection as one step.
+ */
+int shadowkv_snapkv_select(skv_layer *layer, const void *q_obs, int w_obs, int pool, void *stream);
+
+/*
  * Algorithm 2 (Decoding): one step of one layer for all b sequences.
  *   q    device (b, h_q, d)  post-RoPE queries.
  *   out  device (b, h_q, d)  attention output.

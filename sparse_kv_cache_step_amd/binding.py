@@ -26,7 +26,7 @@ SKV_K_COUNT = len(KERNELS)
 
 EXPORTS = (
     "shadowkv_layer_create", "shadowkv_layer_destroy", "shadowkv_prefill_meta", "shadowkv_load_meta",
-    "shadowkv_append", "shadowkv_decode_step", "shadowkv_reset_cache", "shadowkv_get_stats", "shadowkv_reset_stats",
+    "shadowkv_append", "shadowkv_snapkv_select", "shadowkv_decode_step", "shadowkv_reset_cache", "shadowkv_get_stats", "shadowkv_reset_stats",
     "shadowkv_tensor_bytes", "shadowkv_read", "shadowkv_set_overlap", "shadowkv_set_timing",
     "shadowkv_get_timing",
     "shadowkv_host_alloc", "shadowkv_host_free", "shadowkv_last_error", "shadowkv_equiv_bandwidth",
@@ -69,6 +69,7 @@ def lib() -> ctypes.CDLL:
             "shadowkv_prefill_meta": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _VP]),
             "shadowkv_load_meta": (ctypes.c_int, [_VP] * 11),
             "shadowkv_append": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
+            "shadowkv_snapkv_select": (ctypes.c_int, [_VP, _VP, ctypes.c_int, ctypes.c_int, _VP]),
             "shadowkv_decode_step": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
             "shadowkv_reset_cache": (ctypes.c_int, [_VP, _VP]),
             "shadowkv_get_stats": (ctypes.c_int, [_VP, ctypes.POINTER(skv_stats)]),
@@ -126,6 +127,10 @@ def shadowkv_load_meta(h, landmarks, outliers, k_out, v_out, k_loc, v_loc, A, B,
 
 def shadowkv_append(h, k_new, v_new, stream) -> None:
     _check(lib().shadowkv_append(h, k_new, v_new, stream))
+
+
+def shadowkv_snapkv_select(h, q_obs, w_obs, pool, stream) -> None:
+    _check(lib().shadowkv_snapkv_select(h, q_obs, int(w_obs), int(pool), stream))
 
 
 def shadowkv_decode_step(h, q, out, stream) -> None:
@@ -248,15 +253,16 @@ class Layer:
             "k_new": (b, hkv, d), "v_new": (b, hkv, d),
         }[name]
 
-    def _dev(self, name, t, dtype=None, optional=False):
+    def _dev(self, name, t, dtype=None, optional=False, shape=None):
         torch = _torch()
         if t is None:
             if optional:
                 return None
             raise ValueError(f"{name} is required")
         dtype = self.dtype if dtype is None else dtype
-        if tuple(t.shape) != self._shape(name):
-            raise ValueError(f"{name}: shape {tuple(t.shape)} != {self._shape(name)}")
+        shape = self._shape(name) if shape is None else shape
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name}: shape {tuple(t.shape)} != {shape}")
         if t.dtype != dtype:
             raise ValueError(f"{name}: dtype {t.dtype} != {dtype}")
         if t.device != self.device:
@@ -294,6 +300,16 @@ class Layer:
 
     def append(self, k_new, v_new, stream=None):
         shadowkv_append(self.h, self._dev("k_new", k_new), self._dev("v_new", v_new), _stream_ptr(stream))
+
+    def snapkv_select(self, q_obs, pool: int, stream=None):
+        """q_obs: (b, h_q, w_obs, d) post-RoPE window queries."""
+        c = self.cfg
+        if q_obs is None or q_obs.dim() != 4 or tuple(q_obs.shape[:2]) != (c.batch, c.heads_q) \
+                or q_obs.shape[3] != c.head_dim:
+            raise ValueError(f"q_obs: shape must be ({c.batch}, {c.heads_q}, w_obs, {c.head_dim})")
+        w_obs = int(q_obs.shape[2])
+        shadowkv_snapkv_select(self.h, self._dev("q_obs", q_obs, shape=tuple(q_obs.shape)), w_obs, pool,
+                               _stream_ptr(stream))
 
     def decode_step(self, q, out, stream=None):
         shadowkv_decode_step(self.h, self._dev("q", q), self._dev("out", out), _stream_ptr(stream))

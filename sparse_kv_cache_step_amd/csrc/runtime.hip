@@ -195,6 +195,10 @@ struct skv_layer {
     int fetch_waves = 128;
     int score_wgs = 0;  // workgroups of the scoring kernel (0: two tiles per wave)
     int n_app = 0;      // decode tokens appended to the local block since the last prefill / load
+    // SnapKV-style fixed selection: decode steps keep the selection (no
+    // scoring or selection); the missing V is fetched by the first of them
+    bool fixed = false, fetch_pending = false;
+    float *snap_acc = nullptr;  // (b, h_kv, n) summed attention of the observation window
     // timing
     bool overlap = false;  // fetch beside the key rebuild (true) or before it
     bool timing = false;
@@ -349,8 +353,11 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     ALLOC(vc, bh * dm.KC * D * E);
     ALLOC(slot_chunk, bh * dm.k * 4);
     ALLOC(sel, bh * dm.k * 4);
-    ALLOC(P, B * HQ * dm.n * 4);
-    ALLOC(stats, B * HQ * dm.wtiles * sizeof(float2));
+    // U and the tile statistics hold up to kMaxGroup scored rows per KV head
+    // (the SnapKV-style selection scores (head, window position) rows)
+    ALLOC(P, bh * skv::kMaxGroup * dm.n * 4);
+    ALLOC(stats, bh * skv::kMaxGroup * dm.wtiles * sizeof(float2));
+    ALLOC(snap_acc, bh * dm.n * 4);
     ALLOC(S2, bh * dm.n * 4);
     ALLOC(misses, bh * dm.k * sizeof(int2));
     ALLOC(miss_count, bh * 4);
@@ -417,6 +424,7 @@ static int install_common(skv_layer *ly, const void *A, const void *B, void *v_h
     SKV_HIP(skv::launch_transpose_b(dm, B, ly->Bt, st));
     SKV_HIP(skv::launch_cand_mask(dm, ly->outliers, ly->cand, st));
     SKV_HIP(skv::launch_fill_i32(ly->slot_chunk, -1, static_cast<size_t>(dm.b) * dm.hkv * dm.k, st));
+    ly->fixed = ly->fetch_pending = false;
     (void)v_host;
     return SKV_OK;
 }
@@ -502,21 +510,58 @@ int shadowkv_append(skv_layer *ly, const void *k_new, const void *v_new, void *s
     return SKV_OK;
 }
 
+int shadowkv_snapkv_select(skv_layer *ly, const void *q_obs, int w_obs, int pool, void *stream) {
+    if (!ly) return fail(SKV_E_INVAL, "layer is null");
+    if (!q_obs) return fail(SKV_E_INVAL, "null q_obs");
+    if (!ly->ready) return fail(SKV_E_STATE, "snapkv_select before prefill_meta / load_meta");
+    if (w_obs < 1 || w_obs > 4096) return fail(SKV_E_SHAPE, "w_obs must be in [1, 4096]");
+    if (pool < 1 || pool > 63 || pool % 2 == 0) return fail(SKV_E_SHAPE, "pool must be odd, in [1, 63]");
+    const Dims &dm = ly->dm;
+    if (dm.k <= 0) return fail(SKV_E_SHAPE, "top_k is 0: there is nothing to select");
+    if (static_cast<double>(dm.b) * dm.hkv * dm.G * w_obs * dm.d * dm.esize >= static_cast<double>(1u << 30))
+        return fail(SKV_E_SHAPE, "q_obs must be smaller than 1 GiB");
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // passes of up to kMaxGroup (head, window position) rows per KV head
+    const int wp_max = std::max(1, skv::kMaxGroup / dm.G);
+    for (int o0 = 0; o0 < w_obs; o0 += wp_max) {
+        const int wp = std::min(wp_max, w_obs - o0);
+        Dims dv = dm;  // the pass's scored rows as the group's heads
+        dv.G = dm.G * wp;
+        dv.GP = dv.G <= 4 ? 4 : (dv.G <= 8 ? 8 : 16);
+        SKV_HIP(skv::launch_score(dm, q_obs, ly->L, ly->cand, ly->P, ly->stats, ly->score_wgs,
+                                  skv::QRows{w_obs, o0, wp}, st));
+        SKV_HIP(skv::launch_group(dv, ly->P, ly->stats, ly->cand, ly->S2, ly->keys, ly->kbounds, st));
+        SKV_HIP(skv::launch_snap_accum(dm, ly->S2, ly->snap_acc, static_cast<float>(dv.G), o0 == 0, st));
+    }
+    SKV_HIP(skv::launch_snap_pool(dm, ly->snap_acc, ly->cand, ly->S2, ly->keys, ly->kbounds, pool, st));
+    SKV_HIP(skv::launch_select(dm, ly->keys, ly->kbounds, ly->sel, ly->slot_chunk, ly->misses, ly->miss_count,
+                               ly->counters, ly->select_keys_in_lds, st));
+    ly->fixed = true;
+    ly->fetch_pending = true;
+    return SKV_OK;
+}
+
 int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) {
     if (!ly) return fail(SKV_E_INVAL, "layer is null");
     if (!q || !out) return fail(SKV_E_INVAL, "null q or out");
     if (!ly->ready) return fail(SKV_E_STATE, "decode_step before prefill_meta / load_meta");
     hipStream_t st = static_cast<hipStream_t>(stream);
     const Dims dm = dims_with_local(ly->dm, ly->dm.w + ly->n_app);
-    {
-        Timed t(ly, SKV_K_SCORE, st);
-        SKV_HIP(skv::launch_score(dm, q, ly->L, ly->cand, ly->P, ly->stats, ly->score_wgs, st));
-    }
-    {
-        Timed t(ly, SKV_K_SELECT, st);
-        SKV_HIP(skv::launch_group(dm, ly->P, ly->stats, ly->cand, ly->S2, ly->keys, ly->kbounds, st));
-        SKV_HIP(skv::launch_select(dm, ly->keys, ly->kbounds, ly->sel, ly->slot_chunk, ly->misses, ly->miss_count,
-                                   ly->counters, ly->select_keys_in_lds, st));
+    // a fixed (SnapKV-style) selection skips scoring and selection, and
+    // fetches only once, on the first step after it was made
+    const bool select = !ly->fixed, fetch = select || ly->fetch_pending;
+    if (select) {
+        {
+            Timed t(ly, SKV_K_SCORE, st);
+            SKV_HIP(skv::launch_score(dm, q, ly->L, ly->cand, ly->P, ly->stats, ly->score_wgs, skv::QRows{1, 0, 1},
+                                      st));
+        }
+        {
+            Timed t(ly, SKV_K_SELECT, st);
+            SKV_HIP(skv::launch_group(dm, ly->P, ly->stats, ly->cand, ly->S2, ly->keys, ly->kbounds, st));
+            SKV_HIP(skv::launch_select(dm, ly->keys, ly->kbounds, ly->sel, ly->slot_chunk, ly->misses,
+                                       ly->miss_count, ly->counters, ly->select_keys_in_lds, st));
+        }
     }
     if (ly->overlap) {
         // fork: the fetch of missing V on the fetch stream, the key rebuild
@@ -524,7 +569,7 @@ int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) 
         SKV_HIP(hipEventRecord(ly->ev_sel, st));
         SKV_HIP(hipStreamWaitEvent(ly->copy, ly->ev_sel, 0));
         SKV_HIP(hipStreamWaitEvent(ly->comp, ly->ev_sel, 0));
-        {
+        if (fetch) {
             Timed t(ly, SKV_K_FETCH, ly->copy);
             SKV_HIP(skv::launch_fetch(dm, ly->v_host_dev, ly->vc, ly->misses, ly->miss_count, ly->fetch_waves,
                                       ly->copy));
@@ -540,7 +585,7 @@ int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) 
         SKV_HIP(hipStreamWaitEvent(st, ly->ev_fetch, 0));
     } else {
         // one queue: the fetch runs alone on PCIe, then the rebuild
-        {
+        if (fetch) {
             Timed t(ly, SKV_K_FETCH, st);
             SKV_HIP(skv::launch_fetch(dm, ly->v_host_dev, ly->vc, ly->misses, ly->miss_count, ly->fetch_waves,
                                       st));
@@ -551,6 +596,7 @@ int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) 
                                    ly->theta_rev, ly->logits, st));
         }
     }
+    ly->fetch_pending = false;
     {
         Timed t(ly, SKV_K_PV, st);
         SKV_HIP(skv::launch_pv(dm, ly->logits, ly->v_out, ly->vc, ly->v_loc, ly->part_ml, ly->part_acc, st));
@@ -565,6 +611,7 @@ int shadowkv_reset_cache(skv_layer *ly, void *stream) {
     hipStream_t st = static_cast<hipStream_t>(stream);
     SKV_HIP(hipStreamWaitEvent(st, ly->ev_fetch, 0));
     SKV_HIP(skv::launch_fill_i32(ly->slot_chunk, -1, static_cast<size_t>(ly->dm.b) * ly->dm.hkv * ly->dm.k, st));
+    ly->fixed = ly->fetch_pending = false;
     return SKV_OK;
 }
 

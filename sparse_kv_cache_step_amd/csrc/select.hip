@@ -52,14 +52,16 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const uint16_t *__restr
                                                          const uint16_t *__restrict__ L,
                                                          const uint32_t *__restrict__ cand, int mask_words,
                                                          float *__restrict__ U, float2 *__restrict__ stats,
-                                                         int hkv, int G, int n, int wtiles, int rows,
-                                                         int tiles_per_wave, float scale) {
+                                                         int hkv, int Gr, int w_obs, int o_base, int wp,
+                                                         int n, int wtiles, int rows, int tiles_per_wave,
+                                                         float scale) {
     constexpr int KS = D / 32;
     constexpr int ROUNDS = 4;
+    const int G = Gr * wp;  // scored rows (heads) per KV head: see QRows
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int row = lane & 15, quad = lane >> 4;
-    const int hq = hkv * G;
+    const int hq = hkv * Gr;
     const int total = rows * wtiles;
     int T = (blockIdx.x * 4 + wave) * tiles_per_wave;  // this wave's run of tiles
     const int t_end = min(total, T + tiles_per_wave);
@@ -68,15 +70,15 @@ __global__ __launch_bounds__(256) void score_mfma_kernel(const uint16_t *__restr
     // Loads and stores go through buffer resources: the next tile's loads are
     // switched off (not branched around) after the last tile, chunks past n
     // read zeros and their stores are dropped.
-    const Rsrc qr = make_rsrc(q, static_cast<uint32_t>(rows) * G * D * 2);
+    const Rsrc qr = make_rsrc(q, static_cast<uint32_t>(rows) * Gr * w_obs * D * 2);
     const Rsrc cr = make_rsrc(cand, static_cast<uint32_t>(rows) * mask_words * 4);
     const uint32_t lrow_bytes = static_cast<uint32_t>(n) * D * 2;
     auto l_rsrc = [&](int bh) { return make_rsrc(L + static_cast<size_t>(bh) * n * D, lrow_bytes); };
     // query rows of the group: lane row = head; rows past G repeat the last
     // head and their MFMA outputs are ignored
     auto q_off = [&](int bh) {
-        const int b = bh / hkv, h = bh % hkv;
-        return ((b * hq + h * G + min(row, G - 1)) * D + quad * 8) * 2;
+        const int b = bh / hkv, h = bh % hkv, gv = min(row, G - 1);
+        return (((b * hq + h * Gr + gv / wp) * w_obs + o_base + gv % wp) * D + quad * 8) * 2;
     };
     auto load_q = [&](int off, bf16x8 *qa) {
 #pragma unroll
@@ -212,13 +214,17 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void score_generic_kernel(const T *__restrict__ q, const T *__restrict__ L,
                                                             const uint32_t *__restrict__ cand, int mask_words,
                                                             float *__restrict__ U, float2 *__restrict__ stats,
-                                                            int hkv, int G, int n, int wtiles, float scale) {
+                                                            int hkv, int Gr, int w_obs, int o_base, int wp, int n,
+                                                            int wtiles, float scale) {
     __shared__ float qs[kMaxGroup][D];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int bh = blockIdx.y, b = bh / hkv, h = bh % hkv;
-    const int hq = hkv * G;
-    for (int i = threadIdx.x; i < G * D; i += 256)
-        qs[i / D][i % D] = Elem<T>::ld(q, (static_cast<size_t>(b) * hq + h * G) * D + i);
+    const int hq = hkv * Gr, G = Gr * wp;
+    for (int i = threadIdx.x; i < G * D; i += 256) {
+        const int gv = i / D;
+        qs[gv][i % D] = Elem<T>::ld(q, ((static_cast<size_t>(b) * hq + h * Gr + gv / wp) * w_obs + o_base + gv % wp) * D +
+                                           i % D);
+    }
     __syncthreads();
     const int wt = blockIdx.x * 4 + wave;
     if (wt >= wtiles) return;
@@ -652,6 +658,63 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// SnapKV-style selection (the SnapKV review page, 核心公式 and 池化策略), at
+// chunk level against the landmarks.  The importance of a chunk is the
+// attention it receives, summed over the query heads of its KV group and the
+// queries of an observation window; each scoring pass covers up to kMaxGroup
+// (head, window position) rows, and the group kernel leaves their mean
+// softmax in S2.
+//   snap_accum: acc (+)= rows_in_pass * S2, the pass's summed attention;
+//   snap_pool:  pooled[j] = (1/pool) sum over |i - j| <= pool/2 of acc[i]
+//               (zero padding), written to S2 for selectable chunks (0
+//               elsewhere) and as selection keys with per-slice bounds,
+//               exactly the group kernel's outputs, for the select kernel.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void snap_accum_kernel(const float *__restrict__ S2, float *__restrict__ acc,
+                                                         size_t count, float weight, int first) {
+    for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < count; i += gridDim.x * 256ull)
+        acc[i] = (first ? 0.f : acc[i]) + weight * S2[i];
+}
+
+__global__ __launch_bounds__(256) void snap_pool_kernel(const float *__restrict__ acc,
+                                                        const uint32_t *__restrict__ cand, int mask_words,
+                                                        float *__restrict__ S2, uint32_t *__restrict__ keys,
+                                                        uint2 *__restrict__ kbounds, int n, int pool, int slices) {
+    __shared__ uint32_t s_red[2][4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int sl = blockIdx.x, bh = blockIdx.y;
+    const int j0 = sl * kGroupSlice, half = pool / 2;
+    const float *a = acc + static_cast<size_t>(bh) * n;
+    const uint32_t *cm = cand + static_cast<size_t>(bh) * mask_words;
+    const float inv = 1.f / static_cast<float>(pool);
+    uint32_t kmn = 0xffffffffu, kmx = 0u;
+    for (int u = 0; u < kGroupSlice / 256; ++u) {
+        const int j = j0 + tid + 256 * u;
+        if (j >= n) break;
+        float sum = 0.f;
+        for (int i = max(0, j - half); i <= min(n - 1, j + half); ++i) sum += a[i];
+        const float pooled = sum * inv;
+        const bool valid = mask_bit(cm, j);
+        S2[static_cast<size_t>(bh) * n + j] = valid ? pooled : 0.f;
+        const uint32_t key = float_key(pooled);
+        keys[static_cast<size_t>(bh) * n + j] = valid ? key : 0u;
+        if (valid) { kmn = min(kmn, key); kmx = max(kmx, key); }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        kmn = min(kmn, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmn), off, 64)));
+        kmx = max(kmx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(kmx), off, 64)));
+    }
+    if (lane == 0) { s_red[0][wave] = kmn; s_red[1][wave] = kmx; }
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t lo = s_red[0][0], hi = s_red[1][0];
+        for (int w = 1; w < 4; ++w) { lo = min(lo, s_red[0][w]); hi = max(hi, s_red[1][w]); }
+        kbounds[static_cast<size_t>(bh) * slices + sl] = make_uint2(lo, hi);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 static hipError_t allow_lds(const void *fn, size_t bytes) {
@@ -659,10 +722,12 @@ static hipError_t allow_lds(const void *fn, size_t bytes) {
     return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(bytes));
 }
 
-static int score_mode(const Dims &dm) { return dm.G <= 4 ? 0 : (dm.G % 4 == 0 ? 1 : 2); }
+static int score_mode(int G) { return G <= 4 ? 0 : (G % 4 == 0 ? 1 : 2); }
 
 hipError_t launch_score(const Dims &dm, const void *q, const void *landmarks, const uint32_t *cand, float *P,
-                        float2 *stats, int score_wgs, hipStream_t st) {
+                        float2 *stats, int score_wgs, QRows qr, hipStream_t st) {
+    const int Gv = dm.G * qr.wp;  // scored rows per KV head
+    if (Gv > kMaxGroup || qr.wp < 1 || qr.o_base + qr.wp > qr.w_obs) return hipErrorInvalidValue;
     if (dm.bf16) {
         const uint16_t *qq = static_cast<const uint16_t *>(q), *LL = static_cast<const uint16_t *>(landmarks);
         const int rows = dm.b * dm.hkv, total = rows * dm.wtiles;
@@ -672,9 +737,9 @@ hipError_t launch_score(const Dims &dm, const void *q, const void *landmarks, co
         const int tpw = (total + 4 * wgs - 1) / (4 * wgs);
         auto go = [&](auto kern) {
             hipLaunchKernelGGL(kern, dim3(wgs), dim3(256), 0, st, qq, LL, cand, dm.mask_words, P, stats, dm.hkv,
-                               dm.G, dm.n, dm.wtiles, rows, tpw, dm.scale);
+                               dm.G, qr.w_obs, qr.o_base, qr.wp, dm.n, dm.wtiles, rows, tpw, dm.scale);
         };
-        const int m = score_mode(dm);
+        const int m = score_mode(Gv);
         if (dm.d == 128) {
             if (m == 0) go(score_mfma_kernel<128, 0>);
             else if (m == 1) go(score_mfma_kernel<128, 1>);
@@ -689,11 +754,13 @@ hipError_t launch_score(const Dims &dm, const void *q, const void *landmarks, co
         if (dm.d == 128)
             hipLaunchKernelGGL((score_generic_kernel<float, 128>), grid, dim3(256), 0, st,
                                static_cast<const float *>(q), static_cast<const float *>(landmarks), cand,
-                               dm.mask_words, P, stats, dm.hkv, dm.G, dm.n, dm.wtiles, dm.scale);
+                               dm.mask_words, P, stats, dm.hkv, dm.G, qr.w_obs, qr.o_base, qr.wp, dm.n, dm.wtiles,
+                               dm.scale);
         else
             hipLaunchKernelGGL((score_generic_kernel<float, 64>), grid, dim3(256), 0, st,
                                static_cast<const float *>(q), static_cast<const float *>(landmarks), cand,
-                               dm.mask_words, P, stats, dm.hkv, dm.G, dm.n, dm.wtiles, dm.scale);
+                               dm.mask_words, P, stats, dm.hkv, dm.G, qr.w_obs, qr.o_base, qr.wp, dm.n, dm.wtiles,
+                               dm.scale);
     }
     return hipGetLastError();
 }
@@ -741,6 +808,21 @@ hipError_t launch_topo(const Dims &dm, const float *min_cos, int32_t *outliers, 
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(topo_kernel, dim3(dm.b * dm.hkv), dim3(kSelectThreads), lds, st, min_cos, dm.n,
                        dm.n - dm.n_loc, dm.o, outliers, gscratch, keys_in_lds);
+    return hipGetLastError();
+}
+
+hipError_t launch_snap_accum(const Dims &dm, const float *S2, float *acc, float weight, int first, hipStream_t st) {
+    const size_t count = static_cast<size_t>(dm.b) * dm.hkv * dm.n;
+    const int grid = static_cast<int>(std::min<size_t>((count + 255) / 256, 4096));
+    hipLaunchKernelGGL(snap_accum_kernel, dim3(grid), dim3(256), 0, st, S2, acc, count, weight, first);
+    return hipGetLastError();
+}
+
+hipError_t launch_snap_pool(const Dims &dm, const float *acc, const uint32_t *cand, float *S2, uint32_t *keys,
+                            uint2 *kbounds, int pool, hipStream_t st) {
+    const int slices = group_slices(dm);
+    hipLaunchKernelGGL(snap_pool_kernel, dim3(slices, dm.b * dm.hkv), dim3(256), 0, st, acc, cand, dm.mask_words,
+                       S2, keys, kbounds, dm.n, pool, slices);
     return hipGetLastError();
 }
 

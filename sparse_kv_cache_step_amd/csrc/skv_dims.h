@@ -53,10 +53,18 @@ hipError_t launch_append(const Dims &dm, const void *k_new, const void *v_new, c
                          void *v_loc, int row, int pos, hipStream_t st);
 
 // Decode.
+// Query rows of a scoring launch.  q is laid out (b, h_q, w_obs, d); scored
+// row g' (0 <= g' < G * wp) of KV head h is query head h*G + g'/wp at window
+// position o_base + g'%wp.  The decode step scores one query per head
+// (w_obs = wp = 1, o_base = 0); the SnapKV-style selection scores up to
+// kMaxGroup (head, window position) rows per pass.
+struct QRows {
+    int w_obs, o_base, wp;
+};
 // score_wgs: workgroups of the persistent bfloat16 scoring kernel (0: two
-// 64-chunk tiles per wave).
+// 64-chunk tiles per wave).  U and stats hold G * wp scored rows per KV head.
 hipError_t launch_score(const Dims &dm, const void *q, const void *landmarks, const uint32_t *cand,
-                        float *P, float2 *stats, int score_wgs, hipStream_t st);
+                        float *P, float2 *stats, int score_wgs, QRows qr, hipStream_t st);
 // Group score: kbounds holds one (min, max) key pair per row and slice of
 // kGroupSlice chunks.
 int group_slices(const Dims &dm);
@@ -69,6 +77,11 @@ size_t select_static_lds();
 hipError_t launch_select(const Dims &dm, const uint32_t *keys, const uint2 *kbounds, int32_t *sel,
                          int32_t *slot_chunk, int2 *misses, int32_t *miss_count, unsigned long long *counters,
                          int keys_in_lds, hipStream_t st);
+// SnapKV-style selection: accumulate a pass's summed attention, then pool
+// it into S2, selection keys and slice bounds.
+hipError_t launch_snap_accum(const Dims &dm, const float *S2, float *acc, float weight, int first, hipStream_t st);
+hipError_t launch_snap_pool(const Dims &dm, const float *acc, const uint32_t *cand, float *S2, uint32_t *keys,
+                            uint2 *kbounds, int pool, hipStream_t st);
 hipError_t launch_fetch(const Dims &dm, const void *v_host, void *vc, const int2 *misses,
                         const int32_t *miss_count, int waves, hipStream_t st);
 hipError_t launch_qk(const Dims &dm, const void *q, const void *k_out, const void *k_loc, const void *A,

@@ -312,3 +312,96 @@ def test_append_decode_tokens_matches_oracle(case):
     assert e.value.code == skv.SKV_E_SHAPE
     layer.close()
     hb.free()
+
+
+SNAP_CASES = {
+    # binary32, GQA 4: one pass of four window queries and one of two
+    "fp32-g4": (T.with_(b=2, s=2048, d=128, r=48, o=4, k=9, w=32, rho=0.9), 6, 5),
+    # bfloat16 Llama-shaped, GQA 4, two passes
+    "bf16-g4": (synth.LLAMA_32K.with_(b=2, s=8192, k=16, rho=0.9), 6, 7),
+    # GQA 16 (one window query per pass), ragged n = 1500
+    "bf16-g16-ragged": (synth.GLM_244K.with_(b=2, s=12000, o=10, k=23, rho=0.85), 3, 3),
+    # one query head per KV head, 20 window queries (passes of 16 and 4),
+    # the widest pooling
+    "bf16-g1-pool63": (synth.LLAMA_32K.with_(b=1, h_q=4, h_kv=4, d=64, s=4096, r=40, o=3, k=17, w=16,
+                                             true_rank=20, rho=0.9), 20, 63),
+    # one window query and no pooling: the decode step's own selection
+    "bf16-w1-pool1": (synth.LLAMA_32K.with_(h_q=8, h_kv=2, s=2048, r=96, o=4, k=12, rho=0.9), 1, 1),
+}
+
+
+@pytest.mark.parametrize("case", list(SNAP_CASES))
+def test_snapkv_selection_matches_oracle(case):
+    """SnapKV-style fixed selection: the window's summed, pooled importance
+    and its Top-K must match the oracle's (exact or near-tie), the first
+    decode step after it fetches the selected V and the later steps fetch
+    nothing, every step's output must match the oracle's attention over the
+    fixed selection, and reset_cache must return the layer to per-step
+    selection."""
+    wl, w_obs, pool = SNAP_CASES[case]
+    n_dec = 3
+    log(f"[snapkv-{case}] b={wl.b} G={wl.h_q // wl.h_kv} n={wl.n} k={wl.k} w_obs={w_obs} pool={pool}")
+    shape = oracle_shape(wl)
+    k_pre, v = synth.k_pre_numpy(wl), synth.v_numpy(wl)
+    qs = synth.queries_numpy(wl, steps=w_obs + n_dec)
+    q_obs = np.ascontiguousarray(qs[:w_obs].transpose(1, 2, 0, 3))  # (b, h_q, w_obs, d)
+    meta = oracle.prefill(shape, k_pre, v)
+    A_o, B_o = oracle.svd_factors(shape, k_pre)
+    dt = tdtype(wl)
+    k_pre_d, v_d = to_dev(k_pre, dt), to_dev(v, dt)
+    A_d, B_d = svd_factors(k_pre_d, wl.r)
+    layer = skv.Layer(**layer_kwargs(wl))
+    hb = layer.host_buffer()
+    layer.prefill_meta(k_pre_d, v_d, A_d, B_d, hb)
+    torch.cuda.synchronize()
+    # the prefill metadata must agree first: the selection is built on it
+    _compare_prefill(wl, layer, hb, meta, v)
+
+    layer.snapkv_select(to_dev(q_obs, dt), pool)
+    torch.cuda.synchronize()
+    ora = oracle.snapkv_select(shape, q_obs, meta, pool)
+    sel_g = to_np(layer.read(skv.SKV_T_SELECTION))
+    exact = check_selection(sel_g, ora["sel"], ora["pooled"], meta["cand"])
+    pooled_g = to_np(layer.read(skv.SKV_T_GROUP_SCORES))
+    scale = float(np.max(ora["pooled"]))
+    err = float(np.max(np.abs(pooled_g - ora["pooled"])))
+    log(f"[snapkv-{case}] selection exact={exact}, max|pooled - oracle| = {err:.3g} (max {scale:.3g})")
+    assert err <= 1e-5 * scale, f"pooled importance differs by {err}"
+    st0 = layer.stats()
+    assert (st0["hits"], st0["misses"], st0["steps"]) == (0, wl.b * wl.h_kv * wl.k, 1)
+
+    for t in range(n_dec):
+        q_d = to_dev(qs[w_obs + t], dt)
+        out_d = torch.empty_like(q_d)
+        layer.decode_step(q_d, out_d)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_np(layer.read(skv.SKV_T_SELECTION)), sel_g)
+        ref = oracle.attend(shape, qs[w_obs + t], sel_g, A_o, B_o, v, meta)
+        err = float(np.max(np.abs(to_np(out_d) - ref)))
+        log(f"[snapkv-{case}] decode {t}: max|out - oracle| = {err:.3g}")
+        assert err <= OUT_TOL[wl.bf16], f"decode {t}: max abs error {err}"
+        st = layer.stats()
+        assert st == st0, "a fixed selection loaded or counted again"
+    _check_cache_lossless(wl, layer, v, sel_g)
+
+    # reset_cache leaves the fixed selection: the next step selects again
+    layer.reset_cache()
+    q_d = to_dev(qs[w_obs], dt)
+    out_d = torch.empty_like(q_d)
+    layer.decode_step(q_d, out_d)
+    torch.cuda.synchronize()
+    res = oracle.decode(shape, qs[w_obs], meta, A_o, B_o, v)
+    sel_step = to_np(layer.read(skv.SKV_T_SELECTION))
+    check_selection(sel_step, res["sel"], res["S2"], meta["cand"])
+    assert layer.stats()["steps"] == st0["steps"] + 1
+
+    # refused arguments
+    q_bad = to_dev(q_obs, dt)
+    for bad_pool in (0, 2, 65):
+        with pytest.raises(skv.ShadowKVError) as e:
+            layer.snapkv_select(q_bad, bad_pool)
+        assert e.value.code == skv.SKV_E_SHAPE
+    with pytest.raises(ValueError):
+        layer.snapkv_select(q_bad[:, :1], pool)
+    layer.close()
+    hb.free()
