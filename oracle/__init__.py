@@ -18,7 +18,9 @@ adds the two steps that are library routines or pure bookkeeping:
 * ``CacheSim`` -- the per-layer set-difference cache of the Telegram write-up
   ("Часть II"): at step t only I_t \\ I_{t-1} is loaded, the rest is reused.
   The attended set is always I_t, so the cache changes no output; the
-  simulation yields the hit count that defines the hit rate alpha.
+  simulation yields the hit count that defines the hit rate alpha.  A larger
+  least-recently-used capacity is the same cache keeping more than one step's
+  chunks (a reading: the pages size the cache only by the selection).
 """
 from __future__ import annotations
 
@@ -327,26 +329,40 @@ def snapkv_select(shape: Shape, q_obs, meta: dict, pool: int) -> dict:
 
 
 class CacheSim:
-    """Per-layer resident set of the set-difference cache: R_t = I_t, and
-    step t loads only I_t \\ R_{t-1}."""
+    """Per-layer resident set of the V cache.  With capacity None (the
+    set-difference cache of the ShadowKV review page: adjacent decoding steps
+    share chunks) R_t = I_t, and step t loads only I_t \\ R_{t-1}.  With a
+    capacity C >= k chunks per (sequence, KV head) the cache is least recently
+    used: R_t holds I_t and, of R_{t-1} \\ I_t, the C - k chunks selected most
+    recently (equal steps: the lower chunk index stays).  Capacity k is the
+    set-difference cache."""
 
-    def __init__(self, b: int, h_kv: int):
-        self.resident = [[set() for _ in range(h_kv)] for _ in range(b)]
+    def __init__(self, b: int, h_kv: int, capacity: int | None = None):
+        self.capacity = capacity
+        self.step_no = 0
+        # per row: chunk -> the last step that selected it
+        self.resident = [[{} for _ in range(h_kv)] for _ in range(b)]
 
     def step(self, sel) -> tuple[int, int]:
         """Returns (hits, misses) summed over sequences and KV heads."""
         sel = np.asarray(sel)
+        self.step_no += 1
         hits = misses = 0
         for bi, row in enumerate(self.resident):
             for h in range(len(row)):
                 cur = set(int(x) for x in sel[bi, h])
-                hit = len(cur & row[h])
+                hit = len(cur & row[h].keys())
                 hits += hit
                 misses += len(cur) - hit
-                row[h] = cur
+                cap = len(cur) if self.capacity is None else self.capacity
+                assert cap >= len(cur)
+                others = sorted((j for j in row[h] if j not in cur), key=lambda j: (-row[h][j], j))
+                kept = {j: row[h][j] for j in others[:cap - len(cur)]}
+                kept.update({j: self.step_no for j in cur})
+                row[h] = kept
         return hits, misses
 
     def reset(self) -> None:
         for row in self.resident:
             for h in range(len(row)):
-                row[h] = set()
+                row[h] = {}

@@ -526,3 +526,60 @@ def test_snapkv_importance_is_summed_attention_and_pooling_spreads_it():
                 assert {0, 1} <= set(r["sel"][0, h])
         r_nopool = oracle.snapkv_select(shape, qq, m, pool=1)
         assert all(j in r_nopool["sel"][0, h] for h in range(2))
+
+
+def _lru_brute(history, cap):
+    """Resident set after the selections in `history` (lists of chunk sets):
+    the `cap` chunks ever selected with the latest last selection, equal
+    steps ordered by lower chunk index -- the LRU order written out whole."""
+    last = {}
+    for t, cur in enumerate(history):
+        for j in cur:
+            last[j] = t
+    order = sorted(last, key=lambda j: (-last[j], j))
+    return set(order[:cap])
+
+
+def test_lru_cache_is_the_most_recently_selected_chunks():
+    """Capacity C >= k: at every step the hits are the selected chunks that
+    the brute-force LRU set (the C most recently selected chunks over the
+    whole history) held before it; capacity k is the set-difference cache,
+    and hits never decrease as the capacity grows (LRU keeps nested sets)."""
+    rng = np.random.default_rng(15)
+    k, n, steps = 5, 30, 12
+    sels = []
+    prev = np.sort(rng.choice(n, k, replace=False))
+    for t in range(steps):
+        # drift: keep some chunks of the previous step, draw the rest
+        keep = rng.choice(prev, rng.integers(0, k), replace=False)
+        rest = rng.choice(np.setdiff1d(np.arange(n), keep), k - keep.size, replace=False)
+        prev = np.sort(np.concatenate([keep, rest]))
+        sels.append(prev)
+    totals = []
+    for cap in (k, k + 1, 2 * k, 3 * k + 2, n):
+        sim = oracle.CacheSim(1, 1, capacity=cap)
+        plain = oracle.CacheSim(1, 1)
+        hits_total = 0
+        for t, sel in enumerate(sels):
+            before = _lru_brute([set(map(int, s)) for s in sels[:t]], cap) if t else set()
+            hits, misses = sim.step(sel[None, None])
+            assert hits == len(before & set(map(int, sel))) and hits + misses == k
+            assert set(sim.resident[0][0]) == _lru_brute([set(map(int, s)) for s in sels[:t + 1]], cap)
+            if cap == k:
+                assert plain.step(sel[None, None]) == (hits, misses)
+            hits_total += hits
+        totals.append(hits_total)
+    assert totals == sorted(totals) and totals[-1] > totals[0]
+
+
+def test_lru_ties_keep_the_lower_chunk_index():
+    """Hand-worked: k = 2, C = 3.  Step 1 selects {4, 7}, step 2 {1, 2}: the
+    cache can keep one of 4 and 7 (both last selected at step 1) and keeps 4.
+    Step 3 selecting {4, 7} then hits 4 only."""
+    sim = oracle.CacheSim(1, 1, capacity=3)
+    assert sim.step(np.array([[[4, 7]]])) == (0, 2)
+    assert sim.step(np.array([[[1, 2]]])) == (0, 2)
+    assert set(sim.resident[0][0]) == {1, 2, 4}
+    assert sim.step(np.array([[[4, 7]]])) == (1, 1)
+    # {4, 7} at step 3; of {1, 2} (step 2) the lower index stays
+    assert set(sim.resident[0][0]) == {1, 4, 7}
