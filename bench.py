@@ -154,6 +154,9 @@ def main() -> int:
                     help="SnapKV-style fixed selection: after the prefill each layer selects once from a window "
                          "of W queries with average pooling over POOL chunks; the timed steps keep that "
                          "selection (no oracle baseline in this mode)")
+    ap.add_argument("--cache-chunks", type=int, default=0,
+                    help="V chunks resident in HBM per (sequence, KV head): 0 = top-k, the set-difference cache; "
+                         "larger keeps the most recently selected chunks too (least recently used)")
     ap.add_argument("--host-eigh", action="store_true",
                     help="setup: solve the factors' eigenproblems on the host instead of the device")
     ap.add_argument("--sweep", action="store_true",
@@ -217,6 +220,9 @@ def main() -> int:
         torch.cuda.set_device(dev)
         dt = torch.bfloat16 if wl.bf16 else torch.float32
         nq = args.warmup + args.steps
+        # the per-kernel pass decodes the K steps after the timed ones (fresh
+        # queries, so a cache larger than the selection is not replayed warm)
+        nq_all = nq + (args.steps if args.kernel_events == "on" else 0)
         log(f"bench: {wl.name} b={wl.b} s={wl.s} h_q={wl.h_q} h_kv={wl.h_kv} d={wl.d} r={wl.r} o={wl.o} k={wl.k} "
             f"w={wl.w} layers={layers} steps={args.steps} warmup={args.warmup}")
 
@@ -240,7 +246,8 @@ def main() -> int:
             prefill_ms["svd_factors"] += (time.perf_counter() - ts) * 1e3
             lay = skv.Layer(batch=wl.b, heads_q=wl.h_q, heads_kv=wl.h_kv, head_dim=wl.d, seq_len=wl.s, chunk=wl.c,
                             rank=wl.r, n_outlier=wl.o, top_k=wl.k, local_window=wl.w, rope_base=wl.rope_base,
-                            bf16=wl.bf16, max_new=(nq + args.steps) if args.append else 0)
+                            bf16=wl.bf16, max_new=nq_all if args.append else 0,
+                            cache_chunks=args.cache_chunks)
             if l < n_host:
                 host_bufs.append(lay.host_buffer())
             torch.cuda.synchronize()
@@ -250,18 +257,18 @@ def main() -> int:
             prefill_ms["prefill_meta"] += (time.perf_counter() - ts) * 1e3
             if snap:
                 # the observation window's queries come before the decoded ones
-                q_all = synth.queries_torch(wl, l, dev, steps=snap[0] + nq)
+                q_all = synth.queries_torch(wl, l, dev, steps=snap[0] + nq_all)
                 q_obs.append(q_all[:snap[0]].permute(1, 2, 0, 3).contiguous())
                 qs.append(q_all[snap[0]:].contiguous())
                 del q_all
             else:
-                qs.append(synth.queries_torch(wl, l, dev, steps=nq))
+                qs.append(synth.queries_torch(wl, l, dev, steps=nq_all))
             if args.append:
                 # the generated tokens' pre-RoPE keys and values, one per step
                 g = torch.Generator(device=dev)
                 g.manual_seed(1000003 * (l + 1) + wl.wid)
-                new_kv.append((torch.randn((nq, wl.b, wl.h_kv, wl.d), generator=g, device=dev).to(dt),
-                               torch.randn((nq, wl.b, wl.h_kv, wl.d), generator=g, device=dev).to(dt)))
+                new_kv.append((torch.randn((nq_all, wl.b, wl.h_kv, wl.d), generator=g, device=dev).to(dt),
+                               torch.randn((nq_all, wl.b, wl.h_kv, wl.d), generator=g, device=dev).to(dt)))
             torch.cuda.synchronize()
             if l == spot_layer and not args.no_cpu_baseline and not args.append and not snap:
                 sample = [0, wl.b // 2] if wl.b > 1 else [0]
@@ -317,7 +324,8 @@ def main() -> int:
         run_steps(args.warmup, args.steps)
         e1.record(stream)
         torch.cuda.synchronize()
-        last_out = outs[spot_layer].clone()  # output of the last timed step
+        last_out = outs[spot_layer].clone()  # output and selection of the last timed step
+        last_sel = Ls[spot_layer].read(skv.SKV_T_SELECTION)
         wall = time.perf_counter() - wall0
         elapsed = e0.elapsed_time(e1) / 1e3
         log(f"timed: {args.steps} steps x {layers} layers in {elapsed * 1e3:.2f} ms (host wall {wall * 1e3:.2f} ms)")
@@ -327,13 +335,13 @@ def main() -> int:
         alpha = hits / max(1, hits + misses)
         h2d_bytes = sum(s["bytes_h2d"] for s in stats)
 
-        # ---- per-kernel durations: the same steps again with HIP events ----------
+        # ---- per-kernel durations: the next K steps with HIP events --------------
         kern_ms = {name: 0.0 for name in skv.KERNELS}
         kern_steps = 0
         if args.kernel_events == "on":
             for lay in Ls:
                 lay.set_timing(True)
-            run_steps(args.warmup, args.steps)
+            run_steps(nq, args.steps)
             torch.cuda.synchronize()
             for lay in Ls:
                 ms, st = lay.get_timing()
@@ -429,7 +437,7 @@ def main() -> int:
                                       f"scaled to all {wl.b} sequences"}
             if res_last is not None:
                 gpu_out = last_out[seqs].float().cpu().double().numpy()
-                gpu_sel = Ls[spot_layer].read(skv.SKV_T_SELECTION)[seqs].cpu().numpy()
+                gpu_sel = last_sel[seqs].cpu().numpy()
                 parity = {"layer": spot_layer, "step": t_last, "sequences": seqs,
                           "selection_equal": bool(np.array_equal(gpu_sel, res_last["sel"])),
                           "max_abs_err_vs_oracle": float(np.max(np.abs(gpu_out - res_last["out"]))),
@@ -445,6 +453,7 @@ def main() -> int:
             "config": {"workload": wl.name, "batch": wl.b, "seq_len": wl.s, "heads_q": wl.h_q, "heads_kv": wl.h_kv,
                        "head_dim": wl.d, "chunk": wl.c, "rank": wl.r, "outlier_chunks": wl.o, "top_k": wl.k,
                        "local_window": wl.w, "layers": layers, "host_v_buffers": n_host,
+                       "cache_chunks": args.cache_chunks or wl.k,
                        **({"append": True} if args.append else {}),
                        **({"snapkv": {"w_obs": snap[0], "pool": snap[1]}} if snap else {})},
             "us_per_layer_step": round(t_ls * 1e6, 3),

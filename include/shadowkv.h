@@ -65,7 +65,9 @@ enum {
  *   n = seq_len / chunk, n_loc = local_window / chunk;
  *   0 <= n_outlier <= n - n_loc; 0 <= top_k <= n - n_loc - n_outlier and
  *   top_k <= 4096; at least one attended key; 1 <= rank <= 256;
- *   rope_base > 0; 0 <= max_new <= 2^20.
+ *   rope_base > 0; 0 <= max_new <= 2^20;
+ *   cache_chunks 0 (= top_k) or top_k <= cache_chunks <= n - n_loc - n_outlier,
+ *   at most 16384.
  */
 typedef struct {
     int32_t batch;         /* b: sequences decoded together                  */
@@ -82,6 +84,12 @@ typedef struct {
     int32_t dtype;         /* SKV_F32 or SKV_BF16                            */
     int32_t max_new;       /* decode tokens shadowkv_append may add to the
                               local block (0: none)                          */
+    int32_t cache_chunks;  /* C: V chunks resident in HBM per (sequence, KV
+                              head).  0 or top_k: the set-difference cache
+                              (a step reuses what the previous step loaded);
+                              larger: least recently used, keeping besides
+                              the selection the C - k chunks selected most
+                              recently (equal steps: lower chunk index)     */
 } skv_config;
 
 typedef struct skv_layer skv_layer;
@@ -220,14 +228,17 @@ enum {
                                64-chunk tile), 0 off-candidate (last step)    */
     SKV_T_GROUP_SCORES = 5, /* f32 (b, h_kv, n): last step's S2, 0 masked     */
     SKV_T_SELECTION = 6,    /* int32 (b, h_kv, k): last step's I, ascending   */
-    SKV_T_SLOT_CHUNKS = 7,  /* int32 (b, h_kv, k): chunk held by each slot    */
-    SKV_T_CACHE_V = 8,      /* dtype (b, h_kv, k*c, d): resident V by slot    */
+    SKV_T_SLOT_CHUNKS = 7,  /* int32 (b, h_kv, C): chunk held by each slot,
+                               -1 if empty (C = cache_chunks)                 */
+    SKV_T_CACHE_V = 8,      /* dtype (b, h_kv, C*c, d): resident V by slot    */
     SKV_T_K_OUT = 9,        /* dtype (b, h_kv, o*c, d)                        */
     SKV_T_V_OUT = 10,
     SKV_T_K_LOC = 11,       /* dtype (b, h_kv, w + max_new, d): the window's
                                keys, then the appended ones                   */
     SKV_T_V_LOC = 12,
-    SKV_T_COUNT = 13
+    SKV_T_SELECTION_SLOTS = 13, /* int32 (b, h_kv, k): slot holding the i-th
+                                   selected chunk                             */
+    SKV_T_COUNT = 14
 };
 size_t shadowkv_tensor_bytes(const skv_layer *layer, int which);
 int shadowkv_read(skv_layer *layer, int which, void *dst, size_t bytes, void *stream);

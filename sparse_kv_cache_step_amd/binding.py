@@ -20,7 +20,7 @@ SKV_F32, SKV_BF16 = 0, 1
 SKV_OK, SKV_E_INVAL, SKV_E_SHAPE, SKV_E_STATE, SKV_E_NOMEM, SKV_E_HIP = 0, -1, -2, -3, -4, -5
 (SKV_T_LANDMARKS, SKV_T_MIN_COS, SKV_T_OUTLIERS, SKV_T_CAND_MASK, SKV_T_SCORES, SKV_T_GROUP_SCORES,
  SKV_T_SELECTION, SKV_T_SLOT_CHUNKS, SKV_T_CACHE_V, SKV_T_K_OUT, SKV_T_V_OUT, SKV_T_K_LOC,
- SKV_T_V_LOC) = range(13)
+ SKV_T_V_LOC, SKV_T_SELECTION_SLOTS) = range(14)
 KERNELS = ("score", "select", "fetch", "qk", "pv")
 SKV_K_COUNT = len(KERNELS)
 
@@ -38,7 +38,7 @@ class skv_config(ctypes.Structure):
                 ("head_dim", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("chunk", ctypes.c_int32),
                 ("rank", ctypes.c_int32), ("n_outlier", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("local_window", ctypes.c_int32), ("rope_base", ctypes.c_float), ("dtype", ctypes.c_int32),
-                ("max_new", ctypes.c_int32)]
+                ("max_new", ctypes.c_int32), ("cache_chunks", ctypes.c_int32)]
 
 
 class skv_stats(ctypes.Structure):
@@ -230,10 +230,11 @@ class Layer:
     """One model layer's ShadowKV state on the current GPU."""
 
     def __init__(self, *, batch, heads_q, heads_kv, head_dim, seq_len, chunk, rank, n_outlier, top_k,
-                 local_window, rope_base=10000.0, bf16=True, max_new=0):
+                 local_window, rope_base=10000.0, bf16=True, max_new=0, cache_chunks=0):
         torch = _torch()
         self.cfg = skv_config(batch, heads_q, heads_kv, head_dim, seq_len, chunk, rank, n_outlier, top_k,
-                              local_window, float(rope_base), SKV_BF16 if bf16 else SKV_F32, max_new)
+                              local_window, float(rope_base), SKV_BF16 if bf16 else SKV_F32, max_new, cache_chunks)
+        self.cap = cache_chunks if cache_chunks > 0 else top_k  # V cache slots per (sequence, KV head)
         self.dtype = torch.bfloat16 if bf16 else torch.float32
         self.n = seq_len // chunk if chunk > 0 else 0
         self.device = torch.device("cuda", torch.cuda.current_device())
@@ -336,10 +337,11 @@ class Layer:
             SKV_T_CAND_MASK: (torch.int32, (b, hkv, (self.n + 31) // 32)),
             SKV_T_SCORES: (torch.float32, (b, hkv, self.n, hq // hkv)),
             SKV_T_GROUP_SCORES: (torch.float32, (b, hkv, self.n)),
-            SKV_T_SELECTION: (torch.int32, (b, hkv, k)), SKV_T_SLOT_CHUNKS: (torch.int32, (b, hkv, k)),
-            SKV_T_CACHE_V: (dt, (b, hkv, k * ch, d)), SKV_T_K_OUT: (dt, (b, hkv, c.n_outlier * ch, d)),
+            SKV_T_SELECTION: (torch.int32, (b, hkv, k)), SKV_T_SLOT_CHUNKS: (torch.int32, (b, hkv, self.cap)),
+            SKV_T_CACHE_V: (dt, (b, hkv, self.cap * ch, d)), SKV_T_K_OUT: (dt, (b, hkv, c.n_outlier * ch, d)),
             SKV_T_V_OUT: (dt, (b, hkv, c.n_outlier * ch, d)), SKV_T_K_LOC: (dt, (b, hkv, c.local_window + c.max_new, d)),
             SKV_T_V_LOC: (dt, (b, hkv, c.local_window + c.max_new, d)),
+            SKV_T_SELECTION_SLOTS: (torch.int32, (b, hkv, k)),
         }[which]
         t = torch.empty(spec[1], dtype=spec[0], device=self.device)
         nbytes = t.numel() * t.element_size()

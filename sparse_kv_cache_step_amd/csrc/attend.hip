@@ -27,8 +27,8 @@ namespace skv {
 template <int VPL>  // 16-byte vectors per lane and chunk (0: any, looped)
 __global__ __launch_bounds__(256) void fetch_kernel(const u32x4 *__restrict__ v_host, u32x4 *__restrict__ vc,
                                                     const int2 *__restrict__ misses,
-                                                    const int32_t *__restrict__ miss_count, int rows, int k, int n,
-                                                    int chunk_vec) {
+                                                    const int32_t *__restrict__ miss_count, int rows, int k, int cap,
+                                                    int n, int chunk_vec) {
     extern __shared__ int pre[];  // rows + 1 prefix sums
     __shared__ int wsum[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -68,7 +68,7 @@ __global__ __launch_bounds__(256) void fetch_kernel(const u32x4 *__restrict__ v_
     int2 e = g < total ? locate(g, row) : make_int2(0, 0);
     for (; g < total; g += nw) {
         const u32x4 *src = v_host + (static_cast<size_t>(row) * n + e.x) * chunk_vec;
-        u32x4 *dst = vc + (static_cast<size_t>(row) * k + e.y) * chunk_vec;
+        u32x4 *dst = vc + (static_cast<size_t>(row) * cap + e.y) * chunk_vec;
         if constexpr (VPL > 0) {
             u32x4 t[VPL];
 #pragma unroll
@@ -108,7 +108,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void qk_generic_kernel(const T *__restrict__ q, const T *__restrict__ k_out,
                                                          const T *__restrict__ k_loc, const T *__restrict__ A,
                                                          const T *__restrict__ Bt,
-                                                         const int32_t *__restrict__ slot_chunk,
+                                                         const int32_t *__restrict__ sel,
                                                          const double *__restrict__ theta,
                                                          float *__restrict__ logits, int hkv, int G, int s, int c,
                                                          int r, int k, int OC, int KC, int w, int wcap, int NK, int t_out,
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(256) void qk_generic_kernel(const T *__restrict__ q
         const T *Bh = Bt + static_cast<size_t>(bh) * D * r;
         for (int idx = threadIdx.x; idx < cnt * D; idx += 256) {
             const int rr = idx / D, i = idx % D, key = key0 + rr;
-            const int pos = slot_chunk[static_cast<size_t>(bh) * k + key / c] * c + key % c;
+            const int pos = sel[static_cast<size_t>(bh) * k + key / c] * c + key % c;
             const T *arow = A + (static_cast<size_t>(b) * s + pos) * r;
             const T *brow = Bh + static_cast<size_t>(i) * r;
             float acc = 0.f;
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(256) void qk_generic_kernel(const T *__restrict__ q
         constexpr int H = D / 2;
         for (int idx = threadIdx.x; idx < cnt * H; idx += 256) {
             const int rr = idx / H, i = idx % H, key = key0 + rr;
-            const int pos = slot_chunk[static_cast<size_t>(bh) * k + key / c] * c + key % c;
+            const int pos = sel[static_cast<size_t>(bh) * k + key / c] * c + key % c;
             float sn, cs, y1, y2;
             angle_sincos(static_cast<double>(pos) * theta[i], &sn, &cs);
             rope_rotate(Ks[rr][i], Ks[rr][i + H], sn, cs, y1, y2);
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256) void qk_static_mfma_kernel(const uint16_t *__r
 
 // ---------------------------------------------------------------------------
 // Rebuilt keys on MFMA (bfloat16).  Per (sequence, KV head) the rebuild is
-// K[key, :] = A[pos(key), :] . B[h] with pos(key) = chunk(slot) * c + t, a
+// K[key, :] = A[pos(key), :] . B[h] with pos(key) = sel[key / c] * c + key % c, a
 // genuine rank-r x d contraction.  A workgroup takes 256 keys (4 waves x 64);
 // B[h] (stored transposed, d x r) is staged once in LDS and shared by the four
 // waves; each wave requests the gathered A rows of all four of its 16-key
@@ -259,7 +259,7 @@ template <int D, int GP, int NKB>
 __global__ __launch_bounds__(256) void qk_sparse_mfma_kernel(const uint16_t *__restrict__ q,
                                                              const uint16_t *__restrict__ A,
                                                              const uint16_t *__restrict__ Bt,
-                                                             const int32_t *__restrict__ slot_chunk,
+                                                             const int32_t *__restrict__ sel,
                                                              const double *__restrict__ theta_rev,
                                                              float *__restrict__ logits, int hkv, int G, int s,
                                                              int c, int r, int r_pad, int k, int OC, int KC, int NK,
@@ -280,13 +280,13 @@ __global__ __launch_bounds__(256) void qk_sparse_mfma_kernel(const uint16_t *__r
     const int key_base = blockIdx.x * kQkMfmaTile + wave * 64;
     const bool active = key_base < KC;  // wave-uniform
 
-    // The A side does not depend on the staged B: the chunk of every slot
-    // this wave's 64 keys touch (at most 64 slots, one load per lane, then
+    // The A side does not depend on the staged B: the chunk of every
+    // selection position this wave's 64 keys touch (at most 64, one load per lane, then
     // shuffles) and the rotation rates are requested first, and the gathered
     // A rows of all four key blocks and the queries right after B is written
     // to LDS (the staging registers are free by then), before the barrier.
-    const int slot0 = key_base / c;
-    const int my_chunk = slot_chunk[static_cast<size_t>(bh) * k + min(slot0 + lane, k - 1)];
+    const int pos0 = key_base / c;
+    const int my_chunk = sel[static_cast<size_t>(bh) * k + min(pos0 + lane, k - 1)];
     // rotation rates (turns per position) of this lane's dims 16*hb + 4*quad + e
     double thr[HB][4];
 #pragma unroll
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(256) void qk_sparse_mfma_kernel(const uint16_t *__r
         const int key = key_base + mb * 16 + row;
         const bool kv = active && key < KC;
         const int kk = key < KC ? key : key_base;
-        const int chunk = __shfl(my_chunk, kk / c - slot0, 64);
+        const int chunk = __shfl(my_chunk, kk / c - pos0, 64);
         pos[mb] = chunk * c + kk % c;
         const int base = (pos[mb] * r + quad * 8) * 2;
 #pragma unroll
@@ -420,11 +420,15 @@ __device__ __forceinline__ void unpack8(const u32x4 *raw, float *v) {
     }
 }
 
-template <typename T, int D, int GP>
+// IND: the rebuilt block's V is looked up by slot (sel_slot); otherwise
+// selection position i is cache slot i (a cache of exactly k slots, with the
+// rebuilt keys in slot order).
+template <typename T, int D, int GP, bool IND>
 __global__ __launch_bounds__(256) void pv_kernel(const float *__restrict__ logits, const T *__restrict__ v_out,
-                                                 const T *__restrict__ vc, const T *__restrict__ v_loc,
-                                                 float2 *__restrict__ part_ml, float *__restrict__ part_acc,
-                                                 int G, int OC, int KC, int w, int wcap, int NK, int tiles) {
+                                                 const T *__restrict__ vc, const int32_t *__restrict__ sel_slot,
+                                                 const T *__restrict__ v_loc, float2 *__restrict__ part_ml,
+                                                 float *__restrict__ part_acc, int G, int OC, int KC, int c, int k,
+                                                 int cap, int w, int wcap, int NK, int tiles) {
     constexpr int CG = D / 8;              // column groups of 8
     constexpr int RG = 256 / CG;           // row groups
     constexpr int RPT = kPvTile / RG;      // rows per thread
@@ -451,13 +455,26 @@ __global__ __launch_bounds__(256) void pv_kernel(const float *__restrict__ logit
 #pragma unroll
         for (int i = 0; i < kPvTile / 64; ++i) lv[hh][i] = lg[min(lane + 64 * i, cnt - 1)];
     }
-    // 2. the V rows of this thread's 8 columns
+    // 2. the V rows of this thread's 8 columns; a rebuilt key i*c + t reads
+    //    token t of cache slot sel_slot[i] (slots are looked up first, for
+    //    every row, clamped into the block so the loads stay unconditional)
+    int slot[RPT];
+    if constexpr (IND) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int key = key0 + min(rg + RG * i, cnt - 1);
+            const int p = KC > 0 ? min(max(key - OC, 0), KC - 1) : 0;
+            slot[i] = min(max(sel_slot[static_cast<size_t>(bh) * k + p / c], 0), cap - 1);  // kept in the row
+        }
+    }
     u32x4 raw[RPT][VPR];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
         const int key = key0 + min(rg + RG * i, cnt - 1);
+        const T *sparse = IND ? vc + ((static_cast<size_t>(bh) * cap + slot[i]) * c + (key - OC) % c) * D
+                              : vc + (static_cast<size_t>(bh) * KC + (key - OC)) * D;
         const T *vrow = key < OC ? v_out + (static_cast<size_t>(bh) * OC + key) * D
-                      : key < OC + KC ? vc + (static_cast<size_t>(bh) * KC + (key - OC)) * D
+                      : key < OC + KC ? sparse
                                       : v_loc + (static_cast<size_t>(bh) * wcap + (key - OC - KC)) * D;
         const u32x4 *src = reinterpret_cast<const u32x4 *>(vrow + cg * 8);
 #pragma unroll
@@ -618,7 +635,7 @@ hipError_t launch_fetch(const Dims &dm, const void *v_host, void *vc, const int2
         }
         hipLaunchKernelGGL(kern, dim3(std::max(1, (waves + 3) / 4)), dim3(256), lds, st,
                            static_cast<const u32x4 *>(v_host), static_cast<u32x4 *>(vc), misses, miss_count, rows,
-                           dm.k, dm.n, chunk_vec);
+                           dm.k, dm.cap, dm.n, chunk_vec);
         return hipGetLastError();
     };
     switch (chunk_vec) {
@@ -630,7 +647,7 @@ hipError_t launch_fetch(const Dims &dm, const void *v_host, void *vc, const int2
 }
 template <typename T, int D>
 static hipError_t qk_generic_t(const Dims &dm, const void *q, const void *k_out, const void *k_loc, const void *A,
-                               const void *Bt, const int32_t *slot_chunk, const double *theta, float *logits,
+                               const void *Bt, const int32_t *sel, const double *theta, float *logits,
                                hipStream_t st) {
     const int t_out = (dm.OC + kQkTile - 1) / kQkTile;
     const int t_sp = (dm.KC + kQkTile - 1) / kQkTile;
@@ -639,13 +656,13 @@ static hipError_t qk_generic_t(const Dims &dm, const void *q, const void *k_out,
     if (tiles == 0) return hipSuccess;
     hipLaunchKernelGGL((qk_generic_kernel<T, D>), dim3(tiles, dm.b * dm.hkv), dim3(256), 0, st,
                        static_cast<const T *>(q), static_cast<const T *>(k_out), static_cast<const T *>(k_loc),
-                       static_cast<const T *>(A), static_cast<const T *>(Bt), slot_chunk, theta, logits, dm.hkv,
+                       static_cast<const T *>(A), static_cast<const T *>(Bt), sel, theta, logits, dm.hkv,
                        dm.G, dm.s, dm.c, dm.r, dm.k, dm.OC, dm.KC, dm.w, dm.wcap, dm.NK, t_out, t_sp, dm.scale);
     return hipGetLastError();
 }
 
 template <int D, int GP, int NKB>
-static hipError_t qk_mfma_t(const Dims &dm, const void *q, const void *A, const void *Bt, const int32_t *slot_chunk,
+static hipError_t qk_mfma_t(const Dims &dm, const void *q, const void *A, const void *Bt, const int32_t *sel,
                             const double *theta_rev, float *logits, hipStream_t st) {
     if (dm.KC <= 0) return hipSuccess;
     const int r_pad = NKB * 32;
@@ -658,21 +675,21 @@ static hipError_t qk_mfma_t(const Dims &dm, const void *q, const void *A, const 
     dim3 grid((dm.KC + kQkMfmaTile - 1) / kQkMfmaTile, dm.b * dm.hkv);
     hipLaunchKernelGGL((qk_sparse_mfma_kernel<D, GP, NKB>), grid, dim3(256), lds, st,
                        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(A),
-                       static_cast<const uint16_t *>(Bt), slot_chunk, theta_rev, logits, dm.hkv, dm.G, dm.s, dm.c,
+                       static_cast<const uint16_t *>(Bt), sel, theta_rev, logits, dm.hkv, dm.G, dm.s, dm.c,
                        dm.r, r_pad, dm.k, dm.OC, dm.KC, dm.NK, dm.scale);
     return hipGetLastError();
 }
 
 // rank blocks of 32: the smallest supported count that covers the rank
 template <int D, int GP>
-static hipError_t qk_mfma_r(const Dims &dm, const void *q, const void *A, const void *Bt, const int32_t *slot_chunk,
+static hipError_t qk_mfma_r(const Dims &dm, const void *q, const void *A, const void *Bt, const int32_t *sel,
                             const double *theta_rev, float *logits, hipStream_t st) {
     const int need = (dm.r + 31) / 32;
-    if (need <= 2) return qk_mfma_t<D, GP, 2>(dm, q, A, Bt, slot_chunk, theta_rev, logits, st);
-    if (need <= 4) return qk_mfma_t<D, GP, 4>(dm, q, A, Bt, slot_chunk, theta_rev, logits, st);
-    if (need <= 5) return qk_mfma_t<D, GP, 5>(dm, q, A, Bt, slot_chunk, theta_rev, logits, st);
-    if (need <= 6) return qk_mfma_t<D, GP, 6>(dm, q, A, Bt, slot_chunk, theta_rev, logits, st);
-    return qk_mfma_t<D, GP, 8>(dm, q, A, Bt, slot_chunk, theta_rev, logits, st);
+    if (need <= 2) return qk_mfma_t<D, GP, 2>(dm, q, A, Bt, sel, theta_rev, logits, st);
+    if (need <= 4) return qk_mfma_t<D, GP, 4>(dm, q, A, Bt, sel, theta_rev, logits, st);
+    if (need <= 5) return qk_mfma_t<D, GP, 5>(dm, q, A, Bt, sel, theta_rev, logits, st);
+    if (need <= 6) return qk_mfma_t<D, GP, 6>(dm, q, A, Bt, sel, theta_rev, logits, st);
+    return qk_mfma_t<D, GP, 8>(dm, q, A, Bt, sel, theta_rev, logits, st);
 }
 
 template <int D>
@@ -689,56 +706,63 @@ static hipError_t qk_static_t(const Dims &dm, const void *q, const void *k_out, 
 
 template <int D>
 static hipError_t qk_bf16_d(const Dims &dm, const void *q, const void *k_out, const void *k_loc, const void *A,
-                            const void *Bt, const int32_t *slot_chunk, const double *theta_rev,
+                            const void *Bt, const int32_t *sel, const double *theta_rev,
                             float *logits, hipStream_t st) {
     hipError_t e = qk_static_t<D>(dm, q, k_out, k_loc, logits, st);
     if (e != hipSuccess) return e;
     switch (dm.GP) {
-        case 4: return qk_mfma_r<D, 4>(dm, q, A, Bt, slot_chunk, theta_rev, logits, st);
-        case 8: return qk_mfma_r<D, 8>(dm, q, A, Bt, slot_chunk, theta_rev, logits, st);
-        default: return qk_mfma_r<D, 16>(dm, q, A, Bt, slot_chunk, theta_rev, logits, st);
+        case 4: return qk_mfma_r<D, 4>(dm, q, A, Bt, sel, theta_rev, logits, st);
+        case 8: return qk_mfma_r<D, 8>(dm, q, A, Bt, sel, theta_rev, logits, st);
+        default: return qk_mfma_r<D, 16>(dm, q, A, Bt, sel, theta_rev, logits, st);
     }
 }
 
 hipError_t launch_qk(const Dims &dm, const void *q, const void *k_out, const void *k_loc, const void *A,
-                     const void *Bt, const int32_t *slot_chunk, const double *theta, const double *theta_rev,
+                     const void *Bt, const int32_t *sel, const double *theta, const double *theta_rev,
                      float *logits, hipStream_t st) {
     if (dm.bf16 && dm.r % 8 == 0)
-        return dm.d == 128 ? qk_bf16_d<128>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta_rev, logits, st)
-                           : qk_bf16_d<64>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta_rev, logits, st);
+        return dm.d == 128 ? qk_bf16_d<128>(dm, q, k_out, k_loc, A, Bt, sel, theta_rev, logits, st)
+                           : qk_bf16_d<64>(dm, q, k_out, k_loc, A, Bt, sel, theta_rev, logits, st);
     if (dm.bf16)
-        return dm.d == 128 ? qk_generic_t<uint16_t, 128>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta, logits, st)
-                           : qk_generic_t<uint16_t, 64>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta, logits, st);
-    return dm.d == 128 ? qk_generic_t<float, 128>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta, logits, st)
-                       : qk_generic_t<float, 64>(dm, q, k_out, k_loc, A, Bt, slot_chunk, theta, logits, st);
+        return dm.d == 128 ? qk_generic_t<uint16_t, 128>(dm, q, k_out, k_loc, A, Bt, sel, theta, logits, st)
+                           : qk_generic_t<uint16_t, 64>(dm, q, k_out, k_loc, A, Bt, sel, theta, logits, st);
+    return dm.d == 128 ? qk_generic_t<float, 128>(dm, q, k_out, k_loc, A, Bt, sel, theta, logits, st)
+                       : qk_generic_t<float, 64>(dm, q, k_out, k_loc, A, Bt, sel, theta, logits, st);
 }
 
 template <typename T, int D, int GP>
-static hipError_t pv_t(const Dims &dm, const float *logits, const void *v_out, const void *vc, const void *v_loc,
-                       float2 *part_ml, float *part_acc, hipStream_t st) {
-    hipLaunchKernelGGL((pv_kernel<T, D, GP>), dim3(dm.pv_tiles, dm.b * dm.hkv), dim3(256), 0, st, logits,
-                       static_cast<const T *>(v_out), static_cast<const T *>(vc), static_cast<const T *>(v_loc),
-                       part_ml, part_acc, dm.G, dm.OC, dm.KC, dm.w, dm.wcap, dm.NK, dm.pv_tiles);
+static hipError_t pv_t(const Dims &dm, const float *logits, const void *v_out, const void *vc,
+                       const int32_t *sel_slot, const void *v_loc, float2 *part_ml, float *part_acc,
+                       hipStream_t st) {
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3(dm.pv_tiles, dm.b * dm.hkv), dim3(256), 0, st, logits,
+                           static_cast<const T *>(v_out), static_cast<const T *>(vc), sel_slot,
+                           static_cast<const T *>(v_loc), part_ml, part_acc, dm.G, dm.OC, dm.KC, dm.c, dm.k, dm.cap,
+                           dm.w, dm.wcap, dm.NK, dm.pv_tiles);
+    };
+    if (sel_slot) go(pv_kernel<T, D, GP, true>);
+    else go(pv_kernel<T, D, GP, false>);
     return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t pv_d(const Dims &dm, const float *logits, const void *v_out, const void *vc, const void *v_loc,
-                       float2 *part_ml, float *part_acc, hipStream_t st) {
+static hipError_t pv_d(const Dims &dm, const float *logits, const void *v_out, const void *vc,
+                       const int32_t *sel_slot, const void *v_loc, float2 *part_ml, float *part_acc,
+                       hipStream_t st) {
     switch (dm.GP) {
-        case 4: return pv_t<T, D, 4>(dm, logits, v_out, vc, v_loc, part_ml, part_acc, st);
-        case 8: return pv_t<T, D, 8>(dm, logits, v_out, vc, v_loc, part_ml, part_acc, st);
-        default: return pv_t<T, D, 16>(dm, logits, v_out, vc, v_loc, part_ml, part_acc, st);
+        case 4: return pv_t<T, D, 4>(dm, logits, v_out, vc, sel_slot, v_loc, part_ml, part_acc, st);
+        case 8: return pv_t<T, D, 8>(dm, logits, v_out, vc, sel_slot, v_loc, part_ml, part_acc, st);
+        default: return pv_t<T, D, 16>(dm, logits, v_out, vc, sel_slot, v_loc, part_ml, part_acc, st);
     }
 }
 
-hipError_t launch_pv(const Dims &dm, const float *logits, const void *v_out, const void *vc, const void *v_loc,
-                     float2 *part_ml, float *part_acc, hipStream_t st) {
+hipError_t launch_pv(const Dims &dm, const float *logits, const void *v_out, const void *vc, const int32_t *sel_slot,
+                     const void *v_loc, float2 *part_ml, float *part_acc, hipStream_t st) {
     if (dm.bf16)
-        return dm.d == 128 ? pv_d<uint16_t, 128>(dm, logits, v_out, vc, v_loc, part_ml, part_acc, st)
-                           : pv_d<uint16_t, 64>(dm, logits, v_out, vc, v_loc, part_ml, part_acc, st);
-    return dm.d == 128 ? pv_d<float, 128>(dm, logits, v_out, vc, v_loc, part_ml, part_acc, st)
-                       : pv_d<float, 64>(dm, logits, v_out, vc, v_loc, part_ml, part_acc, st);
+        return dm.d == 128 ? pv_d<uint16_t, 128>(dm, logits, v_out, vc, sel_slot, v_loc, part_ml, part_acc, st)
+                           : pv_d<uint16_t, 64>(dm, logits, v_out, vc, sel_slot, v_loc, part_ml, part_acc, st);
+    return dm.d == 128 ? pv_d<float, 128>(dm, logits, v_out, vc, sel_slot, v_loc, part_ml, part_acc, st)
+                       : pv_d<float, 64>(dm, logits, v_out, vc, sel_slot, v_loc, part_ml, part_acc, st);
 }
 
 hipError_t launch_combine(const Dims &dm, const float2 *part_ml, const float *part_acc, void *out, hipStream_t st) {

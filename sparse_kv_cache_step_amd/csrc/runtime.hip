@@ -53,6 +53,9 @@ int make_dims(const skv_config &c, Dims *dm, std::string *why) {
     if (c.rank < 1 || c.rank > 256) return bad("rank must be in [1, 256]");
     if (!(c.rope_base > 0.f)) return bad("rope_base must be > 0");
     if (c.max_new < 0 || c.max_new > (1 << 20)) return bad("max_new must be in [0, 2^20]");
+    if (c.cache_chunks != 0 && (c.cache_chunks < c.top_k || c.cache_chunks > n - n_loc - c.n_outlier))
+        return bad("cache_chunks must be 0 or in [top_k, n - n_loc - n_outlier]");
+    if (c.cache_chunks > 16384) return bad("cache_chunks must be <= 16384");
     const long long nk = 1LL * c.n_outlier * c.chunk + 1LL * c.top_k * c.chunk + c.local_window;
     if (nk < 1) return bad("at least one key must be attended");
     const long long seq_elems = 1LL * c.batch * c.heads_kv * c.seq_len * c.head_dim;
@@ -69,6 +72,7 @@ int make_dims(const skv_config &c, Dims *dm, std::string *why) {
     Dims &d = *dm;
     d.b = c.batch; d.hq = c.heads_q; d.hkv = c.heads_kv; d.d = c.head_dim; d.s = c.seq_len; d.c = c.chunk;
     d.r = c.rank; d.o = c.n_outlier; d.k = c.top_k; d.w = c.local_window;
+    d.cap = c.cache_chunks > 0 ? c.cache_chunks : c.top_k;
     d.wcap = c.local_window + c.max_new;
     d.n = n; d.n_loc = n_loc; d.G = c.heads_q / c.heads_kv;
     d.GP = d.G <= 4 ? 4 : (d.G <= 8 ? 8 : 16);
@@ -174,7 +178,10 @@ struct skv_layer {
     double *theta_rev = nullptr;  // theta_i / (2 pi): turns per position
     // resident V cache
     void *vc = nullptr;
-    int32_t *slot_chunk = nullptr;
+    int32_t *slot_chunk = nullptr;   // (b, h_kv, cap): chunk held by each cache slot, -1 empty
+    uint32_t *slot_stamp = nullptr;  // (b, h_kv, cap): stamp of the slot chunk's last selection
+    int32_t *sel_slot = nullptr;     // (b, h_kv, k): cache slot of each selected chunk
+    uint32_t stamp = 0;              // selections made (stamps of the cache's LRU order)
     // per-step scratch
     int32_t *sel = nullptr;
     float *P = nullptr, *S2 = nullptr, *logits = nullptr, *part_acc = nullptr;
@@ -350,9 +357,11 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     ALLOC(v_out, bh * dm.OC * D * E);
     ALLOC(k_loc, bh * dm.wcap * D * E);
     ALLOC(v_loc, bh * dm.wcap * D * E);
-    ALLOC(vc, bh * dm.KC * D * E);
-    ALLOC(slot_chunk, bh * dm.k * 4);
+    ALLOC(vc, bh * dm.cap * dm.c * D * E);
+    ALLOC(slot_chunk, bh * dm.cap * 4);
+    ALLOC(slot_stamp, bh * dm.cap * 4);
     ALLOC(sel, bh * dm.k * 4);
+    ALLOC(sel_slot, bh * dm.k * 4);
     // U and the tile statistics hold up to kMaxGroup scored rows per KV head
     // (the SnapKV-style selection scores (head, window position) rows)
     ALLOC(P, bh * skv::kMaxGroup * dm.n * 4);
@@ -391,7 +400,8 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
         hipMemcpy(ly->theta_rev, thr.data(), thr.size() * sizeof(double), hipMemcpyHostToDevice) != hipSuccess ||
         hipMemset(ly->counters, 0, 4 * sizeof(unsigned long long)) != hipSuccess ||
         (dm.wcap > 0 && (hipMemset(ly->k_loc, 0, bh * dm.wcap * D * E) != hipSuccess ||
-                         hipMemset(ly->v_loc, 0, bh * dm.wcap * D * E) != hipSuccess)))
+                         hipMemset(ly->v_loc, 0, bh * dm.wcap * D * E) != hipSuccess)) ||
+        (dm.cap > 0 && hipMemset(ly->vc, 0, bh * dm.cap * dm.c * D * E) != hipSuccess))
         return bail(fail(SKV_E_HIP, "initialising layer tables failed"));
     DevStreams *ds = nullptr;
     if ((rc = device_streams(ly->device, &ds))) return bail(rc);
@@ -423,7 +433,7 @@ static int install_common(skv_layer *ly, const void *A, const void *B, void *v_h
     SKV_HIP(hipMemcpyAsync(ly->A, A, static_cast<size_t>(dm.b) * dm.s * dm.r * dm.esize, hipMemcpyDefault, st));
     SKV_HIP(skv::launch_transpose_b(dm, B, ly->Bt, st));
     SKV_HIP(skv::launch_cand_mask(dm, ly->outliers, ly->cand, st));
-    SKV_HIP(skv::launch_fill_i32(ly->slot_chunk, -1, static_cast<size_t>(dm.b) * dm.hkv * dm.k, st));
+    SKV_HIP(skv::launch_fill_i32(ly->slot_chunk, -1, static_cast<size_t>(dm.b) * dm.hkv * dm.cap, st));
     ly->fixed = ly->fetch_pending = false;
     (void)v_host;
     return SKV_OK;
@@ -534,8 +544,9 @@ int shadowkv_snapkv_select(skv_layer *ly, const void *q_obs, int w_obs, int pool
         SKV_HIP(skv::launch_snap_accum(dm, ly->S2, ly->snap_acc, static_cast<float>(dv.G), o0 == 0, st));
     }
     SKV_HIP(skv::launch_snap_pool(dm, ly->snap_acc, ly->cand, ly->S2, ly->keys, ly->kbounds, pool, st));
-    SKV_HIP(skv::launch_select(dm, ly->keys, ly->kbounds, ly->sel, ly->slot_chunk, ly->misses, ly->miss_count,
-                               ly->counters, ly->select_keys_in_lds, st));
+    SKV_HIP(skv::launch_select(dm, ly->keys, ly->kbounds, ly->sel, ly->sel_slot, ly->slot_chunk,
+                               ly->slot_stamp, ++ly->stamp, ly->misses, ly->miss_count, ly->counters,
+                               ly->select_keys_in_lds, st));
     ly->fixed = true;
     ly->fetch_pending = true;
     return SKV_OK;
@@ -547,6 +558,13 @@ int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) 
     if (!ly->ready) return fail(SKV_E_STATE, "decode_step before prefill_meta / load_meta");
     hipStream_t st = static_cast<hipStream_t>(stream);
     const Dims dm = dims_with_local(ly->dm, ly->dm.w + ly->n_app);
+    // with exactly k cache slots the slots hold the selection: the rebuilt
+    // keys go in slot order and PV reads the cache contiguously; a larger
+    // cache holds other chunks too, so the keys go in selection order and PV
+    // looks up each chunk's slot
+    const bool by_slot = dm.cap == dm.k;
+    const int32_t *qk_chunks = by_slot ? ly->slot_chunk : ly->sel;
+    const int32_t *pv_slots = by_slot ? nullptr : ly->sel_slot;
     // a fixed (SnapKV-style) selection skips scoring and selection, and
     // fetches only once, on the first step after it was made
     const bool select = !ly->fixed, fetch = select || ly->fetch_pending;
@@ -559,8 +577,9 @@ int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) 
         {
             Timed t(ly, SKV_K_SELECT, st);
             SKV_HIP(skv::launch_group(dm, ly->P, ly->stats, ly->cand, ly->S2, ly->keys, ly->kbounds, st));
-            SKV_HIP(skv::launch_select(dm, ly->keys, ly->kbounds, ly->sel, ly->slot_chunk, ly->misses,
-                                       ly->miss_count, ly->counters, ly->select_keys_in_lds, st));
+            SKV_HIP(skv::launch_select(dm, ly->keys, ly->kbounds, ly->sel, ly->sel_slot, ly->slot_chunk,
+                                       ly->slot_stamp, ++ly->stamp, ly->misses, ly->miss_count, ly->counters,
+                                       ly->select_keys_in_lds, st));
         }
     }
     if (ly->overlap) {
@@ -577,7 +596,7 @@ int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) 
         SKV_HIP(hipEventRecord(ly->ev_fetch, ly->copy));
         {
             Timed t(ly, SKV_K_QK, ly->comp);
-            SKV_HIP(skv::launch_qk(dm, q, ly->k_out, ly->k_loc, ly->A, ly->Bt, ly->slot_chunk, ly->theta,
+            SKV_HIP(skv::launch_qk(dm, q, ly->k_out, ly->k_loc, ly->A, ly->Bt, qk_chunks, ly->theta,
                                    ly->theta_rev, ly->logits, ly->comp));
         }
         SKV_HIP(hipEventRecord(ly->ev_qk, ly->comp));
@@ -592,14 +611,15 @@ int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) 
         }
         {
             Timed t(ly, SKV_K_QK, st);
-            SKV_HIP(skv::launch_qk(dm, q, ly->k_out, ly->k_loc, ly->A, ly->Bt, ly->slot_chunk, ly->theta,
+            SKV_HIP(skv::launch_qk(dm, q, ly->k_out, ly->k_loc, ly->A, ly->Bt, qk_chunks, ly->theta,
                                    ly->theta_rev, ly->logits, st));
         }
     }
     ly->fetch_pending = false;
     {
         Timed t(ly, SKV_K_PV, st);
-        SKV_HIP(skv::launch_pv(dm, ly->logits, ly->v_out, ly->vc, ly->v_loc, ly->part_ml, ly->part_acc, st));
+        SKV_HIP(skv::launch_pv(dm, ly->logits, ly->v_out, ly->vc, pv_slots, ly->v_loc, ly->part_ml,
+                               ly->part_acc, st));
         SKV_HIP(skv::launch_combine(dm, ly->part_ml, ly->part_acc, out, st));
     }
     if (ly->timing) ++ly->timed_steps;
@@ -610,7 +630,7 @@ int shadowkv_reset_cache(skv_layer *ly, void *stream) {
     if (!ly) return fail(SKV_E_INVAL, "layer is null");
     hipStream_t st = static_cast<hipStream_t>(stream);
     SKV_HIP(hipStreamWaitEvent(st, ly->ev_fetch, 0));
-    SKV_HIP(skv::launch_fill_i32(ly->slot_chunk, -1, static_cast<size_t>(ly->dm.b) * ly->dm.hkv * ly->dm.k, st));
+    SKV_HIP(skv::launch_fill_i32(ly->slot_chunk, -1, static_cast<size_t>(ly->dm.b) * ly->dm.hkv * ly->dm.cap, st));
     ly->fixed = ly->fetch_pending = false;
     return SKV_OK;
 }
@@ -645,8 +665,9 @@ static const void *tensor_ptr(const skv_layer *ly, int which, size_t *bytes) {
         case SKV_T_SCORES: *bytes = bh * dm.n * dm.G * 4; return ly->P;
         case SKV_T_GROUP_SCORES: *bytes = bh * dm.n * 4; return ly->S2;
         case SKV_T_SELECTION: *bytes = bh * dm.k * 4; return ly->sel;
-        case SKV_T_SLOT_CHUNKS: *bytes = bh * dm.k * 4; return ly->slot_chunk;
-        case SKV_T_CACHE_V: *bytes = bh * dm.KC * D * E; return ly->vc;
+        case SKV_T_SLOT_CHUNKS: *bytes = bh * dm.cap * 4; return ly->slot_chunk;
+        case SKV_T_CACHE_V: *bytes = bh * dm.cap * dm.c * D * E; return ly->vc;
+        case SKV_T_SELECTION_SLOTS: *bytes = bh * dm.k * 4; return ly->sel_slot;
         case SKV_T_K_OUT: *bytes = bh * dm.OC * D * E; return ly->k_out;
         case SKV_T_V_OUT: *bytes = bh * dm.OC * D * E; return ly->v_out;
         case SKV_T_K_LOC: *bytes = bh * dm.wcap * D * E; return ly->k_loc;

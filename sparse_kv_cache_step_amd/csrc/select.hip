@@ -313,9 +313,15 @@ __device__ __forceinline__ void block_minmax(uint32_t &mn, uint32_t &mx, SelectS
 // (ballots and popcounts) writes the indices.  Requires blockDim.x == 1024
 // (four bins per thread) and 1 <= k; every thread of the block must call it;
 // sc.hist must be zero on entry and is zero again on return.
-__device__ void radix_topk(const uint32_t *keys, int n, int k, uint32_t kmin, uint32_t kmax, int32_t *out,
-                           int32_t *lds_out, SelectScratch &sc) {
-    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
+struct RadixCut {
+    uint32_t thr;  // the k-th largest key
+    int need_eq;   // keys equal to thr among the k largest
+};
+
+// The threshold passes of radix_topk alone: the k-th largest key and how many
+// keys equal to it the k largest take.
+__device__ RadixCut radix_cut(const uint32_t *keys, int n, int k, uint32_t kmin, uint32_t kmax, SelectScratch &sc) {
+    const int tid = threadIdx.x, nt = blockDim.x;
     const uint32_t range = kmax - kmin;
     int hi = range == 0 ? 0 : 32 - __clz(static_cast<int>(range));  // bits of the offsets
     uint64_t prefix = 0;  // offset bits fixed so far (above hi)
@@ -363,8 +369,15 @@ __device__ void radix_topk(const uint32_t *keys, int n, int k, uint32_t kmin, ui
         krem -= sc.above;
         hi = lo;
     }
-    const uint32_t thr = kmin + static_cast<uint32_t>(prefix);
-    const int need_eq = krem;  // keys equal to thr that are taken, lowest index first
+    return RadixCut{kmin + static_cast<uint32_t>(prefix), krem};
+}
+
+__device__ void radix_topk(const uint32_t *keys, int n, int k, uint32_t kmin, uint32_t kmax, int32_t *out,
+                           int32_t *lds_out, SelectScratch &sc) {
+    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
+    const RadixCut cut = radix_cut(keys, n, k, kmin, kmax, sc);
+    const uint32_t thr = cut.thr;
+    const int need_eq = cut.need_eq;  // keys equal to thr that are taken, lowest index first
 
     // ordered compaction: wave w owns keys [w * seg, (w + 1) * seg)
     const int seg = ((n + nw - 1) / nw + 63) & ~63;
@@ -553,25 +566,33 @@ __global__ __launch_bounds__(256) void group_kernel(const float *__restrict__ U,
 //  1. the row's keys (from the group kernel) into LDS when they fit, and
 //     their bounds from the per-slice minima and maxima;
 //  2. I = ArgTopK(S2, k) by radix selection, ascending;
-//  3. set difference against the resident chunks: a slot keeps its chunk when
-//     the chunk is selected again (hit); the m-th missing chunk (ascending)
-//     goes to the m-th freed slot (ascending); emit the miss list and count
-//     hits and misses.
+//  3. cache update over the row's cap slots: a slot whose chunk is selected
+//     again is a hit (its stamp becomes this step's); of the resident chunks
+//     not selected, the E oldest (smallest stamp; equal stamps: higher chunk
+//     index first) are evicted, E = max(0, misses - empty slots), so that the
+//     cache keeps the selection and, in what room is left, the chunks
+//     selected most recently -- with cap = k, every unselected chunk;
+//  4. the m-th missing chunk (ascending) goes to the m-th free slot
+//     (ascending, empty or evicted); emit the miss list, each selected
+//     chunk's slot, and count hits and misses.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(
     const uint32_t *__restrict__ keys_g, const uint2 *__restrict__ kbounds, int slices, int32_t *__restrict__ sel,
-    int32_t *__restrict__ slot_chunk, int2 *__restrict__ misses, int32_t *__restrict__ miss_count,
-    unsigned long long *__restrict__ counters, int use_lds, int n, int k) {
-    extern __shared__ uint32_t dyn[];
+    int32_t *__restrict__ sel_slot, int32_t *__restrict__ slot_chunk, uint32_t *__restrict__ slot_stamp,
+    uint32_t stamp, int2 *__restrict__ misses, int32_t *__restrict__ miss_count,
+    unsigned long long *__restrict__ counters, int use_lds, int n, int k, int cap) {
+    extern __shared__ __align__(16) uint32_t dyn[];
     __shared__ SelectScratch sc;
     const int tid = threadIdx.x, nt = blockDim.x;
     const int bh = blockIdx.x;
-    int32_t *s_sel = reinterpret_cast<int32_t *>(dyn);  // k selected chunks, ascending
-    int32_t *s_keep = s_sel + k;                        // k: chunk kept by each slot, -1 if freed
-    int32_t *s_hit = s_keep + k;                        // k: 1 if selected chunk i is resident
-    int32_t *s_rank = s_hit + k;                        // k: index in s_sel of the m-th miss
+    // dynamic LDS: the row's keys first (16-byte aligned), when they fit
     const uint32_t *krow = keys_g + static_cast<size_t>(bh) * n;
-    uint32_t *keys = use_lds ? reinterpret_cast<uint32_t *>(s_rank + k) : const_cast<uint32_t *>(krow);
+    uint32_t *keys = use_lds ? dyn : const_cast<uint32_t *>(krow);
+    int32_t *s_sel = reinterpret_cast<int32_t *>(dyn + (use_lds ? n : 0));  // k selected chunks, ascending
+    int32_t *s_sslot = s_sel + k;                       // k: slot of selected chunk i (-1: missing)
+    int32_t *s_rank = s_sslot + k;                      // k: index in s_sel of the m-th miss
+    uint32_t *s_age = reinterpret_cast<uint32_t *>(s_rank + k);  // cap: eviction key (0: not evictable)
+    int32_t *s_free = reinterpret_cast<int32_t *>(s_age + cap);  // cap: rank of a free slot, -1 otherwise
 
     if (use_lds) {
         // 16-byte loads, four per thread in flight (16384 keys per batch)
@@ -593,7 +614,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
         for (int j = 4 * nv + tid; j < n; j += nt) keys[j] = krow[j];
     }
     for (int i = tid; i < 4096; i += nt) sc.hist[i] = 0;
-    for (int i = tid; i < k; i += nt) s_hit[i] = 0;
+    for (int i = tid; i < k; i += nt) s_sslot[i] = -1;
     uint32_t kmn = 0xffffffffu, kmx = 0u;
     for (int i = tid; i < slices; i += nt) {
         const uint2 b2 = kbounds[static_cast<size_t>(bh) * slices + i];
@@ -605,50 +626,105 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
     radix_topk(keys, n, k, kmn, kmx, sel + static_cast<size_t>(bh) * k, s_sel, sc);
     __syncthreads();
 
-    // set difference: a slot keeps its chunk if the chunk is selected again
-    int32_t *gc = slot_chunk + static_cast<size_t>(bh) * k;
-    for (int sl = tid; sl < k; sl += nt) {
+    // hits, and the age (stamp distance, >= 1) of every resident chunk that
+    // is not selected again
+    int32_t *gc = slot_chunk + static_cast<size_t>(bh) * cap;
+    uint32_t *gs = slot_stamp + static_cast<size_t>(bh) * cap;
+    int nres = 0, nhit = 0;
+    uint32_t amn = 0xffffffffu, amx = 0u;
+    for (int sl = tid; sl < cap; sl += nt) {
         const int32_t c = gc[sl];
-        int keep = -1;
+        uint32_t age = 0;
         if (c >= 0) {
+            ++nres;
             int lo = 0, hi = k;
             while (lo < hi) {
                 const int mid = (lo + hi) >> 1;
                 if (s_sel[mid] < c) lo = mid + 1; else hi = mid;
             }
-            if (lo < k && s_sel[lo] == c) { keep = c; s_hit[lo] = 1; }
-        }
-        s_keep[sl] = keep;
-    }
-    __syncthreads();
-    // ascending ranks of the misses (over selection positions) and of the
-    // freed slots (over slot indices), one scan for both
-    int nmiss = 0, nfree = 0;
-    for (int i0 = 0; i0 < k; i0 += nt) {
-        const int i = i0 + tid;
-        const int miss = (i < k && !s_hit[i]) ? 1 : 0;
-        const int fr = (i < k && s_keep[i] < 0) ? 1 : 0;
-        int mi = miss, fi = fr, tm, tf;
-        block_scan2(mi, fi, sc, &tm, &tf);
-        if (miss) s_rank[nmiss + mi - 1] = i;
-        if (fr) s_keep[i] = -2 - (nfree + fi - 1);  // freed slot: -2 - its rank
-        nmiss += tm;
-        nfree += tf;
-    }
-    __syncthreads();
-    // the m-th missing chunk goes to the m-th freed slot
-    int2 *ml = misses + static_cast<size_t>(bh) * k;
-    for (int sl = tid; sl < k; sl += nt) {
-        const int kv = s_keep[sl];
-        if (kv <= -2) {
-            const int r = -2 - kv;
-            if (r < nmiss) {  // freed slots and misses are equal in number
-                const int32_t chunk = s_sel[s_rank[r]];
-                gc[sl] = chunk;
-                ml[r] = make_int2(chunk, sl);
+            if (lo < k && s_sel[lo] == c) {
+                s_sslot[lo] = sl;
+                gs[sl] = stamp;
+                ++nhit;
+            } else {
+                age = stamp - gs[sl];
+                amn = min(amn, age);
+                amx = max(amx, age);
             }
         }
+        s_age[sl] = age;
     }
+    int tres, thit;
+    block_scan2(nres, nhit, sc, &tres, &thit);  // its barriers also publish s_age and s_sslot
+    const int nmiss = k - thit, nempty = cap - tres, ncand = tres - thit;
+    const int evict = max(0, nmiss - nempty);
+    // the evicted slots: ages above cut1, and of those equal to cut1 the
+    // need_eq with the highest chunk index (keys chunk + 1 >= cut2)
+    uint32_t cut1 = 1u, cut2 = 0u;
+    bool tie_split = false;
+    if (evict == 0) {
+        cut1 = 0xffffffffu;  // no age exceeds it; equal ages not taken (cut2 above every key)
+        cut2 = 0xffffffffu;
+        tie_split = true;
+    } else if (evict < ncand) {  // only with more slots than k
+        block_minmax(amn, amx, sc);
+        const RadixCut c1 = radix_cut(s_age, cap, evict, amn, amx, sc);
+        cut1 = c1.thr;
+        int eq = 0, dummy = 0, teq, td;
+        for (int sl = tid; sl < cap; sl += nt) eq += s_age[sl] == cut1 ? 1 : 0;
+        block_scan2(eq, dummy, sc, &teq, &td);
+        if (c1.need_eq < teq) {
+            // equal ages: keys chunk + 1 in s_free, the need_eq largest go
+            for (int sl = tid; sl < cap; sl += nt)
+                s_free[sl] = s_age[sl] == cut1 ? gc[sl] + 1 : 0;
+            __syncthreads();
+            cut2 = radix_cut(reinterpret_cast<const uint32_t *>(s_free), cap, c1.need_eq, 1u,
+                             static_cast<uint32_t>(n), sc).thr;
+            tie_split = true;
+        }
+        // else every slot of age cut1 goes: cut1 alone decides
+    }
+    // else every resident unselected chunk goes (cut1 = 1, no tie split)
+    __syncthreads();
+
+    // ascending ranks of the misses (over selection positions) and of the
+    // free slots (over slot indices), one scan for both
+    int rmiss = 0, rfree = 0;
+    const int span = max(k, cap);
+    for (int i0 = 0; i0 < span; i0 += nt) {
+        const int i = i0 + tid;
+        const int miss = (i < k && s_sslot[i] < 0) ? 1 : 0;
+        bool fr = false;
+        if (i < cap) {
+            const uint32_t a = s_age[i];
+            const bool empty = gc[i] < 0;
+            const bool gone = a != 0 && (a > cut1 || (a == cut1 && (!tie_split ||
+                                                      static_cast<uint32_t>(gc[i] + 1) >= cut2)));
+            fr = empty || gone;
+        }
+        int mi = miss, fi = fr ? 1 : 0, tm, tf;
+        block_scan2(mi, fi, sc, &tm, &tf);
+        if (miss) s_rank[rmiss + mi - 1] = i;
+        if (i < cap) s_free[i] = fr ? rfree + fi - 1 : -1;
+        rmiss += tm;
+        rfree += tf;
+    }
+    __syncthreads();
+    // the m-th missing chunk goes to the m-th free slot
+    int2 *ml = misses + static_cast<size_t>(bh) * k;
+    for (int sl = tid; sl < cap; sl += nt) {
+        const int r = s_free[sl];
+        if (r >= 0 && r < nmiss) {  // free slots number at least the misses
+            const int i = s_rank[r];
+            const int32_t chunk = s_sel[i];
+            gc[sl] = chunk;
+            gs[sl] = stamp;
+            s_sslot[i] = sl;
+            ml[r] = make_int2(chunk, sl);
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < k; i += nt) sel_slot[static_cast<size_t>(bh) * k + i] = s_sslot[i];
     if (tid == 0) {
         miss_count[bh] = nmiss;
         atomicAdd(&counters[0], static_cast<unsigned long long>(k - nmiss));
@@ -766,7 +842,8 @@ hipError_t launch_score(const Dims &dm, const void *q, const void *landmarks, co
 }
 
 size_t select_dynamic_lds(const Dims &dm, bool keys_in_lds) {
-    return 4ull * dm.k * sizeof(int32_t) + (keys_in_lds ? static_cast<size_t>(dm.n) * sizeof(uint32_t) : 0);
+    return (3ull * dm.k + 2ull * dm.cap) * sizeof(int32_t) +
+           (keys_in_lds ? static_cast<size_t>(dm.n) * sizeof(uint32_t) : 0);
 }
 
 size_t select_static_lds() { return sizeof(SelectScratch); }
@@ -790,13 +867,16 @@ hipError_t launch_group(const Dims &dm, const float *P, const float2 *stats, con
 }
 
 hipError_t launch_select(const Dims &dm, const uint32_t *keys, const uint2 *kbounds, int32_t *sel,
-                         int32_t *slot_chunk, int2 *misses, int32_t *miss_count, unsigned long long *counters,
-                         int keys_in_lds, hipStream_t st) {
+                         int32_t *sel_slot, int32_t *slot_chunk, uint32_t *slot_stamp, uint32_t stamp,
+                         int2 *misses, int32_t *miss_count, unsigned long long *counters, int keys_in_lds,
+                         hipStream_t st) {
+    if (dm.k > 0 && dm.cap < dm.k) return hipErrorInvalidValue;
     const size_t lds = select_dynamic_lds(dm, keys_in_lds != 0);
     hipError_t e = allow_lds(reinterpret_cast<const void *>(select_kernel), lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(select_kernel, dim3(dm.b * dm.hkv), dim3(kSelectThreads), lds, st, keys, kbounds,
-                       group_slices(dm), sel, slot_chunk, misses, miss_count, counters, keys_in_lds, dm.n, dm.k);
+                       group_slices(dm), sel, sel_slot, slot_chunk, slot_stamp, stamp, misses, miss_count, counters,
+                       keys_in_lds, dm.n, dm.k, dm.cap);
     return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@ constexpr int kMaxGroup = 16;     // query heads per KV head
 
 struct Dims {
     int b, hq, hkv, d, s, c, r, o, k;
+    int cap;         // V cache slots (chunks) per (sequence, KV head), >= k
     int w;           // local keys attended: the window, plus the tokens appended so far
     int wcap;        // rows of the local K/V buffers: window + append capacity
     int n;           // chunks per sequence
@@ -74,9 +75,14 @@ hipError_t launch_group(const Dims &dm, const float *P, const float2 *stats, con
 // fit) and static part.
 size_t select_dynamic_lds(const Dims &dm, bool keys_in_lds);
 size_t select_static_lds();
+// Selection and cache update: sel (b, h_kv, k) ascending chunks, sel_slot
+// (b, h_kv, k) the cache slot of each; slot_chunk / slot_stamp (b, h_kv, cap)
+// the chunk each slot holds (-1: empty) and the stamp of its last selection;
+// `stamp` is this selection's (one more than the previous selection's).
 hipError_t launch_select(const Dims &dm, const uint32_t *keys, const uint2 *kbounds, int32_t *sel,
-                         int32_t *slot_chunk, int2 *misses, int32_t *miss_count, unsigned long long *counters,
-                         int keys_in_lds, hipStream_t st);
+                         int32_t *sel_slot, int32_t *slot_chunk, uint32_t *slot_stamp, uint32_t stamp,
+                         int2 *misses, int32_t *miss_count, unsigned long long *counters, int keys_in_lds,
+                         hipStream_t st);
 // SnapKV-style selection: accumulate a pass's summed attention, then pool
 // it into S2, selection keys and slice bounds.
 hipError_t launch_snap_accum(const Dims &dm, const float *S2, float *acc, float weight, int first, hipStream_t st);
@@ -84,10 +90,13 @@ hipError_t launch_snap_pool(const Dims &dm, const float *acc, const uint32_t *ca
                             uint2 *kbounds, int pool, hipStream_t st);
 hipError_t launch_fetch(const Dims &dm, const void *v_host, void *vc, const int2 *misses,
                         const int32_t *miss_count, int waves, hipStream_t st);
+// The rebuilt block's key i*c + t is token t of chunk chunks[i]; its value
+// is in cache slot sel_slot[i], or slot i when sel_slot is null (a cache of
+// exactly k slots, chunks = the slots' chunks).
 hipError_t launch_qk(const Dims &dm, const void *q, const void *k_out, const void *k_loc, const void *A,
-                     const void *Bt, const int32_t *slot_chunk, const double *theta, const double *theta_rev,
+                     const void *Bt, const int32_t *chunks, const double *theta, const double *theta_rev,
                      float *logits, hipStream_t st);
-hipError_t launch_pv(const Dims &dm, const float *logits, const void *v_out, const void *vc,
+hipError_t launch_pv(const Dims &dm, const float *logits, const void *v_out, const void *vc, const int32_t *sel_slot,
                      const void *v_loc, float2 *part_ml, float *part_acc, hipStream_t st);
 hipError_t launch_combine(const Dims &dm, const float2 *part_ml, const float *part_acc, void *out,
                           hipStream_t st);

@@ -39,6 +39,17 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name)
 
 
+def test_config_struct_matches_the_header():
+    """The binding's skv_config fields are the header's, in order, with the
+    same widths."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    body = re.search(r"typedef struct \{([^}]*)\} skv_config;", text).group(1)
+    fields = re.findall(r"\b(int32_t|float)\s+(\w+);", body)
+    ctype = {"int32_t": "c_int", "float": "c_float"}
+    got = [(name, t.__name__) for name, t in skv.skv_config._fields_]
+    assert got == [(name, ctype[t]) for t, name in fields]
+
+
 def test_equiv_bandwidth_closed_form(lib):
     bw = skv.shadowkv_equiv_bandwidth(131072, 8, 256, 48, 0.6, 2e12, 31.5e9)
     assert round(bw / 1e12, 1) == 7.2
@@ -65,6 +76,10 @@ def _cfg(**kw):
     (dict(chunk=65, seq_len=65 * 16, local_window=0), skv.SKV_E_SHAPE),
     (dict(n_outlier=0, top_k=0, local_window=0), skv.SKV_E_SHAPE),  # nothing to attend
     (dict(rope_base=0.0), skv.SKV_E_SHAPE),
+    (dict(cache_chunks=7), skv.SKV_E_SHAPE),                # below top_k
+    (dict(cache_chunks=-1), skv.SKV_E_SHAPE),
+    (dict(cache_chunks=121), skv.SKV_E_SHAPE),              # > n - n_loc - o selectable chunks
+    (dict(max_new=-1), skv.SKV_E_SHAPE),
 ])
 def test_invalid_sizes_are_rejected_before_the_device(lib, kw, code):
     with pytest.raises(skv.ShadowKVError) as e:

@@ -100,14 +100,23 @@ def expected_u(P):
     return U
 
 
-def _check_cache_lossless(wl, layer, v, sel):
+def _check_cache_lossless(wl, layer, v, sel, resident=None):
+    """Every occupied cache slot holds its chunk's V exactly, each selected
+    chunk's slot holds that chunk, and the occupied slots are `resident`
+    (per row; default: the selection, the set-difference cache)."""
+    cap = layer.cap
     slots = to_np(layer.read(skv.SKV_T_SLOT_CHUNKS))
-    vc = to_np(layer.read(skv.SKV_T_CACHE_V)).reshape(wl.b, wl.h_kv, wl.k, wl.c, wl.d)
+    sslot = to_np(layer.read(skv.SKV_T_SELECTION_SLOTS))
+    vc = to_np(layer.read(skv.SKV_T_CACHE_V)).reshape(wl.b, wl.h_kv, cap, wl.c, wl.d)
     for b in range(wl.b):
         for h in range(wl.h_kv):
-            assert sorted(slots[b, h]) == sorted(sel[b, h])
-            rows = v[b, h].reshape(wl.n, wl.c, wl.d)[slots[b, h]]
-            np.testing.assert_array_equal(vc[b, h], rows)
+            held = slots[b, h][slots[b, h] >= 0]
+            want = set(int(x) for x in sel[b, h]) if resident is None else set(resident[b][h])
+            assert len(held) == len(set(held.tolist())) and set(held.tolist()) == want
+            np.testing.assert_array_equal(slots[b, h][sslot[b, h]], sel[b, h])
+            occ = np.flatnonzero(slots[b, h] >= 0)
+            rows = v[b, h].reshape(wl.n, wl.c, wl.d)[slots[b, h][occ]]
+            np.testing.assert_array_equal(vc[b, h][occ], rows)
 
 
 @pytest.mark.parametrize("case", list(CASES))
@@ -403,5 +412,67 @@ def test_snapkv_selection_matches_oracle(case):
         assert e.value.code == skv.SKV_E_SHAPE
     with pytest.raises(ValueError):
         layer.snapkv_select(q_bad[:, :1], pool)
+    layer.close()
+    hb.free()
+
+
+LRU_CASES = {
+    # three selections' worth of chunks, bfloat16, b = 2
+    "bf16-cap3k": (synth.LLAMA_32K.with_(b=2, s=8192, k=16, steps=10, rho=0.9), 48),
+    # one spare slot: nearly every step evicts among chunks of equal age
+    "bf16-cap-k+1": (synth.LLAMA_32K.with_(h_q=8, h_kv=2, s=4096, o=4, k=12, steps=10, rho=0.9), 13),
+    # every selectable chunk fits: nothing is evicted, binary32, ragged n
+    "fp32-cap-all": (T.with_(b=2, s=2000, d=128, r=48, o=4, k=9, w=32, steps=8, rho=0.7), 250 - 4 - 4),
+}
+
+
+@pytest.mark.parametrize("case", list(LRU_CASES))
+def test_lru_cache_matches_oracle(case):
+    """A V cache larger than the selection: outputs and selections as the
+    oracle's, hits and misses as the oracle's least-recently-used cache
+    simulation fed the same selections, the occupied slots exactly its
+    resident set, and every slot's V equal to its chunk's."""
+    wl, cap = LRU_CASES[case]
+    log(f"[lru-{case}] b={wl.b} n={wl.n} k={wl.k} cap={cap} steps={wl.steps}")
+    shape = oracle_shape(wl)
+    k_pre, v, qs = synth.k_pre_numpy(wl), synth.v_numpy(wl), synth.queries_numpy(wl)
+    meta = oracle.prefill(shape, k_pre, v)
+    A_o, B_o = oracle.svd_factors(shape, k_pre)
+    dt = tdtype(wl)
+    k_pre_d, v_d = to_dev(k_pre, dt), to_dev(v, dt)
+    A_d, B_d = svd_factors(k_pre_d, wl.r)
+    layer = skv.Layer(**layer_kwargs(wl), cache_chunks=cap)
+    hb = layer.host_buffer()
+    layer.prefill_meta(k_pre_d, v_d, A_d, B_d, hb)
+    sim = oracle.CacheSim(wl.b, wl.h_kv, capacity=cap)
+    plain = oracle.CacheSim(wl.b, wl.h_kv)
+    hits_total = plain_total = 0
+    for t in range(wl.steps):
+        q_d = to_dev(qs[t], dt)
+        out_d = torch.empty_like(q_d)
+        layer.decode_step(q_d, out_d)
+        torch.cuda.synchronize()
+        res = oracle.decode(shape, qs[t], meta, A_o, B_o, v)
+        sel_g = to_np(layer.read(skv.SKV_T_SELECTION))
+        exact = check_selection(sel_g, res["sel"], res["S2"], meta["cand"])
+        ref = res["out"] if exact else oracle.attend(shape, qs[t], sel_g, A_o, B_o, v, meta)
+        err = float(np.max(np.abs(to_np(out_d) - ref)))
+        hits, misses = sim.step(sel_g)
+        hits_total += hits
+        plain_total += plain.step(sel_g)[0]
+        st = layer.stats()
+        log(f"[lru-{case}] step {t}: max|out - oracle| = {err:.3g}, hits {hits} misses {misses}")
+        assert err <= OUT_TOL[wl.bf16], f"step {t}: max abs error {err}"
+        assert (st["hits"], st["misses"]) == (hits_total, (t + 1) * wl.b * wl.h_kv * wl.k - hits_total)
+        _check_cache_lossless(wl, layer, v, sel_g, [[list(r) for r in row] for row in sim.resident])
+    assert hits_total >= plain_total
+    # emptying the cache: the next step misses everything, outputs unchanged
+    layer.reset_cache()
+    q_d = to_dev(qs[0], dt)
+    out_d = torch.empty_like(q_d)
+    layer.decode_step(q_d, out_d)
+    torch.cuda.synchronize()
+    st = layer.stats()
+    assert st["misses"] == (wl.steps + 1) * wl.b * wl.h_kv * wl.k - hits_total
     layer.close()
     hb.free()
