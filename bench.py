@@ -380,7 +380,7 @@ def main() -> int:
             if snap:
                 # a fixed selection runs no scoring: the key rebuild dominates
                 sc = kernels["qk"]
-                roofline = {"kernel": "qk_sparse_mfma_kernel + qk_static_kernel (key rebuild, logits)",
+                roofline = {"kernel": "qk_mfma_kernel (key rebuild + static keys, logits)",
                             "bound": "hbm", "achieved": sc["GBps"], "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                             "frac": sc["frac"], "traffic": None, "bytes_per_launch": sc["bytes_per_launch"],
                             "us_per_launch": sc["us_per_launch"]}

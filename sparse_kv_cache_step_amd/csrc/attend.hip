@@ -168,12 +168,12 @@ __global__ __launch_bounds__(256) void qk_generic_kernel(const T *__restrict__ q
 // on MFMA: C[key, head] = sum_i K[key, i] q[head, i] with 16 keys per
 // v_mfma_f32_16x16x32_bf16 (keys as rows, the group's heads as columns).
 // ---------------------------------------------------------------------------
+// Workgroup `blk` of `nblk` per (sequence, KV head) row; no barrier.
 template <int D>
-__global__ __launch_bounds__(256) void qk_static_mfma_kernel(const uint16_t *__restrict__ q,
-                                                             const uint16_t *__restrict__ k_out,
-                                                             const uint16_t *__restrict__ k_loc,
-                                                             float *__restrict__ logits, int hkv, int G, int OC,
-                                                             int KC, int w, int wcap, int NK, float scale) {
+__device__ __forceinline__ void qk_static_tile(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k_out,
+                                               const uint16_t *__restrict__ k_loc, float *__restrict__ logits,
+                                               int hkv, int G, int OC, int KC, int w, int wcap, int NK, float scale,
+                                               int blk, int nblk) {
     constexpr int KS = D / 32;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int row = lane & 15, quad = lane >> 4;
@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void qk_static_mfma_kernel(const uint16_t *__r
             qb[ks] = __builtin_bit_cast(bf16x8, row < G ? *reinterpret_cast<const u32x4 *>(qrow + ks * 32)
                                                         : u32x4{0u, 0u, 0u, 0u});
     }
-    for (int kb0 = (blockIdx.x * 4 + wave) * 16; kb0 < nstat; kb0 += gridDim.x * 64) {
+    for (int kb0 = (blk * 4 + wave) * 16; kb0 < nstat; kb0 += nblk * 64) {
         const int sk = kb0 + row;
         const uint16_t *src = sk < OC ? k_out + (static_cast<size_t>(bh) * OC + sk) * D
                                       : k_loc + (static_cast<size_t>(bh) * wcap + (sk - OC)) * D;
@@ -255,15 +255,26 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(f32x4 a, f32x4 b) {
     return r;
 }
 
+// One launch takes both key sets.  With rebuilt keys (ts > 0 workgroups per
+// row, 256 keys each) every workgroup then also takes its share of the static
+// keys' 16-key blocks (one block per wave at the usual sizes), so the static
+// logits cost no launch of their own; without them, the tt workgroups of the
+// row only compute static logits.
 template <int D, int GP, int NKB>
-__global__ __launch_bounds__(256) void qk_sparse_mfma_kernel(const uint16_t *__restrict__ q,
-                                                             const uint16_t *__restrict__ A,
-                                                             const uint16_t *__restrict__ Bt,
-                                                             const int32_t *__restrict__ sel,
-                                                             const double *__restrict__ theta_rev,
-                                                             float *__restrict__ logits, int hkv, int G, int s,
-                                                             int c, int r, int r_pad, int k, int OC, int KC, int NK,
-                                                             float scale) {
+__global__ __launch_bounds__(256) void qk_mfma_kernel(const uint16_t *__restrict__ q,
+                                                      const uint16_t *__restrict__ A,
+                                                      const uint16_t *__restrict__ Bt,
+                                                      const int32_t *__restrict__ sel,
+                                                      const double *__restrict__ theta_rev,
+                                                      const uint16_t *__restrict__ k_out,
+                                                      const uint16_t *__restrict__ k_loc,
+                                                      float *__restrict__ logits, int hkv, int G, int s,
+                                                      int c, int r, int r_pad, int k, int OC, int KC, int w,
+                                                      int wcap, int NK, int ts, int tt, float scale) {
+    if (ts == 0) {  // no rebuilt keys: static logits only, no barrier
+        qk_static_tile<D>(q, k_out, k_loc, logits, hkv, G, OC, KC, w, wcap, NK, scale, blockIdx.x, tt);
+        return;
+    }
     static_assert(GP <= 16, "query heads are the rows of one 16-row MFMA block");
     constexpr int NB = D / 16;      // 16-dim blocks
     constexpr int HB = NB / 2;      // blocks holding the first half of the dims
@@ -346,13 +357,12 @@ __global__ __launch_bounds__(256) void qk_sparse_mfma_kernel(const uint16_t *__r
         }
     }
 
-    __syncthreads();
-    if (!active) return;  // no barrier follows
+    __syncthreads();  // the only barrier
 
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
         const int kb0 = key_base + mb * 16;
-        if (kb0 >= KC) break;  // wave-uniform
+        if (!active || kb0 >= KC) break;  // wave-uniform
         f32x4 acc[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -397,6 +407,7 @@ __global__ __launch_bounds__(256) void qk_sparse_mfma_kernel(const uint16_t *__r
             buf_st32(lg[e] * scale, lr, key < KC && g < G ? (g * NK + OC + key) * 4 : kOob);
         }
     }
+    qk_static_tile<D>(q, k_out, k_loc, logits, hkv, G, OC, KC, w, wcap, NK, scale, blockIdx.x, ts);
 }
 
 // ---------------------------------------------------------------------------
@@ -568,7 +579,6 @@ __global__ __launch_bounds__(256) void pv_kernel(const float *__restrict__ logit
         part_acc[((static_cast<size_t>(bh) * G + g) * tiles + tile) * D + i] =
             red[0][g][i] + red[1][g][i] + red[2][g][i] + red[3][g][i];
     }
-
 }
 
 // out[b, g, :] = sum_t e^(m_t - M) acc_t / sum_t e^(m_t - M) l_t over the key
@@ -662,58 +672,49 @@ static hipError_t qk_generic_t(const Dims &dm, const void *q, const void *k_out,
 }
 
 template <int D, int GP, int NKB>
-static hipError_t qk_mfma_t(const Dims &dm, const void *q, const void *A, const void *Bt, const int32_t *sel,
-                            const double *theta_rev, float *logits, hipStream_t st) {
-    if (dm.KC <= 0) return hipSuccess;
+static hipError_t qk_mfma_t(const Dims &dm, const void *q, const void *k_out, const void *k_loc, const void *A,
+                            const void *Bt, const int32_t *sel, const double *theta_rev, float *logits,
+                            hipStream_t st) {
+    const int nstat = dm.OC + dm.w;
+    const int ts = (dm.KC + kQkMfmaTile - 1) / kQkMfmaTile;  // rebuilt-key workgroups per row
+    const int tt = (nstat + 63) / 64;                         // static-only workgroups per row (ts = 0)
+    if (ts + tt == 0) return hipSuccess;
     const int r_pad = NKB * 32;
-    const size_t lds = static_cast<size_t>(D) * (r_pad + 8) * sizeof(uint16_t);
+    const size_t lds = ts > 0 ? static_cast<size_t>(D) * (r_pad + 8) * sizeof(uint16_t) : 0;
     if (lds > 48 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(qk_sparse_mfma_kernel<D, GP, NKB>),
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(qk_mfma_kernel<D, GP, NKB>),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         if (e != hipSuccess) return e;
     }
-    dim3 grid((dm.KC + kQkMfmaTile - 1) / kQkMfmaTile, dm.b * dm.hkv);
-    hipLaunchKernelGGL((qk_sparse_mfma_kernel<D, GP, NKB>), grid, dim3(256), lds, st,
-                       static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(A),
-                       static_cast<const uint16_t *>(Bt), sel, theta_rev, logits, dm.hkv, dm.G, dm.s, dm.c,
-                       dm.r, r_pad, dm.k, dm.OC, dm.KC, dm.NK, dm.scale);
+    dim3 grid(ts > 0 ? ts : tt, dm.b * dm.hkv);
+    hipLaunchKernelGGL((qk_mfma_kernel<D, GP, NKB>), grid, dim3(256), lds, st, static_cast<const uint16_t *>(q),
+                       static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(Bt), sel, theta_rev,
+                       static_cast<const uint16_t *>(k_out), static_cast<const uint16_t *>(k_loc), logits, dm.hkv,
+                       dm.G, dm.s, dm.c, dm.r, r_pad, dm.k, dm.OC, dm.KC, dm.w, dm.wcap, dm.NK, ts, tt, dm.scale);
     return hipGetLastError();
 }
 
 // rank blocks of 32: the smallest supported count that covers the rank
 template <int D, int GP>
-static hipError_t qk_mfma_r(const Dims &dm, const void *q, const void *A, const void *Bt, const int32_t *sel,
-                            const double *theta_rev, float *logits, hipStream_t st) {
+static hipError_t qk_mfma_r(const Dims &dm, const void *q, const void *k_out, const void *k_loc, const void *A,
+                            const void *Bt, const int32_t *sel, const double *theta_rev, float *logits,
+                            hipStream_t st) {
     const int need = (dm.r + 31) / 32;
-    if (need <= 2) return qk_mfma_t<D, GP, 2>(dm, q, A, Bt, sel, theta_rev, logits, st);
-    if (need <= 4) return qk_mfma_t<D, GP, 4>(dm, q, A, Bt, sel, theta_rev, logits, st);
-    if (need <= 5) return qk_mfma_t<D, GP, 5>(dm, q, A, Bt, sel, theta_rev, logits, st);
-    if (need <= 6) return qk_mfma_t<D, GP, 6>(dm, q, A, Bt, sel, theta_rev, logits, st);
-    return qk_mfma_t<D, GP, 8>(dm, q, A, Bt, sel, theta_rev, logits, st);
-}
-
-template <int D>
-static hipError_t qk_static_t(const Dims &dm, const void *q, const void *k_out, const void *k_loc, float *logits,
-                              hipStream_t st) {
-    const int nstat = dm.OC + dm.w;
-    if (nstat <= 0) return hipSuccess;
-    dim3 grid((nstat + 63) / 64, dm.b * dm.hkv);
-    hipLaunchKernelGGL(qk_static_mfma_kernel<D>, grid, dim3(256), 0, st, static_cast<const uint16_t *>(q),
-                       static_cast<const uint16_t *>(k_out), static_cast<const uint16_t *>(k_loc), logits, dm.hkv,
-                       dm.G, dm.OC, dm.KC, dm.w, dm.wcap, dm.NK, dm.scale);
-    return hipGetLastError();
+    if (need <= 2) return qk_mfma_t<D, GP, 2>(dm, q, k_out, k_loc, A, Bt, sel, theta_rev, logits, st);
+    if (need <= 4) return qk_mfma_t<D, GP, 4>(dm, q, k_out, k_loc, A, Bt, sel, theta_rev, logits, st);
+    if (need <= 5) return qk_mfma_t<D, GP, 5>(dm, q, k_out, k_loc, A, Bt, sel, theta_rev, logits, st);
+    if (need <= 6) return qk_mfma_t<D, GP, 6>(dm, q, k_out, k_loc, A, Bt, sel, theta_rev, logits, st);
+    return qk_mfma_t<D, GP, 8>(dm, q, k_out, k_loc, A, Bt, sel, theta_rev, logits, st);
 }
 
 template <int D>
 static hipError_t qk_bf16_d(const Dims &dm, const void *q, const void *k_out, const void *k_loc, const void *A,
                             const void *Bt, const int32_t *sel, const double *theta_rev,
                             float *logits, hipStream_t st) {
-    hipError_t e = qk_static_t<D>(dm, q, k_out, k_loc, logits, st);
-    if (e != hipSuccess) return e;
     switch (dm.GP) {
-        case 4: return qk_mfma_r<D, 4>(dm, q, A, Bt, sel, theta_rev, logits, st);
-        case 8: return qk_mfma_r<D, 8>(dm, q, A, Bt, sel, theta_rev, logits, st);
-        default: return qk_mfma_r<D, 16>(dm, q, A, Bt, sel, theta_rev, logits, st);
+        case 4: return qk_mfma_r<D, 4>(dm, q, k_out, k_loc, A, Bt, sel, theta_rev, logits, st);
+        case 8: return qk_mfma_r<D, 8>(dm, q, k_out, k_loc, A, Bt, sel, theta_rev, logits, st);
+        default: return qk_mfma_r<D, 16>(dm, q, k_out, k_loc, A, Bt, sel, theta_rev, logits, st);
     }
 }
 
@@ -764,6 +765,7 @@ hipError_t launch_pv(const Dims &dm, const float *logits, const void *v_out, con
     return dm.d == 128 ? pv_d<float, 128>(dm, logits, v_out, vc, sel_slot, v_loc, part_ml, part_acc, st)
                        : pv_d<float, 64>(dm, logits, v_out, vc, sel_slot, v_loc, part_ml, part_acc, st);
 }
+
 
 hipError_t launch_combine(const Dims &dm, const float2 *part_ml, const float *part_acc, void *out, hipStream_t st) {
     const int blocks = dm.b * dm.hq;

@@ -100,5 +100,4 @@ hipError_t launch_pv(const Dims &dm, const float *logits, const void *v_out, con
                      const void *v_loc, float2 *part_ml, float *part_acc, hipStream_t st);
 hipError_t launch_combine(const Dims &dm, const float2 *part_ml, const float *part_acc, void *out,
                           hipStream_t st);
-
 }  // namespace skv
