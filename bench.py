@@ -367,7 +367,8 @@ def main() -> int:
             pv_bytes = ab["selected_v"] + ab["outlier_kv"] // 2 + ab["local_kv"] // 2 + ab["out"]
             fetch_bytes = h2d_bytes / max(1, layer_steps)
             for name, nbytes, peak in (("score", score_bytes, PEAK_HBM), ("qk", qk_bytes, PEAK_HBM),
-                                       ("pv", pv_bytes, PEAK_HBM), ("fetch", fetch_bytes, PEAK_PCIE)):
+                                       ("pv", pv_bytes, PEAK_HBM), ("attn", qk_bytes + pv_bytes, PEAK_HBM),
+                                       ("fetch", fetch_bytes, PEAK_PCIE)):
                 us = per_launch_us[name]
                 if not us:
                     continue  # not run in this mode (a fixed selection scores and fetches nothing)
@@ -378,9 +379,11 @@ def main() -> int:
             if per_launch_us["select"]:
                 kernels["select"] = {"us_per_launch": round(per_launch_us["select"], 3)}
             if snap:
-                # a fixed selection runs no scoring: the key rebuild dominates
-                sc = kernels["qk"]
-                roofline = {"kernel": "qk_mfma_kernel (key rebuild + static keys, logits)",
+                # a fixed selection runs no scoring: attention dominates
+                fused = "attn" in kernels
+                sc = kernels["attn" if fused else "qk"]
+                roofline = {"kernel": "attn_mfma_kernel + combine_kernel (rebuild, logits, PV, merge)" if fused
+                            else "qk_mfma_kernel (key rebuild + static keys, logits)",
                             "bound": "hbm", "achieved": sc["GBps"], "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                             "frac": sc["frac"], "traffic": None, "bytes_per_launch": sc["bytes_per_launch"],
                             "us_per_launch": sc["us_per_launch"]}

@@ -21,7 +21,7 @@ SKV_OK, SKV_E_INVAL, SKV_E_SHAPE, SKV_E_STATE, SKV_E_NOMEM, SKV_E_HIP = 0, -1, -
 (SKV_T_LANDMARKS, SKV_T_MIN_COS, SKV_T_OUTLIERS, SKV_T_CAND_MASK, SKV_T_SCORES, SKV_T_GROUP_SCORES,
  SKV_T_SELECTION, SKV_T_SLOT_CHUNKS, SKV_T_CACHE_V, SKV_T_K_OUT, SKV_T_V_OUT, SKV_T_K_LOC,
  SKV_T_V_LOC, SKV_T_SELECTION_SLOTS) = range(14)
-KERNELS = ("score", "select", "fetch", "qk", "pv")
+KERNELS = ("score", "select", "fetch", "qk", "pv", "attn")
 SKV_K_COUNT = len(KERNELS)
 
 EXPORTS = (

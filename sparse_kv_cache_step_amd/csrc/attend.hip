@@ -410,13 +410,7 @@ __global__ __launch_bounds__(256) void qk_mfma_kernel(const uint16_t *__restrict
     qk_static_tile<D>(q, k_out, k_loc, logits, hkv, G, OC, KC, w, wcap, NK, scale, blockIdx.x, ts);
 }
 
-// ---------------------------------------------------------------------------
-// PV over one split of 256 keys: partial (max, sum) and sum_key p * V[key].
-// Thread (row group rg, column group cg) holds 8 columns of 256/(d/8) rows;
-// every V load of the split is issued before the softmax weights are
-// computed.  Partials are reduced across row groups with lane exchanges
-// inside a wave and through LDS across the four waves.
-// ---------------------------------------------------------------------------
+// 8 stored values of one 16-byte (bfloat16) or two 16-byte (binary32) loads.
 template <typename T>
 __device__ __forceinline__ void unpack8(const u32x4 *raw, float *v) {
     if constexpr (sizeof(T) == 2) {
@@ -430,6 +424,302 @@ __device__ __forceinline__ void unpack8(const u32x4 *raw, float *v) {
         for (int i = 0; i < 4; ++i) { v[i] = __uint_as_float(raw[0][i]); v[4 + i] = __uint_as_float(raw[1][i]); }
     }
 }
+
+// ---------------------------------------------------------------------------
+// Fused attention (bfloat16, MFMA): rebuild + RoPE + logits + softmax-weighted
+// values in one launch, the logits never leaving the workgroup.  Each wave is
+// one key split: up to 64 rebuilt keys (workgroup blockIdx.x < ts takes keys
+// 256*blockIdx.x .. +256, 64 per wave, exactly as the QK kernel) and one
+// 16-key block of the static keys (outlier chunks, then the local window:
+// block 4*blockIdx.x + wave).  Per wave:
+//  1. logits of its 64 + 16 keys (MFMA, as in the QK kernel) into LDS, -inf
+//     for keys it does not have;
+//  2. the V rows of those keys requested (lane = row group x 8-column group;
+//     out-of-range keys read a valid row that gets weight 0);
+//  3. per head, the split's max m and the weights exp(logit - m) in LDS, and
+//     their sum l;
+//  4. sum of weight x V over the split, reduced over the row groups with lane
+//     exchanges, written as the split's partial (m, l, acc) for the merge.
+// Workgroups past ts (more static blocks than rebuilt-key waves) skip the
+// rebuild and its barrier (a workgroup-uniform branch).
+// ---------------------------------------------------------------------------
+template <int D, int GP, int NKB, bool IND>
+__global__ __launch_bounds__(256) void attn_mfma_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ A, const uint16_t *__restrict__ Bt,
+    const int32_t *__restrict__ chunks, const int32_t *__restrict__ sel_slot, const double *__restrict__ theta_rev,
+    const uint16_t *__restrict__ k_out, const uint16_t *__restrict__ v_out, const uint16_t *__restrict__ k_loc,
+    const uint16_t *__restrict__ v_loc, const uint16_t *__restrict__ vc, float2 *__restrict__ part_ml,
+    float *__restrict__ part_acc, int hkv, int G, int s, int c, int r, int r_pad, int k, int cap, int OC, int KC,
+    int w, int wcap, int ts, int T, float scale) {
+    static_assert(GP <= 16, "query heads are the rows of one 16-row MFMA block");
+    constexpr int NB = D / 16, HB = NB / 2, NP = NB / 2, MB = 4, STG = D / 8, KS = D / 32;
+    constexpr int KW = 80;                // keys per wave: 64 rebuilt + one 16-key static block
+    constexpr int CG = D / 8;             // 8-column groups
+    constexpr int RGW = 64 / CG;          // row groups per wave
+    constexpr int NR = KW / RGW;          // rows per lane
+    extern __shared__ uint16_t dyn[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int row = lane & 15, quad = lane >> 4;
+    const int bh = blockIdx.y, b = bh / hkv, h = bh % hkv;
+    const int hq = hkv * G;
+    const int ldb = r_pad + 8;
+    const bool rebuild = static_cast<int>(blockIdx.x) < ts;  // workgroup-uniform
+    uint16_t *Bs = dyn;  // D x (r_pad + 8), rebuilding workgroups only
+    float *ps = reinterpret_cast<float *>(dyn + (ts > 0 ? static_cast<size_t>(D) * ldb : 0)) + wave * GP * KW;
+    const int key_base = blockIdx.x * kQkMfmaTile + wave * 64;
+    const bool active = rebuild && key_base < KC;  // wave-uniform
+    const int nstat = OC + w;
+    const int sb0 = (blockIdx.x * 4 + wave) * 16;  // first key of this wave's static block
+
+    // ---- 1a. rebuilt keys' logits ------------------------------------------------
+    if (rebuild) {
+        const int pos0 = key_base / c;
+        const int my_chunk = chunks[static_cast<size_t>(bh) * k + min(pos0 + lane, k - 1)];
+        double thr[HB][4];
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) thr[hb][e] = theta_rev[hb * 16 + quad * 4 + e];
+        {
+            const uint16_t *Btb = Bt + static_cast<size_t>(bh) * D * r;
+            const int vpr = r_pad / 8, total = D * vpr;
+            u32x4 tmp[STG];
+#pragma unroll
+            for (int i = 0; i < STG; ++i) {
+                const int idx = tid + 256 * i;
+                const int nr = idx / vpr, kc = (idx % vpr) * 8;
+                tmp[i] = (idx < total && kc < r)
+                             ? *reinterpret_cast<const u32x4 *>(Btb + static_cast<size_t>(nr) * r + kc)
+                             : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int i = 0; i < STG; ++i) {
+                const int idx = tid + 256 * i;
+                if (idx < total) *reinterpret_cast<u32x4 *>(Bs + (idx / vpr) * ldb + (idx % vpr) * 8) = tmp[i];
+            }
+        }
+        const Rsrc ar = make_rsrc(A + static_cast<size_t>(b) * s * r, static_cast<uint32_t>(s) * r * 2);
+        u32x4 aop[MB][NKB];
+        int pos[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int key = key_base + mb * 16 + row;
+            const bool kv = active && key < KC;
+            const int kk = key < KC ? key : key_base;
+            const int chunk = __shfl(my_chunk, kk / c - pos0, 64);
+            pos[mb] = chunk * c + kk % c;
+            const int base = (pos[mb] * r + quad * 8) * 2;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+                aop[mb][kb] = buf_ld128(ar, kv && kb * 32 + quad * 8 < r ? base + kb * 64 : kOob);
+        }
+        bf16x8 qa[NP];
+        {
+            const uint16_t *qrow = q + (static_cast<size_t>(b) * hq + h * G + min(row, G - 1)) * D + quad * 4;
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const u32x2 lo = *reinterpret_cast<const u32x2 *>(qrow + 32 * p);
+                const u32x2 hi = *reinterpret_cast<const u32x2 *>(qrow + 32 * p + 16);
+                qa[p] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+            }
+        }
+        __syncthreads();  // Bs staged (every wave of a rebuilding workgroup reaches it)
+
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const int kb0 = key_base + mb * 16;
+            f32x4 lg = {0.f, 0.f, 0.f, 0.f};
+            if (active && kb0 < KC) {  // wave-uniform
+                f32x4 acc[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    const bf16x8 bop = __builtin_bit_cast(bf16x8, aop[mb][kb]);
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const bf16x8 aw = __builtin_bit_cast(
+                            bf16x8, *reinterpret_cast<const u32x4 *>(Bs + (nb * 16 + row) * ldb + kb * 32 + quad * 8));
+                        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bop, acc[nb], 0, 0, 0);
+                    }
+                }
+                const double posd = static_cast<double>(pos[mb]);
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const double turns = posd * thr[hb][e];
+                        const float frac = static_cast<float>(turns - rint(turns));
+                        const float sn = __builtin_amdgcn_sinf(frac), cs = __builtin_amdgcn_cosf(frac);
+                        const float x1 = acc[hb][e], x2 = acc[hb + HB][e];
+                        acc[hb][e] = x1 * cs - x2 * sn;
+                        acc[hb + HB][e] = x2 * cs + x1 * sn;
+                    }
+                }
+#pragma unroll
+                for (int p = 0; p < NP; ++p)
+                    lg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[p], pack_bf16x8(acc[2 * p], acc[2 * p + 1]), lg, 0,
+                                                                 0, 0);
+            }
+            // lane (quad, row): heads 4*quad + e of key kb0 + row
+            const bool kv = active && kb0 + row < KC;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int g = quad * 4 + e;
+                if (g < GP) ps[g * KW + mb * 16 + row] = kv ? lg[e] * scale : -INFINITY;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int g = quad * 4 + e;
+                if (g < GP) ps[g * KW + mb * 16 + row] = -INFINITY;
+            }
+    }
+
+    // ---- 1b. the static block's logits (keys as MFMA rows, heads as columns) -----
+    {
+        bf16x8 qb[KS];
+        const uint16_t *qrow = q + (static_cast<size_t>(b) * hq + h * G + min(row, G - 1)) * D + quad * 8;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + ks * 32));
+        const int sk = min(sb0 + row, max(nstat - 1, 0));
+        const uint16_t *src = sk < OC ? k_out + (static_cast<size_t>(bh) * OC + sk) * D
+                                      : k_loc + (static_cast<size_t>(bh) * wcap + (sk - OC)) * D;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (sb0 < nstat) {  // wave-uniform
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(src + ks * 32 + quad * 8);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), qb[ks], acc, 0, 0, 0);
+            }
+        }
+        // lane (quad, row): head `row` of keys sb0 + 4*quad + e
+        if (row < GP) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ps[row * KW + 64 + quad * 4 + e] =
+                    (row < G && sb0 + quad * 4 + e < nstat) ? acc[e] * scale : -INFINITY;
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- 2. V rows of the split: row i*RGW + rg, columns 8*cg .. +8 ---------------
+    const int rg = lane / CG, cg = lane % CG;
+    u32x4 raw[NR];
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const int kk = i * RGW + rg;  // key of the wave's list (0-63 rebuilt, 64-79 static)
+        const uint16_t *vrow;
+        if (kk < 64) {
+            const int key = min(key_base + kk, max(KC - 1, 0));
+            if constexpr (IND) {
+                const int slot = min(max(sel_slot[static_cast<size_t>(bh) * k + key / c], 0), cap - 1);
+                vrow = vc + ((static_cast<size_t>(bh) * cap + slot) * c + key % c) * D;
+            } else {
+                vrow = vc + (static_cast<size_t>(bh) * KC + key) * D;
+            }
+            if (!active) vrow = nstat > 0 ? (OC > 0 ? v_out + static_cast<size_t>(bh) * OC * D
+                                                    : v_loc + static_cast<size_t>(bh) * wcap * D)
+                                          : vrow;
+        } else {
+            const int sk = min(sb0 + (kk - 64), max(nstat - 1, 0));
+            vrow = sk < OC ? v_out + (static_cast<size_t>(bh) * OC + sk) * D
+                           : v_loc + (static_cast<size_t>(bh) * wcap + (sk - OC)) * D;
+        }
+        raw[i] = *reinterpret_cast<const u32x4 *>(vrow + cg * 8);
+    }
+
+    // ---- 3. per head: split max, weights, sum -------------------------------------
+    const int split = blockIdx.x * 4 + wave, S = T * 4;
+#pragma unroll
+    for (int g = 0; g < GP; ++g) {
+        float *pg = ps + g * KW;
+        if (g >= G) {  // padding heads: weight 0
+            pg[lane] = 0.f;
+            if (lane < KW - 64) pg[64 + lane] = 0.f;
+            continue;
+        }
+        const float x0 = pg[lane], x1 = lane < KW - 64 ? pg[64 + lane] : -INFINITY;
+        const float m = wave_max(fmaxf(x0, x1));
+        const float p0 = m == -INFINITY ? 0.f : expf(x0 - m);
+        const float p1 = m == -INFINITY ? 0.f : expf(x1 - m);
+        pg[lane] = p0;
+        if (lane < KW - 64) pg[64 + lane] = p1;
+        const float l = wave_sum(p0 + p1);
+        if (lane == 0) part_ml[(static_cast<size_t>(bh) * G + g) * S + split] = make_float2(m, l);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // ---- 4. weighted sum of V, reduced over the row groups ------------------------
+    float acc[GP][8];
+#pragma unroll
+    for (int g = 0; g < GP; ++g)
+#pragma unroll
+        for (int x = 0; x < 8; ++x) acc[g][x] = 0.f;
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        const int kk = i * RGW + rg;
+        float v[8];
+        unpack8<uint16_t>(&raw[i], v);
+#pragma unroll
+        for (int g = 0; g < GP; ++g) {
+            const float pw = ps[g * KW + kk];
+#pragma unroll
+            for (int x = 0; x < 8; ++x) acc[g][x] += pw * v[x];
+        }
+    }
+    float *pa = part_acc + ((static_cast<size_t>(bh) * G) * S + split) * D;  // head g at + g * S * D
+    if constexpr (RGW == 4) {
+        // two halving lane exchanges: lane group r ends with values
+        // r*(2*GP) .. r*(2*GP) + 2*GP - 1 of the flattened (head, column) list
+        constexpr int NV = GP * 8;
+        float a[NV];
+#pragma unroll
+        for (int g = 0; g < GP; ++g)
+#pragma unroll
+            for (int x = 0; x < 8; ++x) a[g * 8 + x] = acc[g][x];
+#pragma unroll
+        for (int v = 0; v < NV / 2; ++v) a[v] = swap_sum32(a[v], a[v + NV / 2]);
+#pragma unroll
+        for (int v = 0; v < NV / 4; ++v) a[v] = swap_sum16(a[v], a[v + NV / 4]);
+        const int rr = lane >> 4;
+#pragma unroll
+        for (int v = 0; v < NV / 4; ++v) {
+            const int f = rr * (NV / 4) + v, g = f >> 3;
+            if (g < G) pa[static_cast<size_t>(g) * S * D + cg * 8 + (f & 7)] = a[v];
+        }
+    } else {
+#pragma unroll
+        for (int off = CG; off < 64; off <<= 1)
+#pragma unroll
+            for (int g = 0; g < GP; ++g)
+#pragma unroll
+                for (int x = 0; x < 8; ++x) acc[g][x] += __shfl_xor(acc[g][x], off, 64);
+        if (lane < CG) {
+#pragma unroll
+            for (int g = 0; g < GP; ++g) {
+                if (g >= G) break;
+#pragma unroll
+                for (int x = 0; x < 8; ++x) pa[static_cast<size_t>(g) * S * D + cg * 8 + x] = acc[g][x];
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// PV over one split of 256 keys: partial (max, sum) and sum_key p * V[key].
+// Thread (row group rg, column group cg) holds 8 columns of 256/(d/8) rows;
+// every V load of the split is issued before the softmax weights are
+// computed.  Partials are reduced across row groups with lane exchanges
+// inside a wave and through LDS across the four waves.
+// ---------------------------------------------------------------------------
 
 // IND: the rebuilt block's V is looked up by slot (sel_slot); otherwise
 // selection position i is cache slot i (a cache of exactly k slots, with the
@@ -590,7 +880,7 @@ __global__ __launch_bounds__(D) void combine_kernel(const float2 *__restrict__ p
     const int bg = blockIdx.x, i = threadIdx.x;
     const float2 *ml = part_ml + static_cast<size_t>(bg) * tiles;
     const float *pa = part_acc + static_cast<size_t>(bg) * tiles * D + i;
-    constexpr int TMAX = 16;  // splits held in registers (all loads in flight); more are streamed
+    constexpr int TMAX = 32;  // splits held in registers (all loads in flight); more are streamed
     if (tiles <= TMAX) {
         const Rsrc mr = make_rsrc(ml, static_cast<uint32_t>(tiles) * 8);
         const Rsrc ar = make_rsrc(pa - i, static_cast<uint32_t>(tiles) * D * 4);
@@ -767,22 +1057,106 @@ hipError_t launch_pv(const Dims &dm, const float *logits, const void *v_out, con
 }
 
 
-hipError_t launch_combine(const Dims &dm, const float2 *part_ml, const float *part_acc, void *out, hipStream_t st) {
+template <int D, int GP, int NKB, bool IND>
+static hipError_t attn_t(const Dims &dm, const void *q, const void *A, const void *Bt, const int32_t *chunks,
+                         const int32_t *sel_slot, const double *theta_rev, const void *k_out, const void *v_out,
+                         const void *k_loc, const void *v_loc, const void *vc, float2 *part_ml, float *part_acc,
+                         hipStream_t st) {
+    const int ts = (dm.KC + kQkMfmaTile - 1) / kQkMfmaTile;
+    const int T = attn_workgroups(dm);
+    const int r_pad = NKB * 32;
+    const size_t lds = (ts > 0 ? static_cast<size_t>(D) * (r_pad + 8) * sizeof(uint16_t) : 0) +
+                       4ull * GP * 80 * sizeof(float);
+    auto kern = attn_mfma_kernel<D, GP, NKB, IND>;
+    if (lds > 48 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(T, dm.b * dm.hkv), dim3(256), lds, st, static_cast<const uint16_t *>(q),
+                       static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(Bt), chunks, sel_slot,
+                       theta_rev, static_cast<const uint16_t *>(k_out), static_cast<const uint16_t *>(v_out),
+                       static_cast<const uint16_t *>(k_loc), static_cast<const uint16_t *>(v_loc),
+                       static_cast<const uint16_t *>(vc), part_ml, part_acc, dm.hkv, dm.G, dm.s, dm.c, dm.r, r_pad,
+                       dm.k, dm.cap, dm.OC, dm.KC, dm.w, dm.wcap, ts, T, dm.scale);
+    return hipGetLastError();
+}
+
+template <int D, int GP, bool IND>
+static hipError_t attn_r(const Dims &dm, const void *q, const void *A, const void *Bt, const int32_t *chunks,
+                         const int32_t *sel_slot, const double *theta_rev, const void *k_out, const void *v_out,
+                         const void *k_loc, const void *v_loc, const void *vc, float2 *part_ml, float *part_acc,
+                         hipStream_t st) {
+    const int need = (dm.r + 31) / 32;
+#define SKV_ATTN(NKB) \
+    attn_t<D, GP, NKB, IND>(dm, q, A, Bt, chunks, sel_slot, theta_rev, k_out, v_out, k_loc, v_loc, vc, part_ml, \
+                            part_acc, st)
+    if (need <= 2) return SKV_ATTN(2);
+    if (need <= 4) return SKV_ATTN(4);
+    if (need <= 5) return SKV_ATTN(5);
+    if (need <= 6) return SKV_ATTN(6);
+    return SKV_ATTN(8);
+#undef SKV_ATTN
+}
+
+template <int D, bool IND>
+static hipError_t attn_g(const Dims &dm, const void *q, const void *A, const void *Bt, const int32_t *chunks,
+                         const int32_t *sel_slot, const double *theta_rev, const void *k_out, const void *v_out,
+                         const void *k_loc, const void *v_loc, const void *vc, float2 *part_ml, float *part_acc,
+                         hipStream_t st) {
+    switch (dm.GP) {
+        case 4:
+            return attn_r<D, 4, IND>(dm, q, A, Bt, chunks, sel_slot, theta_rev, k_out, v_out, k_loc, v_loc, vc,
+                                     part_ml, part_acc, st);
+        case 8:
+            return attn_r<D, 8, IND>(dm, q, A, Bt, chunks, sel_slot, theta_rev, k_out, v_out, k_loc, v_loc, vc,
+                                     part_ml, part_acc, st);
+        default:
+            return attn_r<D, 16, IND>(dm, q, A, Bt, chunks, sel_slot, theta_rev, k_out, v_out, k_loc, v_loc, vc,
+                                      part_ml, part_acc, st);
+    }
+}
+
+int attn_workgroups(const Dims &dm) {
+    const int ts = (dm.KC + kQkMfmaTile - 1) / kQkMfmaTile;
+    return std::max(ts, (dm.OC + dm.w + 63) / 64);
+}
+
+hipError_t launch_attn(const Dims &dm, const void *q, const void *A, const void *Bt, const int32_t *chunks,
+                       const int32_t *sel_slot, const double *theta_rev, const void *k_out, const void *v_out,
+                       const void *k_loc, const void *v_loc, const void *vc, float2 *part_ml, float *part_acc,
+                       hipStream_t st) {
+    if (!dm.bf16) return hipErrorInvalidValue;
+    if (attn_workgroups(dm) <= 0) return hipSuccess;
+    if (sel_slot) {
+        return dm.d == 128 ? attn_g<128, true>(dm, q, A, Bt, chunks, sel_slot, theta_rev, k_out, v_out, k_loc, v_loc,
+                                               vc, part_ml, part_acc, st)
+                           : attn_g<64, true>(dm, q, A, Bt, chunks, sel_slot, theta_rev, k_out, v_out, k_loc, v_loc,
+                                              vc, part_ml, part_acc, st);
+    }
+    return dm.d == 128 ? attn_g<128, false>(dm, q, A, Bt, chunks, sel_slot, theta_rev, k_out, v_out, k_loc, v_loc, vc,
+                                            part_ml, part_acc, st)
+                       : attn_g<64, false>(dm, q, A, Bt, chunks, sel_slot, theta_rev, k_out, v_out, k_loc, v_loc, vc,
+                                           part_ml, part_acc, st);
+}
+
+hipError_t launch_combine(const Dims &dm, const float2 *part_ml, const float *part_acc, void *out, int splits,
+                          hipStream_t st) {
     const int blocks = dm.b * dm.hq;
     if (dm.bf16) {
         if (dm.d == 128)
             hipLaunchKernelGGL((combine_kernel<uint16_t, 128>), dim3(blocks), dim3(128), 0, st, part_ml, part_acc,
-                               static_cast<uint16_t *>(out), dm.pv_tiles);
+                               static_cast<uint16_t *>(out), splits);
         else
             hipLaunchKernelGGL((combine_kernel<uint16_t, 64>), dim3(blocks), dim3(64), 0, st, part_ml, part_acc,
-                               static_cast<uint16_t *>(out), dm.pv_tiles);
+                               static_cast<uint16_t *>(out), splits);
     } else {
         if (dm.d == 128)
             hipLaunchKernelGGL((combine_kernel<float, 128>), dim3(blocks), dim3(128), 0, st, part_ml, part_acc,
-                               static_cast<float *>(out), dm.pv_tiles);
+                               static_cast<float *>(out), splits);
         else
             hipLaunchKernelGGL((combine_kernel<float, 64>), dim3(blocks), dim3(64), 0, st, part_ml, part_acc,
-                               static_cast<float *>(out), dm.pv_tiles);
+                               static_cast<float *>(out), splits);
     }
     return hipGetLastError();
 }

@@ -202,6 +202,9 @@ struct skv_layer {
     int fetch_waves = 128;
     int score_wgs = 0;  // workgroups of the scoring kernel (0: two tiles per wave)
     int n_app = 0;      // decode tokens appended to the local block since the last prefill / load
+    // bfloat16 on one queue: rebuild, logits and PV in one fused launch
+    // (SKV_ATTN_FUSED=0 selects the separate QK and PV launches)
+    bool fused = false;
     // SnapKV-style fixed selection: decode steps keep the selection (no
     // scoring or selection); the missing V is fetched by the first of them
     bool fixed = false, fetch_pending = false;
@@ -342,6 +345,8 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     // overrides the workgroup count for tuning.
     ly->score_wgs = 0;
     if (const char *e = std::getenv("SKV_SCORE_WGS")) ly->score_wgs = std::max(1, std::atoi(e));
+    ly->fused = dm.bf16 != 0;
+    if (const char *e = std::getenv("SKV_ATTN_FUSED")) ly->fused = ly->fused && std::atoi(e) != 0;
 
     const size_t B = dm.b, HKV = dm.hkv, HQ = dm.hq, D = dm.d, S = dm.s, E = dm.esize;
     const size_t bh = B * HKV;
@@ -374,8 +379,10 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     // every appended token)
     const Dims dfull = dims_with_local(dm, dm.wcap);
     ALLOC(logits, B * HQ * dfull.NK * 4);
-    ALLOC(part_ml, B * HQ * dfull.pv_tiles * sizeof(float2));
-    ALLOC(part_acc, B * HQ * dfull.pv_tiles * D * 4);
+    // split partials: PV's key tiles, or the fused kernel's one split per wave
+    const size_t splits = std::max<size_t>(dfull.pv_tiles, 4ull * skv::attn_workgroups(dfull));
+    ALLOC(part_ml, B * HQ * splits * sizeof(float2));
+    ALLOC(part_acc, B * HQ * splits * D * 4);
     ALLOC(counters, 4 * sizeof(unsigned long long));
     ALLOC(bad, 4);
     ALLOC(theta, D / 2 * sizeof(double));
@@ -603,24 +610,29 @@ int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) 
         SKV_HIP(hipStreamWaitEvent(st, ly->ev_qk, 0));
         SKV_HIP(hipStreamWaitEvent(st, ly->ev_fetch, 0));
     } else {
-        // one queue: the fetch runs alone on PCIe, then the rebuild
+        // one queue: the fetch runs alone on PCIe, then attention
         if (fetch) {
             Timed t(ly, SKV_K_FETCH, st);
             SKV_HIP(skv::launch_fetch(dm, ly->v_host_dev, ly->vc, ly->misses, ly->miss_count, ly->fetch_waves,
                                       st));
         }
-        {
+        if (ly->fused) {
+            Timed t(ly, SKV_K_ATTN, st);
+            SKV_HIP(skv::launch_attn(dm, q, ly->A, ly->Bt, qk_chunks, pv_slots, ly->theta_rev, ly->k_out, ly->v_out,
+                                     ly->k_loc, ly->v_loc, ly->vc, ly->part_ml, ly->part_acc, st));
+            SKV_HIP(skv::launch_combine(dm, ly->part_ml, ly->part_acc, out, 4 * skv::attn_workgroups(dm), st));
+        } else {
             Timed t(ly, SKV_K_QK, st);
             SKV_HIP(skv::launch_qk(dm, q, ly->k_out, ly->k_loc, ly->A, ly->Bt, qk_chunks, ly->theta,
                                    ly->theta_rev, ly->logits, st));
         }
     }
     ly->fetch_pending = false;
-    {
+    if (ly->overlap || !ly->fused) {
         Timed t(ly, SKV_K_PV, st);
         SKV_HIP(skv::launch_pv(dm, ly->logits, ly->v_out, ly->vc, pv_slots, ly->v_loc, ly->part_ml,
                                ly->part_acc, st));
-        SKV_HIP(skv::launch_combine(dm, ly->part_ml, ly->part_acc, out, st));
+        SKV_HIP(skv::launch_combine(dm, ly->part_ml, ly->part_acc, out, dm.pv_tiles, st));
     }
     if (ly->timing) ++ly->timed_steps;
     return SKV_OK;

@@ -245,9 +245,10 @@ def test_error_paths_on_device():
 
 
 def test_overlap_schedule_is_identical():
-    """The fetch beside the key rebuild (second stream) and the default
-    single-queue order run the same kernels: outputs, selections and hit
-    counts must agree bit for bit."""
+    """The fetch beside the key rebuild (second stream, then separate QK and
+    PV launches) and the default single-queue order (the fused attention
+    kernel): selections, cache contents and hit counts must agree bit for
+    bit, outputs up to summation order (a bfloat16 rounding step)."""
     wl = synth.LLAMA_32K.with_(b=2, s=16384, k=32, steps=4, rho=0.9)
     log(f"[overlap] b={wl.b} s={wl.s} k={wl.k} steps={wl.steps}")
     k_pre, v, qs = synth.k_pre_numpy(wl), synth.v_numpy(wl), synth.queries_numpy(wl)
@@ -260,7 +261,7 @@ def test_overlap_schedule_is_identical():
         serial.decode_step(q_d, o1)
         overlap.decode_step(q_d, o2)
         torch.cuda.synchronize()
-        assert torch.equal(o1, o2), f"step {t}: outputs differ between the schedules"
+        assert torch.allclose(o1.float(), o2.float(), atol=4e-3, rtol=1e-2), f"step {t}: outputs differ"
         assert torch.equal(serial.read(skv.SKV_T_SELECTION), overlap.read(skv.SKV_T_SELECTION))
         assert torch.equal(serial.read(skv.SKV_T_CACHE_V), overlap.read(skv.SKV_T_CACHE_V))
     assert serial.stats() == overlap.stats()
@@ -476,3 +477,39 @@ def test_lru_cache_matches_oracle(case):
     assert st["misses"] == (wl.steps + 1) * wl.b * wl.h_kv * wl.k - hits_total
     layer.close()
     hb.free()
+
+
+@pytest.mark.parametrize("case,cap", [("bf16-llama-32k", 0), ("bf16-g16-ragged", 0), ("bf16-d64-g1", 0),
+                                      ("bf16-no-static", 0), ("bf16-llama-32k", 192)])
+def test_fused_attention_matches_separate_kernels(case, cap, monkeypatch):
+    """The fused rebuild + logits + PV kernel (one split per wave) against the
+    separate QK and PV launches on the same layer state: same selections,
+    outputs equal up to summation order."""
+    wl = CASES[case].with_(steps=3)
+    k_pre, v, qs = synth.k_pre_numpy(wl), synth.v_numpy(wl), synth.queries_numpy(wl)
+    dt = tdtype(wl)
+    k_pre_d, v_d = to_dev(k_pre, dt), to_dev(v, dt)
+    A_d, B_d = svd_factors(k_pre_d, wl.r)
+    layers = []
+    for fused in ("1", "0"):
+        monkeypatch.setenv("SKV_ATTN_FUSED", fused)
+        lay = skv.Layer(**layer_kwargs(wl), cache_chunks=cap)
+        hb = lay.host_buffer()
+        lay.prefill_meta(k_pre_d, v_d, A_d, B_d, hb)
+        layers.append((lay, hb))
+    log(f"[fused-{case}-cap{cap}] b={wl.b} G={wl.h_q // wl.h_kv} d={wl.d} k={wl.k} o={wl.o} w={wl.w}")
+    for t in range(wl.steps):
+        q_d = to_dev(qs[t], dt)
+        outs = []
+        for lay, _ in layers:
+            o = torch.empty_like(q_d)
+            lay.decode_step(q_d, o)
+            outs.append(o)
+        torch.cuda.synchronize()
+        assert torch.equal(layers[0][0].read(skv.SKV_T_SELECTION), layers[1][0].read(skv.SKV_T_SELECTION))
+        err = float((outs[0].float() - outs[1].float()).abs().max())
+        log(f"[fused-{case}-cap{cap}] step {t}: max|fused - separate| = {err:.3g}")
+        assert torch.allclose(outs[0].float(), outs[1].float(), atol=4e-3, rtol=1e-2), f"step {t}: {err}"
+    for lay, hb in layers:
+        lay.close()
+        hb.free()
