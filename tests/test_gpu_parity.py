@@ -48,6 +48,14 @@ CASES = {
     "bf16-chunk16": synth.LLAMA_32K.with_(s=8192, c=16, o=3, k=8, w=32, steps=3, rho=0.9),
     "bf16-rank96-chunk4": synth.LLAMA_32K.with_(s=4096, c=4, r=96, o=6, k=16, w=32, steps=3, rho=0.9),
     "bf16-rank192": synth.LLAMA_32K.with_(s=4096, r=192, o=4, k=8, w=32, steps=3, rho=0.9),
+    # GQA 8 and the padded group sizes 2 (-> 4) and 12 (-> 16), rank 64
+    "bf16-g8": synth.LLAMA_32K.with_(b=2, h_q=32, h_kv=4, s=4096, r=64, o=6, k=20, w=24, steps=3, rho=0.9,
+                                     true_rank=40),
+    "bf16-g2": synth.LLAMA_32K.with_(h_q=8, h_kv=4, s=4096, r=64, o=5, k=12, w=32, steps=3, rho=0.9, true_rank=40),
+    "bf16-g12-d64": synth.LLAMA_32K.with_(h_q=24, h_kv=2, d=64, s=6000, r=48, o=7, k=15, w=40, steps=3, rho=0.9,
+                                          true_rank=30),
+    # one rebuilt chunk and many static blocks: most workgroups are static-only
+    "bf16-k1-many-static": synth.LLAMA_32K.with_(h_q=8, h_kv=2, s=8192, o=60, k=1, w=64, steps=2, rho=0.9),
 }
 
 
