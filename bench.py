@@ -61,26 +61,40 @@ def algorithmic_bytes(wl) -> dict:
     }
 
 
-SCORE_SOURCES = ("select.hip", "skv_device.h", "skv_dims.h")  # the files the scoring kernel is built from
+# The sources a kernel's traffic record depends on: the kernel function's
+# own text and its launcher (cut from the file at these markers), plus the
+# device helpers it uses.
+TRAFFIC_KERNELS = {
+    "score": ("score_mfma_kernel", "select.hip",
+              ("template <int D, int MODE>\n__global__ __launch_bounds__(256) void score_mfma_kernel",
+               "hipError_t launch_score(")),
+    "attn": ("attn_mfma_kernel", "attend.hip",
+             ("template <int D, int GP, int NKB, bool IND>\n__global__ __launch_bounds__(256) void attn_mfma_kernel",
+              "static hipError_t attn_t(")),
+}
 
 
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
+def kernel_source_hash(which: str = "score") -> str:
+    _, fname, markers = TRAFFIC_KERNELS[which]
     csrc = os.path.join(ROOT, "sparse_kv_cache_step_amd", "csrc")
-    for f in SCORE_SOURCES:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+    text = open(os.path.join(csrc, fname)).read()
+    h = hashlib.sha256()
+    for m in markers:
+        i = text.index(m)
+        h.update(text[i:text.index("\n}\n", i)].encode())
+    with open(os.path.join(csrc, "skv_device.h"), "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the score kernel from committed rocprofv3
-    counter runs, if they were taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"traffic_score_{workload}.json")
+def measured_traffic(workload: str, which: str = "score"):
+    """HBM bytes per launch of a kernel from committed rocprofv3 counter
+    runs, if they were taken on the kernel's current sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{which}_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_hash") != kernel_source_hash():
+    if rec.get("source_hash") != kernel_source_hash(which):
         return None
     return rec.get("bytes_per_launch")
 
@@ -89,10 +103,12 @@ COPY_BYTES = 256 << 20  # the calibration copy
 
 
 def ingest_counters(fetch_csv: str, write_csv: str, workload: str, command: str) -> int:
-    """Scoring-kernel HBM bytes per launch from two rocprofv3 counter CSVs."""
+    """HBM bytes per launch of the scoring and fused attention kernels from
+    two rocprofv3 counter CSVs, each counter scaled by what it reads for the
+    calibration copy."""
     import csv
 
-    def per_kernel(path, counter):
+    def per_kernel(path, counter, kname):
         vals, names = {}, {}
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
@@ -101,31 +117,39 @@ def ingest_counters(fetch_csv: str, write_csv: str, workload: str, command: str)
             vals[d] = vals.get(d, 0.0) + float(r["Counter_Value"])
             names[d] = r["Kernel_Name"]
         score = sorted(d for d in vals if "score_mfma_kernel" in names[d])
+        mine = sorted(d for d in vals if kname in names[d])
         # the calibration copy is the last copy dispatched before the first
         # scoring launch (bench.py runs it right before the warmup)
         copies = [d for d in vals if "copyBuffer" in names[d] and score and d < score[0]]
-        if not score or not copies:
-            raise SystemExit(f"{path}: no {counter} values for the scoring kernel or the calibration copy")
-        return sum(vals[d] for d in score) / len(score), vals[max(copies)], len(score)
+        if not mine or not copies:
+            return None
+        return sum(vals[d] for d in mine) / len(mine), vals[max(copies)], len(mine)
 
-    f_kib, f_copy_kib, nf = per_kernel(fetch_csv, "FETCH_SIZE")
-    w_kib, w_copy_kib, nw = per_kernel(write_csv, "WRITE_SIZE")
-    f_scale = COPY_BYTES / (f_copy_kib * 1024.0)
-    w_scale = COPY_BYTES / (w_copy_kib * 1024.0)
-    fetch_b = f_kib * 1024.0 * f_scale
-    write_b = w_kib * 1024.0 * w_scale
-    rec = {"workload": workload, "kernel": "score_mfma_kernel", "source_hash": kernel_source_hash(),
-           "fetch_bytes_per_launch": int(fetch_b), "write_bytes_per_launch": int(write_b),
-           "bytes_per_launch": int(fetch_b + write_b),
-           "raw_KiB": {"FETCH_SIZE": f_kib, "WRITE_SIZE": w_kib, "copy_FETCH_SIZE": f_copy_kib,
-                       "copy_WRITE_SIZE": w_copy_kib},
-           "copy_scale": {"FETCH_SIZE": f_scale, "WRITE_SIZE": w_scale}, "dispatches": [nf, nw],
-           "command": command}
-    out = os.path.join(ROOT, "profiles", f"traffic_score_{workload}.json")
-    with open(out, "w") as fh:
-        json.dump(rec, fh, indent=1)
-    print(json.dumps(rec))
-    return 0
+    done = 0
+    for which, (kname, _, _) in TRAFFIC_KERNELS.items():
+        f = per_kernel(fetch_csv, "FETCH_SIZE", kname)
+        w = per_kernel(write_csv, "WRITE_SIZE", kname)
+        if f is None or w is None:
+            print(f"no counter values for {kname} (or the calibration copy)", file=sys.stderr)
+            continue
+        (f_kib, f_copy_kib, nf), (w_kib, w_copy_kib, nw) = f, w
+        f_scale = COPY_BYTES / (f_copy_kib * 1024.0)
+        w_scale = COPY_BYTES / (w_copy_kib * 1024.0)
+        fetch_b = f_kib * 1024.0 * f_scale
+        write_b = w_kib * 1024.0 * w_scale
+        rec = {"workload": workload, "kernel": kname, "source_hash": kernel_source_hash(which),
+               "fetch_bytes_per_launch": int(fetch_b), "write_bytes_per_launch": int(write_b),
+               "bytes_per_launch": int(fetch_b + write_b),
+               "raw_KiB": {"FETCH_SIZE": f_kib, "WRITE_SIZE": w_kib, "copy_FETCH_SIZE": f_copy_kib,
+                           "copy_WRITE_SIZE": w_copy_kib},
+               "copy_scale": {"FETCH_SIZE": f_scale, "WRITE_SIZE": w_scale}, "dispatches": [nf, nw],
+               "command": command}
+        out = os.path.join(ROOT, "profiles", f"traffic_{which}_{workload}.json")
+        with open(out, "w") as fh:
+            json.dump(rec, fh, indent=1)
+        print(json.dumps(rec))
+        done += 1
+    return 0 if done else 1
 
 
 def main() -> int:
@@ -385,7 +409,8 @@ def main() -> int:
                 roofline = {"kernel": "attn_mfma_kernel + combine_kernel (rebuild, logits, PV, merge)" if fused
                             else "qk_mfma_kernel (key rebuild + static keys, logits)",
                             "bound": "hbm", "achieved": sc["GBps"], "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                            "frac": sc["frac"], "traffic": None, "bytes_per_launch": sc["bytes_per_launch"],
+                            "frac": sc["frac"], "traffic": measured_traffic(wl.name, "attn") if fused else None,
+                            "bytes_per_launch": sc["bytes_per_launch"],
                             "us_per_launch": sc["us_per_launch"]}
             else:
                 sc = kernels["score"]
