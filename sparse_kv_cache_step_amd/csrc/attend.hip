@@ -450,7 +450,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     const uint16_t *__restrict__ k_out, const uint16_t *__restrict__ v_out, const uint16_t *__restrict__ k_loc,
     const uint16_t *__restrict__ v_loc, const uint16_t *__restrict__ vc, float2 *__restrict__ part_ml,
     float *__restrict__ part_acc, int hkv, int G, int s, int c, int r, int r_pad, int k, int cap, int OC, int KC,
-    int w, int wcap, int ts, int T, float scale) {
+    int w, int wcap, int ts, int T, int rows, float scale) {
     static_assert(GP <= 16, "query heads are the rows of one 16-row MFMA block");
     constexpr int NB = D / 16, HB = NB / 2, NP = NB / 2, MB = 4, STG = D / 8, KS = D / 32;
     constexpr int KW = 80;                // keys per wave: 64 rebuilt + one 16-key static block
@@ -460,16 +460,24 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     extern __shared__ uint16_t dyn[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, quad = lane >> 4;
-    const int bh = blockIdx.y, b = bh / hkv, h = bh % hkv;
+    // XCD-aware order: workgroups are dispatched to the 8 XCDs round-robin by
+    // linear index, so tile t of row bh is given index (8*(bh/8)*T + 8*t) +
+    // bh%8: all of a row's workgroups share one XCD, and the row's B, which
+    // each of them stages, comes from HBM into that XCD's L2 once.  Indices
+    // past the last row (rows rounded up to 8) exit at once.
+    const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    const int bh = (idx / T) * 8 + xcd, tile = idx % T;
+    if (bh >= rows) return;  // workgroup-uniform, before any barrier
+    const int b = bh / hkv, h = bh % hkv;
     const int hq = hkv * G;
     const int ldb = r_pad + 8;
-    const bool rebuild = static_cast<int>(blockIdx.x) < ts;  // workgroup-uniform
+    const bool rebuild = tile < ts;  // workgroup-uniform
     uint16_t *Bs = dyn;  // D x (r_pad + 8), rebuilding workgroups only
     float *ps = reinterpret_cast<float *>(dyn + (ts > 0 ? static_cast<size_t>(D) * ldb : 0)) + wave * GP * KW;
-    const int key_base = blockIdx.x * kQkMfmaTile + wave * 64;
+    const int key_base = tile * kQkMfmaTile + wave * 64;
     const bool active = rebuild && key_base < KC;  // wave-uniform
     const int nstat = OC + w;
-    const int sb0 = (blockIdx.x * 4 + wave) * 16;  // first key of this wave's static block
+    const int sb0 = (tile * 4 + wave) * 16;  // first key of this wave's static block
 
     // ---- 1a. rebuilt keys' logits ------------------------------------------------
     if (rebuild) {
@@ -635,7 +643,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     }
 
     // ---- 3. per head: split max, weights, sum -------------------------------------
-    const int split = blockIdx.x * 4 + wave, S = T * 4;
+    const int split = tile * 4 + wave, S = T * 4;
 #pragma unroll
     for (int g = 0; g < GP; ++g) {
         float *pg = ps + g * KW;
@@ -1073,12 +1081,13 @@ static hipError_t attn_t(const Dims &dm, const void *q, const void *A, const voi
                                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(T, dm.b * dm.hkv), dim3(256), lds, st, static_cast<const uint16_t *>(q),
+    const int rows = dm.b * dm.hkv, rows8 = (rows + 7) / 8 * 8;
+    hipLaunchKernelGGL(kern, dim3(T * rows8), dim3(256), lds, st, static_cast<const uint16_t *>(q),
                        static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(Bt), chunks, sel_slot,
                        theta_rev, static_cast<const uint16_t *>(k_out), static_cast<const uint16_t *>(v_out),
                        static_cast<const uint16_t *>(k_loc), static_cast<const uint16_t *>(v_loc),
                        static_cast<const uint16_t *>(vc), part_ml, part_acc, dm.hkv, dm.G, dm.s, dm.c, dm.r, r_pad,
-                       dm.k, dm.cap, dm.OC, dm.KC, dm.w, dm.wcap, ts, T, dm.scale);
+                       dm.k, dm.cap, dm.OC, dm.KC, dm.w, dm.wcap, ts, T, rows, dm.scale);
     return hipGetLastError();
 }
 
