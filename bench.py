@@ -375,6 +375,41 @@ def main() -> int:
                     kern_ms[kname] += v_ms
         per_launch_us = {k: (v * 1e3 / kern_steps if kern_steps else None) for k, v in kern_ms.items()}
 
+        # ---- a cold step: every layer's cache emptied, one more step timed ------
+        cold_us = None
+        if not snap and not args.append:
+            for lay in Ls:
+                lay.reset_cache(stream)
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            run_steps(nq - 1, 1)
+            c1.record(stream)
+            torch.cuda.synchronize()
+            cold_us = c0.elapsed_time(c1) * 1e3 / layers
+
+        # ---- the device's own ceilings, measured in this run --------------------
+        peaks = {}
+        try:
+            nb = 1 << 30
+            src = torch.empty(nb, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            hsrc = torch.empty(nb // 4, dtype=torch.uint8, pin_memory=True)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            dst.copy_(src)
+            ev[0].record(stream)
+            dst.copy_(src)
+            ev[1].record(stream)
+            dst[: nb // 4].copy_(hsrc, non_blocking=True)
+            ev[2].record(stream)
+            dst[: nb // 4].copy_(hsrc, non_blocking=True)
+            ev[3].record(stream)
+            torch.cuda.synchronize()
+            peaks = {"hbm_copy_TBps": round(2 * nb / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e12, 3),
+                     "pcie_h2d_pinned_GBps": round((nb // 4) / (ev[2].elapsed_time(ev[3]) * 1e-3) / 1e9, 2)}
+            del src, dst, hsrc
+        except RuntimeError as e:  # not enough memory for the probes: leave them out
+            log(f"device peaks skipped: {e}")
+
         layer_steps = args.steps * layers
         ab = algorithmic_bytes(wl)
         if snap:
@@ -496,6 +531,9 @@ def main() -> int:
             "parity_spot_check": parity,
             "setup_s": round(time.time() - t0, 1),
             "prefill_ms_per_layer": {k: round(v / layers, 2) for k, v in prefill_ms.items()},
+            "tokens_per_s_attention_only": round(value * wl.b / layers, 1),
+            "cold_step_us_per_layer": round(cold_us, 2) if cold_us else None,
+            "device_peaks": peaks,
         }
         if snap:
             line["snapkv_select_us_per_layer"] = round(snap_us, 2)

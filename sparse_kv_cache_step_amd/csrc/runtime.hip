@@ -203,7 +203,7 @@ struct skv_layer {
     int score_wgs = 0;  // workgroups of the scoring kernel (0: two tiles per wave)
     int n_app = 0;      // decode tokens appended to the local block since the last prefill / load
     // bfloat16 on one queue: rebuild, logits and PV in one fused launch
-    // (SKV_ATTN_FUSED=0 selects the separate QK and PV launches)
+    // instead of the separate QK and PV launches
     bool fused = false;
     // SnapKV-style fixed selection: decode steps keep the selection (no
     // scoring or selection); the missing V is fetched by the first of them
@@ -345,8 +345,12 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     // overrides the workgroup count for tuning.
     ly->score_wgs = 0;
     if (const char *e = std::getenv("SKV_SCORE_WGS")) ly->score_wgs = std::max(1, std::atoi(e));
-    ly->fused = dm.bf16 != 0;
-    if (const char *e = std::getenv("SKV_ATTN_FUSED")) ly->fused = ly->fused && std::atoi(e) != 0;
+    // measured on MI355X: the fused kernel wins at GQA 4 (128K b8: 35.7 against
+    // 41.1 us; 60K b48: even) and loses at GQA 16 (244K b12: 90.7 against
+    // 49.4 us, its 16 heads' accumulators halve the occupancy); SKV_ATTN_FUSED=1
+    // or 0 forces either for bfloat16
+    ly->fused = dm.bf16 != 0 && dm.GP == 4;
+    if (const char *e = std::getenv("SKV_ATTN_FUSED")) ly->fused = dm.bf16 != 0 && std::atoi(e) != 0;
 
     const size_t B = dm.b, HKV = dm.hkv, HQ = dm.hq, D = dm.d, S = dm.s, E = dm.esize;
     const size_t bh = B * HKV;
