@@ -622,7 +622,13 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
         kmx = max(kmx, b2.y);
     }
     block_minmax(kmn, kmx, sc);  // its barriers also publish the keys
-    if (k <= 0 || kmn > kmx) return;
+    if (k <= 0 || kmn > kmx) {  // nothing to select: the step still counts
+        if (tid == 0) {
+            miss_count[bh] = 0;
+            if (bh == 0) atomicAdd(&counters[2], 1ull);
+        }
+        return;
+    }
     radix_topk(keys, n, k, kmn, kmx, sel + static_cast<size_t>(bh) * k, s_sel, sc);
     __syncthreads();
 

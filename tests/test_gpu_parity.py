@@ -56,6 +56,11 @@ CASES = {
                                           true_rank=30),
     # one rebuilt chunk and many static blocks: most workgroups are static-only
     "bf16-k1-many-static": synth.LLAMA_32K.with_(h_q=8, h_kv=2, s=8192, o=60, k=1, w=64, steps=2, rho=0.9),
+    # no selection at all (budget 0): outlier and local keys only
+    "bf16-k0": synth.LLAMA_32K.with_(h_q=8, h_kv=2, s=4096, o=8, k=0, w=32, steps=2, rho=0.9),
+    "fp32-k0": T.with_(o=4, k=0, w=32, steps=2),
+    # the largest budget the selection supports (k = 4096)
+    "bf16-k4096": synth.LLAMA_32K.with_(h_q=8, h_kv=2, s=36864, o=48, k=4096, w=32, steps=2, rho=0.9),
 }
 
 
