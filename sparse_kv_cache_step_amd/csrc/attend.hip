@@ -439,7 +439,9 @@ __device__ __forceinline__ void unpack8(const u32x4 *raw, float *v) {
 //  3. per head, the split's max m and the weights exp(logit - m) in LDS, and
 //     their sum l;
 //  4. sum of weight x V over the split, reduced over the row groups with lane
-//     exchanges, written as the split's partial (m, l, acc) for the merge.
+//     exchanges, into LDS;
+//  5. the four waves' partials merged into the workgroup's one (m, l, acc),
+//     written for the merge kernel.
 // Workgroups past ts (more static blocks than rebuilt-key waves) skip the
 // rebuild and its barrier (a workgroup-uniform branch).
 // ---------------------------------------------------------------------------
@@ -643,7 +645,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     }
 
     // ---- 3. per head: split max, weights, sum -------------------------------------
-    const int split = tile * 4 + wave, S = T * 4;
+    float *wacc = ps + (4 - wave) * GP * KW + wave * GP * (D + 2);  // this wave's (m, l, acc) for the merge
 #pragma unroll
     for (int g = 0; g < GP; ++g) {
         float *pg = ps + g * KW;
@@ -659,7 +661,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
         pg[lane] = p0;
         if (lane < KW - 64) pg[64 + lane] = p1;
         const float l = wave_sum(p0 + p1);
-        if (lane == 0) part_ml[(static_cast<size_t>(bh) * G + g) * S + split] = make_float2(m, l);
+        if (lane == 0) { wacc[g * (D + 2) + D] = m; wacc[g * (D + 2) + D + 1] = l; }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -683,7 +685,6 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
             for (int x = 0; x < 8; ++x) acc[g][x] += pw * v[x];
         }
     }
-    float *pa = part_acc + ((static_cast<size_t>(bh) * G) * S + split) * D;  // head g at + g * S * D
     if constexpr (RGW == 4) {
         // two halving lane exchanges: lane group r ends with values
         // r*(2*GP) .. r*(2*GP) + 2*GP - 1 of the flattened (head, column) list
@@ -701,7 +702,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
 #pragma unroll
         for (int v = 0; v < NV / 4; ++v) {
             const int f = rr * (NV / 4) + v, g = f >> 3;
-            if (g < G) pa[static_cast<size_t>(g) * S * D + cg * 8 + (f & 7)] = a[v];
+            if (g < G) wacc[g * (D + 2) + cg * 8 + (f & 7)] = a[v];
         }
     } else {
 #pragma unroll
@@ -715,9 +716,32 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
             for (int g = 0; g < GP; ++g) {
                 if (g >= G) break;
 #pragma unroll
-                for (int x = 0; x < 8; ++x) pa[static_cast<size_t>(g) * S * D + cg * 8 + x] = acc[g][x];
+                for (int x = 0; x < 8; ++x) wacc[g * (D + 2) + cg * 8 + x] = acc[g][x];
             }
         }
+    }
+
+    // ---- 5. the workgroup's four splits merged into one partial --------------------
+    __syncthreads();  // every wave of the workgroup reaches it (no early exit above)
+    const float *all = ps + (4 - wave) * GP * KW;  // (wave, head) records of D + 2 floats
+    for (int idx = tid; idx < G * D; idx += 256) {
+        const int g = idx / D, i = idx % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, all[(wv * GP + g) * (D + 2) + D]);
+        float L = 0.f, a = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int wv = 0; wv < 4; ++wv) {
+                const float *r = all + (wv * GP + g) * (D + 2);
+                const float wgt = expf(r[D] - M);
+                L += wgt * r[D + 1];
+                a += wgt * r[i];
+            }
+        }
+        const size_t rec = (static_cast<size_t>(bh) * G + g) * T + tile;
+        part_acc[rec * D + i] = a;
+        if (i == 0) part_ml[rec] = make_float2(M, L);
     }
 }
 
@@ -1074,7 +1098,7 @@ static hipError_t attn_t(const Dims &dm, const void *q, const void *A, const voi
     const int T = attn_workgroups(dm);
     const int r_pad = NKB * 32;
     const size_t lds = (ts > 0 ? static_cast<size_t>(D) * (r_pad + 8) * sizeof(uint16_t) : 0) +
-                       4ull * GP * 80 * sizeof(float);
+                       4ull * GP * (80 + D + 2) * sizeof(float);
     auto kern = attn_mfma_kernel<D, GP, NKB, IND>;
     if (lds > 48 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),

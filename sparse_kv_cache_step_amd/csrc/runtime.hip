@@ -383,8 +383,8 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     // every appended token)
     const Dims dfull = dims_with_local(dm, dm.wcap);
     ALLOC(logits, B * HQ * dfull.NK * 4);
-    // split partials: PV's key tiles, or the fused kernel's one split per wave
-    const size_t splits = std::max<size_t>(dfull.pv_tiles, 4ull * skv::attn_workgroups(dfull));
+    // split partials: PV's key tiles, or the fused kernel's one split per workgroup
+    const size_t splits = std::max<size_t>(dfull.pv_tiles, skv::attn_workgroups(dfull));
     ALLOC(part_ml, B * HQ * splits * sizeof(float2));
     ALLOC(part_acc, B * HQ * splits * D * 4);
     ALLOC(counters, 4 * sizeof(unsigned long long));
@@ -624,7 +624,7 @@ int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) 
             Timed t(ly, SKV_K_ATTN, st);
             SKV_HIP(skv::launch_attn(dm, q, ly->A, ly->Bt, qk_chunks, pv_slots, ly->theta_rev, ly->k_out, ly->v_out,
                                      ly->k_loc, ly->v_loc, ly->vc, ly->part_ml, ly->part_acc, st));
-            SKV_HIP(skv::launch_combine(dm, ly->part_ml, ly->part_acc, out, 4 * skv::attn_workgroups(dm), st));
+            SKV_HIP(skv::launch_combine(dm, ly->part_ml, ly->part_acc, out, skv::attn_workgroups(dm), st));
         } else {
             Timed t(ly, SKV_K_QK, st);
             SKV_HIP(skv::launch_qk(dm, q, ly->k_out, ly->k_loc, ly->A, ly->Bt, qk_chunks, ly->theta,

@@ -98,9 +98,9 @@ hipError_t launch_qk(const Dims &dm, const void *q, const void *k_out, const voi
                      float *logits, hipStream_t st);
 hipError_t launch_pv(const Dims &dm, const float *logits, const void *v_out, const void *vc, const int32_t *sel_slot,
                      const void *v_loc, float2 *part_ml, float *part_acc, hipStream_t st);
-// Fused attention (bfloat16 only): logits and PV partials in one launch, one
-// split per wave, attn_workgroups(dm) workgroups per row (4 splits each);
-// then launch_combine with splits = 4 * attn_workgroups(dm).
+// Fused attention (bfloat16 only): logits and PV partials in one launch,
+// attn_workgroups(dm) workgroups per row, one split partial each; then
+// launch_combine with splits = attn_workgroups(dm).
 int attn_workgroups(const Dims &dm);
 hipError_t launch_attn(const Dims &dm, const void *q, const void *A, const void *Bt, const int32_t *chunks,
                        const int32_t *sel_slot, const double *theta_rev, const void *k_out, const void *v_out,
