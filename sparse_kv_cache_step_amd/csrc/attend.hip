@@ -912,7 +912,7 @@ __global__ __launch_bounds__(D) void combine_kernel(const float2 *__restrict__ p
     const int bg = blockIdx.x, i = threadIdx.x;
     const float2 *ml = part_ml + static_cast<size_t>(bg) * tiles;
     const float *pa = part_acc + static_cast<size_t>(bg) * tiles * D + i;
-    constexpr int TMAX = 32;  // splits held in registers (all loads in flight); more are streamed
+    constexpr int TMAX = 16;  // splits held in registers (all loads in flight); more are streamed
     if (tiles <= TMAX) {
         const Rsrc mr = make_rsrc(ml, static_cast<uint32_t>(tiles) * 8);
         const Rsrc ar = make_rsrc(pa - i, static_cast<uint32_t>(tiles) * D * 4);
