@@ -668,55 +668,61 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // ---- 4. weighted sum of V, reduced over the row groups ------------------------
-    float acc[GP][8];
+    //         (in groups of up to 4 heads, so the accumulators stay few)
+    constexpr int HG = GP < 4 ? GP : 4;
 #pragma unroll
-    for (int g = 0; g < GP; ++g)
+    for (int h0 = 0; h0 < GP; h0 += HG) {
+        if (h0 >= G) break;  // wave-uniform
+        float acc[HG][8];
 #pragma unroll
-        for (int x = 0; x < 8; ++x) acc[g][x] = 0.f;
+        for (int g = 0; g < HG; ++g)
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
-        const int kk = i * RGW + rg;
-        float v[8];
-        unpack8<uint16_t>(&raw[i], v);
+            for (int x = 0; x < 8; ++x) acc[g][x] = 0.f;
 #pragma unroll
-        for (int g = 0; g < GP; ++g) {
-            const float pw = ps[g * KW + kk];
+        for (int i = 0; i < NR; ++i) {
+            const int kk = i * RGW + rg;
+            float v[8];
+            unpack8<uint16_t>(&raw[i], v);
 #pragma unroll
-            for (int x = 0; x < 8; ++x) acc[g][x] += pw * v[x];
+            for (int g = 0; g < HG; ++g) {
+                const float pw = ps[(h0 + g) * KW + kk];
+#pragma unroll
+                for (int x = 0; x < 8; ++x) acc[g][x] += pw * v[x];
+            }
         }
-    }
-    if constexpr (RGW == 4) {
-        // two halving lane exchanges: lane group r ends with values
-        // r*(2*GP) .. r*(2*GP) + 2*GP - 1 of the flattened (head, column) list
-        constexpr int NV = GP * 8;
-        float a[NV];
+        if constexpr (RGW == 4) {
+            // two halving lane exchanges: lane group r ends with values
+            // r*(2*HG) .. r*(2*HG) + 2*HG - 1 of the flattened (head, column) list
+            constexpr int NV = HG * 8;
+            float a[NV];
 #pragma unroll
-        for (int g = 0; g < GP; ++g)
+            for (int g = 0; g < HG; ++g)
 #pragma unroll
-            for (int x = 0; x < 8; ++x) a[g * 8 + x] = acc[g][x];
+                for (int x = 0; x < 8; ++x) a[g * 8 + x] = acc[g][x];
 #pragma unroll
-        for (int v = 0; v < NV / 2; ++v) a[v] = swap_sum32(a[v], a[v + NV / 2]);
+            for (int v = 0; v < NV / 2; ++v) a[v] = swap_sum32(a[v], a[v + NV / 2]);
 #pragma unroll
-        for (int v = 0; v < NV / 4; ++v) a[v] = swap_sum16(a[v], a[v + NV / 4]);
-        const int rr = lane >> 4;
+            for (int v = 0; v < NV / 4; ++v) a[v] = swap_sum16(a[v], a[v + NV / 4]);
+            const int rr = lane >> 4;
 #pragma unroll
-        for (int v = 0; v < NV / 4; ++v) {
-            const int f = rr * (NV / 4) + v, g = f >> 3;
-            if (g < G) wacc[g * (D + 2) + cg * 8 + (f & 7)] = a[v];
-        }
-    } else {
+            for (int v = 0; v < NV / 4; ++v) {
+                const int f = rr * (NV / 4) + v, g = h0 + (f >> 3);
+                if (g < G) wacc[g * (D + 2) + cg * 8 + (f & 7)] = a[v];
+            }
+        } else {
 #pragma unroll
-        for (int off = CG; off < 64; off <<= 1)
+            for (int off = CG; off < 64; off <<= 1)
 #pragma unroll
-            for (int g = 0; g < GP; ++g)
+                for (int g = 0; g < HG; ++g)
 #pragma unroll
-                for (int x = 0; x < 8; ++x) acc[g][x] += __shfl_xor(acc[g][x], off, 64);
-        if (lane < CG) {
+                    for (int x = 0; x < 8; ++x) acc[g][x] += __shfl_xor(acc[g][x], off, 64);
+            if (lane < CG) {
 #pragma unroll
-            for (int g = 0; g < GP; ++g) {
-                if (g >= G) break;
+                for (int g = 0; g < HG; ++g) {
+                    if (h0 + g >= G) break;
 #pragma unroll
-                for (int x = 0; x < 8; ++x) wacc[g * (D + 2) + cg * 8 + x] = acc[g][x];
+                    for (int x = 0; x < 8; ++x) wacc[(h0 + g) * (D + 2) + cg * 8 + x] = acc[g][x];
+                }
             }
         }
     }
