@@ -427,11 +427,11 @@ __device__ __forceinline__ void unpack8(const u32x4 *raw, float *v) {
 
 // ---------------------------------------------------------------------------
 // Fused attention (bfloat16, MFMA): rebuild + RoPE + logits + softmax-weighted
-// values in one launch, the logits never leaving the workgroup.  Each wave is
-// one key split: up to 64 rebuilt keys (workgroup blockIdx.x < ts takes keys
-// 256*blockIdx.x .. +256, 64 per wave, exactly as the QK kernel) and one
-// 16-key block of the static keys (outlier chunks, then the local window:
-// block 4*blockIdx.x + wave).  Per wave:
+// values in one launch, the logits never leaving the workgroup.  Workgroup
+// `tile` of a row (the XCD-aware order below maps the launch index to (row,
+// tile)) takes rebuilt keys 256*tile .. +256 when tile < ts, 64 per wave
+// exactly as the QK kernel, and each wave one 16-key block of the static keys
+// (outlier chunks, then the local window: block 4*tile + wave).  Per wave:
 //  1. logits of its 64 + 16 keys (MFMA, as in the QK kernel) into LDS, -inf
 //     for keys it does not have;
 //  2. the V rows of those keys requested (lane = row group x 8-column group;
@@ -443,7 +443,8 @@ __device__ __forceinline__ void unpack8(const u32x4 *raw, float *v) {
 //  5. the four waves' partials merged into the workgroup's one (m, l, acc),
 //     written for the merge kernel.
 // Workgroups past ts (more static blocks than rebuilt-key waves) skip the
-// rebuild and its barrier (a workgroup-uniform branch).
+// rebuild and its barrier (a workgroup-uniform branch); every workgroup
+// reaches the final barrier.
 // ---------------------------------------------------------------------------
 template <int D, int GP, int NKB, bool IND>
 __global__ __launch_bounds__(256) void attn_mfma_kernel(
