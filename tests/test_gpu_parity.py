@@ -526,3 +526,79 @@ def test_fused_attention_matches_separate_kernels(case, cap, monkeypatch):
     for lay, hb in layers:
         lay.close()
         hb.free()
+
+
+def test_modes_combined_on_one_layer():
+    """One layer through a sequence of modes, every output against the
+    oracle: per-step selection with a cache of 3k slots, the fork/join
+    schedule, decode-token appends, a SnapKV-style fixed selection, a cache
+    reset back to per-step selection, and the one-queue schedule again.  The
+    hit counts follow the oracle's LRU simulation whenever the layer selects."""
+    wl = synth.LLAMA_32K.with_(b=2, s=8192, k=16, steps=9, rho=0.9)
+    cap, max_new, w_obs, pool = 48, 4, 5, 3
+    shape = oracle_shape(wl)
+    k_pre, v = synth.k_pre_numpy(wl), synth.v_numpy(wl)
+    qs = synth.queries_numpy(wl)
+    rng = np.random.default_rng([wl.wid, 91])
+    new_k = oracle.round_store(rng.standard_normal((max_new, wl.b, wl.h_kv, wl.d)), True)
+    new_v = oracle.round_store(rng.standard_normal((max_new, wl.b, wl.h_kv, wl.d)), True)
+    meta = oracle.prefill(shape, k_pre, v)
+    A_o, B_o = oracle.svd_factors(shape, k_pre)
+    dt = tdtype(wl)
+    k_pre_d, v_d = to_dev(k_pre, dt), to_dev(v, dt)
+    A_d, B_d = svd_factors(k_pre_d, wl.r)
+    layer = skv.Layer(**layer_kwargs(wl), max_new=max_new, cache_chunks=cap)
+    hb = layer.host_buffer()
+    layer.prefill_meta(k_pre_d, v_d, A_d, B_d, hb)
+    sim = oracle.CacheSim(wl.b, wl.h_kv, capacity=cap)
+    hits_total = 0
+
+    def step(t, label, fixed_sel=None):
+        nonlocal hits_total
+        q_d = to_dev(qs[t], dt)
+        out_d = torch.empty_like(q_d)
+        layer.decode_step(q_d, out_d)
+        torch.cuda.synchronize()
+        sel_g = to_np(layer.read(skv.SKV_T_SELECTION))
+        if fixed_sel is None:
+            res = oracle.decode(shape, qs[t], meta, A_o, B_o, v)
+            exact = check_selection(sel_g, res["sel"], res["S2"], meta["cand"])
+            ref = res["out"] if exact else oracle.attend(shape, qs[t], sel_g, A_o, B_o, v, meta)
+            hits_total += sim.step(sel_g)[0]
+            assert layer.stats()["hits"] == hits_total, f"{label}: hit count"
+        else:
+            np.testing.assert_array_equal(sel_g, fixed_sel)
+            ref = oracle.attend(shape, qs[t], sel_g, A_o, B_o, v, meta)
+        err = float(np.max(np.abs(to_np(out_d) - ref)))
+        log(f"[modes] {label} step {t}: max|out - oracle| = {err:.3g}")
+        assert err <= OUT_TOL[True], f"{label}: {err}"
+        _check_cache_lossless(wl, layer, v, sel_g, [[list(r) for r in row] for row in sim.resident])
+        return sel_g
+
+    step(0, "one queue")
+    step(1, "one queue")
+    layer.set_overlap(True)
+    step(2, "fork/join")
+    for i in range(2):  # appends under the fork/join schedule
+        layer.append(to_dev(new_k[i], dt), to_dev(new_v[i], dt))
+        meta = oracle.append(shape, meta, new_k[i], new_v[i])
+        step(3 + i, f"fork/join after {i + 1} appends")
+    layer.set_overlap(False)
+    q_obs = np.ascontiguousarray(qs[5:5 + w_obs].transpose(1, 2, 0, 3))
+    layer.snapkv_select(to_dev(q_obs, dt), pool)
+    torch.cuda.synchronize()
+    snap = oracle.snapkv_select(shape, q_obs, meta, pool)
+    fixed = to_np(layer.read(skv.SKV_T_SELECTION))
+    check_selection(fixed, snap["sel"], snap["pooled"], meta["cand"])
+    hits_total += sim.step(fixed)[0]  # the SnapKV selection goes through the same cache
+    assert layer.stats()["hits"] == hits_total
+    layer.append(to_dev(new_k[2], dt), to_dev(new_v[2], dt))
+    meta = oracle.append(shape, meta, new_k[2], new_v[2])
+    step(5, "fixed selection", fixed_sel=fixed)
+    step(6, "fixed selection", fixed_sel=fixed)
+    layer.reset_cache()
+    sim.reset()
+    step(7, "after reset")
+    step(8, "after reset")
+    layer.close()
+    hb.free()
