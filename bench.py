@@ -65,22 +65,26 @@ def algorithmic_bytes(wl) -> dict:
 # own text and its launcher (cut from the file at these markers), plus the
 # device helpers it uses.
 TRAFFIC_KERNELS = {
-    "score": ("score_mfma_kernel", "select.hip",
-              ("template <int D, int MODE>\n__global__ __launch_bounds__(256) void score_mfma_kernel",
-               "hipError_t launch_score(")),
-    "attn": ("attn_mfma_kernel", "attend.hip",
-             ("template <int D, int GP, int NKB, bool IND>\n__global__ __launch_bounds__(256) void attn_mfma_kernel",
-              "static hipError_t attn_t(")),
+    "score": ("score_mfma_kernel", "select.hip", ("void score_mfma_kernel(", "hipError_t launch_score(")),
+    "attn": ("attn_mfma_kernel", "attend.hip", ("void attn_mfma_kernel(", "static hipError_t attn_t(")),
 }
 
 
-def kernel_source_hash(which: str = "score") -> str:
+def kernel_source_hash(which: str = "score"):
+    """Hash of the kernel's text (from its template line to the end of the
+    function) and of its launcher's, plus the device helpers; None when the
+    markers are not found (then no traffic record matches)."""
     _, fname, markers = TRAFFIC_KERNELS[which]
     csrc = os.path.join(ROOT, "sparse_kv_cache_step_amd", "csrc")
     text = open(os.path.join(csrc, fname)).read()
     h = hashlib.sha256()
     for m in markers:
-        i = text.index(m)
+        i = text.find(m)
+        if i < 0:
+            return None
+        t = text.rfind("template <", 0, i)
+        if t >= 0 and text.count("\n}\n", t, i) == 0:  # the template line of this function
+            i = t
         h.update(text[i:text.index("\n}\n", i)].encode())
     with open(os.path.join(csrc, "skv_device.h"), "rb") as fh:
         h.update(fh.read())
@@ -94,7 +98,8 @@ def measured_traffic(workload: str, which: str = "score"):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_hash") != kernel_source_hash(which):
+    h = kernel_source_hash(which)
+    if h is None or rec.get("source_hash") != h:
         return None
     return rec.get("bytes_per_launch")
 
