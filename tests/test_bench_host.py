@@ -79,3 +79,9 @@ def test_counter_ingestion_scales_by_the_calibration_copy(tmp_path, monkeypatch)
 def test_kernel_source_hash_finds_the_kernel_text(which):
     h = bench.kernel_source_hash(which)
     assert len(h) == 16 and h == bench.kernel_source_hash(which)
+
+
+def test_missing_kernel_text_gives_no_traffic_record(monkeypatch):
+    monkeypatch.setitem(bench.TRAFFIC_KERNELS, "score", ("x", "select.hip", ("void no_such_kernel(",)))
+    assert bench.kernel_source_hash("score") is None
+    assert bench.measured_traffic("llama3-8b-128k-b8", "score") is None
