@@ -192,6 +192,12 @@ struct skv_layer {
     uint32_t *keys = nullptr;    // selection keys (b, h_kv, n)
     uint2 *kbounds = nullptr;    // (min, max) selectable key per row and group slice
     int select_keys_in_lds = 1, topo_keys_in_lds = 1;
+    // the decode selection through slice-local candidates (group_topk +
+    // select over the candidates) when both fit in LDS; else group + select
+    bool topk_cand = false;
+    uint32_t *cand_key = nullptr;  // (b, h_kv, slices, k)
+    int32_t *cand_idx = nullptr;   // (b, h_kv, slices, k)
+    int32_t *cand_count = nullptr; // (b, h_kv, slices)
     int32_t *bad = nullptr;
     // host V
     void *v_host_dev = nullptr;
@@ -397,6 +403,22 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     if (skv::select_dynamic_lds(dm, false) + skv::select_static_lds() > lds_cap)
         return bail(fail(SKV_E_SHAPE, "top_k too large for the select kernel's shared memory"));
     ALLOC(keys, bh * dm.n * 4);
+    // measured on MI355X: with few rows the one-workgroup-per-row selection
+    // leaves most CUs idle and the candidates win (GLM-shaped 244K b12, 24
+    // rows: 47.4 against 53.4 us); at 64 rows they are even and at 384 rows
+    // (60K b48) they lose (66.2 against 56.8 us).  SKV_SELECT_CAND=0/1 forces
+    // either where both fit.
+    ly->topk_cand = dm.k > 0 && skv::group_topk_lds(dm) + skv::select_static_lds() <= lds_cap &&
+                    skv::select_cand_lds(dm) + skv::select_static_lds() <= lds_cap;
+    const bool cand_fits = ly->topk_cand;
+    ly->topk_cand = cand_fits && bh < 64;
+    if (const char *e = std::getenv("SKV_SELECT_CAND")) ly->topk_cand = cand_fits && std::atoi(e) != 0;
+    {
+        const size_t cslots = ly->topk_cand ? bh * skv::topk_slices(dm) * dm.k : 0;
+        ALLOC(cand_key, cslots * 4);
+        ALLOC(cand_idx, cslots * 4);
+        ALLOC(cand_count, (ly->topk_cand ? bh * skv::topk_slices(dm) : 0) * 4);
+    }
     ALLOC(kbounds, bh * skv::group_slices(dm) * sizeof(uint2));
 #undef ALLOC
 
@@ -587,10 +609,18 @@ int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) 
         }
         {
             Timed t(ly, SKV_K_SELECT, st);
-            SKV_HIP(skv::launch_group(dm, ly->P, ly->stats, ly->cand, ly->S2, ly->keys, ly->kbounds, st));
-            SKV_HIP(skv::launch_select(dm, ly->keys, ly->kbounds, ly->sel, ly->sel_slot, ly->slot_chunk,
-                                       ly->slot_stamp, ++ly->stamp, ly->misses, ly->miss_count, ly->counters,
-                                       ly->select_keys_in_lds, st));
+            if (ly->topk_cand) {
+                SKV_HIP(skv::launch_group_topk(dm, ly->P, ly->stats, ly->cand, ly->S2, ly->cand_key, ly->cand_idx,
+                                               ly->cand_count, st));
+                SKV_HIP(skv::launch_select_cand(dm, ly->cand_key, ly->cand_idx, ly->cand_count, ly->sel,
+                                                ly->sel_slot, ly->slot_chunk, ly->slot_stamp, ++ly->stamp,
+                                                ly->misses, ly->miss_count, ly->counters, st));
+            } else {
+                SKV_HIP(skv::launch_group(dm, ly->P, ly->stats, ly->cand, ly->S2, ly->keys, ly->kbounds, st));
+                SKV_HIP(skv::launch_select(dm, ly->keys, ly->kbounds, ly->sel, ly->sel_slot, ly->slot_chunk,
+                                           ly->slot_stamp, ++ly->stamp, ly->misses, ly->miss_count, ly->counters,
+                                           ly->select_keys_in_lds, st));
+            }
         }
     }
     if (ly->overlap) {

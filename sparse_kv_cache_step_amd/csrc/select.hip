@@ -562,6 +562,111 @@ __global__ __launch_bounds__(256) void group_kernel(const float *__restrict__ U,
 }
 
 // ---------------------------------------------------------------------------
+// Group score with a slice-local Top-K, one 1024-thread workgroup per (slice
+// of SL chunks, row): the group kernel's S2 and keys for the slice (steps 1-3
+// above), kept in LDS, then the slice's k largest keys (ties to the lower
+// chunk; every selectable chunk of the slice when it has no more than k),
+// written as the slice's candidates (key, chunk) in ascending chunk order.
+// The row's ArgTopK is among the union of its slices' candidates: a chunk of
+// the row's k largest has fewer than k chunks of the row ahead of it (larger
+// key, or equal key and lower index), hence fewer than k of its own slice.
+// The select kernel then ranks the union (slices x k keys) instead of all n.
+// ---------------------------------------------------------------------------
+template <int GP>
+__global__ __launch_bounds__(kSelectThreads) void group_topk_kernel(
+    const float *__restrict__ U, const float2 *__restrict__ stats, const uint32_t *__restrict__ cand,
+    int mask_words, float *__restrict__ S2, uint32_t *__restrict__ cand_key, int32_t *__restrict__ cand_idx,
+    int32_t *__restrict__ cand_count, int G, int n, int tiles, int SL, int slices, int k) {
+    extern __shared__ __align__(16) uint32_t dyn[];
+    __shared__ SelectScratch sc;
+    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
+    const int sl = blockIdx.x, bh = blockIdx.y;
+    const int j0 = sl * SL, cnt = min(SL, n - j0), t0 = j0 / 64, ntl = (cnt + 63) / 64;
+    uint32_t *keys = dyn;                                    // SL keys of the slice
+    int32_t *s_pos = reinterpret_cast<int32_t *>(keys + SL);  // k positions of the slice's Top-K
+    float *s_w = reinterpret_cast<float *>(s_pos + k);       // (SL / 64) x GP tile weights
+    for (int i = tid; i < 4096; i += nt) sc.hist[i] = 0;
+
+    // 1-2. per head: m_g, Z_g over all the row's tiles, the slice's tile weights
+    for (int g = wave; g < G; g += nw) {
+        const float2 *st = stats + (static_cast<size_t>(bh) * G + g) * tiles;
+        float m = -INFINITY;
+        for (int t = lane; t < tiles; t += 64) m = fmaxf(m, st[t].x);
+        m = wave_max(m);
+        float z = 0.f;
+        for (int t = lane; t < tiles; t += 64) {
+            const float2 x = st[t];
+            z += x.x == -INFINITY ? 0.f : x.y * expf(x.x - m);
+        }
+        z = wave_sum(z);
+        const float inv = z > 0.f ? 1.f / (z * static_cast<float>(G)) : 0.f;
+        for (int tl = lane; tl < ntl; tl += 64) {
+            const float2 x = st[t0 + tl];
+            s_w[tl * GP + g] = x.x == -INFINITY ? 0.f : expf(x.x - m) * inv;
+        }
+    }
+    __syncthreads();
+
+    // 3. S2 and the keys of the slice, four chunks' U rows in flight per thread
+    const float *Ub = U + static_cast<size_t>(bh) * n * G;
+    const uint32_t *cm = cand + static_cast<size_t>(bh) * mask_words;
+    float *s2row = S2 + static_cast<size_t>(bh) * n;
+    uint32_t kmn = 0xffffffffu, kmx = 0u;
+    int nvalid = 0;
+    constexpr int UNR = 4;
+    for (int i0 = tid; i0 < cnt; i0 += UNR * nt) {
+        float v[UNR][GP];
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int j = j0 + min(i0 + u * nt, cnt - 1);
+            if (G == GP) {
+#pragma unroll
+                for (int q4 = 0; q4 < GP / 4; ++q4) {
+                    const float4 f = *reinterpret_cast<const float4 *>(Ub + static_cast<size_t>(j) * GP + 4 * q4);
+                    v[u][4 * q4] = f.x; v[u][4 * q4 + 1] = f.y; v[u][4 * q4 + 2] = f.z; v[u][4 * q4 + 3] = f.w;
+                }
+            } else {
+#pragma unroll
+                for (int g = 0; g < GP; ++g) v[u][g] = g < G ? Ub[static_cast<size_t>(j) * G + g] : 0.f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int i = i0 + u * nt;
+            if (i >= cnt) break;
+            const int j = j0 + i;
+            const bool valid = (cm[j >> 5] >> (j & 31)) & 1u;
+            const float *wt = s_w + (i >> 6) * GP;
+            float acc = 0.f;
+#pragma unroll
+            for (int g = 0; g < GP; ++g)
+                if (g < G) acc += v[u][g] * wt[g];
+            s2row[j] = valid ? acc : 0.f;
+            const uint32_t key = float_key(acc);
+            keys[i] = valid ? key : 0u;
+            if (valid) { kmn = min(kmn, key); kmx = max(kmx, key); ++nvalid; }
+        }
+    }
+    int tv, zero = 0, tz;
+    block_scan2(nvalid, zero, sc, &tv, &tz);
+    block_minmax(kmn, kmx, sc);  // its barriers also publish the keys
+    const int kl = min(k, tv);
+    int32_t *out = cand_idx + (static_cast<size_t>(bh) * slices + sl) * k;
+    if (kl > 0) {
+        // 4. the slice's Top-K (radix selection over the slice's keys)
+        radix_topk(keys, cnt, kl, kmn, kmx, out, s_pos, sc);
+        __syncthreads();
+        uint32_t *ok = cand_key + (static_cast<size_t>(bh) * slices + sl) * k;
+        for (int i = tid; i < kl; i += nt) {
+            const int p = s_pos[i];
+            ok[i] = keys[p];
+            out[i] = j0 + p;
+        }
+    }
+    if (tid == 0) cand_count[static_cast<size_t>(bh) * slices + sl] = kl;
+}
+
+// ---------------------------------------------------------------------------
 // Decode selection, one workgroup per (sequence, KV head) row:
 //  1. the row's keys (from the group kernel) into LDS when they fit, and
 //     their bounds from the per-slice minima and maxima;
@@ -576,8 +681,14 @@ __global__ __launch_bounds__(256) void group_kernel(const float *__restrict__ U,
 //     (ascending, empty or evicted); emit the miss list, each selected
 //     chunk's slot, and count hits and misses.
 // ---------------------------------------------------------------------------
+// CAND: the keys are the slices' candidates from group_topk_kernel (cslices
+// slices of up to k per row, ascending chunk order), ranked here and mapped
+// back to chunks; otherwise all n keys of the row with per-slice bounds.
+template <bool CAND>
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(
-    const uint32_t *__restrict__ keys_g, const uint2 *__restrict__ kbounds, int slices, int32_t *__restrict__ sel,
+    const uint32_t *__restrict__ keys_g, const uint2 *__restrict__ kbounds, int slices,
+    const uint32_t *__restrict__ cand_key, const int32_t *__restrict__ cand_idx,
+    const int32_t *__restrict__ cand_count, int cslices, int32_t *__restrict__ sel,
     int32_t *__restrict__ sel_slot, int32_t *__restrict__ slot_chunk, uint32_t *__restrict__ slot_stamp,
     uint32_t stamp, int2 *__restrict__ misses, int32_t *__restrict__ miss_count,
     unsigned long long *__restrict__ counters, int use_lds, int n, int k, int cap) {
@@ -585,42 +696,64 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
     __shared__ SelectScratch sc;
     const int tid = threadIdx.x, nt = blockDim.x;
     const int bh = blockIdx.x;
-    // dynamic LDS: the row's keys first (16-byte aligned), when they fit
+    // dynamic LDS: the keys first (16-byte aligned): the row's n keys when
+    // they fit, or the candidates (keys, then their chunks)
     const uint32_t *krow = keys_g + static_cast<size_t>(bh) * n;
-    uint32_t *keys = use_lds ? dyn : const_cast<uint32_t *>(krow);
-    int32_t *s_sel = reinterpret_cast<int32_t *>(dyn + (use_lds ? n : 0));  // k selected chunks, ascending
+    const int kcap = CAND ? cslices * k : (use_lds ? n : 0);  // key entries held in LDS
+    uint32_t *keys = (CAND || use_lds) ? dyn : const_cast<uint32_t *>(krow);
+    int32_t *s_ci = reinterpret_cast<int32_t *>(dyn + kcap);  // CAND: the chunk of each candidate
+    int32_t *s_sel = s_ci + (CAND ? kcap : 0);           // k selected chunks, ascending
     int32_t *s_sslot = s_sel + k;                       // k: slot of selected chunk i (-1: missing)
     int32_t *s_rank = s_sslot + k;                      // k: index in s_sel of the m-th miss
     uint32_t *s_age = reinterpret_cast<uint32_t *>(s_rank + k);  // cap: eviction key (0: not evictable)
     int32_t *s_free = reinterpret_cast<int32_t *>(s_age + cap);  // cap: rank of a free slot, -1 otherwise
 
-    if (use_lds) {
-        // 16-byte loads, four per thread in flight (16384 keys per batch)
-        const int nv = (n & 3) == 0 && (reinterpret_cast<uintptr_t>(krow) & 15) == 0 ? n / 4 : 0;
-        const u32x4 *kv = reinterpret_cast<const u32x4 *>(krow);
-        for (int v0 = 0; v0 < nv; v0 += 4 * nt) {
-            u32x4 t[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int v = v0 + tid + u * nt;
-                if (v < nv) t[u] = kv[v];
+    uint32_t kmn = 0xffffffffu, kmx = 0u;
+    int nkeys = n;
+    if constexpr (CAND) {
+        // the slices' candidates, slice after slice (so in ascending chunk order)
+        int off = 0;
+        for (int c = 0; c < cslices; ++c) {
+            const size_t base = (static_cast<size_t>(bh) * cslices + c) * k;
+            const int cnt = cand_count[static_cast<size_t>(bh) * cslices + c];
+            for (int i = tid; i < cnt; i += nt) {
+                const uint32_t key = cand_key[base + i];
+                keys[off + i] = key;
+                s_ci[off + i] = cand_idx[base + i];
+                kmn = min(kmn, key);
+                kmx = max(kmx, key);
             }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int v = v0 + tid + u * nt;
-                if (v < nv) reinterpret_cast<u32x4 *>(keys)[v] = t[u];
-            }
+            off += cnt;
         }
-        for (int j = 4 * nv + tid; j < n; j += nt) keys[j] = krow[j];
+        nkeys = off;
+    } else {
+        if (use_lds) {
+            // 16-byte loads, four per thread in flight (16384 keys per batch)
+            const int nv = (n & 3) == 0 && (reinterpret_cast<uintptr_t>(krow) & 15) == 0 ? n / 4 : 0;
+            const u32x4 *kv = reinterpret_cast<const u32x4 *>(krow);
+            for (int v0 = 0; v0 < nv; v0 += 4 * nt) {
+                u32x4 t[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int v = v0 + tid + u * nt;
+                    if (v < nv) t[u] = kv[v];
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int v = v0 + tid + u * nt;
+                    if (v < nv) reinterpret_cast<u32x4 *>(keys)[v] = t[u];
+                }
+            }
+            for (int j = 4 * nv + tid; j < n; j += nt) keys[j] = krow[j];
+        }
+        for (int i = tid; i < slices; i += nt) {
+            const uint2 b2 = kbounds[static_cast<size_t>(bh) * slices + i];
+            kmn = min(kmn, b2.x);
+            kmx = max(kmx, b2.y);
+        }
     }
     for (int i = tid; i < 4096; i += nt) sc.hist[i] = 0;
     for (int i = tid; i < k; i += nt) s_sslot[i] = -1;
-    uint32_t kmn = 0xffffffffu, kmx = 0u;
-    for (int i = tid; i < slices; i += nt) {
-        const uint2 b2 = kbounds[static_cast<size_t>(bh) * slices + i];
-        kmn = min(kmn, b2.x);
-        kmx = max(kmx, b2.y);
-    }
     block_minmax(kmn, kmx, sc);  // its barriers also publish the keys
     if (k <= 0 || kmn > kmx) {  // nothing to select: the step still counts
         if (tid == 0) {
@@ -629,8 +762,17 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
         }
         return;
     }
-    radix_topk(keys, n, k, kmn, kmx, sel + static_cast<size_t>(bh) * k, s_sel, sc);
+    int32_t *srow = sel + static_cast<size_t>(bh) * k;
+    radix_topk(keys, nkeys, k, kmn, kmx, srow, s_sel, sc);
     __syncthreads();
+    if constexpr (CAND) {  // candidate positions to chunks (still ascending)
+        for (int i = tid; i < k; i += nt) {
+            const int chunk = s_ci[s_sel[i]];
+            s_sel[i] = chunk;
+            srow[i] = chunk;
+        }
+        __syncthreads();
+    }
 
     // hits, and the age (stamp distance, >= 1) of every resident chunk that
     // is not selected again
@@ -852,6 +994,19 @@ size_t select_dynamic_lds(const Dims &dm, bool keys_in_lds) {
            (keys_in_lds ? static_cast<size_t>(dm.n) * sizeof(uint32_t) : 0);
 }
 
+int topk_slice(const Dims &dm) { return dm.k <= 1024 ? 4096 : 16384; }
+
+int topk_slices(const Dims &dm) { return (dm.n + topk_slice(dm) - 1) / topk_slice(dm); }
+
+size_t group_topk_lds(const Dims &dm) {
+    const size_t SL = topk_slice(dm);
+    return SL * sizeof(uint32_t) + static_cast<size_t>(dm.k) * sizeof(int32_t) + SL / 64 * dm.GP * sizeof(float);
+}
+
+size_t select_cand_lds(const Dims &dm) {
+    return (2ull * topk_slices(dm) * dm.k + 3ull * dm.k + 2ull * dm.cap) * sizeof(int32_t);
+}
+
 size_t select_static_lds() { return sizeof(SelectScratch); }
 
 int group_slices(const Dims &dm) { return (dm.n + kGroupSlice - 1) / kGroupSlice; }
@@ -878,11 +1033,47 @@ hipError_t launch_select(const Dims &dm, const uint32_t *keys, const uint2 *kbou
                          hipStream_t st) {
     if (dm.k > 0 && dm.cap < dm.k) return hipErrorInvalidValue;
     const size_t lds = select_dynamic_lds(dm, keys_in_lds != 0);
-    hipError_t e = allow_lds(reinterpret_cast<const void *>(select_kernel), lds);
+    auto kern = select_kernel<false>;
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(select_kernel, dim3(dm.b * dm.hkv), dim3(kSelectThreads), lds, st, keys, kbounds,
-                       group_slices(dm), sel, sel_slot, slot_chunk, slot_stamp, stamp, misses, miss_count, counters,
-                       keys_in_lds, dm.n, dm.k, dm.cap);
+    hipLaunchKernelGGL(kern, dim3(dm.b * dm.hkv), dim3(kSelectThreads), lds, st, keys, kbounds, group_slices(dm),
+                       nullptr, nullptr, nullptr, 0, sel, sel_slot, slot_chunk, slot_stamp, stamp, misses,
+                       miss_count, counters, keys_in_lds, dm.n, dm.k, dm.cap);
+    return hipGetLastError();
+}
+
+hipError_t launch_group_topk(const Dims &dm, const float *P, const float2 *stats, const uint32_t *cand, float *S2,
+                             uint32_t *cand_key, int32_t *cand_idx, int32_t *cand_count, hipStream_t st) {
+    if (dm.k <= 0) return hipSuccess;
+    const int SL = topk_slice(dm), slices = topk_slices(dm);
+    const size_t lds = group_topk_lds(dm);
+    auto go = [&](auto kern) {
+        hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3(slices, dm.b * dm.hkv), dim3(kSelectThreads), lds, st, P, stats, cand,
+                           dm.mask_words, S2, cand_key, cand_idx, cand_count, dm.G, dm.n, dm.wtiles, SL, slices,
+                           dm.k);
+        return hipGetLastError();
+    };
+    switch (dm.GP) {
+        case 4: return go(group_topk_kernel<4>);
+        case 8: return go(group_topk_kernel<8>);
+        default: return go(group_topk_kernel<16>);
+    }
+}
+
+hipError_t launch_select_cand(const Dims &dm, const uint32_t *cand_key, const int32_t *cand_idx,
+                              const int32_t *cand_count, int32_t *sel, int32_t *sel_slot, int32_t *slot_chunk,
+                              uint32_t *slot_stamp, uint32_t stamp, int2 *misses, int32_t *miss_count,
+                              unsigned long long *counters, hipStream_t st) {
+    if (dm.k > 0 && dm.cap < dm.k) return hipErrorInvalidValue;
+    const size_t lds = select_cand_lds(dm);
+    auto kern = select_kernel<true>;
+    hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(dm.b * dm.hkv), dim3(kSelectThreads), lds, st, nullptr, nullptr, 0, cand_key,
+                       cand_idx, cand_count, topk_slices(dm), sel, sel_slot, slot_chunk, slot_stamp, stamp, misses,
+                       miss_count, counters, 0, dm.n, dm.k, dm.cap);
     return hipGetLastError();
 }
 

@@ -83,6 +83,21 @@ hipError_t launch_select(const Dims &dm, const uint32_t *keys, const uint2 *kbou
                          int32_t *sel_slot, int32_t *slot_chunk, uint32_t *slot_stamp, uint32_t stamp,
                          int2 *misses, int32_t *miss_count, unsigned long long *counters, int keys_in_lds,
                          hipStream_t st);
+// The decode path's selection in two kernels: the group score with a
+// slice-local Top-K (topk_slices(dm) slices of topk_slice(dm) chunks per row,
+// up to k candidates each: cand_key / cand_idx (b, h_kv, slices, k),
+// cand_count (b, h_kv, slices)), then the selection over the candidates with
+// the cache update of launch_select.
+int topk_slice(const Dims &dm);
+int topk_slices(const Dims &dm);
+size_t group_topk_lds(const Dims &dm);
+size_t select_cand_lds(const Dims &dm);
+hipError_t launch_group_topk(const Dims &dm, const float *P, const float2 *stats, const uint32_t *cand, float *S2,
+                             uint32_t *cand_key, int32_t *cand_idx, int32_t *cand_count, hipStream_t st);
+hipError_t launch_select_cand(const Dims &dm, const uint32_t *cand_key, const int32_t *cand_idx,
+                              const int32_t *cand_count, int32_t *sel, int32_t *sel_slot, int32_t *slot_chunk,
+                              uint32_t *slot_stamp, uint32_t stamp, int2 *misses, int32_t *miss_count,
+                              unsigned long long *counters, hipStream_t st);
 // SnapKV-style selection: accumulate a pass's summed attention, then pool
 // it into S2, selection keys and slice bounds.
 hipError_t launch_snap_accum(const Dims &dm, const float *S2, float *acc, float weight, int first, hipStream_t st);

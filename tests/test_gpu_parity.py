@@ -602,3 +602,46 @@ def test_modes_combined_on_one_layer():
     step(8, "after reset")
     layer.close()
     hb.free()
+
+
+SELECT_CASES = {
+    # two 4096-chunk slices, the second ragged (n = 5000)
+    "bf16-two-slices": synth.LLAMA_32K.with_(h_q=8, h_kv=2, s=40000, o=12, k=100, w=32, steps=2, rho=0.9),
+    # budgets above 1024 take 16384-chunk slices: two, the second ragged (n = 20000)
+    "bf16-k1500-two-slices": synth.LLAMA_32K.with_(b=1, h_q=4, h_kv=1, s=160000, o=16, k=1500, w=64, steps=2,
+                                                   rho=0.9),
+    # a budget larger than a slice's share of candidates (k = 1000, slices of 4096, n = 9000)
+    "fp32-three-slices": T.with_(s=72000, d=64, r=32, o=9, k=1000, w=16, steps=2, rho=0.9, n_scaled_chunks=6),
+}
+
+
+@pytest.mark.parametrize("cand", ["1", "0"])
+@pytest.mark.parametrize("case", list(SELECT_CASES))
+def test_selection_paths_match_oracle(case, cand, monkeypatch):
+    """The two ways to the ArgTopK, forced in turn: slice-local candidates
+    merged by a second pass, and one pass over the whole row.  Each is checked
+    against the oracle's selection (exact or near-tie swaps) and output."""
+    wl = SELECT_CASES[case]
+    monkeypatch.setenv("SKV_SELECT_CAND", cand)
+    shape = oracle_shape(wl)
+    k_pre, v, qs = synth.k_pre_numpy(wl), synth.v_numpy(wl), synth.queries_numpy(wl)
+    meta = oracle.prefill(shape, k_pre, v)
+    A_o, B_o = oracle.svd_factors(shape, k_pre)
+    layer, hb = _gpu_state(wl, k_pre, v)
+    log(f"[select-{case}-cand{cand}] b={wl.b} h_kv={wl.h_kv} n={wl.n} k={wl.k} o={wl.o} w={wl.w}")
+    for t in range(qs.shape[0]):
+        q_d = to_dev(qs[t], tdtype(wl))
+        out_d = torch.empty_like(q_d)
+        layer.decode_step(q_d, out_d)
+        torch.cuda.synchronize()
+        res = oracle.decode(shape, qs[t], meta, A_o, B_o, v)
+        sel_g = to_np(layer.read(skv.SKV_T_SELECTION))
+        exact = check_selection(sel_g, res["sel"], res["S2"], meta["cand"])
+        ref = res["out"] if exact else oracle.attend(shape, qs[t], sel_g, A_o, B_o, v, meta)
+        err = float(np.max(np.abs(to_np(out_d) - ref)))
+        log(f"[select-{case}-cand{cand}] step {t}: selection {'exact' if exact else 'near-tie'}, "
+            f"max|out - oracle| = {err:.3g}")
+        assert err <= OUT_TOL[wl.bf16], f"step {t}: {err}"
+        _check_cache_lossless(wl, layer, v, sel_g)
+    layer.close()
+    hb.free()
