@@ -90,10 +90,30 @@ template <> struct Elem<uint16_t> {
 // ---------------------------------------------------------------------------
 // Wave64 reductions.
 // ---------------------------------------------------------------------------
+// The float reductions take the four in-row steps with DPP moves (quad
+// exchanges, then the mirrors within 8 and within 16 lanes) and the two
+// cross-row steps with the gfx950 permlane swaps, so no step goes through
+// LDS.  Every step combines a lane with its partner symmetrically, so all 64
+// lanes end with bitwise the same result.
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <typename Op> __device__ __forceinline__ float wave_reduce(float v, Op op) {
+    v = op(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]: lane ^ 1
+    v = op(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]: lane ^ 2
+    v = op(v, dpp_mov<0x141>(v));  // row_half_mirror: lane i <-> 7 - i within 8
+    v = op(v, dpp_mov<0x140>(v));  // row_mirror: lane i <-> 15 - i within 16
+    // rows 0/1 and 2/3: the swap leaves row 2j in one result and row 2j+1 in
+    // the other, lane for lane
+    const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = op(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+    // lanes l and l + 32 likewise
+    const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return op(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-    return v;
+    return wave_reduce(v, [](float a, float b) { return a + b; });
 }
 
 __device__ __forceinline__ double wave_sum_d(double v) {
@@ -103,9 +123,7 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
-    return v;
+    return wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 // Merge two (running max, sum of exp(x - max)) pairs.
