@@ -710,6 +710,15 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
 
     uint32_t kmn = 0xffffffffu, kmx = 0u;
     int nkeys = n;
+    // with no more cache slots than threads, each thread's slot entry is read
+    // here, beside the keys, rather than after the Top-K
+    const bool one_slot = cap <= nt;
+    int32_t my_c = -1;
+    uint32_t my_s = 0u;
+    if (one_slot && tid < cap) {
+        my_c = slot_chunk[static_cast<size_t>(bh) * cap + tid];
+        my_s = slot_stamp[static_cast<size_t>(bh) * cap + tid];
+    }
     if constexpr (CAND) {
         // the slices' candidates, slice after slice (so in ascending chunk order)
         int off = 0;
@@ -778,10 +787,12 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
     // is not selected again
     int32_t *gc = slot_chunk + static_cast<size_t>(bh) * cap;
     uint32_t *gs = slot_stamp + static_cast<size_t>(bh) * cap;
+    // slot sl's chunk before this step's update (sl == tid when one_slot)
+    auto chunk_of = [&](int sl) { return one_slot ? my_c : gc[sl]; };
     int nres = 0, nhit = 0;
     uint32_t amn = 0xffffffffu, amx = 0u;
     for (int sl = tid; sl < cap; sl += nt) {
-        const int32_t c = gc[sl];
+        const int32_t c = chunk_of(sl);
         uint32_t age = 0;
         if (c >= 0) {
             ++nres;
@@ -795,7 +806,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
                 gs[sl] = stamp;
                 ++nhit;
             } else {
-                age = stamp - gs[sl];
+                age = stamp - (one_slot ? my_s : gs[sl]);
                 amn = min(amn, age);
                 amx = max(amx, age);
             }
@@ -824,7 +835,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
         if (c1.need_eq < teq) {
             // equal ages: keys chunk + 1 in s_free, the need_eq largest go
             for (int sl = tid; sl < cap; sl += nt)
-                s_free[sl] = s_age[sl] == cut1 ? gc[sl] + 1 : 0;
+                s_free[sl] = s_age[sl] == cut1 ? chunk_of(sl) + 1 : 0;
             __syncthreads();
             cut2 = radix_cut(reinterpret_cast<const uint32_t *>(s_free), cap, c1.need_eq, 1u,
                              static_cast<uint32_t>(n), sc).thr;
@@ -845,9 +856,10 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
         bool fr = false;
         if (i < cap) {
             const uint32_t a = s_age[i];
-            const bool empty = gc[i] < 0;
+            const int32_t ci = chunk_of(i);  // i == tid when one_slot (i < cap <= nt)
+            const bool empty = ci < 0;
             const bool gone = a != 0 && (a > cut1 || (a == cut1 && (!tie_split ||
-                                                      static_cast<uint32_t>(gc[i] + 1) >= cut2)));
+                                                      static_cast<uint32_t>(ci + 1) >= cut2)));
             fr = empty || gone;
         }
         int mi = miss, fi = fr ? 1 : 0, tm, tf;
