@@ -157,6 +157,20 @@ def ingest_counters(fetch_csv: str, write_csv: str, workload: str, command: str)
     return 0 if done else 1
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (first processor in /proc/cpuinfo), or the
+    platform's processor string where that file is missing."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -499,7 +513,7 @@ def main() -> int:
             threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
             cores = min(threads, os.cpu_count() or 1, len(seqs) * wl.h_kv)
             cpu_baseline = {"value": round(1.0 / (per_seq_step * wl.b), 4), "unit": "layer-steps/s", "cores": cores,
-                            "kind": "oracle",
+                            "kind": "oracle", "cpu_model": cpu_model(),
                             "sample": f"{n_done} decode steps (steps 0..{nq - 1}, cycled) of sequences {seqs} "
                                       f"(of {wl.b}) of layer {spot_layer}; {cpu_s:.1f} s of CPU time; "
                                       f"scaled to all {wl.b} sequences"}

@@ -85,3 +85,9 @@ def test_missing_kernel_text_gives_no_traffic_record(monkeypatch):
     monkeypatch.setitem(bench.TRAFFIC_KERNELS, "score", ("x", "select.hip", ("void no_such_kernel(",)))
     assert bench.kernel_source_hash("score") is None
     assert bench.measured_traffic("llama3-8b-128k-b8", "score") is None
+
+
+def test_cpu_model_is_named():
+    """The oracle's timing names the host CPU it ran on."""
+    name = bench.cpu_model()
+    assert isinstance(name, str) and name.strip()
