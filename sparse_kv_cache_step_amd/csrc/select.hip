@@ -256,10 +256,31 @@ struct SelectScratch {
     int above;
 };
 
+// The waves' pairs of partials in sc.wtmp (blockDim.x / 64 of each): this
+// wave's exclusive prefix of both and their totals.  Lane w of every wave
+// loads wave w's pair, a scan across those lanes forms the inclusive sums,
+// and lane reads hand each wave the entries it needs, so no thread walks the
+// list.  Call between the barrier that publishes wtmp and the next write.
+__device__ __forceinline__ void wave_partials_prefix(const SelectScratch &sc, int *pa, int *pb, int *ta, int *tb) {
+    const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int x = lane < nw ? sc.wtmp[0][lane] : 0, y = lane < nw ? sc.wtmp[1][lane] : 0;
+    for (int off = 1; off < nw; off <<= 1) {
+        const int x2 = __shfl_up(x, off, 64), y2 = __shfl_up(y, off, 64);
+        if (lane >= off) { x += x2; y += y2; }
+    }
+    const int src = wave > 0 ? wave - 1 : 0;
+    const int px = __builtin_amdgcn_readlane(x, src), py = __builtin_amdgcn_readlane(y, src);
+    *pa = wave > 0 ? px : 0;
+    *pb = wave > 0 ? py : 0;
+    *ta = __builtin_amdgcn_readlane(x, nw - 1);
+    *tb = __builtin_amdgcn_readlane(y, nw - 1);
+}
+
 // Inclusive prefix sums of two per-thread counts over the threads of the
 // block in one pass (one pair of barriers); totals in *ta, *tb.
 __device__ __forceinline__ void block_scan2(int &a, int &b, SelectScratch &sc, int *ta, int *tb) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
         const int x = __shfl_up(a, off, 64), y = __shfl_up(b, off, 64);
@@ -267,18 +288,11 @@ __device__ __forceinline__ void block_scan2(int &a, int &b, SelectScratch &sc, i
     }
     if (lane == 63) { sc.wtmp[0][wave] = a; sc.wtmp[1][wave] = b; }
     __syncthreads();
-    int pa = 0, pb = 0, sa = 0, sb = 0;
-    for (int w = 0; w < nw; ++w) {
-        const int x = sc.wtmp[0][w], y = sc.wtmp[1][w];
-        if (w < wave) { pa += x; pb += y; }
-        sa += x;
-        sb += y;
-    }
+    int pa, pb;
+    wave_partials_prefix(sc, &pa, &pb, ta, tb);
     __syncthreads();
     a += pa;
     b += pb;
-    *ta = sa;
-    *tb = sb;
 }
 
 // Minimum and maximum of per-thread values over the block (one pair of
@@ -292,10 +306,15 @@ __device__ __forceinline__ void block_minmax(uint32_t &mn, uint32_t &mx, SelectS
     }
     if (lane == 0) { sc.wtmp[0][wave] = static_cast<int>(mn); sc.wtmp[1][wave] = static_cast<int>(mx); }
     __syncthreads();
-    for (int w = 0; w < nw; ++w) {
-        mn = min(mn, static_cast<uint32_t>(sc.wtmp[0][w]));
-        mx = max(mx, static_cast<uint32_t>(sc.wtmp[1][w]));
+    // lane w < nw takes wave w's pair; lanes past nw hold the identities
+    uint32_t a = lane < nw ? static_cast<uint32_t>(sc.wtmp[0][lane]) : 0xffffffffu;
+    uint32_t c = lane < nw ? static_cast<uint32_t>(sc.wtmp[1][lane]) : 0u;
+    for (int off = 1; off < nw; off <<= 1) {
+        a = min(a, static_cast<uint32_t>(__shfl_xor(static_cast<int>(a), off, 64)));
+        c = max(c, static_cast<uint32_t>(__shfl_xor(static_cast<int>(c), off, 64)));
     }
+    mn = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(a), 0));
+    mx = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(c), 0));
     __syncthreads();
 }
 
@@ -396,8 +415,8 @@ __device__ void radix_topk(const uint32_t *keys, int n, int k, uint32_t kmin, ui
     }
     if (lane == 0) { sc.wtmp[0][wave] = cg; sc.wtmp[1][wave] = ce; }
     __syncthreads();
-    int gt_run = 0, eq_run = 0;
-    for (int w = 0; w < wave; ++w) { gt_run += sc.wtmp[0][w]; eq_run += sc.wtmp[1][w]; }
+    int gt_run, eq_run, gt_all, eq_all;
+    wave_partials_prefix(sc, &gt_run, &eq_run, &gt_all, &eq_all);
     __syncthreads();
     const uint64_t below = (1ull << lane) - 1ull;
     for (int jb = j0; jb < j1 && gt_run + min(eq_run, need_eq) < k; jb += 256) {
