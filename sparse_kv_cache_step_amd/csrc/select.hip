@@ -432,7 +432,7 @@ __device__ void radix_topk(const uint32_t *keys, int n, int k, uint32_t kmin, ui
             if (g || (e && eb < need_eq)) {
                 const int pos = gb + min(eb, need_eq);
                 if (pos < k) {
-                    out[pos] = j;
+                    if (out) out[pos] = j;
                     if (lds_out) lds_out[pos] = j;
                 }
             }
@@ -450,16 +450,22 @@ __global__ __launch_bounds__(kSelectThreads) void topo_kernel(const float *__res
     extern __shared__ uint32_t dyn[];
     __shared__ SelectScratch sc;
     const int row = blockIdx.x;
-    uint32_t *keys = use_lds ? dyn : gscratch + static_cast<size_t>(row) * n;
+    // LDS keys through dyn itself, global ones through gk (see select_kernel)
+    uint32_t *gk = gscratch + static_cast<size_t>(row) * n;
     uint32_t kmn = 0xffffffffu, kmx = 0u;
     for (int j = threadIdx.x; j < n; j += blockDim.x) {
         const uint32_t key = j < n_valid ? float_key(-min_cos[static_cast<size_t>(row) * n + j]) : 0u;
-        keys[j] = key;
+        if (use_lds) dyn[j] = key;
+        else gk[j] = key;
         if (j < n_valid) { kmn = min(kmn, key); kmx = max(kmx, key); }
     }
     for (int i = threadIdx.x; i < 4096; i += blockDim.x) sc.hist[i] = 0;
     block_minmax(kmn, kmx, sc);  // its barriers also publish keys and hist
-    if (o > 0 && kmn <= kmx) radix_topk(keys, n, o, kmn, kmx, out + static_cast<size_t>(row) * o, nullptr, sc);
+    if (o > 0 && kmn <= kmx) {
+        int32_t *orow = out + static_cast<size_t>(row) * o;
+        if (use_lds) radix_topk(dyn, n, o, kmn, kmx, orow, nullptr, sc);
+        else radix_topk(gk, n, o, kmn, kmx, orow, nullptr, sc);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -673,7 +679,7 @@ __global__ __launch_bounds__(kSelectThreads) void group_topk_kernel(
     int32_t *out = cand_idx + (static_cast<size_t>(bh) * slices + sl) * k;
     if (kl > 0) {
         // 4. the slice's Top-K (radix selection over the slice's keys)
-        radix_topk(keys, cnt, kl, kmn, kmx, out, s_pos, sc);
+        radix_topk(keys, cnt, kl, kmn, kmx, nullptr, s_pos, sc);
         __syncthreads();
         uint32_t *ok = cand_key + (static_cast<size_t>(bh) * slices + sl) * k;
         for (int i = tid; i < kl; i += nt) {
@@ -719,7 +725,10 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
     // they fit, or the candidates (keys, then their chunks)
     const uint32_t *krow = keys_g + static_cast<size_t>(bh) * n;
     const int kcap = CAND ? cslices * k : (use_lds ? n : 0);  // key entries held in LDS
-    uint32_t *keys = (CAND || use_lds) ? dyn : const_cast<uint32_t *>(krow);
+    // keys in LDS are reached through dyn itself (never through a pointer
+    // that may also be global), so their accesses compile to LDS instructions
+    const bool lds_keys = CAND || use_lds;
+    uint32_t *keys = dyn;
     int32_t *s_ci = reinterpret_cast<int32_t *>(dyn + kcap);  // CAND: the chunk of each candidate
     int32_t *s_sel = s_ci + (CAND ? kcap : 0);           // k selected chunks, ascending
     int32_t *s_sslot = s_sel + k;                       // k: slot of selected chunk i (-1: missing)
@@ -732,12 +741,12 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
     // with no more cache slots than threads, each thread's slot entry is read
     // here, beside the keys, rather than after the Top-K
     const bool one_slot = cap <= nt;
-    int32_t my_c = -1;
-    uint32_t my_s = 0u;
-    if (one_slot && tid < cap) {
-        my_c = slot_chunk[static_cast<size_t>(bh) * cap + tid];
-        my_s = slot_stamp[static_cast<size_t>(bh) * cap + tid];
-    }
+    // (buffer loads: no branch around them, so they and the keys' loads are
+    // all in flight together)
+    const Rsrc scr = make_rsrc(slot_chunk + static_cast<size_t>(bh) * cap, static_cast<uint32_t>(cap) * 4);
+    const Rsrc ssr = make_rsrc(slot_stamp + static_cast<size_t>(bh) * cap, static_cast<uint32_t>(cap) * 4);
+    const int32_t my_c = static_cast<int32_t>(buf_ld32(scr, one_slot && tid < cap ? tid * 4 : kOob));
+    const uint32_t my_s = buf_ld32(ssr, one_slot && tid < cap ? tid * 4 : kOob);
     if constexpr (CAND) {
         // the slices' candidates, slice after slice (so in ascending chunk order)
         int off = 0;
@@ -756,23 +765,24 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
         nkeys = off;
     } else {
         if (use_lds) {
-            // 16-byte loads, four per thread in flight (16384 keys per batch)
+            // 16-byte buffer loads, four per thread in flight (16384 keys per
+            // batch); offsets past the row read zeros and are not stored
             const int nv = (n & 3) == 0 && (reinterpret_cast<uintptr_t>(krow) & 15) == 0 ? n / 4 : 0;
-            const u32x4 *kv = reinterpret_cast<const u32x4 *>(krow);
+            const Rsrc kr = make_rsrc(krow, static_cast<uint32_t>(n) * 4);
             for (int v0 = 0; v0 < nv; v0 += 4 * nt) {
                 u32x4 t[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int v = v0 + tid + u * nt;
-                    if (v < nv) t[u] = kv[v];
+                    t[u] = buf_ld128(kr, v < nv ? v * 16 : kOob);
                 }
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const int v = v0 + tid + u * nt;
-                    if (v < nv) reinterpret_cast<u32x4 *>(keys)[v] = t[u];
+                    if (v < nv) reinterpret_cast<u32x4 *>(dyn)[v] = t[u];
                 }
             }
-            for (int j = 4 * nv + tid; j < n; j += nt) keys[j] = krow[j];
+            for (int j = 4 * nv + tid; j < n; j += nt) dyn[j] = krow[j];
         }
         for (int i = tid; i < slices; i += nt) {
             const uint2 b2 = kbounds[static_cast<size_t>(bh) * slices + i];
@@ -790,15 +800,15 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
         }
         return;
     }
+    // the selection stays in LDS until the last phase: on this chip a wait
+    // for a load also waits for every earlier store, so the kernel's global
+    // stores all come after its last global load
     int32_t *srow = sel + static_cast<size_t>(bh) * k;
-    radix_topk(keys, nkeys, k, kmn, kmx, srow, s_sel, sc);
+    if (lds_keys) radix_topk(dyn, nkeys, k, kmn, kmx, nullptr, s_sel, sc);
+    else radix_topk(krow, nkeys, k, kmn, kmx, nullptr, s_sel, sc);
     __syncthreads();
     if constexpr (CAND) {  // candidate positions to chunks (still ascending)
-        for (int i = tid; i < k; i += nt) {
-            const int chunk = s_ci[s_sel[i]];
-            s_sel[i] = chunk;
-            srow[i] = chunk;
-        }
+        for (int i = tid; i < k; i += nt) s_sel[i] = s_ci[s_sel[i]];
         __syncthreads();
     }
 
@@ -821,8 +831,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
                 if (s_sel[mid] < c) lo = mid + 1; else hi = mid;
             }
             if (lo < k && s_sel[lo] == c) {
-                s_sslot[lo] = sl;
-                gs[sl] = stamp;
+                s_sslot[lo] = sl;  // a hit: its stamp is renewed in the last phase
                 ++nhit;
             } else {
                 age = stamp - (one_slot ? my_s : gs[sl]);
@@ -889,7 +898,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
         rfree += tf;
     }
     __syncthreads();
-    // the m-th missing chunk goes to the m-th free slot
+    // the m-th missing chunk goes to the m-th free slot; hits (resident, age
+    // 0) keep theirs with a new stamp
     int2 *ml = misses + static_cast<size_t>(bh) * k;
     for (int sl = tid; sl < cap; sl += nt) {
         const int r = s_free[sl];
@@ -900,10 +910,15 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
             gs[sl] = stamp;
             s_sslot[i] = sl;
             ml[r] = make_int2(chunk, sl);
+        } else if (r < 0 && s_age[sl] == 0 && chunk_of(sl) >= 0) {
+            gs[sl] = stamp;
         }
     }
     __syncthreads();
-    for (int i = tid; i < k; i += nt) sel_slot[static_cast<size_t>(bh) * k + i] = s_sslot[i];
+    for (int i = tid; i < k; i += nt) {
+        srow[i] = s_sel[i];
+        sel_slot[static_cast<size_t>(bh) * k + i] = s_sslot[i];
+    }
     if (tid == 0) {
         miss_count[bh] = nmiss;
         atomicAdd(&counters[0], static_cast<unsigned long long>(k - nmiss));
