@@ -437,6 +437,9 @@ LRU_CASES = {
     "bf16-cap-k+1": (synth.LLAMA_32K.with_(h_q=8, h_kv=2, s=4096, o=4, k=12, steps=10, rho=0.9), 13),
     # every selectable chunk fits: nothing is evicted, binary32, ragged n
     "fp32-cap-all": (T.with_(b=2, s=2000, d=128, r=48, o=4, k=9, w=32, steps=8, rho=0.7), 250 - 4 - 4),
+    # more slots than the select kernel's 1024 threads (slot entries read in
+    # a loop), filled by fast-drifting queries so that the later steps evict
+    "bf16-cap1100": (synth.LLAMA_32K.with_(h_q=8, h_kv=2, s=32768, o=48, k=200, steps=12, rho=0.3), 1100),
 }
 
 
