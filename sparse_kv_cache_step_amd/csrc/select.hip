@@ -319,7 +319,8 @@ __device__ __forceinline__ void block_minmax(uint32_t &mn, uint32_t &mx, SelectS
 }
 
 // The k largest of keys[0, n), exact ties to the lower index, written to
-// out[0, k) (and to lds_out if given) in ascending index order.  The caller
+// out[0, k) and/or lds_out[0, k) (each if not null) in ascending index
+// order.  The caller
 // passes kmin <= kmax bounding the candidate keys: at least k keys lie in
 // [kmin, kmax], none above kmax, and keys below kmin are never taken.
 // Radix selection runs on the offsets key - kmin, 12 bits per pass from the
