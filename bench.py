@@ -425,6 +425,11 @@ def main() -> int:
             torch.cuda.synchronize()
             peaks = {"hbm_copy_TBps": round(2 * nb / (ev[0].elapsed_time(ev[1]) * 1e-3) / 1e12, 3),
                      "pcie_h2d_pinned_GBps": round((nb // 4) / (ev[2].elapsed_time(ev[3]) * 1e-3) / 1e9, 2)}
+            # a plain streaming read of the 1 GiB buffer (4x the last-level
+            # cache): the ceiling a read-only kernel reaches on this device
+            src.fill_(1)
+            peaks["hbm_read_TBps"] = round(skv.shadowkv_probe_hbm_read(src.data_ptr(), nb, 5, stream.cuda_stream)
+                                           / 1e3, 3)
             del src, dst, hsrc
         except RuntimeError as e:  # not enough memory for the probes: leave them out
             log(f"device peaks skipped: {e}")
@@ -456,6 +461,16 @@ def main() -> int:
                                  "frac": round(gbs * 1e9 / peak, 4) if gbs else None}
             if per_launch_us["select"]:
                 kernels["select"] = {"us_per_launch": round(per_launch_us["select"], 3)}
+            # scoring and attention together: the two HBM streams of the step
+            att = "attn" if "attn" in kernels else None
+            if "score" in kernels and (att or ("qk" in kernels and "pv" in kernels)):
+                parts = [kernels["score"]] + ([kernels[att]] if att else [kernels["qk"], kernels["pv"]])
+                nb_sa = sum(k_["bytes_per_launch"] for k_ in parts)
+                us_sa = sum(k_["us_per_launch"] for k_ in parts)
+                gbs_sa = nb_sa / (us_sa * 1e-6) / 1e9
+                kernels["score_plus_attn"] = {"us_per_launch": round(us_sa, 3), "bytes_per_launch": int(nb_sa),
+                                              "GBps": round(gbs_sa, 1), "peak_GBps": PEAK_HBM / 1e9,
+                                              "frac": round(gbs_sa * 1e9 / PEAK_HBM, 4)}
             if snap:
                 # a fixed selection runs no scoring: attention dominates
                 fused = "attn" in kernels
@@ -473,6 +488,16 @@ def main() -> int:
                             "achieved": sc["GBps"], "peak": PEAK_HBM / 1e9, "unit": "GB/s", "frac": sc["frac"],
                             "traffic": traffic, "bytes_per_launch": sc["bytes_per_launch"],
                             "us_per_launch": sc["us_per_launch"]}
+
+        # the same fractions against the read ceiling measured in this run
+        read_ceiling = peaks.get("hbm_read_TBps")
+        if read_ceiling:
+            for kk in kernels.values():
+                if kk.get("GBps") and kk.get("peak_GBps") == PEAK_HBM / 1e9:
+                    kk["frac_of_read_ceiling"] = round(kk["GBps"] / (read_ceiling * 1e3), 4)
+            if roofline:
+                roofline["frac_of_read_ceiling"] = round(roofline["achieved"] / (read_ceiling * 1e3), 4)
+                roofline["read_ceiling_GBps"] = round(read_ceiling * 1e3, 1)
 
         fetch_gbs = kernels.get("fetch", {}).get("GBps") if kernels else None
         closed_form = None
@@ -513,7 +538,8 @@ def main() -> int:
             threads = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or (os.cpu_count() or 1)
             cores = min(threads, os.cpu_count() or 1, len(seqs) * wl.h_kv)
             cpu_baseline = {"value": round(1.0 / (per_seq_step * wl.b), 4), "unit": "layer-steps/s", "cores": cores,
-                            "kind": "oracle", "cpu_model": cpu_model(),
+                            "kind": "oracle", "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+                            "omp_threads": threads,
                             "sample": f"{n_done} decode steps (steps 0..{nq - 1}, cycled) of sequences {seqs} "
                                       f"(of {wl.b}) of layer {spot_layer}; {cpu_s:.1f} s of CPU time; "
                                       f"scaled to all {wl.b} sequences"}

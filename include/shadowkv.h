@@ -188,6 +188,8 @@ int shadowkv_append(skv_layer *layer, const void *k_new, const void *v_new, void
  * The hit / miss counters count the selection as one step.
  */
 int shadowkv_snapkv_select(skv_layer *layer, const void *q_obs, int w_obs, int pool, void *stream);
+/* (A second selection before any decode step first fetches the V that the
+ * previous selection still owes, on `stream`, so the cache stays lossless.) */
 
 /*
  * Algorithm 2 (Decoding): one step of one layer for all b sequences.
@@ -212,7 +214,8 @@ int shadowkv_decode_step(skv_layer *layer, const void *q, void *out, void *strea
  * lossless, so outputs do not change; only the hit counts do. */
 int shadowkv_reset_cache(skv_layer *layer, void *stream);
 
-/* Read the counters (synchronizes the layer's streams). */
+/* Read the counters.  Waits for the work this layer's calls enqueued last
+ * (on whatever stream they were given), not for the rest of the device. */
 int shadowkv_get_stats(skv_layer *layer, skv_stats *out);
 int shadowkv_reset_stats(skv_layer *layer);
 
@@ -255,7 +258,7 @@ int shadowkv_set_overlap(skv_layer *layer, int enable);
 
 /* Per-kernel timing with HIP events recorded on the stream each kernel runs
  * on.  While enabled, every decode step records a start/stop pair around
- * each kernel.  shadowkv_get_timing synchronizes, writes the summed
+ * each kernel.  shadowkv_get_timing waits for those events, writes the summed
  * milliseconds of each kernel (SKV_K_COUNT entries) and the number of steps
  * they cover, and clears the record. */
 enum {
@@ -285,6 +288,14 @@ const char *shadowkv_last_error(void);
  * hit rate; the result has the unit of b_gpu. */
 double shadowkv_equiv_bandwidth(double S, double C, double K, double O, double alpha,
                                 double b_gpu, double b_pcie);
+
+/* Measurement aid, not part of the method: the best rate (1e9 B/s) at which a
+ * plain streaming kernel reads `bytes` (>= 1 MiB; make it larger than the
+ * device's last-level cache) of device memory at `buf`, over `reps` passes at
+ * each of a few launch shapes.  The caller owns `buf`; its contents are read,
+ * never written.  Runs on `stream` and waits for it.  SKV_E_INVAL for a null
+ * pointer, reps < 1 or too few bytes; SKV_E_HIP if a launch or event fails. */
+int shadowkv_probe_hbm_read(const void *buf, size_t bytes, int reps, void *stream, double *gbps_out);
 
 #ifdef __cplusplus
 }

@@ -46,8 +46,16 @@ class _Cfg(ctypes.Structure):
         ("d", ctypes.c_int32), ("s", ctypes.c_int32), ("c", ctypes.c_int32),
         ("r", ctypes.c_int32), ("o", ctypes.c_int32), ("k", ctypes.c_int32),
         ("w", ctypes.c_int32), ("rope_base", ctypes.c_double), ("bf16", ctypes.c_int32),
-        ("n_app", ctypes.c_int32),
+        ("n_app", ctypes.c_int32), ("plant", ctypes.c_int32),
     ]
+
+
+# Deliberate mistakes orc_attend can plant in the rebuilt-key block; only the
+# tests that show a parity case discriminates use them.  PLANT_BF16_REBUILT is
+# no mistake: the rebuilt, rotated keys rounded to bfloat16 before the logits,
+# as the bfloat16 kernels do (the share of the error bar that rounding uses).
+(PLANT_NONE, PLANT_ZERO_REBUILT, PLANT_NO_ROPE_REBUILT, PLANT_POS_PLUS_ONE, PLANT_NO_OUTLIERS,
+ PLANT_BF16_REBUILT) = range(6)
 
 
 @dataclass(frozen=True)
@@ -70,9 +78,9 @@ class Shape:
     def n(self) -> int:
         return self.s // self.c
 
-    def _c(self, n_app: int = 0) -> _Cfg:
+    def _c(self, n_app: int = 0, plant: int = PLANT_NONE) -> _Cfg:
         return _Cfg(self.b, self.h_q, self.h_kv, self.d, self.s, self.c, self.r,
-                    self.o, self.k, self.w, float(self.rope_base), int(self.bf16), int(n_app))
+                    self.o, self.k, self.w, float(self.rope_base), int(self.bf16), int(n_app), int(plant))
 
 
 def build(force: bool = False) -> str:
@@ -240,13 +248,14 @@ def _n_app(shape: Shape, meta: dict) -> int:
 # --------------------------------------------------------------------------
 # Algorithm 2
 # --------------------------------------------------------------------------
-def attend(shape: Shape, q, sel, A, B, v_host, meta: dict) -> np.ndarray:
-    """Algorithm 2 steps 3-4 for a given selection (b, h_kv, k)."""
+def attend(shape: Shape, q, sel, A, B, v_host, meta: dict, plant: int = PLANT_NONE) -> np.ndarray:
+    """Algorithm 2 steps 3-4 for a given selection (b, h_kv, k).  `plant`
+    (tests only) plants one of the PLANT_* mistakes."""
     q, A, B, v_host = _f64(q), _f64(A), _f64(B), _f64(v_host)
     sel = np.ascontiguousarray(sel, dtype=np.int32)
     assert sel.shape == (shape.b, shape.h_kv, shape.k)
     out = np.empty((shape.b, shape.h_q, shape.d))
-    cfg = shape._c(_n_app(shape, meta))
+    cfg = shape._c(_n_app(shape, meta), plant)
     m = {key: _f64(meta[key]) for key in ("k_out", "v_out", "k_loc", "v_loc")}
     rc = _lib().orc_attend(ctypes.byref(cfg), _p(q, _D), _p(sel, _I32), _p(A, _D), _p(B, _D),
                            _p(v_host, _D), _p(m["k_out"], _D), _p(m["v_out"], _D),

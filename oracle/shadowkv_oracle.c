@@ -61,7 +61,25 @@ typedef struct {
     int32_t bf16;    /* 1: stored tensors are bfloat16         */
     int32_t n_app;   /* decode tokens appended after the window:
                         the local block holds w + n_app tokens  */
+    int32_t plant;   /* 0 always, except in the tests that show a
+                        parity case would catch a broken rebuild:
+                        ORC_PLANT_* below                       */
 } orc_cfg;
+
+/* Deliberate mistakes in the rebuilt-key block of orc_attend, planted only by
+ * the tests that check a parity case discriminates (a correct kernel must be
+ * far closer to the unplanted oracle than any of these). */
+enum {
+    ORC_PLANT_NONE = 0,
+    ORC_PLANT_ZERO_REBUILT = 1,     /* rebuilt keys replaced by zeros          */
+    ORC_PLANT_NO_ROPE_REBUILT = 2,  /* rebuilt keys left unrotated             */
+    ORC_PLANT_POS_PLUS_ONE = 3,     /* rebuilt keys rotated one position late  */
+    ORC_PLANT_NO_OUTLIERS = 4,      /* outlier block left out of the softmax   */
+    /* Not a mistake: rebuilt, rotated keys rounded to bfloat16 before the
+     * logits, the quantisation point of the bfloat16 kernels.  Its distance
+     * from the unplanted result is the share of the error bar it uses. */
+    ORC_PLANT_BF16_REBUILT = 5
+};
 
 enum { ORC_OK = 0, ORC_E_SHAPE = -2, ORC_E_NOMEM = -4 };
 
@@ -303,7 +321,15 @@ int orc_attend(const orc_cfg *cfg, const double *q, const int32_t *sel,
                     row[i] = acc;
                 }
                 size_t dst = ((size_t)o * c + (size_t)a * c + t) * d;
-                orc_rope_row(row, Ks + dst, d, (double)pos, cfg->rope_base);
+                if (cfg->plant == ORC_PLANT_ZERO_REBUILT)
+                    for (int32_t i = 0; i < d; ++i) row[i] = 0.0;
+                if (cfg->plant == ORC_PLANT_NO_ROPE_REBUILT)
+                    memcpy(Ks + dst, row, sizeof(double) * d);
+                else
+                    orc_rope_row(row, Ks + dst, d, (double)pos + (cfg->plant == ORC_PLANT_POS_PLUS_ONE),
+                                 cfg->rope_base);
+                if (cfg->plant == ORC_PLANT_BF16_REBUILT)
+                    for (int32_t i = 0; i < d; ++i) Ks[dst + i] = orc_round_bf16(Ks[dst + i]);
                 memcpy(Vs + dst, v_host + ((size_t)bh * s + (size_t)pos) * d, sizeof(double) * d);
             }
         }
@@ -313,6 +339,7 @@ int orc_attend(const orc_cfg *cfg, const double *q, const int32_t *sel,
         memcpy(Vs + base, v_loc + (size_t)bh * w * d, sizeof(double) * (size_t)w * d);
 
         /* softmax(q K^T / sqrt(d)) V for each query head of the group. */
+        const int32_t j0 = cfg->plant == ORC_PLANT_NO_OUTLIERS ? o * c : 0;
         for (int32_t gi = 0; gi < G; ++gi) {
             int32_t g = (bh % H) * G + gi;
             const double *qg = q + ((size_t)b * Hq + g) * d;
@@ -320,7 +347,7 @@ int orc_attend(const orc_cfg *cfg, const double *q, const int32_t *sel,
             for (int32_t j = 0; j < nk; ++j) {
                 double acc = 0.0;
                 for (int32_t i = 0; i < d; ++i) acc += qg[i] * Ks[(size_t)j * d + i];
-                logit[j] = acc * scale;
+                logit[j] = j < j0 ? -INFINITY : acc * scale;
                 if (logit[j] > mx) mx = logit[j];
             }
             double z = 0.0;

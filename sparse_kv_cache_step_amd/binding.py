@@ -30,6 +30,7 @@ EXPORTS = (
     "shadowkv_tensor_bytes", "shadowkv_read", "shadowkv_set_overlap", "shadowkv_set_timing",
     "shadowkv_get_timing",
     "shadowkv_host_alloc", "shadowkv_host_free", "shadowkv_last_error", "shadowkv_equiv_bandwidth",
+    "shadowkv_probe_hbm_read",
 )
 
 
@@ -84,6 +85,8 @@ def lib() -> ctypes.CDLL:
             "shadowkv_host_free": (ctypes.c_int, [_VP]),
             "shadowkv_last_error": (ctypes.c_char_p, []),
             "shadowkv_equiv_bandwidth": (ctypes.c_double, [ctypes.c_double] * 7),
+            "shadowkv_probe_hbm_read": (ctypes.c_int, [_VP, ctypes.c_size_t, ctypes.c_int, _VP,
+                                                       ctypes.POINTER(ctypes.c_double)]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -105,6 +108,15 @@ def shadowkv_last_error() -> str:
 
 def shadowkv_equiv_bandwidth(S, C, K, O, alpha, b_gpu, b_pcie) -> float:
     return lib().shadowkv_equiv_bandwidth(S, C, K, O, alpha, b_gpu, b_pcie)
+
+
+def shadowkv_probe_hbm_read(buf, nbytes: int, reps: int, stream) -> float:
+    """Streaming-read ceiling (GB/s) over `nbytes` of device memory at `buf`."""
+    out = ctypes.c_double()
+    rc = lib().shadowkv_probe_hbm_read(buf, nbytes, reps, stream, ctypes.byref(out))
+    if rc != SKV_OK:
+        raise ShadowKVError(rc, "read probe failed")
+    return out.value
 
 
 def shadowkv_layer_create(cfg: skv_config) -> int:

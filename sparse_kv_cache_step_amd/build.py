@@ -24,15 +24,10 @@ FLAGS = [
 ]
 
 
-def build(force: bool = True, verbose: bool = False) -> str:
-    """Compile every HIP source into one shared library.  With force=False
-    the library is rebuilt only when a source or header is newer."""
-    if not force and os.path.exists(LIB_PATH):
-        t = os.path.getmtime(LIB_PATH)
-        if all(os.path.getmtime(f) <= t for f in SOURCES + HEADERS):
-            return LIB_PATH
-    tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-o", tmp, *SOURCES]
+OBJ_DIR = os.path.join(PKG, "_build")
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -41,6 +36,26 @@ def build(force: bool = True, verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
+
+
+def build(force: bool = True, verbose: bool = False) -> str:
+    """Compile every HIP source (one hipcc process each, in parallel) and
+    link them into one shared library.  With force=False the library is
+    rebuilt only when a source or header is newer."""
+    if not force and os.path.exists(LIB_PATH):
+        t = os.path.getmtime(LIB_PATH)
+        if all(os.path.getmtime(f) <= t for f in SOURCES + HEADERS):
+            return LIB_PATH
+    from concurrent.futures import ThreadPoolExecutor
+
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    objs = [os.path.join(OBJ_DIR, os.path.basename(src) + ".o") for src in SOURCES]
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        list(ex.map(lambda so: _run([HIPCC, *compile_flags, "-c", "-o", so[1], so[0]], verbose),
+                    zip(SOURCES, objs)))
+    tmp = LIB_PATH + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-fPIC", "-shared", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

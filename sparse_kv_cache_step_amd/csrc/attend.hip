@@ -226,9 +226,9 @@ __device__ __forceinline__ void qk_static_tile(const uint16_t *__restrict__ q, c
 // (i, i + d/2) sits in one lane and each lane rotates its own key at its own
 // position.  The logits are a second contraction on MFMA: in a fixed
 // permutation of the head dimension (dims 32p + 4*(l >> 4) + e and
-// 32p + 16 + 4*(l >> 4) + e of dim pair p), the rotated keys, rounded to
-// bfloat16, already sit in the B-operand layout, and the group's queries,
-// permuted the same way, are the A operand (query heads as rows).
+// 32p + 16 + 4*(l >> 4) + e of dim pair p), the rotated keys, split into two
+// bfloat16 terms, already sit in the B-operand layout, and the group's
+// queries, permuted the same way, are the A operand (query heads as rows).
 // ---------------------------------------------------------------------------
 // v_permlane32_swap exchanges the upper 32 lanes of its first operand with the
 // lower 32 lanes of its second, so the sum of the two results holds, in lanes
@@ -245,14 +245,33 @@ __device__ __forceinline__ float swap_sum16(float lo, float hi) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-__device__ __forceinline__ bf16x8 pack_bf16x8(f32x4 a, f32x4 b) {
-    bf16x8 r;
+// The rebuilt, rotated keys enter the logit MFMA as two bfloat16 terms,
+// hi = bf16(x) and lo = bf16(x - hi) (x - hi is exact in binary32), so
+// q . x = q . hi + q . lo carries ~16 significant bits of every key instead
+// of bfloat16's 8: one rounding of the keys would cost up to ~1e-2 of output
+// at sharp attention, the same order as the bfloat16 error bar.
+__device__ __forceinline__ void split_bf16x8(f32x4 a, f32x4 b, bf16x8 &hi, bf16x8 &lo) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        r[e] = static_cast<__bf16>(a[e]);
-        r[4 + e] = static_cast<__bf16>(b[e]);
+        const __bf16 ha = static_cast<__bf16>(a[e]), hb = static_cast<__bf16>(b[e]);
+        hi[e] = ha;
+        hi[4 + e] = hb;
+        lo[e] = static_cast<__bf16>(a[e] - static_cast<float>(ha));
+        lo[4 + e] = static_cast<__bf16>(b[e] - static_cast<float>(hb));
     }
-    return r;
+}
+
+// logits of one 16-key block: lg += q . (hi + lo) over the NP 32-dim pairs
+template <int NP>
+__device__ __forceinline__ f32x4 logits_hilo(const bf16x8 *qa, const f32x4 *acc, f32x4 lg) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        bf16x8 hi, lo;
+        split_bf16x8(acc[2 * p], acc[2 * p + 1], hi, lo);
+        lg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[p], hi, lg, 0, 0, 0);
+        lg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[p], lo, lg, 0, 0, 0);
+    }
+    return lg;
 }
 
 // One launch takes both key sets.  With rebuilt keys (ts > 0 workgroups per
@@ -396,10 +415,7 @@ __global__ __launch_bounds__(256) void qk_mfma_kernel(const uint16_t *__restrict
 
         // logits[head, key] = sum over dims of q . K_rot: lane (quad, row)
         // ends with heads 4*quad + e of key kb0 + row
-        f32x4 lg = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int p = 0; p < NP; ++p)
-            lg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[p], pack_bf16x8(acc[2 * p], acc[2 * p + 1]), lg, 0, 0, 0);
+        const f32x4 lg = logits_hilo<NP>(qa, acc, f32x4{0.f, 0.f, 0.f, 0.f});
         const int key = kb0 + row;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -567,10 +583,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
                         acc[hb + HB][e] = x2 * cs + x1 * sn;
                     }
                 }
-#pragma unroll
-                for (int p = 0; p < NP; ++p)
-                    lg = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[p], pack_bf16x8(acc[2 * p], acc[2 * p + 1]), lg, 0,
-                                                                 0, 0);
+                lg = logits_hilo<NP>(qa, acc, lg);
             }
             // lane (quad, row): heads 4*quad + e of key kb0 + row
             const bool kv = active && kb0 + row < KC;

@@ -205,6 +205,10 @@ struct skv_layer {
     // shared per-device streams for the host-V fetch and the key rebuild
     hipStream_t copy = nullptr, comp = nullptr;
     hipEvent_t ev_sel = nullptr, ev_fetch = nullptr, ev_qk = nullptr;
+    // recorded on the caller's stream at the end of every call that enqueues
+    // work: the counters and timings are read after it, so reading them waits
+    // for this layer's work only
+    hipEvent_t ev_done = nullptr;
     int fetch_waves = 128;
     int score_wgs = 0;  // workgroups of the scoring kernel (0: two tiles per wave)
     int n_app = 0;      // decode tokens appended to the local block since the last prefill / load
@@ -254,6 +258,13 @@ void release(skv_layer *ly) {
     if (ly->ev_sel) (void)hipEventDestroy(ly->ev_sel);
     if (ly->ev_fetch) (void)hipEventDestroy(ly->ev_fetch);
     if (ly->ev_qk) (void)hipEventDestroy(ly->ev_qk);
+    if (ly->ev_done) (void)hipEventDestroy(ly->ev_done);
+}
+
+// The end of the layer's latest enqueued work on `st`.
+int mark_done(skv_layer *ly, hipStream_t st) {
+    SKV_HIP(hipEventRecord(ly->ev_done, st));
+    return SKV_OK;
 }
 
 hipEvent_t pool_event(skv_layer *ly) {
@@ -442,7 +453,8 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     ly->comp = ds->comp;
     if (hipEventCreateWithFlags(&ly->ev_sel, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&ly->ev_fetch, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&ly->ev_qk, hipEventDisableTiming) != hipSuccess)
+        hipEventCreateWithFlags(&ly->ev_qk, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ly->ev_done, hipEventDisableTiming) != hipSuccess)
         return bail(fail(SKV_E_HIP, "creating events failed"));
 
     // Host-V fetch: enough waves to keep PCIe busy (a few hundred 2 KB chunk
@@ -499,7 +511,7 @@ int shadowkv_prefill_meta(skv_layer *ly, const void *k_pre, const void *k_rope, 
     ly->v_host_dev = vdev;
     ly->n_app = 0;
     ly->ready = true;
-    return SKV_OK;
+    return mark_done(ly, st);
 }
 
 int shadowkv_load_meta(skv_layer *ly, const void *landmarks, const int32_t *outliers, const void *k_out,
@@ -537,7 +549,7 @@ int shadowkv_load_meta(skv_layer *ly, const void *landmarks, const int32_t *outl
     ly->v_host_dev = vdev;
     ly->n_app = 0;
     ly->ready = true;
-    return SKV_OK;
+    return mark_done(ly, st);
 }
 
 int shadowkv_append(skv_layer *ly, const void *k_new, const void *v_new, void *stream) {
@@ -550,7 +562,7 @@ int shadowkv_append(skv_layer *ly, const void *k_new, const void *v_new, void *s
     SKV_HIP(skv::launch_append(dm, k_new, v_new, ly->theta, ly->k_loc, ly->v_loc, dm.w + ly->n_app,
                                dm.s + ly->n_app, st));
     ++ly->n_app;
-    return SKV_OK;
+    return mark_done(ly, st);
 }
 
 int shadowkv_snapkv_select(skv_layer *ly, const void *q_obs, int w_obs, int pool, void *stream) {
@@ -564,6 +576,14 @@ int shadowkv_snapkv_select(skv_layer *ly, const void *q_obs, int w_obs, int pool
     if (static_cast<double>(dm.b) * dm.hkv * dm.G * w_obs * dm.d * dm.esize >= static_cast<double>(1u << 30))
         return fail(SKV_E_SHAPE, "q_obs must be smaller than 1 GiB");
     hipStream_t st = static_cast<hipStream_t>(stream);
+    // A selection made by an earlier call whose missing V no decode step has
+    // fetched yet: its chunks already own their cache slots, so they would
+    // count as hits of this selection.  Fetch them first, which keeps the
+    // cache lossless.
+    if (ly->fetch_pending) {
+        SKV_HIP(skv::launch_fetch(dm, ly->v_host_dev, ly->vc, ly->misses, ly->miss_count, ly->fetch_waves, st));
+        ly->fetch_pending = false;
+    }
     // passes of up to kMaxGroup (head, window position) rows per KV head
     const int wp_max = std::max(1, skv::kMaxGroup / dm.G);
     for (int o0 = 0; o0 < w_obs; o0 += wp_max) {
@@ -582,7 +602,7 @@ int shadowkv_snapkv_select(skv_layer *ly, const void *q_obs, int w_obs, int pool
                                ly->select_keys_in_lds, st));
     ly->fixed = true;
     ly->fetch_pending = true;
-    return SKV_OK;
+    return mark_done(ly, st);
 }
 
 int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) {
@@ -669,7 +689,7 @@ int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) 
         SKV_HIP(skv::launch_combine(dm, ly->part_ml, ly->part_acc, out, dm.pv_tiles, st));
     }
     if (ly->timing) ++ly->timed_steps;
-    return SKV_OK;
+    return mark_done(ly, st);
 }
 
 int shadowkv_reset_cache(skv_layer *ly, void *stream) {
@@ -678,14 +698,17 @@ int shadowkv_reset_cache(skv_layer *ly, void *stream) {
     SKV_HIP(hipStreamWaitEvent(st, ly->ev_fetch, 0));
     SKV_HIP(skv::launch_fill_i32(ly->slot_chunk, -1, static_cast<size_t>(ly->dm.b) * ly->dm.hkv * ly->dm.cap, st));
     ly->fixed = ly->fetch_pending = false;
-    return SKV_OK;
+    return mark_done(ly, st);
 }
 
+// The counters are read and cleared on the layer's copy stream after the
+// layer's latest work: neither waits for anything else on the device.
 int shadowkv_get_stats(skv_layer *ly, skv_stats *out) {
     if (!ly || !out) return fail(SKV_E_INVAL, "null argument");
-    SKV_HIP(hipDeviceSynchronize());
     unsigned long long c[4] = {0, 0, 0, 0};
-    SKV_HIP(hipMemcpy(c, ly->counters, sizeof(c), hipMemcpyDeviceToHost));
+    SKV_HIP(hipStreamWaitEvent(ly->copy, ly->ev_done, 0));
+    SKV_HIP(hipMemcpyAsync(c, ly->counters, sizeof(c), hipMemcpyDeviceToHost, ly->copy));
+    SKV_HIP(hipStreamSynchronize(ly->copy));
     out->hits = static_cast<int64_t>(c[0]);
     out->misses = static_cast<int64_t>(c[1]);
     out->steps = static_cast<int64_t>(c[2]);
@@ -695,8 +718,9 @@ int shadowkv_get_stats(skv_layer *ly, skv_stats *out) {
 
 int shadowkv_reset_stats(skv_layer *ly) {
     if (!ly) return fail(SKV_E_INVAL, "layer is null");
-    SKV_HIP(hipDeviceSynchronize());
-    SKV_HIP(hipMemset(ly->counters, 0, 4 * sizeof(unsigned long long)));
+    SKV_HIP(hipStreamWaitEvent(ly->copy, ly->ev_done, 0));
+    SKV_HIP(skv::launch_fill_i32(reinterpret_cast<int32_t *>(ly->counters), 0, 8, ly->copy));
+    SKV_HIP(hipStreamSynchronize(ly->copy));
     return SKV_OK;
 }
 
@@ -756,10 +780,10 @@ int shadowkv_set_timing(skv_layer *ly, int enable) {
 
 int shadowkv_get_timing(skv_layer *ly, double *ms_out, int64_t *steps_out) {
     if (!ly || !ms_out) return fail(SKV_E_INVAL, "null argument");
-    SKV_HIP(hipDeviceSynchronize());
     for (int i = 0; i < SKV_K_COUNT; ++i) ms_out[i] = 0.0;
     for (const Mark &m : ly->marks) {
         float ms = 0.f;
+        SKV_HIP(hipEventSynchronize(m.stop));  // this kernel's own stream, up to its stop
         SKV_HIP(hipEventElapsedTime(&ms, m.start, m.stop));
         ms_out[m.kernel] += ms;
     }

@@ -15,7 +15,10 @@ Pre-RoPE keys are a seeded low-rank factor product plus Gaussian noise,
 with U_b (s x R) and W_b (R x h_kv*d) entries N(0,1)/sqrt(R).  Values and
 queries are N(0, 1).  Queries drift between steps as
     Q_t = rho Q_{t-1} + sqrt(1 - rho^2) N(0, 1),
-so consecutive steps select overlapping chunk sets.
+so consecutive steps select overlapping chunk sets.  A workload may scale the
+queries by a constant (q_scale) after drawing them: with N(0,1) queries and
+keys of norm ~1 the logits q.k/sqrt(d) have a spread of ~0.1 and attention is
+nearly uniform, so a larger scale makes outputs depend sharply on every key.
 
 Seeds: numpy SeedSequence([workload, layer, sequence, tag]) with tag 0 = U,
 1 = W, 2 = noise, 3 = V, 4 = Q_0, 5 = Q innovations, 6 = special-chunk choice.
@@ -60,6 +63,7 @@ class Workload:
     n_noisy_chunks: int = 0   # chunks whose noise term is scaled
     noisy_scale: float = 1.0
     rope_base: float = 10000.0
+    q_scale: float = 1.0      # every query is drawn, then multiplied by this (sharper attention)
 
     @property
     def n(self) -> int:
@@ -177,7 +181,7 @@ def queries_numpy(wl: Workload, layer: int = 0, steps: int | None = None) -> np.
         for t in range(steps):
             if t > 0:
                 q = wl.rho * q + np.sqrt(1.0 - wl.rho ** 2) * innov.standard_normal((wl.h_q, wl.d))
-            out[t, seq] = _store(wl, q)
+            out[t, seq] = _store(wl, q * wl.q_scale)
     return out
 
 
@@ -246,5 +250,5 @@ def queries_torch(wl: Workload, layer: int, device, steps: int | None = None):
         for t in range(steps):
             if t > 0:
                 q = wl.rho * q + a * torch.randn((wl.h_q, wl.d), generator=g, device=device)
-            out[t, seq] = _tstore(torch, wl, q)
+            out[t, seq] = _tstore(torch, wl, q * wl.q_scale)
     return out

@@ -20,6 +20,12 @@ from sparse_kv_cache_step_amd import synth
 NEAR_TIE_REL = 1e-5
 OUT_TOL = {False: 1e-4, True: 2e-2}
 
+# Queries x8 sharpen attention so that a broken key rebuild misses the
+# bfloat16 bar (tests/test_parity_discrimination.py shows it on these inputs):
+# the Llama-3-8B-shaped 32K single layer, four i.i.d. steps.
+SHARP_32K = synth.LLAMA_32K.with_(q_scale=8.0, steps=4)
+SHARP_Q = 8.0
+
 
 def log(*a):
     print(*a, flush=True, file=sys.stderr)

@@ -16,8 +16,8 @@ import pytest
 import torch
 
 import oracle
-from parity_helpers import (OUT_TOL, bf16_ulp, check_outliers, check_selection, layer_kwargs, log, oracle_shape,
-                            tdtype, to_dev, to_np)
+from parity_helpers import (OUT_TOL, SHARP_32K, bf16_ulp, check_outliers, check_selection, layer_kwargs, log,
+                            oracle_shape, tdtype, to_dev, to_np)
 from sparse_kv_cache_step_amd import binding as skv
 from sparse_kv_cache_step_amd import synth
 from sparse_kv_cache_step_amd.setup import svd_factors
@@ -34,6 +34,13 @@ CASES = {
     "fp32-chunk4": T.with_(s=512, c=4, o=3, k=9, w=12, steps=2, rho=0.9),
     # the Llama-3-8B-shaped 32K single layer, 16 steps
     "bf16-llama-32k": synth.LLAMA_32K,
+    # the same with queries x8: attention sharp enough that zeroed, unrotated
+    # or misplaced rebuilt keys miss the bar by 5-150x (shown on the CPU)
+    "bf16-llama-32k-sharp": SHARP_32K,
+    # sharp queries through the separate QK + PV kernels (GQA 16 and 8)
+    "bf16-g16-sharp": synth.GLM_244K.with_(b=2, s=12000, o=10, k=23, steps=3, q_scale=8.0),
+    "bf16-g8-sharp": synth.LLAMA_32K.with_(b=2, h_q=32, h_kv=4, s=4096, r=64, o=6, k=20, w=24, steps=3, rho=0.9,
+                                           true_rank=40, q_scale=8.0),
     # GLM-shaped GQA 16, ragged n = 1500, rank 160
     "bf16-g16-ragged": synth.GLM_244K.with_(b=2, s=12000, o=10, k=23, steps=4),
     # one query head per KV head, d = 64, rank padded (40 -> 64)
@@ -426,6 +433,48 @@ def test_snapkv_selection_matches_oracle(case):
         assert e.value.code == skv.SKV_E_SHAPE
     with pytest.raises(ValueError):
         layer.snapkv_select(q_bad[:, :1], pool)
+    layer.close()
+    hb.free()
+
+
+def test_snapkv_select_twice_then_decode():
+    """Two SnapKV-style selections with different windows and no decode step
+    between them, then decode steps: the second selection's hits must be the
+    set intersection with the first (whose V it fetches first), the cache
+    must hold exactly the V of the second selection, and every output must
+    match the oracle's attention over it."""
+    wl = synth.LLAMA_32K.with_(b=2, s=8192, k=16, rho=0.5)
+    w_obs, pool = 4, 3
+    shape = oracle_shape(wl)
+    k_pre, v = synth.k_pre_numpy(wl), synth.v_numpy(wl)
+    qs = synth.queries_numpy(wl, steps=2 * w_obs + 2)
+    meta = oracle.prefill(shape, k_pre, v)
+    A_o, B_o = oracle.svd_factors(shape, k_pre)
+    layer, hb = _gpu_state(wl, k_pre, v)
+    dt = tdtype(wl)
+    sim = oracle.CacheSim(wl.b, wl.h_kv)
+    hits_total = 0
+    for i in range(2):
+        q_obs = np.ascontiguousarray(qs[i * w_obs:(i + 1) * w_obs].transpose(1, 2, 0, 3))
+        layer.snapkv_select(to_dev(q_obs, dt), pool)
+        torch.cuda.synchronize()
+        ora = oracle.snapkv_select(shape, q_obs, meta, pool)
+        sel_g = to_np(layer.read(skv.SKV_T_SELECTION))
+        check_selection(sel_g, ora["sel"], ora["pooled"], meta["cand"])
+        hits_total += sim.step(sel_g)[0]
+        assert layer.stats()["hits"] == hits_total
+    log(f"[snapkv-twice] hits of the second selection: {hits_total} (of {wl.b * wl.h_kv * wl.k})")
+    for t in range(2):
+        q_d = to_dev(qs[2 * w_obs + t], dt)
+        out_d = torch.empty_like(q_d)
+        layer.decode_step(q_d, out_d)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_np(layer.read(skv.SKV_T_SELECTION)), sel_g)
+        ref = oracle.attend(shape, qs[2 * w_obs + t], sel_g, A_o, B_o, v, meta)
+        err = float(np.max(np.abs(to_np(out_d) - ref)))
+        log(f"[snapkv-twice] decode {t}: max|out - oracle| = {err:.3g}")
+        assert err <= OUT_TOL[True]
+        _check_cache_lossless(wl, layer, v, sel_g)
     layer.close()
     hb.free()
 
