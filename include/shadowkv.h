@@ -210,6 +210,24 @@ int shadowkv_snapkv_select(skv_layer *layer, const void *q_obs, int w_obs, int p
  */
 int shadowkv_decode_step(skv_layer *layer, const void *q, void *out, void *stream);
 
+/*
+ * shadowkv_decode_step for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, same results; it calls no hipMalloc, hipFree
+ * or other allocating routine.  The step's scratch (landmark scores, tile
+ * statistics, group scores, selection keys or candidates, logits, split
+ * partials) lives in one 128 MiB device array per GPU, held from the first
+ * call on that GPU until the process ends, instead of in the layer's own
+ * buffers.  Every layer and every call on one GPU shares that array: calls
+ * that overlap on one GPU (different streams, not ordered) race and give
+ * wrong results.  Per-kernel timing is not recorded, and the score reads of
+ * shadowkv_read (SKV_T_SCORES, SKV_T_GROUP_SCORES) keep the last
+ * shadowkv_decode_step's values.  SKV_E_SHAPE, before any work is enqueued,
+ * when the layer's step needs more than 128 MiB of scratch (e.g. b = 48 at
+ * 60K with GQA 4 needs ~84 MB, the GLM-shaped 244K b = 12 ~64 MB).
+ */
+int shadowkv_decode_step_noalloc(skv_layer *layer, const void *q, void *out, void *stream);
+
 /* Empty the resident V cache (all later chunks load again).  The cache is
  * lossless, so outputs do not change; only the hit counts do. */
 int shadowkv_reset_cache(skv_layer *layer, void *stream);

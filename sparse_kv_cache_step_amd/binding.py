@@ -26,7 +26,8 @@ SKV_K_COUNT = len(KERNELS)
 
 EXPORTS = (
     "shadowkv_layer_create", "shadowkv_layer_destroy", "shadowkv_prefill_meta", "shadowkv_load_meta",
-    "shadowkv_append", "shadowkv_snapkv_select", "shadowkv_decode_step", "shadowkv_reset_cache", "shadowkv_get_stats", "shadowkv_reset_stats",
+    "shadowkv_append", "shadowkv_snapkv_select", "shadowkv_decode_step", "shadowkv_decode_step_noalloc",
+    "shadowkv_reset_cache", "shadowkv_get_stats", "shadowkv_reset_stats",
     "shadowkv_tensor_bytes", "shadowkv_read", "shadowkv_set_overlap", "shadowkv_set_timing",
     "shadowkv_get_timing",
     "shadowkv_host_alloc", "shadowkv_host_free", "shadowkv_last_error", "shadowkv_equiv_bandwidth",
@@ -72,6 +73,7 @@ def lib() -> ctypes.CDLL:
             "shadowkv_append": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
             "shadowkv_snapkv_select": (ctypes.c_int, [_VP, _VP, ctypes.c_int, ctypes.c_int, _VP]),
             "shadowkv_decode_step": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
+            "shadowkv_decode_step_noalloc": (ctypes.c_int, [_VP, _VP, _VP, _VP]),
             "shadowkv_reset_cache": (ctypes.c_int, [_VP, _VP]),
             "shadowkv_get_stats": (ctypes.c_int, [_VP, ctypes.POINTER(skv_stats)]),
             "shadowkv_reset_stats": (ctypes.c_int, [_VP]),
@@ -147,6 +149,10 @@ def shadowkv_snapkv_select(h, q_obs, w_obs, pool, stream) -> None:
 
 def shadowkv_decode_step(h, q, out, stream) -> None:
     _check(lib().shadowkv_decode_step(h, q, out, stream))
+
+
+def shadowkv_decode_step_noalloc(h, q, out, stream) -> None:
+    _check(lib().shadowkv_decode_step_noalloc(h, q, out, stream))
 
 
 def shadowkv_reset_cache(h, stream) -> None:
@@ -326,6 +332,9 @@ class Layer:
 
     def decode_step(self, q, out, stream=None):
         shadowkv_decode_step(self.h, self._dev("q", q), self._dev("out", out), _stream_ptr(stream))
+
+    def decode_step_noalloc(self, q, out, stream=None):
+        shadowkv_decode_step_noalloc(self.h, self._dev("q", q), self._dev("out", out), _stream_ptr(stream))
 
     def reset_cache(self, stream=None):
         shadowkv_reset_cache(self.h, _stream_ptr(stream))

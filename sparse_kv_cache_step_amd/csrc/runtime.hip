@@ -228,6 +228,21 @@ struct skv_layer {
     int64_t timed_steps = 0;
 };
 
+// Per-step scratch of a decode step: written and read within one step.
+struct StepScratch {
+    float *P;            // U (b, h_kv, n, G): exp(P - tile max)
+    float2 *stats;       // (b, h_kv, G, ceil(n/64)) tile (max, sum)
+    float *S2;           // (b, h_kv, n) group scores
+    uint32_t *keys;      // (b, h_kv, n) selection keys (one-pass selection)
+    uint2 *kbounds;      // (b, h_kv, group slices) key bounds
+    uint32_t *cand_key;  // (b, h_kv, slices, k) slice candidates (two-pass selection)
+    int32_t *cand_idx;
+    int32_t *cand_count; // (b, h_kv, slices)
+    float *logits;       // (b, h_q, NK) (separate QK + PV kernels)
+    float2 *part_ml;     // (b, h_q, splits) split (max, sum)
+    float *part_acc;     // (b, h_q, splits, d) split sums
+};
+
 namespace {
 
 int dalloc(skv_layer *ly, size_t bytes, void **p) {
@@ -282,8 +297,8 @@ struct Timed {
     int kernel;
     hipStream_t st;
     hipEvent_t stop = nullptr;
-    Timed(skv_layer *l, int k, hipStream_t s) : ly(l), kernel(k), st(s) {
-        if (!ly->timing) return;
+    Timed(skv_layer *l, int k, hipStream_t s, bool on) : ly(l), kernel(k), st(s) {
+        if (!on || !ly->timing) return;
         hipEvent_t start = pool_event(ly);
         stop = pool_event(ly);
         if (!start || !stop) { stop = nullptr; return; }
@@ -605,12 +620,10 @@ int shadowkv_snapkv_select(skv_layer *ly, const void *q_obs, int w_obs, int pool
     return mark_done(ly, st);
 }
 
-int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) {
-    if (!ly) return fail(SKV_E_INVAL, "layer is null");
-    if (!q || !out) return fail(SKV_E_INVAL, "null q or out");
-    if (!ly->ready) return fail(SKV_E_STATE, "decode_step before prefill_meta / load_meta");
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    const Dims dm = dims_with_local(ly->dm, ly->dm.w + ly->n_app);
+// One decode step (Algorithm 2) with its per-step scratch in `sc`.  `timed`:
+// bracket the kernels with the layer's timing events when timing is on.
+static int decode_impl(skv_layer *ly, const void *q, void *out, hipStream_t st, const Dims &dm,
+                       const StepScratch &sc, bool timed) {
     // with exactly k cache slots the slots hold the selection: the rebuilt
     // keys go in slot order and PV reads the cache contiguously; a larger
     // cache holds other chunks too, so the keys go in selection order and PV
@@ -623,21 +636,21 @@ int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) 
     const bool select = !ly->fixed, fetch = select || ly->fetch_pending;
     if (select) {
         {
-            Timed t(ly, SKV_K_SCORE, st);
-            SKV_HIP(skv::launch_score(dm, q, ly->L, ly->cand, ly->P, ly->stats, ly->score_wgs, skv::QRows{1, 0, 1},
+            Timed t(ly, SKV_K_SCORE, st, timed);
+            SKV_HIP(skv::launch_score(dm, q, ly->L, ly->cand, sc.P, sc.stats, ly->score_wgs, skv::QRows{1, 0, 1},
                                       st));
         }
         {
-            Timed t(ly, SKV_K_SELECT, st);
+            Timed t(ly, SKV_K_SELECT, st, timed);
             if (ly->topk_cand) {
-                SKV_HIP(skv::launch_group_topk(dm, ly->P, ly->stats, ly->cand, ly->S2, ly->cand_key, ly->cand_idx,
-                                               ly->cand_count, st));
-                SKV_HIP(skv::launch_select_cand(dm, ly->cand_key, ly->cand_idx, ly->cand_count, ly->sel,
+                SKV_HIP(skv::launch_group_topk(dm, sc.P, sc.stats, ly->cand, sc.S2, sc.cand_key, sc.cand_idx,
+                                               sc.cand_count, st));
+                SKV_HIP(skv::launch_select_cand(dm, sc.cand_key, sc.cand_idx, sc.cand_count, ly->sel,
                                                 ly->sel_slot, ly->slot_chunk, ly->slot_stamp, ++ly->stamp,
                                                 ly->misses, ly->miss_count, ly->counters, st));
             } else {
-                SKV_HIP(skv::launch_group(dm, ly->P, ly->stats, ly->cand, ly->S2, ly->keys, ly->kbounds, st));
-                SKV_HIP(skv::launch_select(dm, ly->keys, ly->kbounds, ly->sel, ly->sel_slot, ly->slot_chunk,
+                SKV_HIP(skv::launch_group(dm, sc.P, sc.stats, ly->cand, sc.S2, sc.keys, sc.kbounds, st));
+                SKV_HIP(skv::launch_select(dm, sc.keys, sc.kbounds, ly->sel, ly->sel_slot, ly->slot_chunk,
                                            ly->slot_stamp, ++ly->stamp, ly->misses, ly->miss_count, ly->counters,
                                            ly->select_keys_in_lds, st));
             }
@@ -650,15 +663,15 @@ int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) 
         SKV_HIP(hipStreamWaitEvent(ly->copy, ly->ev_sel, 0));
         SKV_HIP(hipStreamWaitEvent(ly->comp, ly->ev_sel, 0));
         if (fetch) {
-            Timed t(ly, SKV_K_FETCH, ly->copy);
+            Timed t(ly, SKV_K_FETCH, ly->copy, timed);
             SKV_HIP(skv::launch_fetch(dm, ly->v_host_dev, ly->vc, ly->misses, ly->miss_count, ly->fetch_waves,
                                       ly->copy));
         }
         SKV_HIP(hipEventRecord(ly->ev_fetch, ly->copy));
         {
-            Timed t(ly, SKV_K_QK, ly->comp);
+            Timed t(ly, SKV_K_QK, ly->comp, timed);
             SKV_HIP(skv::launch_qk(dm, q, ly->k_out, ly->k_loc, ly->A, ly->Bt, qk_chunks, ly->theta,
-                                   ly->theta_rev, ly->logits, ly->comp));
+                                   ly->theta_rev, sc.logits, ly->comp));
         }
         SKV_HIP(hipEventRecord(ly->ev_qk, ly->comp));
         SKV_HIP(hipStreamWaitEvent(st, ly->ev_qk, 0));
@@ -666,30 +679,135 @@ int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) 
     } else {
         // one queue: the fetch runs alone on PCIe, then attention
         if (fetch) {
-            Timed t(ly, SKV_K_FETCH, st);
+            Timed t(ly, SKV_K_FETCH, st, timed);
             SKV_HIP(skv::launch_fetch(dm, ly->v_host_dev, ly->vc, ly->misses, ly->miss_count, ly->fetch_waves,
                                       st));
         }
         if (ly->fused) {
-            Timed t(ly, SKV_K_ATTN, st);
+            Timed t(ly, SKV_K_ATTN, st, timed);
             SKV_HIP(skv::launch_attn(dm, q, ly->A, ly->Bt, qk_chunks, pv_slots, ly->theta_rev, ly->k_out, ly->v_out,
-                                     ly->k_loc, ly->v_loc, ly->vc, ly->part_ml, ly->part_acc, st));
-            SKV_HIP(skv::launch_combine(dm, ly->part_ml, ly->part_acc, out, skv::attn_workgroups(dm), st));
+                                     ly->k_loc, ly->v_loc, ly->vc, sc.part_ml, sc.part_acc, st));
+            SKV_HIP(skv::launch_combine(dm, sc.part_ml, sc.part_acc, out, skv::attn_workgroups(dm), st));
         } else {
-            Timed t(ly, SKV_K_QK, st);
+            Timed t(ly, SKV_K_QK, st, timed);
             SKV_HIP(skv::launch_qk(dm, q, ly->k_out, ly->k_loc, ly->A, ly->Bt, qk_chunks, ly->theta,
-                                   ly->theta_rev, ly->logits, st));
+                                   ly->theta_rev, sc.logits, st));
         }
     }
     ly->fetch_pending = false;
     if (ly->overlap || !ly->fused) {
-        Timed t(ly, SKV_K_PV, st);
-        SKV_HIP(skv::launch_pv(dm, ly->logits, ly->v_out, ly->vc, pv_slots, ly->v_loc, ly->part_ml,
-                               ly->part_acc, st));
-        SKV_HIP(skv::launch_combine(dm, ly->part_ml, ly->part_acc, out, dm.pv_tiles, st));
+        Timed t(ly, SKV_K_PV, st, timed);
+        SKV_HIP(skv::launch_pv(dm, sc.logits, ly->v_out, ly->vc, pv_slots, ly->v_loc, sc.part_ml,
+                               sc.part_acc, st));
+        SKV_HIP(skv::launch_combine(dm, sc.part_ml, sc.part_acc, out, dm.pv_tiles, st));
     }
-    if (ly->timing) ++ly->timed_steps;
+    if (timed && ly->timing) ++ly->timed_steps;
     return mark_done(ly, st);
+}
+
+int shadowkv_decode_step(skv_layer *ly, const void *q, void *out, void *stream) {
+    if (!ly) return fail(SKV_E_INVAL, "layer is null");
+    if (!q || !out) return fail(SKV_E_INVAL, "null q or out");
+    if (!ly->ready) return fail(SKV_E_STATE, "decode_step before prefill_meta / load_meta");
+    const Dims dm = dims_with_local(ly->dm, ly->dm.w + ly->n_app);
+    const StepScratch sc{ly->P, ly->stats, ly->S2, ly->keys, ly->kbounds, ly->cand_key, ly->cand_idx,
+                         ly->cand_count, ly->logits, ly->part_ml, ly->part_acc};
+    return decode_impl(ly, q, out, static_cast<hipStream_t>(stream), dm, sc, true);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Decoding without allocation.  shadowkv_decode_step_noalloc takes the step's
+// scratch (the buffers of StepScratch) from `scratch`, a file-scope device
+// array of kStaticScratchBytes, instead of the layer's own.  In host code
+// `scratch` names a host-side stand-in, never a device address: its device
+// address is looked up once per device (with that device current) and only
+// that address reaches kernels.  Every call on one GPU shares its array.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kStaticScratchBytes = size_t(128) << 20;  // 128 MiB per GPU
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mutex;
+void *g_scratch_dev[64] = {};  // device address of `scratch` on each device
+
+int static_scratch(int device, void **out) {
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (device < 0 || device >= 64) return fail(SKV_E_INVAL, "device index out of range");
+    if (!g_scratch_dev[device]) {
+        int cur = -1;
+        SKV_HIP(hipGetDevice(&cur));
+        if (cur != device) SKV_HIP(hipSetDevice(device));
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != device) SKV_HIP(hipSetDevice(cur));
+        if (e != hipSuccess || !p)
+            return fail(SKV_E_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+        g_scratch_dev[device] = p;
+    }
+    *out = g_scratch_dev[device];
+    return SKV_OK;
+}
+
+// The step's scratch carved from `base` in 256-byte aligned pieces, only the
+// buffers this layer's schedule uses; returns the bytes taken (base null:
+// the size only, every pointer null).
+size_t carve_step_scratch(const skv_layer *ly, const Dims &dm, char *base, StepScratch *sc) {
+    size_t used = 0;
+    auto take = [&](size_t bytes) -> char * {
+        const size_t off = (used + 255) / 256 * 256;
+        used = off + std::max<size_t>(bytes, 4);
+        return base ? base + off : nullptr;
+    };
+    const size_t bh = static_cast<size_t>(dm.b) * dm.hkv, hq = static_cast<size_t>(dm.b) * dm.hq;
+    *sc = StepScratch{};
+    if (!ly->fixed) {  // scoring and selection run
+        sc->P = reinterpret_cast<float *>(take(bh * dm.G * dm.n * 4));
+        sc->stats = reinterpret_cast<float2 *>(take(bh * dm.G * dm.wtiles * sizeof(float2)));
+        sc->S2 = reinterpret_cast<float *>(take(bh * dm.n * 4));
+        if (ly->topk_cand) {
+            const size_t cs = bh * skv::topk_slices(dm);
+            sc->cand_key = reinterpret_cast<uint32_t *>(take(cs * dm.k * 4));
+            sc->cand_idx = reinterpret_cast<int32_t *>(take(cs * dm.k * 4));
+            sc->cand_count = reinterpret_cast<int32_t *>(take(cs * 4));
+        } else {
+            sc->keys = reinterpret_cast<uint32_t *>(take(bh * dm.n * 4));
+            sc->kbounds = reinterpret_cast<uint2 *>(take(bh * skv::group_slices(dm) * sizeof(uint2)));
+        }
+    }
+    const bool separate = ly->overlap || !ly->fused;
+    if (separate) sc->logits = reinterpret_cast<float *>(take(hq * dm.NK * 4));
+    const size_t splits = separate ? static_cast<size_t>(dm.pv_tiles) : skv::attn_workgroups(dm);
+    sc->part_ml = reinterpret_cast<float2 *>(take(hq * splits * sizeof(float2)));
+    sc->part_acc = reinterpret_cast<float *>(take(hq * splits * dm.d * 4));
+    return used;
+}
+
+}  // namespace
+
+extern "C" {
+
+int shadowkv_decode_step_noalloc(skv_layer *ly, const void *q, void *out, void *stream) {
+    if (!ly) return fail(SKV_E_INVAL, "layer is null");
+    if (!q || !out) return fail(SKV_E_INVAL, "null q or out");
+    const Dims dm = dims_with_local(ly->dm, ly->dm.w + ly->n_app);
+    StepScratch sc{};
+    const size_t need = carve_step_scratch(ly, dm, nullptr, &sc);
+    if (need > kStaticScratchBytes)
+        return fail(SKV_E_SHAPE, "this layer's decode step needs " + std::to_string(need) +
+                                     " bytes of scratch; the static scratch holds " +
+                                     std::to_string(kStaticScratchBytes) + " (use shadowkv_decode_step)");
+    if (!ly->ready) return fail(SKV_E_STATE, "decode_step before prefill_meta / load_meta");
+    void *base = nullptr;
+    int rc = static_scratch(ly->device, &base);
+    if (rc) return rc;
+    carve_step_scratch(ly, dm, static_cast<char *>(base), &sc);
+    return decode_impl(ly, q, out, static_cast<hipStream_t>(stream), dm, sc, false);
 }
 
 int shadowkv_reset_cache(skv_layer *ly, void *stream) {
