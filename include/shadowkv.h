@@ -286,8 +286,7 @@ enum {
     SKV_K_QK = 3,       /* logits: static keys, rebuilt keys + RoPE         */
     SKV_K_PV = 4,       /* probabilities times values, split merge          */
     SKV_K_ATTN = 5,     /* fused rebuild + logits + PV, split merge: bfloat16
-                           on one queue with 4 query heads per KV head (QK
-                           and PV then read 0); otherwise 0                 */
+                           on one queue (QK and PV then read 0); otherwise 0 */
     SKV_K_COUNT = 6
 };
 int shadowkv_set_timing(skv_layer *layer, int enable);

@@ -442,28 +442,50 @@ __device__ __forceinline__ void unpack8(const u32x4 *raw, float *v) {
 }
 
 // ---------------------------------------------------------------------------
+// Row-of-16 reduction (DPP inside each 16-lane row): every lane of the row
+// ends with the row's result.
+template <typename Op> __device__ __forceinline__ float row16_reduce(float v, Op op) {
+    v = op(v, dpp_mov<0xB1>(v));
+    v = op(v, dpp_mov<0x4E>(v));
+    v = op(v, dpp_mov<0x141>(v));
+    v = op(v, dpp_mov<0x140>(v));
+    return v;
+}
+
+// Two floats that hold bfloat16 values, as two bfloat16 in one dword (exact).
+__device__ __forceinline__ uint32_t pack2_exact(float a, float b) {
+    return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+}
+
+// ---------------------------------------------------------------------------
 // Fused attention (bfloat16, MFMA): rebuild + RoPE + logits + softmax-weighted
 // values in one launch, the logits never leaving the workgroup.  Workgroup
 // `tile` of a row (the XCD-aware order below maps the launch index to (row,
 // tile)) takes rebuilt keys 256*tile .. +256 when tile < ts, 64 per wave
 // exactly as the QK kernel, and each wave one 16-key block of the static keys
 // (outlier chunks, then the local window: block 4*tile + wave).  Per wave:
-//  1. logits of its 64 + 16 keys (MFMA, as in the QK kernel) into LDS, -inf
-//     for keys it does not have;
-//  2. the V rows of those keys requested (lane = row group x 8-column group;
-//     out-of-range keys read a valid row that gets weight 0);
-//  3. per head, the split's max m and the weights exp(logit - m) in LDS, and
-//     their sum l;
-//  4. sum of weight x V over the split, reduced over the row groups with lane
-//     exchanges, into LDS;
-//  5. the four waves' partials merged into the workgroup's one (m, l, acc),
+//  1. the queries, the static block's keys and its value rows are requested,
+//     then the gathered A rows of the four 16-key rebuilt blocks;
+//  2. per rebuilt block: Gather(A, I) . B on MFMA, RoPE in registers, logits
+//     on MFMA (keys split into bfloat16 hi + lo); as soon as a block's A rows
+//     are consumed its value rows are requested;
+//  3. the static block's logits on MFMA.  Every block's logits come out with
+//     lane (quad, row) holding heads 4*quad + e of key `row`, so each head's
+//     softmax over the wave's 80 keys is a reduction inside a 16-lane row;
+//  4. sum over keys of weight x V on MFMA.  The contraction runs over keys,
+//     so each block's value rows (lane = key) are first turned column-major
+//     by an MFMA against a 0/1 selector -- exact, one product per output --
+//     whose output layout is the B operand of the weighted sum; the weights,
+//     through LDS in the same key order, are its A operand (bfloat16 hi + lo);
+//  5. the four waves' partials merged into the workgroup's (m, l, acc),
 //     written for the merge kernel.
+// With 16 heads per KV head the heads fill every row of the logit and
+// weighted-sum MFMAs, so the kernel costs about the same at GQA 4 and 16.
 // Workgroups past ts (more static blocks than rebuilt-key waves) skip the
 // rebuild and its barrier (a workgroup-uniform branch); every workgroup
 // reaches the final barrier.
-// ---------------------------------------------------------------------------
 template <int D, int GP, int NKB, bool IND>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ A, const uint16_t *__restrict__ Bt,
     const int32_t *__restrict__ chunks, const int32_t *__restrict__ sel_slot, const double *__restrict__ theta_rev,
     const uint16_t *__restrict__ k_out, const uint16_t *__restrict__ v_out, const uint16_t *__restrict__ k_loc,
@@ -471,11 +493,11 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     float *__restrict__ part_acc, int hkv, int G, int s, int c, int r, int r_pad, int k, int cap, int OC, int KC,
     int w, int wcap, int ts, int T, int rows, float scale) {
     static_assert(GP <= 16, "query heads are the rows of one 16-row MFMA block");
-    constexpr int NB = D / 16, HB = NB / 2, NP = NB / 2, MB = 4, STG = D / 8, KS = D / 32;
-    constexpr int KW = 80;                // keys per wave: 64 rebuilt + one 16-key static block
-    constexpr int CG = D / 8;             // 8-column groups
-    constexpr int RGW = 64 / CG;          // row groups per wave
-    constexpr int NR = KW / RGW;          // rows per lane
+    constexpr int NB = D / 16, HB = NB / 2, NP = NB / 2, MB = 4, STG = D / 8;
+    constexpr int KB = D / 32;                      // 32-column slabs of a value row
+    constexpr int PW = 84;                          // LDS row of one head's 80 weights
+    constexpr int RP = D + 2;                       // merge record of one head: D sums, max, sum
+    constexpr int RGN = GP * (PW > RP ? PW : RP);   // LDS floats of one wave
     extern __shared__ uint16_t dyn[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, quad = lane >> 4;
@@ -491,43 +513,96 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
     const int hq = hkv * G;
     const int ldb = r_pad + 8;
     const bool rebuild = tile < ts;  // workgroup-uniform
-    uint16_t *Bs = dyn;  // D x (r_pad + 8), rebuilding workgroups only
-    float *ps = reinterpret_cast<float *>(dyn + (ts > 0 ? static_cast<size_t>(D) * ldb : 0)) + wave * GP * KW;
+    uint16_t *Bs = dyn;              // D x (r_pad + 8), rebuilding workgroups only
+    // per wave: first its weights (GP x PW floats), then, once it has read
+    // them, its merge record (GP x RP floats)
+    float *rec = reinterpret_cast<float *>(dyn + (ts > 0 ? static_cast<size_t>(D) * ldb : 0));
+    float *ps = rec + wave * RGN;
     const int key_base = tile * kQkMfmaTile + wave * 64;
     const bool active = rebuild && key_base < KC;  // wave-uniform
     const int nstat = OC + w;
     const int sb0 = (tile * 4 + wave) * 16;  // first key of this wave's static block
 
-    // ---- 1a. rebuilt keys' logits ------------------------------------------------
+    // ---- 1. queries and the static block -------------------------------------------
+    // the group's queries as the logit MFMA's A operand: lane (quad, row)
+    // holds head `row` (rows past G repeat the last head; their outputs are
+    // dropped) in the permuted dim order 32p + 4*quad + e, 32p + 16 + 4*quad + e
+    bf16x8 qa[NP];
+    {
+        const uint16_t *qrow = q + (static_cast<size_t>(b) * hq + h * G + min(row, G - 1)) * D + quad * 4;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const u32x2 lo = *reinterpret_cast<const u32x2 *>(qrow + 32 * p);
+            const u32x2 hi = *reinterpret_cast<const u32x2 *>(qrow + 32 * p + 16);
+            qa[p] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        }
+    }
+    // the static block: keys in the same permuted dims (B operand), value
+    // rows with lane (quad, row) holding key `row`, columns 32*kb + 8*quad .. +8
+    const bool has_stat = sb0 < nstat;  // wave-uniform
+    const int sk = min(sb0 + row, max(nstat - 1, 0));
+    const uint16_t *skrow = sk < OC ? k_out + (static_cast<size_t>(bh) * OC + sk) * D
+                                    : k_loc + (static_cast<size_t>(bh) * wcap + (sk - OC)) * D;
+    const uint16_t *svrow = sk < OC ? v_out + (static_cast<size_t>(bh) * OC + sk) * D
+                                    : v_loc + (static_cast<size_t>(bh) * wcap + (sk - OC)) * D;
+    bf16x8 sko[NP];
+    u32x4 svr[KB];
+    if (has_stat) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const u32x2 lo = *reinterpret_cast<const u32x2 *>(skrow + 32 * p + quad * 4);
+            const u32x2 hi = *reinterpret_cast<const u32x2 *>(skrow + 32 * p + 16 + quad * 4);
+            sko[p] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) svr[kb] = *reinterpret_cast<const u32x4 *>(svrow + kb * 32 + quad * 8);
+    }
+
+    // ---- 2. rebuilt blocks ---------------------------------------------------------
+    f32x4 lg[MB + 1];  // logits, block MB is the static one
+    u32x4 vr[MB][KB];  // value rows of the rebuilt blocks, laid out as svr
+#pragma unroll
+    for (int mb = 0; mb <= MB; ++mb) lg[mb] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) vr[mb][kb] = u32x4{0u, 0u, 0u, 0u};
     if (rebuild) {
         const int pos0 = key_base / c;
         const int my_chunk = chunks[static_cast<size_t>(bh) * k + min(pos0 + lane, k - 1)];
-        double thr[HB][4];
+        // rotation rates (turns per position) of this lane's dims
+        // 16*hb + 4*quad + e: theta_rev[4*quad + e] times the ratio of the
+        // rates 16*hb dims apart, theta_rev[16*hb] / theta_rev[0]
+        double thr0[4], rat[HB];
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb)
+        for (int e = 0; e < 4; ++e) thr0[e] = theta_rev[quad * 4 + e];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) thr[hb][e] = theta_rev[hb * 16 + quad * 4 + e];
+        for (int hb = 0; hb < HB; ++hb) rat[hb] = theta_rev[hb * 16] / theta_rev[0];
         {
+            // stage B[h] (transposed, d x r) with every load in flight
             const uint16_t *Btb = Bt + static_cast<size_t>(bh) * D * r;
             const int vpr = r_pad / 8, total = D * vpr;
             u32x4 tmp[STG];
 #pragma unroll
             for (int i = 0; i < STG; ++i) {
-                const int idx = tid + 256 * i;
-                const int nr = idx / vpr, kc = (idx % vpr) * 8;
-                tmp[i] = (idx < total && kc < r)
-                             ? *reinterpret_cast<const u32x4 *>(Btb + static_cast<size_t>(nr) * r + kc)
-                             : u32x4{0u, 0u, 0u, 0u};
+                const int ix = tid + 256 * i;
+                const int nr = ix / vpr, kc = (ix % vpr) * 8;
+                tmp[i] = (ix < total && kc < r) ? *reinterpret_cast<const u32x4 *>(Btb + static_cast<size_t>(nr) * r + kc)
+                                                : u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
             for (int i = 0; i < STG; ++i) {
-                const int idx = tid + 256 * i;
-                if (idx < total) *reinterpret_cast<u32x4 *>(Bs + (idx / vpr) * ldb + (idx % vpr) * 8) = tmp[i];
+                const int ix = tid + 256 * i;
+                if (ix < total) *reinterpret_cast<u32x4 *>(Bs + (ix / vpr) * ldb + (ix % vpr) * 8) = tmp[i];
             }
         }
+        // Gathered A row of this lane's key in each 16-key block, 8 rank
+        // values per 32-wide rank block, through a buffer resource over this
+        // sequence's A: keys past KC and rank columns past r read zeros
+        // without a memory access, so no branch surrounds a load.
         const Rsrc ar = make_rsrc(A + static_cast<size_t>(b) * s * r, static_cast<uint32_t>(s) * r * 2);
         u32x4 aop[MB][NKB];
-        int pos[MB];
+        int pos[MB], vkey[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int key = key_base + mb * 16 + row;
@@ -535,28 +610,20 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
             const int kk = key < KC ? key : key_base;
             const int chunk = __shfl(my_chunk, kk / c - pos0, 64);
             pos[mb] = chunk * c + kk % c;
+            vkey[mb] = key < KC ? key : (KC > 0 ? KC - 1 : 0);  // a valid value row; its weight is 0
             const int base = (pos[mb] * r + quad * 8) * 2;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
                 aop[mb][kb] = buf_ld128(ar, kv && kb * 32 + quad * 8 < r ? base + kb * 64 : kOob);
-        }
-        bf16x8 qa[NP];
-        {
-            const uint16_t *qrow = q + (static_cast<size_t>(b) * hq + h * G + min(row, G - 1)) * D + quad * 4;
-#pragma unroll
-            for (int p = 0; p < NP; ++p) {
-                const u32x2 lo = *reinterpret_cast<const u32x2 *>(qrow + 32 * p);
-                const u32x2 hi = *reinterpret_cast<const u32x2 *>(qrow + 32 * p + 16);
-                qa[p] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-            }
         }
         __syncthreads();  // Bs staged (every wave of a rebuilding workgroup reaches it)
 
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int kb0 = key_base + mb * 16;
-            f32x4 lg = {0.f, 0.f, 0.f, 0.f};
             if (active && kb0 < KC) {  // wave-uniform
+                // K^T[dim, key] = sum_r Bt[dim, r] A[key, r]: lane (quad, row)
+                // ends with key `row`, dims 16*nb + 4*quad + e
                 f32x4 acc[NB];
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -570,12 +637,30 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
                         acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bop, acc[nb], 0, 0, 0);
                     }
                 }
+                // the block's value rows, requested now that its A rows are consumed
+                {
+                    const int key = vkey[mb];
+                    const uint16_t *vrow;
+                    if constexpr (IND) {
+                        const int slot = min(max(sel_slot[static_cast<size_t>(bh) * k + key / c], 0), cap - 1);
+                        vrow = vc + ((static_cast<size_t>(bh) * cap + slot) * c + key % c) * D;
+                    } else {
+                        vrow = vc + (static_cast<size_t>(bh) * KC + key) * D;
+                    }
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) vr[mb][kb] = *reinterpret_cast<const u32x4 *>(vrow + kb * 32 + quad * 8);
+                }
+                // RoPE of this lane's key at its original position: the angle
+                // in turns, pos * theta_i / (2 pi), is reduced to [-1/2, 1/2]
+                // in double precision and fed to the hardware sin/cos (which
+                // take turns)
                 const double posd = static_cast<double>(pos[mb]);
 #pragma unroll
                 for (int hb = 0; hb < HB; ++hb) {
+                    const double ph = posd * rat[hb];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const double turns = posd * thr[hb][e];
+                        const double turns = ph * thr0[e];
                         const float frac = static_cast<float>(turns - rint(turns));
                         const float sn = __builtin_amdgcn_sinf(frac), cs = __builtin_amdgcn_cosf(frac);
                         const float x1 = acc[hb][e], x2 = acc[hb + HB][e];
@@ -583,185 +668,141 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(
                         acc[hb + HB][e] = x2 * cs + x1 * sn;
                     }
                 }
-                lg = logits_hilo<NP>(qa, acc, lg);
-            }
-            // lane (quad, row): heads 4*quad + e of key kb0 + row
-            const bool kv = active && kb0 + row < KC;
+                const f32x4 l4 = logits_hilo<NP>(qa, acc, f32x4{0.f, 0.f, 0.f, 0.f});
+                const bool kv = kb0 + row < KC;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int g = quad * 4 + e;
-                if (g < GP) ps[g * KW + mb * 16 + row] = kv ? lg[e] * scale : -INFINITY;
+                for (int e = 0; e < 4; ++e) lg[mb][e] = kv ? l4[e] * scale : -INFINITY;
             }
         }
+    }
+    // ---- 3. the static block's logits ------------------------------------------------
+    if (has_stat) {
+        f32x4 l4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < NP; ++p) l4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[p], sko[p], l4, 0, 0, 0);
+        const bool kv = sb0 + row < nstat;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lg[MB][e] = kv ? l4[e] * scale : -INFINITY;
     } else {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int g = quad * 4 + e;
-                if (g < GP) ps[g * KW + mb * 16 + row] = -INFINITY;
-            }
+        for (int kb = 0; kb < KB; ++kb) svr[kb] = u32x4{0u, 0u, 0u, 0u};
     }
 
-    // ---- 1b. the static block's logits (keys as MFMA rows, heads as columns) -----
-    {
-        bf16x8 qb[KS];
-        const uint16_t *qrow = q + (static_cast<size_t>(b) * hq + h * G + min(row, G - 1)) * D + quad * 8;
+    // ---- softmax per head 4*quad + e over the wave's 80 keys; weights to LDS -------
+    float mrow[4], lrow[4];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(qrow + ks * 32));
-        const int sk = min(sb0 + row, max(nstat - 1, 0));
-        const uint16_t *src = sk < OC ? k_out + (static_cast<size_t>(bh) * OC + sk) * D
-                                      : k_loc + (static_cast<size_t>(bh) * wcap + (sk - OC)) * D;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (sb0 < nstat) {  // wave-uniform
+    for (int e = 0; e < 4; ++e) {
+        float m = lg[0][e];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const u32x4 v = *reinterpret_cast<const u32x4 *>(src + ks * 32 + quad * 8);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), qb[ks], acc, 0, 0, 0);
-            }
+        for (int mb = 1; mb <= MB; ++mb) m = fmaxf(m, lg[mb][e]);
+        m = row16_reduce(m, [](float x, float y) { return fmaxf(x, y); });
+        float l = 0.f;
+#pragma unroll
+        for (int mb = 0; mb <= MB; ++mb) {
+            const float p = m == -INFINITY ? 0.f : expf(lg[mb][e] - m);
+            lg[mb][e] = p;
+            l += p;
         }
-        // lane (quad, row): head `row` of keys sb0 + 4*quad + e
-        if (row < GP) {
+        l = row16_reduce(l, [](float x, float y) { return x + y; });
+        mrow[e] = m;
+        lrow[e] = l;
+        const int g = quad * 4 + e;
+        if (g < GP) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                ps[row * KW + 64 + quad * 4 + e] =
-                    (row < G && sb0 + quad * 4 + e < nstat) ? acc[e] * scale : -INFINITY;
+            for (int mb = 0; mb <= MB; ++mb) ps[g * PW + mb * 16 + row] = lg[mb][e];
         }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // ---- 2. V rows of the split: row i*RGW + rg, columns 8*cg .. +8 ---------------
-    const int rg = lane / CG, cg = lane % CG;
-    u32x4 raw[NR];
+    // ---- 4. sum of weight x V on MFMA ------------------------------------------------
+    // 0/1 selectors: lane (row = n, quad = kq) of the B operand holds rows
+    // 8*kq .. +8 of the 32 x 16 matrix with ones at (n + 16*half, n), so
+    // V-slab x selector = the slab's columns 16*half .. +16, with lane
+    // (quad, n) holding keys 4*quad + e of column n: a value row turned
+    // column-major, each output one exact product
+    bf16x8 sel01[2];
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
-        const int kk = i * RGW + rg;  // key of the wave's list (0-63 rebuilt, 64-79 static)
-        const uint16_t *vrow;
-        if (kk < 64) {
-            const int key = min(key_base + kk, max(KC - 1, 0));
-            if constexpr (IND) {
-                const int slot = min(max(sel_slot[static_cast<size_t>(bh) * k + key / c], 0), cap - 1);
-                vrow = vc + ((static_cast<size_t>(bh) * cap + slot) * c + key % c) * D;
-            } else {
-                vrow = vc + (static_cast<size_t>(bh) * KC + key) * D;
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sel01[hf][j] = static_cast<__bf16>(quad * 8 + j == row + 16 * hf ? 1.0f : 0.0f);
+    // step st contracts the block pair (2*st, 2*st + 1) over the keys
+    // {16*mb0 + 4*kq + e} then {16*mb1 + 4*kq + e}: the weights (A operand,
+    // lane (head row, kq)) in that key order from LDS, the values (B operand)
+    // from the two blocks' column-major outputs
+    const int prow = min(row, GP - 1);
+    f32x4 pacc[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) pacc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 3; ++st) {
+        const int mb0 = 2 * st, mb1 = 2 * st + 1;  // block MB = 4 is the static one, block 5 is empty
+        const float4 p0 = *reinterpret_cast<const float4 *>(ps + prow * PW + mb0 * 16 + quad * 4);
+        const float4 p1 = mb1 <= MB ? *reinterpret_cast<const float4 *>(ps + prow * PW + mb1 * 16 + quad * 4)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+        bf16x8 phi, plo;
+        split_bf16x8(f32x4{p0.x, p0.y, p0.z, p0.w}, f32x4{p1.x, p1.y, p1.z, p1.w}, phi, plo);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const u32x4 v0 = mb0 < MB ? vr[mb0][kb] : svr[kb];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const f32x4 t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v0), sel01[hf],
+                                                                          f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                f32x4 t1 = {0.f, 0.f, 0.f, 0.f};
+                if (mb1 < MB)
+                    t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vr[mb1][kb]), sel01[hf],
+                                                                 f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                else if (mb1 == MB)
+                    t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, svr[kb]), sel01[hf],
+                                                                 f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                const bf16x8 vop = __builtin_bit_cast(
+                    bf16x8, u32x4{pack2_exact(t0[0], t0[1]), pack2_exact(t0[2], t0[3]), pack2_exact(t1[0], t1[1]),
+                                  pack2_exact(t1[2], t1[3])});
+                const int nb = kb * 2 + hf;  // output columns 16*nb .. +16
+                pacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(phi, vop, pacc[nb], 0, 0, 0);
+                pacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(plo, vop, pacc[nb], 0, 0, 0);
             }
-            if (!active) vrow = nstat > 0 ? (OC > 0 ? v_out + static_cast<size_t>(bh) * OC * D
-                                                    : v_loc + static_cast<size_t>(bh) * wcap * D)
-                                          : vrow;
-        } else {
-            const int sk = min(sb0 + (kk - 64), max(nstat - 1, 0));
-            vrow = sk < OC ? v_out + (static_cast<size_t>(bh) * OC + sk) * D
-                           : v_loc + (static_cast<size_t>(bh) * wcap + (sk - OC)) * D;
         }
-        raw[i] = *reinterpret_cast<const u32x4 *>(vrow + cg * 8);
     }
 
-    // ---- 3. per head: split max, weights, sum -------------------------------------
-    float *wacc = ps + (4 - wave) * GP * KW + wave * GP * (D + 2);  // this wave's (m, l, acc) for the merge
-#pragma unroll
-    for (int g = 0; g < GP; ++g) {
-        float *pg = ps + g * KW;
-        if (g >= G) {  // padding heads: weight 0
-            pg[lane] = 0.f;
-            if (lane < KW - 64) pg[64 + lane] = 0.f;
-            continue;
-        }
-        const float x0 = pg[lane], x1 = lane < KW - 64 ? pg[64 + lane] : -INFINITY;
-        const float m = wave_max(fmaxf(x0, x1));
-        const float p0 = m == -INFINITY ? 0.f : expf(x0 - m);
-        const float p1 = m == -INFINITY ? 0.f : expf(x1 - m);
-        pg[lane] = p0;
-        if (lane < KW - 64) pg[64 + lane] = p1;
-        const float l = wave_sum(p0 + p1);
-        if (lane == 0) { wacc[g * (D + 2) + D] = m; wacc[g * (D + 2) + D + 1] = l; }
-    }
+    // ---- 5. this wave's partial per head into LDS (over its own weights, all
+    //         read above), then the workgroup's four partials merged ---------------
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // ---- 4. weighted sum of V, reduced over the row groups ------------------------
-    //         (in groups of up to 4 heads, so the accumulators stay few)
-    constexpr int HG = GP < 4 ? GP : 4;
 #pragma unroll
-    for (int h0 = 0; h0 < GP; h0 += HG) {
-        if (h0 >= G) break;  // wave-uniform
-        float acc[HG][8];
+    for (int e = 0; e < 4; ++e) {
+        const int g = quad * 4 + e;  // lane (quad, row): head g, column 16*nb + row
+        if (g < G) {
 #pragma unroll
-        for (int g = 0; g < HG; ++g)
-#pragma unroll
-            for (int x = 0; x < 8; ++x) acc[g][x] = 0.f;
-#pragma unroll
-        for (int i = 0; i < NR; ++i) {
-            const int kk = i * RGW + rg;
-            float v[8];
-            unpack8<uint16_t>(&raw[i], v);
-#pragma unroll
-            for (int g = 0; g < HG; ++g) {
-                const float pw = ps[(h0 + g) * KW + kk];
-#pragma unroll
-                for (int x = 0; x < 8; ++x) acc[g][x] += pw * v[x];
-            }
-        }
-        if constexpr (RGW == 4) {
-            // two halving lane exchanges: lane group r ends with values
-            // r*(2*HG) .. r*(2*HG) + 2*HG - 1 of the flattened (head, column) list
-            constexpr int NV = HG * 8;
-            float a[NV];
-#pragma unroll
-            for (int g = 0; g < HG; ++g)
-#pragma unroll
-                for (int x = 0; x < 8; ++x) a[g * 8 + x] = acc[g][x];
-#pragma unroll
-            for (int v = 0; v < NV / 2; ++v) a[v] = swap_sum32(a[v], a[v + NV / 2]);
-#pragma unroll
-            for (int v = 0; v < NV / 4; ++v) a[v] = swap_sum16(a[v], a[v + NV / 4]);
-            const int rr = lane >> 4;
-#pragma unroll
-            for (int v = 0; v < NV / 4; ++v) {
-                const int f = rr * (NV / 4) + v, g = h0 + (f >> 3);
-                if (g < G) wacc[g * (D + 2) + cg * 8 + (f & 7)] = a[v];
-            }
-        } else {
-#pragma unroll
-            for (int off = CG; off < 64; off <<= 1)
-#pragma unroll
-                for (int g = 0; g < HG; ++g)
-#pragma unroll
-                    for (int x = 0; x < 8; ++x) acc[g][x] += __shfl_xor(acc[g][x], off, 64);
-            if (lane < CG) {
-#pragma unroll
-                for (int g = 0; g < HG; ++g) {
-                    if (h0 + g >= G) break;
-#pragma unroll
-                    for (int x = 0; x < 8; ++x) wacc[(h0 + g) * (D + 2) + cg * 8 + x] = acc[g][x];
-                }
+            for (int nb = 0; nb < NB; ++nb) ps[g * RP + nb * 16 + row] = pacc[nb][e];
+            if (row == 0) {
+                ps[g * RP + D] = mrow[e];
+                ps[g * RP + D + 1] = lrow[e];
             }
         }
     }
-
-    // ---- 5. the workgroup's four splits merged into one partial --------------------
     __syncthreads();  // every wave of the workgroup reaches it (no early exit above)
-    const float *all = ps + (4 - wave) * GP * KW;  // (wave, head) records of D + 2 floats
-    for (int idx = tid; idx < G * D; idx += 256) {
-        const int g = idx / D, i = idx % D;
+    for (int ix = tid; ix < G * D; ix += 256) {
+        const int g = ix / D, i = ix % D;
         float M = -INFINITY;
 #pragma unroll
-        for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, all[(wv * GP + g) * (D + 2) + D]);
-        float L = 0.f, a = 0.f;
+        for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, rec[wv * RGN + g * RP + D]);
+        float Ls = 0.f, a = 0.f;
         if (M != -INFINITY) {
 #pragma unroll
             for (int wv = 0; wv < 4; ++wv) {
-                const float *r = all + (wv * GP + g) * (D + 2);
-                const float wgt = expf(r[D] - M);
-                L += wgt * r[D + 1];
-                a += wgt * r[i];
+                const float *rr = rec + wv * RGN + g * RP;
+                const float wgt = expf(rr[D] - M);
+                Ls += wgt * rr[D + 1];
+                a += wgt * rr[i];
             }
         }
-        const size_t rec = (static_cast<size_t>(bh) * G + g) * T + tile;
-        part_acc[rec * D + i] = a;
-        if (i == 0) part_ml[rec] = make_float2(M, L);
+        const size_t rc = (static_cast<size_t>(bh) * G + g) * T + tile;
+        part_acc[rc * D + i] = a;
+        if (i == 0) part_ml[rc] = make_float2(M, Ls);
     }
 }
 
@@ -1117,8 +1158,8 @@ static hipError_t attn_t(const Dims &dm, const void *q, const void *A, const voi
     const int ts = (dm.KC + kQkMfmaTile - 1) / kQkMfmaTile;
     const int T = attn_workgroups(dm);
     const int r_pad = NKB * 32;
-    const size_t lds = (ts > 0 ? static_cast<size_t>(D) * (r_pad + 8) * sizeof(uint16_t) : 0) +
-                       4ull * GP * (80 + D + 2) * sizeof(float);
+    constexpr int RGN = GP * (84 > D + 2 ? 84 : D + 2);  // LDS floats per wave: weights, then merge record
+    const size_t lds = (ts > 0 ? static_cast<size_t>(D) * (r_pad + 8) * sizeof(uint16_t) : 0) + 4ull * RGN * sizeof(float);
     auto kern = attn_mfma_kernel<D, GP, NKB, IND>;
     if (lds > 48 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),

@@ -377,11 +377,10 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     // overrides the workgroup count for tuning.
     ly->score_wgs = 0;
     if (const char *e = std::getenv("SKV_SCORE_WGS")) ly->score_wgs = std::max(1, std::atoi(e));
-    // measured on MI355X: the fused kernel wins at GQA 4 (128K b8: 35.7 against
-    // 41.1 us; 60K b48: even) and loses at GQA 16 (244K b12: 90.7 against
-    // 49.4 us, its 16 heads' accumulators halve the occupancy); SKV_ATTN_FUSED=1
-    // or 0 forces either for bfloat16
-    ly->fused = dm.bf16 != 0 && dm.GP == 4;
+    // bfloat16 takes the fused kernel at every group size (its weighted sum
+    // runs on MFMA, whose 16 rows the heads fill at GQA 16); SKV_ATTN_FUSED=0
+    // or 1 forces the separate QK + PV kernels or the fused one
+    ly->fused = dm.bf16 != 0;
     if (const char *e = std::getenv("SKV_ATTN_FUSED")) ly->fused = dm.bf16 != 0 && std::atoi(e) != 0;
 
     const size_t B = dm.b, HKV = dm.hkv, HQ = dm.hq, D = dm.d, S = dm.s, E = dm.esize;

@@ -227,7 +227,18 @@ def test_load_meta_decode_and_reset_cache():
     assert st["hits"] - hits_warm == wl.b * wl.h_kv * wl.k  # no hits after the reset
     w_np, c_np = to_np(warm), to_np(cold)
     np.testing.assert_array_equal(w_np, outs[-1])  # same resident layout -> bitwise equal
-    assert np.all(np.abs(w_np - c_np) <= 2 * bf16_ulp(w_np))
+    # another slot order: other splits and summation order.  The weights enter
+    # the weighted sum as bfloat16 hi + lo (16 significant bits, relative
+    # error <= 2^-17 each), so besides two output roundings the outputs may
+    # differ by up to 2^-16 max|V| absolutely, which matters near zero only.
+    diff = np.abs(w_np - c_np)
+    floor = 2.0 ** -16 * float(np.max(np.abs(v)))
+    log(f"[load_meta] warm vs cold cache: max diff {diff.max():.3g} (absolute floor {floor:.3g})")
+    assert np.all(diff <= 2 * bf16_ulp(w_np) + floor)
+    res = oracle.decode(shape, qs[-1], meta, A_o, B_o, v)
+    cold_err = float(np.max(np.abs(c_np - res["out"])))
+    log(f"[load_meta] cold step: max|out - oracle| = {cold_err:.3g}")
+    assert cold_err <= OUT_TOL[True]
     layer.close()
     hb.free()
 
