@@ -466,7 +466,8 @@ __device__ __forceinline__ uint32_t pack2_exact(float a, float b) {
 // (outlier chunks, then the local window: block 4*tile + wave).  Per wave:
 //  1. the queries, the static block's keys and its value rows are requested,
 //     then the gathered A rows of the four 16-key rebuilt blocks;
-//  2. per rebuilt block: Gather(A, I) . B on MFMA, RoPE in registers, logits
+//  2. per pair of rebuilt blocks: Gather(A, I) . B on MFMA (each staged B
+//     operand feeds both blocks), then per block RoPE in registers and logits
 //     on MFMA (keys split into bfloat16 hi + lo); as soon as a block's A rows
 //     are consumed its value rows are requested;
 //  3. the static block's logits on MFMA.  Every block's logits come out with
@@ -618,60 +619,76 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
         __syncthreads();  // Bs staged (every wave of a rebuilding workgroup reaches it)
 
+        // The blocks go in pairs (BP = 2, ranks 97..192): each staged Bt
+        // operand read from LDS feeds both blocks' MFMAs, which halves the LDS
+        // traffic of the rebuild.  With fewer or more rank blocks the second
+        // block's registers do not fit beside the rest, so blocks go singly.
+        constexpr int BP = (NKB >= 4 && NKB <= 6) ? 2 : 1;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const int kb0 = key_base + mb * 16;
-            if (active && kb0 < KC) {  // wave-uniform
+        for (int mp = 0; mp < MB; mp += BP) {
+            if (active && key_base + mp * 16 < KC) {  // wave-uniform
                 // K^T[dim, key] = sum_r Bt[dim, r] A[key, r]: lane (quad, row)
-                // ends with key `row`, dims 16*nb + 4*quad + e
-                f32x4 acc[NB];
+                // ends with key `row`, dims 16*nb + 4*quad + e, of each block
+                f32x4 acc[BP][NB];
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int x = 0; x < BP; ++x)
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) acc[x][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb) {
-                    const bf16x8 bop = __builtin_bit_cast(bf16x8, aop[mb][kb]);
+                    bf16x8 bop[BP];
+#pragma unroll
+                    for (int x = 0; x < BP; ++x) bop[x] = __builtin_bit_cast(bf16x8, aop[mp + x][kb]);
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
                         const bf16x8 aw = __builtin_bit_cast(
                             bf16x8, *reinterpret_cast<const u32x4 *>(Bs + (nb * 16 + row) * ldb + kb * 32 + quad * 8));
-                        acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bop, acc[nb], 0, 0, 0);
+#pragma unroll
+                        for (int x = 0; x < BP; ++x)
+                            acc[x][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bop[x], acc[x][nb], 0, 0, 0);
                     }
                 }
-                // the block's value rows, requested now that its A rows are consumed
-                {
-                    const int key = vkey[mb];
-                    const uint16_t *vrow;
-                    if constexpr (IND) {
-                        const int slot = min(max(sel_slot[static_cast<size_t>(bh) * k + key / c], 0), cap - 1);
-                        vrow = vc + ((static_cast<size_t>(bh) * cap + slot) * c + key % c) * D;
-                    } else {
-                        vrow = vc + (static_cast<size_t>(bh) * KC + key) * D;
+#pragma unroll
+                for (int x = 0; x < BP; ++x) {
+                    const int mb = mp + x, kb0 = key_base + mb * 16;
+                    // the block's value rows, requested now that its A rows are consumed
+                    {
+                        const int key = vkey[mb];
+                        const uint16_t *vrow;
+                        if constexpr (IND) {
+                            const int slot = min(max(sel_slot[static_cast<size_t>(bh) * k + key / c], 0), cap - 1);
+                            vrow = vc + ((static_cast<size_t>(bh) * cap + slot) * c + key % c) * D;
+                        } else {
+                            vrow = vc + (static_cast<size_t>(bh) * KC + key) * D;
+                        }
+#pragma unroll
+                        for (int kb = 0; kb < KB; ++kb)
+                            vr[mb][kb] = *reinterpret_cast<const u32x4 *>(vrow + kb * 32 + quad * 8);
                     }
+                    // RoPE of this lane's key at its original position: the
+                    // angle in turns, pos * theta_i / (2 pi), is reduced to
+                    // [-1/2, 1/2] in double precision and fed to the hardware
+                    // sin/cos (which take turns)
+                    f32x4 *ac = acc[x];
+                    const double posd = static_cast<double>(pos[mb]);
 #pragma unroll
-                    for (int kb = 0; kb < KB; ++kb) vr[mb][kb] = *reinterpret_cast<const u32x4 *>(vrow + kb * 32 + quad * 8);
-                }
-                // RoPE of this lane's key at its original position: the angle
-                // in turns, pos * theta_i / (2 pi), is reduced to [-1/2, 1/2]
-                // in double precision and fed to the hardware sin/cos (which
-                // take turns)
-                const double posd = static_cast<double>(pos[mb]);
+                    for (int hb = 0; hb < HB; ++hb) {
+                        const double ph = posd * rat[hb];
 #pragma unroll
-                for (int hb = 0; hb < HB; ++hb) {
-                    const double ph = posd * rat[hb];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const double turns = ph * thr0[e];
-                        const float frac = static_cast<float>(turns - rint(turns));
-                        const float sn = __builtin_amdgcn_sinf(frac), cs = __builtin_amdgcn_cosf(frac);
-                        const float x1 = acc[hb][e], x2 = acc[hb + HB][e];
-                        acc[hb][e] = x1 * cs - x2 * sn;
-                        acc[hb + HB][e] = x2 * cs + x1 * sn;
+                        for (int e = 0; e < 4; ++e) {
+                            const double turns = ph * thr0[e];
+                            const float frac = static_cast<float>(turns - rint(turns));
+                            const float sn = __builtin_amdgcn_sinf(frac), cs = __builtin_amdgcn_cosf(frac);
+                            const float x1 = ac[hb][e], x2 = ac[hb + HB][e];
+                            ac[hb][e] = x1 * cs - x2 * sn;
+                            ac[hb + HB][e] = x2 * cs + x1 * sn;
+                        }
                     }
-                }
-                const f32x4 l4 = logits_hilo<NP>(qa, acc, f32x4{0.f, 0.f, 0.f, 0.f});
-                const bool kv = kb0 + row < KC;
+                    const f32x4 l4 = logits_hilo<NP>(qa, ac, f32x4{0.f, 0.f, 0.f, 0.f});
+                    const bool kv = kb0 + row < KC;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) lg[mb][e] = kv ? l4[e] * scale : -INFINITY;
+                    for (int e = 0; e < 4; ++e) lg[mb][e] = kv ? l4[e] * scale : -INFINITY;
+                }
             }
         }
     }
