@@ -200,8 +200,6 @@ def main() -> int:
     ap.add_argument("--cache-chunks", type=int, default=0,
                     help="V chunks resident in HBM per (sequence, KV head): 0 = top-k, the set-difference cache; "
                          "larger keeps the most recently selected chunks too (least recently used)")
-    ap.add_argument("--host-eigh", action="store_true",
-                    help="setup: solve the factors' eigenproblems on the host instead of the device")
     ap.add_argument("--sweep", action="store_true",
                     help="run chunk-size / budget / rank variants of the workload, one JSON line each")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -224,7 +222,6 @@ def main() -> int:
 
     from sparse_kv_cache_step_amd import binding as skv
     from sparse_kv_cache_step_amd import synth
-    from sparse_kv_cache_step_amd.setup import svd_factors
 
     if not os.path.exists(skv.LIB_PATH):
         import __graft_entry__
@@ -278,15 +275,15 @@ def main() -> int:
         new_kv = []  # decode-token append: (keys, values) per layer
         q_obs = []  # SnapKV-style selection: each layer's window queries
         spot_layer = layers - 1
-        prefill_ms = {"svd_factors": 0.0, "prefill_meta": 0.0}
+        prefill_ms = {"factorize": 0.0, "prefill_meta": 0.0}
         for l in range(layers):
             k_pre = synth.k_pre_torch(wl, l, dev)
             v = synth.v_torch(wl, l, dev)
             torch.cuda.synchronize()
             ts = time.perf_counter()
-            A, B = svd_factors(k_pre, wl.r, host_eigh=args.host_eigh)
+            A, B = skv.factorize(k_pre, wl.r)
             torch.cuda.synchronize()
-            prefill_ms["svd_factors"] += (time.perf_counter() - ts) * 1e3
+            prefill_ms["factorize"] += (time.perf_counter() - ts) * 1e3
             lay = skv.Layer(batch=wl.b, heads_q=wl.h_q, heads_kv=wl.h_kv, head_dim=wl.d, seq_len=wl.s, chunk=wl.c,
                             rank=wl.r, n_outlier=wl.o, top_k=wl.k, local_window=wl.w, rope_base=wl.rope_base,
                             bf16=wl.bf16, max_new=nq_all if args.append else 0,

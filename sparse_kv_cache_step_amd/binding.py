@@ -31,7 +31,7 @@ EXPORTS = (
     "shadowkv_tensor_bytes", "shadowkv_read", "shadowkv_set_overlap", "shadowkv_set_timing",
     "shadowkv_get_timing",
     "shadowkv_host_alloc", "shadowkv_host_free", "shadowkv_last_error", "shadowkv_equiv_bandwidth",
-    "shadowkv_probe_hbm_read",
+    "shadowkv_probe_hbm_read", "shadowkv_factorize",
 )
 
 
@@ -89,6 +89,8 @@ def lib() -> ctypes.CDLL:
             "shadowkv_equiv_bandwidth": (ctypes.c_double, [ctypes.c_double] * 7),
             "shadowkv_probe_hbm_read": (ctypes.c_int, [_VP, ctypes.c_size_t, ctypes.c_int, _VP,
                                                        ctypes.POINTER(ctypes.c_double)]),
+            "shadowkv_factorize": (ctypes.c_int, [ctypes.c_int] * 6 + [_VP, _VP, _VP, _VP,
+                                                                        ctypes.POINTER(ctypes.c_int)]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -212,6 +214,27 @@ def _stream_ptr(stream):
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream
+
+
+def factorize(k_pre, rank: int, stream=None, return_sweeps: bool = False):
+    """Low-rank key factors on k_pre's GPU (shadowkv_factorize): k_pre
+    (b, h_kv, s, d), bfloat16 or binary32, contiguous.  Returns A (b, s, rank)
+    and B (b, h_kv, rank, d) in k_pre's dtype (and the eigensolver's sweep
+    count with return_sweeps)."""
+    torch = _torch()
+    if k_pre.dim() != 4 or not k_pre.is_cuda or not k_pre.is_contiguous():
+        raise ValueError("k_pre must be a contiguous (b, h_kv, s, d) device tensor")
+    if k_pre.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"k_pre: dtype {k_pre.dtype} is neither bfloat16 nor float32")
+    b, hkv, s, d = k_pre.shape
+    A = torch.empty((b, s, rank), dtype=k_pre.dtype, device=k_pre.device)
+    B = torch.empty((b, hkv, rank, d), dtype=k_pre.dtype, device=k_pre.device)
+    sweeps = ctypes.c_int()
+    with torch.cuda.device(k_pre.device):
+        _check(lib().shadowkv_factorize(SKV_BF16 if k_pre.dtype == torch.bfloat16 else SKV_F32, b, hkv, s, d, rank,
+                                        k_pre.data_ptr(), A.data_ptr(), B.data_ptr(), _stream_ptr(stream),
+                                        ctypes.byref(sweeps)))
+    return (A, B, sweeps.value) if return_sweeps else (A, B)
 
 
 class HostBuffer:

@@ -326,6 +326,20 @@ extern "C" {
 
 const char *shadowkv_last_error(void) { return g_last_error.c_str(); }
 
+int shadowkv_factorize(int dtype, int batch, int heads_kv, int seq_len, int head_dim, int rank, const void *k_pre,
+                       void *A, void *B, void *stream, int *sweeps_out) {
+    if (!k_pre || !A || !B) return fail(SKV_E_INVAL, "null k_pre, A or B");
+    if (dtype != SKV_F32 && dtype != SKV_BF16) return fail(SKV_E_INVAL, "dtype must be SKV_F32 or SKV_BF16");
+    if (batch < 1 || heads_kv < 1 || seq_len < 1) return fail(SKV_E_SHAPE, "batch, heads_kv and seq_len must be >= 1");
+    if (head_dim != 64 && head_dim != 128) return fail(SKV_E_SHAPE, "head_dim must be 64 or 128");
+    if (rank < 1 || rank > 256) return fail(SKV_E_SHAPE, "rank must be in [1, 256]");
+    if (heads_kv * head_dim > 4096) return fail(SKV_E_SHAPE, "heads_kv * head_dim must be <= 4096");
+    std::string why;
+    const int rc = skv::factorize_device(dtype == SKV_BF16, batch, heads_kv, seq_len, head_dim, rank, k_pre, A, B,
+                                         static_cast<hipStream_t>(stream), &why, sweeps_out);
+    return rc ? fail(SKV_E_HIP, why) : SKV_OK;
+}
+
 double shadowkv_equiv_bandwidth(double S, double C, double K, double O, double alpha, double b_gpu, double b_pcie) {
     return 2.0 * S * b_gpu / (S / C + 2.0 * (K + O) * C + (1.0 - alpha) * K * C * b_gpu / b_pcie);
 }

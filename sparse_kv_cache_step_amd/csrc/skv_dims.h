@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <string>
+
 namespace skv {
 
 // Tile sizes.
@@ -34,6 +36,12 @@ struct Dims {
     int r_pad;       // rank rounded up to 32
     float scale;     // 1 / sqrt(d)
 };
+
+// Low-rank key factors of `batch` sequences (A, B <- SVD(K_pre) through the
+// Gram matrix's eigenvectors, in double precision; see factor.hip).  Returns
+// 0, or -5 with the failing HIP call in *why.
+int factorize_device(int bf16, int batch, int hkv, int s, int d, int r, const void *k_pre, void *A, void *B,
+                     hipStream_t st, std::string *why, int *sweeps_out);
 
 // ---- launchers (return the launch status) ----------------------------------
 // Prefill.

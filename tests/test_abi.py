@@ -92,3 +92,19 @@ def test_null_arguments(lib):
     assert lib.shadowkv_layer_create(None, None) == skv.SKV_E_INVAL
     assert lib.shadowkv_decode_step(None, None, None, None) == skv.SKV_E_INVAL
     assert lib.shadowkv_tensor_bytes(None, 0) == 0
+
+
+@pytest.mark.parametrize("args, code", [
+    ((skv.SKV_BF16, 1, 8, 1024, 128, 160, None, 1, 1), skv.SKV_E_INVAL),   # null k_pre
+    ((7, 1, 8, 1024, 128, 160, 1, 1, 1), skv.SKV_E_INVAL),                  # dtype
+    ((skv.SKV_BF16, 0, 8, 1024, 128, 160, 1, 1, 1), skv.SKV_E_SHAPE),       # batch
+    ((skv.SKV_BF16, 1, 8, 0, 128, 160, 1, 1, 1), skv.SKV_E_SHAPE),          # seq_len
+    ((skv.SKV_BF16, 1, 8, 1024, 96, 160, 1, 1, 1), skv.SKV_E_SHAPE),        # head_dim
+    ((skv.SKV_BF16, 1, 8, 1024, 128, 0, 1, 1, 1), skv.SKV_E_SHAPE),         # rank
+    ((skv.SKV_BF16, 1, 8, 1024, 128, 257, 1, 1, 1), skv.SKV_E_SHAPE),       # rank
+    ((skv.SKV_BF16, 1, 64, 1024, 128, 160, 1, 1, 1), skv.SKV_E_SHAPE),      # n = 8192 > 4096
+])
+def test_factorize_rejects_bad_arguments_before_the_device(lib, args, code):
+    # the pointer arguments are never dereferenced on these paths
+    assert lib.shadowkv_factorize(*args, None, None) == code
+    assert skv.shadowkv_last_error()

@@ -27,7 +27,6 @@ from oracle import Shape
 from parity_helpers import OUT_TOL, SHARP_Q, bf16_ulp, check_outliers, check_selection, log, to_np
 from sparse_kv_cache_step_amd import binding as skv
 from sparse_kv_cache_step_amd import synth
-from sparse_kv_cache_step_amd.setup import svd_factors
 
 pytestmark = pytest.mark.gpu
 
@@ -54,7 +53,7 @@ def test_full_size_sampled_sequence(case):
     qs = synth.queries_torch(wl, layer_id, dev, steps=steps)
     # then the next queries of the same drift, x8
     qs = torch.cat([qs, synth.queries_torch(wl.with_(q_scale=q_sharp), layer_id, dev, steps=steps + sharp)[steps:]])
-    A, B = svd_factors(k_pre, wl.r)
+    A, B = skv.factorize(k_pre, wl.r)
     layer = skv.Layer(batch=wl.b, heads_q=wl.h_q, heads_kv=wl.h_kv, head_dim=wl.d, seq_len=wl.s, chunk=wl.c,
                       rank=wl.r, n_outlier=wl.o, top_k=wl.k, local_window=wl.w, bf16=True)
     hb = layer.host_buffer()

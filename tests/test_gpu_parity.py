@@ -20,7 +20,6 @@ from parity_helpers import (OUT_TOL, SHARP_32K, bf16_ulp, check_outliers, check_
                             oracle_shape, tdtype, to_dev, to_np)
 from sparse_kv_cache_step_amd import binding as skv
 from sparse_kv_cache_step_amd import synth
-from sparse_kv_cache_step_amd.setup import svd_factors
 
 pytestmark = pytest.mark.gpu
 
@@ -74,7 +73,7 @@ CASES = {
 def _gpu_state(wl, k_pre, v):
     dt = tdtype(wl)
     k_pre_d, v_d = to_dev(k_pre, dt), to_dev(v, dt)
-    A_d, B_d = svd_factors(k_pre_d, wl.r)
+    A_d, B_d = skv.factorize(k_pre_d, wl.r)
     layer = skv.Layer(**layer_kwargs(wl))
     hb = layer.host_buffer()
     layer.prefill_meta(k_pre_d, v_d, A_d, B_d, hb)
@@ -324,7 +323,7 @@ def test_append_decode_tokens_matches_oracle(case):
     A_o, B_o = oracle.svd_factors(shape, k_pre)
     dt = tdtype(wl)
     k_pre_d, v_d = to_dev(k_pre, dt), to_dev(v, dt)
-    A_d, B_d = svd_factors(k_pre_d, wl.r)
+    A_d, B_d = skv.factorize(k_pre_d, wl.r)
     layer = skv.Layer(**layer_kwargs(wl), max_new=max_new)
     hb = layer.host_buffer()
     layer.prefill_meta(k_pre_d, v_d, A_d, B_d, hb)
@@ -390,7 +389,7 @@ def test_snapkv_selection_matches_oracle(case):
     A_o, B_o = oracle.svd_factors(shape, k_pre)
     dt = tdtype(wl)
     k_pre_d, v_d = to_dev(k_pre, dt), to_dev(v, dt)
-    A_d, B_d = svd_factors(k_pre_d, wl.r)
+    A_d, B_d = skv.factorize(k_pre_d, wl.r)
     layer = skv.Layer(**layer_kwargs(wl))
     hb = layer.host_buffer()
     layer.prefill_meta(k_pre_d, v_d, A_d, B_d, hb)
@@ -517,7 +516,7 @@ def test_lru_cache_matches_oracle(case):
     A_o, B_o = oracle.svd_factors(shape, k_pre)
     dt = tdtype(wl)
     k_pre_d, v_d = to_dev(k_pre, dt), to_dev(v, dt)
-    A_d, B_d = svd_factors(k_pre_d, wl.r)
+    A_d, B_d = skv.factorize(k_pre_d, wl.r)
     layer = skv.Layer(**layer_kwargs(wl), cache_chunks=cap)
     hb = layer.host_buffer()
     layer.prefill_meta(k_pre_d, v_d, A_d, B_d, hb)
@@ -565,7 +564,7 @@ def test_fused_attention_matches_separate_kernels(case, cap, monkeypatch):
     k_pre, v, qs = synth.k_pre_numpy(wl), synth.v_numpy(wl), synth.queries_numpy(wl)
     dt = tdtype(wl)
     k_pre_d, v_d = to_dev(k_pre, dt), to_dev(v, dt)
-    A_d, B_d = svd_factors(k_pre_d, wl.r)
+    A_d, B_d = skv.factorize(k_pre_d, wl.r)
     layers = []
     for fused in ("1", "0"):
         monkeypatch.setenv("SKV_ATTN_FUSED", fused)
@@ -609,7 +608,7 @@ def test_modes_combined_on_one_layer():
     A_o, B_o = oracle.svd_factors(shape, k_pre)
     dt = tdtype(wl)
     k_pre_d, v_d = to_dev(k_pre, dt), to_dev(v, dt)
-    A_d, B_d = svd_factors(k_pre_d, wl.r)
+    A_d, B_d = skv.factorize(k_pre_d, wl.r)
     layer = skv.Layer(**layer_kwargs(wl), max_new=max_new, cache_chunks=cap)
     hb = layer.host_buffer()
     layer.prefill_meta(k_pre_d, v_d, A_d, B_d, hb)

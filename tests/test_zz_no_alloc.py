@@ -12,7 +12,6 @@ import torch
 from parity_helpers import OUT_TOL, layer_kwargs, log, tdtype, to_dev
 from sparse_kv_cache_step_amd import binding as skv
 from sparse_kv_cache_step_amd import synth
-from sparse_kv_cache_step_amd.setup import svd_factors
 
 pytestmark = pytest.mark.gpu
 
@@ -22,7 +21,7 @@ def _pair(wl):
     dt = tdtype(wl)
     k_pre, v = synth.k_pre_numpy(wl), synth.v_numpy(wl)
     k_d, v_d = to_dev(k_pre, dt), to_dev(v, dt)
-    A, B = svd_factors(k_d, wl.r)
+    A, B = skv.factorize(k_d, wl.r)
     out = []
     for _ in range(2):
         lay = skv.Layer(**layer_kwargs(wl))
