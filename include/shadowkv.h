@@ -64,7 +64,8 @@ enum {
  *   local_window a multiple of chunk, 0 <= local_window <= seq_len;
  *   n = seq_len / chunk, n_loc = local_window / chunk;
  *   0 <= n_outlier <= n - n_loc; 0 <= top_k <= n - n_loc - n_outlier and
- *   top_k <= 4096; at least one attended key; 1 <= rank <= 256;
+ *   top_k <= 4096; at least one attended key; 1 <= rank <= 256 (a multiple
+ *   of 8 for bfloat16);
  *   rope_base > 0; 0 <= max_new <= 2^20;
  *   cache_chunks 0 (= top_k) or top_k <= cache_chunks <= n - n_loc - n_outlier,
  *   at most 16384.

@@ -492,7 +492,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint16_t *__restrict__ k_out, const uint16_t *__restrict__ v_out, const uint16_t *__restrict__ k_loc,
     const uint16_t *__restrict__ v_loc, const uint16_t *__restrict__ vc, float2 *__restrict__ part_ml,
     float *__restrict__ part_acc, int hkv, int G, int s, int c, int r, int r_pad, int k, int cap, int OC, int KC,
-    int w, int wcap, int ts, int T, int rows, float scale) {
+    int w, int wcap, int ts, int T, int rows, float scale, int cshift) {
     static_assert(GP <= 16, "query heads are the rows of one 16-row MFMA block");
     constexpr int NB = D / 16, HB = NB / 2, NP = NB / 2, MB = 4, STG = D / 8;
     constexpr int KB = D / 32;                      // 32-column slabs of a value row
@@ -502,6 +502,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     extern __shared__ uint16_t dyn[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, quad = lane >> 4;
+    // logits in base-2 units (log2(e) folded into the scale), so the softmax
+    // takes v_exp_f32 directly; the split's max goes out in natural units
+    constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+    const float scale2 = scale * kLog2e;
     // XCD-aware order: workgroups are dispatched to the 8 XCDs round-robin by
     // linear index, so tile t of row bh is given index (8*(bh/8)*T + 8*t) +
     // bh%8: all of a row's workgroups share one XCD, and the row's B, which
@@ -512,7 +516,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (bh >= rows) return;  // workgroup-uniform, before any barrier
     const int b = bh / hkv, h = bh % hkv;
     const int hq = hkv * G;
-    const int ldb = r_pad + 8;
+    const int ldb = NKB * 32 + 8;   // r_pad = 32 * NKB
     const bool rebuild = tile < ts;  // workgroup-uniform
     uint16_t *Bs = dyn;              // D x (r_pad + 8), rebuilding workgroups only
     // per wave: first its weights (GP x PW floats), then, once it has read
@@ -569,32 +573,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) vr[mb][kb] = u32x4{0u, 0u, 0u, 0u};
     if (rebuild) {
-        const int pos0 = key_base / c;
+        const int pos0 = cshift >= 0 ? key_base >> cshift : key_base / c;
         const int my_chunk = chunks[static_cast<size_t>(bh) * k + min(pos0 + lane, k - 1)];
         // rotation rates (turns per position) of this lane's dims
         // 16*hb + 4*quad + e: theta_rev[4*quad + e] times the ratio of the
         // rates 16*hb dims apart, theta_rev[16*hb] / theta_rev[0]
         double thr0[4], rat[HB];
+        const double inv_thr0 = 1.0 / theta_rev[0];
 #pragma unroll
         for (int e = 0; e < 4; ++e) thr0[e] = theta_rev[quad * 4 + e];
 #pragma unroll
-        for (int hb = 0; hb < HB; ++hb) rat[hb] = theta_rev[hb * 16] / theta_rev[0];
+        for (int hb = 0; hb < HB; ++hb) rat[hb] = theta_rev[hb * 16] * inv_thr0;
         {
-            // stage B[h] (transposed, d x r) with every load in flight
-            const uint16_t *Btb = Bt + static_cast<size_t>(bh) * D * r;
-            const int vpr = r_pad / 8, total = D * vpr;
-            u32x4 tmp[STG];
+            // stage B[h] (transposed, d x r) with every load in flight: row
+            // nr of Bt, 8 rank values from kc; ranks past r read zeros
+            // through the buffer resource's range check
+            constexpr int VPR = NKB * 4, TOT = D * VPR, NIT = (TOT + 255) / 256;
+            const Rsrc brs = make_rsrc(Bt + static_cast<size_t>(bh) * D * r, static_cast<uint32_t>(D) * r * 2);
+            u32x4 tmp[NIT];
 #pragma unroll
-            for (int i = 0; i < STG; ++i) {
+            for (int i = 0; i < NIT; ++i) {
                 const int ix = tid + 256 * i;
-                const int nr = ix / vpr, kc = (ix % vpr) * 8;
-                tmp[i] = (ix < total && kc < r) ? *reinterpret_cast<const u32x4 *>(Btb + static_cast<size_t>(nr) * r + kc)
-                                                : u32x4{0u, 0u, 0u, 0u};
+                const int nr = ix / VPR, kc = (ix % VPR) * 8;
+                tmp[i] = buf_ld128(brs, (ix < TOT && kc < r) ? (nr * r + kc) * 2 : kOob);
             }
 #pragma unroll
-            for (int i = 0; i < STG; ++i) {
+            for (int i = 0; i < NIT; ++i) {
                 const int ix = tid + 256 * i;
-                if (ix < total) *reinterpret_cast<u32x4 *>(Bs + (ix / vpr) * ldb + (ix % vpr) * 8) = tmp[i];
+                if (ix < TOT) *reinterpret_cast<u32x4 *>(Bs + (ix / VPR) * ldb + (ix % VPR) * 8) = tmp[i];
             }
         }
         // Gathered A row of this lane's key in each 16-key block, 8 rank
@@ -609,8 +615,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int key = key_base + mb * 16 + row;
             const bool kv = active && key < KC;
             const int kk = key < KC ? key : key_base;
-            const int chunk = __shfl(my_chunk, kk / c - pos0, 64);
-            pos[mb] = chunk * c + kk % c;
+            const int kq = cshift >= 0 ? kk >> cshift : kk / c;  // c = 2^cshift: shifts
+            const int chunk = __shfl(my_chunk, kq - pos0, 64);
+            pos[mb] = chunk * c + (kk - kq * c);
             vkey[mb] = key < KC ? key : (KC > 0 ? KC - 1 : 0);  // a valid value row; its weight is 0
             const int base = (pos[mb] * r + quad * 8) * 2;
 #pragma unroll
@@ -687,7 +694,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     const f32x4 l4 = logits_hilo<NP>(qa, ac, f32x4{0.f, 0.f, 0.f, 0.f});
                     const bool kv = kb0 + row < KC;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) lg[mb][e] = kv ? l4[e] * scale : -INFINITY;
+                    for (int e = 0; e < 4; ++e) lg[mb][e] = kv ? l4[e] * scale2 : -INFINITY;
                 }
             }
         }
@@ -699,7 +706,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         for (int p = 0; p < NP; ++p) l4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[p], sko[p], l4, 0, 0, 0);
         const bool kv = sb0 + row < nstat;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) lg[MB][e] = kv ? l4[e] * scale : -INFINITY;
+        for (int e = 0; e < 4; ++e) lg[MB][e] = kv ? l4[e] * scale2 : -INFINITY;
     } else {
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) svr[kb] = u32x4{0u, 0u, 0u, 0u};
@@ -716,7 +723,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         float l = 0.f;
 #pragma unroll
         for (int mb = 0; mb <= MB; ++mb) {
-            const float p = m == -INFINITY ? 0.f : expf(lg[mb][e] - m);
+            const float p = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(lg[mb][e] - m);
             lg[mb][e] = p;
             l += p;
         }
@@ -812,14 +819,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int wv = 0; wv < 4; ++wv) {
                 const float *rr = rec + wv * RGN + g * RP;
-                const float wgt = expf(rr[D] - M);
+                const float wgt = __builtin_amdgcn_exp2f(rr[D] - M);
                 Ls += wgt * rr[D + 1];
                 a += wgt * rr[i];
             }
         }
         const size_t rc = (static_cast<size_t>(bh) * G + g) * T + tile;
         part_acc[rc * D + i] = a;
-        if (i == 0) part_ml[rc] = make_float2(M, Ls);
+        if (i == 0) part_ml[rc] = make_float2(M * kLn2, Ls);  // natural-log units for the merge kernel
     }
 }
 
@@ -986,8 +993,14 @@ __global__ __launch_bounds__(256) void pv_kernel(const float *__restrict__ logit
 template <typename T, int D>
 __global__ __launch_bounds__(D) void combine_kernel(const float2 *__restrict__ part_ml,
                                                     const float *__restrict__ part_acc, T *__restrict__ out,
-                                                    int tiles) {
-    const int bg = blockIdx.x, i = threadIdx.x;
+                                                    int tiles, int G, int rows) {
+    // XCD-aware order, as the fused attention kernel's: query head g of row bh
+    // (sequence, KV head) runs on XCD bh % 8, where that row's splits were
+    // written.  Indices past the last row (rows rounded up to 8) exit at once.
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int bh = (j / G) * 8 + xcd;
+    if (bh >= rows) return;
+    const int bg = bh * G + j % G, i = threadIdx.x;
     const float2 *ml = part_ml + static_cast<size_t>(bg) * tiles;
     const float *pa = part_acc + static_cast<size_t>(bg) * tiles * D + i;
     constexpr int TMAX = 16;  // splits held in registers (all loads in flight); more are streamed
@@ -1189,7 +1202,8 @@ static hipError_t attn_t(const Dims &dm, const void *q, const void *A, const voi
                        theta_rev, static_cast<const uint16_t *>(k_out), static_cast<const uint16_t *>(v_out),
                        static_cast<const uint16_t *>(k_loc), static_cast<const uint16_t *>(v_loc),
                        static_cast<const uint16_t *>(vc), part_ml, part_acc, dm.hkv, dm.G, dm.s, dm.c, dm.r, r_pad,
-                       dm.k, dm.cap, dm.OC, dm.KC, dm.w, dm.wcap, ts, T, rows, dm.scale);
+                       dm.k, dm.cap, dm.OC, dm.KC, dm.w, dm.wcap, ts, T, rows, dm.scale,
+                       (dm.c & (dm.c - 1)) == 0 ? __builtin_ctz(dm.c) : -1);
     return hipGetLastError();
 }
 
@@ -1253,21 +1267,21 @@ hipError_t launch_attn(const Dims &dm, const void *q, const void *A, const void 
 
 hipError_t launch_combine(const Dims &dm, const float2 *part_ml, const float *part_acc, void *out, int splits,
                           hipStream_t st) {
-    const int blocks = dm.b * dm.hq;
+    const int rows = dm.b * dm.hkv, blocks = (rows + 7) / 8 * 8 * dm.G;
     if (dm.bf16) {
         if (dm.d == 128)
             hipLaunchKernelGGL((combine_kernel<uint16_t, 128>), dim3(blocks), dim3(128), 0, st, part_ml, part_acc,
-                               static_cast<uint16_t *>(out), splits);
+                               static_cast<uint16_t *>(out), splits, dm.G, rows);
         else
             hipLaunchKernelGGL((combine_kernel<uint16_t, 64>), dim3(blocks), dim3(64), 0, st, part_ml, part_acc,
-                               static_cast<uint16_t *>(out), splits);
+                               static_cast<uint16_t *>(out), splits, dm.G, rows);
     } else {
         if (dm.d == 128)
             hipLaunchKernelGGL((combine_kernel<float, 128>), dim3(blocks), dim3(128), 0, st, part_ml, part_acc,
-                               static_cast<float *>(out), splits);
+                               static_cast<float *>(out), splits, dm.G, rows);
         else
             hipLaunchKernelGGL((combine_kernel<float, 64>), dim3(blocks), dim3(64), 0, st, part_ml, part_acc,
-                               static_cast<float *>(out), splits);
+                               static_cast<float *>(out), splits, dm.G, rows);
     }
     return hipGetLastError();
 }

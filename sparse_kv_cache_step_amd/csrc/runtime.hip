@@ -51,6 +51,8 @@ int make_dims(const skv_config &c, Dims *dm, std::string *why) {
     if (c.top_k < 0 || c.top_k > n - n_loc - c.n_outlier) return bad("top_k must be in [0, n - n_loc - n_outlier]");
     if (c.top_k > 4096) return bad("top_k must be <= 4096");
     if (c.rank < 1 || c.rank > 256) return bad("rank must be in [1, 256]");
+    // the bfloat16 rebuild reads 8 rank values per 16-byte load of an A or B row
+    if (c.dtype == SKV_BF16 && c.rank % 8) return bad("bfloat16 layers need rank a multiple of 8");
     if (!(c.rope_base > 0.f)) return bad("rope_base must be > 0");
     if (c.max_new < 0 || c.max_new > (1 << 20)) return bad("max_new must be in [0, 2^20]");
     if (c.cache_chunks != 0 && (c.cache_chunks < c.top_k || c.cache_chunks > n - n_loc - c.n_outlier))

@@ -73,6 +73,7 @@ def _cfg(**kw):
     (dict(top_k=121), skv.SKV_E_SHAPE),                     # > n - n_loc - o
     (dict(rank=0), skv.SKV_E_SHAPE),
     (dict(rank=257), skv.SKV_E_SHAPE),
+    (dict(rank=100, dtype=skv.SKV_BF16), skv.SKV_E_SHAPE),  # bfloat16 rank not a multiple of 8
     (dict(chunk=65, seq_len=65 * 16, local_window=0), skv.SKV_E_SHAPE),
     (dict(n_outlier=0, top_k=0, local_window=0), skv.SKV_E_SHAPE),  # nothing to attend
     (dict(rope_base=0.0), skv.SKV_E_SHAPE),
