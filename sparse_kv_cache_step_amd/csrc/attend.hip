@@ -250,15 +250,24 @@ __device__ __forceinline__ float swap_sum16(float lo, float hi) {
 // q . x = q . hi + q . lo carries ~16 significant bits of every key instead
 // of bfloat16's 8: one rounding of the keys would cost up to ~1e-2 of output
 // at sharp attention, the same order as the bfloat16 error bar.
+// Adjacent values are converted in pairs (one v_cvt_pk_bf16_f32 each), and
+// hi goes back to binary32 by shifting its bits into place.
+__device__ __forceinline__ uint32_t cvt2_bf16(float x, float y) {
+    typedef __attribute__((ext_vector_type(2))) float f32x2;
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x, y}, bf16x2));
+}
 __device__ __forceinline__ void split_bf16x8(f32x4 a, f32x4 b, bf16x8 &hi, bf16x8 &lo) {
+    const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    u32x4 h, l;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const __bf16 ha = static_cast<__bf16>(a[e]), hb = static_cast<__bf16>(b[e]);
-        hi[e] = ha;
-        hi[4 + e] = hb;
-        lo[e] = static_cast<__bf16>(a[e] - static_cast<float>(ha));
-        lo[4 + e] = static_cast<__bf16>(b[e] - static_cast<float>(hb));
+    for (int k = 0; k < 4; ++k) {
+        h[k] = cvt2_bf16(v[2 * k], v[2 * k + 1]);
+        const float h0 = __uint_as_float(h[k] << 16), h1 = __uint_as_float(h[k] & 0xffff0000u);
+        l[k] = cvt2_bf16(v[2 * k] - h0, v[2 * k + 1] - h1);
     }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
 }
 
 // logits of one 16-key block: lg += q . (hi + lo) over the NP 32-dim pairs
@@ -453,8 +462,9 @@ template <typename Op> __device__ __forceinline__ float row16_reduce(float v, Op
 }
 
 // Two floats that hold bfloat16 values, as two bfloat16 in one dword (exact).
+// (v_perm_b32: the upper two bytes of a, then those of b)
 __device__ __forceinline__ uint32_t pack2_exact(float a, float b) {
-    return (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xffff0000u);
+    return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
 }
 
 // ---------------------------------------------------------------------------
