@@ -502,7 +502,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const uint16_t *__restrict__ k_out, const uint16_t *__restrict__ v_out, const uint16_t *__restrict__ k_loc,
     const uint16_t *__restrict__ v_loc, const uint16_t *__restrict__ vc, float2 *__restrict__ part_ml,
     float *__restrict__ part_acc, int hkv, int G, int s, int c, int r, int r_pad, int k, int cap, int OC, int KC,
-    int w, int wcap, int ts, int T, int rows, float scale, int cshift) {
+    int w, int wcap, int ts, int T, int rows, float scale, int cshift, int kpw) {
     static_assert(GP <= 16, "query heads are the rows of one 16-row MFMA block");
     constexpr int NB = D / 16, HB = NB / 2, NP = NB / 2, MB = 4, STG = D / 8;
     constexpr int KB = D / 32;                      // 32-column slabs of a value row
@@ -533,8 +533,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // them, its merge record (GP x RP floats)
     float *rec = reinterpret_cast<float *>(dyn + (ts > 0 ? static_cast<size_t>(D) * ldb : 0));
     float *ps = rec + wave * RGN;
-    const int key_base = tile * kQkMfmaTile + wave * 64;
+    const int key_base = tile * 4 * kpw + wave * kpw;
     const bool active = rebuild && key_base < KC;  // wave-uniform
+    const int kend = min(KC, key_base + kpw);       // end of this wave's rebuilt keys
     const int nstat = OC + w;
     const int sb0 = (tile * 4 + wave) * 16;  // first key of this wave's static block
 
@@ -623,12 +624,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int key = key_base + mb * 16 + row;
-            const bool kv = active && key < KC;
-            const int kk = key < KC ? key : key_base;
+            const bool kv = active && key < kend;
+            const int kk = key < kend ? key : key_base;
             const int kq = cshift >= 0 ? kk >> cshift : kk / c;  // c = 2^cshift: shifts
             const int chunk = __shfl(my_chunk, kq - pos0, 64);
             pos[mb] = chunk * c + (kk - kq * c);
-            vkey[mb] = key < KC ? key : (KC > 0 ? KC - 1 : 0);  // a valid value row; its weight is 0
+            vkey[mb] = key < kend ? key : (KC > 0 ? KC - 1 : 0);  // a valid value row; its weight is 0
             const int base = (pos[mb] * r + quad * 8) * 2;
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
@@ -643,7 +644,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         constexpr int BP = (NKB >= 4 && NKB <= 6) ? 2 : 1;
 #pragma unroll
         for (int mp = 0; mp < MB; mp += BP) {
-            if (active && key_base + mp * 16 < KC) {  // wave-uniform
+            if (active && key_base + mp * 16 < kend) {  // wave-uniform
                 // K^T[dim, key] = sum_r Bt[dim, r] A[key, r]: lane (quad, row)
                 // ends with key `row`, dims 16*nb + 4*quad + e, of each block
                 f32x4 acc[BP][NB];
@@ -702,7 +703,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                         }
                     }
                     const f32x4 l4 = logits_hilo<NP>(qa, ac, f32x4{0.f, 0.f, 0.f, 0.f});
-                    const bool kv = kb0 + row < KC;
+                    const bool kv = kb0 + row < kend;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) lg[mb][e] = kv ? l4[e] * scale2 : -INFINITY;
                 }
@@ -1195,7 +1196,7 @@ static hipError_t attn_t(const Dims &dm, const void *q, const void *A, const voi
                          const int32_t *sel_slot, const double *theta_rev, const void *k_out, const void *v_out,
                          const void *k_loc, const void *v_loc, const void *vc, float2 *part_ml, float *part_acc,
                          hipStream_t st) {
-    const int ts = (dm.KC + kQkMfmaTile - 1) / kQkMfmaTile;
+    const int ts = (dm.KC + 4 * dm.kpw - 1) / (4 * dm.kpw);
     const int T = attn_workgroups(dm);
     const int r_pad = NKB * 32;
     constexpr int RGN = GP * (84 > D + 2 ? 84 : D + 2);  // LDS floats per wave: weights, then merge record
@@ -1213,7 +1214,7 @@ static hipError_t attn_t(const Dims &dm, const void *q, const void *A, const voi
                        static_cast<const uint16_t *>(k_loc), static_cast<const uint16_t *>(v_loc),
                        static_cast<const uint16_t *>(vc), part_ml, part_acc, dm.hkv, dm.G, dm.s, dm.c, dm.r, r_pad,
                        dm.k, dm.cap, dm.OC, dm.KC, dm.w, dm.wcap, ts, T, rows, dm.scale,
-                       (dm.c & (dm.c - 1)) == 0 ? __builtin_ctz(dm.c) : -1);
+                       (dm.c & (dm.c - 1)) == 0 ? __builtin_ctz(dm.c) : -1, dm.kpw);
     return hipGetLastError();
 }
 
@@ -1253,7 +1254,7 @@ static hipError_t attn_g(const Dims &dm, const void *q, const void *A, const voi
 }
 
 int attn_workgroups(const Dims &dm) {
-    const int ts = (dm.KC + kQkMfmaTile - 1) / kQkMfmaTile;
+    const int ts = (dm.KC + 4 * dm.kpw - 1) / (4 * dm.kpw);
     return std::max(ts, (dm.OC + dm.w + 63) / 64);
 }
 

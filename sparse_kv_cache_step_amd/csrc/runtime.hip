@@ -86,6 +86,7 @@ int make_dims(const skv_config &c, Dims *dm, std::string *why) {
     d.esize = c.dtype == SKV_BF16 ? 2 : 4;
     d.bf16 = c.dtype == SKV_BF16;
     d.r_pad = round_up(c.rank, 32);
+    d.kpw = 64;  // rebuilt keys per wave of the fused attention kernel
     d.scale = 1.0f / std::sqrt(static_cast<float>(c.head_dim));
     return SKV_OK;
 }
@@ -373,6 +374,11 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     std::string why;
     int rc = make_dims(*cfg, &dm, &why);
     if (rc) return fail(rc, why);
+    // SKV_TOPK_SLICE (a multiple of 64): chunks per slice of the two-pass Top-K
+    if (const char *e = std::getenv("SKV_TOPK_SLICE")) {
+        const int v = std::atoi(e);
+        if (v >= 64 && v % 64 == 0) dm.tslice = v;
+    }
 
     skv_layer *ly = new skv_layer();
     ly->cfg = *cfg;
@@ -389,6 +395,15 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, ly->device) != hipSuccess)
         return bail(fail(SKV_E_HIP, "hipDeviceGetAttribute(MaxSharedMemoryPerBlock) failed"));
     ly->lds_limit = lds;
+    // rebuilt keys per wave of the fused attention kernel: 64 (measured at
+    // 128K b8 and the GLM shape, 48 and 32 keys per wave were slower: their
+    // extra workgroups each stage B again); SKV_ATTN_KPW (48, 32 or 16) forces
+    // another
+    if (const char *e = std::getenv("SKV_ATTN_KPW")) {
+        const int v = std::atoi(e);
+        if (v == 64 || v == 48 || v == 32 || v == 16) dm.kpw = v;
+        ly->dm.kpw = dm.kpw;
+    }
     // Scoring grid: 0 picks two 64-chunk tiles per wave; SKV_SCORE_WGS
     // overrides the workgroup count for tuning.
     ly->score_wgs = 0;

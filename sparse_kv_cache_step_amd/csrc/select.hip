@@ -1041,7 +1041,7 @@ size_t select_dynamic_lds(const Dims &dm, bool keys_in_lds) {
            (keys_in_lds ? static_cast<size_t>(dm.n) * sizeof(uint32_t) : 0);
 }
 
-int topk_slice(const Dims &dm) { return dm.k <= 1024 ? 4096 : 16384; }
+int topk_slice(const Dims &dm) { return dm.tslice > 0 ? dm.tslice : dm.k <= 1024 ? 4096 : 16384; }
 
 int topk_slices(const Dims &dm) { return (dm.n + topk_slice(dm) - 1) / topk_slice(dm); }
 

@@ -35,6 +35,8 @@ struct Dims {
     int bf16;        // storage type
     int r_pad;       // rank rounded up to 32
     float scale;     // 1 / sqrt(d)
+    int tslice;      // chunks per slice of the two-pass Top-K (0: by k)
+    int kpw;         // rebuilt keys per wave of the fused attention kernel (64, 48 or 32)
 };
 
 // Low-rank key factors of `batch` sequences (A, B <- SVD(K_pre) through the

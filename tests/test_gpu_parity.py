@@ -140,7 +140,21 @@ def _check_cache_lossless(wl, layer, v, sel, resident=None):
 
 @pytest.mark.parametrize("case", list(CASES))
 def test_end_to_end_matches_oracle(case):
-    wl = CASES[case]
+    _end_to_end(case, CASES[case])
+
+
+# The fused kernel's rebuilt keys per wave (64 by default; 48, 32 or 16 when
+# forced) on discriminating cases; 48 keys start waves mid-chunk at chunk 16,
+# and the fourth block of a wave is then empty.
+@pytest.mark.parametrize("case,kpw", [("bf16-llama-32k-sharp", 48), ("bf16-llama-32k-sharp", 32),
+                                      ("bf16-llama-32k-sharp", 16), ("bf16-g16-sharp", 64),
+                                      ("bf16-g16-sharp", 32), ("bf16-chunk16", 48), ("bf16-rank96-chunk4", 48)])
+def test_keys_per_wave_matches_oracle(case, kpw, monkeypatch):
+    monkeypatch.setenv("SKV_ATTN_KPW", str(kpw))
+    _end_to_end(f"{case}-kpw{kpw}", CASES[case])
+
+
+def _end_to_end(case, wl):
     log(f"[{case}] b={wl.b} h_q={wl.h_q} h_kv={wl.h_kv} d={wl.d} s={wl.s} c={wl.c} r={wl.r} o={wl.o} "
         f"k={wl.k} w={wl.w} bf16={wl.bf16} steps={wl.steps}")
     shape = oracle_shape(wl)
