@@ -495,8 +495,8 @@ __device__ __forceinline__ uint32_t pack2_exact(float a, float b) {
 // Workgroups past ts (more static blocks than rebuilt-key waves) skip the
 // rebuild and its barrier (a workgroup-uniform branch); every workgroup
 // reaches the final barrier.
-template <int D, int GP, int NKB, bool IND>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(
+template <int D, int GP, int NKB, bool IND, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_mfma_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ A, const uint16_t *__restrict__ Bt,
     const int32_t *__restrict__ chunks, const int32_t *__restrict__ sel_slot, const double *__restrict__ theta_rev,
     const uint16_t *__restrict__ k_out, const uint16_t *__restrict__ v_out, const uint16_t *__restrict__ k_loc,
@@ -533,11 +533,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // them, its merge record (GP x RP floats)
     float *rec = reinterpret_cast<float *>(dyn + (ts > 0 ? static_cast<size_t>(D) * ldb : 0));
     float *ps = rec + wave * RGN;
-    const int key_base = tile * 4 * kpw + wave * kpw;
+    const int key_base = tile * NW * kpw + wave * kpw;
     const bool active = rebuild && key_base < KC;  // wave-uniform
     const int kend = min(KC, key_base + kpw);       // end of this wave's rebuilt keys
     const int nstat = OC + w;
-    const int sb0 = (tile * 4 + wave) * 16;  // first key of this wave's static block
+    const int sb0 = (tile * NW + wave) * 16;  // first key of this wave's static block
 
     // ---- 1. queries and the static block -------------------------------------------
     // the group's queries as the logit MFMA's A operand: lane (quad, row)
@@ -599,18 +599,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             // stage B[h] (transposed, d x r) with every load in flight: row
             // nr of Bt, 8 rank values from kc; ranks past r read zeros
             // through the buffer resource's range check
-            constexpr int VPR = NKB * 4, TOT = D * VPR, NIT = (TOT + 255) / 256;
+            constexpr int VPR = NKB * 4, TOT = D * VPR, NT = 64 * NW, NIT = (TOT + NT - 1) / NT;
             const Rsrc brs = make_rsrc(Bt + static_cast<size_t>(bh) * D * r, static_cast<uint32_t>(D) * r * 2);
             u32x4 tmp[NIT];
 #pragma unroll
             for (int i = 0; i < NIT; ++i) {
-                const int ix = tid + 256 * i;
+                const int ix = tid + NT * i;
                 const int nr = ix / VPR, kc = (ix % VPR) * 8;
                 tmp[i] = buf_ld128(brs, (ix < TOT && kc < r) ? (nr * r + kc) * 2 : kOob);
             }
 #pragma unroll
             for (int i = 0; i < NIT; ++i) {
-                const int ix = tid + 256 * i;
+                const int ix = tid + NT * i;
                 if (ix < TOT) *reinterpret_cast<u32x4 *>(Bs + (ix / VPR) * ldb + (ix % VPR) * 8) = tmp[i];
             }
         }
@@ -820,15 +820,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         }
     }
     __syncthreads();  // every wave of the workgroup reaches it (no early exit above)
-    for (int ix = tid; ix < G * D; ix += 256) {
+    for (int ix = tid; ix < G * D; ix += 64 * NW) {
         const int g = ix / D, i = ix % D;
         float M = -INFINITY;
 #pragma unroll
-        for (int wv = 0; wv < 4; ++wv) M = fmaxf(M, rec[wv * RGN + g * RP + D]);
+        for (int wv = 0; wv < NW; ++wv) M = fmaxf(M, rec[wv * RGN + g * RP + D]);
         float Ls = 0.f, a = 0.f;
         if (M != -INFINITY) {
 #pragma unroll
-            for (int wv = 0; wv < 4; ++wv) {
+            for (int wv = 0; wv < NW; ++wv) {
                 const float *rr = rec + wv * RGN + g * RP;
                 const float wgt = __builtin_amdgcn_exp2f(rr[D] - M);
                 Ls += wgt * rr[D + 1];
@@ -1191,24 +1191,24 @@ hipError_t launch_pv(const Dims &dm, const float *logits, const void *v_out, con
 }
 
 
-template <int D, int GP, int NKB, bool IND>
+template <int D, int GP, int NKB, bool IND, int NW>
 static hipError_t attn_t(const Dims &dm, const void *q, const void *A, const void *Bt, const int32_t *chunks,
                          const int32_t *sel_slot, const double *theta_rev, const void *k_out, const void *v_out,
                          const void *k_loc, const void *v_loc, const void *vc, float2 *part_ml, float *part_acc,
                          hipStream_t st) {
-    const int ts = (dm.KC + 4 * dm.kpw - 1) / (4 * dm.kpw);
+    const int ts = (dm.KC + NW * dm.kpw - 1) / (NW * dm.kpw);
     const int T = attn_workgroups(dm);
     const int r_pad = NKB * 32;
     constexpr int RGN = GP * (84 > D + 2 ? 84 : D + 2);  // LDS floats per wave: weights, then merge record
-    const size_t lds = (ts > 0 ? static_cast<size_t>(D) * (r_pad + 8) * sizeof(uint16_t) : 0) + 4ull * RGN * sizeof(float);
-    auto kern = attn_mfma_kernel<D, GP, NKB, IND>;
+    const size_t lds = (ts > 0 ? static_cast<size_t>(D) * (r_pad + 8) * sizeof(uint16_t) : 0) + static_cast<size_t>(NW) * RGN * sizeof(float);
+    auto kern = attn_mfma_kernel<D, GP, NKB, IND, NW>;
     if (lds > 48 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         if (e != hipSuccess) return e;
     }
     const int rows = dm.b * dm.hkv, rows8 = (rows + 7) / 8 * 8;
-    hipLaunchKernelGGL(kern, dim3(T * rows8), dim3(256), lds, st, static_cast<const uint16_t *>(q),
+    hipLaunchKernelGGL(kern, dim3(T * rows8), dim3(64 * NW), lds, st, static_cast<const uint16_t *>(q),
                        static_cast<const uint16_t *>(A), static_cast<const uint16_t *>(Bt), chunks, sel_slot,
                        theta_rev, static_cast<const uint16_t *>(k_out), static_cast<const uint16_t *>(v_out),
                        static_cast<const uint16_t *>(k_loc), static_cast<const uint16_t *>(v_loc),
@@ -1225,10 +1225,16 @@ static hipError_t attn_r(const Dims &dm, const void *q, const void *A, const voi
                          hipStream_t st) {
     const int need = (dm.r + 31) / 32;
 #define SKV_ATTN(NKB) \
-    attn_t<D, GP, NKB, IND>(dm, q, A, Bt, chunks, sel_slot, theta_rev, k_out, v_out, k_loc, v_loc, vc, part_ml, \
-                            part_acc, st)
+    attn_t<D, GP, NKB, IND, 4>(dm, q, A, Bt, chunks, sel_slot, theta_rev, k_out, v_out, k_loc, v_loc, vc, part_ml, \
+                               part_acc, st)
     if (need <= 2) return SKV_ATTN(2);
     if (need <= 4) return SKV_ATTN(4);
+    if constexpr (D == 128) {
+        // 8-wave workgroups (one per CU, sharing one staged B) at rank 129..160
+        if (need <= 5 && dm.attn_nw == 8)
+            return attn_t<D, GP, 5, IND, 8>(dm, q, A, Bt, chunks, sel_slot, theta_rev, k_out, v_out, k_loc, v_loc,
+                                            vc, part_ml, part_acc, st);
+    }
     if (need <= 5) return SKV_ATTN(5);
     if (need <= 6) return SKV_ATTN(6);
     return SKV_ATTN(8);
@@ -1253,9 +1259,12 @@ static hipError_t attn_g(const Dims &dm, const void *q, const void *A, const voi
     }
 }
 
+int attn_waves(const Dims &dm) { return dm.bf16 && dm.attn_nw == 8 && dm.d == 128 && (dm.r + 31) / 32 == 5 ? 8 : 4; }
+
 int attn_workgroups(const Dims &dm) {
-    const int ts = (dm.KC + 4 * dm.kpw - 1) / (4 * dm.kpw);
-    return std::max(ts, (dm.OC + dm.w + 63) / 64);
+    const int nw = attn_waves(dm);
+    const int ts = (dm.KC + nw * dm.kpw - 1) / (nw * dm.kpw);
+    return std::max(ts, (dm.OC + dm.w + 16 * nw - 1) / (16 * nw));
 }
 
 hipError_t launch_attn(const Dims &dm, const void *q, const void *A, const void *Bt, const int32_t *chunks,

@@ -87,6 +87,7 @@ int make_dims(const skv_config &c, Dims *dm, std::string *why) {
     d.bf16 = c.dtype == SKV_BF16;
     d.r_pad = round_up(c.rank, 32);
     d.kpw = 64;  // rebuilt keys per wave of the fused attention kernel
+    d.attn_nw = 4;
     d.scale = 1.0f / std::sqrt(static_cast<float>(c.head_dim));
     return SKV_OK;
 }
@@ -399,6 +400,22 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     // 128K b8 and the GLM shape, 48 and 32 keys per wave were slower: their
     // extra workgroups each stage B again); SKV_ATTN_KPW (48, 32 or 16) forces
     // another
+    // waves per fused attention workgroup: 8 (one workgroup per CU, one
+    // staged B for 512 keys) when the launch then still fits the CUs at once,
+    // else 4 (measured: 128K b8 31.9 -> 30.7 us, GLM-shaped 244K b12 31.9 ->
+    // 30.9 us with 8; 60K b48, three rounds of workgroups, 89 -> 128 us);
+    // SKV_ATTN_WAVES (4 or 8) forces it
+    {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, ly->device) != hipSuccess || cus < 1)
+            return bail(fail(SKV_E_HIP, "hipDeviceGetAttribute(MultiprocessorCount) failed"));
+        Dims t = dims_with_local(dm, dm.wcap);
+        t.attn_nw = 8;
+        dm.attn_nw = skv::attn_waves(t) == 8 && static_cast<long long>(dm.b) * dm.hkv * skv::attn_workgroups(t) <= cus
+                         ? 8 : 4;
+        if (const char *e = std::getenv("SKV_ATTN_WAVES")) dm.attn_nw = std::atoi(e) == 8 ? 8 : 4;
+        ly->dm.attn_nw = dm.attn_nw;
+    }
     if (const char *e = std::getenv("SKV_ATTN_KPW")) {
         const int v = std::atoi(e);
         if (v == 64 || v == 48 || v == 32 || v == 16) dm.kpw = v;

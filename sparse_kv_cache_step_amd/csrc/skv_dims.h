@@ -36,7 +36,8 @@ struct Dims {
     int r_pad;       // rank rounded up to 32
     float scale;     // 1 / sqrt(d)
     int tslice;      // chunks per slice of the two-pass Top-K (0: by k)
-    int kpw;         // rebuilt keys per wave of the fused attention kernel (64, 48 or 32)
+    int kpw;         // rebuilt keys per wave of the fused attention kernel (64, 48, 32 or 16)
+    int attn_nw;     // waves per fused attention workgroup (4, or 8 where built)
 };
 
 // Low-rank key factors of `batch` sequences (A, B <- SVD(K_pre) through the
@@ -127,6 +128,8 @@ hipError_t launch_pv(const Dims &dm, const float *logits, const void *v_out, con
 // attn_workgroups(dm) workgroups per row, one split partial each; then
 // launch_combine with splits = attn_workgroups(dm).
 int attn_workgroups(const Dims &dm);
+// Waves per fused attention workgroup for dm (8 only where that variant is built).
+int attn_waves(const Dims &dm);
 hipError_t launch_attn(const Dims &dm, const void *q, const void *A, const void *Bt, const int32_t *chunks,
                        const int32_t *sel_slot, const double *theta_rev, const void *k_out, const void *v_out,
                        const void *k_loc, const void *v_loc, const void *vc, float2 *part_ml, float *part_acc,

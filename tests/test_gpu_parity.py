@@ -143,15 +143,18 @@ def test_end_to_end_matches_oracle(case):
     _end_to_end(case, CASES[case])
 
 
-# The fused kernel's rebuilt keys per wave (64 by default; 48, 32 or 16 when
-# forced) on discriminating cases; 48 keys start waves mid-chunk at chunk 16,
-# and the fourth block of a wave is then empty.
-@pytest.mark.parametrize("case,kpw", [("bf16-llama-32k-sharp", 48), ("bf16-llama-32k-sharp", 32),
-                                      ("bf16-llama-32k-sharp", 16), ("bf16-g16-sharp", 64),
-                                      ("bf16-g16-sharp", 32), ("bf16-chunk16", 48), ("bf16-rank96-chunk4", 48)])
-def test_keys_per_wave_matches_oracle(case, kpw, monkeypatch):
+# The fused kernel's shapes on discriminating cases: rebuilt keys per wave
+# (64 by default; 48, 32 or 16 when forced; 48 keys start waves mid-chunk at
+# chunk 16 and leave a wave's fourth block empty) and waves per workgroup (8
+# where the launch fits the CUs at once at rank 129..160, else 4).
+@pytest.mark.parametrize("case,kpw,waves", [("bf16-llama-32k-sharp", 48, 8), ("bf16-llama-32k-sharp", 32, 8),
+                                            ("bf16-llama-32k-sharp", 16, 8), ("bf16-llama-32k-sharp", 64, 4),
+                                            ("bf16-g16-sharp", 64, 4), ("bf16-g16-sharp", 32, 8),
+                                            ("bf16-chunk16", 48, 8), ("bf16-rank96-chunk4", 48, 4)])
+def test_attention_shapes_match_oracle(case, kpw, waves, monkeypatch):
     monkeypatch.setenv("SKV_ATTN_KPW", str(kpw))
-    _end_to_end(f"{case}-kpw{kpw}", CASES[case])
+    monkeypatch.setenv("SKV_ATTN_WAVES", str(waves))
+    _end_to_end(f"{case}-kpw{kpw}-w{waves}", CASES[case])
 
 
 def _end_to_end(case, wl):
