@@ -427,6 +427,18 @@ def main() -> int:
             src.fill_(1)
             peaks["hbm_read_TBps"] = round(skv.shadowkv_probe_hbm_read(src.data_ptr(), nb, 5, stream.cuda_stream)
                                            / 1e3, 3)
+            # the host-issued alternative to the device-initiated fetch: about a
+            # step's misses (half the selection) as 2 KB chunks scattered over
+            # the pinned buffer, one hipMemcpyAsync each, then one batch
+            chunk_b = wl.c * wl.d * (2 if wl.bf16 else 4)
+            n_cp = max(1, wl.k * wl.b * wl.h_kv // 2)
+            rng = np.random.default_rng(0)
+            picks = rng.choice(hsrc.numel() // chunk_b, size=min(n_cp, hsrc.numel() // chunk_b), replace=False)
+            each, batch = skv.shadowkv_probe_host_copies(hsrc.data_ptr(), hsrc.numel(), dst.data_ptr(), chunk_b,
+                                                         [int(x) for x in picks], 2, stream.cuda_stream)
+            peaks["host_copies_per_chunk_GBps"] = round(each, 2)
+            peaks["host_copies_batch_GBps"] = round(batch, 2)
+            peaks["host_copies_chunks"] = int(len(picks))
             del src, dst, hsrc
         except RuntimeError as e:  # not enough memory for the probes: leave them out
             log(f"device peaks skipped: {e}")

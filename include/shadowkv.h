@@ -345,6 +345,22 @@ double shadowkv_equiv_bandwidth(double S, double C, double K, double O, double a
  * pointer, reps < 1 or too few bytes; SKV_E_HIP if a launch or event fails. */
 int shadowkv_probe_hbm_read(const void *buf, size_t bytes, int reps, void *stream, double *gbps_out);
 
+/* Measurement aid, not part of the method: the host-issued alternative to the
+ * device-initiated V fetch (the review page, section 三, Algorithm 2 step 3;
+ * the pages overlap host-driven copies with the key rebuild).  Copies
+ * n_chunks chunks of chunk_bytes from the pinned host buffer `host`
+ * (host_bytes long; chunk i starts at host_chunk[i] * chunk_bytes, a host
+ * array) to consecutive chunks of the device buffer `dev`, first with one
+ * hipMemcpyAsync per chunk, then with one hipMemcpyBatchAsync, `reps` times
+ * each on `stream`, and returns the best rate (1e9 B/s) of each (the batch
+ * rate is 0 when the HIP runtime in the process lacks the call).  The caller
+ * owns all buffers; `dev` must hold n_chunks * chunk_bytes.  Waits for the
+ * stream.  SKV_E_INVAL for a null pointer, a chunk outside the host buffer,
+ * reps or n_chunks < 1; SKV_E_HIP if a copy or event fails. */
+int shadowkv_probe_host_copies(const void *host, size_t host_bytes, void *dev, size_t chunk_bytes, int n_chunks,
+                               const int64_t *host_chunk, int reps, void *stream, double *gbps_each,
+                               double *gbps_batch);
+
 #ifdef __cplusplus
 }
 #endif

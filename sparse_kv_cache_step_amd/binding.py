@@ -31,7 +31,7 @@ EXPORTS = (
     "shadowkv_tensor_bytes", "shadowkv_read", "shadowkv_set_overlap", "shadowkv_set_timing",
     "shadowkv_get_timing",
     "shadowkv_host_alloc", "shadowkv_host_free", "shadowkv_last_error", "shadowkv_equiv_bandwidth",
-    "shadowkv_probe_hbm_read", "shadowkv_factorize",
+    "shadowkv_probe_hbm_read", "shadowkv_factorize", "shadowkv_probe_host_copies",
 )
 
 
@@ -91,6 +91,9 @@ def lib() -> ctypes.CDLL:
                                                        ctypes.POINTER(ctypes.c_double)]),
             "shadowkv_factorize": (ctypes.c_int, [ctypes.c_int] * 6 + [_VP, _VP, _VP, _VP,
                                                                         ctypes.POINTER(ctypes.c_int)]),
+            "shadowkv_probe_host_copies": (ctypes.c_int, [_VP, ctypes.c_size_t, _VP, ctypes.c_size_t, ctypes.c_int,
+                                                          _VP, ctypes.c_int, _VP, ctypes.POINTER(ctypes.c_double),
+                                                          ctypes.POINTER(ctypes.c_double)]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -121,6 +124,20 @@ def shadowkv_probe_hbm_read(buf, nbytes: int, reps: int, stream) -> float:
     if rc != SKV_OK:
         raise ShadowKVError(rc, "read probe failed")
     return out.value
+
+
+def shadowkv_probe_host_copies(host, host_bytes: int, dev, chunk_bytes: int, host_chunks, reps: int,
+                               stream) -> tuple[float, float]:
+    """Host-issued chunk copies (GB/s): one hipMemcpyAsync per chunk, and one
+    hipMemcpyBatchAsync; host_chunks is a sequence of chunk indices."""
+    n = len(host_chunks)
+    arr = (ctypes.c_int64 * n)(*host_chunks)
+    each, batch = ctypes.c_double(), ctypes.c_double()
+    rc = lib().shadowkv_probe_host_copies(host, host_bytes, dev, chunk_bytes, n, arr, reps, stream,
+                                          ctypes.byref(each), ctypes.byref(batch))
+    if rc != SKV_OK:
+        raise ShadowKVError(rc, "host-copy probe failed")
+    return each.value, batch.value
 
 
 def shadowkv_layer_create(cfg: skv_config) -> int:
