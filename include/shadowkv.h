@@ -316,7 +316,8 @@ int shadowkv_get_timing(skv_layer *layer, double *ms_out, int64_t *steps_out);
  * eigenvalues at the end, and returns when the factors are written.
  * SKV_E_INVAL for a null pointer or a bad dtype; SKV_E_SHAPE unless
  * batch, heads_kv, seq_len >= 1, head_dim in {64, 128}, rank in [1, 256],
- * heads_kv * head_dim <= 4096; SKV_E_HIP if an allocation, launch or copy
+ * heads_kv * head_dim <= 2048 (the eigensolver's cost grows as n^3: a sweep is
+ * n - 1 rounds over two n x n matrices); SKV_E_HIP if an allocation, launch or copy
  * fails.  `sweeps_out` (may be NULL) receives the sweeps the slowest batch
  * took.
  */

@@ -337,7 +337,7 @@ int shadowkv_factorize(int dtype, int batch, int heads_kv, int seq_len, int head
     if (batch < 1 || heads_kv < 1 || seq_len < 1) return fail(SKV_E_SHAPE, "batch, heads_kv and seq_len must be >= 1");
     if (head_dim != 64 && head_dim != 128) return fail(SKV_E_SHAPE, "head_dim must be 64 or 128");
     if (rank < 1 || rank > 256) return fail(SKV_E_SHAPE, "rank must be in [1, 256]");
-    if (heads_kv * head_dim > 4096) return fail(SKV_E_SHAPE, "heads_kv * head_dim must be <= 4096");
+    if (heads_kv * head_dim > 2048) return fail(SKV_E_SHAPE, "heads_kv * head_dim must be <= 2048");
     std::string why;
     const int rc = skv::factorize_device(dtype == SKV_BF16, batch, heads_kv, seq_len, head_dim, rank, k_pre, A, B,
                                          static_cast<hipStream_t>(stream), &why, sweeps_out);

@@ -103,7 +103,7 @@ def test_null_arguments(lib):
     ((skv.SKV_BF16, 1, 8, 1024, 96, 160, 1, 1, 1), skv.SKV_E_SHAPE),        # head_dim
     ((skv.SKV_BF16, 1, 8, 1024, 128, 0, 1, 1, 1), skv.SKV_E_SHAPE),         # rank
     ((skv.SKV_BF16, 1, 8, 1024, 128, 257, 1, 1, 1), skv.SKV_E_SHAPE),       # rank
-    ((skv.SKV_BF16, 1, 64, 1024, 128, 160, 1, 1, 1), skv.SKV_E_SHAPE),      # n = 8192 > 4096
+    ((skv.SKV_BF16, 1, 32, 1024, 128, 160, 1, 1, 1), skv.SKV_E_SHAPE),      # n = 4096 > 2048
 ])
 def test_factorize_rejects_bad_arguments_before_the_device(lib, args, code):
     # the pointer arguments are never dereferenced on these paths
