@@ -97,7 +97,8 @@ typedef struct skv_layer skv_layer;
 
 /* Counters accumulated by the decode steps since creation or the last
  * shadowkv_reset_stats.  hits/misses count chunks per (sequence, KV head);
- * bytes_h2d is the V payload read from pinned host memory. */
+ * bytes_h2d is what the V fetch read from pinned host memory (raw chunks at
+ * 2 bytes a value, coded ones at 12 bits a value plus their escapes). */
 typedef struct {
     int64_t steps;
     int64_t hits;
@@ -125,14 +126,27 @@ void shadowkv_layer_destroy(skv_layer *layer);
  *   A           device (b, s, r)        left factor, shared by the KV heads.
  *   B           device (b, h_kv, r, d)  right factor per KV head;
  *               A[b] . B[b,h] approximates head h's pre-RoPE keys.
- *   v_host      pinned host (b, h_kv, s, d): receives V (the offload of
- *               step 5); must stay allocated while the layer is used.
+ *   v_host      pinned host (b, h_kv, s, d) bytes of dtype: receives V (the
+ *               offload of step 5), each chunk in its own c*d-value slot; must
+ *               stay allocated while the layer is used.  For bfloat16 layers
+ *               with c*d in {512, 1024, 2048} a chunk is written in a
+ *               lossless 12-bit form, because the decode step's V fetch is
+ *               bound by PCIe: N = c*d bytes of sign and mantissa, N/2 bytes
+ *               of 4-bit exponent offsets from the chunk's base (offset 15:
+ *               escape), then 4 bytes per escape, (value index << 8) |
+ *               exponent, for the values whose exponent lies below the base;
+ *               the base is the chunk's largest exponent minus 14 (at least
+ *               0), and chunks with more than 64 escapes stay raw.  Lane l of
+ *               64 owns values l*N/64 ..: its bytes at l*N/64, its offsets
+ *               (value q at bits 4*(q % 8) of 32-bit word q/8) at
+ *               N + l*N/128.  SKV_T_V_CODES gives each chunk's form; the fetch
+ *               restores V bit for bit.
  * Computes the chunk means of the post-RoPE keys (landmarks), each chunk's
  * minimum cosine to its landmark, the n_outlier chunks with the lowest
  * minimum (ties: lower index; chunks of the local window excluded), gathers
  * the full-rank post-RoPE K and V of outlier chunks and of the last
- * local_window tokens, marks the remaining chunks selectable, copies V to
- * v_host and empties the resident V cache.
+ * local_window tokens, marks the remaining chunks selectable, writes V to
+ * v_host (raw or coded, above) and empties the resident V cache.
  */
 int shadowkv_prefill_meta(skv_layer *layer, const void *k_pre, const void *k_rope,
                           const void *v, const void *A, const void *B,
@@ -260,7 +274,11 @@ enum {
     SKV_T_V_LOC = 12,
     SKV_T_SELECTION_SLOTS = 13, /* int32 (b, h_kv, k): slot holding the i-th
                                    selected chunk                             */
-    SKV_T_COUNT = 14
+    SKV_T_V_CODES = 14,     /* uint32 (b, h_kv, n): each host V chunk's code
+                               word: 0 raw, else bit 31 set, the escape count
+                               in bits 16..23 and the exponent base in bits
+                               0..7 of the 12-bit form (shadowkv_prefill_meta) */
+    SKV_T_COUNT = 15
 };
 size_t shadowkv_tensor_bytes(const skv_layer *layer, int which);
 int shadowkv_read(skv_layer *layer, int which, void *dst, size_t bytes, void *stream);

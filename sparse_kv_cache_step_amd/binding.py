@@ -20,7 +20,7 @@ SKV_F32, SKV_BF16 = 0, 1
 SKV_OK, SKV_E_INVAL, SKV_E_SHAPE, SKV_E_STATE, SKV_E_NOMEM, SKV_E_HIP = 0, -1, -2, -3, -4, -5
 (SKV_T_LANDMARKS, SKV_T_MIN_COS, SKV_T_OUTLIERS, SKV_T_CAND_MASK, SKV_T_SCORES, SKV_T_GROUP_SCORES,
  SKV_T_SELECTION, SKV_T_SLOT_CHUNKS, SKV_T_CACHE_V, SKV_T_K_OUT, SKV_T_V_OUT, SKV_T_K_LOC,
- SKV_T_V_LOC, SKV_T_SELECTION_SLOTS) = range(14)
+ SKV_T_V_LOC, SKV_T_SELECTION_SLOTS, SKV_T_V_CODES) = range(15)
 KERNELS = ("score", "select", "fetch", "qk", "pv", "attn")
 SKV_K_COUNT = len(KERNELS)
 
@@ -403,6 +403,7 @@ class Layer:
             SKV_T_V_OUT: (dt, (b, hkv, c.n_outlier * ch, d)), SKV_T_K_LOC: (dt, (b, hkv, c.local_window + c.max_new, d)),
             SKV_T_V_LOC: (dt, (b, hkv, c.local_window + c.max_new, d)),
             SKV_T_SELECTION_SLOTS: (torch.int32, (b, hkv, k)),
+            SKV_T_V_CODES: (torch.int32, (b, hkv, self.n)),
         }[which]
         t = torch.empty(spec[1], dtype=spec[0], device=self.device)
         nbytes = t.numel() * t.element_size()

@@ -27,8 +27,10 @@ namespace skv {
 template <int VPL>  // 16-byte vectors per lane and chunk (0: any, looped)
 __global__ __launch_bounds__(256) void fetch_kernel(const u32x4 *__restrict__ v_host, u32x4 *__restrict__ vc,
                                                     const int2 *__restrict__ misses,
-                                                    const int32_t *__restrict__ miss_count, int rows, int k, int cap,
-                                                    int n, int chunk_vec) {
+                                                    const int32_t *__restrict__ miss_count,
+                                                    const uint32_t *__restrict__ vcode,
+                                                    unsigned long long *__restrict__ counters, int rows, int k,
+                                                    int cap, int n, int chunk_vec) {
     extern __shared__ int pre[];  // rows + 1 prefix sums
     __shared__ int wsum[4];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -64,22 +66,83 @@ __global__ __launch_bounds__(256) void fetch_kernel(const u32x4 *__restrict__ v_
         row = lo;
         return misses[static_cast<size_t>(lo) * k + (g - pre[lo])];
     };
+    unsigned long long wire = 0;  // bytes this wave read over PCIe
     int g = gw, row = 0;
     int2 e = g < total ? locate(g, row) : make_int2(0, 0);
+    uint32_t code = g < total && vcode ? vcode[static_cast<size_t>(row) * n + e.x] : 0u;
     for (; g < total; g += nw) {
         const u32x4 *src = v_host + (static_cast<size_t>(row) * n + e.x) * chunk_vec;
         u32x4 *dst = vc + (static_cast<size_t>(row) * cap + e.y) * chunk_vec;
         if constexpr (VPL > 0) {
-            u32x4 t[VPL];
+            constexpr int Q = 8 * VPL;  // values per lane
+            const int N = 64 * Q;
+            if (code & 0x80000000u) {  // wave-uniform: the 12-bit form (see prefill.hip)
+                const int base = static_cast<int>(code & 0xffu), nesc = static_cast<int>((code >> 16) & 0xffu);
+                const uint8_t *sb = reinterpret_cast<const uint8_t *>(src);
+                uint32_t bw[Q / 4], nwd[Q / 8];
+                if constexpr (Q == 8) {
+                    const u32x2 b2 = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(sb) + lane);
+                    bw[0] = b2[0]; bw[1] = b2[1];
+                    nwd[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(sb + N) + lane);
+                } else if constexpr (Q == 16) {
+                    const u32x4 b4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(sb) + lane);
+                    bw[0] = b4[0]; bw[1] = b4[1]; bw[2] = b4[2]; bw[3] = b4[3];
+                    const u32x2 n2 = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(sb + N) + lane);
+                    nwd[0] = n2[0]; nwd[1] = n2[1];
+                } else {
+                    const u32x4 b4a = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(sb) + 2 * lane);
+                    const u32x4 b4b = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(sb) + 2 * lane + 1);
+                    bw[0] = b4a[0]; bw[1] = b4a[1]; bw[2] = b4a[2]; bw[3] = b4a[3];
+                    bw[4] = b4b[0]; bw[5] = b4b[1]; bw[6] = b4b[2]; bw[7] = b4b[3];
+                    const u32x4 n4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(sb + N) + lane);
+                    nwd[0] = n4[0]; nwd[1] = n4[1]; nwd[2] = n4[2]; nwd[3] = n4[3];
+                }
+                const uint32_t esc = lane < nesc
+                    ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(sb + 3 * N / 2) + lane) : 0u;
+                // the next miss is located while this chunk's host reads are in flight
+                int row_n = row;
+                const int2 e_n = g + nw < total ? locate(g + nw, row_n) : e;
+                const uint32_t code_n = g + nw < total && vcode ? vcode[static_cast<size_t>(row_n) * n + e_n.x] : 0u;
+                uint32_t x[Q];
 #pragma unroll
-            for (int u = 0; u < VPL; ++u) t[u] = __builtin_nontemporal_load(src + u * 64 + lane);
-            // the next miss is located while this chunk's host reads are in flight
-            int row_n = row;
-            const int2 e_n = g + nw < total ? locate(g + nw, row_n) : e;
+                for (int q = 0; q < Q; ++q) {
+                    const uint32_t byte = (bw[q >> 2] >> (8 * (q & 3))) & 0xffu;
+                    const uint32_t ex = static_cast<uint32_t>(base) + ((nwd[q >> 3] >> (4 * (q & 7))) & 0xfu);
+                    x[q] = ((byte & 0x80u) << 8) | ((ex & 0xffu) << 7) | (byte & 0x7fu);
+                }
+                // escapes: the exponent itself, for the lane owning the value
+                for (int j = 0; j < nesc; ++j) {
+                    const uint32_t ej = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(esc), j));
+                    const int idx = static_cast<int>(ej >> 8);
+                    if (idx / Q == lane) {
 #pragma unroll
-            for (int u = 0; u < VPL; ++u) dst[u * 64 + lane] = t[u];
-            row = row_n;
-            e = e_n;
+                        for (int q = 0; q < Q; ++q)
+                            if (q == idx % Q) x[q] = (x[q] & 0x807fu) | ((ej & 0xffu) << 7);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < VPL; ++u)
+                    dst[lane * VPL + u] = u32x4{x[8 * u] | (x[8 * u + 1] << 16), x[8 * u + 2] | (x[8 * u + 3] << 16),
+                                                x[8 * u + 4] | (x[8 * u + 5] << 16), x[8 * u + 6] | (x[8 * u + 7] << 16)};
+                wire += static_cast<unsigned long long>(3 * N / 2 + 4 * nesc);
+                row = row_n;
+                e = e_n;
+                code = code_n;
+            } else {
+                u32x4 t[VPL];
+#pragma unroll
+                for (int u = 0; u < VPL; ++u) t[u] = __builtin_nontemporal_load(src + u * 64 + lane);
+                // the next miss is located while this chunk's host reads are in flight
+                int row_n = row;
+                const int2 e_n = g + nw < total ? locate(g + nw, row_n) : e;
+                const uint32_t code_n = g + nw < total && vcode ? vcode[static_cast<size_t>(row_n) * n + e_n.x] : 0u;
+#pragma unroll
+                for (int u = 0; u < VPL; ++u) dst[u * 64 + lane] = t[u];
+                wire += static_cast<unsigned long long>(chunk_vec) * 16;
+                row = row_n;
+                e = e_n;
+                code = code_n;
+            }
         } else {
             for (int i0 = 0; i0 < chunk_vec; i0 += 256) {
                 u32x4 t[4];
@@ -94,9 +157,11 @@ __global__ __launch_bounds__(256) void fetch_kernel(const u32x4 *__restrict__ v_
                     if (i < chunk_vec) dst[i] = t[u];
                 }
             }
+            wire += static_cast<unsigned long long>(chunk_vec) * 16;
             if (g + nw < total) e = locate(g + nw, row);
         }
     }
+    if (counters && lane == 0 && wire) atomicAdd(&counters[3], wire);
 }
 
 // ---------------------------------------------------------------------------
@@ -1056,7 +1121,7 @@ __global__ __launch_bounds__(D) void combine_kernel(const float2 *__restrict__ p
 // Launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_fetch(const Dims &dm, const void *v_host, void *vc, const int2 *misses, const int32_t *miss_count,
-                        int waves, hipStream_t st) {
+                        const uint32_t *vcode, unsigned long long *counters, int waves, hipStream_t st) {
     if (dm.k <= 0) return hipSuccess;
     const int rows = dm.b * dm.hkv;
     const int chunk_vec = dm.c * dm.d * dm.esize / 16;
@@ -1068,8 +1133,8 @@ hipError_t launch_fetch(const Dims &dm, const void *v_host, void *vc, const int2
             if (e != hipSuccess) return e;
         }
         hipLaunchKernelGGL(kern, dim3(std::max(1, (waves + 3) / 4)), dim3(256), lds, st,
-                           static_cast<const u32x4 *>(v_host), static_cast<u32x4 *>(vc), misses, miss_count, rows,
-                           dm.k, dm.cap, dm.n, chunk_vec);
+                           static_cast<const u32x4 *>(v_host), static_cast<u32x4 *>(vc), misses, miss_count, vcode,
+                           counters, rows, dm.k, dm.cap, dm.n, chunk_vec);
         return hipGetLastError();
     };
     switch (chunk_vec) {

@@ -1,7 +1,10 @@
 // Prefill-side kernels of the ShadowKV step (review page, section 三,
 // Algorithm 1 steps 2-5): RoPE of the pre-RoPE keys, chunk means
 // (landmarks), each chunk's minimum token-to-landmark cosine, the static
-// outlier / local-window buffers and the selectable-chunk bitmask.
+// outlier / local-window buffers and the selectable-chunk bitmask; and the
+// 12-bit form in which host V crosses PCIe.
+#include <algorithm>
+
 #include "skv_device.h"
 
 namespace skv {
@@ -296,6 +299,122 @@ hipError_t launch_append(const Dims &dm, const void *k_new, const void *v_new, c
                            : append_t<uint16_t, 64>(dm, k_new, v_new, theta, k_loc, v_loc, row, pos, st);
     return dm.d == 128 ? append_t<float, 128>(dm, k_new, v_new, theta, k_loc, v_loc, row, pos, st)
                        : append_t<float, 64>(dm, k_new, v_new, theta, k_loc, v_loc, row, pos, st);
+}
+
+
+// ---------------------------------------------------------------------------
+// Host V in a lossless 12-bit form (bfloat16 chunks of N = 512, 1024 or 2048
+// values).  The V fetch is bound by PCIe, so each chunk crosses it as
+//   N bytes      sign and mantissa of every value (bits 15 and 6..0),
+//   N / 2 bytes  its exponent as a 4-bit offset from the chunk's base,
+//                base = max(0, largest exponent - 14); offset 15 marks an
+//                escape,
+//   4 B each     the escapes: (value index << 8) | exponent, for values whose
+//                exponent lies below the base (zeros, tiny values), in index
+//                order,
+// in the chunk's own slot of the host buffer; a chunk with more than 64
+// escapes (or NaN / Inf, whose exponent 255 moves the base) stays raw.  Lane
+// l of a chunk's wave owns values l*Q .. l*Q+Q-1 (Q = N / 64): its Q bytes at
+// l*Q, its Q nibbles (value q in bits 4*(q % 8) of word q / 8) at N + l*Q/2.
+// The chunk's code word (device memory) says which: bit 31 set = coded, with
+// the escape count in bits 16..23 and the base in bits 0..7; 0 = raw.
+// ---------------------------------------------------------------------------
+template <int Q>
+__global__ __launch_bounds__(256) void vcode_kernel(const uint16_t *__restrict__ v, uint8_t *__restrict__ out,
+                                                    uint32_t *__restrict__ code, long long nchunks) {
+    constexpr int N = 64 * Q;
+    const int lane = threadIdx.x & 63;
+    const long long nw = static_cast<long long>(gridDim.x) * 4;
+    for (long long ch = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6); ch < nchunks; ch += nw) {
+        // this lane's Q values (2Q bytes: Q / 8 16-byte loads)
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(v + ch * N) + lane * (Q / 8);
+        uint32_t w[Q / 2];
+#pragma unroll
+        for (int u = 0; u < Q / 8; ++u) {
+            const u32x4 t = src[u];
+            w[4 * u] = t[0]; w[4 * u + 1] = t[1]; w[4 * u + 2] = t[2]; w[4 * u + 3] = t[3];
+        }
+        int emax = 0;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) emax = max(emax, static_cast<int>((w[q >> 1] >> (16 * (q & 1) + 7)) & 0xffu));
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) emax = max(emax, __shfl_xor(emax, off, 64));
+        const int base = max(0, emax - 14);
+        int nesc_lane = 0;
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+            nesc_lane += static_cast<int>((w[q >> 1] >> (16 * (q & 1) + 7)) & 0xffu) < base ? 1 : 0;
+        int incl = nesc_lane;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int t = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += t;
+        }
+        const int nesc = __shfl(incl, 63, 64);
+        uint8_t *dst = out + ch * 2 * N;
+        if (nesc > 64) {  // stays raw
+            u32x4 *d4 = reinterpret_cast<u32x4 *>(dst) + lane * (Q / 8);
+#pragma unroll
+            for (int u = 0; u < Q / 8; ++u) d4[u] = u32x4{w[4 * u], w[4 * u + 1], w[4 * u + 2], w[4 * u + 3]};
+            if (lane == 0) code[ch] = 0u;
+            continue;
+        }
+        uint32_t bw[Q / 4], nw4[Q / 8];
+#pragma unroll
+        for (int i = 0; i < Q / 4; ++i) bw[i] = 0u;
+#pragma unroll
+        for (int i = 0; i < Q / 8; ++i) nw4[i] = 0u;
+        int slot = incl - nesc_lane;  // this lane's first escape entry
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            const uint32_t x = (w[q >> 1] >> (16 * (q & 1))) & 0xffffu;
+            const int e = static_cast<int>((x >> 7) & 0xffu);
+            const uint32_t byte = ((x >> 8) & 0x80u) | (x & 0x7fu);
+            const bool esc = e < base;
+            bw[q >> 2] |= byte << (8 * (q & 3));
+            nw4[q >> 3] |= static_cast<uint32_t>(esc ? 15 : e - base) << (4 * (q & 7));
+            if (esc) {
+                reinterpret_cast<uint32_t *>(dst + 3 * N / 2)[slot] =
+                    (static_cast<uint32_t>(lane * Q + q) << 8) | static_cast<uint32_t>(e);
+                ++slot;
+            }
+        }
+        uint32_t *bp = reinterpret_cast<uint32_t *>(dst) + lane * (Q / 4);
+#pragma unroll
+        for (int i = 0; i < Q / 4; ++i) bp[i] = bw[i];
+        uint32_t *np = reinterpret_cast<uint32_t *>(dst + N) + lane * (Q / 8);
+#pragma unroll
+        for (int i = 0; i < Q / 8; ++i) np[i] = nw4[i];
+        if (lane == 0) code[ch] = 0x80000000u | (static_cast<uint32_t>(nesc) << 16) | static_cast<uint32_t>(base);
+    }
+}
+
+int vcode_values(const Dims &dm) {
+    const int N = dm.c * dm.d;
+    return dm.bf16 && (N == 512 || N == 1024 || N == 2048) ? N : 0;
+}
+
+hipError_t launch_vcode(const Dims &dm, const void *v, void *out, uint32_t *code, long long nchunks,
+                        hipStream_t st) {
+    if (nchunks <= 0) return hipSuccess;
+    const int blocks = static_cast<int>(std::min<long long>((nchunks + 3) / 4, 8192));
+    switch (vcode_values(dm)) {
+        case 512:
+            hipLaunchKernelGGL(vcode_kernel<8>, dim3(blocks), dim3(256), 0, st, static_cast<const uint16_t *>(v),
+                               static_cast<uint8_t *>(out), code, nchunks);
+            break;
+        case 1024:
+            hipLaunchKernelGGL(vcode_kernel<16>, dim3(blocks), dim3(256), 0, st, static_cast<const uint16_t *>(v),
+                               static_cast<uint8_t *>(out), code, nchunks);
+            break;
+        case 2048:
+            hipLaunchKernelGGL(vcode_kernel<32>, dim3(blocks), dim3(256), 0, st, static_cast<const uint16_t *>(v),
+                               static_cast<uint8_t *>(out), code, nchunks);
+            break;
+        default:
+            return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace skv

@@ -116,7 +116,12 @@ struct DevStreams {
     bool ready = false;
     hipStream_t fetch = nullptr, comp = nullptr;
     int fetch_cus = 0;
+    // staging of host V's coded form on its way to the host (the prefill's
+    // offload on the fetch stream; allocated by the first prefill that codes,
+    // kept until the process ends)
+    void *stage = nullptr;
 };
+constexpr size_t kStageBytes = size_t(64) << 20;
 std::mutex g_dev_mutex;
 DevStreams g_dev[64];
 
@@ -164,6 +169,19 @@ int device_streams(int device, DevStreams **out) {
     return SKV_OK;
 }
 
+// The device's staging buffer for host V's coded form (allocated once).
+int device_stage(int device, void **out) {
+    std::lock_guard<std::mutex> lock(g_dev_mutex);
+    if (device < 0 || device >= 64) return fail(SKV_E_INVAL, "device index out of range");
+    DevStreams &ds = g_dev[device];
+    if (!ds.stage && hipMalloc(&ds.stage, kStageBytes) != hipSuccess) {
+        ds.stage = nullptr;
+        return fail(SKV_E_NOMEM, "staging buffer for host V (64 MiB) could not be allocated");
+    }
+    *out = ds.stage;
+    return SKV_OK;
+}
+
 }  // namespace
 
 struct skv_layer {
@@ -192,7 +210,7 @@ struct skv_layer {
     float2 *stats = nullptr, *part_ml = nullptr;
     int2 *misses = nullptr;
     int32_t *miss_count = nullptr;
-    unsigned long long *counters = nullptr;  // hits, misses, steps
+    unsigned long long *counters = nullptr;  // hits, misses, steps, bytes read from host V
     uint32_t *keys = nullptr;    // selection keys (b, h_kv, n)
     uint2 *kbounds = nullptr;    // (min, max) selectable key per row and group slice
     int select_keys_in_lds = 1, topo_keys_in_lds = 1;
@@ -205,6 +223,10 @@ struct skv_layer {
     int32_t *bad = nullptr;
     // host V
     void *v_host_dev = nullptr;
+    // (b, h_kv, n): each host V chunk's code word (0: raw; else the 12-bit
+    // form the prefill wrote, see prefill.hip); vcoded: the prefill codes
+    uint32_t *vcode = nullptr;
+    bool vcoded = false;
     bool ready = false;
     // shared per-device streams for the host-V fetch and the key rebuild
     hipStream_t copy = nullptr, comp = nullptr;
@@ -430,6 +452,10 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     // or 1 forces the separate QK + PV kernels or the fused one
     ly->fused = dm.bf16 != 0;
     if (const char *e = std::getenv("SKV_ATTN_FUSED")) ly->fused = dm.bf16 != 0 && std::atoi(e) != 0;
+    // host V crosses PCIe in its 12-bit form where the chunks allow it;
+    // SKV_HOST_V_CODE=0 keeps it raw
+    ly->vcoded = skv::vcode_values(dm) > 0;
+    if (const char *e = std::getenv("SKV_HOST_V_CODE")) ly->vcoded = ly->vcoded && std::atoi(e) != 0;
 
     const size_t B = dm.b, HKV = dm.hkv, HQ = dm.hq, D = dm.d, S = dm.s, E = dm.esize;
     const size_t bh = B * HKV;
@@ -467,6 +493,7 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     ALLOC(part_ml, B * HQ * splits * sizeof(float2));
     ALLOC(part_acc, B * HQ * splits * D * 4);
     ALLOC(counters, 4 * sizeof(unsigned long long));
+    ALLOC(vcode, bh * dm.n * 4);
     ALLOC(bad, 4);
     ALLOC(theta, D / 2 * sizeof(double));
     ALLOC(theta_rev, D / 2 * sizeof(double));
@@ -561,8 +588,25 @@ int shadowkv_prefill_meta(skv_layer *ly, const void *k_pre, const void *k_rope, 
     // which need only HBM; the caller's stream waits for it at the end.
     SKV_HIP(hipEventRecord(ly->ev_sel, st));
     SKV_HIP(hipStreamWaitEvent(ly->copy, ly->ev_sel, 0));
-    SKV_HIP(hipMemcpyAsync(v_host, v, static_cast<size_t>(dm.b) * dm.hkv * dm.s * dm.d * dm.esize,
-                           hipMemcpyDeviceToHost, ly->copy));
+    const long long nchunks = static_cast<long long>(dm.b) * dm.hkv * dm.n;
+    if (ly->vcoded) {
+        // chunk by chunk into the 12-bit form, through the device's staging
+        // buffer, 64 MiB at a time (the chunks of V are contiguous)
+        void *stage = nullptr;
+        if ((rc = device_stage(ly->device, &stage))) return rc;
+        const long long cb = 2LL * skv::vcode_values(dm), per = static_cast<long long>(kStageBytes) / cb;
+        for (long long c0 = 0; c0 < nchunks; c0 += per) {
+            const long long cnt = std::min(per, nchunks - c0);
+            SKV_HIP(skv::launch_vcode(dm, static_cast<const char *>(v) + c0 * cb, stage, ly->vcode + c0, cnt,
+                                      ly->copy));
+            SKV_HIP(hipMemcpyAsync(static_cast<char *>(v_host) + c0 * cb, stage, static_cast<size_t>(cnt * cb),
+                                   hipMemcpyDeviceToHost, ly->copy));
+        }
+    } else {
+        SKV_HIP(hipMemcpyAsync(v_host, v, static_cast<size_t>(dm.b) * dm.hkv * dm.s * dm.d * dm.esize,
+                               hipMemcpyDeviceToHost, ly->copy));
+        SKV_HIP(skv::launch_fill_i32(reinterpret_cast<int32_t *>(ly->vcode), 0, static_cast<size_t>(nchunks), ly->copy));
+    }
     SKV_HIP(hipEventRecord(ly->ev_fetch, ly->copy));
     SKV_HIP(skv::launch_landmarks(dm, k_pre, k_rope, ly->theta, ly->L, ly->min_cos, st));
     SKV_HIP(skv::launch_topo(dm, ly->min_cos, ly->outliers, ly->keys, ly->topo_keys_in_lds, st));
@@ -607,6 +651,8 @@ int shadowkv_load_meta(skv_layer *ly, const void *landmarks, const int32_t *outl
         SKV_HIP(hipMemcpy2DAsync(ly->k_loc, pitch, k_loc, row, row, bh, hipMemcpyDefault, st));
         SKV_HIP(hipMemcpy2DAsync(ly->v_loc, pitch, v_loc, row, row, bh, hipMemcpyDefault, st));
     }
+    // the caller's host V is raw
+    SKV_HIP(skv::launch_fill_i32(reinterpret_cast<int32_t *>(ly->vcode), 0, bh * dm.n, st));
     if ((rc = install_common(ly, A, B, v_host, st))) return rc;
     ly->v_host_dev = vdev;
     ly->n_app = 0;
@@ -643,7 +689,7 @@ int shadowkv_snapkv_select(skv_layer *ly, const void *q_obs, int w_obs, int pool
     // count as hits of this selection.  Fetch them first, which keeps the
     // cache lossless.
     if (ly->fetch_pending) {
-        SKV_HIP(skv::launch_fetch(dm, ly->v_host_dev, ly->vc, ly->misses, ly->miss_count, ly->fetch_waves, st));
+        SKV_HIP(skv::launch_fetch(dm, ly->v_host_dev, ly->vc, ly->misses, ly->miss_count, ly->vcode, ly->counters, ly->fetch_waves, st));
         ly->fetch_pending = false;
     }
     // passes of up to kMaxGroup (head, window position) rows per KV head
@@ -711,7 +757,7 @@ static int decode_impl(skv_layer *ly, const void *q, void *out, hipStream_t st, 
         SKV_HIP(hipStreamWaitEvent(ly->comp, ly->ev_sel, 0));
         if (fetch) {
             Timed t(ly, SKV_K_FETCH, ly->copy, timed);
-            SKV_HIP(skv::launch_fetch(dm, ly->v_host_dev, ly->vc, ly->misses, ly->miss_count, ly->fetch_waves,
+            SKV_HIP(skv::launch_fetch(dm, ly->v_host_dev, ly->vc, ly->misses, ly->miss_count, ly->vcode, ly->counters, ly->fetch_waves,
                                       ly->copy));
         }
         SKV_HIP(hipEventRecord(ly->ev_fetch, ly->copy));
@@ -727,7 +773,7 @@ static int decode_impl(skv_layer *ly, const void *q, void *out, hipStream_t st, 
         // one queue: the fetch runs alone on PCIe, then attention
         if (fetch) {
             Timed t(ly, SKV_K_FETCH, st, timed);
-            SKV_HIP(skv::launch_fetch(dm, ly->v_host_dev, ly->vc, ly->misses, ly->miss_count, ly->fetch_waves,
+            SKV_HIP(skv::launch_fetch(dm, ly->v_host_dev, ly->vc, ly->misses, ly->miss_count, ly->vcode, ly->counters, ly->fetch_waves,
                                       st));
         }
         if (ly->fused) {
@@ -877,7 +923,7 @@ int shadowkv_get_stats(skv_layer *ly, skv_stats *out) {
     out->hits = static_cast<int64_t>(c[0]);
     out->misses = static_cast<int64_t>(c[1]);
     out->steps = static_cast<int64_t>(c[2]);
-    out->bytes_h2d = out->misses * ly->dm.c * ly->dm.d * ly->dm.esize;
+    out->bytes_h2d = static_cast<int64_t>(c[3]);  // counted by the fetch: what crossed PCIe
     return SKV_OK;
 }
 
@@ -903,6 +949,7 @@ static const void *tensor_ptr(const skv_layer *ly, int which, size_t *bytes) {
         case SKV_T_SLOT_CHUNKS: *bytes = bh * dm.cap * 4; return ly->slot_chunk;
         case SKV_T_CACHE_V: *bytes = bh * dm.cap * dm.c * D * E; return ly->vc;
         case SKV_T_SELECTION_SLOTS: *bytes = bh * dm.k * 4; return ly->sel_slot;
+        case SKV_T_V_CODES: *bytes = bh * dm.n * 4; return ly->vcode;
         case SKV_T_K_OUT: *bytes = bh * dm.OC * D * E; return ly->k_out;
         case SKV_T_V_OUT: *bytes = bh * dm.OC * D * E; return ly->v_out;
         case SKV_T_K_LOC: *bytes = bh * dm.wcap * D * E; return ly->k_loc;

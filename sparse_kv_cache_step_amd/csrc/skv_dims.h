@@ -58,6 +58,12 @@ hipError_t launch_gather_static(const Dims &dm, const void *k_pre, const void *k
 hipError_t launch_cand_mask(const Dims &dm, const int32_t *outliers, uint32_t *cand, hipStream_t st);
 hipError_t launch_transpose_b(const Dims &dm, const void *B, void *Bt, hipStream_t st);
 hipError_t launch_fill_i32(int32_t *p, int32_t value, size_t count, hipStream_t st);
+// Host V's 12-bit form (prefill.hip): chunk values N when the layer's chunks
+// can take it (bfloat16, N in {512, 1024, 2048}), else 0; the encoder writes
+// nchunks chunks of v (raw, contiguous) into out (2N bytes each, coded or
+// raw) and each chunk's code word.
+int vcode_values(const Dims &dm);
+hipError_t launch_vcode(const Dims &dm, const void *v, void *out, uint32_t *code, long long nchunks, hipStream_t st);
 hipError_t launch_validate_outliers(const Dims &dm, const int32_t *outliers, int32_t *bad, hipStream_t st);
 // Decode-token append: rotate the new key (pre-RoPE, (b, h_kv, d)) at `pos`
 // and write it and its value to row `row` of the local buffers.
@@ -115,7 +121,8 @@ hipError_t launch_snap_accum(const Dims &dm, const float *S2, float *acc, float 
 hipError_t launch_snap_pool(const Dims &dm, const float *acc, const uint32_t *cand, float *S2, uint32_t *keys,
                             uint2 *kbounds, int pool, hipStream_t st);
 hipError_t launch_fetch(const Dims &dm, const void *v_host, void *vc, const int2 *misses,
-                        const int32_t *miss_count, int waves, hipStream_t st);
+                        const int32_t *miss_count, const uint32_t *vcode, unsigned long long *counters, int waves,
+                        hipStream_t st);
 // The rebuilt block's key i*c + t is token t of chunk chunks[i]; its value
 // is in cache slot sel_slot[i], or slot i when sel_slot is null (a cache of
 // exactly k slots, chunks = the slots' chunks).

@@ -111,3 +111,46 @@ def check_outliers(out_gpu: np.ndarray, out_ora: np.ndarray, min_cos_ora: np.nda
 def bf16_ulp(x: np.ndarray) -> np.ndarray:
     ax = np.maximum(np.abs(x), 2.0 ** -126)
     return 2.0 ** (np.floor(np.log2(ax)) - 7)
+
+
+def decode_host_v(hb, codes: np.ndarray, wl) -> np.ndarray:
+    """The pinned host V buffer of a prefilled layer as stored values, each
+    chunk decoded from the form its code word names: raw, or the 12-bit form
+    the header documents under shadowkv_prefill_meta (bytes of sign and
+    mantissa, 4-bit exponent offsets from the chunk's base, 4-byte escapes).
+    Returns the raw bits: uint16 (bfloat16) or uint32 (binary32), shaped
+    (b, h_kv, s, d)."""
+    import torch
+    b, h, s, d, c = wl.b, wl.h_kv, wl.s, wl.d, wl.c
+    esz = 2 if wl.bf16 else 4
+    raw = hb.tensor(torch.uint8, (b * h * s * d * esz,)).numpy().copy()
+    if not wl.bf16:
+        return raw.view(np.uint32).reshape(b, h, s, d)
+    N = c * d
+    chunks = raw.reshape(-1, 2 * N)
+    out = chunks.view(np.uint16).copy()  # raw chunks as they are
+    code = codes.reshape(-1).astype(np.int64) & 0xffffffff
+    coded = np.flatnonzero(code & 0x80000000)
+    if coded.size:
+        cb = chunks[coded]
+        byte = cb[:, :N].astype(np.uint32)
+        nib = cb[:, N:N + N // 2]
+        off = np.empty((coded.size, N), dtype=np.uint32)
+        off[:, 0::2] = nib & 0xf
+        off[:, 1::2] = nib >> 4
+        base = (code[coded] & 0xff).astype(np.uint32)[:, None]
+        e = (base + off) & 0xff
+        vals = ((byte & 0x80) << 8) | (e << 7) | (byte & 0x7f)
+        nesc = (code[coded] >> 16) & 0xff
+        for i in np.flatnonzero(nesc):
+            ent = cb[i, 3 * N // 2:3 * N // 2 + 4 * int(nesc[i])].view(np.uint32)
+            idx = (ent >> 8).astype(np.int64)
+            vals[i, idx] = (vals[i, idx] & 0x807f) | ((ent & 0xff) << 7)
+        out[coded] = vals.astype(np.uint16)
+    return out.reshape(b, h, s, d)
+
+
+def bits_of(x: np.ndarray, bf16: bool) -> np.ndarray:
+    """Stored bits of values held as float64/float32 numbers of the storage type."""
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    return (f.view(np.uint32) >> 16).astype(np.uint16) if bf16 else f.view(np.uint32)

@@ -16,8 +16,8 @@ import pytest
 import torch
 
 import oracle
-from parity_helpers import (OUT_TOL, SHARP_32K, bf16_ulp, check_outliers, check_selection, layer_kwargs, log,
-                            oracle_shape, tdtype, to_dev, to_np)
+from parity_helpers import (OUT_TOL, SHARP_32K, bf16_ulp, bits_of, check_outliers, check_selection, decode_host_v,
+                            layer_kwargs, log, oracle_shape, tdtype, to_dev, to_np)
 from sparse_kv_cache_step_amd import binding as skv
 from sparse_kv_cache_step_amd import synth
 
@@ -103,8 +103,9 @@ def _compare_prefill(wl, layer, hb, meta, v):
     words = layer.read(skv.SKV_T_CAND_MASK).cpu().numpy().view(np.uint32)
     bits = ((words[..., :, None] >> np.arange(32, dtype=np.uint32)) & 1).reshape(wl.b, wl.h_kv, -1)[..., :wl.n]
     np.testing.assert_array_equal(bits, meta["cand"])
-    hv = hb.tensor(tdtype(wl), (wl.b, wl.h_kv, wl.s, wl.d)).float().numpy()
-    np.testing.assert_array_equal(hv, v)
+    # host V, each chunk decoded from its stored form, equals V bit for bit
+    codes = layer.read(skv.SKV_T_V_CODES).cpu().numpy()
+    np.testing.assert_array_equal(decode_host_v(hb, codes, wl), bits_of(v, wl.bf16))
 
 
 def expected_u(P):
@@ -426,6 +427,8 @@ def test_snapkv_selection_matches_oracle(case):
     assert err <= 1e-5 * scale, f"pooled importance differs by {err}"
     st0 = layer.stats()
     assert (st0["hits"], st0["misses"], st0["steps"]) == (0, wl.b * wl.h_kv * wl.k, 1)
+    assert st0["bytes_h2d"] == 0  # the selection's V is fetched by the first decode step
+    raw_bytes = wl.b * wl.h_kv * wl.k * wl.c * wl.d * (2 if wl.bf16 else 4)
 
     for t in range(n_dec):
         q_d = to_dev(qs[w_obs + t], dt)
@@ -438,7 +441,11 @@ def test_snapkv_selection_matches_oracle(case):
         log(f"[snapkv-{case}] decode {t}: max|out - oracle| = {err:.3g}")
         assert err <= OUT_TOL[wl.bf16], f"decode {t}: max abs error {err}"
         st = layer.stats()
-        assert st == st0, "a fixed selection loaded or counted again"
+        if t == 0:  # the one fetch: raw binary32, or bfloat16 in its 12-bit form where coded
+            assert 0 < st["bytes_h2d"] <= raw_bytes and (wl.bf16 or st["bytes_h2d"] == raw_bytes)
+            st1 = st
+        assert {k: st[k] for k in ("hits", "misses", "steps")} == {k: st0[k] for k in ("hits", "misses", "steps")}
+        assert st == st1, "a fixed selection loaded or counted again"
     _check_cache_lossless(wl, layer, v, sel_g)
 
     # reset_cache leaves the fixed selection: the next step selects again
@@ -722,5 +729,76 @@ def test_selection_paths_match_oracle(case, cand, monkeypatch):
             f"max|out - oracle| = {err:.3g}")
         assert err <= OUT_TOL[wl.bf16], f"step {t}: {err}"
         _check_cache_lossless(wl, layer, v, sel_g)
+    layer.close()
+    hb.free()
+
+
+def test_host_v_coding_edge_chunks():
+    """Host V's 12-bit form on chunks made to test it, every selectable chunk
+    fetched (full budget): zeros (coded, no escapes), 10 and 64 values below
+    the exponent window (coded with escapes), 65 such values, a NaN and an
+    Inf, and values over 2^-100 .. 2^100 (raw).  The host buffer decodes to V
+    bit for bit, each chunk's code word says the expected form, and after a
+    decode step the resident cache holds every chunk's V bit for bit."""
+    wl = synth.LLAMA_32K.with_(h_q=8, h_kv=2, s=1024, o=4, k=120, w=32, steps=1, rho=0.9)
+    k_pre, v, qs = synth.k_pre_numpy(wl), synth.v_numpy(wl), synth.queries_numpy(wl)
+    rng = np.random.default_rng(11)
+    N = wl.c * wl.d
+    vv = v.reshape(wl.b, wl.h_kv, wl.n, N).copy()
+    tiny = 2.0 ** -40
+    special = {  # (sequence, head, chunk): expected escapes, or -1 for raw
+        (0, 0, 3): 0, (0, 0, 5): 10, (0, 1, 6): 64, (0, 1, 7): -1, (0, 0, 9): -1, (0, 1, 11): -1, (0, 0, 13): -1}
+    vv[0, 0, 3] = 0.0
+    for key, cnt in ((5, 10), (6, 64), (7, 65)):
+        hh = 0 if key == 5 else 1
+        idx = rng.choice(N, size=cnt, replace=False)
+        vv[0, hh, key, idx] = tiny * rng.choice([-1.0, 1.0], size=cnt)
+    vv[0, 0, 9, 17] = np.nan
+    vv[0, 1, 11, 100] = np.inf
+    vv[0, 0, 13] = np.exp2(rng.uniform(-100, 100, size=N)) * rng.choice([-1.0, 1.0], size=N)
+    # the local window and the outliers are not fetched; keep the special
+    # chunks selectable by placing them early (chunks 3..13 of 128)
+    v2 = vv.reshape(v.shape)
+    dt = tdtype(wl)
+    v_d = to_dev(v2, dt)
+    v2 = to_np(v_d)  # the stored (bfloat16) values
+    k_d = to_dev(k_pre, dt)
+    A_d, B_d = skv.factorize(k_d, wl.r)
+    layer = skv.Layer(**layer_kwargs(wl))
+    hb = layer.host_buffer()
+    layer.prefill_meta(k_d, v_d, A_d, B_d, hb)
+    torch.cuda.synchronize()
+    codes = layer.read(skv.SKV_T_V_CODES).cpu().numpy().astype(np.int64) & 0xffffffff
+    np.testing.assert_array_equal(decode_host_v(hb, codes, wl), bits_of(v2, True))
+    for (bi, hh, ch), want in special.items():
+        cw = int(codes[bi, hh, ch])
+        if want < 0:
+            assert cw == 0, f"chunk {(bi, hh, ch)} should stay raw, code {cw:#x}"
+        else:
+            assert cw & 0x80000000 and ((cw >> 16) & 0xff) == want, f"chunk {(bi, hh, ch)}: code {cw:#x}"
+    coded = float(np.mean((codes & 0x80000000) != 0))
+    log(f"[host-v-coding] coded chunks {coded:.3f}; special chunks as expected")
+    out = torch.empty_like(to_dev(qs[0], dt))
+    layer.decode_step(to_dev(qs[0], dt), out)
+    torch.cuda.synchronize()
+    cap = layer.cap
+    slots = to_np(layer.read(skv.SKV_T_SLOT_CHUNKS))
+    vc = layer.read(skv.SKV_T_CACHE_V).view(torch.int16).cpu().numpy().view(np.uint16)
+    vc = vc.reshape(wl.b, wl.h_kv, cap, N)
+    vbits = bits_of(v2, True).reshape(wl.b, wl.h_kv, wl.n, N)
+    fetched = 0
+    for bi in range(wl.b):
+        for hh in range(wl.h_kv):
+            occ = np.flatnonzero(slots[bi, hh] >= 0)
+            np.testing.assert_array_equal(vc[bi, hh, occ], vbits[bi, hh, slots[bi, hh, occ].astype(np.int64)])
+            fetched += occ.size
+    outl = to_np(layer.read(skv.SKV_T_OUTLIERS))
+    for (bi, hh, ch) in special:  # every selectable chunk is selected (full budget)
+        if ch not in set(outl[bi, hh].tolist()):
+            assert ch in set(slots[bi, hh].tolist()), f"special chunk {(bi, hh, ch)} was not fetched"
+    st = layer.stats()
+    log(f"[host-v-coding] {fetched} chunks fetched, {st['bytes_h2d']} bytes over PCIe "
+        f"({st['bytes_h2d'] / (fetched * 2 * N):.3f} of raw)")
+    assert st["bytes_h2d"] < fetched * 2 * N
     layer.close()
     hb.free()
