@@ -155,7 +155,7 @@ int shadowkv_prefill_meta(skv_layer *layer, const void *k_pre, const void *k_rop
 /*
  * Install precomputed prefill metadata instead of computing it (resume from
  * saved metadata).  All device pointers except v_host (pinned host, already
- * holding V of shape (b, h_kv, s, d)):
+ * holding V of shape (b, h_kv, s, d), raw: the fetch reads it as it is):
  *   landmarks (b, h_kv, n, d); outliers int32 (b, h_kv, o), each row
  *   strictly ascending, values in [0, n - n_loc); k_out, v_out
  *   (b, h_kv, o*c, d) post-RoPE; k_loc, v_loc (b, h_kv, w, d) post-RoPE;
