@@ -185,6 +185,7 @@ def main() -> int:
     ap.add_argument("--kernel-events", choices=["on", "off"], default="on")
     ap.add_argument("--overlap", choices=["on", "off"], default="off",
                     help="fetch beside the key rebuild (on) or before it (off)")
+    ap.add_argument("--batch", type=int, default=None, help="sequences per layer override")
     ap.add_argument("--chunk", type=int, default=None,
                     help="chunk size override (top-k and outlier chunks scaled to keep their token budgets)")
     ap.add_argument("--top-k", type=int, default=None, help="selected chunks per KV head (budget) override")
@@ -607,6 +608,8 @@ def main() -> int:
         for g in grid:
             print(json.dumps(run_one(variant(base, **g))), flush=True)
         return 0
+    if args.batch:
+        base = base.with_(name=f"{base.name}[b={args.batch}]", b=args.batch)
     line = run_one(variant(base, args.chunk, args.top_k, args.rank, args.outlier_chunks))
     print(json.dumps(line), flush=True)
     return 0
