@@ -182,6 +182,8 @@ def main() -> int:
                     help="layers share this many pinned host-V buffers (0: one per layer)")
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true",
+                    help="skip the device-ceiling probes (for profiler runs that count every dispatch)")
     ap.add_argument("--kernel-events", choices=["on", "off"], default="on")
     ap.add_argument("--overlap", choices=["on", "off"], default="off",
                     help="fetch beside the key rebuild (on) or before it (off)")
@@ -407,6 +409,8 @@ def main() -> int:
         # ---- the device's own ceilings, measured in this run --------------------
         peaks = {}
         try:
+            if args.no_probes:
+                raise RuntimeError("--no-probes")
             nb = 1 << 30
             src = torch.empty(nb, dtype=torch.uint8, device=dev)
             dst = torch.empty_like(src)
