@@ -217,6 +217,10 @@ struct skv_layer {
     // the decode selection through slice-local candidates (group_topk +
     // select over the candidates) when both fit in LDS; else group + select
     bool topk_cand = false;
+    // the one-pass selection with the group score computed in the same
+    // kernel (no group kernel)
+    bool select_fused = false;
+    int cus = 0;
     uint32_t *cand_key = nullptr;  // (b, h_kv, slices, k)
     int32_t *cand_idx = nullptr;   // (b, h_kv, slices, k)
     int32_t *cand_count = nullptr; // (b, h_kv, slices)
@@ -431,6 +435,7 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
         int cus = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, ly->device) != hipSuccess || cus < 1)
             return bail(fail(SKV_E_HIP, "hipDeviceGetAttribute(MultiprocessorCount) failed"));
+        ly->cus = cus;
         Dims t = dims_with_local(dm, dm.wcap);
         t.attn_nw = 8;
         dm.attn_nw = skv::attn_waves(t) == 8 && static_cast<long long>(dm.b) * dm.hkv * skv::attn_workgroups(t) <= cus
@@ -513,6 +518,21 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     const bool cand_fits = ly->topk_cand;
     ly->topk_cand = cand_fits && bh < 64;
     if (const char *e = std::getenv("SKV_SELECT_CAND")) ly->topk_cand = cand_fits && std::atoi(e) != 0;
+    // The group score inside the selection kernel, where the rows alone fill
+    // the CUs: one CU reads a row's U at a fraction of the device rate, so
+    // with fewer rows the wide group kernel wins (measured on MI355X: 60K
+    // b48, 384 rows: 44.4 against 47.5 us for group + select; 128K b8, 64
+    // rows: 28.9 against 26.9 us, and splitting each row's score over four
+    // workgroups, the last of which selects, 29.2 us).  SKV_SELECT_FUSED=0/1
+    // forces either where it fits.
+    {
+        const bool fits = skv::select_fused_lds(dm) + skv::select_static_lds() <= lds_cap;
+        bool want = fits && !ly->topk_cand && static_cast<long long>(bh) >= ly->cus;
+        if (const char *e = std::getenv("SKV_SELECT_FUSED")) want = fits && std::atoi(e) != 0;
+        if (const char *e = std::getenv("SKV_SELECT_CAND")) want = want && std::atoi(e) == 0;
+        ly->select_fused = want;
+        if (want) ly->topk_cand = false;
+    }
     {
         const size_t cslots = ly->topk_cand ? bh * skv::topk_slices(dm) * dm.k : 0;
         ALLOC(cand_key, cslots * 4);
@@ -735,7 +755,11 @@ static int decode_impl(skv_layer *ly, const void *q, void *out, hipStream_t st, 
         }
         {
             Timed t(ly, SKV_K_SELECT, st, timed);
-            if (ly->topk_cand) {
+            if (ly->select_fused) {
+                SKV_HIP(skv::launch_select_fused(dm, sc.P, sc.stats, ly->cand, sc.S2, ly->sel, ly->sel_slot,
+                                                 ly->slot_chunk, ly->slot_stamp, ++ly->stamp, ly->misses,
+                                                 ly->miss_count, ly->counters, st));
+            } else if (ly->topk_cand) {
                 SKV_HIP(skv::launch_group_topk(dm, sc.P, sc.stats, ly->cand, sc.S2, sc.cand_key, sc.cand_idx,
                                                sc.cand_count, st));
                 SKV_HIP(skv::launch_select_cand(dm, sc.cand_key, sc.cand_idx, sc.cand_count, ly->sel,

@@ -9,6 +9,8 @@
 //           resident chunks (miss list, hit counts).
 // The same radix selection picks the prefill's outlier chunks.
 #include <algorithm>
+#include <cstdlib>
+#include <type_traits>
 
 #include "skv_device.h"
 
@@ -265,10 +267,8 @@ __device__ __forceinline__ void wave_partials_prefix(const SelectScratch &sc, in
     const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     int x = lane < nw ? sc.wtmp[0][lane] : 0, y = lane < nw ? sc.wtmp[1][lane] : 0;
-    for (int off = 1; off < nw; off <<= 1) {
-        const int x2 = __shfl_up(x, off, 64), y2 = __shfl_up(y, off, 64);
-        if (lane >= off) { x += x2; y += y2; }
-    }
+    x = wave_incl_scan(x);
+    y = wave_incl_scan(y);
     const int src = wave > 0 ? wave - 1 : 0;
     const int px = __builtin_amdgcn_readlane(x, src), py = __builtin_amdgcn_readlane(y, src);
     *pa = wave > 0 ? px : 0;
@@ -281,11 +281,8 @@ __device__ __forceinline__ void wave_partials_prefix(const SelectScratch &sc, in
 // block in one pass (one pair of barriers); totals in *ta, *tb.
 __device__ __forceinline__ void block_scan2(int &a, int &b, SelectScratch &sc, int *ta, int *tb) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int x = __shfl_up(a, off, 64), y = __shfl_up(b, off, 64);
-        if (lane >= off) { a += x; b += y; }
-    }
+    a = wave_incl_scan(a);
+    b = wave_incl_scan(b);
     if (lane == 63) { sc.wtmp[0][wave] = a; sc.wtmp[1][wave] = b; }
     __syncthreads();
     int pa, pb;
@@ -441,6 +438,128 @@ __device__ void radix_topk(const uint32_t *keys, int n, int k, uint32_t kmin, ui
             eq_run += __popcll(be);
         }
     }
+}
+
+// radix_topk with the keys in registers, for rows of at most blockDim.x * KPT
+// keys: thread t holds keys[KPT t .. KPT t + KPT) (LDS, zeros from n to
+// blockDim.x * KPT), read once.  Each pass: the threads add their matching
+// keys to the histogram; then wave 0 alone finds the bin of the krem-th
+// largest offset -- lane L owns the 64 bins of block 63 - L (lane 0 the
+// highest), held so that bins 4m .. 4m + 3 of all blocks are 64 consecutive
+// 16-byte words (bin 64 j + i at hist_pos), four sums of 16 bins per lane, a
+// wave prefix sum, the owner lane's 16 bins -- and clears the histogram: two
+// barriers a pass.  The ordered compaction is one prefix sum of the threads'
+// counts (their keys are contiguous).  The selection goes to s_sel[0, k),
+// ascending; with MARK each selected key keys[j] is replaced by its position
+// + 1, which no key takes (selectable keys are at least 2^31, the others 0).
+// Requires blockDim.x == 1024 and 1 <= k; sc.hist zero on entry and on
+// return.
+__device__ __forceinline__ int hist_pos(uint32_t b) {
+    return static_cast<int>(((b & 63u) >> 2) * 256u + (b >> 6) * 4u + (b & 3u));
+}
+
+template <int KPT, bool MARK>
+__device__ __forceinline__ void radix_topk_regs(uint32_t *keys, int n, int k, uint32_t kmin, uint32_t kmax,
+                                                int32_t *s_sel, SelectScratch &sc) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint32_t kr[KPT];
+#pragma unroll
+    for (int v = 0; v < KPT / 4; ++v) {
+        const u32x4 x = reinterpret_cast<const u32x4 *>(keys)[tid * (KPT / 4) + v];
+        kr[4 * v] = x[0]; kr[4 * v + 1] = x[1]; kr[4 * v + 2] = x[2]; kr[4 * v + 3] = x[3];
+    }
+    const uint32_t range = kmax - kmin;
+    int hi = range == 0 ? 0 : 32 - __clz(static_cast<int>(range));  // bits of the offsets
+    uint64_t prefix = 0;  // offset bits fixed so far (above hi)
+    int krem = k;
+    const int blk = 63 - lane;  // wave 0: this lane's block of 64 bins (lane 0: the highest)
+    while (hi > 0) {
+        const int lo = hi > 12 ? hi - 12 : 0;
+        const uint32_t dmask = (1u << (hi - lo)) - 1u;
+        // offsets matching the prefix: equal to it in the bits at and above hi
+        const uint32_t himask = hi >= 32 ? 0u : ~((1u << hi) - 1u), want = static_cast<uint32_t>(prefix);
+#pragma unroll
+        for (int u = 0; u < KPT; ++u) {
+            const uint32_t rel = kr[u] - kmin;
+            if (kr[u] >= kmin && (rel & himask) == want) atomicAdd(&sc.hist[hist_pos((rel >> lo) & dmask)], 1u);
+        }
+        __syncthreads();  // the histogram is complete (and the previous digit read by all)
+        if (wave == 0) {
+            u32x4 *h4 = reinterpret_cast<u32x4 *>(sc.hist);
+            int sub[4] = {0, 0, 0, 0};
+#pragma unroll 1
+            for (int q = 0; q < 4; ++q) {
+                u32x4 x[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) x[m] = h4[(4 * q + m) * 64 + blk];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) sub[q] += static_cast<int>(x[m][0] + x[m][1] + x[m][2] + x[m][3]);
+            }
+            const int sum = sub[0] + sub[1] + sub[2] + sub[3];
+            const int incl = wave_incl_scan(sum), excl = incl - sum;
+            const uint64_t owner = __ballot(excl < krem && krem <= incl);
+            const int src = owner ? __ffsll(static_cast<long long>(owner)) - 1 : 0;
+            if (lane == src) {
+                int acc = excl, q = 0;
+#pragma unroll
+                for (int i = 3; i >= 0; --i) {
+                    if (acc + sub[i] >= krem) { q = i; break; }
+                    acc += sub[i];
+                }
+                u32x4 x[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) x[m] = h4[(4 * q + m) * 64 + blk];
+                int digit = blk * 64 + q * 16, above = acc;
+                bool found = false;
+#pragma unroll
+                for (int i = 15; i >= 0; --i) {
+                    const int c = static_cast<int>(x[i >> 2][i & 3]);
+                    if (!found && acc + c >= krem) { found = true; digit = blk * 64 + q * 16 + i; above = acc; }
+                    acc += c;
+                }
+                sc.digit = static_cast<uint32_t>(digit);
+                sc.above = above;
+            }
+            // every lane's reads above precede its clears (same lane, in order)
+#pragma unroll
+            for (int m = 0; m < 16; ++m) h4[m * 64 + blk] = u32x4{0u, 0u, 0u, 0u};
+        }
+        __syncthreads();
+        prefix |= static_cast<uint64_t>(sc.digit) << lo;
+        krem -= sc.above;
+        hi = lo;
+    }
+    const uint32_t thr = kmin + static_cast<uint32_t>(prefix);  // the k-th largest key
+    const int need_eq = krem;  // keys equal to thr that are taken, lowest index first
+    int cg = 0, ce = 0;
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+        cg += kr[u] > thr ? 1 : 0;
+        ce += kr[u] == thr ? 1 : 0;
+    }
+    int ig = cg, ie = ce, tg, te;
+    block_scan2(ig, ie, sc, &tg, &te);  // also orders the digit reads above before wtmp's reuse
+    int gb = ig - cg, eb = ie - ce;     // keys of lower index: greater, equal
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+        const int j = tid * KPT + u;
+        const bool g = kr[u] > thr, e = kr[u] == thr;
+        if (g || (e && eb < need_eq)) {
+            const int pos = gb + min(eb, need_eq);
+            if (pos < k) {
+                s_sel[pos] = j;
+                if constexpr (MARK) keys[j] = static_cast<uint32_t>(pos + 1);
+            }
+        }
+        gb += g ? 1 : 0;
+        eb += e ? 1 : 0;
+    }
+}
+
+// keys per thread of the register form for a row of n keys (0: rows longer
+// than 1024 x 32 keep radix_topk)
+__host__ __device__ constexpr int select_kpt(int n) {
+    return n <= 8192 ? 8 : (n <= 16384 ? 16 : (n <= 32768 ? 32 : 0));
 }
 
 // Outlier selection for the prefill: the o chunks with the lowest minimum
@@ -693,6 +812,108 @@ __global__ __launch_bounds__(kSelectThreads) void group_topk_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// The group score of one row into LDS, by a whole workgroup (group_kernel's
+// steps 1-3 with the same arithmetic): the per-head maxima and sums over the
+// row's tiles, the tile weights into s_w (tiles x GP), then S2 for every
+// chunk, written to S2 and as keys into keys[0, n) (LDS), with the smallest
+// and largest selectable key of this thread's chunks.  The first chunks' U
+// rows are requested before the reduction, and each batch of chunks while
+// the previous one is scored.  Every thread must call it (one barrier).
+template <int GP>
+__device__ __forceinline__ void group_score_lds(const float *__restrict__ U, const float2 *__restrict__ stats,
+                                                const uint32_t *__restrict__ cand, int mask_words,
+                                                float *__restrict__ S2, uint32_t *keys, float *s_w, int G, int n,
+                                                int tiles, int bh, uint32_t &kmn, uint32_t &kmx) {
+    const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wave = tid >> 6, nw = nt >> 6;
+    constexpr int UNR = 32 / GP;
+    const float *Ub = U + static_cast<size_t>(bh) * n * G;
+    const uint32_t *cm = cand + static_cast<size_t>(bh) * mask_words;
+    float *s2row = S2 + static_cast<size_t>(bh) * n;
+    const int per = UNR * nt, iters = (n + per - 1) / per;
+    float v[2][UNR][GP];
+    uint32_t word[2][UNR];
+    auto load = [&](int buf, int it) {
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int j = min(it * per + u * nt + tid, n - 1);
+            word[buf][u] = cm[j >> 5];
+            if (G == GP) {
+#pragma unroll
+                for (int q4 = 0; q4 < GP / 4; ++q4) {
+                    const float4 f = *reinterpret_cast<const float4 *>(Ub + static_cast<size_t>(j) * GP + 4 * q4);
+                    v[buf][u][4 * q4] = f.x; v[buf][u][4 * q4 + 1] = f.y;
+                    v[buf][u][4 * q4 + 2] = f.z; v[buf][u][4 * q4 + 3] = f.w;
+                }
+            } else {
+#pragma unroll
+                for (int g = 0; g < GP; ++g) v[buf][u][g] = g < G ? Ub[static_cast<size_t>(j) * G + g] : 0.f;
+            }
+        }
+    };
+    auto score = [&](int buf, int it) {
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) {
+            const int j = it * per + u * nt + tid;
+            if (j >= n) break;
+            const bool valid = (word[buf][u] >> (j & 31)) & 1u;
+            const float *wt = s_w + (j >> 6) * GP;
+            float acc = 0.f;
+#pragma unroll
+            for (int g = 0; g < GP; ++g)
+                if (g < G) acc += v[buf][u][g] * wt[g];
+            s2row[j] = valid ? acc : 0.f;
+            const uint32_t key = float_key(acc);
+            keys[j] = valid ? key : 0u;
+            if (valid) { kmn = min(kmn, key); kmx = max(kmx, key); }
+        }
+    };
+    load(0, 0);
+    // per head (a wave each): m_g, Z_g over the row's tiles, the tile weights
+    for (int g = wave; g < G; g += nw) {
+        const float2 *st = stats + (static_cast<size_t>(bh) * G + g) * tiles;
+        constexpr int TPL = 8;
+        float2 sv[TPL];
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            const int t = lane + 64 * i;
+            sv[i] = t < tiles ? st[t] : make_float2(-INFINITY, 0.f);
+        }
+        float m = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) m = fmaxf(m, sv[i].x);
+        for (int t = lane + 64 * TPL; t < tiles; t += 64) m = fmaxf(m, st[t].x);
+        m = wave_max(m);
+        float z = 0.f;
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) z += sv[i].x == -INFINITY ? 0.f : sv[i].y * expf(sv[i].x - m);
+        for (int t = lane + 64 * TPL; t < tiles; t += 64) {
+            const float2 x = st[t];
+            z += x.x == -INFINITY ? 0.f : x.y * expf(x.x - m);
+        }
+        z = wave_sum(z);
+        const float inv = z > 0.f ? 1.f / (z * static_cast<float>(G)) : 0.f;
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            const int t = lane + 64 * i;
+            if (t < tiles) s_w[t * GP + g] = sv[i].x == -INFINITY ? 0.f : expf(sv[i].x - m) * inv;
+        }
+        for (int t = lane + 64 * TPL; t < tiles; t += 64) {
+            const float2 x = st[t];
+            s_w[t * GP + g] = x.x == -INFINITY ? 0.f : expf(x.x - m) * inv;
+        }
+    }
+    __syncthreads();
+    for (int it = 0; it < iters; it += 2) {
+        if (it + 1 < iters) load(1, it + 1);
+        score(0, it);
+        if (it + 1 < iters) {
+            if (it + 2 < iters) load(0, it + 2);
+            score(1, it + 1);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Decode selection, one workgroup per (sequence, KV head) row:
 //  1. the row's keys (from the group kernel) into LDS when they fit, and
 //     their bounds from the per-slice minima and maxima;
@@ -709,9 +930,16 @@ __global__ __launch_bounds__(kSelectThreads) void group_topk_kernel(
 // ---------------------------------------------------------------------------
 // CAND: the keys are the slices' candidates from group_topk_kernel (cslices
 // slices of up to k per row, ascending chunk order), ranked here and mapped
-// back to chunks; otherwise all n keys of the row with per-slice bounds.
-template <bool CAND>
+// back to chunks.  GP > 0: the keys are the group score, computed in step 1
+// from U and the tile statistics (group_score_lds) straight into LDS, which
+// saves the group kernel's launch and the keys' round trip through memory
+// (it pays where the rows alone fill the CUs: one CU reads a row's U at a
+// fraction of the device rate).  Otherwise all n keys of the row with
+// per-slice bounds.
+template <bool CAND, int GP, int KPT>
 __global__ __launch_bounds__(kSelectThreads) void select_kernel(
+    const float *__restrict__ U, const float2 *__restrict__ stats, const uint32_t *__restrict__ cand,
+    int mask_words, float *__restrict__ S2, int G, int tiles,
     const uint32_t *__restrict__ keys_g, const uint2 *__restrict__ kbounds, int slices,
     const uint32_t *__restrict__ cand_key, const int32_t *__restrict__ cand_idx,
     const int32_t *__restrict__ cand_count, int cslices, int32_t *__restrict__ sel,
@@ -725,7 +953,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
     // dynamic LDS: the keys first (16-byte aligned): the row's n keys when
     // they fit, or the candidates (keys, then their chunks)
     const uint32_t *krow = keys_g + static_cast<size_t>(bh) * n;
-    const int kcap = CAND ? cslices * k : (use_lds ? n : 0);  // key entries held in LDS
+    // key entries held in LDS (the register form pads the row with zeros to 1024 x KPT)
+    const int kcap = CAND ? cslices * k : (KPT > 0 ? kSelectThreads * KPT : (use_lds ? n : 0));
     // keys in LDS are reached through dyn itself (never through a pointer
     // that may also be global), so their accesses compile to LDS instructions
     const bool lds_keys = CAND || use_lds;
@@ -736,6 +965,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
     int32_t *s_rank = s_sslot + k;                      // k: index in s_sel of the m-th miss
     uint32_t *s_age = reinterpret_cast<uint32_t *>(s_rank + k);  // cap: eviction key (0: not evictable)
     int32_t *s_free = reinterpret_cast<int32_t *>(s_age + cap);  // cap: rank of a free slot, -1 otherwise
+    float *s_w = reinterpret_cast<float *>(s_free + cap);        // GP > 0: tiles x GP tile weights
 
     uint32_t kmn = 0xffffffffu, kmx = 0u;
     int nkeys = n;
@@ -765,6 +995,13 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
         }
         nkeys = off;
     } else {
+        bool from_global = true;
+        if constexpr (GP > 0) {
+            // the group score computed here, straight into LDS
+            group_score_lds<GP>(U, stats, cand, mask_words, S2, dyn, s_w, G, n, tiles, bh, kmn, kmx);
+            from_global = false;
+        }
+        if (from_global) {
         if (use_lds) {
             // 16-byte buffer loads, four per thread in flight (16384 keys per
             // batch); offsets past the row read zeros and are not stored
@@ -790,7 +1027,10 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
             kmn = min(kmn, b2.x);
             kmx = max(kmx, b2.y);
         }
+        }
     }
+    if constexpr (KPT > 0)
+        for (int j = n + tid; j < kcap; j += nt) dyn[j] = 0u;
     for (int i = tid; i < 4096; i += nt) sc.hist[i] = 0;
     for (int i = tid; i < k; i += nt) s_sslot[i] = -1;
     block_minmax(kmn, kmx, sc);  // its barriers also publish the keys
@@ -805,7 +1045,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
     // for a load also waits for every earlier store, so the kernel's global
     // stores all come after its last global load
     int32_t *srow = sel + static_cast<size_t>(bh) * k;
-    if (lds_keys) radix_topk(dyn, nkeys, k, kmn, kmx, nullptr, s_sel, sc);
+    if constexpr (KPT > 0) radix_topk_regs<KPT, true>(dyn, nkeys, k, kmn, kmx, s_sel, sc);
+    else if (lds_keys) radix_topk(dyn, nkeys, k, kmn, kmx, nullptr, s_sel, sc);
     else radix_topk(krow, nkeys, k, kmn, kmx, nullptr, s_sel, sc);
     __syncthreads();
     if constexpr (CAND) {  // candidate positions to chunks (still ascending)
@@ -827,9 +1068,15 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
         if (c >= 0) {
             ++nres;
             int lo = 0, hi = k;
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (s_sel[mid] < c) lo = mid + 1; else hi = mid;
+            if constexpr (KPT > 0) {
+                // the selection marked its chunks' keys with position + 1
+                const uint32_t mk = c < n ? dyn[c] : 0u;
+                lo = mk >= 1u && mk <= static_cast<uint32_t>(k) ? static_cast<int>(mk) - 1 : k;
+            } else {
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if (s_sel[mid] < c) lo = mid + 1; else hi = mid;
+                }
             }
             if (lo < k && s_sel[lo] == c) {
                 s_sslot[lo] = sl;  // a hit: its stamp is renewed in the last phase
@@ -1036,9 +1283,16 @@ hipError_t launch_score(const Dims &dm, const void *q, const void *landmarks, co
     return hipGetLastError();
 }
 
+int select_kpt_of(const Dims &dm) {
+    if (const char *e = std::getenv("SKV_SELECT_REGS"))
+        if (std::atoi(e) == 0) return 0;
+    return select_kpt(dm.n);
+}
+
 size_t select_dynamic_lds(const Dims &dm, bool keys_in_lds) {
-    return (3ull * dm.k + 2ull * dm.cap) * sizeof(int32_t) +
-           (keys_in_lds ? static_cast<size_t>(dm.n) * sizeof(uint32_t) : 0);
+    const int kpt = keys_in_lds ? select_kpt_of(dm) : 0;
+    const size_t kent = kpt > 0 ? static_cast<size_t>(kSelectThreads) * kpt : static_cast<size_t>(dm.n);
+    return (3ull * dm.k + 2ull * dm.cap) * sizeof(int32_t) + (keys_in_lds ? kent * sizeof(uint32_t) : 0);
 }
 
 int topk_slice(const Dims &dm) { return dm.tslice > 0 ? dm.tslice : dm.k <= 1024 ? 4096 : 16384; }
@@ -1079,14 +1333,57 @@ hipError_t launch_select(const Dims &dm, const uint32_t *keys, const uint2 *kbou
                          int2 *misses, int32_t *miss_count, unsigned long long *counters, int keys_in_lds,
                          hipStream_t st) {
     if (dm.k > 0 && dm.cap < dm.k) return hipErrorInvalidValue;
+    const int kpt = keys_in_lds ? select_kpt_of(dm) : 0;
     const size_t lds = select_dynamic_lds(dm, keys_in_lds != 0);
-    auto kern = select_kernel<false>;
-    hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(dm.b * dm.hkv), dim3(kSelectThreads), lds, st, keys, kbounds, group_slices(dm),
-                       nullptr, nullptr, nullptr, 0, sel, sel_slot, slot_chunk, slot_stamp, stamp, misses,
-                       miss_count, counters, keys_in_lds, dm.n, dm.k, dm.cap);
-    return hipGetLastError();
+    auto go = [&](auto kern) {
+        hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3(dm.b * dm.hkv), dim3(kSelectThreads), lds, st, nullptr, nullptr, nullptr, 0,
+                           nullptr, 0, 0, keys, kbounds, group_slices(dm), nullptr, nullptr, nullptr, 0, sel,
+                           sel_slot, slot_chunk, slot_stamp, stamp, misses, miss_count, counters, keys_in_lds, dm.n,
+                           dm.k, dm.cap);
+        return hipGetLastError();
+    };
+    switch (kpt) {
+        case 8: return go(select_kernel<false, 0, 8>);
+        case 16: return go(select_kernel<false, 0, 16>);
+        case 32: return go(select_kernel<false, 0, 32>);
+        default: return go(select_kernel<false, 0, 0>);
+    }
+}
+
+size_t select_fused_lds(const Dims &dm) {
+    return select_dynamic_lds(dm, true) + static_cast<size_t>(dm.wtiles) * dm.GP * sizeof(float);
+}
+
+hipError_t launch_select_fused(const Dims &dm, const float *P, const float2 *stats, const uint32_t *cand, float *S2,
+                               int32_t *sel, int32_t *sel_slot, int32_t *slot_chunk, uint32_t *slot_stamp,
+                               uint32_t stamp, int2 *misses, int32_t *miss_count, unsigned long long *counters,
+                               hipStream_t st) {
+    if (dm.k > 0 && dm.cap < dm.k) return hipErrorInvalidValue;
+    const size_t lds = select_fused_lds(dm);
+    auto go = [&](auto kern) {
+        hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), lds);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3(dm.b * dm.hkv), dim3(kSelectThreads), lds, st, P, stats, cand, dm.mask_words,
+                           S2, dm.G, dm.wtiles, nullptr, nullptr, 0, nullptr, nullptr, nullptr, 0, sel, sel_slot,
+                           slot_chunk, slot_stamp, stamp, misses, miss_count, counters, 1, dm.n, dm.k, dm.cap);
+        return hipGetLastError();
+    };
+    auto by_kpt = [&](auto gp) {
+        constexpr int G4 = decltype(gp)::value;
+        switch (select_kpt_of(dm)) {
+            case 8: return go(select_kernel<false, G4, 8>);
+            case 16: return go(select_kernel<false, G4, 16>);
+            case 32: return go(select_kernel<false, G4, 32>);
+            default: return go(select_kernel<false, G4, 0>);
+        }
+    };
+    switch (dm.GP) {
+        case 4: return by_kpt(std::integral_constant<int, 4>{});
+        case 8: return by_kpt(std::integral_constant<int, 8>{});
+        default: return by_kpt(std::integral_constant<int, 16>{});
+    }
 }
 
 hipError_t launch_group_topk(const Dims &dm, const float *P, const float2 *stats, const uint32_t *cand, float *S2,
@@ -1115,10 +1412,11 @@ hipError_t launch_select_cand(const Dims &dm, const uint32_t *cand_key, const in
                               unsigned long long *counters, hipStream_t st) {
     if (dm.k > 0 && dm.cap < dm.k) return hipErrorInvalidValue;
     const size_t lds = select_cand_lds(dm);
-    auto kern = select_kernel<true>;
+    auto kern = select_kernel<true, 0, 0>;
     hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(dm.b * dm.hkv), dim3(kSelectThreads), lds, st, nullptr, nullptr, 0, cand_key,
+    hipLaunchKernelGGL(kern, dim3(dm.b * dm.hkv), dim3(kSelectThreads), lds, st, nullptr, nullptr, nullptr, 0,
+                       nullptr, 0, 0, nullptr, nullptr, 0, cand_key,
                        cand_idx, cand_count, topk_slices(dm), sel, sel_slot, slot_chunk, slot_stamp, stamp, misses,
                        miss_count, counters, 0, dm.n, dm.k, dm.cap);
     return hipGetLastError();

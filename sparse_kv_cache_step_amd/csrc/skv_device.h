@@ -112,6 +112,24 @@ template <typename Op> __device__ __forceinline__ float wave_reduce(float v, Op 
     return op(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
 }
 
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele inside each row of
+// 16 lanes with DPP row shifts (lanes shifted in from outside the row add 0),
+// then each row adds the totals of the rows before it, read from lanes 15,
+// 31 and 47.  No step goes through LDS.
+template <int CTRL> __device__ __forceinline__ int dpp_i32(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    x += dpp_i32<0x111>(x);  // row_shr:1
+    x += dpp_i32<0x112>(x);  // row_shr:2
+    x += dpp_i32<0x114>(x);  // row_shr:4
+    x += dpp_i32<0x118>(x);  // row_shr:8
+    const int row = (threadIdx.x & 63) >> 4;
+    const int t0 = __builtin_amdgcn_readlane(x, 15), t1 = __builtin_amdgcn_readlane(x, 31),
+              t2 = __builtin_amdgcn_readlane(x, 47);
+    return x + (row > 0 ? t0 : 0) + (row > 1 ? t1 : 0) + (row > 2 ? t2 : 0);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
     return wave_reduce(v, [](float a, float b) { return a + b; });
 }

@@ -115,6 +115,13 @@ hipError_t launch_select_cand(const Dims &dm, const uint32_t *cand_key, const in
                               const int32_t *cand_count, int32_t *sel, int32_t *sel_slot, int32_t *slot_chunk,
                               uint32_t *slot_stamp, uint32_t stamp, int2 *misses, int32_t *miss_count,
                               unsigned long long *counters, hipStream_t st);
+// The group score and the selection in one kernel (one workgroup per row,
+// the keys in LDS): launch_group's S2 and launch_select's outputs.
+size_t select_fused_lds(const Dims &dm);
+hipError_t launch_select_fused(const Dims &dm, const float *P, const float2 *stats, const uint32_t *cand, float *S2,
+                               int32_t *sel, int32_t *sel_slot, int32_t *slot_chunk, uint32_t *slot_stamp,
+                               uint32_t stamp, int2 *misses, int32_t *miss_count, unsigned long long *counters,
+                               hipStream_t st);
 // SnapKV-style selection: accumulate a pass's summed attention, then pool
 // it into S2, selection keys and slice bounds.
 hipError_t launch_snap_accum(const Dims &dm, const float *S2, float *acc, float weight, int first, hipStream_t st);

@@ -698,17 +698,26 @@ SELECT_CASES = {
                                                    rho=0.9),
     # a budget larger than a slice's share of candidates (k = 1000, slices of 4096, n = 9000)
     "fp32-three-slices": T.with_(s=72000, d=64, r=32, o=9, k=1000, w=16, steps=2, rho=0.9, n_scaled_chunks=6),
+    # a row shorter than one 256-key block of the single-wave selection, k of 3
+    "fp32-short-row": T.with_(s=1000, d=64, r=32, o=4, k=3, w=16, steps=3, rho=0.9),
 }
 
 
-@pytest.mark.parametrize("cand", ["1", "0"])
+# (SKV_SELECT_FUSED, SKV_SELECT_CAND) of each way to the ArgTopK
+SELECT_PATHS = {"fused": ("1", "0"), "row": ("0", "0"), "cand": ("0", "1")}
+
+
+@pytest.mark.parametrize("cand", list(SELECT_PATHS))
 @pytest.mark.parametrize("case", list(SELECT_CASES))
 def test_selection_paths_match_oracle(case, cand, monkeypatch):
-    """The two ways to the ArgTopK, forced in turn: slice-local candidates
-    merged by a second pass, and one pass over the whole row.  Each is checked
-    against the oracle's selection (exact or near-tie swaps) and output."""
+    """The ways to the ArgTopK, forced in turn: one pass over the whole row
+    with the group score computed in the same kernel, the same after the group
+    kernel, and slice-local candidates merged by a second pass.  Each is
+    checked against the oracle's selection (exact or near-tie swaps) and
+    output, over several steps (the cache update)."""
     wl = SELECT_CASES[case]
-    monkeypatch.setenv("SKV_SELECT_CAND", cand)
+    monkeypatch.setenv("SKV_SELECT_FUSED", SELECT_PATHS[cand][0])
+    monkeypatch.setenv("SKV_SELECT_CAND", SELECT_PATHS[cand][1])
     shape = oracle_shape(wl)
     k_pre, v, qs = synth.k_pre_numpy(wl), synth.v_numpy(wl), synth.queries_numpy(wl)
     meta = oracle.prefill(shape, k_pre, v)
