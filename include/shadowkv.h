@@ -98,7 +98,7 @@ typedef struct skv_layer skv_layer;
 /* Counters accumulated by the decode steps since creation or the last
  * shadowkv_reset_stats.  hits/misses count chunks per (sequence, KV head);
  * bytes_h2d is what the V fetch read from pinned host memory (raw chunks at
- * 2 bytes a value, coded ones at 12 bits a value plus their escapes). */
+ * 2 bytes a value, coded ones in their coded size: see shadowkv_prefill_meta). */
 typedef struct {
     int64_t steps;
     int64_t hits;
@@ -115,8 +115,8 @@ void shadowkv_layer_destroy(skv_layer *layer);
 
 /*
  * Algorithm 1 (Pre-filling), steps 2-5, on the device.  Step 1's factors are
- * inputs: the review page places the SVD of the pre-RoPE keys in prefill and
- * the build computes it once on the host side, outside this library.
+ * inputs (shadowkv_factorize computes them on the device; any factors of the
+ * documented shapes will do).
  *   k_pre       device (b, h_kv, s, d)  pre-RoPE keys.
  *   k_rope      device (b, h_kv, s, d)  post-RoPE keys, or NULL: then they
  *               are computed here from k_pre (rotate-half RoPE, 0-based
@@ -129,18 +129,29 @@ void shadowkv_layer_destroy(skv_layer *layer);
  *   v_host      pinned host (b, h_kv, s, d) bytes of dtype: receives V (the
  *               offload of step 5), each chunk in its own c*d-value slot; must
  *               stay allocated while the layer is used.  For bfloat16 layers
- *               with c*d in {512, 1024, 2048} a chunk is written in a
- *               lossless 12-bit form, because the decode step's V fetch is
- *               bound by PCIe: N = c*d bytes of sign and mantissa, N/2 bytes
- *               of 4-bit exponent offsets from the chunk's base (offset 15:
- *               escape), then 4 bytes per escape, (value index << 8) |
- *               exponent, for the values whose exponent lies below the base;
- *               the base is the chunk's largest exponent minus 14 (at least
- *               0), and chunks with more than 64 escapes stay raw.  Lane l of
- *               64 owns values l*N/64 ..: its bytes at l*N/64, its offsets
- *               (value q at bits 4*(q % 8) of 32-bit word q/8) at
- *               N + l*N/128.  SKV_T_V_CODES gives each chunk's form; the fetch
- *               restores V bit for bit.
+ *               with N = c*d in {512, 1024, 2048} a chunk is written in the
+ *               smaller of two lossless coded forms, because the decode
+ *               step's V fetch is bound by PCIe.  Lane l of 64 owns values
+ *               l*Q .. l*Q+Q-1 (Q = N/64); both forms start with N bytes of
+ *               sign and mantissa (lane l's at l*Q).
+ *               The 12-bit form: N/2 bytes of 4-bit exponent offsets from
+ *               the base, the chunk's largest exponent minus 14 (at least
+ *               0), lane l's at N + l*Q/2, value q at bits 4*(q % 8) of
+ *               32-bit word q/8, offset 15 marking an escape; then from
+ *               N + N/2 4 bytes per escape, (value index << 8) | exponent,
+ *               for the values whose exponent lies below the base.
+ *               The class form: with top = the largest exponent minus 1 (at
+ *               least 0), N/4 bytes of 2-bit classes, lane l's at
+ *               N + l*Q/4, value q at bits 2*(q % 16) of 32-bit word q/16:
+ *               0, 1, 2 = exponent top, top-1, top-2, 3 = in the side
+ *               stream; from N + N/4 the side stream of S bytes (a multiple
+ *               of 4), a 3-bit code per class-3 value in value order, code i
+ *               at bits 3i..3i+2 (bit 0 of byte 0 first): 0 = top+1, x in
+ *               1..6 = top-2-x, 7 = an escape; then from N + N/4 + S the
+ *               escapes as above.
+ *               A chunk with more than 64 escapes in both forms stays raw.
+ *               SKV_T_V_CODES gives each chunk's form; the fetch restores V
+ *               bit for bit.
  * Computes the chunk means of the post-RoPE keys (landmarks), each chunk's
  * minimum cosine to its landmark, the n_outlier chunks with the lowest
  * minimum (ties: lower index; chunks of the local window excluded), gathers
@@ -275,9 +286,11 @@ enum {
     SKV_T_SELECTION_SLOTS = 13, /* int32 (b, h_kv, k): slot holding the i-th
                                    selected chunk                             */
     SKV_T_V_CODES = 14,     /* uint32 (b, h_kv, n): each host V chunk's code
-                               word: 0 raw, else bit 31 set, the escape count
-                               in bits 16..23 and the exponent base in bits
-                               0..7 of the 12-bit form (shadowkv_prefill_meta) */
+                               word (forms: shadowkv_prefill_meta): 0 raw;
+                               bit 31 alone: 12-bit form, escape count in bits
+                               16..23, base in bits 0..7; bits 31 and 30: class
+                               form, S/4 in bits 20..27, escape count in bits
+                               8..15, top in bits 0..7                         */
     SKV_T_COUNT = 15
 };
 size_t shadowkv_tensor_bytes(const skv_layer *layer, int which);

@@ -33,6 +33,9 @@ __global__ __launch_bounds__(256) void fetch_kernel(const u32x4 *__restrict__ v_
                                                     int cap, int n, int chunk_vec) {
     extern __shared__ int pre[];  // rows + 1 prefix sums
     __shared__ int wsum[4];
+    // per wave: a class-form chunk's side stream (up to 3N/8 bytes, with slack)
+    constexpr int SW = VPL > 0 ? (3 * 512 * VPL / 8) / 4 + 8 : 1;
+    __shared__ uint32_t s_side[4][SW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int carry = 0;
     for (int base = 0; base < rows; base += 256) {
@@ -76,7 +79,92 @@ __global__ __launch_bounds__(256) void fetch_kernel(const u32x4 *__restrict__ v_
         if constexpr (VPL > 0) {
             constexpr int Q = 8 * VPL;  // values per lane
             const int N = 64 * Q;
-            if (code & 0x80000000u) {  // wave-uniform: the 12-bit form (see prefill.hip)
+            if ((code & 0xC0000000u) == 0xC0000000u) {  // wave-uniform: the class form (see prefill.hip)
+                const int top = static_cast<int>(code & 0xffu), nesc = static_cast<int>((code >> 8) & 0xffu);
+                const int S = static_cast<int>((code >> 20) & 0xffu) * 4;
+                const uint8_t *sb = reinterpret_cast<const uint8_t *>(src);
+                uint32_t bw[Q / 4], cw[(Q + 15) / 16];
+                if constexpr (Q == 8) {
+                    const u32x2 b2 = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(sb) + lane);
+                    bw[0] = b2[0]; bw[1] = b2[1];
+                    cw[0] = __builtin_nontemporal_load(reinterpret_cast<const uint16_t *>(sb + N) + lane);
+                } else if constexpr (Q == 16) {
+                    const u32x4 b4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(sb) + lane);
+                    bw[0] = b4[0]; bw[1] = b4[1]; bw[2] = b4[2]; bw[3] = b4[3];
+                    cw[0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(sb + N) + lane);
+                } else {
+                    const u32x4 b4a = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(sb) + 2 * lane);
+                    const u32x4 b4b = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(sb) + 2 * lane + 1);
+                    bw[0] = b4a[0]; bw[1] = b4a[1]; bw[2] = b4a[2]; bw[3] = b4a[3];
+                    bw[4] = b4b[0]; bw[5] = b4b[1]; bw[6] = b4b[2]; bw[7] = b4b[3];
+                    const u32x2 c2 = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(sb + N) + lane);
+                    cw[0] = c2[0]; cw[1] = c2[1];
+                }
+                // the side stream, 16 bytes a lane, and the escapes
+                const u32x4 sv = 16 * lane < S ? __builtin_nontemporal_load(
+                                                     reinterpret_cast<const u32x4 *>(sb + N + N / 4) + lane)
+                                               : u32x4{0u, 0u, 0u, 0u};
+                const uint32_t esc = lane < nesc
+                    ? __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(sb + N + N / 4 + S) + lane) : 0u;
+                // the next miss is located while this chunk's host reads are in flight
+                int row_n = row;
+                const int2 e_n = g + nw < total ? locate(g + nw, row_n) : e;
+                const uint32_t code_n = g + nw < total && vcode ? vcode[static_cast<size_t>(row_n) * n + e_n.x] : 0u;
+                uint32_t *side = s_side[wave];
+                if (16 * lane < S) reinterpret_cast<u32x4 *>(side)[lane] = sv;
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                // the stream holds the class-3 codes in value order, so this
+                // lane's start is the class-3 count of the lanes before it
+                int n3l = 0;
+#pragma unroll
+                for (int h = 0; h < (Q + 15) / 16; ++h) n3l += __popc(cw[h] & (cw[h] >> 1) & 0x55555555u);
+                int pos = 3 * (wave_incl_scan(n3l) - n3l);
+                uint32_t x[Q];
+#pragma unroll
+                for (int h = 0; h < (Q + 15) / 16; ++h) {
+                    // a 64-bit window of the stream at pos (a group of 16
+                    // values takes at most 48 bits)
+                    const int w0 = pos >> 5, sh = pos & 31;
+                    uint64_t win = (static_cast<uint64_t>(side[w0]) | (static_cast<uint64_t>(side[w0 + 1]) << 32)) >> sh;
+                    if (sh) win |= static_cast<uint64_t>(side[w0 + 2]) << (64 - sh);
+                    const uint32_t c = cw[h];
+                    constexpr int GQ = Q < 16 ? Q : 16;
+#pragma unroll
+                    for (int q = 0; q < GQ; ++q) {
+                        const int cl = static_cast<int>((c >> (2 * q)) & 3u);
+                        int ex = top - cl;
+                        if (cl == 3) {
+                            const int xc = static_cast<int>(win & 7u);
+                            win >>= 3;
+                            pos += 3;
+                            ex = xc == 0 ? top + 1 : top - 2 - xc;  // 7: an escape, patched below
+                        }
+                        const int qq = 16 * h + q;
+                        const uint32_t byte = (bw[qq >> 2] >> (8 * (qq & 3))) & 0xffu;
+                        x[qq] = ((byte & 0x80u) << 8) | ((static_cast<uint32_t>(ex) & 0xffu) << 7) | (byte & 0x7fu);
+                    }
+                }
+                // escapes: the exponent itself, for the lane owning the value
+                for (int j = 0; j < nesc; ++j) {
+                    const uint32_t ej = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(esc), j));
+                    const int idx = static_cast<int>(ej >> 8);
+                    if (idx / Q == lane) {
+#pragma unroll
+                        for (int q = 0; q < Q; ++q)
+                            if (q == idx % Q) x[q] = (x[q] & 0x807fu) | ((ej & 0xffu) << 7);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < VPL; ++u)
+                    dst[lane * VPL + u] = u32x4{x[8 * u] | (x[8 * u + 1] << 16), x[8 * u + 2] | (x[8 * u + 3] << 16),
+                                                x[8 * u + 4] | (x[8 * u + 5] << 16), x[8 * u + 6] | (x[8 * u + 7] << 16)};
+                wire += static_cast<unsigned long long>(N + N / 4 + S + 4 * nesc);
+                row = row_n;
+                e = e_n;
+                code = code_n;
+            } else if (code & 0x80000000u) {  // wave-uniform: the 12-bit form (see prefill.hip)
                 const int base = static_cast<int>(code & 0xffu), nesc = static_cast<int>((code >> 16) & 0xffu);
                 const uint8_t *sb = reinterpret_cast<const uint8_t *>(src);
                 uint32_t bw[Q / 4], nwd[Q / 8];

@@ -303,29 +303,49 @@ hipError_t launch_append(const Dims &dm, const void *k_new, const void *v_new, c
 
 
 // ---------------------------------------------------------------------------
-// Host V in a lossless 12-bit form (bfloat16 chunks of N = 512, 1024 or 2048
-// values).  The V fetch is bound by PCIe, so each chunk crosses it as
-//   N bytes      sign and mantissa of every value (bits 15 and 6..0),
-//   N / 2 bytes  its exponent as a 4-bit offset from the chunk's base,
-//                base = max(0, largest exponent - 14); offset 15 marks an
-//                escape,
+// Host V in a lossless coded form (bfloat16 chunks of N = 512, 1024 or 2048
+// values).  The V fetch is bound by PCIe, so each chunk crosses it in the
+// smaller of two forms, in the chunk's own slot of the host buffer (2N bytes).
+// Lane l of a chunk's wave owns values l*Q .. l*Q+Q-1 (Q = N / 64).  Both
+// forms start with
+//   N bytes      sign and mantissa of every value (bits 15 and 6..0), lane l's
+//                Q bytes at l*Q,
+// and keep the exponents (bits 14..7) as follows.
+// The 12-bit form:
+//   N / 2 bytes  4-bit offsets from the chunk's base, base = max(0, largest
+//                exponent - 14), offset 15 marking an escape; lane l's at
+//                N + l*Q/2, value q in bits 4*(q % 8) of word q / 8;
 //   4 B each     the escapes: (value index << 8) | exponent, for values whose
 //                exponent lies below the base (zeros, tiny values), in index
-//                order,
-// in the chunk's own slot of the host buffer; a chunk with more than 64
-// escapes (or NaN / Inf, whose exponent 255 moves the base) stays raw.  Lane
-// l of a chunk's wave owns values l*Q .. l*Q+Q-1 (Q = N / 64): its Q bytes at
-// l*Q, its Q nibbles (value q in bits 4*(q % 8) of word q / 8) at N + l*Q/2.
-// The chunk's code word (device memory) says which: bit 31 set = coded, with
-// the escape count in bits 16..23 and the base in bits 0..7; 0 = raw.
+//                order, from N + N/2.
+// The class form (about 10.6 bits a value on normally distributed values,
+// whose exponents cluster a little below the chunk's largest): with
+// top = max(largest exponent - 1, 0),
+//   N / 4 bytes  2-bit classes: 0, 1, 2 = exponent top, top - 1, top - 2;
+//                3 = in the side stream; lane l's at N + l*Q/4, value q in
+//                bits 2*(q % 16) of word q / 16;
+//   S bytes      the side stream, from N + N/4: a 3-bit code for each value of
+//                class 3, in value order, code i in bits 3i .. 3i+2 (bit 0 of
+//                byte 0 first): 0 = exponent top + 1, x in 1..6 = top - 2 - x,
+//                7 = an escape; S = ceil(3 * count / 8) rounded up to 4;
+//   4 B each     the escapes, as above, from N + N/4 + S.
+// A chunk that takes neither form within 64 escapes (NaN and Inf, whose
+// exponent 255 moves the window, or a spread of magnitudes) stays raw.  The
+// chunk's code word (device memory) says which: 0 = raw; bit 31 alone = the
+// 12-bit form, escape count in bits 16..23, base in bits 0..7; bits 31 and 30
+// = the class form, S / 4 in bits 20..27, escape count in bits 8..15, top in
+// bits 0..7.
 // ---------------------------------------------------------------------------
 template <int Q>
 __global__ __launch_bounds__(256) void vcode_kernel(const uint16_t *__restrict__ v, uint8_t *__restrict__ out,
-                                                    uint32_t *__restrict__ code, long long nchunks) {
+                                                    uint32_t *__restrict__ code, long long nchunks, int forms) {
     constexpr int N = 64 * Q;
-    const int lane = threadIdx.x & 63;
+    constexpr int SW = (3 * N / 8 + 3) / 4 + 4;  // side-stream words per wave (with slack)
+    __shared__ uint32_t s_side[4][SW];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t *side = s_side[wave];
     const long long nw = static_cast<long long>(gridDim.x) * 4;
-    for (long long ch = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6); ch < nchunks; ch += nw) {
+    for (long long ch = static_cast<long long>(blockIdx.x) * 4 + wave; ch < nchunks; ch += nw) {
         // this lane's Q values (2Q bytes: Q / 8 16-byte loads)
         const u32x4 *src = reinterpret_cast<const u32x4 *>(v + ch * N) + lane * (Q / 8);
         uint32_t w[Q / 2];
@@ -334,58 +354,121 @@ __global__ __launch_bounds__(256) void vcode_kernel(const uint16_t *__restrict__
             const u32x4 t = src[u];
             w[4 * u] = t[0]; w[4 * u + 1] = t[1]; w[4 * u + 2] = t[2]; w[4 * u + 3] = t[3];
         }
+        auto expo = [&](int q) { return static_cast<int>((w[q >> 1] >> (16 * (q & 1) + 7)) & 0xffu); };
         int emax = 0;
 #pragma unroll
-        for (int q = 0; q < Q; ++q) emax = max(emax, static_cast<int>((w[q >> 1] >> (16 * (q & 1) + 7)) & 0xffu));
+        for (int q = 0; q < Q; ++q) emax = max(emax, expo(q));
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) emax = max(emax, __shfl_xor(emax, off, 64));
-        const int base = max(0, emax - 14);
-        int nesc_lane = 0;
+        const int base = max(0, emax - 14), top = max(emax - 1, 0);
+        // per value: 12-bit escape; class-form class and side code
+        auto side_code = [&](int e) {  // 3-bit code of a class-3 exponent
+            const int d = top - e;
+            return e == top + 1 ? 0 : (d >= 3 && d <= 8 ? d - 2 : 7);
+        };
+        int esc12 = 0, n3 = 0, esc2 = 0;
 #pragma unroll
-        for (int q = 0; q < Q; ++q)
-            nesc_lane += static_cast<int>((w[q >> 1] >> (16 * (q & 1) + 7)) & 0xffu) < base ? 1 : 0;
-        int incl = nesc_lane;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int t = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += t;
+        for (int q = 0; q < Q; ++q) {
+            const int e = expo(q), d = top - e;
+            esc12 += e < base ? 1 : 0;
+            if (d < 0 || d > 2) {
+                ++n3;
+                esc2 += side_code(e) == 7 ? 1 : 0;
+            }
         }
-        const int nesc = __shfl(incl, 63, 64);
+        const int i12 = wave_incl_scan(esc12), i3 = wave_incl_scan(n3), i2 = wave_incl_scan(esc2);
+        const int nesc12 = __builtin_amdgcn_readlane(i12, 63), n3t = __builtin_amdgcn_readlane(i3, 63),
+                  nesc2 = __builtin_amdgcn_readlane(i2, 63);
+        const int S = (3 * n3t + 31) / 32 * 4;
+        const int size12 = (forms & 1) && nesc12 <= 64 ? 3 * N / 2 + 4 * nesc12 : 1 << 30;
+        const int size2 =
+            (forms & 2) && nesc2 <= 64 && N + N / 4 + S + 4 * nesc2 <= 2 * N ? N + N / 4 + S + 4 * nesc2 : 1 << 30;
         uint8_t *dst = out + ch * 2 * N;
-        if (nesc > 64) {  // stays raw
+        if (size12 >= (1 << 30) && size2 >= (1 << 30)) {  // stays raw
             u32x4 *d4 = reinterpret_cast<u32x4 *>(dst) + lane * (Q / 8);
 #pragma unroll
             for (int u = 0; u < Q / 8; ++u) d4[u] = u32x4{w[4 * u], w[4 * u + 1], w[4 * u + 2], w[4 * u + 3]};
             if (lane == 0) code[ch] = 0u;
             continue;
         }
-        uint32_t bw[Q / 4], nw4[Q / 8];
+        // sign and mantissa bytes (both forms)
+        uint32_t bw[Q / 4];
 #pragma unroll
         for (int i = 0; i < Q / 4; ++i) bw[i] = 0u;
 #pragma unroll
-        for (int i = 0; i < Q / 8; ++i) nw4[i] = 0u;
-        int slot = incl - nesc_lane;  // this lane's first escape entry
-#pragma unroll
         for (int q = 0; q < Q; ++q) {
             const uint32_t x = (w[q >> 1] >> (16 * (q & 1))) & 0xffffu;
-            const int e = static_cast<int>((x >> 7) & 0xffu);
-            const uint32_t byte = ((x >> 8) & 0x80u) | (x & 0x7fu);
-            const bool esc = e < base;
-            bw[q >> 2] |= byte << (8 * (q & 3));
-            nw4[q >> 3] |= static_cast<uint32_t>(esc ? 15 : e - base) << (4 * (q & 7));
-            if (esc) {
-                reinterpret_cast<uint32_t *>(dst + 3 * N / 2)[slot] =
-                    (static_cast<uint32_t>(lane * Q + q) << 8) | static_cast<uint32_t>(e);
-                ++slot;
-            }
+            bw[q >> 2] |= (((x >> 8) & 0x80u) | (x & 0x7fu)) << (8 * (q & 3));
         }
         uint32_t *bp = reinterpret_cast<uint32_t *>(dst) + lane * (Q / 4);
 #pragma unroll
         for (int i = 0; i < Q / 4; ++i) bp[i] = bw[i];
-        uint32_t *np = reinterpret_cast<uint32_t *>(dst + N) + lane * (Q / 8);
+        if (size2 < size12) {
+            // the class form: classes, side stream (built in LDS), escapes
+            uint32_t cw[(Q + 15) / 16];
 #pragma unroll
-        for (int i = 0; i < Q / 8; ++i) np[i] = nw4[i];
-        if (lane == 0) code[ch] = 0x80000000u | (static_cast<uint32_t>(nesc) << 16) | static_cast<uint32_t>(base);
+            for (int i = 0; i < (Q + 15) / 16; ++i) cw[i] = 0u;
+            for (int i = lane; i < SW; i += 64) side[i] = 0u;
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            int pos = 3 * (i3 - n3);   // this lane's first side-stream bit
+            int slot = i2 - esc2;      // this lane's first escape entry
+            uint32_t *ep = reinterpret_cast<uint32_t *>(dst + N + N / 4 + S);
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const int e = expo(q), d = top - e;
+                const int c = d >= 0 && d <= 2 ? d : 3;
+                cw[q >> 4] |= static_cast<uint32_t>(c) << (2 * (q & 15));
+                if (c == 3) {
+                    const int x = side_code(e);
+                    // a code may straddle two words
+                    atomicOr(&side[pos >> 5], static_cast<uint32_t>(x) << (pos & 31));
+                    if ((pos & 31) > 29) atomicOr(&side[(pos >> 5) + 1], static_cast<uint32_t>(x) >> (32 - (pos & 31)));
+                    pos += 3;
+                    if (x == 7) {
+                        ep[slot] = (static_cast<uint32_t>(lane * Q + q) << 8) | static_cast<uint32_t>(e);
+                        ++slot;
+                    }
+                }
+            }
+            if constexpr (Q == 8) {
+                reinterpret_cast<uint16_t *>(dst + N)[lane] = static_cast<uint16_t>(cw[0]);
+            } else {
+                uint32_t *cp = reinterpret_cast<uint32_t *>(dst + N) + lane * (Q / 16);
+#pragma unroll
+                for (int i = 0; i < Q / 16; ++i) cp[i] = cw[i];
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            uint32_t *sp = reinterpret_cast<uint32_t *>(dst + N + N / 4);
+            for (int i = lane; i < S / 4; i += 64) sp[i] = side[i];
+            if (lane == 0)
+                code[ch] = 0xC0000000u | (static_cast<uint32_t>(S / 4) << 20) | (static_cast<uint32_t>(nesc2) << 8) |
+                           static_cast<uint32_t>(top);
+        } else {
+            // the 12-bit form: offsets and escapes
+            uint32_t nw4[Q / 8];
+#pragma unroll
+            for (int i = 0; i < Q / 8; ++i) nw4[i] = 0u;
+            int slot = i12 - esc12;  // this lane's first escape entry
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const int e = expo(q);
+                const bool esc = e < base;
+                nw4[q >> 3] |= static_cast<uint32_t>(esc ? 15 : e - base) << (4 * (q & 7));
+                if (esc) {
+                    reinterpret_cast<uint32_t *>(dst + 3 * N / 2)[slot] =
+                        (static_cast<uint32_t>(lane * Q + q) << 8) | static_cast<uint32_t>(e);
+                    ++slot;
+                }
+            }
+            uint32_t *np = reinterpret_cast<uint32_t *>(dst + N) + lane * (Q / 8);
+#pragma unroll
+            for (int i = 0; i < Q / 8; ++i) np[i] = nw4[i];
+            if (lane == 0) code[ch] = 0x80000000u | (static_cast<uint32_t>(nesc12) << 16) | static_cast<uint32_t>(base);
+        }
     }
 }
 
@@ -394,22 +477,22 @@ int vcode_values(const Dims &dm) {
     return dm.bf16 && (N == 512 || N == 1024 || N == 2048) ? N : 0;
 }
 
-hipError_t launch_vcode(const Dims &dm, const void *v, void *out, uint32_t *code, long long nchunks,
+hipError_t launch_vcode(const Dims &dm, int forms, const void *v, void *out, uint32_t *code, long long nchunks,
                         hipStream_t st) {
     if (nchunks <= 0) return hipSuccess;
     const int blocks = static_cast<int>(std::min<long long>((nchunks + 3) / 4, 8192));
     switch (vcode_values(dm)) {
         case 512:
             hipLaunchKernelGGL(vcode_kernel<8>, dim3(blocks), dim3(256), 0, st, static_cast<const uint16_t *>(v),
-                               static_cast<uint8_t *>(out), code, nchunks);
+                               static_cast<uint8_t *>(out), code, nchunks, forms);
             break;
         case 1024:
             hipLaunchKernelGGL(vcode_kernel<16>, dim3(blocks), dim3(256), 0, st, static_cast<const uint16_t *>(v),
-                               static_cast<uint8_t *>(out), code, nchunks);
+                               static_cast<uint8_t *>(out), code, nchunks, forms);
             break;
         case 2048:
             hipLaunchKernelGGL(vcode_kernel<32>, dim3(blocks), dim3(256), 0, st, static_cast<const uint16_t *>(v),
-                               static_cast<uint8_t *>(out), code, nchunks);
+                               static_cast<uint8_t *>(out), code, nchunks, forms);
             break;
         default:
             return hipErrorInvalidValue;

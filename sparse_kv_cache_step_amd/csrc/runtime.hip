@@ -231,6 +231,7 @@ struct skv_layer {
     // form the prefill wrote, see prefill.hip); vcoded: the prefill codes
     uint32_t *vcode = nullptr;
     bool vcoded = false;
+    int vforms = 3;  // coded forms the prefill may pick: bit 0 the 12-bit form, bit 1 the class form
     bool ready = false;
     // shared per-device streams for the host-V fetch and the key rebuild
     hipStream_t copy = nullptr, comp = nullptr;
@@ -239,7 +240,7 @@ struct skv_layer {
     // work: the counters and timings are read after it, so reading them waits
     // for this layer's work only
     hipEvent_t ev_done = nullptr;
-    int fetch_waves = 128;
+    int fetch_waves = 256;
     int score_wgs = 0;  // workgroups of the scoring kernel (0: two tiles per wave)
     int n_app = 0;      // decode tokens appended to the local block since the last prefill / load
     // bfloat16 on one queue: rebuild, logits and PV in one fused launch
@@ -457,10 +458,14 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
     // or 1 forces the separate QK + PV kernels or the fused one
     ly->fused = dm.bf16 != 0;
     if (const char *e = std::getenv("SKV_ATTN_FUSED")) ly->fused = dm.bf16 != 0 && std::atoi(e) != 0;
-    // host V crosses PCIe in its 12-bit form where the chunks allow it;
-    // SKV_HOST_V_CODE=0 keeps it raw
+    // host V crosses PCIe in a coded form where the chunks allow it;
+    // SKV_HOST_V_CODE=0 keeps it raw, 1 allows only the 12-bit form
     ly->vcoded = skv::vcode_values(dm) > 0;
-    if (const char *e = std::getenv("SKV_HOST_V_CODE")) ly->vcoded = ly->vcoded && std::atoi(e) != 0;
+    if (const char *e = std::getenv("SKV_HOST_V_CODE")) {
+        const int f = std::atoi(e);
+        ly->vcoded = ly->vcoded && f != 0;
+        ly->vforms = f == 1 ? 1 : 3;  // 1: the 12-bit form only
+    }
 
     const size_t B = dm.b, HKV = dm.hkv, HQ = dm.hq, D = dm.d, S = dm.s, E = dm.esize;
     const size_t bh = B * HKV;
@@ -566,9 +571,11 @@ int shadowkv_layer_create(const skv_config *cfg, skv_layer **out) {
         hipEventCreateWithFlags(&ly->ev_done, hipEventDisableTiming) != hipSuccess)
         return bail(fail(SKV_E_HIP, "creating events failed"));
 
-    // Host-V fetch: enough waves to keep PCIe busy (a few hundred 2 KB chunk
-    // reads in flight), not so many that the slow host reads crowd the memory
-    // path of the kernels running beside them.  SKV_FETCH_WAVES overrides the
+    // Host-V fetch: enough waves to keep PCIe busy (a few hundred chunk reads
+    // in flight while waves decode the coded forms), not so many that the
+    // slow host reads crowd the memory path of the kernels running beside
+    // them (measured, 128K b8 with the class form: 128 waves 43.4 GB/s of
+    // coded bytes, 256 52.4, 512 50.7, 1024 52.2).  SKV_FETCH_WAVES overrides the
     // default for tuning.
     if (const char *e = std::getenv("SKV_FETCH_WAVES")) ly->fetch_waves = std::max(4, std::atoi(e));
 
@@ -617,7 +624,7 @@ int shadowkv_prefill_meta(skv_layer *ly, const void *k_pre, const void *k_rope, 
         const long long cb = 2LL * skv::vcode_values(dm), per = static_cast<long long>(kStageBytes) / cb;
         for (long long c0 = 0; c0 < nchunks; c0 += per) {
             const long long cnt = std::min(per, nchunks - c0);
-            SKV_HIP(skv::launch_vcode(dm, static_cast<const char *>(v) + c0 * cb, stage, ly->vcode + c0, cnt,
+            SKV_HIP(skv::launch_vcode(dm, ly->vforms, static_cast<const char *>(v) + c0 * cb, stage, ly->vcode + c0, cnt,
                                       ly->copy));
             SKV_HIP(hipMemcpyAsync(static_cast<char *>(v_host) + c0 * cb, stage, static_cast<size_t>(cnt * cb),
                                    hipMemcpyDeviceToHost, ly->copy));

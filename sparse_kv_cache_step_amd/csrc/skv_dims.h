@@ -63,7 +63,9 @@ hipError_t launch_fill_i32(int32_t *p, int32_t value, size_t count, hipStream_t 
 // nchunks chunks of v (raw, contiguous) into out (2N bytes each, coded or
 // raw) and each chunk's code word.
 int vcode_values(const Dims &dm);
-hipError_t launch_vcode(const Dims &dm, const void *v, void *out, uint32_t *code, long long nchunks, hipStream_t st);
+// forms: bit 0 allows the 12-bit form, bit 1 the class form.
+hipError_t launch_vcode(const Dims &dm, int forms, const void *v, void *out, uint32_t *code, long long nchunks,
+                        hipStream_t st);
 hipError_t launch_validate_outliers(const Dims &dm, const int32_t *outliers, int32_t *bad, hipStream_t st);
 // Decode-token append: rotate the new key (pre-RoPE, (b, h_kv, d)) at `pos`
 // and write it and its value to row `row` of the local buffers.

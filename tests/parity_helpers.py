@@ -113,11 +113,67 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
     return 2.0 ** (np.floor(np.log2(ax)) - 7)
 
 
+def decode_host_v_chunks(chunks: np.ndarray, code: np.ndarray, N: int) -> np.ndarray:
+    """Stored bfloat16 bits (uint16, (count, N)) of host-V chunk slots
+    (uint8, (count, 2N)) in the forms their code words name, as the header
+    documents under shadowkv_prefill_meta: 0 raw; bit 31 alone the 12-bit
+    form (bytes of sign and mantissa, 4-bit exponent offsets from the base in
+    bits 0..7, escapes counted in bits 16..23); bits 31 and 30 the class form
+    (2-bit classes from top in bits 0..7, a 3-bit side stream of S = 4 x bits
+    20..27 bytes, escapes counted in bits 8..15).  Lane l of 64 owns values
+    l*Q .. l*Q+Q-1, Q = N / 64."""
+    code = code.astype(np.int64) & 0xffffffff
+    out = np.ascontiguousarray(chunks).view(np.uint16).reshape(-1, N).copy()  # raw chunks as they are
+    Q = N // 64
+    byte = chunks[:, :N].astype(np.uint32)
+    sign_mant = ((byte & 0x80) << 8) | (byte & 0x7f)
+    f12 = np.flatnonzero((code & 0xC0000000) == 0x80000000)
+    if f12.size:
+        nib = chunks[f12, N:N + N // 2]
+        off = np.empty((f12.size, N), dtype=np.uint32)
+        off[:, 0::2] = nib & 0xf
+        off[:, 1::2] = nib >> 4
+        e = ((code[f12] & 0xff).astype(np.uint32)[:, None] + off) & 0xff
+        vals = sign_mant[f12] | (e << 7)
+        nesc = (code[f12] >> 16) & 0xff
+        for i in np.flatnonzero(nesc):
+            ent = chunks[f12[i], 3 * N // 2:3 * N // 2 + 4 * int(nesc[i])].copy().view(np.uint32)
+            idx = (ent >> 8).astype(np.int64)
+            vals[i, idx] = (vals[i, idx] & 0x807f) | ((ent & 0xff) << 7)
+        out[f12] = vals.astype(np.uint16)
+    fc = np.flatnonzero((code & 0xC0000000) == 0xC0000000)
+    for i in fc:
+        cw, row = int(code[i]), chunks[i]
+        top, nesc, S = cw & 0xff, (cw >> 8) & 0xff, ((cw >> 20) & 0xff) * 4
+        # classes: value q (lane-major) in bits 2*(q % 4) of byte q // 4
+        cb = row[N:N + N // 4]
+        cls = np.stack([(cb >> (2 * j)) & 3 for j in range(4)], axis=1).reshape(N).astype(np.int64)
+        e = top - cls
+        sel = np.flatnonzero(cls == 3)  # value order
+        bits = np.unpackbits(row[N + N // 4:N + N // 4 + S], bitorder="little")
+        for m, v in enumerate(sel):
+            xc = int(bits[3 * m]) | (int(bits[3 * m + 1]) << 1) | (int(bits[3 * m + 2]) << 2)
+            e[v] = top + 1 if xc == 0 else top - 2 - xc  # 7: an escape, set below
+        ent = row[N + N // 4 + S:N + N // 4 + S + 4 * nesc].copy().view(np.uint32)
+        e[(ent >> 8).astype(np.int64)] = ent & 0xff
+        out[i] = (sign_mant[i] | ((e.astype(np.uint32) & 0xff) << 7)).astype(np.uint16)
+    return out
+
+
+def host_v_form(code: int):
+    """(form, escapes) of a host-V chunk's code word: ("raw", 0),
+    ("12-bit", n) or ("class", n)."""
+    code = int(code) & 0xffffffff
+    if (code & 0xC0000000) == 0xC0000000:
+        return "class", (code >> 8) & 0xff
+    if code & 0x80000000:
+        return "12-bit", (code >> 16) & 0xff
+    return "raw", 0
+
+
 def decode_host_v(hb, codes: np.ndarray, wl) -> np.ndarray:
     """The pinned host V buffer of a prefilled layer as stored values, each
-    chunk decoded from the form its code word names: raw, or the 12-bit form
-    the header documents under shadowkv_prefill_meta (bytes of sign and
-    mantissa, 4-bit exponent offsets from the chunk's base, 4-byte escapes).
+    chunk decoded from the form its code word names (decode_host_v_chunks).
     Returns the raw bits: uint16 (bfloat16) or uint32 (binary32), shaped
     (b, h_kv, s, d)."""
     import torch
@@ -127,27 +183,7 @@ def decode_host_v(hb, codes: np.ndarray, wl) -> np.ndarray:
     if not wl.bf16:
         return raw.view(np.uint32).reshape(b, h, s, d)
     N = c * d
-    chunks = raw.reshape(-1, 2 * N)
-    out = chunks.view(np.uint16).copy()  # raw chunks as they are
-    code = codes.reshape(-1).astype(np.int64) & 0xffffffff
-    coded = np.flatnonzero(code & 0x80000000)
-    if coded.size:
-        cb = chunks[coded]
-        byte = cb[:, :N].astype(np.uint32)
-        nib = cb[:, N:N + N // 2]
-        off = np.empty((coded.size, N), dtype=np.uint32)
-        off[:, 0::2] = nib & 0xf
-        off[:, 1::2] = nib >> 4
-        base = (code[coded] & 0xff).astype(np.uint32)[:, None]
-        e = (base + off) & 0xff
-        vals = ((byte & 0x80) << 8) | (e << 7) | (byte & 0x7f)
-        nesc = (code[coded] >> 16) & 0xff
-        for i in np.flatnonzero(nesc):
-            ent = cb[i, 3 * N // 2:3 * N // 2 + 4 * int(nesc[i])].view(np.uint32)
-            idx = (ent >> 8).astype(np.int64)
-            vals[i, idx] = (vals[i, idx] & 0x807f) | ((ent & 0xff) << 7)
-        out[coded] = vals.astype(np.uint16)
-    return out.reshape(b, h, s, d)
+    return decode_host_v_chunks(raw.reshape(-1, 2 * N), codes.reshape(-1), N).reshape(b, h, s, d)
 
 
 def bits_of(x: np.ndarray, bf16: bool) -> np.ndarray:

@@ -16,8 +16,8 @@ import pytest
 import torch
 
 import oracle
-from parity_helpers import (OUT_TOL, SHARP_32K, bf16_ulp, bits_of, check_outliers, check_selection, decode_host_v,
-                            layer_kwargs, log, oracle_shape, tdtype, to_dev, to_np)
+from parity_helpers import (bf16_ulp, bits_of, check_outliers, check_selection, decode_host_v, host_v_form,
+                            layer_kwargs, log, oracle_shape, OUT_TOL, SHARP_32K, tdtype, to_dev, to_np)
 from sparse_kv_cache_step_amd import binding as skv
 from sparse_kv_cache_step_amd import synth
 
@@ -743,12 +743,14 @@ def test_selection_paths_match_oracle(case, cand, monkeypatch):
 
 
 def test_host_v_coding_edge_chunks():
-    """Host V's 12-bit form on chunks made to test it, every selectable chunk
-    fetched (full budget): zeros (coded, no escapes), 10 and 64 values below
-    the exponent window (coded with escapes), 65 such values, a NaN and an
-    Inf, and values over 2^-100 .. 2^100 (raw).  The host buffer decodes to V
-    bit for bit, each chunk's code word says the expected form, and after a
-    decode step the resident cache holds every chunk's V bit for bit."""
+    """Host V's coded forms on chunks made to test them, every selectable
+    chunk fetched (full budget): zeros (coded, no escapes), 10 and 64 values
+    far below the chunk's largest (coded, with at least that many escapes),
+    65 such values, a NaN and an Inf, and values over 2^-100 .. 2^100 (raw);
+    the other chunks, normally distributed, take the class form.  The host
+    buffer decodes to V bit for bit, each chunk's code word says the expected
+    form and its coded bytes fit the chunk's slot, and after a decode step the
+    resident cache holds every chunk's V bit for bit."""
     wl = synth.LLAMA_32K.with_(h_q=8, h_kv=2, s=1024, o=4, k=120, w=32, steps=1, rho=0.9)
     k_pre, v, qs = synth.k_pre_numpy(wl), synth.v_numpy(wl), synth.queries_numpy(wl)
     rng = np.random.default_rng(11)
@@ -781,12 +783,21 @@ def test_host_v_coding_edge_chunks():
     np.testing.assert_array_equal(decode_host_v(hb, codes, wl), bits_of(v2, True))
     for (bi, hh, ch), want in special.items():
         cw = int(codes[bi, hh, ch])
+        form, nesc = host_v_form(cw)
         if want < 0:
-            assert cw == 0, f"chunk {(bi, hh, ch)} should stay raw, code {cw:#x}"
+            assert form == "raw", f"chunk {(bi, hh, ch)} should stay raw, code {cw:#x}"
         else:
-            assert cw & 0x80000000 and ((cw >> 16) & 0xff) == want, f"chunk {(bi, hh, ch)}: code {cw:#x}"
-    coded = float(np.mean((codes & 0x80000000) != 0))
-    log(f"[host-v-coding] coded chunks {coded:.3f}; special chunks as expected")
+            assert form != "raw" and nesc >= want, f"chunk {(bi, hh, ch)}: code {cw:#x}"
+    forms = [host_v_form(cw) for cw in codes.reshape(-1)]
+    for cw, (form, nesc) in zip(codes.reshape(-1), forms):
+        size = {"raw": 2 * N, "12-bit": 3 * N // 2 + 4 * nesc,
+                "class": N + N // 4 + 4 * ((int(cw) >> 20) & 0xff) + 4 * nesc}[form]
+        assert size <= 2 * N and nesc <= 64
+    plain = [forms[i][0] for i in range(len(forms))
+             if np.unravel_index(i, codes.shape) not in special]
+    frac = {f: plain.count(f) / len(plain) for f in ("class", "12-bit", "raw")}
+    log(f"[host-v-coding] forms of the normally distributed chunks: {frac}; special chunks as expected")
+    assert frac["class"] >= 0.9
     out = torch.empty_like(to_dev(qs[0], dt))
     layer.decode_step(to_dev(qs[0], dt), out)
     torch.cuda.synchronize()
