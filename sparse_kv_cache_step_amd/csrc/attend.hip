@@ -34,8 +34,9 @@ __global__ __launch_bounds__(256) void fetch_kernel(const u32x4 *__restrict__ v_
     extern __shared__ int pre[];  // rows + 1 prefix sums
     __shared__ int wsum[4];
     // per wave: a class-form chunk's side stream (up to 3N/8 bytes, with slack)
-    constexpr int SW = VPL > 0 ? (3 * 512 * VPL / 8) / 4 + 8 : 1;
-    __shared__ uint32_t s_side[4][SW];
+    // (rows of whole 16-byte words: 3N/8 bytes is a multiple of 16)
+    constexpr int SW = VPL > 0 ? (3 * 512 * VPL / 8) / 4 + 8 : 4;
+    __shared__ __align__(16) uint32_t s_side[4][SW];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int carry = 0;
     for (int base = 0; base < rows; base += 256) {
@@ -462,7 +463,7 @@ __global__ __launch_bounds__(256) void qk_mfma_kernel(const uint16_t *__restrict
     constexpr int NP = NB / 2;      // 32-dim pairs of blocks (logit MFMA steps)
     constexpr int MB = 4;           // 16-key blocks per wave
     constexpr int STG = D / 8;      // B staging vectors per thread (r_pad <= 256)
-    extern __shared__ uint16_t dyn[];
+    extern __shared__ __align__(16) uint16_t dyn[];
     uint16_t *Bs = dyn;             // D x (r_pad + 8)
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, quad = lane >> 4;
@@ -662,7 +663,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     constexpr int PW = 84;                          // LDS row of one head's 80 weights
     constexpr int RP = D + 2;                       // merge record of one head: D sums, max, sum
     constexpr int RGN = GP * (PW > RP ? PW : RP);   // LDS floats of one wave
-    extern __shared__ uint16_t dyn[];
+    extern __shared__ __align__(16) uint16_t dyn[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int row = lane & 15, quad = lane >> 4;
     // logits in base-2 units (log2(e) folded into the scale), so the softmax
