@@ -559,7 +559,7 @@ __device__ __forceinline__ void radix_topk_regs(uint32_t *keys, int n, int k, ui
 // keys per thread of the register form for a row of n keys (0: rows longer
 // than 1024 x 32 keep radix_topk)
 __host__ __device__ constexpr int select_kpt(int n) {
-    return n <= 8192 ? 8 : (n <= 16384 ? 16 : (n <= 32768 ? 32 : 0));
+    return n <= 4096 ? 4 : (n <= 8192 ? 8 : (n <= 16384 ? 16 : (n <= 32768 ? 32 : 0)));
 }
 
 // Outlier selection for the prefill: the o chunks with the lowest minimum
@@ -717,7 +717,7 @@ __global__ __launch_bounds__(256) void group_kernel(const float *__restrict__ U,
 // key, or equal key and lower index), hence fewer than k of its own slice.
 // The select kernel then ranks the union (slices x k keys) instead of all n.
 // ---------------------------------------------------------------------------
-template <int GP>
+template <int GP, int KPT>
 __global__ __launch_bounds__(kSelectThreads) void group_topk_kernel(
     const float *__restrict__ U, const float2 *__restrict__ stats, const uint32_t *__restrict__ cand,
     int mask_words, float *__restrict__ S2, uint32_t *__restrict__ cand_key, int32_t *__restrict__ cand_idx,
@@ -792,6 +792,8 @@ __global__ __launch_bounds__(kSelectThreads) void group_topk_kernel(
             if (valid) { kmn = min(kmn, key); kmx = max(kmx, key); ++nvalid; }
         }
     }
+    if constexpr (KPT > 0)  // the register form reads 1024 x KPT (= SL) keys
+        for (int i = cnt + tid; i < SL; i += nt) keys[i] = 0u;
     int tv, zero = 0, tz;
     block_scan2(nvalid, zero, sc, &tv, &tz);
     block_minmax(kmn, kmx, sc);  // its barriers also publish the keys
@@ -799,7 +801,8 @@ __global__ __launch_bounds__(kSelectThreads) void group_topk_kernel(
     int32_t *out = cand_idx + (static_cast<size_t>(bh) * slices + sl) * k;
     if (kl > 0) {
         // 4. the slice's Top-K (radix selection over the slice's keys)
-        radix_topk(keys, cnt, kl, kmn, kmx, nullptr, s_pos, sc);
+        if constexpr (KPT > 0) radix_topk_regs<KPT, false>(keys, cnt, kl, kmn, kmx, s_pos, sc);
+        else radix_topk(keys, cnt, kl, kmn, kmx, nullptr, s_pos, sc);
         __syncthreads();
         uint32_t *ok = cand_key + (static_cast<size_t>(bh) * slices + sl) * k;
         for (int i = tid; i < kl; i += nt) {
@@ -954,13 +957,13 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
     // they fit, or the candidates (keys, then their chunks)
     const uint32_t *krow = keys_g + static_cast<size_t>(bh) * n;
     // key entries held in LDS (the register form pads the row with zeros to 1024 x KPT)
-    const int kcap = CAND ? cslices * k : (KPT > 0 ? kSelectThreads * KPT : (use_lds ? n : 0));
+    const int kcap = KPT > 0 ? kSelectThreads * KPT : (CAND ? cslices * k : (use_lds ? n : 0));
     // keys in LDS are reached through dyn itself (never through a pointer
     // that may also be global), so their accesses compile to LDS instructions
     const bool lds_keys = CAND || use_lds;
     uint32_t *keys = dyn;
-    int32_t *s_ci = reinterpret_cast<int32_t *>(dyn + kcap);  // CAND: the chunk of each candidate
-    int32_t *s_sel = s_ci + (CAND ? kcap : 0);           // k selected chunks, ascending
+    int32_t *s_ci = reinterpret_cast<int32_t *>(dyn + kcap);  // CAND: the chunk of each of cslices * k candidates
+    int32_t *s_sel = s_ci + (CAND ? cslices * k : 0);    // k selected chunks, ascending
     int32_t *s_sslot = s_sel + k;                       // k: slot of selected chunk i (-1: missing)
     int32_t *s_rank = s_sslot + k;                      // k: index in s_sel of the m-th miss
     uint32_t *s_age = reinterpret_cast<uint32_t *>(s_rank + k);  // cap: eviction key (0: not evictable)
@@ -1029,8 +1032,8 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
         }
         }
     }
-    if constexpr (KPT > 0)
-        for (int j = n + tid; j < kcap; j += nt) dyn[j] = 0u;
+    if constexpr (KPT > 0)  // the register form reads kcap keys: zeros past the row (or the candidates)
+        for (int j = nkeys + tid; j < kcap; j += nt) dyn[j] = 0u;
     for (int i = tid; i < 4096; i += nt) sc.hist[i] = 0;
     for (int i = tid; i < k; i += nt) s_sslot[i] = -1;
     block_minmax(kmn, kmx, sc);  // its barriers also publish the keys
@@ -1045,7 +1048,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
     // for a load also waits for every earlier store, so the kernel's global
     // stores all come after its last global load
     int32_t *srow = sel + static_cast<size_t>(bh) * k;
-    if constexpr (KPT > 0) radix_topk_regs<KPT, true>(dyn, nkeys, k, kmn, kmx, s_sel, sc);
+    if constexpr (KPT > 0) radix_topk_regs<KPT, !CAND>(dyn, nkeys, k, kmn, kmx, s_sel, sc);
     else if (lds_keys) radix_topk(dyn, nkeys, k, kmn, kmx, nullptr, s_sel, sc);
     else radix_topk(krow, nkeys, k, kmn, kmx, nullptr, s_sel, sc);
     __syncthreads();
@@ -1068,7 +1071,7 @@ __global__ __launch_bounds__(kSelectThreads) void select_kernel(
         if (c >= 0) {
             ++nres;
             int lo = 0, hi = k;
-            if constexpr (KPT > 0) {
+            if constexpr (KPT > 0 && !CAND) {
                 // the selection marked its chunks' keys with position + 1
                 const uint32_t mk = c < n ? dyn[c] : 0u;
                 lo = mk >= 1u && mk <= static_cast<uint32_t>(k) ? static_cast<int>(mk) - 1 : k;
@@ -1304,8 +1307,17 @@ size_t group_topk_lds(const Dims &dm) {
     return SL * sizeof(uint32_t) + static_cast<size_t>(dm.k) * sizeof(int32_t) + SL / 64 * dm.GP * sizeof(float);
 }
 
+static int select_cand_kpt(const Dims &dm) {
+    if (const char *e = std::getenv("SKV_SELECT_REGS"))
+        if (std::atoi(e) == 0) return 0;
+    return select_kpt(topk_slices(dm) * dm.k);
+}
+
 size_t select_cand_lds(const Dims &dm) {
-    return (2ull * topk_slices(dm) * dm.k + 3ull * dm.k + 2ull * dm.cap) * sizeof(int32_t);
+    const int kpt = select_cand_kpt(dm);
+    const size_t cs = static_cast<size_t>(topk_slices(dm)) * dm.k;
+    const size_t kent = kpt > 0 ? static_cast<size_t>(kSelectThreads) * kpt : cs;
+    return (kent + cs + 3ull * dm.k + 2ull * dm.cap) * sizeof(int32_t);
 }
 
 size_t select_static_lds() { return sizeof(SelectScratch); }
@@ -1399,10 +1411,24 @@ hipError_t launch_group_topk(const Dims &dm, const float *P, const float2 *stats
                            dm.k);
         return hipGetLastError();
     };
+    // the register form when a slice is exactly 1024 x KPT keys
+    int kpt = select_kpt(SL);
+    if (kpt == 0 || SL != kSelectThreads * kpt) kpt = 0;
+    if (const char *e = std::getenv("SKV_SELECT_REGS"))
+        if (std::atoi(e) == 0) kpt = 0;
+    auto by_kpt = [&](auto gp) {
+        constexpr int G4 = decltype(gp)::value;
+        switch (kpt) {
+            case 4: return go(group_topk_kernel<G4, 4>);
+            case 8: return go(group_topk_kernel<G4, 8>);
+            case 16: return go(group_topk_kernel<G4, 16>);
+            default: return go(group_topk_kernel<G4, 0>);
+        }
+    };
     switch (dm.GP) {
-        case 4: return go(group_topk_kernel<4>);
-        case 8: return go(group_topk_kernel<8>);
-        default: return go(group_topk_kernel<16>);
+        case 4: return by_kpt(std::integral_constant<int, 4>{});
+        case 8: return by_kpt(std::integral_constant<int, 8>{});
+        default: return by_kpt(std::integral_constant<int, 16>{});
     }
 }
 
@@ -1413,6 +1439,13 @@ hipError_t launch_select_cand(const Dims &dm, const uint32_t *cand_key, const in
     if (dm.k > 0 && dm.cap < dm.k) return hipErrorInvalidValue;
     const size_t lds = select_cand_lds(dm);
     auto kern = select_kernel<true, 0, 0>;
+    switch (select_cand_kpt(dm)) {
+        case 4: kern = select_kernel<true, 0, 4>; break;
+        case 8: kern = select_kernel<true, 0, 8>; break;
+        case 16: kern = select_kernel<true, 0, 16>; break;
+        case 32: kern = select_kernel<true, 0, 32>; break;
+        default: break;
+    }
     hipError_t e = allow_lds(reinterpret_cast<const void *>(kern), lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(dm.b * dm.hkv), dim3(kSelectThreads), lds, st, nullptr, nullptr, nullptr, 0,

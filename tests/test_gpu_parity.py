@@ -703,8 +703,9 @@ SELECT_CASES = {
 }
 
 
-# (SKV_SELECT_FUSED, SKV_SELECT_CAND) of each way to the ArgTopK
-SELECT_PATHS = {"fused": ("1", "0"), "row": ("0", "0"), "cand": ("0", "1")}
+# (SKV_SELECT_FUSED, SKV_SELECT_CAND, SKV_SELECT_REGS) of each way to the ArgTopK
+SELECT_PATHS = {"fused": ("1", "0", "1"), "row": ("0", "0", "1"), "cand": ("0", "1", "1"),
+                "row-lds": ("0", "0", "0"), "cand-lds": ("0", "1", "0")}
 
 
 @pytest.mark.parametrize("cand", list(SELECT_PATHS))
@@ -712,12 +713,14 @@ SELECT_PATHS = {"fused": ("1", "0"), "row": ("0", "0"), "cand": ("0", "1")}
 def test_selection_paths_match_oracle(case, cand, monkeypatch):
     """The ways to the ArgTopK, forced in turn: one pass over the whole row
     with the group score computed in the same kernel, the same after the group
-    kernel, and slice-local candidates merged by a second pass.  Each is
-    checked against the oracle's selection (exact or near-tie swaps) and
-    output, over several steps (the cache update)."""
+    kernel, and slice-local candidates merged by a second pass, with the keys
+    held in registers through the radix passes (the default) or read from LDS
+    each pass.  Each is checked against the oracle's selection (exact or
+    near-tie swaps) and output, over several steps (the cache update)."""
     wl = SELECT_CASES[case]
     monkeypatch.setenv("SKV_SELECT_FUSED", SELECT_PATHS[cand][0])
     monkeypatch.setenv("SKV_SELECT_CAND", SELECT_PATHS[cand][1])
+    monkeypatch.setenv("SKV_SELECT_REGS", SELECT_PATHS[cand][2])
     shape = oracle_shape(wl)
     k_pre, v, qs = synth.k_pre_numpy(wl), synth.v_numpy(wl), synth.queries_numpy(wl)
     meta = oracle.prefill(shape, k_pre, v)
