@@ -22,7 +22,13 @@ namespace skv {
 // after another), find each miss's row by binary search, and copy the missing
 // chunk (c * d elements, contiguous on both sides) from pinned host memory
 // into its cache slot, every load of the chunk in flight before the stores.
-// Only real misses are visited, so the PCIe reads are issued back to back.
+// A chunk stored in a coded form (its code word, see prefill.hip) is read in
+// that form and decoded in registers: the 12-bit form's exponents are offsets
+// from the chunk's base; the class form's are 2-bit classes below the chunk's
+// top plus, for class 3, 3-bit codes from a side stream that the wave stages
+// in LDS and each lane reads at its own bit position (a wave prefix sum of
+// the lanes' class-3 counts); escapes patch their values' exponents.  Only
+// real misses are visited, so the PCIe reads are issued back to back.
 // ---------------------------------------------------------------------------
 template <int VPL>  // 16-byte vectors per lane and chunk (0: any, looped)
 __global__ __launch_bounds__(256) void fetch_kernel(const u32x4 *__restrict__ v_host, u32x4 *__restrict__ vc,

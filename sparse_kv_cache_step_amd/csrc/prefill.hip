@@ -2,7 +2,7 @@
 // Algorithm 1 steps 2-5): RoPE of the pre-RoPE keys, chunk means
 // (landmarks), each chunk's minimum token-to-landmark cosine, the static
 // outlier / local-window buffers and the selectable-chunk bitmask; and the
-// 12-bit form in which host V crosses PCIe.
+// coded forms in which host V crosses PCIe.
 #include <algorithm>
 
 #include "skv_device.h"

@@ -227,7 +227,7 @@ struct skv_layer {
     int32_t *bad = nullptr;
     // host V
     void *v_host_dev = nullptr;
-    // (b, h_kv, n): each host V chunk's code word (0: raw; else the 12-bit
+    // (b, h_kv, n): each host V chunk's code word (0: raw; else which coded
     // form the prefill wrote, see prefill.hip); vcoded: the prefill codes
     uint32_t *vcode = nullptr;
     bool vcoded = false;
@@ -617,7 +617,7 @@ int shadowkv_prefill_meta(skv_layer *ly, const void *k_pre, const void *k_rope, 
     SKV_HIP(hipStreamWaitEvent(ly->copy, ly->ev_sel, 0));
     const long long nchunks = static_cast<long long>(dm.b) * dm.hkv * dm.n;
     if (ly->vcoded) {
-        // chunk by chunk into the 12-bit form, through the device's staging
+        // chunk by chunk into a coded form, through the device's staging
         // buffer, 64 MiB at a time (the chunks of V are contiguous)
         void *stage = nullptr;
         if ((rc = device_stage(ly->device, &stage))) return rc;

@@ -58,7 +58,7 @@ hipError_t launch_gather_static(const Dims &dm, const void *k_pre, const void *k
 hipError_t launch_cand_mask(const Dims &dm, const int32_t *outliers, uint32_t *cand, hipStream_t st);
 hipError_t launch_transpose_b(const Dims &dm, const void *B, void *Bt, hipStream_t st);
 hipError_t launch_fill_i32(int32_t *p, int32_t value, size_t count, hipStream_t st);
-// Host V's 12-bit form (prefill.hip): chunk values N when the layer's chunks
+// Host V's coded forms (prefill.hip): chunk values N when the layer's chunks
 // can take it (bfloat16, N in {512, 1024, 2048}), else 0; the encoder writes
 // nchunks chunks of v (raw, contiguous) into out (2N bytes each, coded or
 // raw) and each chunk's code word.

@@ -441,7 +441,7 @@ def test_snapkv_selection_matches_oracle(case):
         log(f"[snapkv-{case}] decode {t}: max|out - oracle| = {err:.3g}")
         assert err <= OUT_TOL[wl.bf16], f"decode {t}: max abs error {err}"
         st = layer.stats()
-        if t == 0:  # the one fetch: raw binary32, or bfloat16 in its 12-bit form where coded
+        if t == 0:  # the one fetch: raw binary32, or bfloat16 in its coded forms where coded
             assert 0 < st["bytes_h2d"] <= raw_bytes and (wl.bf16 or st["bytes_h2d"] == raw_bytes)
             st1 = st
         assert {k: st[k] for k in ("hits", "misses", "steps")} == {k: st0[k] for k in ("hits", "misses", "steps")}
