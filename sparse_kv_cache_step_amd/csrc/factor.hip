@@ -10,12 +10,17 @@
 //                        of M split into slices that each write a partial
 //   gram_sum_kernel      G = the slices' partials summed in slice order,
 //                        mirrored; the eigenvector accumulator set to I
-//   jacobi_rot_kernel    one round of the parallel two-sided Jacobi method:
-//                        for each of the round's n/2 disjoint index pairs the
-//                        plane rotation that zeroes the pair's off-diagonal
-//                        entry
-//   jacobi_apply_kernel  G <- R^T G R (one 2 x 2 block per thread)
-//   jacobi_vec_kernel    V <- V R
+//   the eigensolver, the parallel two-sided (cyclic) Jacobi method in one of
+//   two round forms:
+//     32-index super-blocks (n a multiple of 32, n >= 64; the default):
+//       jacobi_block_solve_kernel, jacobi_block_apply_kernel,
+//       jacobi_block_vec_kernel (described at their definitions)
+//     single index pairs:
+//       jacobi_rot_kernel    for each of the round's n/2 disjoint index pairs
+//                            the plane rotation that zeroes the pair's
+//                            off-diagonal entry
+//       jacobi_apply_kernel  G <- R^T G R (one 2 x 2 block per thread)
+//       jacobi_vec_kernel    V <- V R
 //   offdiag_kernel       off-diagonal and total squared sums (convergence)
 //   gather_b_kernel      W = the r leading eigenvectors, and B
 //   factor_a_kernel      A = M W, rounded once to the storage type
@@ -177,26 +182,33 @@ __global__ __launch_bounds__(256) void gram_sum_kernel(const double *__restrict_
     V[seq * nn + idx] = p == q ? 1.0 : 0.0;
 }
 
-// The rotation (c, s) of round position i: with a = G[2i][2i], b =
-// G[2i+1][2i+1], e = G[2i][2i+1], R = [[c, s], [-s, c]] makes the block of
-// R^T G R at the pair diagonal: t = s/c is the root of smaller magnitude of
-// t^2 + 2 theta t - 1 = 0, theta = (b - a) / (2e).  Entries negligible
-// against the diagonal (or zero) are left alone.
+// The rotation (c, s) of a pair with diagonal entries a, b and off-diagonal
+// entry e: R = [[c, s], [-s, c]] makes the pair's block of R^T G R diagonal.
+// t = s / c is the root of smaller magnitude of t^2 + 2 theta t - 1 = 0,
+// theta = (b - a) / (2e), here written t = 2e sgn(h) / (|h| + sqrt(h^2 + 4e^2))
+// with h = b - a: two square roots and two divisions (the Gram entries are far
+// from overflowing the squares).  Entries below 1e-18 of sqrt(|a b|), or zero,
+// are left alone.
+__device__ __forceinline__ double2 jacobi_rotation(double a, double b, double e) {
+    double c = 1.0, sn = 0.0;
+    if (e != 0.0 && e * e > 1e-36 * fabs(a * b)) {
+        const double h = b - a, e2 = 2.0 * e;
+        const double t = (h >= 0.0 ? e2 : -e2) / (fabs(h) + sqrt(h * h + e2 * e2));
+        c = 1.0 / sqrt(t * t + 1.0);
+        sn = t * c;
+    }
+    return make_double2(c, sn);
+}
+
+// One round's rotations: position i pairs indices 2i and 2i + 1.
 __global__ __launch_bounds__(256) void jacobi_rot_kernel(const double *__restrict__ G, double2 *__restrict__ rot,
                                                          int n) {
     const int h = n / 2, i = blockIdx.x * 256 + threadIdx.x, seq = blockIdx.y;
     if (i >= h) return;
     const double *g = G + static_cast<size_t>(seq) * n * n;
-    const double a = g[static_cast<size_t>(2 * i) * n + 2 * i], b = g[static_cast<size_t>(2 * i + 1) * n + 2 * i + 1];
-    const double e = g[static_cast<size_t>(2 * i) * n + 2 * i + 1];
-    double c = 1.0, sn = 0.0;
-    if (e != 0.0 && fabs(e) > 1e-18 * sqrt(fabs(a) * fabs(b))) {
-        const double theta = (b - a) / (2.0 * e);
-        const double t = (theta >= 0.0 ? 1.0 : -1.0) / (fabs(theta) + sqrt(theta * theta + 1.0));
-        c = 1.0 / sqrt(t * t + 1.0);
-        sn = t * c;
-    }
-    rot[static_cast<size_t>(seq) * h + i] = make_double2(c, sn);
+    rot[static_cast<size_t>(seq) * h + i] =
+        jacobi_rotation(g[static_cast<size_t>(2 * i) * n + 2 * i], g[static_cast<size_t>(2 * i + 1) * n + 2 * i + 1],
+                        g[static_cast<size_t>(2 * i) * n + 2 * i + 1]);
 }
 
 // Block (i, j) of the round: X' = R_i^T X R_j, written at the next round's
@@ -243,6 +255,247 @@ __global__ __launch_bounds__(256) void jacobi_vec_kernel(const double *__restric
     const double2 rj = rot[static_cast<size_t>(seq) * h + j];
     Vn[base + next_place(2 * j, n)] = rj.x * v.x - rj.y * v.y;
     Vn[base + next_place(2 * j + 1, n)] = rj.y * v.x + rj.x * v.y;
+}
+
+// ---------------------------------------------------------------------------
+// Block Jacobi.  The n indices form nb = n / 16 blocks of 16, kept (like the
+// single indices above) in the order of the current round: round position I
+// holds the block pair (2I, 2I+1), a 32-index super-block, and between rounds
+// the blocks move round the same cycle as single indices do (next_place over
+// nb places), so nb - 1 rounds pair every two blocks once: a sweep.  A round:
+//   jacobi_block_solve_kernel  each super-block's 32 x 32 diagonal tile,
+//                              diagonalised in LDS by cyclic two-sided Jacobi
+//                              sweeps (the plane rotations above, 16 disjoint
+//                              pairs at a time), giving the tile's orthogonal
+//                              Q_I; the rotated tile goes to its next places
+//   jacobi_block_apply_kernel  the other tiles: Q_I^T G_IJ Q_J at the next
+//                              places, so that G <- J^T G J with
+//                              J = diag(Q_0, Q_1, ...)
+//   jacobi_block_vec_kernel    V <- V J
+// As in the single-index method every pair of indices is rotated in every
+// sweep (inside the super-block that holds both), in sixteen times fewer
+// rounds, each a few small products instead of a pass per rotation.
+// ---------------------------------------------------------------------------
+constexpr int kJB = 16;          // indices per block
+constexpr int kJS = 2 * kJB;     // indices per super-block (a round position)
+constexpr int kJPad = kJS + 1;   // LDS row stride of a 32 x 32 tile (doubles)
+
+// Index at position k (of 32) in step t (of 31) of an inner sweep: index 0
+// stays, the others advance one place round a circle of 31 each step, and the
+// step pairs positions k and 31 - k, so 31 steps pair every two indices once.
+__device__ __forceinline__ int inner_pos(int k, int t) { return k == 0 ? 0 : 1 + (k - 1 + t) % (kJS - 1); }
+
+// Place in the next round of row or column u (< 32) of super-block I.
+__device__ __forceinline__ int block_next(int I, int u, int nb) {
+    return next_place(2 * I + u / kJB, nb) * kJB + u % kJB;
+}
+
+typedef __attribute__((ext_vector_type(4))) double f64x4;
+
+// D += A B on the double-precision matrix cores, 16 x 16 x 4: lane l gives
+// A[l % 16][l / 16] and B[l / 16][l % 16], and holds D[4 j + l / 16][l % 16]
+// in element j (rows interleaved across the four elements).
+__device__ __forceinline__ f64x4 mfma_f64(double a, double b, f64x4 d) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, d, 0, 0, 0);
+}
+
+// Workgroup (I, seq).  Inner sweeps run while the tile's off-diagonal mass is
+// above 1e-30 of its total and still falling a hundredfold per sweep once
+// below 1e-22 (the rounding floor), at most max_sweeps.  The tile is double
+// buffered: a step reads its pairs' 2 x 2 diagonal blocks (each thread works
+// out the two rotations it needs) and its own block from one buffer and
+// writes the other, so a step takes one barrier.
+__global__ __launch_bounds__(256) void jacobi_block_solve_kernel(const double *__restrict__ G, double *__restrict__ Gn,
+                                                                 double *__restrict__ Qb, int n, int max_sweeps) {
+    __shared__ double S[2][kJS][kJPad];
+    __shared__ double Qm[kJS][kJPad];
+    __shared__ double red[2][4];
+    const int I = blockIdx.x, seq = blockIdx.y, tid = threadIdx.x, nb = n / kJB;
+    const size_t base = static_cast<size_t>(seq) * n * n;
+    const double *g = G + base + static_cast<size_t>(I) * kJS * n + I * kJS;
+    for (int x = tid; x < kJS * kJS; x += 256) {
+        const int u = x / kJS, v = x % kJS;
+        S[0][u][v] = g[static_cast<size_t>(u) * n + v];
+        Qm[u][v] = u == v ? 1.0 : 0.0;
+    }
+    __syncthreads();
+    const int br = tid >> 4, bc = tid & 15;  // this thread's 2 x 2 block: row pair br, column pair bc
+    int cur = 0;
+    double prev = 0.0;
+    for (int sw = 0;; ++sw) {
+        double off = 0.0, tot = 0.0;
+        for (int x = tid; x < kJS * kJS; x += 256) {
+            const double v = S[cur][x / kJS][x % kJS];
+            tot += v * v;
+            if (x / kJS != x % kJS) off += v * v;
+        }
+        off = wave_sum_d(off);
+        tot = wave_sum_d(tot);
+        if ((tid & 63) == 0) {
+            red[0][tid >> 6] = off;
+            red[1][tid >> 6] = tot;
+        }
+        __syncthreads();
+        const double o = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+        const double a = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+        const bool stop = !(o > 1e-30 * a) || sw == max_sweeps || (sw > 0 && o <= 1e-22 * a && o > 0.01 * prev);
+        prev = o;
+        if (stop) break;  // the same in every thread
+        for (int t = 0; t < kJS - 1; ++t) {
+            const double(*X)[kJPad] = S[cur];
+            double(*Y)[kJPad] = S[cur ^ 1];
+            const int p0 = inner_pos(br, t), q0 = inner_pos(kJS - 1 - br, t);
+            const int p1 = inner_pos(bc, t), q1 = inner_pos(kJS - 1 - bc, t);
+            const double2 ri = jacobi_rotation(X[p0][p0], X[q0][q0], X[p0][q0]);
+            const double2 rj = jacobi_rotation(X[p1][p1], X[q1][q1], X[p1][q1]);
+            const double x00 = X[p0][p1], x01 = X[p0][q1], x10 = X[q0][p1], x11 = X[q0][q1];
+            const double y00 = rj.x * x00 - rj.y * x01, y01 = rj.y * x00 + rj.x * x01;
+            const double y10 = rj.x * x10 - rj.y * x11, y11 = rj.y * x10 + rj.x * x11;
+            double z00 = ri.x * y00 - ri.y * y10, z01 = ri.x * y01 - ri.y * y11;
+            double z10 = ri.y * y00 + ri.x * y10, z11 = ri.y * y01 + ri.x * y11;
+            if (br == bc) z01 = z10 = 0.0;
+            Y[p0][p1] = z00;
+            Y[p0][q1] = z01;
+            Y[q0][p1] = z10;
+            Y[q0][q1] = z11;
+            // Q <- Q R on columns p1, q1 of rows 2 br and 2 br + 1 (this thread's alone)
+#pragma unroll
+            for (int w = 0; w < 2; ++w) {
+                const int row = 2 * br + w;
+                const double qa = Qm[row][p1], qb = Qm[row][q1];
+                Qm[row][p1] = rj.x * qa - rj.y * qb;
+                Qm[row][q1] = rj.y * qa + rj.x * qb;
+            }
+            cur ^= 1;
+            __syncthreads();
+        }
+    }
+    double *q = Qb + (static_cast<size_t>(seq) * (n / kJS) + I) * kJS * kJS;
+    for (int x = tid; x < kJS * kJS; x += 256) {
+        const int u = x / kJS, v = x % kJS;
+        q[x] = Qm[u][v];
+        Gn[base + static_cast<size_t>(block_next(I, u, nb)) * n + block_next(I, v, nb)] = S[cur][u][v];
+    }
+}
+
+// One wave per tile pair (I, J), I < J: Y = Q_I^T G_IJ Q_J on the matrix
+// cores (T = G_IJ Q_J, staged in LDS as the second product's B operand), Y
+// written at tile (I, J)'s next places and its transpose at tile (J, I)'s,
+// which keeps G exactly symmetric.
+__global__ __launch_bounds__(64) void jacobi_block_apply_kernel(const double *__restrict__ G, double *__restrict__ Gn,
+                                                                const double *__restrict__ Qb, int n) {
+    __shared__ double T[kJS][kJPad];
+    const int ns = n / kJS, seq = blockIdx.y, l = threadIdx.x, lr = l & 15, lk = l >> 4, nb = n / kJB;
+    int p = blockIdx.x, I = 0;
+    while (p >= ns - 1 - I) {
+        p -= ns - 1 - I;
+        ++I;
+    }
+    const int J = I + 1 + p;
+    const size_t base = static_cast<size_t>(seq) * n * n;
+    const double *g = G + base + static_cast<size_t>(I) * kJS * n + J * kJS;
+    const double *qi = Qb + (static_cast<size_t>(seq) * ns + I) * kJS * kJS;
+    const double *qj = Qb + (static_cast<size_t>(seq) * ns + J) * kJS * kJS;
+    // The contraction index k runs as 16 c + 4 (l / 16) + e: a lane reads four
+    // consecutive k of its row (32 bytes, a whole 128-byte row segment per 16
+    // lanes) and feeds them to four products, element e to the e-th.
+    f64x4 acc[2][2] = {};
+#pragma unroll
+    for (int c = 0; c < kJS / 16; ++c) {
+        const int k0 = 16 * c + 4 * lk;
+        const f64x4 a0 = *reinterpret_cast<const f64x4 *>(g + static_cast<size_t>(lr) * n + k0);
+        const f64x4 a1 = *reinterpret_cast<const f64x4 *>(g + static_cast<size_t>(16 + lr) * n + k0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const double b0 = qj[(k0 + e) * kJS + lr], b1 = qj[(k0 + e) * kJS + 16 + lr];
+            acc[0][0] = mfma_f64(a0[e], b0, acc[0][0]);
+            acc[0][1] = mfma_f64(a0[e], b1, acc[0][1]);
+            acc[1][0] = mfma_f64(a1[e], b0, acc[1][0]);
+            acc[1][1] = mfma_f64(a1[e], b1, acc[1][1]);
+        }
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) T[rb * 16 + 4 * j + lk][cb * 16 + lr] = acc[rb][cb][j];
+    __syncthreads();
+    f64x4 y[2][2] = {};
+#pragma unroll
+    for (int st = 0; st < kJS / 4; ++st) {
+        const int k = 4 * st + lk;
+        const double a0 = qi[k * kJS + lr], a1 = qi[k * kJS + 16 + lr];  // (Q_I^T)[row][k] = Q_I[k][row]
+        const double b0 = T[k][lr], b1 = T[k][16 + lr];
+        y[0][0] = mfma_f64(a0, b0, y[0][0]);
+        y[0][1] = mfma_f64(a0, b1, y[0][1]);
+        y[1][0] = mfma_f64(a1, b0, y[1][0]);
+        y[1][1] = mfma_f64(a1, b1, y[1][1]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int u = rb * 16 + 4 * j + lk;
+            const size_t row = base + static_cast<size_t>(block_next(I, u, nb)) * n;
+#pragma unroll
+            for (int cb = 0; cb < 2; ++cb) {
+                Gn[row + block_next(J, cb * 16 + lr, nb)] = y[rb][cb][j];
+                T[u][cb * 16 + lr] = y[rb][cb][j];
+            }
+        }
+    __syncthreads();
+    // tile (J, I): row v of it is column v of Y
+    const int u = l & 31, cu = block_next(I, u, nb);
+#pragma unroll 4
+    for (int it = 0; it < kJS / 2; ++it) {
+        const int v = 2 * it + (l >> 5);
+        Gn[base + static_cast<size_t>(block_next(J, v, nb)) * n + cu] = T[u][v];
+    }
+}
+
+// V <- V J: one wave per 64 rows of super-block J's 32 columns, times Q_J on
+// the matrix cores, written at the next round's column places (rows stay).
+__global__ __launch_bounds__(64) void jacobi_block_vec_kernel(const double *__restrict__ V, double *__restrict__ Vn,
+                                                              const double *__restrict__ Qb, int n) {
+    const int ns = n / kJS, J = blockIdx.y, seq = blockIdx.z, l = threadIdx.x, lr = l & 15, lk = l >> 4, nb = n / kJB;
+    const int r0 = blockIdx.x * 64;
+    const size_t base = static_cast<size_t>(seq) * n * n;
+    const double *qj = Qb + (static_cast<size_t>(seq) * ns + J) * kJS * kJS;
+    // k runs as 16 c + 4 (l / 16) + e, as in the apply kernel
+    f64x4 acc[4][2] = {};
+#pragma unroll
+    for (int c = 0; c < kJS / 16; ++c) {
+        const int k0 = 16 * c + 4 * lk;
+        f64x4 a[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+            const int row = r0 + rb * 16 + lr;
+            a[rb] = row < n ? *reinterpret_cast<const f64x4 *>(V + base + static_cast<size_t>(row) * n + J * kJS + k0)
+                            : f64x4{0.0, 0.0, 0.0, 0.0};
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const double b0 = qj[(k0 + e) * kJS + lr], b1 = qj[(k0 + e) * kJS + 16 + lr];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                acc[rb][0] = mfma_f64(a[rb][e], b0, acc[rb][0]);
+                acc[rb][1] = mfma_f64(a[rb][e], b1, acc[rb][1]);
+            }
+        }
+    }
+    const int c0 = block_next(J, lr, nb), c1 = block_next(J, 16 + lr, nb);
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int row = r0 + rb * 16 + 4 * j + lk;
+            if (row < n) {
+                Vn[base + static_cast<size_t>(row) * n + c0] = acc[rb][0][j];
+                Vn[base + static_cast<size_t>(row) * n + c1] = acc[rb][1][j];
+            }
+        }
 }
 
 // Squared sums of the off-diagonal entries and of all entries: workgroup
@@ -353,7 +606,9 @@ __global__ __launch_bounds__(256) void factor_a_kernel(const T *__restrict__ kp,
 // Host side: batches of up to 8 sequences; the eigensolver's sweeps run until
 // the off-diagonal mass (sum of squares) is below 1e-28 of the total, or below
 // 1e-20 and no longer falling tenfold per sweep (the rounding floor), or 30
-// sweeps have run.  SKV_FACTOR_LOG=1 prints the measure after every sweep.
+// sweeps have run.  Each sweep's measure is read while the next sweep runs, so
+// one sweep past the deciding one is done.  SKV_FACTOR_LOG=1 prints the
+// measure after every sweep.
 // ---------------------------------------------------------------------------
 #define FZ_HIP(expr)                                                                         \
     do {                                                                                     \
@@ -378,14 +633,25 @@ int factorize_device(int bf16, int batch, int hkv, int s, int d, int r, const vo
     const size_t nn = static_cast<size_t>(n) * n;
     const size_t esz = bf16 ? 2 : 4;
     double *part = nullptr, *G0 = nullptr, *G1 = nullptr, *V0 = nullptr, *V1 = nullptr, *W = nullptr;
-    double2 *rot = nullptr, *offs = nullptr;
+    double2 *rot = nullptr, *offs = nullptr, *offs_pin = nullptr;
+    hipEvent_t ev[2] = {nullptr, nullptr};
     int32_t *sel = nullptr;
     int rc = 0, max_sweeps = 0;
-    std::vector<double2> offs_h(static_cast<size_t>(group) * 64);
     std::vector<double> diag(n);
     std::vector<int32_t> sel_h(static_cast<size_t>(group) * rr);
     std::vector<int32_t> order(n);
     const bool log_sweeps = std::getenv("SKV_FACTOR_LOG") != nullptr;
+    // 32-index super-blocks when n is a multiple of 32 with at least 4 blocks
+    // of 16 (the round cycle needs 4 places); SKV_FACTOR_BLOCK=0 keeps the
+    // single-index rounds
+    const char *fb = std::getenv("SKV_FACTOR_BLOCK");
+    const bool blockwise = n % kJS == 0 && n / kJB >= 4 && !(fb && fb[0] == '0');
+    const int nsb = n / kJS;
+    // inner sweeps per super-block and round at most: one sweep a round costs
+    // the fewest rounds' time (the outer sweeps finish what it leaves)
+    const char *fi = std::getenv("SKV_FACTOR_INNER");
+    const int inner = fi && std::atoi(fi) > 0 ? std::atoi(fi) : 1;
+    double *Qb = nullptr;
     FZ_HIP(hipMalloc(&part, static_cast<size_t>(ns) * group * nn * 8));
     FZ_HIP(hipMalloc(&G0, group * nn * 8));
     FZ_HIP(hipMalloc(&G1, group * nn * 8));
@@ -393,8 +659,13 @@ int factorize_device(int bf16, int batch, int hkv, int s, int d, int r, const vo
     FZ_HIP(hipMalloc(&V1, group * nn * 8));
     FZ_HIP(hipMalloc(&W, static_cast<size_t>(group) * n * rr * 8));
     FZ_HIP(hipMalloc(&rot, static_cast<size_t>(group) * h * sizeof(double2)));
-    FZ_HIP(hipMalloc(&offs, static_cast<size_t>(group) * 64 * sizeof(double2)));
+    FZ_HIP(hipMalloc(&offs, static_cast<size_t>(group) * 2 * 64 * sizeof(double2)));
+    FZ_HIP(hipHostMalloc(reinterpret_cast<void **>(&offs_pin), static_cast<size_t>(group) * 2 * 64 * sizeof(double2),
+                         hipHostMallocDefault));
+    FZ_HIP(hipEventCreateWithFlags(&ev[0], hipEventDisableTiming));
+    FZ_HIP(hipEventCreateWithFlags(&ev[1], hipEventDisableTiming));
     FZ_HIP(hipMalloc(&sel, static_cast<size_t>(group) * rr * 4));
+    if (blockwise) FZ_HIP(hipMalloc(&Qb, static_cast<size_t>(group) * nsb * kJS * kJS * 8));
     for (int g0 = 0; g0 < batch; g0 += group) {
         const int gc = batch - g0 < group ? batch - g0 : group;
         const char *kp = static_cast<const char *>(k_pre) + static_cast<size_t>(g0) * hkv * s * d * esz;
@@ -411,23 +682,50 @@ int factorize_device(int bf16, int batch, int hkv, int s, int d, int r, const vo
                            G0, V0, n, ns, gc);
         FZ_HIP(hipGetLastError());
         double *Gc = G0, *Gn = G1, *Vc = V0, *Vn = V1;
-        int sweep = 0;
-        std::vector<double> prev_rel(gc, 1.0);
-        for (; sweep < 30; ++sweep) {
-            for (int round = 0; round < n - 1; ++round) {
-                hipLaunchKernelGGL(jacobi_rot_kernel, dim3((h + 255) / 256, gc), dim3(256), 0, st, Gc, rot, n);
-                hipLaunchKernelGGL(jacobi_apply_kernel, dim3((h / 16) * (h / 16), gc), dim3(256), 0, st, Gc, Gn, rot,
-                                   n);
-                hipLaunchKernelGGL(jacobi_vec_kernel, dim3(static_cast<unsigned>((static_cast<size_t>(n) * h + 255) / 256), gc),
-                                   dim3(256), 0, st, Vc, Vn, rot, n);
-                std::swap(Gc, Gn);
-                std::swap(Vc, Vn);
+        // one sweep's rounds and its measure, read back through slot k % 2
+        auto enqueue_sweep = [&](int k) -> hipError_t {
+            if (blockwise) {
+                for (int round = 0; round < n / kJB - 1; ++round) {
+                    hipLaunchKernelGGL(jacobi_block_solve_kernel, dim3(nsb, gc), dim3(256), 0, st, Gc, Gn, Qb, n,
+                                       inner);
+                    hipLaunchKernelGGL(jacobi_block_apply_kernel, dim3(nsb * (nsb - 1) / 2, gc), dim3(64), 0, st, Gc,
+                                       Gn, Qb, n);
+                    hipLaunchKernelGGL(jacobi_block_vec_kernel, dim3((n + 63) / 64, nsb, gc), dim3(64), 0, st, Vc, Vn,
+                                       Qb, n);
+                    std::swap(Gc, Gn);
+                    std::swap(Vc, Vn);
+                }
+            } else {
+                for (int round = 0; round < n - 1; ++round) {
+                    hipLaunchKernelGGL(jacobi_rot_kernel, dim3((h + 255) / 256, gc), dim3(256), 0, st, Gc, rot, n);
+                    hipLaunchKernelGGL(jacobi_apply_kernel, dim3((h / 16) * (h / 16), gc), dim3(256), 0, st, Gc, Gn,
+                                       rot, n);
+                    hipLaunchKernelGGL(jacobi_vec_kernel,
+                                       dim3(static_cast<unsigned>((static_cast<size_t>(n) * h + 255) / 256), gc),
+                                       dim3(256), 0, st, Vc, Vn, rot, n);
+                    std::swap(Gc, Gn);
+                    std::swap(Vc, Vn);
+                }
             }
-            FZ_HIP(hipGetLastError());
-            hipLaunchKernelGGL(offdiag_kernel, dim3(64, gc), dim3(256), 0, st, Gc, offs, n);
-            FZ_HIP(hipMemcpyAsync(offs_h.data(), offs, static_cast<size_t>(gc) * 64 * sizeof(double2),
-                                  hipMemcpyDeviceToHost, st));
-            FZ_HIP(hipStreamSynchronize(st));
+            const size_t slot = static_cast<size_t>(k & 1) * group * 64;
+            hipLaunchKernelGGL(offdiag_kernel, dim3(64, gc), dim3(256), 0, st, Gc, offs + slot, n);
+            hipError_t e = hipGetLastError();
+            if (e == hipSuccess)
+                e = hipMemcpyAsync(offs_pin + slot, offs + slot, static_cast<size_t>(gc) * 64 * sizeof(double2),
+                                   hipMemcpyDeviceToHost, st);
+            if (e == hipSuccess) e = hipEventRecord(ev[k & 1], st);
+            return e;
+        };
+        std::vector<double> prev_rel(gc, 1.0);
+        int queued = 1;
+        FZ_HIP(enqueue_sweep(0));
+        for (int sweep = 0; sweep < 30; ++sweep) {
+            // the next sweep is queued before this one's measure is read, so
+            // the device stays busy while the host waits; a sweep past
+            // convergence only refines the result
+            if (queued < 30) FZ_HIP(enqueue_sweep(queued++));
+            FZ_HIP(hipEventSynchronize(ev[sweep & 1]));
+            const double2 *m = offs_pin + static_cast<size_t>(sweep & 1) * group * 64;
             // converged: the off-diagonal mass is at 1e-28 of the total, or
             // it has reached the rounding floor (below 1e-20 and no longer
             // falling tenfold per sweep)
@@ -435,19 +733,17 @@ int factorize_device(int bf16, int batch, int hkv, int s, int d, int r, const vo
             for (int q = 0; q < gc; ++q) {
                 double off = 0.0, tot = 0.0;
                 for (int k = 0; k < 64; ++k) {
-                    off += offs_h[q * 64 + k].x;
-                    tot += offs_h[q * 64 + k].y;
+                    off += m[q * 64 + k].x;
+                    tot += m[q * 64 + k].y;
                 }
                 const double rel = tot > 0.0 ? off / tot : 0.0;
                 if (log_sweeps) fprintf(stderr, "factorize: sequence %d sweep %d off/total %.3e\n", g0 + q, sweep, rel);
                 if (!(rel <= 1e-28 || (rel <= 1e-20 && rel > 0.1 * prev_rel[q]))) done_all = false;
                 prev_rel[q] = rel;
             }
-            if (done_all) {
-                ++sweep;
-                break;
-            }
+            if (done_all) break;
         }
+        const int sweep = queued;
         if (sweep > max_sweeps) max_sweeps = sweep;
         // the rr largest eigenvalues (ties: lower place first)
         for (int q = 0; q < gc; ++q) {
@@ -488,7 +784,11 @@ done:
     if (W) (void)hipFree(W);
     if (rot) (void)hipFree(rot);
     if (offs) (void)hipFree(offs);
+    if (offs_pin) (void)hipHostFree(offs_pin);
+    if (ev[0]) (void)hipEventDestroy(ev[0]);
+    if (ev[1]) (void)hipEventDestroy(ev[1]);
     if (sel) (void)hipFree(sel);
+    if (Qb) (void)hipFree(Qb);
     if (sweeps_out) *sweeps_out = max_sweeps;
     return rc;
 }

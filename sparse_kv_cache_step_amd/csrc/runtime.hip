@@ -296,7 +296,11 @@ int dalloc_t(skv_layer *ly, size_t bytes, P **p) {
 }
 
 void release(skv_layer *ly) {
-    (void)hipDeviceSynchronize();
+    // the layer's work ends at ev_done on the caller's stream (every call that
+    // enqueues work records it) and on the shared copy and rebuild streams
+    if (ly->ev_done) (void)hipEventSynchronize(ly->ev_done);
+    if (ly->copy) (void)hipStreamSynchronize(ly->copy);
+    if (ly->comp) (void)hipStreamSynchronize(ly->comp);
     for (void *p : ly->allocs) (void)hipFree(p);
     ly->allocs.clear();
     for (hipEvent_t e : ly->ev_pool) (void)hipEventDestroy(e);

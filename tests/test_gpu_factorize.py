@@ -11,7 +11,9 @@ heads' keys to ~1e-7.  Checked per sequence:
   * the singular values (column norms of A);
   * orthonormal rows of B (all heads together);
   * zero columns of A and rows of B past n = h_kv * d;
-  * batches of more than the eight sequences solved at once.
+  * batches of more than the eight sequences solved at once;
+  * both round forms of the eigensolver (32-index super-blocks, single
+    index pairs).
 """
 import dataclasses
 
@@ -40,14 +42,21 @@ def _products(A, B):
     return np.einsum("bsr,bhrd->bhsd", A, B)
 
 
-@pytest.mark.parametrize("case", list(CASES))
-def test_factorize_matches_the_oracle_svd(case):
+# The eigensolver's two round forms: 32-index super-blocks (the default where
+# n is a multiple of 32 and at least 64) and single index pairs.
+PATHS = {"block": "1", "single": "0"}
+PARAMS = [(c, "block") for c in CASES] + [("tiny-fp32", "single"), ("bf16-glm-shape", "single")]
+
+
+@pytest.mark.parametrize("case,path", PARAMS, ids=[f"{c}-{p}" for c, p in PARAMS])
+def test_factorize_matches_the_oracle_svd(case, path, monkeypatch):
+    monkeypatch.setenv("SKV_FACTOR_BLOCK", PATHS[path])
     wl = CASES[case]
     k_pre = synth.k_pre_numpy(wl)
     b, hkv, s, d = k_pre.shape
     n, r = hkv * d, wl.r
     rr = min(r, n)
-    log(f"[{case}] b={b} h_kv={hkv} s={s} d={d} r={r} n={n} dtype={'bf16' if wl.bf16 else 'f32'}")
+    log(f"[{case}/{path}] b={b} h_kv={hkv} s={s} d={d} r={r} n={n} dtype={'bf16' if wl.bf16 else 'f32'}")
     A_g, B_g, sweeps = skv.factorize(to_dev(k_pre, tdtype(wl)), r, return_sweeps=True)
     torch.cuda.synchronize()
     A_g, B_g = to_np(A_g), to_np(B_g)
