@@ -22,6 +22,8 @@
 //       jacobi_apply_kernel  G <- R^T G R (one 2 x 2 block per thread)
 //       jacobi_vec_kernel    V <- V R
 //   offdiag_kernel       off-diagonal and total squared sums (convergence)
+//   diag_kernel          the eigenvalues (G's diagonal), read by the host to
+//                        pick the r largest
 //   gather_b_kernel      W = the r leading eigenvectors, and B
 //   factor_a_kernel      A = M W, rounded once to the storage type
 //
@@ -525,6 +527,12 @@ __global__ __launch_bounds__(256) void offdiag_kernel(const double *__restrict__
     if (threadIdx.x == 0) out[seq * 64 + blockIdx.x] = make_double2(so[0], st[0]);
 }
 
+// out[seq][x] = G[seq][x][x]
+__global__ __launch_bounds__(256) void diag_kernel(const double *__restrict__ G, double *__restrict__ out, int n) {
+    const int x = blockIdx.x * 256 + threadIdx.x, seq = blockIdx.y;
+    if (x < n) out[static_cast<size_t>(seq) * n + x] = G[static_cast<size_t>(seq) * n * n + static_cast<size_t>(x) * (n + 1)];
+}
+
 // W[x][j] = V[x][sel[j]] (j < rr, double), and B[h][j][i] = V[h*d + i][sel[j]]
 // rounded to the storage type (zero for rr <= j < r).
 template <typename T>
@@ -632,12 +640,12 @@ int factorize_device(int bf16, int batch, int hkv, int s, int d, int r, const vo
     const int rps = ((s + ns - 1) / ns + kGK - 1) / kGK * kGK;
     const size_t nn = static_cast<size_t>(n) * n;
     const size_t esz = bf16 ? 2 : 4;
-    double *part = nullptr, *G0 = nullptr, *G1 = nullptr, *V0 = nullptr, *V1 = nullptr, *W = nullptr;
+    double *part = nullptr, *G0 = nullptr, *G1 = nullptr, *V0 = nullptr, *V1 = nullptr, *W = nullptr, *dg = nullptr;
     double2 *rot = nullptr, *offs = nullptr, *offs_pin = nullptr;
     hipEvent_t ev[2] = {nullptr, nullptr};
     int32_t *sel = nullptr;
     int rc = 0, max_sweeps = 0;
-    std::vector<double> diag(n);
+    std::vector<double> diag(static_cast<size_t>(group) * n);
     std::vector<int32_t> sel_h(static_cast<size_t>(group) * rr);
     std::vector<int32_t> order(n);
     const bool log_sweeps = std::getenv("SKV_FACTOR_LOG") != nullptr;
@@ -658,6 +666,7 @@ int factorize_device(int bf16, int batch, int hkv, int s, int d, int r, const vo
     FZ_HIP(hipMalloc(&V0, group * nn * 8));
     FZ_HIP(hipMalloc(&V1, group * nn * 8));
     FZ_HIP(hipMalloc(&W, static_cast<size_t>(group) * n * rr * 8));
+    FZ_HIP(hipMalloc(&dg, static_cast<size_t>(group) * n * 8));
     FZ_HIP(hipMalloc(&rot, static_cast<size_t>(group) * h * sizeof(double2)));
     FZ_HIP(hipMalloc(&offs, static_cast<size_t>(group) * 2 * 64 * sizeof(double2)));
     FZ_HIP(hipHostMalloc(reinterpret_cast<void **>(&offs_pin), static_cast<size_t>(group) * 2 * 64 * sizeof(double2),
@@ -745,13 +754,16 @@ int factorize_device(int bf16, int batch, int hkv, int s, int d, int r, const vo
         }
         const int sweep = queued;
         if (sweep > max_sweeps) max_sweeps = sweep;
-        // the rr largest eigenvalues (ties: lower place first)
+        // the rr largest eigenvalues (ties: lower place first), the diagonals
+        // gathered on the device and read in one copy
+        hipLaunchKernelGGL(diag_kernel, dim3((n + 255) / 256, gc), dim3(256), 0, st, Gc, dg, n);
+        FZ_HIP(hipGetLastError());
+        FZ_HIP(hipMemcpyAsync(diag.data(), dg, static_cast<size_t>(gc) * n * 8, hipMemcpyDeviceToHost, st));
+        FZ_HIP(hipStreamSynchronize(st));
         for (int q = 0; q < gc; ++q) {
-            FZ_HIP(hipMemcpy2DAsync(diag.data(), 8, Gc + q * nn, static_cast<size_t>(n + 1) * 8, 8, n,
-                                    hipMemcpyDeviceToHost, st));
-            FZ_HIP(hipStreamSynchronize(st));
+            const double *dq = diag.data() + static_cast<size_t>(q) * n;
             for (int x = 0; x < n; ++x) order[x] = x;
-            std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return diag[a] > diag[b]; });
+            std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return dq[a] > dq[b]; });
             for (int j = 0; j < rr; ++j) sel_h[static_cast<size_t>(q) * rr + j] = order[j];
         }
         FZ_HIP(hipMemcpyAsync(sel, sel_h.data(), static_cast<size_t>(gc) * rr * 4, hipMemcpyHostToDevice, st));
@@ -782,6 +794,7 @@ done:
     if (V0) (void)hipFree(V0);
     if (V1) (void)hipFree(V1);
     if (W) (void)hipFree(W);
+    if (dg) (void)hipFree(dg);
     if (rot) (void)hipFree(rot);
     if (offs) (void)hipFree(offs);
     if (offs_pin) (void)hipHostFree(offs_pin);
