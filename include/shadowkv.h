@@ -333,23 +333,25 @@ int shadowkv_get_timing(skv_layer *layer, double *ms_out, int64_t *steps_out);
  * leading right singular vectors of M), A = M V_r and B = V_r^T split by
  * head, so A[b] . B[b, h] is the best rank-`rank` approximation of head h's
  * keys.  Everything runs on the device in double precision: the Gram matrix,
- * a parallel cyclic two-sided Jacobi eigensolver (until the off-diagonal
- * mass, a sum of squares, is below 1e-28 of the total or has stopped falling
- * at its rounding floor below 1e-20; at most 30 sweeps), and A = M V_r; A and
- * B are rounded once to `dtype`.
+ * a parallel cyclic two-sided Jacobi eigensolver on 32-index super-blocks
+ * (until the off-diagonal mass, a sum of squares, is below 1e-28 of the total
+ * or has stopped falling at its rounding floor below 1e-20; at most 30
+ * sweeps, and one sweep past the deciding one, which was queued while its
+ * measure was read), and A = M V_r; A and B are rounded once to `dtype`.
  *   k_pre  device (batch, heads_kv, seq_len, head_dim), `dtype`
  *   A      device (batch, seq_len, rank), written
  *   B      device (batch, heads_kv, rank, head_dim), written
  * With rank > n the columns past n are zero.  The call allocates its own
  * device scratch (about 0.5 GB at n = 1024: the Gram partials, two copies of
  * the matrix and of the eigenvectors for 8 sequences at a time), runs on
- * `stream`, reads back the convergence measure once per sweep and the
- * eigenvalues at the end, and returns when the factors are written.
+ * `stream`, reads back the convergence measure once per sweep (through a
+ * small pinned buffer) and the eigenvalues at the end, and returns when the
+ * factors are written.
  * SKV_E_INVAL for a null pointer or a bad dtype; SKV_E_SHAPE unless
  * batch, heads_kv, seq_len >= 1, head_dim in {64, 128}, rank in [1, 256],
  * heads_kv * head_dim <= 2048 (the eigensolver's cost grows as n^3: a sweep is
- * n - 1 rounds over two n x n matrices); SKV_E_HIP if an allocation, launch or copy
- * fails.  `sweeps_out` (may be NULL) receives the sweeps the slowest batch
+ * n/16 - 1 rounds over two n x n matrices); SKV_E_HIP if an allocation, launch or
+ * copy fails.  `sweeps_out` (may be NULL) receives the sweeps the slowest batch
  * took.
  */
 int shadowkv_factorize(int dtype, int batch, int heads_kv, int seq_len, int head_dim, int rank,
