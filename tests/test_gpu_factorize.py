@@ -34,6 +34,8 @@ CASES = {
     "fp32-b10": synth.TINY_FP32.with_(b=10, s=256, r=16, true_rank=12),
     "bf16-llama-32k": synth.LLAMA_32K,
     "bf16-glm-shape": synth.GLM_244K.with_(b=2, s=8192),
+    # the largest n the call takes (h_kv * d = 2048): 128 block places, 64 super-blocks
+    "bf16-n2048": synth.LLAMA_32K.with_(b=1, h_kv=16, s=4096),
 }
 
 
