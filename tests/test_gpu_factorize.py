@@ -13,7 +13,8 @@ heads' keys to ~1e-7.  Checked per sequence:
   * zero columns of A and rows of B past n = h_kv * d;
   * batches of more than the eight sequences solved at once;
   * both round forms of the eigensolver (32-index super-blocks, single
-    index pairs).
+    index pairs);
+  * all-zero keys (the degenerate case: A = 0, orthonormal B, finite).
 """
 import dataclasses
 
@@ -98,3 +99,25 @@ def test_factorize_matches_the_oracle_svd(case, path, monkeypatch):
         # full rank: the factors reproduce the keys
         M = k_pre.astype(np.float64)
         assert np.max(np.abs(P_g - M)) <= 1e-5 * np.max(np.abs(M))
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+def test_factorize_zero_keys(path, monkeypatch):
+    """All-zero keys: the Gram matrix is zero, every rotation is skipped and
+    the first sweep's measure (0 of 0) decides; the factors are A = 0 and
+    orthonormal rows of B (the singular vectors of a zero matrix are any
+    orthonormal set), with nothing non-finite."""
+    monkeypatch.setenv("SKV_FACTOR_BLOCK", PATHS[path])
+    b, hkv, s, d, r = 2, 2, 256, 64, 24
+    k_pre = torch.zeros((b, hkv, s, d), dtype=torch.float32, device="cuda")
+    A_g, B_g, sweeps = skv.factorize(k_pre, r, return_sweeps=True)
+    torch.cuda.synchronize()
+    A_g, B_g = to_np(A_g), to_np(B_g)
+    log(f"[zero keys/{path}] {sweeps} sweeps")
+    assert 1 <= sweeps <= 2
+    assert np.all(np.isfinite(A_g)) and np.all(np.isfinite(B_g))
+    assert np.all(A_g == 0)
+    n = hkv * d
+    for bi in range(b):
+        Bm = B_g[bi].transpose(1, 0, 2).reshape(r, n)
+        assert np.max(np.abs(Bm @ Bm.T - np.eye(r))) <= 1e-6
