@@ -6,8 +6,9 @@
 // eigenvectors of the Gram matrix G = M^T M, and the rank-r factors are
 // A = M V_r (= U_r S_r) and B = V_r^T split by head, so A . B is M's best
 // rank-r approximation.  Kernels:
-//   gram_kernel          G in 128 x 128 tiles of its upper triangle, the rows
-//                        of M split into slices that each write a partial
+//   gram_kernel          G in 128 x 128 tiles of its upper triangle on the
+//                        fp64 matrix cores, the rows of M split into slices
+//                        that each write a partial
 //   gram_sum_kernel      G = the slices' partials summed in slice order,
 //                        mirrored; the eigenvector accumulator set to I
 //   the eigensolver, the parallel two-sided (cyclic) Jacobi method in one of
@@ -94,22 +95,36 @@ __device__ __forceinline__ int next_place(int x, int n) {
 
 // ---------------------------------------------------------------------------
 // Partial Gram tiles.  Workgroup (pair, slice, seq): output tile (tp, tq),
-// tp <= tq, over rows [slice * rps, min(s, (slice + 1) * rps)) of M.  Thread
-// (ty, tx) accumulates rows tp*128 + ty + 16i and columns tq*128 + tx + 16j
-// (i, j < 8) in double; slabs of 16 rows of both column ranges are staged in
-// LDS as doubles, the next slab loaded into registers while this one is used.
-// Columns past n read zeros.
+// tp <= tq, over rows [slice * rps, min(s, (slice + 1) * rps)) of M.  Slabs of
+// 16 rows of both column ranges are staged in LDS as doubles (the next slab
+// loaded into registers while this one is used; columns past n read zeros),
+// and wave w accumulates the 64 x 64 quadrant (rows 64 (w / 2), columns
+// 64 (w % 2)) of the tile on the double-precision matrix cores: per 4 rows of
+// the slab, 4 x 4 products of 16 x 16 blocks, the A operand the slab's P
+// columns (M^T) and the B operand its Q columns.
 // ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(4))) double f64x4;
+
+// D += A B on the double-precision matrix cores, 16 x 16 x 4: lane l gives
+// A[l % 16][l / 16] and B[l / 16][l % 16], and holds D[4 j + l / 16][l % 16]
+// in element j (rows interleaved across the four elements).
+__device__ __forceinline__ f64x4 mfma_f64(double a, double b, f64x4 d) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, d, 0, 0, 0);
+}
+
+constexpr int kGPad = kGT + 8;  // LDS row of a staged slab (doubles), off the 64-bank period
+
 template <typename T>
 __global__ __launch_bounds__(256) void gram_kernel(const T *__restrict__ kp, double *__restrict__ part, int hkv,
                                                    int s, int d, int n, int nt, int rps, int nseq) {
-    __shared__ double Ps[kGK][kGT];
-    __shared__ double Qs[kGK][kGT];
+    __shared__ double Ps[kGK][kGPad];
+    __shared__ double Qs[kGK][kGPad];
     int x = blockIdx.x, tp = 0;
     while (x >= nt - tp) { x -= nt - tp; ++tp; }
     const int tq = tp + x;
     const int slice = blockIdx.y, seq = blockIdx.z;
-    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, lk = lane >> 4;
+    const int wy = wave >> 1, wx = wave & 1;
     const int t_begin = slice * rps, t_end = min(s, t_begin + rps);
     // staging: row tid / 16 of the slab, columns 8 * (tid % 16) .. + 8 of each tile
     const int srow = tid >> 4, scol = (tid & 15) * 8;
@@ -118,11 +133,7 @@ __global__ __launch_bounds__(256) void gram_kernel(const T *__restrict__ kp, dou
     auto src = [&](int col, int t) {  // M[t, col] of a column below n
         return kseq + (static_cast<size_t>(col / d) * s + t) * d + col % d;
     };
-    double acc[8][8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
+    f64x4 acc[4][4] = {};
     double pv[8], qv[8];
     {
         const int t = t_begin + srow;
@@ -141,31 +152,33 @@ __global__ __launch_bounds__(256) void gram_kernel(const T *__restrict__ kp, dou
             load8_f64(src(min(pc, n - 8), min(t, s - 1)), t < t_end && pc < n, pv);
             load8_f64(src(min(qc, n - 8), min(t, s - 1)), t < t_end && qc < n, qv);
         }
-#pragma unroll 4
-        for (int k = 0; k < kGK; ++k) {
-            double a[8], b[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) a[i] = Ps[k][ty + 16 * i];
+        for (int k0 = 0; k0 < kGK; k0 += 4) {
+            double a[4], b[4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) b[j] = Qs[k][tx + 16 * j];
+            for (int i = 0; i < 4; ++i) a[i] = Ps[k0 + lk][64 * wy + 16 * i + lr];  // (M^T)[p][t] = M[t][p]
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int j = 0; j < 4; ++j) b[j] = Qs[k0 + lk][64 * wx + 16 * j + lr];
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = mfma_f64(a[i], b[j], acc[i][j]);
         }
         __syncthreads();
     }
     double *out = part + (static_cast<size_t>(slice) * nseq + seq) * n * n;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int p = tp * kGT + ty + 16 * i;
-        if (p >= n) continue;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int q = tq * kGT + tx + 16 * j;
-            if (q < n) out[static_cast<size_t>(p) * n + q] = acc[i][j];
+        for (int e = 0; e < 4; ++e) {
+            const int p = tp * kGT + 64 * wy + 16 * i + 4 * e + lk;
+            if (p >= n) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int q = tq * kGT + 64 * wx + 16 * j + lr;
+                if (q < n) out[static_cast<size_t>(p) * n + q] = acc[i][j][e];
+            }
         }
-    }
 }
 
 // G[p][q] = sum over slices (in slice order) of the tile holding (p, q) or
@@ -292,14 +305,6 @@ __device__ __forceinline__ int block_next(int I, int u, int nb) {
     return next_place(2 * I + u / kJB, nb) * kJB + u % kJB;
 }
 
-typedef __attribute__((ext_vector_type(4))) double f64x4;
-
-// D += A B on the double-precision matrix cores, 16 x 16 x 4: lane l gives
-// A[l % 16][l / 16] and B[l / 16][l % 16], and holds D[4 j + l / 16][l % 16]
-// in element j (rows interleaved across the four elements).
-__device__ __forceinline__ f64x4 mfma_f64(double a, double b, f64x4 d) {
-    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, d, 0, 0, 0);
-}
 
 // Workgroup (I, seq).  Inner sweeps run while the tile's off-diagonal mass is
 // above 1e-30 of its total and still falling a hundredfold per sweep once
@@ -549,65 +554,98 @@ __global__ __launch_bounds__(256) void gather_b_kernel(const double *__restrict_
     Elem<T>::st(B, ((static_cast<size_t>(seq) * (n / d) + hh) * r + j) * d + i, Elem<T>::rnd_d(v));
 }
 
-// A[t][j] = M[t] . W[:, j] for j < rr (zero for rr <= j < r), accumulated in
-// double and rounded once.  Workgroup: 64 rows t x 64 columns j; slabs of 32
-// columns of M (transposed into LDS) and 32 rows of W.
+// 4 consecutive stored values as doubles (8 B of bfloat16, 16 B of binary32)
 template <typename T>
+__device__ __forceinline__ void load4_f64(const T *p, bool ok, double *o) {
+    if constexpr (sizeof(T) == 2) {
+        const u32x2 r = ok ? *reinterpret_cast<const u32x2 *>(p) : u32x2{0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            o[2 * e] = static_cast<double>(__uint_as_float(r[e] << 16));
+            o[2 * e + 1] = static_cast<double>(__uint_as_float(r[e] & 0xffff0000u));
+        }
+    } else {
+        const u32x4 r = ok ? *reinterpret_cast<const u32x4 *>(p) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = static_cast<double>(__uint_as_float(r[e]));
+    }
+}
+
+constexpr int kFX = 16;  // columns of M (rows of W) per staged slab
+
+// A[t][j] = M[t] . W[:, j] for j < rr (zero for rr <= j < r), accumulated in
+// double and rounded once.  Workgroup: 64 rows t, every column j; wave w the
+// 16 rows 16 w .. + 15, as NCB >= r / 16 products of 16 x 16 blocks on the
+// double-precision matrix cores.  Slabs of 16 columns of M (transposed into
+// LDS) and the same 16 rows of W (zero past rr) are staged, the next slab
+// loaded into registers while this one is used.
+template <typename T, int NCB>
 __global__ __launch_bounds__(256) void factor_a_kernel(const T *__restrict__ kp, const double *__restrict__ W,
                                                        T *__restrict__ A, int hkv, int s, int d, int r, int rr) {
-    __shared__ double Ms[32][64 + 1];
-    __shared__ double Ws[32][64];
+    constexpr int wcols = 16 * NCB, ncb = NCB;
+    __shared__ double Ms[kFX][64 + 1];
+    __shared__ double Ws[kFX][wcols + 8];
     const int n = hkv * d;
-    const int seq = blockIdx.z, t0 = blockIdx.x * 64, j0 = blockIdx.y * 64;
-    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+    const int seq = blockIdx.z, t0 = blockIdx.x * 64;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, lr = lane & 15, lk = lane >> 4;
     const T *kseq = kp + static_cast<size_t>(seq) * hkv * s * d;
     const double *wseq = W + static_cast<size_t>(seq) * n * rr;
-    double acc[4][4];
+    // staging: M row t0 + tid / 4, columns x0 + 4 (tid % 4) .. + 4; W entries
+    // tid + 256 u of the slab's 16 x wcols (u < ncb)
+    const int mt = tid >> 2, mx = (tid & 3) * 4;
+    auto load_slab = [&](int x0, double *mv, double *wv) {
+        const int t = t0 + mt, x = x0 + mx;
+        load4_f64(kseq + (static_cast<size_t>(x / d) * s + min(t, s - 1)) * d + x % d, t < s, mv);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+        for (int u = 0; u < ncb; ++u) {
+            const int e = tid + 256 * u, row = e / wcols, col = e % wcols;
+            wv[u] = col < rr ? wseq[static_cast<size_t>(x0 + row) * rr + col] : 0.0;
+        }
+    };
+    f64x4 acc[NCB] = {};
+    double mv[4], wv[NCB];
+    load_slab(0, mv, wv);
+    for (int x0 = 0; x0 < n; x0 += kFX) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
-    // staging: M rows t0 + tid / 4, columns x0 + 8 * (tid % 4) .. + 8;
-    // W rows x0 + tid / 8, columns j0 + 8 * (tid % 8) .. + 8
-    const int mt = tid >> 2, mx = (tid & 3) * 8, wx = tid >> 3, wj = (tid & 7) * 8;
-    for (int x0 = 0; x0 < n; x0 += 32) {
-        {
-            const int t = t0 + mt, x = x0 + mx;
-            double v[8];
-            load8_f64(kseq + (static_cast<size_t>(x / d) * s + min(t, s - 1)) * d + x % d, t < s, v);
+        for (int e = 0; e < 4; ++e) Ms[mx + e][mt] = mv[e];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) Ms[mx + e][mt] = v[e];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int j = j0 + wj + e;
-                Ws[wx][wj + e] = j < rr ? wseq[static_cast<size_t>(x0 + wx) * rr + j] : 0.0;
-            }
+        for (int u = 0; u < ncb; ++u) {
+            const int e = tid + 256 * u;
+            Ws[e / wcols][e % wcols] = wv[u];
         }
         __syncthreads();
-#pragma unroll 8
-        for (int k = 0; k < 32; ++k) {
-            double a[4], b[4];
+        if (x0 + kFX < n) load_slab(x0 + kFX, mv, wv);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = Ms[k][ty + 16 * i];
+        for (int k0 = 0; k0 < kFX; k0 += 4) {
+            const double a = Ms[k0 + lk][16 * wave + lr];  // A[row][k] = M[t0 + 16 w + row][x0 + k]
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = Ws[k][tx + 16 * j];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+            for (int cb = 0; cb < ncb; ++cb) acc[cb] = mfma_f64(a, Ws[k0 + lk][16 * cb + lr], acc[cb]);
         }
         __syncthreads();
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int t = t0 + ty + 16 * i;
-        if (t >= s) continue;
+    for (int cb = 0; cb < ncb; ++cb) {
+        const int jj = 16 * cb + lr;
+        if (jj >= r) continue;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int jj = j0 + tx + 16 * j;
-            if (jj < r) Elem<T>::st(A, (static_cast<size_t>(seq) * s + t) * r + jj, Elem<T>::rnd_d(jj < rr ? acc[i][j] : 0.0));
+        for (int e = 0; e < 4; ++e) {
+            const int t = t0 + 16 * wave + 4 * e + lk;
+            if (t < s) Elem<T>::st(A, (static_cast<size_t>(seq) * s + t) * r + jj, Elem<T>::rnd_d(jj < rr ? acc[cb][e] : 0.0));
         }
     }
+}
+
+// factor_a_kernel with the fewest column blocks (of 4, 8, 10, 12, 16) that
+// cover r <= 256
+template <typename T>
+void launch_factor_a(const T *kp, const double *W, T *A, int hkv, int s, int d, int r, int rr, dim3 grid,
+                     hipStream_t st) {
+    const int ncb = (r + 15) / 16;
+    if (ncb <= 4) hipLaunchKernelGGL((factor_a_kernel<T, 4>), grid, dim3(256), 0, st, kp, W, A, hkv, s, d, r, rr);
+    else if (ncb <= 8) hipLaunchKernelGGL((factor_a_kernel<T, 8>), grid, dim3(256), 0, st, kp, W, A, hkv, s, d, r, rr);
+    else if (ncb <= 10) hipLaunchKernelGGL((factor_a_kernel<T, 10>), grid, dim3(256), 0, st, kp, W, A, hkv, s, d, r, rr);
+    else if (ncb <= 12) hipLaunchKernelGGL((factor_a_kernel<T, 12>), grid, dim3(256), 0, st, kp, W, A, hkv, s, d, r, rr);
+    else hipLaunchKernelGGL((factor_a_kernel<T, 16>), grid, dim3(256), 0, st, kp, W, A, hkv, s, d, r, rr);
 }
 
 // ---------------------------------------------------------------------------
@@ -635,10 +673,28 @@ int factorize_device(int bf16, int batch, int hkv, int s, int d, int r, const vo
     const int n = hkv * d, h = n / 2, rr = r < n ? r : n;
     const int group = batch < 8 ? batch : 8;
     const int nt = (n + kGT - 1) / kGT, npair = nt * (nt + 1) / 2;
-    int ns = (1024 + npair * group - 1) / (npair * group);
+    // row slices of the Gram launch: at least about 1024 workgroups, and of up
+    // to four times that many the count whose workgroups fill the last round
+    // of resident ones best (two per CU), slices of at least 256 rows
+    int cus = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                   hipSuccess || cus < 1)
+        cus = 256;
     const int max_ns = (s + 255) / 256;
-    if (ns > max_ns) ns = max_ns;
-    if (ns < 1) ns = 1;
+    const int ns0 = std::max(1, std::min(max_ns, (1024 + npair * group - 1) / (npair * group)));
+    int ns = ns0;
+    {
+        const long long slots = 2LL * cus;
+        double best = 0.0;
+        for (int c = ns0; c <= std::min(max_ns, 4 * ns0); ++c) {
+            const long long wgs = static_cast<long long>(npair) * group * c;
+            const double fill = static_cast<double>(wgs) / static_cast<double>((wgs + slots - 1) / slots * slots);
+            if (fill > best + 1e-9) {
+                best = fill;
+                ns = c;
+            }
+        }
+    }
     const int rps = ((s + ns - 1) / ns + kGK - 1) / kGK * kGK;
     const size_t nn = static_cast<size_t>(n) * n;
     const size_t esz = bf16 ? 2 : 4;
@@ -787,18 +843,17 @@ int factorize_device(int bf16, int batch, int hkv, int s, int d, int r, const vo
         FZ_HIP(hipMemcpyAsync(sel, sel_h.data(), static_cast<size_t>(gc) * rr * 4, hipMemcpyHostToDevice, st));
         {
             const dim3 gb(static_cast<unsigned>((static_cast<size_t>(n) * r + 255) / 256), gc);
-            const dim3 ga((s + 63) / 64, (r + 63) / 64, gc);
+            const dim3 ga((s + 63) / 64, 1, gc);
             if (bf16) {
                 hipLaunchKernelGGL(gather_b_kernel<uint16_t>, gb, dim3(256), 0, st, Vc, sel, W,
                                    reinterpret_cast<uint16_t *>(Bg), n, d, r, rr);
-                hipLaunchKernelGGL(factor_a_kernel<uint16_t>, ga, dim3(256), 0, st,
-                                   reinterpret_cast<const uint16_t *>(kp), W, reinterpret_cast<uint16_t *>(Ag), hkv,
-                                   s, d, r, rr);
+                launch_factor_a(reinterpret_cast<const uint16_t *>(kp), W, reinterpret_cast<uint16_t *>(Ag), hkv, s,
+                                d, r, rr, ga, st);
             } else {
                 hipLaunchKernelGGL(gather_b_kernel<float>, gb, dim3(256), 0, st, Vc, sel, W,
                                    reinterpret_cast<float *>(Bg), n, d, r, rr);
-                hipLaunchKernelGGL(factor_a_kernel<float>, ga, dim3(256), 0, st, reinterpret_cast<const float *>(kp),
-                                   W, reinterpret_cast<float *>(Ag), hkv, s, d, r, rr);
+                launch_factor_a(reinterpret_cast<const float *>(kp), W, reinterpret_cast<float *>(Ag), hkv, s, d, r,
+                                rr, ga, st);
             }
             FZ_HIP(hipGetLastError());
         }
