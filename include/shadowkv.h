@@ -334,7 +334,7 @@ int shadowkv_get_timing(skv_layer *layer, double *ms_out, int64_t *steps_out);
  * head, so A[b] . B[b, h] is the best rank-`rank` approximation of head h's
  * keys.  Everything runs on the device in double precision: the Gram matrix,
  * a parallel cyclic two-sided Jacobi eigensolver on 32-index super-blocks
- * (until the off-diagonal mass, a sum of squares, is below 1e-24 of the total
+ * (until the off-diagonal mass, a sum of squares, is below 1e-22 of the total
  * or has stopped falling at its rounding floor below 1e-20; at most 30
  * sweeps, and one sweep past the deciding one, which was queued while its
  * measure was read and, the convergence being quadratic there, ends near the
