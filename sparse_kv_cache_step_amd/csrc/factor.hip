@@ -13,7 +13,7 @@
 //                        mirrored; the eigenvector accumulator set to I
 //   the eigensolver, the parallel two-sided (cyclic) Jacobi method in one of
 //   two round forms:
-//     32-index super-blocks (n a multiple of 32, n >= 64; the default):
+//     super-blocks of 2 JB indices, JB = 16 (the default) or 32:
 //       jacobi_block_solve_kernel, jacobi_block_apply_kernel,
 //       jacobi_block_vec_kernel (described at their definitions)
 //     single index pairs:
@@ -280,68 +280,83 @@ __global__ __launch_bounds__(256) void jacobi_vec_kernel(const double *__restric
 }
 
 // ---------------------------------------------------------------------------
-// Block Jacobi.  The n indices form nb = n / 16 blocks of 16, kept (like the
-// single indices above) in the order of the current round: round position I
-// holds the block pair (2I, 2I+1), a 32-index super-block, and between rounds
-// the blocks move round the same cycle as single indices do (next_place over
-// nb places), so nb - 1 rounds pair every two blocks once: a sweep.  A round:
-//   jacobi_block_solve_kernel  each super-block's 32 x 32 diagonal tile,
+// Block Jacobi.  The n indices form nb = n / JB blocks of JB (16 or 32), kept
+// (like the single indices above) in the order of the current round: round
+// position I holds the block pair (2I, 2I+1), a JS = 2 JB index super-block,
+// and between rounds the blocks move round the same cycle as single indices
+// do (next_place over nb places), so nb - 1 rounds pair every two blocks
+// once: a sweep.  A round:
+//   jacobi_block_solve_kernel  each super-block's JS x JS diagonal tile,
 //                              diagonalised in LDS by cyclic two-sided Jacobi
-//                              sweeps (the plane rotations above, 16 disjoint
-//                              pairs at a time), giving the tile's orthogonal
-//                              Q_I; the rotated tile goes to its next places
+//                              sweeps (the plane rotations above, JS/2
+//                              disjoint pairs at a time), giving the tile's
+//                              orthogonal Q_I; the rotated tile goes to its
+//                              next places
 //   jacobi_block_apply_kernel  the other tiles: Q_I^T G_IJ Q_J at the next
 //                              places, so that G <- J^T G J with
 //                              J = diag(Q_0, Q_1, ...)
 //   jacobi_block_vec_kernel    V <- V J
 // As in the single-index method every pair of indices is rotated in every
-// sweep (inside the super-block that holds both), in sixteen times fewer
-// rounds, each a few small products instead of a pass per rotation.
+// sweep (inside the super-block that holds both), in JB times fewer rounds,
+// each a few small products instead of a pass per rotation.  The apply and
+// eigenvector launches move all of G and V whatever JB is, so larger blocks
+// (fewer rounds) move fewer bytes a sweep.
 // ---------------------------------------------------------------------------
-constexpr int kJB = 16;          // indices per block
-constexpr int kJS = 2 * kJB;     // indices per super-block (a round position)
-constexpr int kJPad = kJS + 1;   // LDS row stride of a 32 x 32 tile (doubles)
+template <int JB>
+struct JBlk {
+    static constexpr int JS = 2 * JB;            // indices per super-block (a round position)
+    static constexpr int Pad = JS + 1;           // LDS row stride of a JS x JS tile (doubles)
+    static constexpr int NT = (JS / 2) * (JS / 2);  // solve threads: one 2 x 2 block each per step
+    static constexpr int NBK = JS / 16;          // 16 x 16 MFMA blocks per tile side
+};
 
-// Index at position k (of 32) in step t (of 31) of an inner sweep: index 0
-// stays, the others advance one place round a circle of 31 each step, and the
-// step pairs positions k and 31 - k, so 31 steps pair every two indices once.
-__device__ __forceinline__ int inner_pos(int k, int t) { return k == 0 ? 0 : 1 + (k - 1 + t) % (kJS - 1); }
+// Index at position k (of JS) in step t (of JS - 1) of an inner sweep: index
+// 0 stays, the others advance one place round a circle of JS - 1 each step,
+// and the step pairs positions k and JS - 1 - k, so JS - 1 steps pair every
+// two indices once.
+template <int JS>
+__device__ __forceinline__ int inner_pos(int k, int t) { return k == 0 ? 0 : 1 + (k - 1 + t) % (JS - 1); }
 
-// Place in the next round of row or column u (< 32) of super-block I.
+// Place in the next round of row or column u (< 2 JB) of super-block I.
+template <int JB>
 __device__ __forceinline__ int block_next(int I, int u, int nb) {
-    return next_place(2 * I + u / kJB, nb) * kJB + u % kJB;
+    return next_place(2 * I + u / JB, nb) * JB + u % JB;
 }
-
 
 // Workgroup (I, seq).  Inner sweeps run while the tile's off-diagonal mass is
 // above 1e-30 of its total and still falling a hundredfold per sweep once
 // below 1e-22 (the rounding floor), at most max_sweeps.  The tile is double
-// buffered: a step reads its pairs' 2 x 2 diagonal blocks (each thread works
-// out the two rotations it needs) and its own block from one buffer and
-// writes the other, so a step takes one barrier.
-__global__ __launch_bounds__(256) void jacobi_block_solve_kernel(const double *__restrict__ G, double *__restrict__ Gn,
-                                                                 double *__restrict__ Qb, int n, int max_sweeps) {
-    __shared__ double S[2][kJS][kJPad];
-    __shared__ double Qm[kJS][kJPad];
-    __shared__ double red[2][4];
-    const int I = blockIdx.x, seq = blockIdx.y, tid = threadIdx.x, nb = n / kJB;
+// buffered: a step reads its pairs' 2 x 2 diagonal blocks and its own block
+// from one buffer and writes the other, so a step takes one barrier.  Each
+// lane works out one rotation, its column pair's, and takes its row pair's
+// from the lane of the same wave that holds it.
+template <int JB>
+__global__ __launch_bounds__(JBlk<JB>::NT) void jacobi_block_solve_kernel(const double *__restrict__ G,
+                                                                        double *__restrict__ Gn,
+                                                                        double *__restrict__ Qb, int n,
+                                                                        int max_sweeps) {
+    constexpr int JS = JBlk<JB>::JS, Pad = JBlk<JB>::Pad, NT = JBlk<JB>::NT, NW = NT / 64, H = JS / 2;
+    __shared__ double S[2][JS][Pad];
+    __shared__ double Qm[JS][Pad];
+    __shared__ double red[2][NW];
+    const int I = blockIdx.x, seq = blockIdx.y, tid = threadIdx.x, nb = n / JB;
     const size_t base = static_cast<size_t>(seq) * n * n;
-    const double *g = G + base + static_cast<size_t>(I) * kJS * n + I * kJS;
-    for (int x = tid; x < kJS * kJS; x += 256) {
-        const int u = x / kJS, v = x % kJS;
+    const double *g = G + base + static_cast<size_t>(I) * JS * n + I * JS;
+    for (int x = tid; x < JS * JS; x += NT) {
+        const int u = x / JS, v = x % JS;
         S[0][u][v] = g[static_cast<size_t>(u) * n + v];
         Qm[u][v] = u == v ? 1.0 : 0.0;
     }
     __syncthreads();
-    const int br = tid >> 4, bc = tid & 15;  // this thread's 2 x 2 block: row pair br, column pair bc
+    const int br = tid / H, bc = tid % H;  // this thread's 2 x 2 block: row pair br, column pair bc
     int cur = 0;
     double prev = 0.0;
     for (int sw = 0;; ++sw) {
         double off = 0.0, tot = 0.0;
-        for (int x = tid; x < kJS * kJS; x += 256) {
-            const double v = S[cur][x / kJS][x % kJS];
+        for (int x = tid; x < JS * JS; x += NT) {
+            const double v = S[cur][x / JS][x % JS];
             tot += v * v;
-            if (x / kJS != x % kJS) off += v * v;
+            if (x / JS != x % JS) off += v * v;
         }
         off = wave_sum_d(off);
         tot = wave_sum_d(tot);
@@ -350,18 +365,24 @@ __global__ __launch_bounds__(256) void jacobi_block_solve_kernel(const double *_
             red[1][tid >> 6] = tot;
         }
         __syncthreads();
-        const double o = red[0][0] + red[0][1] + red[0][2] + red[0][3];
-        const double a = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+        double o = 0.0, a = 0.0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+            o += red[0][w];
+            a += red[1][w];
+        }
         const bool stop = !(o > 1e-30 * a) || sw == max_sweeps || (sw > 0 && o <= 1e-22 * a && o > 0.01 * prev);
         prev = o;
         if (stop) break;  // the same in every thread
-        for (int t = 0; t < kJS - 1; ++t) {
-            const double(*X)[kJPad] = S[cur];
-            double(*Y)[kJPad] = S[cur ^ 1];
-            const int p0 = inner_pos(br, t), q0 = inner_pos(kJS - 1 - br, t);
-            const int p1 = inner_pos(bc, t), q1 = inner_pos(kJS - 1 - bc, t);
-            const double2 ri = jacobi_rotation(X[p0][p0], X[q0][q0], X[p0][q0]);
+        for (int t = 0; t < JS - 1; ++t) {
+            const double(*X)[Pad] = S[cur];
+            double(*Y)[Pad] = S[cur ^ 1];
+            const int p0 = inner_pos<JS>(br, t), q0 = inner_pos<JS>(JS - 1 - br, t);
+            const int p1 = inner_pos<JS>(bc, t), q1 = inner_pos<JS>(JS - 1 - bc, t);
+            // this lane's rotation is pair bc's (bc = lane mod H, H dividing
+            // 64); pair br's (br < H) is lane br's, read across the wave
             const double2 rj = jacobi_rotation(X[p1][p1], X[q1][q1], X[p1][q1]);
+            const double2 ri = make_double2(__shfl(rj.x, br, 64), __shfl(rj.y, br, 64));
             const double x00 = X[p0][p1], x01 = X[p0][q1], x10 = X[q0][p1], x11 = X[q0][q1];
             const double y00 = rj.x * x00 - rj.y * x01, y01 = rj.y * x00 + rj.x * x01;
             const double y10 = rj.x * x10 - rj.y * x11, y11 = rj.y * x10 + rj.x * x11;
@@ -384,11 +405,11 @@ __global__ __launch_bounds__(256) void jacobi_block_solve_kernel(const double *_
             __syncthreads();
         }
     }
-    double *q = Qb + (static_cast<size_t>(seq) * (n / kJS) + I) * kJS * kJS;
-    for (int x = tid; x < kJS * kJS; x += 256) {
-        const int u = x / kJS, v = x % kJS;
+    double *q = Qb + (static_cast<size_t>(seq) * (n / JS) + I) * JS * JS;
+    for (int x = tid; x < JS * JS; x += NT) {
+        const int u = x / JS, v = x % JS;
         q[x] = Qm[u][v];
-        Gn[base + static_cast<size_t>(block_next(I, u, nb)) * n + block_next(I, v, nb)] = S[cur][u][v];
+        Gn[base + static_cast<size_t>(block_next<JB>(I, u, nb)) * n + block_next<JB>(I, v, nb)] = S[cur][u][v];
     }
 }
 
@@ -396,10 +417,12 @@ __global__ __launch_bounds__(256) void jacobi_block_solve_kernel(const double *_
 // cores (T = G_IJ Q_J, staged in LDS as the second product's B operand), Y
 // written at tile (I, J)'s next places and its transpose at tile (J, I)'s,
 // which keeps G exactly symmetric.
+template <int JB>
 __global__ __launch_bounds__(64) void jacobi_block_apply_kernel(const double *__restrict__ G, double *__restrict__ Gn,
                                                                 const double *__restrict__ Qb, int n) {
-    __shared__ double T[kJS][kJPad];
-    const int ns = n / kJS, seq = blockIdx.y, l = threadIdx.x, lr = l & 15, lk = l >> 4, nb = n / kJB;
+    constexpr int JS = JBlk<JB>::JS, Pad = JBlk<JB>::Pad, NBK = JBlk<JB>::NBK;
+    __shared__ double T[JS][Pad];
+    const int ns = n / JS, seq = blockIdx.y, l = threadIdx.x, lr = l & 15, lk = l >> 4, nb = n / JB;
     int p = blockIdx.x, I = 0;
     while (p >= ns - 1 - I) {
         p -= ns - 1 - I;
@@ -407,107 +430,122 @@ __global__ __launch_bounds__(64) void jacobi_block_apply_kernel(const double *__
     }
     const int J = I + 1 + p;
     const size_t base = static_cast<size_t>(seq) * n * n;
-    const double *g = G + base + static_cast<size_t>(I) * kJS * n + J * kJS;
-    const double *qi = Qb + (static_cast<size_t>(seq) * ns + I) * kJS * kJS;
-    const double *qj = Qb + (static_cast<size_t>(seq) * ns + J) * kJS * kJS;
+    const double *g = G + base + static_cast<size_t>(I) * JS * n + J * JS;
+    const double *qi = Qb + (static_cast<size_t>(seq) * ns + I) * JS * JS;
+    const double *qj = Qb + (static_cast<size_t>(seq) * ns + J) * JS * JS;
     // The contraction index k runs as 16 c + 4 (l / 16) + e: a lane reads four
     // consecutive k of its row (32 bytes, a whole 128-byte row segment per 16
     // lanes) and feeds them to four products, element e to the e-th.
-    f64x4 acc[2][2] = {};
+    f64x4 acc[NBK][NBK] = {};
 #pragma unroll
-    for (int c = 0; c < kJS / 16; ++c) {
+    for (int c = 0; c < JS / 16; ++c) {
         const int k0 = 16 * c + 4 * lk;
-        const f64x4 a0 = *reinterpret_cast<const f64x4 *>(g + static_cast<size_t>(lr) * n + k0);
-        const f64x4 a1 = *reinterpret_cast<const f64x4 *>(g + static_cast<size_t>(16 + lr) * n + k0);
+        f64x4 a[NBK];
+#pragma unroll
+        for (int rb = 0; rb < NBK; ++rb)
+            a[rb] = *reinterpret_cast<const f64x4 *>(g + static_cast<size_t>(16 * rb + lr) * n + k0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const double b0 = qj[(k0 + e) * kJS + lr], b1 = qj[(k0 + e) * kJS + 16 + lr];
-            acc[0][0] = mfma_f64(a0[e], b0, acc[0][0]);
-            acc[0][1] = mfma_f64(a0[e], b1, acc[0][1]);
-            acc[1][0] = mfma_f64(a1[e], b0, acc[1][0]);
-            acc[1][1] = mfma_f64(a1[e], b1, acc[1][1]);
+            double b[NBK];
+#pragma unroll
+            for (int cb = 0; cb < NBK; ++cb) b[cb] = qj[(k0 + e) * JS + 16 * cb + lr];
+#pragma unroll
+            for (int rb = 0; rb < NBK; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < NBK; ++cb) acc[rb][cb] = mfma_f64(a[rb][e], b[cb], acc[rb][cb]);
         }
     }
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < NBK; ++rb)
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
+        for (int cb = 0; cb < NBK; ++cb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) T[rb * 16 + 4 * j + lk][cb * 16 + lr] = acc[rb][cb][j];
+            for (int j = 0; j < 4; ++j) {
+                T[16 * rb + 4 * j + lk][16 * cb + lr] = acc[rb][cb][j];
+                acc[rb][cb][j] = 0.0;
+            }
     __syncthreads();
-    f64x4 y[2][2] = {};
-#pragma unroll
-    for (int st = 0; st < kJS / 4; ++st) {
+    // Y = Q_I^T T, accumulated in acc again
+#pragma unroll 4
+    for (int st = 0; st < JS / 4; ++st) {
         const int k = 4 * st + lk;
-        const double a0 = qi[k * kJS + lr], a1 = qi[k * kJS + 16 + lr];  // (Q_I^T)[row][k] = Q_I[k][row]
-        const double b0 = T[k][lr], b1 = T[k][16 + lr];
-        y[0][0] = mfma_f64(a0, b0, y[0][0]);
-        y[0][1] = mfma_f64(a0, b1, y[0][1]);
-        y[1][0] = mfma_f64(a1, b0, y[1][0]);
-        y[1][1] = mfma_f64(a1, b1, y[1][1]);
+        double a[NBK], b[NBK];
+#pragma unroll
+        for (int rb = 0; rb < NBK; ++rb) a[rb] = qi[k * JS + 16 * rb + lr];  // (Q_I^T)[row][k] = Q_I[k][row]
+#pragma unroll
+        for (int cb = 0; cb < NBK; ++cb) b[cb] = T[k][16 * cb + lr];
+#pragma unroll
+        for (int rb = 0; rb < NBK; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < NBK; ++cb) acc[rb][cb] = mfma_f64(a[rb], b[cb], acc[rb][cb]);
     }
     __syncthreads();
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+    for (int rb = 0; rb < NBK; ++rb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int u = rb * 16 + 4 * j + lk;
-            const size_t row = base + static_cast<size_t>(block_next(I, u, nb)) * n;
+            const int u = 16 * rb + 4 * j + lk;
+            const size_t row = base + static_cast<size_t>(block_next<JB>(I, u, nb)) * n;
 #pragma unroll
-            for (int cb = 0; cb < 2; ++cb) {
-                Gn[row + block_next(J, cb * 16 + lr, nb)] = y[rb][cb][j];
-                T[u][cb * 16 + lr] = y[rb][cb][j];
+            for (int cb = 0; cb < NBK; ++cb) {
+                Gn[row + block_next<JB>(J, 16 * cb + lr, nb)] = acc[rb][cb][j];
+                T[u][16 * cb + lr] = acc[rb][cb][j];
             }
         }
     __syncthreads();
-    // tile (J, I): row v of it is column v of Y
-    const int u = l & 31, cu = block_next(I, u, nb);
+    // tile (J, I): row v of it is column v of Y; a pass writes 64 / JS rows
+    const int u = l % JS, cu = block_next<JB>(I, u, nb);
 #pragma unroll 4
-    for (int it = 0; it < kJS / 2; ++it) {
-        const int v = 2 * it + (l >> 5);
-        Gn[base + static_cast<size_t>(block_next(J, v, nb)) * n + cu] = T[u][v];
+    for (int it = 0; it < JS * JS / 64; ++it) {
+        const int v = it * (64 / JS) + l / JS;
+        Gn[base + static_cast<size_t>(block_next<JB>(J, v, nb)) * n + cu] = T[u][v];
     }
 }
 
-// V <- V J: one wave per 64 rows of super-block J's 32 columns, times Q_J on
+// V <- V J: one wave per 64 rows of super-block J's JS columns, times Q_J on
 // the matrix cores, written at the next round's column places (rows stay).
+template <int JB>
 __global__ __launch_bounds__(64) void jacobi_block_vec_kernel(const double *__restrict__ V, double *__restrict__ Vn,
                                                               const double *__restrict__ Qb, int n) {
-    const int ns = n / kJS, J = blockIdx.y, seq = blockIdx.z, l = threadIdx.x, lr = l & 15, lk = l >> 4, nb = n / kJB;
+    constexpr int JS = JBlk<JB>::JS, NBK = JBlk<JB>::NBK;
+    const int ns = n / JS, J = blockIdx.y, seq = blockIdx.z, l = threadIdx.x, lr = l & 15, lk = l >> 4, nb = n / JB;
     const int r0 = blockIdx.x * 64;
     const size_t base = static_cast<size_t>(seq) * n * n;
-    const double *qj = Qb + (static_cast<size_t>(seq) * ns + J) * kJS * kJS;
+    const double *qj = Qb + (static_cast<size_t>(seq) * ns + J) * JS * JS;
     // k runs as 16 c + 4 (l / 16) + e, as in the apply kernel
-    f64x4 acc[4][2] = {};
+    f64x4 acc[4][NBK] = {};
 #pragma unroll
-    for (int c = 0; c < kJS / 16; ++c) {
+    for (int c = 0; c < JS / 16; ++c) {
         const int k0 = 16 * c + 4 * lk;
         f64x4 a[4];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) {
             const int row = r0 + rb * 16 + lr;
-            a[rb] = row < n ? *reinterpret_cast<const f64x4 *>(V + base + static_cast<size_t>(row) * n + J * kJS + k0)
+            a[rb] = row < n ? *reinterpret_cast<const f64x4 *>(V + base + static_cast<size_t>(row) * n + J * JS + k0)
                             : f64x4{0.0, 0.0, 0.0, 0.0};
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const double b0 = qj[(k0 + e) * kJS + lr], b1 = qj[(k0 + e) * kJS + 16 + lr];
+            double b[NBK];
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                acc[rb][0] = mfma_f64(a[rb][e], b0, acc[rb][0]);
-                acc[rb][1] = mfma_f64(a[rb][e], b1, acc[rb][1]);
-            }
+            for (int cb = 0; cb < NBK; ++cb) b[cb] = qj[(k0 + e) * JS + 16 * cb + lr];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < NBK; ++cb) acc[rb][cb] = mfma_f64(a[rb][e], b[cb], acc[rb][cb]);
         }
     }
-    const int c0 = block_next(J, lr, nb), c1 = block_next(J, 16 + lr, nb);
+    int col[NBK];
+#pragma unroll
+    for (int cb = 0; cb < NBK; ++cb) col[cb] = block_next<JB>(J, 16 * cb + lr, nb);
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int row = r0 + rb * 16 + 4 * j + lk;
             if (row < n) {
-                Vn[base + static_cast<size_t>(row) * n + c0] = acc[rb][0][j];
-                Vn[base + static_cast<size_t>(row) * n + c1] = acc[rb][1][j];
+#pragma unroll
+                for (int cb = 0; cb < NBK; ++cb) Vn[base + static_cast<size_t>(row) * n + col[cb]] = acc[rb][cb][j];
             }
         }
 }
@@ -714,12 +752,19 @@ int factorize_device(int bf16, int batch, int hkv, int s, int d, int r, const vo
     std::vector<int32_t> sel_h(static_cast<size_t>(group) * rr);
     std::vector<int32_t> order(n);
     const bool log_sweeps = std::getenv("SKV_FACTOR_LOG") != nullptr;
-    // 32-index super-blocks when n is a multiple of 32 with at least 4 blocks
-    // of 16 (the round cycle needs 4 places); SKV_FACTOR_BLOCK=0 keeps the
+    // block rounds: blocks of 16 where n is a multiple of 32 with at least 4
+    // of them (the round cycle needs 4 places).  Blocks of 32 halve the
+    // rounds and the apply and eigenvector passes a sweep, but their tile
+    // solve (63 steps over 16 waves) costs more than that saves (128K b8:
+    // 78.7 against 70.4 ms of rounds a layer); SKV_FACTOR_BLOCK=32 asks for
+    // them where n is a multiple of 64 with at least 4, 0 keeps the
     // single-index rounds
     const char *fb = std::getenv("SKV_FACTOR_BLOCK");
-    const bool blockwise = n % kJS == 0 && n / kJB >= 4 && !(fb && fb[0] == '0');
-    const int nsb = n / kJS;
+    const int fbv = fb ? std::atoi(fb) : 1;
+    const bool fit32 = n % 64 == 0 && n / 32 >= 4, fit16 = n % 32 == 0 && n / 16 >= 4;
+    const int jb = fbv == 0 ? 0 : (fbv == 32 && fit32 ? 32 : (fit16 ? 16 : 0));
+    const bool blockwise = jb > 0;
+    const int js = 2 * jb, nsb = blockwise ? n / js : 0;
     // inner sweeps per super-block and round at most: one sweep a round costs
     // the fewest rounds' time (the outer sweeps finish what it leaves)
     const char *fi = std::getenv("SKV_FACTOR_INNER");
@@ -739,7 +784,7 @@ int factorize_device(int bf16, int batch, int hkv, int s, int d, int r, const vo
     FZ_HIP(hipEventCreateWithFlags(&ev[0], hipEventDisableTiming));
     FZ_HIP(hipEventCreateWithFlags(&ev[1], hipEventDisableTiming));
     FZ_HIP(hipMalloc(&sel, static_cast<size_t>(group) * rr * 4));
-    if (blockwise) FZ_HIP(hipMalloc(&Qb, static_cast<size_t>(group) * nsb * kJS * kJS * 8));
+    if (blockwise) FZ_HIP(hipMalloc(&Qb, static_cast<size_t>(group) * nsb * js * js * 8));
     for (int g0 = 0; g0 < batch; g0 += group) {
         const int gc = batch - g0 < group ? batch - g0 : group;
         const char *kp = static_cast<const char *>(k_pre) + static_cast<size_t>(g0) * hkv * s * d * esz;
@@ -759,13 +804,22 @@ int factorize_device(int bf16, int batch, int hkv, int s, int d, int r, const vo
         // one sweep's rounds and its measure, read back through slot k % 2
         auto enqueue_sweep = [&](int k) -> hipError_t {
             if (blockwise) {
-                for (int round = 0; round < n / kJB - 1; ++round) {
-                    hipLaunchKernelGGL(jacobi_block_solve_kernel, dim3(nsb, gc), dim3(256), 0, st, Gc, Gn, Qb, n,
-                                       inner);
-                    hipLaunchKernelGGL(jacobi_block_apply_kernel, dim3(nsb * (nsb - 1) / 2, gc), dim3(64), 0, st, Gc,
-                                       Gn, Qb, n);
-                    hipLaunchKernelGGL(jacobi_block_vec_kernel, dim3((n + 63) / 64, nsb, gc), dim3(64), 0, st, Vc, Vn,
-                                       Qb, n);
+                for (int round = 0; round < n / jb - 1; ++round) {
+                    if (jb == 32) {
+                        hipLaunchKernelGGL(jacobi_block_solve_kernel<32>, dim3(nsb, gc), dim3(JBlk<32>::NT), 0, st,
+                                           Gc, Gn, Qb, n, inner);
+                        hipLaunchKernelGGL(jacobi_block_apply_kernel<32>, dim3(nsb * (nsb - 1) / 2, gc), dim3(64), 0,
+                                           st, Gc, Gn, Qb, n);
+                        hipLaunchKernelGGL(jacobi_block_vec_kernel<32>, dim3((n + 63) / 64, nsb, gc), dim3(64), 0, st,
+                                           Vc, Vn, Qb, n);
+                    } else {
+                        hipLaunchKernelGGL(jacobi_block_solve_kernel<16>, dim3(nsb, gc), dim3(JBlk<16>::NT), 0, st,
+                                           Gc, Gn, Qb, n, inner);
+                        hipLaunchKernelGGL(jacobi_block_apply_kernel<16>, dim3(nsb * (nsb - 1) / 2, gc), dim3(64), 0,
+                                           st, Gc, Gn, Qb, n);
+                        hipLaunchKernelGGL(jacobi_block_vec_kernel<16>, dim3((n + 63) / 64, nsb, gc), dim3(64), 0, st,
+                                           Vc, Vn, Qb, n);
+                    }
                     std::swap(Gc, Gn);
                     std::swap(Vc, Vn);
                 }

@@ -12,8 +12,8 @@ heads' keys to ~1e-7.  Checked per sequence:
   * orthonormal rows of B (all heads together);
   * zero columns of A and rows of B past n = h_kv * d;
   * batches of more than the eight sequences solved at once;
-  * both round forms of the eigensolver (32-index super-blocks, single
-    index pairs);
+  * the eigensolver's round forms (super-blocks of 32 and of 64 indices,
+    single index pairs);
   * all-zero keys (the degenerate case: A = 0, orthonormal B, finite).
 """
 import dataclasses
@@ -45,10 +45,13 @@ def _products(A, B):
     return np.einsum("bsr,bhrd->bhsd", A, B)
 
 
-# The eigensolver's two round forms: 32-index super-blocks (the default where
-# n is a multiple of 32 and at least 64) and single index pairs.
-PATHS = {"block": "1", "single": "0"}
-PARAMS = [(c, "block") for c in CASES] + [("tiny-fp32", "single"), ("bf16-glm-shape", "single")]
+# The eigensolver's round forms: super-blocks of 32 indices (blocks of 16,
+# the default), of 64 indices (blocks of 32, asked for), and single index
+# pairs.
+PATHS = {"block": "1", "block32": "32", "single": "0"}
+PARAMS = ([(c, "block") for c in CASES] + [("tiny-fp32", "block32"), ("bf16-glm-shape", "block32"),
+                                           ("bf16-llama-32k", "block32")]
+          + [("tiny-fp32", "single"), ("bf16-glm-shape", "single")])
 
 
 @pytest.mark.parametrize("case,path", PARAMS, ids=[f"{c}-{p}" for c, p in PARAMS])
