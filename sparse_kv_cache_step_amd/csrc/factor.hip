@@ -351,7 +351,7 @@ __global__ __launch_bounds__(JBlk<JB>::NT) void jacobi_block_solve_kernel(const 
     const int br = tid / H, bc = tid % H;  // this thread's 2 x 2 block: row pair br, column pair bc
     int cur = 0;
     double prev = 0.0;
-    for (int sw = 0;; ++sw) {
+    for (int sw = 0; sw < max_sweeps; ++sw) {
         double off = 0.0, tot = 0.0;
         for (int x = tid; x < JS * JS; x += NT) {
             const double v = S[cur][x / JS][x % JS];
@@ -371,9 +371,9 @@ __global__ __launch_bounds__(JBlk<JB>::NT) void jacobi_block_solve_kernel(const 
             o += red[0][w];
             a += red[1][w];
         }
-        const bool stop = !(o > 1e-30 * a) || sw == max_sweeps || (sw > 0 && o <= 1e-22 * a && o > 0.01 * prev);
+        const bool stop = !(o > 1e-30 * a) || (sw > 0 && o <= 1e-22 * a && o > 0.01 * prev);
         prev = o;
-        if (stop) break;  // the same in every thread
+        if (stop) break;  // the same in every thread (red is rewritten only after the steps' barriers)
         for (int t = 0; t < JS - 1; ++t) {
             const double(*X)[Pad] = S[cur];
             double(*Y)[Pad] = S[cur ^ 1];
