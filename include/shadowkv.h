@@ -343,8 +343,9 @@ int shadowkv_get_timing(skv_layer *layer, double *ms_out, int64_t *steps_out);
  *   A      device (batch, seq_len, rank), written
  *   B      device (batch, heads_kv, rank, head_dim), written
  * With rank > n the columns past n are zero.  The call allocates its own
- * device scratch (about 0.5 GB at n = 1024: the Gram partials, two copies of
- * the matrix and of the eigenvectors for 8 sequences at a time), runs on
+ * device scratch (about 1.3 GB at n = 1024: the Gram partials of up to 16 row
+ * slices, two copies of the matrix and of the eigenvectors for 8 sequences at
+ * a time), runs on
  * `stream`, reads back the convergence measure once per sweep (through a
  * small pinned buffer) and the eigenvalues at the end, and returns when the
  * factors are written.
